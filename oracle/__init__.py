@@ -1,0 +1,169 @@
+"""fp64 CPU oracle for QK-Norm -- TEST INFRASTRUCTURE ONLY.
+
+Only the tests, the smoke check and the bench's CPU-baseline leg may import
+this package.  The HIP library never calls it and has no fallback to it.
+
+The arithmetic lives in ``qknorm_oracle.c`` (plain C, fp64, OpenMP over
+tokens); this module only marshals numpy arrays.  Every function returns the
+fp64 result ``y`` (V and padding columns copied through) and the result rounded
+once, to nearest-even, to the I/O dtype ``yr`` (same storage as the input:
+float32, or uint16 bf16 bit patterns).
+
+Pins (tests/test_oracle_pins.py): unit RMS, scale invariance, the shard-sum
+identity, exact brute force on tiny inputs, closed-form rows, per-head vs
+layerwise identities, numpy/torch library cross-checks, and rounding against
+torch's fp64 -> bf16 conversion.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "qknorm_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+F32 = 0
+BF16 = 1
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile the C oracle with gcc (-O2, no fast-math, OpenMP)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp"
+        cmd = ["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fopenmp",
+               "-fPIC", "-shared", "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build(force=False)
+        lib = ctypes.CDLL(_LIB)
+        P, I64, I32, D = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_double
+        lib.oracle_per_head.argtypes = [P, I32, I64, I64, I32, I32, I32, P, P, D, P, P]
+        lib.oracle_layerwise.argtypes = [P, I32, I64, I64, I64, I64, P, P, D, I32, P, P]
+        lib.oracle_partials.argtypes = [P, I32, I64, I64, I64, I64, I32, P, P]
+        lib.oracle_apply.argtypes = [P, I32, I64, I64, I64, I64, P, P, I32, D, D, P, P, D, P, P]
+        lib.oracle_round.argtypes = [P, I64, I32, P]
+        for f in (lib.oracle_per_head, lib.oracle_layerwise, lib.oracle_partials,
+                  lib.oracle_apply, lib.oracle_round, lib.oracle_max_threads):
+            f.restype = I32
+        _lib = lib
+    return _lib
+
+
+def max_threads() -> int:
+    """OpenMP threads the oracle's parallel loops use."""
+    return int(_load().oracle_max_threads())
+
+
+def _storage(dtype: int):
+    if dtype == F32:
+        return np.float32
+    if dtype == BF16:
+        return np.uint16
+    raise ValueError(f"unknown dtype code {dtype}")
+
+
+def _arr(a, dtype):
+    a = np.ascontiguousarray(a, dtype=_storage(dtype))
+    return a, a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _opt(a, dtype):
+    if a is None:
+        return None, None
+    return _arr(a, dtype)
+
+
+def _outs(shape, dtype, want_y=True):
+    y = np.empty(shape, dtype=np.float64) if want_y else None
+    yr = np.empty(shape, dtype=_storage(dtype))
+    yp = y.ctypes.data_as(ctypes.c_void_p) if want_y else None
+    return y, yr, yp, yr.ctypes.data_as(ctypes.c_void_p)
+
+
+def _check(rc, what):
+    if rc != 0:
+        raise ValueError(f"oracle {what}: arguments rejected")
+
+
+def per_head(x, dtype, hq, hkv, head_dim, gamma_q, gamma_k, eps, want_y=True):
+    """Per-head QK-Norm of fused rows x[T, ld] (Q heads, then K heads, then V)."""
+    x, xp = _arr(x, dtype)
+    T, ld = x.shape
+    gq_keep, gq = _arr(gamma_q, dtype)
+    gk_keep, gk = _opt(gamma_k, dtype)
+    y, yr, yp, yrp = _outs(x.shape, dtype, want_y)
+    _check(_load().oracle_per_head(xp, dtype, T, ld, hq, hkv, head_dim, gq, gk,
+                                   float(eps), yp, yrp), "per_head")
+    return y, yr
+
+
+def layerwise(x, dtype, wq, wk, gamma_q, gamma_k, eps, nshards=1, want_y=True):
+    """Layerwise QK-Norm of fused rows over the full Q and K widths via shard sums."""
+    x, xp = _arr(x, dtype)
+    T, ld = x.shape
+    gq_keep, gq = _opt(gamma_q, dtype)
+    gk_keep, gk = _opt(gamma_k, dtype)
+    y, yr, yp, yrp = _outs(x.shape, dtype, want_y)
+    _check(_load().oracle_layerwise(xp, dtype, T, ld, wq, wk, gq, gk, float(eps), nshards,
+                                    yp, yrp), "layerwise")
+    return y, yr
+
+
+def partials(x, dtype, wq, wk, nshards):
+    """fp64 shard sums of squares, each shaped [nshards, T]."""
+    x, xp = _arr(x, dtype)
+    T, ld = x.shape
+    pq = np.empty((nshards, T), dtype=np.float64)
+    pk = np.empty((nshards, T), dtype=np.float64)
+    _check(_load().oracle_partials(xp, dtype, T, ld, wq, wk, nshards,
+                                   pq.ctypes.data_as(ctypes.c_void_p),
+                                   pk.ctypes.data_as(ctypes.c_void_p)), "partials")
+    return pq, pk
+
+
+def apply(x, dtype, wq, wk, part_q, part_k, norm_wq, norm_wk, gamma_q, gamma_k, eps,
+          want_y=True):
+    """Normalise with given partials [nparts, T] and divisors norm_wq, norm_wk."""
+    x, xp = _arr(x, dtype)
+    T, ld = x.shape
+    pq = np.ascontiguousarray(part_q, dtype=np.float64)
+    pk = np.ascontiguousarray(part_k, dtype=np.float64)
+    nparts = pq.shape[0]
+    gq_keep, gq = _opt(gamma_q, dtype)
+    gk_keep, gk = _opt(gamma_k, dtype)
+    y, yr, yp, yrp = _outs(x.shape, dtype, want_y)
+    _check(_load().oracle_apply(xp, dtype, T, ld, wq, wk, pq.ctypes.data_as(ctypes.c_void_p),
+                                pk.ctypes.data_as(ctypes.c_void_p), nparts, float(norm_wq),
+                                float(norm_wk), gq, gk, float(eps), yp, yrp), "apply")
+    return y, yr
+
+
+def round_to(v, dtype):
+    """Round fp64 values once, to nearest-even, to dtype storage."""
+    v = np.ascontiguousarray(v, dtype=np.float64)
+    out = np.empty(v.shape, dtype=_storage(dtype))
+    _check(_load().oracle_round(v.ctypes.data_as(ctypes.c_void_p), v.size, dtype,
+                                out.ctypes.data_as(ctypes.c_void_p)), "round")
+    return out
+
+
+def decode(a, dtype):
+    """Exact fp64 values of stored elements (bf16 patterns widened)."""
+    a = np.asarray(a)
+    if dtype == F32:
+        return a.astype(np.float64)
+    with np.errstate(invalid="ignore"):
+        return (a.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)

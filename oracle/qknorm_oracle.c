@@ -1,0 +1,290 @@
+/*
+ * QK-Norm oracle: a plain, slow, fp64 CPU implementation of what the method
+ * computes.  TEST INFRASTRUCTURE ONLY -- it is what the HIP library is checked
+ * against, never a path the library takes.  It shares no code with the HIP
+ * sources (its own decode, its own rounding, its own loops).
+ *
+ * What is computed (restated from the pages, not copied):
+ *
+ *  RMSNorm of a width-n group x with weights g
+ *      S   = sum_j x_j^2
+ *      y_j = g_j * x_j / sqrt(S / n + eps)
+ *  -- "SwiftQK" verdict page (pith.science, arXiv 2608.09160), core
+ *     discovery and key machinery: the divisor is sqrt(S_global/H + eps) with
+ *     S_global the sum of squares over the full width H, and the result is
+ *     multiplied by the RMS weights.  eps sits inside the square root, added
+ *     to the mean square.
+ *
+ *  Per-head QK-Norm: n = head_dim, one group per Q head and per K head; one
+ *  gamma of length head_dim for all Q heads, another for all K heads.
+ *  -- sglang PR "Add turbomind_rms_norm to accelerate QK norm in Qwen3
+ *     models" (#13189), Motivation and Modifications: an RMSNorm whose hidden
+ *     size is the head dimension (128).
+ *
+ *  Layerwise QK-Norm: n = the whole projected Q width (and separately the
+ *  whole K width); gamma as wide as the group.
+ *  -- SwiftQK summary page (newx.sg), Abstract: the normalisation factor
+ *     depends on the full hidden vector.
+ *
+ *  Shard partials: S = sum over shards r of S_local,r; each shard is a
+ *  contiguous equal slice; the divisor stays the FULL width.
+ *  -- SwiftQK verdict page, key machinery (the per-rank factor over
+ *     S_local,r is replaced by the global one over sum_r S_local,r).
+ *
+ *  Fused row layout: [Q (hq*D) | K (hkv*D) | V (hkv*D)], split by widths,
+ *  V not normalised.
+ *  -- "Explain combined QKV projection ..." lesson, section "With GQA".
+ *
+ * Readings taken where the pages are silent: compute in fp64; gamma is a plain
+ * per-channel multiplier (no 1+gamma); columns outside Q and K (V, padding)
+ * are copied through unchanged; outputs are also given rounded once, to
+ * nearest-even, to the I/O dtype.
+ *
+ * dtype codes: 0 = fp32, 1 = bf16 (stored as its 16-bit pattern).
+ * Every function returns 0, or -1 on an argument it cannot use.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* ------------------------------------------------------------------ I/O -- */
+
+/* Exact value of element i of a stored fp32 or bf16 array. */
+static double load_value(const void *p, int dtype, int64_t i)
+{
+    if (dtype == 0)
+        return (double)((const float *)p)[i];
+    uint32_t bits = (uint32_t)((const uint16_t *)p)[i] << 16;
+    float f;
+    memcpy(&f, &bits, sizeof f);
+    return (double)f;
+}
+
+/* Round v to the nearest bf16, ties to even, in a single step from fp64.
+ * bf16 keeps 8 significant bits; below 2^-126 the spacing is fixed at 2^-133. */
+static uint16_t round_to_bf16(double v)
+{
+    if (isnan(v))
+        return 0x7FC0;
+    if (isinf(v))
+        return v > 0 ? 0x7F80 : 0xFF80;
+    if (v == 0.0)
+        return signbit(v) ? 0x8000 : 0x0000;
+    int e;
+    frexp(v, &e);                      /* |v| = m * 2^e, 0.5 <= m < 1 */
+    if (e < -125)
+        e = -125;
+    double q = nearbyint(ldexp(v, 8 - e));   /* default mode: nearest, ties even */
+    double r = ldexp(q, e - 8);
+    if (fabs(r) > 3.3895313892515355e38)     /* beyond the largest finite bf16 */
+        return r > 0 ? 0x7F80 : 0xFF80;
+    float f = (float)r;                      /* exact: r has at most 8 significant bits */
+    uint32_t bits;
+    memcpy(&bits, &f, sizeof bits);
+    return (uint16_t)(bits >> 16);
+}
+
+static void store_rounded(void *p, int dtype, int64_t i, double v)
+{
+    if (dtype == 0)
+        ((float *)p)[i] = (float)v;          /* C conversion: nearest, ties even */
+    else
+        ((uint16_t *)p)[i] = round_to_bf16(v);
+}
+
+static void copy_raw(void *dst, const void *src, int dtype, int64_t i)
+{
+    if (dtype == 0)
+        ((float *)dst)[i] = ((const float *)src)[i];
+    else
+        ((uint16_t *)dst)[i] = ((const uint16_t *)src)[i];
+}
+
+/* --------------------------------------------------------------- pieces -- */
+
+/* Sum of squares of n consecutive stored values starting at element off,
+ * left to right. */
+static double sum_of_squares(const void *x, int dtype, int64_t off, int64_t n)
+{
+    double s = 0.0;
+    for (int64_t j = 0; j < n; ++j) {
+        double v = load_value(x, dtype, off + j);
+        s += v * v;
+    }
+    return s;
+}
+
+/* Normalise one group with a given total S: y_j = x_j * g_j / sqrt(S/n + eps).
+ * x element off+j pairs with gamma element goff+j. */
+static void apply_group(const void *x, int dtype, int64_t off, int64_t width,
+                        double S, double n, const void *g, int64_t goff,
+                        double eps, double *y, void *yr)
+{
+    double inv = 1.0 / sqrt(S / n + eps);
+    for (int64_t j = 0; j < width; ++j) {
+        double v = load_value(x, dtype, off + j) * load_value(g, dtype, goff + j) * inv;
+        if (y)
+            y[off + j] = v;
+        if (yr)
+            store_rounded(yr, dtype, off + j, v);
+    }
+}
+
+/* Columns that no normalisation touches are passed through unchanged. */
+static void pass_through(const void *x, int dtype, int64_t off, int64_t width,
+                         double *y, void *yr)
+{
+    for (int64_t j = 0; j < width; ++j) {
+        if (y)
+            y[off + j] = load_value(x, dtype, off + j);
+        if (yr)
+            copy_raw(yr, x, dtype, off + j);
+    }
+}
+
+/* Total of one group computed through nshards contiguous equal shards:
+ * each shard summed left to right, then the shard sums added in order. */
+static double sharded_total(const void *x, int dtype, int64_t off, int64_t width,
+                            int nshards)
+{
+    int64_t sw = width / nshards;
+    double S = 0.0;
+    for (int r = 0; r < nshards; ++r)
+        S += sum_of_squares(x, dtype, off + (int64_t)r * sw, sw);
+    return S;
+}
+
+static int bad_dtype(int dtype) { return dtype != 0 && dtype != 1; }
+
+/* ------------------------------------------------------------ entry points -- */
+
+int oracle_max_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/* Per-head QK-Norm on fused rows x[T, ld]: Q heads 0..hq-1 at columns h*D with
+ * gamma_q, K heads 0..hkv-1 at columns hq*D + h*D with gamma_k (both of length
+ * D).  Writes the fp64 result to y[T*ld] and the dtype-rounded result to
+ * yr[T*ld]; either may be NULL. */
+int oracle_per_head(const void *x, int dtype, int64_t T, int64_t ld, int hq, int hkv,
+                    int D, const void *gamma_q, const void *gamma_k, double eps,
+                    double *y, void *yr)
+{
+    if (bad_dtype(dtype) || T < 0 || hq < 0 || hkv < 0 || D <= 0 ||
+        ld < (int64_t)(hq + hkv) * D)
+        return -1;
+    const int64_t wq = (int64_t)hq * D, wk = (int64_t)hkv * D;
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+        const int64_t row = t * ld;
+        for (int h = 0; h < hq; ++h) {
+            int64_t off = row + (int64_t)h * D;
+            double S = sum_of_squares(x, dtype, off, D);
+            apply_group(x, dtype, off, D, S, (double)D, gamma_q, 0, eps, y, yr);
+        }
+        for (int h = 0; h < hkv; ++h) {
+            int64_t off = row + wq + (int64_t)h * D;
+            double S = sum_of_squares(x, dtype, off, D);
+            apply_group(x, dtype, off, D, S, (double)D, gamma_k, 0, eps, y, yr);
+        }
+        pass_through(x, dtype, row + wq + wk, ld - wq - wk, y, yr);
+    }
+    return 0;
+}
+
+/* Layerwise QK-Norm on fused rows: Q = columns [0, wq) with gamma_q[wq], K =
+ * columns [wq, wq+wk) with gamma_k[wk].  The total of each group is taken as
+ * nshards contiguous shard sums added in order; the mean divides by the full
+ * group width.  nshards must divide wq and wk. */
+int oracle_layerwise(const void *x, int dtype, int64_t T, int64_t ld, int64_t wq,
+                     int64_t wk, const void *gamma_q, const void *gamma_k, double eps,
+                     int nshards, double *y, void *yr)
+{
+    if (bad_dtype(dtype) || T < 0 || wq < 0 || wk < 0 || ld < wq + wk || nshards <= 0 ||
+        wq % nshards != 0 || wk % nshards != 0)
+        return -1;
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+        const int64_t row = t * ld;
+        if (wq > 0) {
+            double S = sharded_total(x, dtype, row, wq, nshards);
+            apply_group(x, dtype, row, wq, S, (double)wq, gamma_q, 0, eps, y, yr);
+        }
+        if (wk > 0) {
+            double S = sharded_total(x, dtype, row + wq, wk, nshards);
+            apply_group(x, dtype, row + wq, wk, S, (double)wk, gamma_k, 0, eps, y, yr);
+        }
+        pass_through(x, dtype, row + wq + wk, ld - wq - wk, y, yr);
+    }
+    return 0;
+}
+
+/* Shard partial sums of squares: part_q[r*T + t] over Q columns
+ * [r*wq/R, (r+1)*wq/R) of row t, and likewise part_k over K. */
+int oracle_partials(const void *x, int dtype, int64_t T, int64_t ld, int64_t wq,
+                    int64_t wk, int nshards, double *part_q, double *part_k)
+{
+    if (bad_dtype(dtype) || T < 0 || wq < 0 || wk < 0 || ld < wq + wk || nshards <= 0 ||
+        wq % nshards != 0 || wk % nshards != 0)
+        return -1;
+    const int64_t sq = wq / nshards, sk = wk / nshards;
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+        for (int r = 0; r < nshards; ++r) {
+            if (part_q)
+                part_q[(int64_t)r * T + t] = sum_of_squares(x, dtype, t * ld + r * sq, sq);
+            if (part_k)
+                part_k[(int64_t)r * T + t] = sum_of_squares(x, dtype, t * ld + wq + r * sk, sk);
+        }
+    }
+    return 0;
+}
+
+/* Apply with given partials: S_t = sum over r < nparts of part[r*T + t] (in
+ * order), mean = S_t / norm_w, then the same per-channel scaling over the
+ * local widths wq, wk.  Under tensor parallelism the local width is a slice
+ * and norm_w is the full width; on one device norm_w equals the width. */
+int oracle_apply(const void *x, int dtype, int64_t T, int64_t ld, int64_t wq, int64_t wk,
+                 const double *part_q, const double *part_k, int nparts, double norm_wq,
+                 double norm_wk, const void *gamma_q, const void *gamma_k, double eps,
+                 double *y, void *yr)
+{
+    if (bad_dtype(dtype) || T < 0 || wq < 0 || wk < 0 || ld < wq + wk || nparts <= 0)
+        return -1;
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+        const int64_t row = t * ld;
+        if (wq > 0) {
+            double S = 0.0;
+            for (int r = 0; r < nparts; ++r)
+                S += part_q[(int64_t)r * T + t];
+            apply_group(x, dtype, row, wq, S, norm_wq, gamma_q, 0, eps, y, yr);
+        }
+        if (wk > 0) {
+            double S = 0.0;
+            for (int r = 0; r < nparts; ++r)
+                S += part_k[(int64_t)r * T + t];
+            apply_group(x, dtype, row + wq, wk, S, norm_wk, gamma_k, 0, eps, y, yr);
+        }
+        pass_through(x, dtype, row + wq + wk, ld - wq - wk, y, yr);
+    }
+    return 0;
+}
+
+/* Rounding helper exposed for the rounding pin: n fp64 values to dtype. */
+int oracle_round(const double *v, int64_t n, int dtype, void *out)
+{
+    if (bad_dtype(dtype) || n < 0)
+        return -1;
+    for (int64_t i = 0; i < n; ++i)
+        store_rounded(out, dtype, i, v[i]);
+    return 0;
+}

@@ -1,0 +1,442 @@
+"""Checks that pin the fp64 oracle to something other than itself.
+
+Each ``check_*`` function raises AssertionError on a violation.  They are
+plain functions, not tests, so that ``test_oracle_pins`` can run them against
+the real oracle and ``test_oracle_mutants`` can run them against deliberately
+broken builds of it (each mutant must fail at least one check).
+
+What each pins:
+  brute force      exact rational sum of squares, 60-digit decimal sqrt and
+                   quotient on tiny inputs (any dropped term, wrong sign,
+                   index, operand or divisor)
+  unit RMS         gamma = 1, eps = 0 -> mean of y^2 is 1 in every group
+  eps identity     gamma = 1, eps > 0 -> mean of y^2 = ms / (ms + eps)
+  scale (2^k)      eps = 0 -> f(2^k x) == f(x) bit for bit
+  shard identity   shard sums equal the exact shard sums, and add up to the
+                   exact total; the result does not depend on the shard count
+  closed forms     k equal-magnitude nonzeros in a width-n group give
+                   gamma * sign * sqrt(n / k)
+  identities       per-head on one W-wide head == layerwise over W; per-head
+                   == layerwise applied head by head
+  libraries        numpy's and torch's fp64 RMSNorm formulas
+  rounding         fp64 -> bf16 against torch's conversion and exact
+                   rational nearest-even; fp64 -> fp32 against numpy
+  pass-through     V and padding columns come out byte-identical
+"""
+from __future__ import annotations
+
+import math
+from decimal import Decimal, getcontext
+from fractions import Fraction
+
+import numpy as np
+
+import oracle
+from qk_norm_amd import synth
+
+getcontext().prec = 60
+
+F32, BF16 = oracle.F32, oracle.BF16
+
+
+# ------------------------------------------------------------------ helpers --
+
+def _rng_problem(seed, T, ld, dtype, scale=1.0):
+    x = synth.to_dtype(synth.normal(seed, 0, T * ld).reshape(T, ld) * scale, dtype)
+    return x
+
+
+def _gamma(seed, n, dtype, stream=3):
+    return synth.make_gamma(seed, stream, n, dtype)
+
+
+def _exact(v_stored, dtype):
+    """Exact rational values of stored elements."""
+    return [Fraction(float(d)) for d in oracle.decode(np.asarray(v_stored).ravel(), dtype)]
+
+
+def _dec(fr: Fraction) -> Decimal:
+    return Decimal(fr.numerator) / Decimal(fr.denominator)
+
+
+def _exact_group(xs, gs, S: Fraction, n: int, eps: float):
+    """Exact y_j = x_j g_j / sqrt(S/n + eps) to 60 digits (Decimal)."""
+    ms = S / n + Fraction(eps)
+    inv = Decimal(1) / _dec(ms).sqrt()
+    return [_dec(x) * _dec(g) * inv for x, g in zip(xs, gs)]
+
+
+def _ulps(a: float, exact: Decimal) -> float:
+    e = float(exact)
+    if not math.isfinite(a):
+        return math.inf
+    if e == 0.0:
+        return 0.0 if a == 0.0 else math.inf
+    return abs(Decimal(a) - exact) / Decimal(math.ulp(e))
+
+
+def _bf16_value(bits: int) -> Fraction:
+    return Fraction(float(oracle.decode(np.array([bits], dtype=np.uint16), BF16)[0]))
+
+
+def _nearest_bf16(exact: Decimal) -> tuple[int, bool]:
+    """bf16 pattern nearest to an exact value (ties to even); also whether the
+    value lies so close to a rounding midpoint that an fp64 approximation of it
+    may legitimately round either way."""
+    import torch
+    approx = float(exact)
+    b = int(torch.tensor([approx], dtype=torch.float32).to(torch.bfloat16).view(torch.int16)[0]) & 0xFFFF
+    cands = {b, (b + 1) & 0xFFFF, (b - 1) & 0xFFFF}
+    ex = Fraction(exact)
+    best = None
+    for c in cands:
+        if (c & 0x7F80) == 0x7F80:      # inf / nan patterns
+            continue
+        d = abs(_bf16_value(c) - ex)
+        key = (d, c & 1)
+        if best is None or key < best[0]:
+            best = (key, c)
+    c = best[1]
+    # distance to the nearest midpoint, in fp64 ulps of the value
+    near_mid = False
+    for n in ((c + 1) & 0xFFFF, (c - 1) & 0xFFFF):
+        if (n & 0x7F80) == 0x7F80:
+            continue
+        mid = (_bf16_value(c) + _bf16_value(n)) / 2
+        if approx != 0.0 and abs(mid - ex) <= 8 * Fraction(math.ulp(approx)):
+            near_mid = True
+    return c, near_mid
+
+
+# ------------------------------------------------------------- brute force --
+
+def _check_rows_exact(x, y, yr, dtype, groups, eps, label):
+    """groups: list of (row, col0, n, gamma_array, shard_count, divisor)."""
+    for (t, c0, n, g, R, div) in groups:
+        xs = _exact(x[t, c0:c0 + n], dtype)
+        gs = _exact(g[:n], dtype)
+        S = sum((v * v for v in xs), Fraction(0))
+        ex = _exact_group(xs, gs, S, div, eps)
+        for j in range(n):
+            got = float(y[t, c0 + j])
+            u = _ulps(got, ex[j])
+            assert u <= 4, f"{label}: row {t} col {c0 + j}: {got!r} vs exact {ex[j]} ({u} ulp)"
+            if dtype == BF16:
+                want, ambiguous = _nearest_bf16(ex[j])
+                gotb = int(yr[t, c0 + j])
+                assert gotb == want or ambiguous, \
+                    f"{label}: row {t} col {c0 + j}: bf16 {gotb:#06x} vs nearest {want:#06x}"
+            else:
+                want = np.float32(float(ex[j]))
+                assert yr[t, c0 + j] == want or abs(float(yr[t, c0 + j]) - float(want)) <= \
+                    math.ulp(float(want)), f"{label}: fp32 rounding at row {t} col {c0 + j}"
+
+
+def check_brute_force():
+    seed = 100
+    for dtype in (F32, BF16):
+        for D in (1, 2, 4, 8):
+            for (hq, hkv, extra) in ((1, 0, 0), (3, 1, D), (2, 2, 3)):
+                T = 3
+                ld = (hq + hkv) * D + extra
+                seed += 1
+                x = _rng_problem(seed, T, ld, dtype, scale=3.0)
+                gq = _gamma(seed, D, dtype, 3)
+                gk = _gamma(seed, D, dtype, 4)
+                eps = synth.eps_f32(1e-6 if seed % 2 else 0.25)
+                y, yr = oracle.per_head(x, dtype, hq, hkv, D, gq, gk, eps)
+                groups = []
+                for t in range(T):
+                    for h in range(hq):
+                        groups.append((t, h * D, D, gq, 1, D))
+                    for h in range(hkv):
+                        groups.append((t, hq * D + h * D, D, gk, 1, D))
+                _check_rows_exact(x, y, yr, dtype, groups, eps, f"per_head D={D} hq={hq} hkv={hkv}")
+        for (wq, wk, R, extra) in ((16, 8, 1, 0), (32, 16, 4, 5), (64, 32, 8, 32), (24, 0, 3, 1)):
+            T = 2
+            ld = wq + wk + extra
+            seed += 1
+            x = _rng_problem(seed, T, ld, dtype, scale=0.5)
+            gq = _gamma(seed, wq, dtype, 3)
+            gk = _gamma(seed, wk, dtype, 4) if wk else None
+            eps = synth.eps_f32(1e-6)
+            y, yr = oracle.layerwise(x, dtype, wq, wk, gq, gk, eps, nshards=R)
+            groups = []
+            for t in range(T):
+                groups.append((t, 0, wq, gq, R, wq))
+                if wk:
+                    groups.append((t, wq, wk, gk, R, wk))
+            _check_rows_exact(x, y, yr, dtype, groups, eps, f"layerwise wq={wq} wk={wk} R={R}")
+
+
+def check_apply_exact():
+    """Apply with given partials under a tensor-parallel reading: the local
+    slice is normalised with partials of the whole vector and the full-width
+    divisor."""
+    seed = 300
+    for dtype in (F32, BF16):
+        T, W, N = 3, 48, 4          # full width 48 split over 4 "ranks" of 12
+        seed += 1
+        full = _rng_problem(seed, T, W, dtype)
+        g = _gamma(seed, W, dtype)
+        eps = synth.eps_f32(1e-6)
+        sw = W // N
+        # exact partials of each slice, rounded to fp64 (what a rank would send)
+        parts = np.array([[float(sum((v * v for v in _exact(full[t, r * sw:(r + 1) * sw], dtype)),
+                                     Fraction(0))) for t in range(T)] for r in range(N)])
+        for r in range(N):
+            xs = np.ascontiguousarray(full[:, r * sw:(r + 1) * sw])
+            y, yr = oracle.apply(xs, dtype, sw, 0, parts, np.zeros((N, T)), W, 1,
+                                 g[r * sw:(r + 1) * sw], None, eps)
+            for t in range(T):
+                xe = _exact(xs[t], dtype)
+                ge = _exact(g[r * sw:(r + 1) * sw], dtype)
+                S = sum((Fraction(p) for p in parts[:, t]), Fraction(0))
+                ex = _exact_group(xe, ge, S, W, eps)
+                for j in range(sw):
+                    assert _ulps(float(y[t, j]), ex[j]) <= 4, "apply with given partials"
+
+
+# -------------------------------------------------------------- invariants --
+
+def check_unit_rms():
+    for dtype in (F32, BF16):
+        x = _rng_problem(7, 5, 3 * 128 + 64, dtype, scale=4.0)
+        ones = synth.to_dtype(np.ones(128), dtype)
+        y, _ = oracle.per_head(x, dtype, 2, 1, 128, ones, ones, 0.0)
+        for t in range(5):
+            for h in range(3):
+                m = np.mean(y[t, h * 128:(h + 1) * 128] ** 2)
+                assert abs(m - 1.0) <= 1e-14, f"unit RMS per-head: {m!r}"
+        xl = _rng_problem(8, 4, 512 + 256 + 8, dtype)
+        y, _ = oracle.layerwise(xl, dtype, 512, 256, synth.to_dtype(np.ones(512), dtype),
+                                synth.to_dtype(np.ones(256), dtype), 0.0, nshards=8)
+        for t in range(4):
+            for (c0, n) in ((0, 512), (512, 256)):
+                m = np.mean(y[t, c0:c0 + n] ** 2)
+                assert abs(m - 1.0) <= 1e-14, f"unit RMS layerwise: {m!r}"
+
+
+def check_eps_identity():
+    for dtype in (F32, BF16):
+        x = _rng_problem(9, 4, 2 * 64, dtype, scale=0.01)
+        ones = synth.to_dtype(np.ones(64), dtype)
+        eps = synth.eps_f32(1e-4)
+        y, _ = oracle.per_head(x, dtype, 1, 1, 64, ones, ones, eps)
+        xd = oracle.decode(x, dtype)
+        for t in range(4):
+            for h in range(2):
+                seg = xd[t, h * 64:(h + 1) * 64]
+                ms = math.fsum(float(v) * float(v) for v in seg) / 64
+                want = ms / (ms + eps)
+                got = np.mean(y[t, h * 64:(h + 1) * 64] ** 2)
+                assert abs(got - want) <= 1e-13 * want, f"eps identity: {got!r} vs {want!r}"
+
+
+def check_scale_pow2():
+    for dtype in (F32, BF16):
+        x = _rng_problem(10, 3, 3 * 32, dtype)
+        gq, gk = _gamma(10, 32, dtype, 3), _gamma(10, 32, dtype, 4)
+        xd = oracle.decode(x, dtype)
+        y0, _ = oracle.per_head(x, dtype, 2, 1, 32, gq, gk, 0.0)
+        l0, _ = oracle.layerwise(x, dtype, 64, 32, _gamma(10, 64, dtype), gk, 0.0, nshards=4)
+        for k in (-7, -1, 3, 12):
+            xs = synth.to_dtype(xd * 2.0 ** k, dtype)
+            assert np.array_equal(oracle.decode(xs, dtype), xd * 2.0 ** k)
+            y1, _ = oracle.per_head(xs, dtype, 2, 1, 32, gq, gk, 0.0)
+            assert np.array_equal(y0, y1), f"per-head scale invariance 2^{k}"
+            l1, _ = oracle.layerwise(xs, dtype, 64, 32, _gamma(10, 64, dtype), gk, 0.0, nshards=4)
+            assert np.array_equal(l0, l1), f"layerwise scale invariance 2^{k}"
+        # with eps > 0 the change is first order in eps: |f(cx) - f(x)| ~ |f| eps |c^-2 - 1| / (2 ms)
+        eps = synth.eps_f32(1e-3)
+        c = 0.25
+        ya, _ = oracle.per_head(x, dtype, 2, 1, 32, gq, gk, eps)
+        yb, _ = oracle.per_head(synth.to_dtype(xd * c, dtype), dtype, 2, 1, 32, gq, gk, eps)
+        for t in range(3):
+            for h in range(3):
+                seg = xd[t, h * 32:(h + 1) * 32]
+                ms = float(np.mean(seg ** 2))
+                bound = abs(c ** -2 - 1) * eps / (2 * ms) * 1.5 + 1e-15
+                a = ya[t, h * 32:(h + 1) * 32]
+                b = yb[t, h * 32:(h + 1) * 32]
+                assert np.all(np.abs(a - b) <= bound * np.abs(a) + 1e-300), "eps scale bound"
+                assert np.all(np.abs(b) < np.abs(a)), "scaling down with eps > 0 must shrink |y|"
+
+
+def check_shard_identity():
+    for dtype in (F32, BF16):
+        for (wq, wk, R) in ((256, 64, 8), (96, 48, 3), (64, 64, 1)):
+            T = 3
+            x = _rng_problem(11 + R, T, wq + wk + 16, dtype, scale=5.0)
+            pq, pk = oracle.partials(x, dtype, wq, wk, R)
+            assert pq.shape == (R, T) and pk.shape == (R, T)
+            for t in range(T):
+                for (c0, w, parts) in ((0, wq, pq), (wq, wk, pk)):
+                    sw = w // R
+                    total = Fraction(0)
+                    for r in range(R):
+                        ex = sum((v * v for v in _exact(x[t, c0 + r * sw:c0 + (r + 1) * sw], dtype)),
+                                 Fraction(0))
+                        total += ex
+                        got = Fraction(float(parts[r, t]))
+                        assert abs(got - ex) <= ex * Fraction(sw, 2 ** 53), \
+                            f"shard {r} of row {t}: {float(got)} vs {float(ex)}"
+                    summed = math.fsum(float(p) for p in parts[:, t])
+                    assert abs(Fraction(summed) - total) <= total * Fraction(w + R, 2 ** 53), \
+                        "sum of shard partials vs exact total"
+            g = _gamma(12, wq, dtype)
+            gk = _gamma(12, wk, dtype, 4)
+            a, _ = oracle.layerwise(x, dtype, wq, wk, g, gk, 1e-6, nshards=R)
+            b, _ = oracle.layerwise(x, dtype, wq, wk, g, gk, 1e-6, nshards=1)
+            assert np.all(np.abs(a - b) <= 1e-14 * np.abs(b) + 1e-300), "result vs shard count"
+
+
+def check_closed_form():
+    """k nonzeros of magnitude a in a width-n group, eps = 0: y = g sign(x) sqrt(n/k)."""
+    cases = [(128, 2, 8.0), (128, 8, 4.0), (128, 32, 2.0), (128, 128, 1.0),
+             (4096, 1, 64.0), (4096, 4, 32.0), (4096, 16, 16.0), (1024, 1, 32.0),
+             (8192, 2, 64.0), (8192, 8, 32.0)]
+    for dtype in (F32, BF16):
+        for (n, k, root) in cases:
+            for a in (1.0, 0.375, 3.0, 2.0 ** -20):
+                x = np.zeros((1, n))
+                idx = np.arange(0, n, n // k)[:k]
+                x[0, idx] = a * np.where(np.arange(k) % 2 == 0, 1.0, -1.0)
+                xs = synth.to_dtype(x, dtype)
+                g = _gamma(n + k, n, dtype)
+                gd = oracle.decode(g, dtype)
+                if n <= 128:
+                    y, yr = oracle.per_head(xs, dtype, 1, 0, n, g, None, 0.0)
+                else:
+                    y, yr = oracle.layerwise(xs, dtype, n, 0, g, None, 0.0, nshards=8)
+                want = np.zeros(n)
+                want[idx] = gd[idx] * np.sign(x[0, idx]) * root
+                if a == 1.0 or a == 2.0 ** -20:
+                    assert np.array_equal(y[0], want), f"closed form exact n={n} k={k} a={a}"
+                else:
+                    assert np.all(np.abs(y[0] - want) <= 4 * np.spacing(np.abs(want))), \
+                        f"closed form n={n} k={k} a={a}"
+                assert np.array_equal(yr[0], synth.to_dtype(want, dtype)), \
+                    f"closed form rounded n={n} k={k} a={a}"
+    # width-1 group: y = g x / sqrt(x^2 + eps); with eps = 0 just g * sign(x)
+    for dtype in (F32, BF16):
+        x = synth.to_dtype(np.array([[3.0, -0.5, 1e-3]]), dtype)
+        g = synth.to_dtype(np.array([1.25]), dtype)
+        y, _ = oracle.per_head(x, dtype, 3, 0, 1, g, None, 0.0)
+        assert np.array_equal(y[0], 1.25 * np.sign(oracle.decode(x, dtype)[0]))
+        eps = 0.5
+        y, _ = oracle.per_head(x, dtype, 3, 0, 1, g, None, eps)
+        xd = oracle.decode(x, dtype)[0]
+        want = 1.25 * xd / np.sqrt(xd * xd + eps)
+        assert np.all(np.abs(y[0] - want) <= 2 * np.spacing(np.abs(want)))
+
+
+def check_identities():
+    for dtype in (F32, BF16):
+        T, W = 4, 256
+        x = _rng_problem(13, T, W + 40, dtype)
+        g = _gamma(13, W, dtype)
+        a, ar = oracle.per_head(x, dtype, 1, 0, W, g, None, 1e-6)
+        b, br = oracle.layerwise(x, dtype, W, 0, g, None, 1e-6, nshards=1)
+        assert np.array_equal(a, b) and np.array_equal(ar, br), "per-head on one head == layerwise"
+        # per-head == layerwise on each head slice
+        H, D = 6, 64
+        x = _rng_problem(14, T, H * D, dtype)
+        g = _gamma(14, D, dtype)
+        a, _ = oracle.per_head(x, dtype, H, 0, D, g, None, 1e-6)
+        flat = x.reshape(T * H, D)
+        b, _ = oracle.layerwise(flat, dtype, D, 0, g, None, 1e-6, nshards=2)
+        assert np.all(np.abs(a.reshape(T * H, D) - b) <= 1e-14 * np.abs(b) + 1e-300)
+        # K heads use gamma_k and start at column hq*D
+        hq, hkv = 3, 2
+        x = _rng_problem(15, T, (hq + 2 * hkv) * D, dtype)
+        gq, gk = _gamma(15, D, dtype, 3), _gamma(15, D, dtype, 4)
+        a, _ = oracle.per_head(x, dtype, hq, hkv, D, gq, gk, 1e-6)
+        kk = np.ascontiguousarray(x[:, hq * D:(hq + hkv) * D])
+        b, _ = oracle.per_head(kk, dtype, hkv, 0, D, gk, None, 1e-6)
+        assert np.array_equal(a[:, hq * D:(hq + hkv) * D], b), "K heads"
+
+
+def check_libraries():
+    import torch
+    for dtype in (F32, BF16):
+        T, H, D = 6, 5, 128
+        x = _rng_problem(16, T, H * D, dtype, scale=2.0)
+        g = _gamma(16, D, dtype)
+        eps = synth.eps_f32(1e-6)
+        y, _ = oracle.per_head(x, dtype, H, 0, D, g, None, eps)
+        xd = oracle.decode(x, dtype).reshape(T, H, D)
+        gd = oracle.decode(g, dtype)
+        ref = xd / np.sqrt(np.mean(xd ** 2, axis=-1, keepdims=True) + eps) * gd
+        assert np.all(np.abs(y.reshape(T, H, D) - ref) <= 1e-14 * np.abs(ref) + 1e-300), "numpy"
+        tref = torch.nn.functional.rms_norm(torch.from_numpy(xd), (D,), torch.from_numpy(gd),
+                                            eps=eps).numpy()
+        assert np.all(np.abs(y.reshape(T, H, D) - tref) <= 1e-14 * np.abs(tref) + 1e-300), "torch"
+        # layerwise against torch over the whole Q and the whole K width
+        wq, wk = 512, 128
+        x = _rng_problem(17, T, wq + wk + 128, dtype)
+        gq, gk = _gamma(17, wq, dtype), _gamma(17, wk, dtype, 4)
+        y, _ = oracle.layerwise(x, dtype, wq, wk, gq, gk, eps, nshards=8)
+        xd = oracle.decode(x, dtype)
+        for (c0, w, gg) in ((0, wq, gq), (wq, wk, gk)):
+            tref = torch.nn.functional.rms_norm(torch.from_numpy(xd[:, c0:c0 + w].copy()), (w,),
+                                                torch.from_numpy(oracle.decode(gg, dtype)),
+                                                eps=eps).numpy()
+            assert np.all(np.abs(y[:, c0:c0 + w] - tref) <= 1e-14 * np.abs(tref) + 1e-300)
+
+
+def check_rounding():
+    import torch
+    # every bf16 pattern is a fixed point
+    allb = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    vals = oracle.decode(allb, BF16)
+    finite = np.isfinite(vals)
+    r = oracle.round_to(vals[finite], BF16)
+    zero_or_same = (r == allb[finite])
+    assert zero_or_same.all(), "bf16 patterns must round to themselves"
+    # midpoints between neighbours (exact in fp32): ties go to the even pattern
+    pos = allb[(allb < 0x7F7F)]
+    lo = oracle.decode(pos, BF16)
+    hi = oracle.decode((pos + 1).astype(np.uint16), BF16)
+    mid = (lo + hi) / 2
+    got = oracle.round_to(mid, BF16)
+    tor = torch.from_numpy(mid).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(got, tor), "midpoints vs torch"
+    want_even = np.where(pos % 2 == 0, pos, pos + 1).astype(np.uint16)
+    assert np.array_equal(got, want_even), "ties to even"
+    # just off the midpoints (by far less than an fp32 spacing): direct rounding
+    up = np.nextafter(mid, np.inf)
+    dn = np.nextafter(mid, -np.inf)
+    assert np.array_equal(oracle.round_to(up, BF16), (pos + 1).astype(np.uint16)), "above midpoint"
+    assert np.array_equal(oracle.round_to(dn, BF16), pos), "below midpoint"
+    assert np.array_equal(oracle.round_to(-up, BF16), ((pos + 1) | 0x8000).astype(np.uint16))
+    # random values that are exact in fp32 (torch converts through fp32)
+    v = synth.normal(77, 0, 200000) * np.exp(synth.normal(78, 0, 200000) * 8)
+    v32 = v.astype(np.float32).astype(np.float64)
+    tor = torch.from_numpy(v32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(oracle.round_to(v32, BF16), tor), "random fp32-exact values vs torch"
+    # fp32 output rounding is numpy's cast
+    assert np.array_equal(oracle.round_to(v, F32), v.astype(np.float32)), "fp32 rounding"
+    # signed zeros and overflow
+    assert list(oracle.round_to(np.array([0.0, -0.0, 1e39, -1e39]), BF16)) == [0, 0x8000, 0x7F80, 0xFF80]
+
+
+def check_pass_through():
+    for dtype in (F32, BF16):
+        hq, hkv, D, pad = 4, 2, 64, 24
+        ld = (hq + 2 * hkv) * D + pad
+        x = _rng_problem(18, 5, ld, dtype)
+        gq, gk = _gamma(18, D, dtype, 3), _gamma(18, D, dtype, 4)
+        y, yr = oracle.per_head(x, dtype, hq, hkv, D, gq, gk, 1e-6)
+        c = (hq + hkv) * D
+        assert np.array_equal(yr[:, c:].view(np.uint8), np.ascontiguousarray(x[:, c:]).view(np.uint8))
+        assert np.array_equal(y[:, c:], oracle.decode(x[:, c:], dtype))
+        assert not np.array_equal(yr[:, :c], x[:, :c])
+        y, yr = oracle.layerwise(x, dtype, hq * D, hkv * D, _gamma(18, hq * D, dtype),
+                                 _gamma(18, hkv * D, dtype, 4), 1e-6, nshards=2)
+        assert np.array_equal(yr[:, c:].view(np.uint8), np.ascontiguousarray(x[:, c:]).view(np.uint8))
+
+
+ALL_CHECKS = [check_brute_force, check_apply_exact, check_unit_rms, check_eps_identity,
+              check_scale_pow2, check_shard_identity, check_closed_form, check_identities,
+              check_libraries, check_rounding, check_pass_through]
