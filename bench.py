@@ -1,0 +1,344 @@
+"""QK-Norm bench on one MI355X.
+
+Default workload (the headline metric): per-head QK-Norm, standalone
+[T=4096, H=48, D=128] bf16, in place.  One step = one qknorm_per_head call over
+one such batch; the batches rotate through a pool of >= 1 GiB of identical
+copies so that no step finds its rows in the 256 MB Infinity Cache.
+
+Reported (one JSON line):
+  value          whole-job throughput, algorithmic GB/s (each Q/K element read
+                 once and written once, plus gamma once) over the timed steps
+  ms_per_step    host wall time per step between synchronisations
+  roofline       per-launch kernel time from HIP events recorded around every
+                 launch in the timed region, algorithmic bytes / that time,
+                 against MI355X's 8 TB/s HBM peak; traffic from the committed
+                 rocprofv3 counter summary when it matches the current source
+  cpu_baseline   the fp64 CPU oracle on the same input, on the host's cores
+  cases          the T=32768 large-prefill case (layerwise fused, two-phase,
+                 per-head), fused GQA T=8192, and decode-size launch floors
+
+Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--quick] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "QK-Norm µs/call + achieved HBM GB/s (% of peak), 4096 tok×48 heads×128 bf16"
+HBM_PEAK_GBS = 8000.0
+POOL_BYTES = 1 << 30
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "per_head_bf16_T4096_H48_D128.pmc.md")
+KERNEL_SOURCES = [os.path.join(ROOT, "qk_norm_amd", "csrc", f) for f in
+                  ("qknorm_kernels.hip", "qknorm_device.hpp", "qknorm_api.hip", "qknorm_launch.hpp")]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(bytes_alg: float):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or None
+    if there is none or it was taken on other kernel sources."""
+    if not os.path.exists(PMC_SUMMARY):
+        return None
+    text = open(PMC_SUMMARY).read()
+    kv = dict(re.findall(r"^- (\w+): ([^\s]+)", text, flags=re.M))
+    try:
+        if kv.get("source_sha256") != source_hash():
+            return None
+        return float(kv["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+# ----------------------------------------------------------------- devices --
+
+def to_device(a, dtype, torch, dev):
+    import numpy as np
+    from qk_norm_amd import synth
+    if dtype == synth.F32:
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+
+class Timer:
+    """Per-launch HIP events on the launch stream plus host wall time."""
+
+    def __init__(self, torch, n):
+        self.torch = torch
+        self.ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(n)]
+
+    def run(self, steps, launch):
+        torch = self.torch
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            s, e = self.ev[i]
+            s.record()
+            launch(i)
+            e.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        per = sorted(s.elapsed_time(e) * 1e3 for s, e in self.ev[:steps])  # us
+        return wall, per
+
+
+def stats(per_us):
+    n = len(per_us)
+    return {"mean_us": sum(per_us) / n, "p10_us": per_us[int(0.1 * (n - 1))],
+            "p50_us": per_us[(n - 1) // 2], "p90_us": per_us[int(0.9 * (n - 1))]}
+
+
+def pool_count(buf_bytes: int, min_copies=2) -> int:
+    return max(min_copies, math.ceil(POOL_BYTES / buf_bytes))
+
+
+# ------------------------------------------------------------------- cases --
+
+def bench_per_head(q, torch, dev, p, steps, warmup, label):
+    lib = q.load()
+    n = pool_count(p.T * p.ld * 2)
+    base = to_device(p.x, p.dtype, torch, dev)
+    pool = [base.clone() for _ in range(n)]
+    del base
+    gq = to_device(p.gamma_q, p.dtype, torch, dev)
+    gk = to_device(p.gamma_k, p.dtype, torch, dev) if p.gamma_k is not None else None
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    args = [(t.data_ptr(), p.T, p.ld, p.hq, p.hkv, p.head_dim, gq.data_ptr(),
+             gk.data_ptr() if gk is not None else None, p.eps, p.dtype, stream) for t in pool]
+
+    def launch(i):
+        rc = lib.qknorm_per_head(*args[i % n])
+        if rc:
+            raise RuntimeError(f"qknorm_per_head: {q.strerror(rc)}")
+
+    for i in range(warmup):
+        launch(i)
+    timer = Timer(torch, steps)
+    wall, per = timer.run(steps, launch)
+    bytes_alg = 2 * p.T * (p.wq + p.wk) * 2 + (p.head_dim * 2) * (1 + (p.hkv > 0))
+    st = stats(per)
+    del pool
+    torch.cuda.empty_cache()
+    log(f"{label}: {st['mean_us']:.2f} us/launch, {bytes_alg / st['mean_us'] / 1e3:.0f} GB/s")
+    return {"label": label, "bytes": bytes_alg, "wall_s": wall, "steps": steps, "pool": n, **st,
+            "gbs": bytes_alg / (st["mean_us"] * 1e-6) / 1e9}
+
+
+def bench_layerwise(q, torch, dev, p, steps, warmup):
+    lib = q.load()
+    n = pool_count(p.T * p.ld * 2)
+    base = to_device(p.x, p.dtype, torch, dev)
+    pool = [base.clone() for _ in range(n)]
+    del base
+    gq = to_device(p.gamma_q, p.dtype, torch, dev)
+    gk = to_device(p.gamma_k, p.dtype, torch, dev)
+    pq = torch.empty(p.nshards, p.T, dtype=torch.float32, device=dev)
+    pk = torch.empty(p.nshards, p.T, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    R = p.nshards
+
+    def fused(i):
+        t = pool[i % n]
+        rc = lib.qknorm_layerwise(t.data_ptr(), p.T, p.ld, p.wq, p.wk, gq.data_ptr(), gk.data_ptr(),
+                                  p.eps, R, p.dtype, stream)
+        if rc:
+            raise RuntimeError(q.strerror(rc))
+
+    def partial(i):
+        t = pool[i % n]
+        rc = lib.qknorm_partial_sumsq(t.data_ptr(), p.T, p.ld, p.wq, p.wk, R, pq.data_ptr(),
+                                      pk.data_ptr(), p.dtype, stream)
+        if rc:
+            raise RuntimeError(q.strerror(rc))
+
+    def apply(i):
+        t = pool[i % n]
+        rc = lib.qknorm_apply_scalar(t.data_ptr(), p.T, p.ld, p.wq, p.wk, pq.data_ptr(),
+                                     pk.data_ptr(), R, p.wq, p.wk, gq.data_ptr(), gk.data_ptr(),
+                                     p.eps, p.dtype, stream)
+        if rc:
+            raise RuntimeError(q.strerror(rc))
+
+    qk_bytes = p.T * (p.wq + p.wk) * 2
+    g_bytes = (p.wq + p.wk) * 2
+    out = {}
+    for name, fn, nbytes in (("layerwise_fused", fused, 2 * qk_bytes + g_bytes),
+                             ("partial_sumsq", partial, qk_bytes + 2 * R * p.T * 4),
+                             ("apply_scalar", apply, 2 * qk_bytes + g_bytes + 2 * R * p.T * 4)):
+        for i in range(warmup):
+            fn(i)
+        wall, per = Timer(torch, steps).run(steps, fn)
+        st = stats(per)
+        out[name] = {"bytes": nbytes, **st, "gbs": nbytes / (st["mean_us"] * 1e-6) / 1e9}
+        log(f"cfg5 {name}: {st['mean_us']:.2f} us/launch, {out[name]['gbs']:.0f} GB/s")
+    two = out["partial_sumsq"]["mean_us"] + out["apply_scalar"]["mean_us"]
+    out["two_phase_total"] = {"mean_us": two, "bytes": 3 * qk_bytes + g_bytes + 4 * R * p.T * 4,
+                              "gbs_vs_fused_alg_bytes": (2 * qk_bytes + g_bytes) / (two * 1e-6) / 1e9}
+    del pool
+    torch.cuda.empty_cache()
+    return out
+
+
+def bench_decode_floor(q, torch, dev, T, H, reps=200):
+    """Per-launch time of a tiny per-head call: eager (events) and hipGraph replay."""
+    from qk_norm_amd import synth
+    p = synth.cfg2(T=T, H=H)
+    x = to_device(p.x, p.dtype, torch, dev)
+    g = to_device(p.gamma_q, p.dtype, torch, dev)
+
+    def launch(_i=0):
+        q.qknorm_per_head(x, H, 0, 128, g, None, p.eps)
+
+    for _ in range(20):
+        launch()
+    _, per = Timer(torch, reps).run(reps, launch)
+    st = stats(per)
+    # graph of 100 launches: per-launch floor without host overhead
+    graph = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(graph, stream=s):
+            for _ in range(100):
+                launch()
+    torch.cuda.synchronize()
+    graph.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    floor = e0.elapsed_time(e1) * 1e3 / 500
+    return {"T": T, "H": H, "event_p50_us": st["p50_us"], "graph_per_launch_us": floor}
+
+
+def cpu_baseline(p, budget_s=10.0):
+    import oracle
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.per_head(p.x, p.dtype, p.hq, p.hkv, p.head_dim, p.gamma_q, p.gamma_k, p.eps)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or el / n * (n + 1) > 3 * budget_s:
+            break
+    bytes_alg = 2 * p.T * (p.wq + p.wk) * 2 + p.head_dim * 2
+    return {"value": bytes_alg * n / el / 1e9, "unit": "GB/s", "cores": oracle.max_threads(),
+            "kind": "oracle",
+            "sample": f"{n} full call(s) of the fp64 C oracle on the same [4096,48,128] bf16 input "
+                      f"({el:.1f} s)", "us_per_call": el / n * 1e6}
+
+
+# -------------------------------------------------------------------- main --
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--quick", action="store_true", help="headline case only")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--case", default="headline",
+                    choices=["headline", "cfg5_layerwise", "cfg5_per_head", "copy"],
+                    help="single case for profiling runs")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: this QK-Norm build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    import qk_norm_amd as q
+    from qk_norm_amd import synth
+    q.load()
+    dev = torch.device("cuda:0")
+
+    if args.case == "copy":
+        # plain device copy of known size, for scaling the FETCH/WRITE counters
+        n = 256 << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(10):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"case": "copy", "bytes_read": n, "bytes_written": n}))
+        return
+    if args.case == "cfg5_layerwise":
+        p = synth.cfg5(T=32768)
+        print(json.dumps({"case": "cfg5_layerwise", **bench_layerwise(q, torch, dev, p, args.steps, args.warmup)}))
+        return
+    if args.case == "cfg5_per_head":
+        p = synth.cfg5(T=32768, mode="per_head")
+        print(json.dumps({"case": "cfg5_per_head",
+                          **bench_per_head(q, torch, dev, p, args.steps, args.warmup, "cfg5 per-head")}))
+        return
+
+    t_start = time.perf_counter()
+    p = synth.cfg2(T=4096, H=48)
+    head = bench_per_head(q, torch, dev, p, args.steps, args.warmup, "headline per-head")
+    bytes_alg = head["bytes"]
+    value = bytes_alg * args.steps / head["wall_s"] / 1e9
+    achieved = head["gbs"]
+    result = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(head["wall_s"] / args.steps * 1e3, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "io_dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "per-head QK-Norm, standalone [T=4096, H=48, D=128] bf16, in place",
+                   "T": 4096, "H": 48, "head_dim": 128, "eps": 1e-6, "seed": p.seed,
+                   "rotating_pool_copies": head["pool"]},
+        "us_per_call": round(head["mean_us"], 3),
+        "us_per_call_p10_p50_p90": [round(head["p10_us"], 3), round(head["p50_us"], 3), round(head["p90_us"], 3)],
+        "pct_of_hbm_peak": round(100 * achieved / HBM_PEAK_GBS, 2),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": read_traffic(bytes_alg),
+                     "kernel": "per_head_kernel<bf16, 16 lanes/head>",
+                     "bytes_per_launch": bytes_alg},
+    }
+    if not args.quick:
+        cases = {}
+        p5 = synth.cfg5(T=32768)
+        cases["cfg5_T32768_layerwise"] = bench_layerwise(q, torch, dev, p5, 50, 5)
+        p5h = synth.cfg5(T=32768, mode="per_head")
+        del p5
+        c = bench_per_head(q, torch, dev, p5h, 50, 5, "cfg5 per-head")
+        cases["cfg5_T32768_per_head"] = {k: c[k] for k in ("bytes", "mean_us", "p50_us", "gbs")}
+        del p5h
+        c = bench_per_head(q, torch, dev, synth.cfg3(T=8192), 100, 10, "cfg3 fused GQA T=8192")
+        cases["cfg3_T8192_per_head"] = {k: c[k] for k in ("bytes", "mean_us", "p50_us", "gbs")}
+        cases["decode_floor"] = [bench_decode_floor(q, torch, dev, T, 48) for T in (1, 16, 128)]
+        result["cases"] = cases
+    if not args.no_cpu:
+        result["cpu_baseline"] = cpu_baseline(p)
+    result["bench_wall_s"] = round(time.perf_counter() - t_start, 1)
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()

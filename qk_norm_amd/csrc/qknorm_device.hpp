@@ -1,0 +1,130 @@
+// Device-side building blocks for the gfx950 QK-Norm kernels.
+//
+// Everything here works on 16-byte vectors (one global_load_dwordx4 /
+// global_store_dwordx4 per lane): 8 bf16 or 4 fp32 values.  Sums of squares
+// are fp32; cross-lane reduction uses DPP row operations inside 16-lane rows
+// and the gfx950 permlane swaps across rows, so no LDS is touched.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qknorm {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+enum : int { kF32 = 0, kBF16 = 1 };
+
+template <int DT> struct IoTraits;
+template <> struct IoTraits<kF32> {
+  static constexpr int kElems = 4;   // values per 16-byte vector
+  static constexpr int kBytes = 4;
+};
+template <> struct IoTraits<kBF16> {
+  static constexpr int kElems = 8;
+  static constexpr int kBytes = 2;
+};
+
+// ----------------------------------------------------------------- memory --
+
+template <bool NT>
+__device__ __forceinline__ u32x4 load16(const void* p) {
+  if constexpr (NT)
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  else
+    return *reinterpret_cast<const u32x4*>(p);
+}
+
+template <bool NT>
+__device__ __forceinline__ void store16(void* p, u32x4 v) {
+  if constexpr (NT)
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+  else
+    *reinterpret_cast<u32x4*>(p) = v;
+}
+
+// ------------------------------------------------------------ conversions --
+
+// Widen one 16-byte vector to fp32 (exact for both dtypes).
+template <int DT>
+__device__ __forceinline__ void unpack(u32x4 v, float (&f)[IoTraits<DT>::kElems]) {
+  if constexpr (DT == kBF16) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = __uint_as_float(v[i] << 16);
+      f[2 * i + 1] = __uint_as_float(v[i] & 0xFFFF0000u);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) f[i] = __uint_as_float(v[i]);
+  }
+}
+
+// Round fp32 to the I/O dtype (bf16: v_cvt_pk_bf16_f32, nearest-even) and pack.
+template <int DT>
+__device__ __forceinline__ u32x4 pack(const float (&f)[IoTraits<DT>::kElems]) {
+  u32x4 v;
+  if constexpr (DT == kBF16) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      bf16x2 h = {(__bf16)f[2 * i], (__bf16)f[2 * i + 1]};
+      v[i] = __builtin_bit_cast(uint32_t, h);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = __float_as_uint(f[i]);
+  }
+  return v;
+}
+
+// Sum of squares of one vector, left to right, one fused multiply-add each.
+template <int DT>
+__device__ __forceinline__ float vec_sumsq(const float (&f)[IoTraits<DT>::kElems], float acc) {
+#pragma unroll
+  for (int i = 0; i < IoTraits<DT>::kElems; ++i) acc = __builtin_fmaf(f[i], f[i], acc);
+  return acc;
+}
+
+// ---------------------------------------------------------- lane reduction --
+//
+// Each stage adds a lane's value to a partner's; fp32 addition commutes, so
+// both partners hold the same bits afterwards and, after the last stage,
+// every lane of the group holds the identical total.
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_add(float v) {
+  return v + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                           0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over aligned groups of LANES consecutive lanes (LANES in 2..64).
+template <int LANES>
+__device__ __forceinline__ float group_sum(float v) {
+  static_assert(LANES == 2 || LANES == 4 || LANES == 8 || LANES == 16 || LANES == 32 ||
+                    LANES == 64, "group must be a power of two up to the wave");
+  v = dpp_add<0xB1>(v);                       // quad_perm [1,0,3,2]: pairs
+  if constexpr (LANES >= 4) v = dpp_add<0x4E>(v);   // quad_perm [2,3,0,1]: quads
+  if constexpr (LANES >= 8) v = dpp_add<0x141>(v);  // row_half_mirror: half-rows of 8
+  if constexpr (LANES >= 16) v = dpp_add<0x140>(v); // row_mirror: rows of 16
+  if constexpr (LANES >= 32) {
+    // v_permlane16_swap: with both operands v, the two results hold the even
+    // and the odd 16-lane row of each 32-lane half, so their sum is the
+    // 32-lane total in every lane.
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+  if constexpr (LANES >= 64) {
+    // v_permlane32_swap: the two results hold the low and the high half.
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+  return v;
+}
+
+// 1 / sqrt(ms + eps) with v_rsq_f32 (about 1 ulp).
+__device__ __forceinline__ float rms_scale(float sumsq, float width, float eps) {
+  return __builtin_amdgcn_rsqf(sumsq / width + eps);
+}
+
+}  // namespace qknorm

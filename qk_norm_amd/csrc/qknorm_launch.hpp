@@ -1,0 +1,57 @@
+// Internal interface between the C-ABI front end and the kernel launchers.
+// Arguments reaching these functions have already been validated on the host.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qknorm {
+
+struct PerHeadArgs {
+  void* qkv;
+  int64_t T, ld;
+  int32_t hq, hkv, head_dim;
+  const void* gamma_q;
+  const void* gamma_k;
+  float eps;
+  int32_t dtype;
+};
+
+struct LayerwiseArgs {
+  void* qkv;
+  int64_t T, ld, wq, wk;
+  const void* gamma_q;
+  const void* gamma_k;
+  float eps;
+  int32_t nshards, dtype;
+};
+
+struct PartialArgs {
+  const void* qkv;
+  int64_t T, ld, wq, wk;
+  int32_t nshards;
+  float* part_q;
+  float* part_k;
+  int32_t dtype;
+};
+
+struct ApplyArgs {
+  void* qkv;
+  int64_t T, ld, wq, wk;
+  const float* part_q;
+  const float* part_k;
+  int32_t nparts;
+  int64_t norm_wq, norm_wk;
+  const void* gamma_q;
+  const void* gamma_k;
+  float eps;
+  int32_t dtype;
+};
+
+// `cus` is the compute-unit count of the current device (grid sizing).
+hipError_t launch_per_head(const PerHeadArgs& a, hipStream_t s, int cus);
+hipError_t launch_layerwise(const LayerwiseArgs& a, hipStream_t s, int cus);
+hipError_t launch_partial_sumsq(const PartialArgs& a, hipStream_t s, int cus);
+hipError_t launch_apply_scalar(const ApplyArgs& a, hipStream_t s, int cus);
+
+}  // namespace qknorm

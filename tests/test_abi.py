@@ -1,0 +1,174 @@
+"""The C-ABI library on the host: it loads, exports what the header declares,
+and rejects bad arguments before any HIP call (CPU only, no kernel runs)."""
+import ctypes
+import math
+import os
+import re
+import subprocess
+
+import pytest
+
+import qk_norm_amd as q
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qknorm.h")
+
+A16 = 0x10000          # a fake, 16-byte aligned "device" address (never dereferenced)
+BF16, F32 = q.QKNORM_BF16, q.QKNORM_F32
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(qknorm_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return q.load()
+
+
+def test_header_declares_the_entry_points():
+    assert _declared() == sorted(q.EXPORTED)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in _declared():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", q.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    syms = {l.split()[-1] for l in out.splitlines() if l.strip()}
+    for name in _declared():
+        assert name in syms, f"{name} not exported with C linkage"
+
+
+def test_header_constants_match_binding():
+    text = open(HEADER).read()
+    consts = dict(re.findall(r"#define\s+(QKNORM_[A-Z0-9_]+)\s+(-?\d+)", text))
+    for k, v in consts.items():
+        if hasattr(q, k):
+            assert getattr(q, k) == int(v), k
+
+
+def test_abi_version_and_strerror(lib):
+    assert q.abi_version() == 1
+    for code in range(-8, 1):
+        s = q.strerror(code)
+        assert isinstance(s, str) and s
+    assert q.strerror(0) == "success"
+    assert "unknown" in q.strerror(12345)
+
+
+def test_gfx950_code_object_in_library():
+    data = open(q.LIB_PATH, "rb").read()
+    assert b"gfx950" in data
+
+
+# ------------------------------------------------------------- validation --
+
+def ph(lib, qkv=A16, T=4, ld=3072, hq=16, hkv=4, D=128, gq=A16, gk=A16, eps=1e-6, dt=F32):
+    return lib.qknorm_per_head(qkv, T, ld, hq, hkv, D, gq, gk, eps, dt, None)
+
+
+def lw(lib, qkv=A16, T=4, ld=6144, wq=4096, wk=1024, gq=A16, gk=A16, eps=1e-6, R=8, dt=BF16):
+    return lib.qknorm_layerwise(qkv, T, ld, wq, wk, gq, gk, eps, R, dt, None)
+
+
+def ps(lib, qkv=A16, T=4, ld=6144, wq=4096, wk=1024, R=8, pq=A16, pk=A16, dt=BF16):
+    return lib.qknorm_partial_sumsq(qkv, T, ld, wq, wk, R, pq, pk, dt, None)
+
+
+def ap(lib, qkv=A16, T=4, ld=6144, wq=4096, wk=1024, pq=A16, pk=A16, n=8, nwq=4096, nwk=1024,
+       gq=A16, gk=A16, eps=1e-6, dt=BF16):
+    return lib.qknorm_apply_scalar(qkv, T, ld, wq, wk, pq, pk, n, nwq, nwk, gq, gk, eps, dt, None)
+
+
+@pytest.mark.parametrize("call", [ph, lw, ps, ap], ids=["per_head", "layerwise", "partial", "apply"])
+def test_bad_dtype(lib, call):
+    assert call(lib, dt=2) == q.QKNORM_E_DTYPE
+    assert call(lib, dt=-1) == q.QKNORM_E_DTYPE
+
+
+@pytest.mark.parametrize("call", [ph, lw, ap], ids=["per_head", "layerwise", "apply"])
+@pytest.mark.parametrize("eps", [-1e-6, math.nan, math.inf, -math.inf])
+def test_bad_eps(lib, call, eps):
+    assert call(lib, eps=eps) == q.QKNORM_E_EPS
+
+
+def test_zero_eps_is_valid_and_T0_is_a_noop(lib):
+    # T == 0: everything valid, nothing launched, no HIP call made
+    assert ph(lib, T=0, eps=0.0) == q.QKNORM_OK
+    assert lw(lib, T=0) == q.QKNORM_OK
+    assert ps(lib, T=0) == q.QKNORM_OK
+    assert ap(lib, T=0) == q.QKNORM_OK
+    # and with NULL buffers, since nothing would be touched
+    assert ph(lib, qkv=None, T=0, gq=None, gk=None) == q.QKNORM_OK
+    assert lw(lib, qkv=None, T=0, gq=None, gk=None) == q.QKNORM_OK
+    assert ps(lib, qkv=None, T=0, pq=None, pk=None) == q.QKNORM_OK
+    assert ap(lib, qkv=None, T=0, pq=None, pk=None, gq=None, gk=None) == q.QKNORM_OK
+    # empty widths are no-ops too
+    assert ph(lib, hq=0, hkv=0, gq=None, gk=None) == q.QKNORM_OK
+
+
+def test_shapes(lib):
+    assert ph(lib, T=-1) == q.QKNORM_E_SHAPE
+    assert ph(lib, hq=-1) == q.QKNORM_E_SHAPE
+    assert ph(lib, hkv=-2) == q.QKNORM_E_SHAPE
+    assert ph(lib, D=0) == q.QKNORM_E_SHAPE
+    assert ph(lib, ld=2559) == q.QKNORM_E_SHAPE            # < (16+4)*128
+    assert ph(lib, ld=-4) == q.QKNORM_E_SHAPE
+    assert lw(lib, ld=5119) == q.QKNORM_E_SHAPE
+    assert lw(lib, wq=-8) == q.QKNORM_E_SHAPE
+    assert lw(lib, R=0) == q.QKNORM_E_SHAPE
+    assert lw(lib, R=-3) == q.QKNORM_E_SHAPE
+    assert lw(lib, R=3) == q.QKNORM_E_SHAPE                # does not divide 4096
+    assert lw(lib, wq=4000, R=8) == q.QKNORM_E_ALIGN        # 500 bf16 = 1000 B per shard
+    assert ps(lib, R=7) == q.QKNORM_E_SHAPE
+    assert ap(lib, n=0) == q.QKNORM_E_SHAPE
+    assert ap(lib, nwq=4095) == q.QKNORM_E_SHAPE            # full width below local width
+    assert ap(lib, nwk=0) == q.QKNORM_E_SHAPE
+
+
+def test_null_pointers(lib):
+    assert ph(lib, qkv=None) == q.QKNORM_E_NULLPTR
+    assert ph(lib, gq=None) == q.QKNORM_E_NULLPTR
+    assert ph(lib, gk=None) == q.QKNORM_E_NULLPTR           # hkv > 0 needs gamma_k
+    assert lw(lib, qkv=None) == q.QKNORM_E_NULLPTR
+    assert lw(lib, gk=None) == q.QKNORM_E_NULLPTR
+    assert ps(lib, pq=None) == q.QKNORM_E_NULLPTR
+    assert ps(lib, pk=None) == q.QKNORM_E_NULLPTR
+    assert ap(lib, pk=None) == q.QKNORM_E_NULLPTR
+    assert ap(lib, gq=None) == q.QKNORM_E_NULLPTR
+
+
+def test_alignment(lib):
+    assert ph(lib, qkv=A16 + 8) == q.QKNORM_E_ALIGN
+    assert ph(lib, gq=A16 + 4) == q.QKNORM_E_ALIGN
+    assert ph(lib, ld=3073) == q.QKNORM_E_ALIGN             # pitch 12292 B
+    assert lw(lib, ld=6145) == q.QKNORM_E_ALIGN
+    assert lw(lib, gq=A16 + 2) == q.QKNORM_E_ALIGN
+    assert ps(lib, pq=A16 + 1) == q.QKNORM_E_ALIGN
+    assert ap(lib, pk=A16 + 2) == q.QKNORM_E_ALIGN
+    assert ap(lib, wq=4092, nwq=4096) == q.QKNORM_E_ALIGN  # Q/K boundary off a 16 B vector
+
+
+def test_unsupported(lib):
+    assert ph(lib, D=96, ld=20 * 96) == q.QKNORM_E_UNSUPPORTED
+    assert ph(lib, D=512, ld=20 * 512) == q.QKNORM_E_UNSUPPORTED
+    assert lw(lib, R=2048, wq=4096 * 8, wk=2048 * 8, ld=6144 * 8) == q.QKNORM_E_UNSUPPORTED
+    assert ap(lib, n=4096) == q.QKNORM_E_UNSUPPORTED
+
+
+def test_binding_refuses_cpu_tensors():
+    torch = pytest.importorskip("torch")
+    x = torch.zeros(4, 256, dtype=torch.bfloat16)
+    g = torch.ones(128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU"):
+        q.qknorm_per_head(x, 2, 0, 128, g)
+    with pytest.raises(ValueError, match="GPU"):
+        q.qknorm_layerwise(x, 256, 0, torch.ones(256, dtype=torch.bfloat16))
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    with pytest.raises(RuntimeError, match="not built"):
+        q.load(str(tmp_path / "nope.so"))

@@ -1,0 +1,184 @@
+"""Per-head QK-Norm: the HIP kernels against the fp64 oracle, through the C ABI."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import qk_norm_amd as q
+from qk_norm_amd import synth
+from gpu_util import (Guarded, assert_bytes_equal, assert_close_to_oracle, host_to_device,
+                      ulp_histogram)
+
+pytestmark = pytest.mark.gpu
+
+
+def run_per_head(p: synth.Problem, check_ulp=True):
+    """Run the GPU per-head path on problem p and check it against the oracle."""
+    print(f"[per_head] {p.name} T={p.T} ld={p.ld} hq={p.hq} hkv={p.hkv} D={p.head_dim}", flush=True)
+    buf = Guarded(p.x, p.dtype)
+    gq = host_to_device(p.gamma_q, p.dtype)
+    gk = host_to_device(p.gamma_k, p.dtype) if p.gamma_k is not None else None
+    q.qknorm_per_head(buf.t, p.hq, p.hkv, p.head_dim, gq, gk, p.eps)
+    torch.cuda.synchronize()
+    got = buf.host()
+    assert buf.guards_intact(), "write outside the tensor"
+    y64, yr = oracle.per_head(p.x, p.dtype, p.hq, p.hkv, p.head_dim, p.gamma_q, p.gamma_k, p.eps)
+    qk = p.wq + p.wk
+    relmax = assert_close_to_oracle(got[:, :qk], y64[:, :qk], p.dtype, label=p.name)
+    assert_bytes_equal(got[:, qk:], p.x[:, qk:], f"{p.name}: V/padding columns")
+    if check_ulp:
+        hist = ulp_histogram(got[:, :qk], yr[:, :qk], p.dtype)
+        assert max(hist) <= 1, f"{p.name}: ulp histogram {hist}"
+        if p.dtype == synth.BF16 and qk * p.T > 10000:
+            assert hist.get(0, 0) / (qk * p.T) > 0.99, f"{p.name}: ulp histogram {hist}"
+    return got, relmax
+
+
+def test_cfg1_per_head_f32():
+    run_per_head(synth.cfg1())
+
+
+@pytest.mark.parametrize("H", synth.CFG2_SWEEP_H)
+@pytest.mark.parametrize("T", synth.CFG2_SWEEP_T)
+def test_cfg2_per_head_bf16_sweep(T, H):
+    run_per_head(synth.cfg2(T=T, H=H))
+
+
+@pytest.mark.parametrize("T", synth.CFG3_SWEEP_T)
+def test_cfg3_fused_gqa_bf16(T):
+    run_per_head(synth.cfg3(T=T))
+
+
+@pytest.mark.parametrize("dtype", [synth.F32, synth.BF16])
+@pytest.mark.parametrize("D", [64, 128, 256])
+def test_head_dims(dtype, D):
+    # ragged: 37 rows x (5 Q + 3 K) heads, padding after V
+    p = synth.per_head_problem(f"dims_D{D}", 21, dtype, 37, 5, 3, D, ld=(5 + 6) * D + 64,
+                               token_scale=(0.1, 10.0))
+    run_per_head(p)
+
+
+@pytest.mark.parametrize("dtype", [synth.F32, synth.BF16])
+@pytest.mark.parametrize("T,hq,hkv", [(1, 1, 0), (3, 1, 1), (7, 0, 3), (129, 3, 1), (1000, 7, 2)])
+def test_ragged_head_counts(dtype, T, hq, hkv):
+    p = synth.per_head_problem(f"ragged_T{T}_{hq}_{hkv}", 22, dtype, T, hq, hkv, 128,
+                               ld=(hq + 2 * hkv) * 128 + 8 * (dtype == synth.BF16) + 4 * (dtype == synth.F32))
+    run_per_head(p)
+
+
+def test_t0_is_a_noop():
+    x = torch.randn(0, 6144, device="cuda").to(torch.bfloat16)
+    g = torch.ones(128, device="cuda", dtype=torch.bfloat16)
+    q.qknorm_per_head(x, 32, 8, 128, g, g)
+    torch.cuda.synchronize()
+
+
+def test_zero_rows_and_eps_zero_closed_forms():
+    # zero head with eps > 0 -> zeros; k equal-magnitude nonzeros with eps = 0 ->
+    # gamma * sign * sqrt(D/k) exactly in bf16
+    D, H, T = 128, 8, 4
+    x = np.zeros((T, H * D))
+    roots = {}
+    for h, k in enumerate([2, 8, 32, 128, 2, 8, 32, 128]):
+        if h == 0:
+            continue
+        idx = np.arange(0, D, D // k)[:k]
+        x[:, h * D + idx] = 0.75 * np.where(np.arange(k) % 2 == 0, 1.0, -1.0)
+        roots[h] = (idx, np.sqrt(D / k))
+    for dtype in (synth.F32, synth.BF16):
+        xs = synth.to_dtype(x, dtype)
+        g = synth.make_gamma(3, 3, D, dtype)
+        for eps in (0.0, synth.eps_f32(1e-6)):
+            buf = Guarded(xs, dtype)
+            q.qknorm_per_head(buf.t, H, 0, D, host_to_device(g, dtype), None, eps)
+            torch.cuda.synchronize()
+            got = buf.host()
+            gd = oracle.decode(got, dtype)
+            if eps > 0.0:
+                assert np.all(gd[:, :D] == 0.0), "zero head with eps > 0 must stay zero"
+            else:
+                # 0 / sqrt(0): NaN by IEEE, on both sides
+                assert np.all(np.isnan(gd[:, :D]))
+                gd[:, :D] = 0.0
+            if eps == 0.0:
+                want = np.zeros((T, H * D))
+                for h, (idx, root) in roots.items():
+                    want[:, h * D + idx] = oracle.decode(g, dtype)[idx] * np.sign(x[:, h * D + idx]) * root
+                if dtype == synth.BF16:
+                    assert np.array_equal(got[:, D:], synth.to_dtype(want, dtype)[:, D:]), \
+                        "closed form, bit exact"
+                else:
+                    assert np.all(np.abs(gd[:, D:] - want[:, D:]) <= 1e-5 * np.abs(want[:, D:]))
+            y64, _ = oracle.per_head(xs, dtype, H, 0, D, g, None, eps)
+            assert_close_to_oracle(got[:, D:], y64[:, D:], dtype, label=f"closed forms eps={eps}")
+
+
+def test_extreme_magnitudes():
+    # per-token scales from 1e-8 to 1e8 keep fp32 sums of squares in range
+    T, H, D = 16, 4, 128
+    z = synth.normal(31, 0, T * H * D).reshape(T, H * D)
+    z *= (10.0 ** np.linspace(-8, 8, T))[:, None]
+    for dtype in (synth.F32, synth.BF16):
+        p = synth.Problem("extreme", dtype, T, H * D, H * D, 0, synth.to_dtype(z, dtype),
+                          synth.make_gamma(31, 3, D, dtype), None, synth.eps_f32(1e-6), hq=H,
+                          hkv=0, head_dim=D)
+        run_per_head(p, check_ulp=False)
+
+
+def test_bitwise_deterministic():
+    p = synth.cfg3(T=512)
+    a, _ = run_per_head(p)
+    b, _ = run_per_head(p)
+    assert np.array_equal(a, b)
+
+
+def test_standalone_3d_tensor_and_side_stream():
+    p = synth.cfg2(T=256, H=32)
+    x = host_to_device(p.x, p.dtype).view(256, 32, 128)
+    g = host_to_device(p.gamma_q, p.dtype)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        q.qknorm_per_head(x, 32, 0, 128, g, None, p.eps)
+    s.synchronize()
+    y64, _ = oracle.per_head(p.x, p.dtype, 32, 0, 128, p.gamma_q, None, p.eps)
+    got = x.view(256, 32 * 128).cpu().view(torch.int16).numpy().view(np.uint16)
+    assert_close_to_oracle(got, y64, p.dtype, label="3d on a side stream")
+
+
+def test_rows_with_pitch_view():
+    # a [T, (hq+hkv)*D] view into a wider buffer: pitch from stride(0)
+    p = synth.cfg3(T=64)
+    full = host_to_device(p.x, p.dtype)
+    view = full[:, : p.wq + p.wk]
+    q.qknorm_per_head(view, p.hq, p.hkv, p.head_dim, host_to_device(p.gamma_q, p.dtype),
+                      host_to_device(p.gamma_k, p.dtype), p.eps)
+    torch.cuda.synchronize()
+    got = full.cpu().view(torch.int16).numpy().view(np.uint16)
+    y64, _ = oracle.per_head(p.x, p.dtype, p.hq, p.hkv, p.head_dim, p.gamma_q, p.gamma_k, p.eps)
+    assert_close_to_oracle(got[:, : p.wq + p.wk], y64[:, : p.wq + p.wk], p.dtype, label="view")
+    assert_bytes_equal(got[:, p.wq + p.wk:], p.x[:, p.wq + p.wk:], "V")
+
+
+def test_graph_replay_matches_eager():
+    p = synth.cfg3(T=64)
+    src = host_to_device(p.x, p.dtype)
+    work = src.clone()
+    gq, gk = host_to_device(p.gamma_q, p.dtype), host_to_device(p.gamma_k, p.dtype)
+    q.qknorm_per_head(work, p.hq, p.hkv, p.head_dim, gq, gk, p.eps)
+    torch.cuda.synchronize()
+    eager = work.clone()
+    work.copy_(src)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            q.qknorm_per_head(work, p.hq, p.hkv, p.head_dim, gq, gk, p.eps)
+    torch.cuda.synchronize()
+    for _ in range(4):
+        work.copy_(src)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(work.view(torch.int16), eager.view(torch.int16))
