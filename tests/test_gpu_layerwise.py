@@ -58,8 +58,11 @@ def check_against_oracle(p, got, label):
     qk = p.wq + p.wk
     assert_close_to_oracle(got[:, :qk], y64[:, :qk], p.dtype, label=label)
     assert_bytes_equal(got[:, qk:], p.x[:, qk:], f"{label}: V/padding columns")
-    hist = ulp_histogram(got[:, :qk], yr[:, :qk], p.dtype)
-    assert max(hist) <= 1, f"{label}: ulp histogram {hist}"
+    if p.dtype == synth.BF16:
+        # one bf16 ulp is the tolerance itself: never more than 1 ulp from the
+        # oracle's own rounding (fp32 I/O is held to its 1e-5 relative bound)
+        hist = ulp_histogram(got[:, :qk], yr[:, :qk], p.dtype)
+        assert max(hist) <= 1, f"{label}: ulp histogram {hist}"
 
 
 def check_partials(p, pq, pk):

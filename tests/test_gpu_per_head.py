@@ -26,7 +26,7 @@ def run_per_head(p: synth.Problem, check_ulp=True):
     qk = p.wq + p.wk
     relmax = assert_close_to_oracle(got[:, :qk], y64[:, :qk], p.dtype, label=p.name)
     assert_bytes_equal(got[:, qk:], p.x[:, qk:], f"{p.name}: V/padding columns")
-    if check_ulp:
+    if check_ulp and p.dtype == synth.BF16:
         hist = ulp_histogram(got[:, :qk], yr[:, :qk], p.dtype)
         assert max(hist) <= 1, f"{p.name}: ulp histogram {hist}"
         if p.dtype == synth.BF16 and qk * p.T > 10000:
