@@ -15,6 +15,7 @@
  *   qkv   fused rows [T, ld] in device memory, row-major, ld in ELEMENTS.
  *         Row t starts at element t*ld.  Columns [0, wq) are Q, [wq, wq+wk)
  *         are K, and columns >= wq+wk (V, padding) are never read or written.
+ *         The row pitch ld*esize may be at most 64 MiB (QKNORM_E_UNSUPPORTED).
  *         (Lesson "Explain combined QKV projection and why it's faster than
  *         three separate projections?", section "With GQA": the fused output
  *         is Q heads, then K heads, then V heads, split by those widths.)

@@ -10,6 +10,7 @@
 namespace {
 
 constexpr int64_t kMaxShards = 1024;
+constexpr int64_t kMaxPitchBytes = INT64_C(1) << 26;
 constexpr int64_t kMaxHeadIndex = INT64_C(1) << 31;   // T * heads must stay below this
 constexpr int64_t kMaxRows = (INT64_C(1) << 31) - (INT64_C(1) << 20);
 
@@ -32,7 +33,8 @@ int check_region(const void* qkv, int64_t T, int64_t ld, int64_t wq, int64_t wk,
   if (ld < wq + wk) return QKNORM_E_SHAPE;
   const bool touched = T > 0 && wq + wk > 0;
   if (touched && qkv == nullptr) return QKNORM_E_NULLPTR;
-  if (ld > (INT64_C(1) << 40) || T * (ld + 1) > (INT64_C(1) << 46)) return QKNORM_E_UNSUPPORTED;
+  // rows are addressed with 32-bit buffer offsets: pitch at most 64 MiB
+  if (ld * es > kMaxPitchBytes || T * (ld + 1) > (INT64_C(1) << 46)) return QKNORM_E_UNSUPPORTED;
   if (touched && (!aligned16(qkv) || (ld * es) % 16 != 0)) return QKNORM_E_ALIGN;
   if ((wq * es) % 16 != 0 || (wk * es) % 16 != 0) return QKNORM_E_ALIGN;
   return QKNORM_OK;

@@ -27,22 +27,51 @@ template <> struct IoTraits<kBF16> {
 };
 
 // ----------------------------------------------------------------- memory --
+//
+// Streamed rows go through buffer loads/stores so each access carries explicit
+// cache-policy bits: "nt sc1" (streaming, no reuse expected) measured best for
+// in-place read-modify-write streams on MI355X.  A buffer descriptor must be
+// wave-uniform (SGPRs); offsets are 32-bit per lane, and any access past
+// num_records reads 0 / is dropped by the hardware range check.
 
-template <bool NT>
+// gfx9-family buffer descriptor word 3 (raw byte addressing).
+constexpr int kRsrcWord3 = 0x00020000;
+// CPol bits for buffer ops on gfx94x/gfx950: sc0 = 1, nt = 2, sc1 = 16.
+#ifndef QKNORM_LOAD_POLICY
+#define QKNORM_LOAD_POLICY 18      // nt sc1
+#endif
+#ifndef QKNORM_STORE_POLICY
+#define QKNORM_STORE_POLICY 18     // nt sc1
+#endif
+constexpr int kLoadPolicy = QKNORM_LOAD_POLICY;
+constexpr int kStorePolicy = QKNORM_STORE_POLICY;
+
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+
+__device__ __forceinline__ Rsrc make_rsrc(const void* base, uint64_t bytes) {
+  const uint32_t n = bytes > 0xFFFFFFFFull ? 0xFFFFFFFFu : (uint32_t)bytes;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, n, kRsrcWord3);
+}
+
+__device__ __forceinline__ u32x4 stream_load(Rsrc r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kLoadPolicy);
+}
+
+__device__ __forceinline__ void stream_store(Rsrc r, uint32_t off, u32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, kStorePolicy);
+}
+
+// Small, reused data (gamma): default policy, kept in the caches.
+__device__ __forceinline__ u32x4 cached_load(Rsrc r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+
 __device__ __forceinline__ u32x4 load16(const void* p) {
-  if constexpr (NT)
-    return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-  else
-    return *reinterpret_cast<const u32x4*>(p);
+  return *reinterpret_cast<const u32x4*>(p);
 }
 
-template <bool NT>
-__device__ __forceinline__ void store16(void* p, u32x4 v) {
-  if constexpr (NT)
-    __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
-  else
-    *reinterpret_cast<u32x4*>(p) = v;
-}
+// Force a value the compiler cannot prove uniform into an SGPR.
+__device__ __forceinline__ uint32_t uniform(uint32_t v) { return __builtin_amdgcn_readfirstlane(v); }
 
 // ------------------------------------------------------------ conversions --
 
@@ -122,9 +151,11 @@ __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 
-// 1 / sqrt(ms + eps) with v_rsq_f32 (about 1 ulp).
-__device__ __forceinline__ float rms_scale(float sumsq, float width, float eps) {
-  return __builtin_amdgcn_rsqf(sumsq / width + eps);
+// 1 / sqrt(S/n + eps): the mean square plus eps as one fused multiply-add
+// with 1/n (rounded to fp32 on the host, exact for power-of-two widths),
+// then v_rsq_f32 (about 1 ulp).
+__device__ __forceinline__ float rms_scale(float sumsq, float inv_width, float eps) {
+  return __builtin_amdgcn_rsqf(__builtin_fmaf(sumsq, inv_width, eps));
 }
 
 }  // namespace qknorm

@@ -6,22 +6,20 @@
 #include "qknorm_device.hpp"
 #include "qknorm_launch.hpp"
 
-#ifndef QKNORM_NT
-#define QKNORM_NT 1            // non-temporal loads/stores for the streamed rows
+#ifndef QKNORM_PH_THREADS
+#define QKNORM_PH_THREADS 512      // threads per per-head block
 #endif
 #ifndef QKNORM_PH_UNROLL
-#define QKNORM_PH_UNROLL 4     // heads per 16-lane group per loop trip
+#define QKNORM_PH_UNROLL 2         // heads per lane group per loop trip
 #endif
 #ifndef QKNORM_PH_BLOCKS_PER_CU
-#define QKNORM_PH_BLOCKS_PER_CU 8
+#define QKNORM_PH_BLOCKS_PER_CU 24 // per-head grid cap, blocks per CU
 #endif
 #ifndef QKNORM_LW_WAVES_PER_CU
-#define QKNORM_LW_WAVES_PER_CU 32   // grid cap for the row kernels, in waves per CU
+#define QKNORM_LW_WAVES_PER_CU 4096  // layerwise grid cap, waves per CU (large: one row per block)
 #endif
 
 namespace qknorm {
-
-static constexpr bool kNT = QKNORM_NT != 0;
 
 // =================================================================== per head
 //
@@ -33,60 +31,138 @@ static constexpr bool kNT = QKNORM_NT != 0;
 // is a Q head with gamma_q, otherwise a K head with gamma_k.  (t, h) are kept
 // incrementally so the loop has no integer division.
 
-template <int DT, int LPH, int U>
-__global__ __launch_bounds__(256) void per_head_kernel(
-    uint8_t* __restrict__ qkv, int64_t ld_bytes, uint32_t T, uint32_t H, uint32_t hq,
-    const uint8_t* __restrict__ gamma_q, const uint8_t* __restrict__ gamma_k, float eps,
-    float head_dim, uint32_t stride_rows, uint32_t stride_heads) {
+// Addresses of one trip: U heads per lane group starting at the wave's head
+// (tw, hw).  CONTIG: rows are back to back with no padding, so the heads form
+// one flat array and no row wrap is needed.
+//
+// Loads and stores are issued unconditionally (straight-line code, so the
+// compiler can keep the next trip's loads in flight while this trip is being
+// computed).  The descriptor spans exactly the bytes this trip may touch; a
+// lane without a head gets an offset past that span, and a trip past the end
+// of the tensor gets an empty descriptor, so the hardware range check turns
+// those accesses into no-ops (loads return 0, stores are dropped).
+template <int LPH, int U, bool CONTIG>
+struct PerHeadTrip {
+  Rsrc rs;
+  uint32_t off[U];
+  bool isq[U];
+
+  static constexpr uint32_t kNoHead = 0xFFFFFFF0u;
+
+  __device__ __forceinline__ void setup(uint8_t* qkv, uint32_t ld_bytes, uint32_t T, uint32_t H,
+                                        uint32_t hq, uint32_t row_bytes, bool live, uint32_t tw,
+                                        uint32_t hw, uint32_t sub, uint32_t grp) {
+    constexpr uint32_t HPW = 64 / LPH;
+    constexpr uint32_t CH = HPW * U;
+    constexpr uint32_t head_bytes = LPH * 16;
+    tw = live ? tw : 0;
+    hw = live ? hw : 0;
+    // bytes from the wave's first head to the end of the tensor (the last row
+    // ends with its K heads); CONTIG: tw = 0 and hw is the flat head index
+    const uint64_t first = (uint64_t)tw * ld_bytes + (CONTIG ? (uint64_t)hw * head_bytes : 0);
+    const uint64_t rest = CONTIG ? ((uint64_t)T * H - hw) * head_bytes
+                                 : (uint64_t)(T - 1 - tw) * ld_bytes + row_bytes;
+    // bytes this trip can reach: CH heads, possibly wrapping into later rows
+    uint64_t span;
+    if constexpr (CONTIG)
+      span = (uint64_t)CH * head_bytes;
+    else
+      span = (uint64_t)((hw + CH - 1) / H) * ld_bytes + row_bytes;
+    rs = make_rsrc(qkv + first, live ? (span < rest ? span : rest) : 0);
+#pragma unroll
+    for (uint32_t u = 0; u < U; ++u) {
+      const uint32_t k = u * HPW + grp;      // head index from the wave's first head
+      if constexpr (CONTIG) {
+        const bool ok = hw + k < T * H;
+        isq[u] = hq != 0;                    // one region only: all Q or all K heads
+        off[u] = ok ? k * head_bytes + sub * 16 : kNoHead;
+      } else {
+        uint32_t hu = hw + k, dt = 0;
+        if (hu >= H) {                       // wrap into the following row(s)
+          dt = hu / H;
+          hu -= dt * H;
+        }
+        isq[u] = hu < hq;
+        off[u] = tw + dt < T ? dt * ld_bytes + hu * head_bytes + sub * 16 : kNoHead;
+      }
+    }
+  }
+};
+
+// Software-pipelined: the next trip's loads are issued before the current
+// trip's reduction and stores, so each lane keeps 2*U loads in flight and the
+// dependent arithmetic of one trip overlaps the memory latency of the next.
+template <int DT, int LPH, int U, bool CONTIG>
+__global__ __launch_bounds__(QKNORM_PH_THREADS) void per_head_kernel(
+    uint8_t* __restrict__ qkv, uint32_t ld_bytes, uint32_t T, uint32_t H, uint32_t hq,
+    uint32_t row_bytes, const uint8_t* __restrict__ gamma_q, const uint8_t* __restrict__ gamma_k,
+    float eps, float inv_d, uint32_t stride_rows, uint32_t stride_heads) {
   using IO = IoTraits<DT>;
+  using Trip = PerHeadTrip<LPH, U, CONTIG>;
   constexpr int E = IO::kElems;
-  constexpr int HPW = 64 / LPH;              // heads per wave step
-  constexpr uint32_t CH = HPW * U;           // heads per wave per trip
+  constexpr uint32_t CH = (64 / LPH) * U;    // heads per wave per trip
   const uint32_t lane = threadIdx.x & 63;
   const uint32_t sub = lane % LPH;           // 16-byte slot inside the head
   const uint32_t grp = lane / LPH;           // head slot inside the wave step
-  const int64_t head_bytes = (int64_t)LPH * 16;
 
-  // gamma of this lane's columns, kept in registers for the whole kernel
-  // (a NULL gamma belongs to a region with no heads and is never applied)
+  // gamma is staged once per block in LDS: a global load of the same few
+  // lines by every wave of the grid would make those lines an L2 hot spot.
+  __shared__ u32x4 g_lds[2][LPH];
+  if (threadIdx.x < LPH) {
+    g_lds[0][threadIdx.x] = gamma_q ? load16(gamma_q + threadIdx.x * 16) : u32x4{0, 0, 0, 0};
+    g_lds[1][threadIdx.x] = gamma_k ? load16(gamma_k + threadIdx.x * 16) : u32x4{0, 0, 0, 0};
+  }
+
+  // (tw, hw): row and head of the wave's first head this trip (wave-uniform).
+  // T*H < 2^31 is checked on the host, so 32-bit arithmetic suffices; a
+  // single-region tensor starts at row 0 with the flat head index in hw.
+  const uint32_t wave = uniform((blockIdx.x * blockDim.x + threadIdx.x) >> 6);
+  const uint32_t g0 = wave * CH;
+  uint32_t tw = CONTIG ? 0 : g0 / H;
+  uint32_t hw = CONTIG ? g0 : g0 - tw * H;
+  const bool live = CONTIG ? hw < T * H : tw < T;
+
+  // first trip's loads go out before the barrier so it overlaps their latency
+  Trip cur;
+  u32x4 vc[U];
+  cur.setup(qkv, ld_bytes, T, H, hq, row_bytes, live, tw, hw, sub, grp);
+#pragma unroll
+  for (uint32_t u = 0; u < U; ++u) vc[u] = stream_load(cur.rs, cur.off[u]);
+
+  __syncthreads();
   float gq[E], gk[E];
-  unpack<DT>(gamma_q ? load16<false>(gamma_q + sub * 16) : u32x4{0, 0, 0, 0}, gq);
-  unpack<DT>(gamma_k ? load16<false>(gamma_k + sub * 16) : u32x4{0, 0, 0, 0}, gk);
+  unpack<DT>(g_lds[0][sub], gq);
+  unpack<DT>(g_lds[1][sub], gk);
+  if (!live) return;
 
-  const uint32_t wave = (blockIdx.x * blockDim.x + threadIdx.x) >> 6;
-  // first head of this lane: wave*CH + grp
-  uint64_t g0 = (uint64_t)wave * CH + grp;
-  uint32_t t = (uint32_t)(g0 / H);
-  uint32_t h = (uint32_t)(g0 - (uint64_t)t * H);
-
-  while (t < T) {
-    u32x4 v[U];
-    uint8_t* p[U];
-    bool ok[U], isq[U];
+  while (true) {
+    // next trip: advance by the whole grid (stride_rows rows, stride_heads heads;
+    // a flat index for single-region tensors)
+    uint32_t tn = tw + stride_rows, hn = hw + stride_heads;
+    if (!CONTIG && hn >= H) { hn -= H; ++tn; }
+    const bool more = CONTIG ? hn < T * H : tn < T;
+    Trip nxt;
+    u32x4 vn[U];
+    nxt.setup(qkv, ld_bytes, T, H, hq, row_bytes, more, tn, hn, sub, grp);
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      uint32_t hu = h + u * HPW, tu = t;
-      while (hu >= H) { hu -= H; ++tu; }
-      ok[u] = tu < T;
-      isq[u] = hu < hq;
-      p[u] = qkv + (int64_t)tu * ld_bytes + (int64_t)hu * head_bytes + sub * 16;
-      if (ok[u]) v[u] = load16<kNT>(p[u]);
-    }
+    for (uint32_t u = 0; u < U; ++u) vn[u] = stream_load(nxt.rs, nxt.off[u]);
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
+    for (uint32_t u = 0; u < U; ++u) {
       float x[E];
-      unpack<DT>(ok[u] ? v[u] : u32x4{0, 0, 0, 0}, x);
-      float s = group_sum<LPH>(vec_sumsq<DT>(x, 0.f));
-      float r = rms_scale(s, head_dim, eps);
+      unpack<DT>(vc[u], x);
+      const float s = group_sum<LPH>(vec_sumsq<DT>(x, 0.f));
+      const float r = rms_scale(s, inv_d, eps);
       float y[E];
 #pragma unroll
-      for (int e = 0; e < E; ++e) y[e] = (x[e] * (isq[u] ? gq[e] : gk[e])) * r;
-      if (ok[u]) store16<kNT>(p[u], pack<DT>(y));
+      for (int e = 0; e < E; ++e) y[e] = (x[e] * (cur.isq[u] ? gq[e] : gk[e])) * r;
+      stream_store(cur.rs, cur.off[u], pack<DT>(y));
     }
-    // advance by the whole grid: stride_rows rows and stride_heads heads
-    h += stride_heads;
-    t += stride_rows;
-    if (h >= H) { h -= H; ++t; }
+    if (!more) break;
+    cur = nxt;
+#pragma unroll
+    for (uint32_t u = 0; u < U; ++u) vc[u] = vn[u];
+    tw = tn;
+    hw = hn;
   }
 }
 
@@ -107,7 +183,7 @@ struct RowGeom {
   uint32_t q_vecs, k_vecs;      // 16-byte vectors of Q and of K per row
   uint32_t nshards;
   uint32_t q_svecs, k_svecs;    // vectors per shard
-  float wq, wk;                 // divisors (full widths)
+  float inv_wq, inv_wk;         // 1 / full widths (fp32)
 };
 
 __device__ __forceinline__ float combine(const float* __restrict__ p, uint32_t n, int64_t stride) {
@@ -136,22 +212,22 @@ __device__ __forceinline__ void slots_load_gamma(const uint8_t* __restrict__ gam
 #pragma unroll
   for (int j = 0; j < VPL; ++j) {
     const uint32_t r = wave + i * nw, v = lane + k * 64;
-    S.g[j] = (r < R && v < svecs) ? load16<false>(gamma + ((int64_t)r * svecs + v) * 16)
+    S.g[j] = (r < R && v < svecs) ? load16(gamma + ((uint64_t)r * svecs + v) * 16)
                                   : u32x4{0, 0, 0, 0};
     if (++k == trips) { k = 0; ++i; }
   }
 }
 
 template <int DT, int VPL>
-__device__ __forceinline__ void slots_load(const uint8_t* __restrict__ reg, uint32_t svecs,
-                                           uint32_t R, uint32_t wave, uint32_t nw, uint32_t lane,
+__device__ __forceinline__ void slots_load(Rsrc rs, uint32_t reg_off, uint32_t svecs, uint32_t R,
+                                           uint32_t wave, uint32_t nw, uint32_t lane,
                                            Slots<VPL>& S) {
   const uint32_t trips = (svecs + 63) / 64;
   uint32_t i = 0, k = 0;
 #pragma unroll
   for (int j = 0; j < VPL; ++j) {
     const uint32_t r = wave + i * nw, v = lane + k * 64;
-    S.x[j] = (r < R && v < svecs) ? load16<kNT>(reg + ((int64_t)r * svecs + v) * 16)
+    S.x[j] = (r < R && v < svecs) ? stream_load(rs, reg_off + (r * svecs + v) * 16)
                                   : u32x4{0, 0, 0, 0};
     if (++k == trips) { k = 0; ++i; }
   }
@@ -183,7 +259,7 @@ __device__ __forceinline__ void slots_partials(uint32_t svecs, uint32_t R, uint3
 }
 
 template <int DT, int VPL>
-__device__ __forceinline__ void slots_apply(uint8_t* __restrict__ reg, uint32_t svecs, uint32_t R,
+__device__ __forceinline__ void slots_apply(Rsrc rs, uint32_t reg_off, uint32_t svecs, uint32_t R,
                                             uint32_t wave, uint32_t nw, uint32_t lane,
                                             const Slots<VPL>& S, float scale) {
   using IO = IoTraits<DT>;
@@ -198,7 +274,7 @@ __device__ __forceinline__ void slots_apply(uint8_t* __restrict__ reg, uint32_t 
       unpack<DT>(S.g[j], g);
 #pragma unroll
       for (int e = 0; e < IO::kElems; ++e) y[e] = (x[e] * g[e]) * scale;
-      store16<kNT>(reg + ((int64_t)r * svecs + v) * 16, pack<DT>(y));
+      stream_store(rs, reg_off + (r * svecs + v) * 16, pack<DT>(y));
     }
     if (++k == trips) { k = 0; ++i; }
   }
@@ -207,33 +283,39 @@ __device__ __forceinline__ void slots_apply(uint8_t* __restrict__ reg, uint32_t 
 // --- streamed shards (MODE 1 and 2): same order, dynamic loops ---------------
 
 template <int DT>
-__device__ __forceinline__ float shard_sumsq_stream(const uint8_t* __restrict__ sp,
-                                                    uint32_t svecs, uint32_t lane) {
+__device__ __forceinline__ float shard_sumsq_stream(Rsrc rs, uint32_t shard_off, uint32_t svecs,
+                                                    uint32_t lane) {
   using IO = IoTraits<DT>;
   const uint32_t trips = (svecs + 63) / 64;
   float acc = 0.f;
   for (uint32_t k = 0; k < trips; ++k) {
     const uint32_t v = lane + k * 64;
     float x[IO::kElems];
-    unpack<DT>(v < svecs ? load16<kNT>(sp + (int64_t)v * 16) : u32x4{0, 0, 0, 0}, x);
+    unpack<DT>(v < svecs ? stream_load(rs, shard_off + v * 16) : u32x4{0, 0, 0, 0}, x);
     acc = vec_sumsq<DT>(x, acc);
   }
   return group_sum<64>(acc);
 }
 
 template <int DT>
-__device__ __forceinline__ void apply_stream(uint8_t* __restrict__ reg,
+__device__ __forceinline__ void apply_stream(Rsrc rs, uint32_t reg_off,
                                              const uint8_t* __restrict__ gamma, uint32_t nvecs,
                                              uint32_t tid, uint32_t nthreads, float scale) {
   using IO = IoTraits<DT>;
   for (uint32_t v = tid; v < nvecs; v += nthreads) {
     float x[IO::kElems], g[IO::kElems], y[IO::kElems];
-    unpack<DT>(load16<kNT>(reg + (int64_t)v * 16), x);
-    unpack<DT>(load16<false>(gamma + (int64_t)v * 16), g);
+    unpack<DT>(stream_load(rs, reg_off + v * 16), x);
+    unpack<DT>(load16(gamma + (uint64_t)v * 16), g);
 #pragma unroll
     for (int e = 0; e < IO::kElems; ++e) y[e] = (x[e] * g[e]) * scale;
-    store16<kNT>(reg + (int64_t)v * 16, pack<DT>(y));
+    stream_store(rs, reg_off + v * 16, pack<DT>(y));
   }
+}
+
+// Descriptor over the Q+K part of row t (wave-uniform).
+__device__ __forceinline__ Rsrc row_rsrc(const uint8_t* qkv, uint64_t ld_bytes, uint32_t t,
+                                         uint32_t qk_vecs) {
+  return make_rsrc(qkv + (uint64_t)t * ld_bytes, (uint64_t)qk_vecs * 16);
 }
 
 // Fused layerwise, row kept in registers (VPL slots per region per lane).
@@ -243,30 +325,30 @@ __global__ __launch_bounds__(512) void layerwise_regs_kernel(
     const uint8_t* __restrict__ gamma_k, float eps) {
   extern __shared__ float lds[];               // [2 buffers][Q, K][nshards]
   const uint32_t lane = threadIdx.x & 63;
-  const uint32_t wave = threadIdx.x >> 6;
+  const uint32_t wave = uniform(threadIdx.x >> 6);
   const uint32_t nw = blockDim.x >> 6;
   const uint32_t R = G.nshards;
   const uint32_t Rq = G.q_vecs ? R : 0, Rk = G.k_vecs ? R : 0;
+  const uint32_t k_off = G.q_vecs * 16;
   Slots<VPL> sq, sk;
   slots_load_gamma<DT, VPL>(gamma_q, G.q_svecs, Rq, wave, nw, lane, sq);
   slots_load_gamma<DT, VPL>(gamma_k, G.k_svecs, Rk, wave, nw, lane, sk);
   uint32_t parity = 0;
   for (uint32_t t = blockIdx.x; t < G.T; t += gridDim.x, parity ^= 1) {
-    uint8_t* qreg = qkv + (int64_t)t * G.ld_bytes;
-    uint8_t* kreg = qreg + (int64_t)G.q_vecs * 16;
+    const Rsrc rs = row_rsrc(qkv, G.ld_bytes, t, G.q_vecs + G.k_vecs);
     float* pq = lds + parity * 2 * R;
     float* pk = pq + R;
-    slots_load<DT, VPL>(qreg, G.q_svecs, Rq, wave, nw, lane, sq);
-    slots_load<DT, VPL>(kreg, G.k_svecs, Rk, wave, nw, lane, sk);
+    slots_load<DT, VPL>(rs, 0, G.q_svecs, Rq, wave, nw, lane, sq);
+    slots_load<DT, VPL>(rs, k_off, G.k_svecs, Rk, wave, nw, lane, sk);
     slots_partials<DT, VPL>(G.q_svecs, Rq, wave, nw, lane, sq, pq);
     slots_partials<DT, VPL>(G.k_svecs, Rk, wave, nw, lane, sk, pk);
     __syncthreads();
     // Double-buffered partials: this buffer is next written two trips later,
     // after every thread has passed the next trip's barrier.
-    if (Rq) slots_apply<DT, VPL>(qreg, G.q_svecs, Rq, wave, nw, lane, sq,
-                                 rms_scale(combine(pq, R, 1), G.wq, eps));
-    if (Rk) slots_apply<DT, VPL>(kreg, G.k_svecs, Rk, wave, nw, lane, sk,
-                                 rms_scale(combine(pk, R, 1), G.wk, eps));
+    if (Rq) slots_apply<DT, VPL>(rs, 0, G.q_svecs, Rq, wave, nw, lane, sq,
+                                 rms_scale(combine(pq, R, 1), G.inv_wq, eps));
+    if (Rk) slots_apply<DT, VPL>(rs, k_off, G.k_svecs, Rk, wave, nw, lane, sk,
+                                 rms_scale(combine(pk, R, 1), G.inv_wk, eps));
   }
 }
 
@@ -278,32 +360,32 @@ __global__ __launch_bounds__(512) void layerwise_stream_kernel(
     const uint8_t* __restrict__ gamma_k, float eps) {
   extern __shared__ float lds[];
   const uint32_t lane = threadIdx.x & 63;
-  const uint32_t wave = threadIdx.x >> 6;
+  const uint32_t wave = uniform(threadIdx.x >> 6);
   const uint32_t nw = blockDim.x >> 6;
   const uint32_t R = G.nshards;
+  const uint32_t k_off = G.q_vecs * 16;
   uint32_t parity = 0;
   for (uint32_t t = blockIdx.x; t < G.T; t += gridDim.x, parity ^= 1) {
-    uint8_t* qreg = qkv + (int64_t)t * G.ld_bytes;
-    uint8_t* kreg = qreg + (int64_t)G.q_vecs * 16;
+    const Rsrc rs = row_rsrc(qkv, G.ld_bytes, t, G.q_vecs + G.k_vecs);
     float* pq = lds + parity * 2 * R;
     float* pk = pq + R;
     for (uint32_t r = wave; r < R; r += nw) {
       if (G.q_vecs) {
-        const float s = shard_sumsq_stream<DT>(qreg + (int64_t)r * G.q_svecs * 16, G.q_svecs, lane);
+        const float s = shard_sumsq_stream<DT>(rs, r * G.q_svecs * 16, G.q_svecs, lane);
         if (lane == 0) pq[r] = s;
       }
       if (G.k_vecs) {
-        const float s = shard_sumsq_stream<DT>(kreg + (int64_t)r * G.k_svecs * 16, G.k_svecs, lane);
+        const float s = shard_sumsq_stream<DT>(rs, k_off + r * G.k_svecs * 16, G.k_svecs, lane);
         if (lane == 0) pk[r] = s;
       }
     }
     __syncthreads();
     if (G.q_vecs)
-      apply_stream<DT>(qreg, gamma_q, G.q_vecs, threadIdx.x, blockDim.x,
-                       rms_scale(combine(pq, R, 1), G.wq, eps));
+      apply_stream<DT>(rs, 0, gamma_q, G.q_vecs, threadIdx.x, blockDim.x,
+                       rms_scale(combine(pq, R, 1), G.inv_wq, eps));
     if (G.k_vecs)
-      apply_stream<DT>(kreg, gamma_k, G.k_vecs, threadIdx.x, blockDim.x,
-                       rms_scale(combine(pk, R, 1), G.wk, eps));
+      apply_stream<DT>(rs, k_off, gamma_k, G.k_vecs, threadIdx.x, blockDim.x,
+                       rms_scale(combine(pk, R, 1), G.inv_wk, eps));
   }
 }
 
@@ -319,16 +401,14 @@ __global__ __launch_bounds__(256) void partial_sumsq_kernel(const uint8_t* __res
   const uint64_t nk = G.k_vecs ? (uint64_t)G.T * G.nshards : 0;
   const uint64_t total = nq + nk;
   const uint64_t nwaves = ((uint64_t)gridDim.x * blockDim.x) >> 6;
-  for (uint64_t i = ((uint64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6; i < total;
-       i += nwaves) {
+  for (uint64_t i = uniform((blockIdx.x * blockDim.x + threadIdx.x) >> 6); i < total; i += nwaves) {
     const bool isk = i >= nq;
     const uint64_t w = isk ? i - nq : i;
     const uint32_t t = (uint32_t)(w / G.nshards), r = (uint32_t)(w % G.nshards);
     const uint32_t svecs = isk ? G.k_svecs : G.q_svecs;
-    const uint8_t* sp = qkv + (int64_t)t * G.ld_bytes +
-                        (int64_t)((isk ? G.q_vecs : 0) + r * svecs) * 16;
-    const float s = shard_sumsq_stream<DT>(sp, svecs, lane);
-    if (lane == 0) (isk ? part_k : part_q)[(int64_t)r * G.T + t] = s;
+    const Rsrc rs = row_rsrc(qkv, G.ld_bytes, t, G.q_vecs + G.k_vecs);
+    const float s = shard_sumsq_stream<DT>(rs, ((isk ? G.q_vecs : 0) + r * svecs) * 16, svecs, lane);
+    if (lane == 0) (isk ? part_k : part_q)[(uint64_t)r * G.T + t] = s;
   }
 }
 
@@ -336,18 +416,18 @@ __global__ __launch_bounds__(256) void partial_sumsq_kernel(const uint8_t* __res
 // K.  scale = rsq((sum over r < nparts of part[r*T + t]) / norm_w + eps).
 template <int DT>
 __global__ __launch_bounds__(256) void apply_scalar_kernel(
-    uint8_t* __restrict__ qkv, int64_t ld_bytes, uint32_t T, uint32_t q_vecs, uint32_t k_vecs,
+    uint8_t* __restrict__ qkv, uint64_t ld_bytes, uint32_t T, uint32_t q_vecs, uint32_t k_vecs,
     const float* __restrict__ part_q, const float* __restrict__ part_k, uint32_t nparts,
-    float norm_wq, float norm_wk, const uint8_t* __restrict__ gamma_q,
+    float inv_norm_wq, float inv_norm_wk, const uint8_t* __restrict__ gamma_q,
     const uint8_t* __restrict__ gamma_k, float eps) {
   for (uint32_t t = blockIdx.x; t < T; t += gridDim.x) {
-    uint8_t* row = qkv + (int64_t)t * ld_bytes;
+    const Rsrc rs = row_rsrc(qkv, ld_bytes, t, q_vecs + k_vecs);
     if (q_vecs)
-      apply_stream<DT>(row, gamma_q, q_vecs, threadIdx.x, blockDim.x,
-                       rms_scale(combine(part_q + t, nparts, T), norm_wq, eps));
+      apply_stream<DT>(rs, 0, gamma_q, q_vecs, threadIdx.x, blockDim.x,
+                       rms_scale(combine(part_q + t, nparts, T), inv_norm_wq, eps));
     if (k_vecs)
-      apply_stream<DT>(row + (int64_t)q_vecs * 16, gamma_k, k_vecs, threadIdx.x, blockDim.x,
-                       rms_scale(combine(part_k + t, nparts, T), norm_wk, eps));
+      apply_stream<DT>(rs, q_vecs * 16, gamma_k, k_vecs, threadIdx.x, blockDim.x,
+                       rms_scale(combine(part_k + t, nparts, T), inv_norm_wk, eps));
   }
 }
 
@@ -357,8 +437,9 @@ template <int DT, int LPH>
 static hipError_t launch_per_head_t(const PerHeadArgs& a, hipStream_t s, int cus) {
   constexpr int U = QKNORM_PH_UNROLL;
   constexpr uint64_t CH = (64 / LPH) * U;
-  constexpr int kBlock = 256;
+  constexpr int kBlock = QKNORM_PH_THREADS;
   constexpr uint64_t heads_per_block = CH * (kBlock / 64);
+  const int es = IoTraits<DT>::kBytes;
   const uint64_t H = (uint64_t)a.hq + a.hkv;
   const uint64_t total = (uint64_t)a.T * H;
   uint64_t blocks = (total + heads_per_block - 1) / heads_per_block;
@@ -366,11 +447,14 @@ static hipError_t launch_per_head_t(const PerHeadArgs& a, hipStream_t s, int cus
   if (blocks > cap) blocks = cap;
   if (blocks < 1) blocks = 1;
   const uint64_t stride = blocks * heads_per_block;   // heads advanced per trip
-  hipLaunchKernelGGL((per_head_kernel<DT, LPH, U>), dim3((uint32_t)blocks), dim3(kBlock), 0, s,
-                     (uint8_t*)a.qkv, a.ld * (int64_t)IoTraits<DT>::kBytes, (uint32_t)a.T,
-                     (uint32_t)H, (uint32_t)a.hq, (const uint8_t*)a.gamma_q,
-                     (const uint8_t*)a.gamma_k, a.eps, (float)a.head_dim,
-                     (uint32_t)(stride / H), (uint32_t)(stride % H));
+  const bool contig = a.hq == 0 || a.hkv == 0 ? (a.ld == (int64_t)H * a.head_dim) : false;
+  auto kern = contig ? per_head_kernel<DT, LPH, U, true> : per_head_kernel<DT, LPH, U, false>;
+  hipLaunchKernelGGL(kern, dim3((uint32_t)blocks), dim3(kBlock), 0, s, (uint8_t*)a.qkv,
+                     (uint32_t)(a.ld * es), (uint32_t)a.T, (uint32_t)H, (uint32_t)a.hq,
+                     (uint32_t)(H * a.head_dim * es), (const uint8_t*)a.gamma_q,
+                     (const uint8_t*)a.gamma_k, a.eps, 1.0f / (float)a.head_dim,
+                     contig ? 0u : (uint32_t)(stride / H),
+                     contig ? (uint32_t)stride : (uint32_t)(stride % H));
   return hipGetLastError();
 }
 
@@ -401,8 +485,8 @@ static RowGeom make_geom(int64_t T, int64_t ld, int64_t wq, int64_t wk, int32_t 
   G.nshards = (uint32_t)nshards;
   G.q_svecs = G.q_vecs / G.nshards;
   G.k_svecs = G.k_vecs / G.nshards;
-  G.wq = (float)wq;
-  G.wk = (float)wk;
+  G.inv_wq = wq ? 1.0f / (float)wq : 0.f;
+  G.inv_wk = wk ? 1.0f / (float)wk : 0.f;
   return G;
 }
 
@@ -457,7 +541,7 @@ static hipError_t launch_partial_dt(const PartialArgs& a, hipStream_t s, int cus
   const RowGeom G = make_geom(a.T, a.ld, a.wq, a.wk, a.nshards, IoTraits<DT>::kBytes);
   const uint64_t items = (uint64_t)a.T * a.nshards * ((a.wq > 0) + (a.wk > 0));
   uint64_t blocks = (items + 3) / 4;
-  const uint64_t cap = (uint64_t)cus * 8;
+  const uint64_t cap = (uint64_t)cus * (QKNORM_LW_WAVES_PER_CU / 4);
   if (blocks > cap) blocks = cap;
   if (blocks < 1) blocks = 1;
   hipLaunchKernelGGL((partial_sumsq_kernel<DT>), dim3((uint32_t)blocks), dim3(256), 0, s,
@@ -473,13 +557,14 @@ template <int DT>
 static hipError_t launch_apply_dt(const ApplyArgs& a, hipStream_t s, int cus) {
   const int esize = IoTraits<DT>::kBytes;
   uint64_t blocks = a.T;
-  const uint64_t cap = (uint64_t)cus * 8;
+  const uint64_t cap = (uint64_t)cus * (QKNORM_LW_WAVES_PER_CU / 4);
   if (blocks > cap) blocks = cap;
   if (blocks < 1) blocks = 1;
   hipLaunchKernelGGL((apply_scalar_kernel<DT>), dim3((uint32_t)blocks), dim3(256), 0, s,
-                     (uint8_t*)a.qkv, a.ld * esize, (uint32_t)a.T, (uint32_t)(a.wq * esize / 16),
+                     (uint8_t*)a.qkv, (uint64_t)(a.ld * esize), (uint32_t)a.T, (uint32_t)(a.wq * esize / 16),
                      (uint32_t)(a.wk * esize / 16), a.part_q, a.part_k, (uint32_t)a.nparts,
-                     (float)a.norm_wq, (float)a.norm_wk, (const uint8_t*)a.gamma_q,
+                     a.norm_wq ? 1.0f / (float)a.norm_wq : 0.f,
+                     a.norm_wk ? 1.0f / (float)a.norm_wk : 0.f, (const uint8_t*)a.gamma_q,
                      (const uint8_t*)a.gamma_k, a.eps);
   return hipGetLastError();
 }

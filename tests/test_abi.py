@@ -157,6 +157,9 @@ def test_unsupported(lib):
     assert ph(lib, D=512, ld=20 * 512) == q.QKNORM_E_UNSUPPORTED
     assert lw(lib, R=2048, wq=4096 * 8, wk=2048 * 8, ld=6144 * 8) == q.QKNORM_E_UNSUPPORTED
     assert ap(lib, n=4096) == q.QKNORM_E_UNSUPPORTED
+    # rows are addressed with 32-bit offsets: pitch above 64 MiB is refused
+    assert ph(lib, ld=(1 << 24) + 4, T=2) == q.QKNORM_E_UNSUPPORTED      # fp32: 64 MiB + 16 B
+    assert lw(lib, ld=(1 << 25) + 8, T=2) == q.QKNORM_E_UNSUPPORTED      # bf16
 
 
 def test_binding_refuses_cpu_tensors():

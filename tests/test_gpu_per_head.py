@@ -182,3 +182,15 @@ def test_graph_replay_matches_eager():
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(work.view(torch.int16), eager.view(torch.int16))
+
+
+@pytest.mark.parametrize("dtype", [synth.F32, synth.BF16])
+@pytest.mark.parametrize("hq,hkv", [(0, 5), (5, 0), (3, 2)])
+def test_rows_without_v_or_padding(dtype, hq, hkv):
+    # ld == (hq + hkv) * D: rows back to back; single-region tensors take the
+    # flat path, and a K-only tensor must still use gamma_k
+    D = 128
+    p = synth.per_head_problem(f"packed_{hq}_{hkv}", 23, dtype, 33, hq, hkv, D, ld=(hq + hkv) * D)
+    if p.gamma_k is None:
+        p.gamma_k = synth.make_gamma(23, 4, D, dtype)
+    run_per_head(p)
