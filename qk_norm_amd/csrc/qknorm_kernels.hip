@@ -16,7 +16,7 @@
 #define QKNORM_PH_BLOCKS_PER_CU 24 // per-head grid cap, blocks per CU
 #endif
 #ifndef QKNORM_LW_WAVES_PER_CU
-#define QKNORM_LW_WAVES_PER_CU 4096  // layerwise grid cap, waves per CU (large: one row per block)
+#define QKNORM_LW_WAVES_PER_CU 384   // layerwise grid cap, waves per CU
 #endif
 
 namespace qknorm {
@@ -30,6 +30,27 @@ namespace qknorm {
 // g = t*H + h over the Q and K heads of every row (H = hq + hkv); head h < hq
 // is a Q head with gamma_q, otherwise a K head with gamma_k.  (t, h) are kept
 // incrementally so the loop has no integer division.
+
+#ifndef QKNORM_PH_GAMMA_SGPR
+#define QKNORM_PH_GAMMA_SGPR 1
+#endif
+static constexpr bool kGammaSgpr = QKNORM_PH_GAMMA_SGPR != 0;
+
+// The 4*LPH gamma dwords of a head, read at uniform addresses (scalar loads),
+// then lane group `sub` keeps dwords 4*sub .. 4*sub+3.
+template <int LPH>
+__device__ __forceinline__ void gamma_to_lanes(const uint32_t* __restrict__ g, uint32_t sub,
+                                               u32x4& out) {
+  uint32_t w[4 * LPH];
+#pragma unroll
+  for (int k = 0; k < 4 * LPH; ++k) w[k] = g[k];   // all loads first (batched scalar loads)
+#pragma unroll
+  for (uint32_t j = 0; j < LPH; ++j) {
+    const uint32_t mask = 0u - (uint32_t)(sub == j);  // all ones in lane group j
+#pragma unroll
+    for (int i = 0; i < 4; ++i) out[i] |= w[j * 4 + i] & mask;
+  }
+}
 
 // Addresses of one trip: U heads per lane group starting at the wave's head
 // (tw, hw).  CONTIG: rows are back to back with no padding, so the heads form
@@ -92,7 +113,7 @@ struct PerHeadTrip {
 // Software-pipelined: the next trip's loads are issued before the current
 // trip's reduction and stores, so each lane keeps 2*U loads in flight and the
 // dependent arithmetic of one trip overlaps the memory latency of the next.
-template <int DT, int LPH, int U, bool CONTIG>
+template <int DT, int LPH, int U, bool CONTIG, bool ONE>
 __global__ __launch_bounds__(QKNORM_PH_THREADS) void per_head_kernel(
     uint8_t* __restrict__ qkv, uint32_t ld_bytes, uint32_t T, uint32_t H, uint32_t hq,
     uint32_t row_bytes, const uint8_t* __restrict__ gamma_q, const uint8_t* __restrict__ gamma_k,
@@ -104,14 +125,6 @@ __global__ __launch_bounds__(QKNORM_PH_THREADS) void per_head_kernel(
   const uint32_t lane = threadIdx.x & 63;
   const uint32_t sub = lane % LPH;           // 16-byte slot inside the head
   const uint32_t grp = lane / LPH;           // head slot inside the wave step
-
-  // gamma is staged once per block in LDS: a global load of the same few
-  // lines by every wave of the grid would make those lines an L2 hot spot.
-  __shared__ u32x4 g_lds[2][LPH];
-  if (threadIdx.x < LPH) {
-    g_lds[0][threadIdx.x] = gamma_q ? load16(gamma_q + threadIdx.x * 16) : u32x4{0, 0, 0, 0};
-    g_lds[1][threadIdx.x] = gamma_k ? load16(gamma_k + threadIdx.x * 16) : u32x4{0, 0, 0, 0};
-  }
 
   // (tw, hw): row and head of the wave's first head this trip (wave-uniform).
   // T*H < 2^31 is checked on the host, so 32-bit arithmetic suffices; a
@@ -128,12 +141,56 @@ __global__ __launch_bounds__(QKNORM_PH_THREADS) void per_head_kernel(
   cur.setup(qkv, ld_bytes, T, H, hq, row_bytes, live, tw, hw, sub, grp);
 #pragma unroll
   for (uint32_t u = 0; u < U; ++u) vc[u] = stream_load(cur.rs, cur.off[u]);
+  __builtin_amdgcn_sched_barrier(0);           // keep the row loads ahead of the gamma work
 
-  __syncthreads();
+  // gamma: a vector load of the same few lines by every wave of the grid
+  // makes those lines an L2 hot spot.  Short heads (LPH <= 16, at most 64
+  // dwords of gamma) read it with scalar loads through the scalar cache and
+  // hand each lane its 4 dwords with selects, which run while the row loads
+  // are in flight; longer heads stage it once per block in LDS.
   float gq[E], gk[E];
-  unpack<DT>(g_lds[0][sub], gq);
-  unpack<DT>(g_lds[1][sub], gk);
+  if constexpr (kGammaSgpr && LPH <= 16) {
+    // both pointers are valid here (the launcher stands in a readable address
+    // for a NULL gamma, whose values are then never applied), so the loads
+    // are unconditional and stay behind the row loads
+    u32x4 wq = {0, 0, 0, 0}, wk = {0, 0, 0, 0};
+    if constexpr (CONTIG) {
+      // one region only: just the gamma of that region
+      gamma_to_lanes<LPH>(reinterpret_cast<const uint32_t*>(hq ? gamma_q : gamma_k), sub, wq);
+      wk = wq;
+    } else {
+      gamma_to_lanes<LPH>(reinterpret_cast<const uint32_t*>(gamma_q), sub, wq);
+      gamma_to_lanes<LPH>(reinterpret_cast<const uint32_t*>(gamma_k), sub, wk);
+    }
+    unpack<DT>(wq, gq);
+    unpack<DT>(wk, gk);
+  } else {
+    __shared__ u32x4 g_lds[2][LPH];
+    if (threadIdx.x < LPH) {
+      g_lds[0][threadIdx.x] = gamma_q ? load16(gamma_q + threadIdx.x * 16) : u32x4{0, 0, 0, 0};
+      g_lds[1][threadIdx.x] = gamma_k ? load16(gamma_k + threadIdx.x * 16) : u32x4{0, 0, 0, 0};
+    }
+    __syncthreads();
+    unpack<DT>(g_lds[0][sub], gq);
+    unpack<DT>(g_lds[1][sub], gk);
+  }
   if (!live) return;
+
+  if constexpr (ONE) {
+    // the grid covers every head in one trip: no loop, no prefetch
+#pragma unroll
+    for (uint32_t u = 0; u < U; ++u) {
+      float x[E];
+      unpack<DT>(vc[u], x);
+      const float s = group_sum<LPH>(vec_sumsq<DT>(x, 0.f));
+      const float r = rms_scale(s, inv_d, eps);
+      float y[E];
+#pragma unroll
+      for (int e = 0; e < E; ++e) y[e] = (x[e] * (cur.isq[u] ? gq[e] : gk[e])) * r;
+      stream_store(cur.rs, cur.off[u], pack<DT>(y));
+    }
+    return;
+  }
 
   while (true) {
     // next trip: advance by the whole grid (stride_rows rows, stride_heads heads;
@@ -218,6 +275,11 @@ __device__ __forceinline__ void slots_load_gamma(const uint8_t* __restrict__ gam
   }
 }
 
+// Loads are unconditional (an invalid slot gets an offset past the row's
+// descriptor and reads 0), so a whole row's loads can stay in flight while the
+// previous row is being reduced.
+constexpr uint32_t kOutOfRange = 0xFFFFFFF0u;
+
 template <int DT, int VPL>
 __device__ __forceinline__ void slots_load(Rsrc rs, uint32_t reg_off, uint32_t svecs, uint32_t R,
                                            uint32_t wave, uint32_t nw, uint32_t lane,
@@ -227,8 +289,7 @@ __device__ __forceinline__ void slots_load(Rsrc rs, uint32_t reg_off, uint32_t s
 #pragma unroll
   for (int j = 0; j < VPL; ++j) {
     const uint32_t r = wave + i * nw, v = lane + k * 64;
-    S.x[j] = (r < R && v < svecs) ? stream_load(rs, reg_off + (r * svecs + v) * 16)
-                                  : u32x4{0, 0, 0, 0};
+    S.x[j] = stream_load(rs, (r < R && v < svecs) ? reg_off + (r * svecs + v) * 16 : kOutOfRange);
     if (++k == trips) { k = 0; ++i; }
   }
 }
@@ -268,14 +329,13 @@ __device__ __forceinline__ void slots_apply(Rsrc rs, uint32_t reg_off, uint32_t 
 #pragma unroll
   for (int j = 0; j < VPL; ++j) {
     const uint32_t r = wave + i * nw, v = lane + k * 64;
-    if (r < R && v < svecs) {
-      float x[IO::kElems], g[IO::kElems], y[IO::kElems];
-      unpack<DT>(S.x[j], x);
-      unpack<DT>(S.g[j], g);
+    float x[IO::kElems], g[IO::kElems], y[IO::kElems];
+    unpack<DT>(S.x[j], x);
+    unpack<DT>(S.g[j], g);
 #pragma unroll
-      for (int e = 0; e < IO::kElems; ++e) y[e] = (x[e] * g[e]) * scale;
-      stream_store(rs, reg_off + (r * svecs + v) * 16, pack<DT>(y));
-    }
+    for (int e = 0; e < IO::kElems; ++e) y[e] = (x[e] * g[e]) * scale;
+    stream_store(rs, (r < R && v < svecs) ? reg_off + (r * svecs + v) * 16 : kOutOfRange,
+                 pack<DT>(y));
     if (++k == trips) { k = 0; ++i; }
   }
 }
@@ -319,7 +379,49 @@ __device__ __forceinline__ Rsrc row_rsrc(const uint8_t* qkv, uint64_t ld_bytes, 
 }
 
 // Fused layerwise, row kept in registers (VPL slots per region per lane).
-template <int DT, int VPL>
+// A block walks rows blockIdx.x, +gridDim.x, ...; gamma slots are loaded once
+// per block.  Two register sets A and B take alternate rows: while one row is
+// reduced, combined and stored, the next row's loads are already in flight in
+// the other set (no register copies between them, so nothing forces a wait on
+// the previous row's stores).
+template <int QV, int KV>
+struct LwRow {
+  Slots<QV> q;
+  Slots<KV> k;
+};
+
+template <int DT, int QV, int KV>
+__device__ __forceinline__ void lw_issue(uint8_t* qkv, const RowGeom& G, uint32_t t, bool live,
+                                         uint32_t Rq, uint32_t Rk, uint32_t wave, uint32_t nw,
+                                         uint32_t lane, Rsrc& rs, LwRow<QV, KV>& row) {
+  rs = row_rsrc(qkv, G.ld_bytes, live ? t : 0, live ? G.q_vecs + G.k_vecs : 0);
+  slots_load<DT, QV>(rs, 0, G.q_svecs, Rq, wave, nw, lane, row.q);
+  slots_load<DT, KV>(rs, G.q_vecs * 16, G.k_svecs, Rk, wave, nw, lane, row.k);
+}
+
+template <int DT, int QV, int KV>
+__device__ __forceinline__ void lw_finish(const RowGeom& G, Rsrc rs, uint32_t Rq, uint32_t Rk,
+                                          uint32_t wave, uint32_t nw, uint32_t lane, float eps,
+                                          LwRow<QV, KV>& row, const LwRow<QV, KV>& gam,
+                                          float* __restrict__ part) {
+  const uint32_t R = G.nshards;
+  float* pq = part;
+  float* pk = part + R;
+  slots_partials<DT, QV>(G.q_svecs, Rq, wave, nw, lane, row.q, pq);
+  slots_partials<DT, KV>(G.k_svecs, Rk, wave, nw, lane, row.k, pk);
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < QV; ++j) row.q.g[j] = gam.q.g[j];
+#pragma unroll
+  for (int j = 0; j < KV; ++j) row.k.g[j] = gam.k.g[j];
+  if (Rq) slots_apply<DT, QV>(rs, 0, G.q_svecs, Rq, wave, nw, lane, row.q,
+                              rms_scale(combine(pq, R, 1), G.inv_wq, eps));
+  if (Rk) slots_apply<DT, KV>(rs, G.q_vecs * 16, G.k_svecs, Rk, wave, nw, lane, row.k,
+                              rms_scale(combine(pk, R, 1), G.inv_wk, eps));
+}
+
+// QV / KV: register slots per lane for Q and for K (a lane's shard vectors).
+template <int DT, int QV, int KV>
 __global__ __launch_bounds__(512) void layerwise_regs_kernel(
     uint8_t* __restrict__ qkv, RowGeom G, const uint8_t* __restrict__ gamma_q,
     const uint8_t* __restrict__ gamma_k, float eps) {
@@ -329,26 +431,31 @@ __global__ __launch_bounds__(512) void layerwise_regs_kernel(
   const uint32_t nw = blockDim.x >> 6;
   const uint32_t R = G.nshards;
   const uint32_t Rq = G.q_vecs ? R : 0, Rk = G.k_vecs ? R : 0;
-  const uint32_t k_off = G.q_vecs * 16;
-  Slots<VPL> sq, sk;
-  slots_load_gamma<DT, VPL>(gamma_q, G.q_svecs, Rq, wave, nw, lane, sq);
-  slots_load_gamma<DT, VPL>(gamma_k, G.k_svecs, Rk, wave, nw, lane, sk);
-  uint32_t parity = 0;
-  for (uint32_t t = blockIdx.x; t < G.T; t += gridDim.x, parity ^= 1) {
-    const Rsrc rs = row_rsrc(qkv, G.ld_bytes, t, G.q_vecs + G.k_vecs);
-    float* pq = lds + parity * 2 * R;
-    float* pk = pq + R;
-    slots_load<DT, VPL>(rs, 0, G.q_svecs, Rq, wave, nw, lane, sq);
-    slots_load<DT, VPL>(rs, k_off, G.k_svecs, Rk, wave, nw, lane, sk);
-    slots_partials<DT, VPL>(G.q_svecs, Rq, wave, nw, lane, sq, pq);
-    slots_partials<DT, VPL>(G.k_svecs, Rk, wave, nw, lane, sk, pk);
-    __syncthreads();
-    // Double-buffered partials: this buffer is next written two trips later,
-    // after every thread has passed the next trip's barrier.
-    if (Rq) slots_apply<DT, VPL>(rs, 0, G.q_svecs, Rq, wave, nw, lane, sq,
-                                 rms_scale(combine(pq, R, 1), G.inv_wq, eps));
-    if (Rk) slots_apply<DT, VPL>(rs, k_off, G.k_svecs, Rk, wave, nw, lane, sk,
-                                 rms_scale(combine(pk, R, 1), G.inv_wk, eps));
+  const uint32_t stride = gridDim.x;
+
+  uint32_t t = blockIdx.x;
+  LwRow<QV, KV> a, b, gam;
+  Rsrc ra, rb;
+  lw_issue<DT, QV, KV>(qkv, G, t, t < G.T, Rq, Rk, wave, nw, lane, ra, a);
+  slots_load_gamma<DT, QV>(gamma_q, G.q_svecs, Rq, wave, nw, lane, gam.q);
+  slots_load_gamma<DT, KV>(gamma_k, G.k_svecs, Rk, wave, nw, lane, gam.k);
+  if (t >= G.T) return;                        // whole block: no barrier is skipped by part of it
+
+  // LDS partials alternate between two buffers, one per register set: a
+  // buffer is written again only after every thread has passed the barrier of
+  // the row in between.
+  while (true) {
+    const uint32_t t1 = t + stride;
+    const bool more1 = t1 < G.T;
+    lw_issue<DT, QV, KV>(qkv, G, t1, more1, Rq, Rk, wave, nw, lane, rb, b);
+    lw_finish<DT, QV, KV>(G, ra, Rq, Rk, wave, nw, lane, eps, a, gam, lds);
+    if (!more1) break;
+    const uint32_t t2 = t1 + stride;
+    const bool more2 = t2 < G.T;
+    lw_issue<DT, QV, KV>(qkv, G, t2, more2, Rq, Rk, wave, nw, lane, ra, a);
+    lw_finish<DT, QV, KV>(G, rb, Rq, Rk, wave, nw, lane, eps, b, gam, lds + 2 * R);
+    if (!more2) break;
+    t = t2;
   }
 }
 
@@ -448,11 +555,21 @@ static hipError_t launch_per_head_t(const PerHeadArgs& a, hipStream_t s, int cus
   if (blocks < 1) blocks = 1;
   const uint64_t stride = blocks * heads_per_block;   // heads advanced per trip
   const bool contig = a.hq == 0 || a.hkv == 0 ? (a.ld == (int64_t)H * a.head_dim) : false;
-  auto kern = contig ? per_head_kernel<DT, LPH, U, true> : per_head_kernel<DT, LPH, U, false>;
+  const bool one = stride >= total;             // a single trip covers every head
+  auto kern = contig ? (one ? per_head_kernel<DT, LPH, U, true, true>
+                            : per_head_kernel<DT, LPH, U, true, false>)
+                     : (one ? per_head_kernel<DT, LPH, U, false, true>
+                            : per_head_kernel<DT, LPH, U, false, false>);
+  // A NULL gamma serves a region without heads; stand in the other gamma (or
+  // the first head of qkv, at least one head long) so gamma reads stay valid.
+  const void* gq = a.gamma_q ? a.gamma_q : (a.gamma_k ? a.gamma_k : a.qkv);
+  const void* gk = a.gamma_k ? a.gamma_k : gq;
+  const bool gsgpr = kGammaSgpr && LPH <= 16;
   hipLaunchKernelGGL(kern, dim3((uint32_t)blocks), dim3(kBlock), 0, s, (uint8_t*)a.qkv,
                      (uint32_t)(a.ld * es), (uint32_t)a.T, (uint32_t)H, (uint32_t)a.hq,
-                     (uint32_t)(H * a.head_dim * es), (const uint8_t*)a.gamma_q,
-                     (const uint8_t*)a.gamma_k, a.eps, 1.0f / (float)a.head_dim,
+                     (uint32_t)(H * a.head_dim * es),
+                     (const uint8_t*)(gsgpr ? gq : a.gamma_q),
+                     (const uint8_t*)(gsgpr ? gk : a.gamma_k), a.eps, 1.0f / (float)a.head_dim,
                      contig ? 0u : (uint32_t)(stride / H),
                      contig ? (uint32_t)stride : (uint32_t)(stride % H));
   return hipGetLastError();
@@ -490,14 +607,13 @@ static RowGeom make_geom(int64_t T, int64_t ld, int64_t wq, int64_t wk, int32_t 
   return G;
 }
 
-// Waves per block and register slots per lane for a layerwise geometry.
-static void layerwise_shape(const RowGeom& G, uint32_t* nw, uint32_t* vpl) {
+// Waves per block and register slots per lane (Q and K) for a layerwise geometry.
+static void layerwise_shape(const RowGeom& G, uint32_t* nw, uint32_t* qv, uint32_t* kv) {
   const uint32_t w = G.nshards < 8 ? G.nshards : 8;
   const uint32_t per_wave = (G.nshards + w - 1) / w;
-  const uint32_t q = G.q_vecs ? per_wave * ((G.q_svecs + 63) / 64) : 0;
-  const uint32_t k = G.k_vecs ? per_wave * ((G.k_svecs + 63) / 64) : 0;
   *nw = w;
-  *vpl = q > k ? q : k;
+  *qv = G.q_vecs ? per_wave * ((G.q_svecs + 63) / 64) : 0;
+  *kv = G.k_vecs ? per_wave * ((G.k_svecs + 63) / 64) : 0;
 }
 
 static uint32_t row_blocks(uint32_t T, uint32_t nw, int cus) {
@@ -507,24 +623,41 @@ static uint32_t row_blocks(uint32_t T, uint32_t nw, int cus) {
   return (uint32_t)(b < 1 ? 1 : b);
 }
 
-template <int DT, int VPL>
+template <int DT, int QV, int KV>
 static hipError_t launch_lw_regs(const RowGeom& G, uint32_t nw, const LayerwiseArgs& a,
                                  hipStream_t s, int cus) {
-  hipLaunchKernelGGL((layerwise_regs_kernel<DT, VPL>), dim3(row_blocks(G.T, nw, cus)),
+  hipLaunchKernelGGL((layerwise_regs_kernel<DT, QV, KV>), dim3(row_blocks(G.T, nw, cus)),
                      dim3(nw * 64), (size_t)4 * G.nshards * sizeof(float), s, (uint8_t*)a.qkv, G,
                      (const uint8_t*)a.gamma_q, (const uint8_t*)a.gamma_k, a.eps);
   return hipGetLastError();
 }
 
+static int slot_class(uint32_t n) { return n <= 1 ? 1 : n <= 2 ? 2 : n <= 4 ? 4 : 0; }
+
+template <int DT, int QV>
+static hipError_t launch_lw_regs_k(const RowGeom& G, uint32_t nw, int kc, const LayerwiseArgs& a,
+                                   hipStream_t s, int cus) {
+  switch (kc) {
+    case 1: return launch_lw_regs<DT, QV, 1>(G, nw, a, s, cus);
+    case 2: return launch_lw_regs<DT, QV, 2>(G, nw, a, s, cus);
+    default: return launch_lw_regs<DT, QV, 4>(G, nw, a, s, cus);
+  }
+}
+
 template <int DT>
 static hipError_t launch_layerwise_dt(const LayerwiseArgs& a, hipStream_t s, int cus) {
   const RowGeom G = make_geom(a.T, a.ld, a.wq, a.wk, a.nshards, IoTraits<DT>::kBytes);
-  uint32_t nw, vpl;
-  layerwise_shape(G, &nw, &vpl);
-  if (vpl <= 1) return launch_lw_regs<DT, 1>(G, nw, a, s, cus);
-  if (vpl <= 2) return launch_lw_regs<DT, 2>(G, nw, a, s, cus);
-  if (vpl <= 4) return launch_lw_regs<DT, 4>(G, nw, a, s, cus);
-  if (vpl <= 8) return launch_lw_regs<DT, 8>(G, nw, a, s, cus);
+  uint32_t nw, qv, kv;
+  layerwise_shape(G, &nw, &qv, &kv);
+  const int qc = slot_class(qv), kc = slot_class(kv);
+  if (qc && kc) {
+    switch (qc) {
+      case 1: return launch_lw_regs_k<DT, 1>(G, nw, kc, a, s, cus);
+      case 2: return launch_lw_regs_k<DT, 2>(G, nw, kc, a, s, cus);
+      default: return launch_lw_regs_k<DT, 4>(G, nw, kc, a, s, cus);
+    }
+  }
+  // rows too wide for the register slots
   hipLaunchKernelGGL((layerwise_stream_kernel<DT>), dim3(row_blocks(G.T, nw, cus)), dim3(nw * 64),
                      (size_t)4 * G.nshards * sizeof(float), s, (uint8_t*)a.qkv, G,
                      (const uint8_t*)a.gamma_q, (const uint8_t*)a.gamma_k, a.eps);
