@@ -13,7 +13,7 @@
 #define QKNORM_PH_UNROLL 2         // heads per lane group per loop trip
 #endif
 #ifndef QKNORM_PH_BLOCKS_PER_CU
-#define QKNORM_PH_BLOCKS_PER_CU 24 // per-head grid cap, blocks per CU
+#define QKNORM_PH_BLOCKS_PER_CU 160 // per-head grid cap, blocks per CU (one trip for most sizes)
 #endif
 #ifndef QKNORM_LW_WAVES_PER_CU
 #define QKNORM_LW_WAVES_PER_CU 384   // layerwise grid cap, waves per CU
@@ -144,26 +144,20 @@ __global__ __launch_bounds__(QKNORM_PH_THREADS) void per_head_kernel(
   __builtin_amdgcn_sched_barrier(0);           // keep the row loads ahead of the gamma work
 
   // gamma: a vector load of the same few lines by every wave of the grid
-  // makes those lines an L2 hot spot.  Short heads (LPH <= 16, at most 64
-  // dwords of gamma) read it with scalar loads through the scalar cache and
-  // hand each lane its 4 dwords with selects, which run while the row loads
-  // are in flight; longer heads stage it once per block in LDS.
+  // makes those lines an L2 hot spot.  A single-region tensor with short heads
+  // (LPH <= 16, at most 64 dwords of gamma) reads its one gamma with scalar
+  // loads through the scalar cache and hands each lane its 4 dwords with
+  // selects, which run while the row loads are in flight.  Otherwise (two
+  // gammas, or longer heads) gamma is staged once per block in LDS, which
+  // measured faster there.
   float gq[E], gk[E];
-  if constexpr (kGammaSgpr && LPH <= 16) {
-    // both pointers are valid here (the launcher stands in a readable address
-    // for a NULL gamma, whose values are then never applied), so the loads
-    // are unconditional and stay behind the row loads
-    u32x4 wq = {0, 0, 0, 0}, wk = {0, 0, 0, 0};
-    if constexpr (CONTIG) {
-      // one region only: just the gamma of that region
-      gamma_to_lanes<LPH>(reinterpret_cast<const uint32_t*>(hq ? gamma_q : gamma_k), sub, wq);
-      wk = wq;
-    } else {
-      gamma_to_lanes<LPH>(reinterpret_cast<const uint32_t*>(gamma_q), sub, wq);
-      gamma_to_lanes<LPH>(reinterpret_cast<const uint32_t*>(gamma_k), sub, wk);
-    }
-    unpack<DT>(wq, gq);
-    unpack<DT>(wk, gk);
+  if constexpr (kGammaSgpr && CONTIG && LPH <= 16) {
+    // the launcher stands in a readable address for a NULL gamma, so the
+    // loads are unconditional and stay behind the row loads
+    u32x4 w = {0, 0, 0, 0};
+    gamma_to_lanes<LPH>(reinterpret_cast<const uint32_t*>(hq ? gamma_q : gamma_k), sub, w);
+    unpack<DT>(w, gq);
+    unpack<DT>(w, gk);
   } else {
     __shared__ u32x4 g_lds[2][LPH];
     if (threadIdx.x < LPH) {
@@ -496,33 +490,170 @@ __global__ __launch_bounds__(512) void layerwise_stream_kernel(
   }
 }
 
-// Phase A: one wave per (row, shard) of Q and of K; lane 0 stores the partial
-// at part[r*T + t].  Work item i < T*R is Q (row i / R, shard i % R), the
-// next T*R items are K.
+// Phase A.  A wave takes one shard of one region (Q or K) over a block of 32
+// consecutive rows and ends with lane j holding the partial of row t0 + j,
+// stored with one coalesced 128-byte write at part[r*T + t0 ...].  (32 rows
+// keep the block's descriptor below 2^31 bytes, well under the out-of-range
+// offset used for masked lanes.)
+//
+// A shard of svecs >= 64 vectors is reduced exactly like the fused kernel
+// (lane l takes vectors l, l+64, ..., then the 64-lane sum).  A shard of
+// fewer vectors uses lane groups of LG = next power of two >= svecs lanes,
+// 64/LG rows per step; lane i of a group takes vector i, and the LG-lane sum
+// equals the 64-lane sum of the fused kernel bit for bit, because the lanes it
+// leaves out hold exact zeros (x + 0 == x).
+__device__ __forceinline__ float group_sum_n(float v, uint32_t lg) {
+  switch (lg) {                                // wave-uniform
+    case 2: return group_sum<2>(v);
+    case 4: return group_sum<4>(v);
+    case 8: return group_sum<8>(v);
+    case 16: return group_sum<16>(v);
+    case 32: return group_sum<32>(v);
+    default: return group_sum<64>(v);
+  }
+}
+
+constexpr uint32_t kRowBlock = 32;
+
 template <int DT>
 __global__ __launch_bounds__(256) void partial_sumsq_kernel(const uint8_t* __restrict__ qkv,
                                                             RowGeom G, float* __restrict__ part_q,
                                                             float* __restrict__ part_k) {
+  using IO = IoTraits<DT>;
   const uint32_t lane = threadIdx.x & 63;
-  const uint64_t nq = G.q_vecs ? (uint64_t)G.T * G.nshards : 0;
-  const uint64_t nk = G.k_vecs ? (uint64_t)G.T * G.nshards : 0;
-  const uint64_t total = nq + nk;
-  const uint64_t nwaves = ((uint64_t)gridDim.x * blockDim.x) >> 6;
-  for (uint64_t i = uniform((blockIdx.x * blockDim.x + threadIdx.x) >> 6); i < total; i += nwaves) {
+  const uint32_t R = G.nshards;
+  const uint32_t nblk = (G.T + kRowBlock - 1) / kRowBlock;
+  const uint32_t nq = G.q_vecs ? R * nblk : 0;
+  const uint32_t nk = G.k_vecs ? R * nblk : 0;
+  const uint32_t nwaves = (gridDim.x * blockDim.x) >> 6;
+  for (uint32_t i = uniform((blockIdx.x * blockDim.x + threadIdx.x) >> 6); i < nq + nk;
+       i += nwaves) {
     const bool isk = i >= nq;
-    const uint64_t w = isk ? i - nq : i;
-    const uint32_t t = (uint32_t)(w / G.nshards), r = (uint32_t)(w % G.nshards);
+    const uint32_t w = isk ? i - nq : i;
+    const uint32_t r = w % R, blk = w / R;
     const uint32_t svecs = isk ? G.k_svecs : G.q_svecs;
-    const Rsrc rs = row_rsrc(qkv, G.ld_bytes, t, G.q_vecs + G.k_vecs);
-    const float s = shard_sumsq_stream<DT>(rs, ((isk ? G.q_vecs : 0) + r * svecs) * 16, svecs, lane);
-    if (lane == 0) (isk ? part_k : part_q)[(uint64_t)r * G.T + t] = s;
+    const uint32_t shard_off = ((isk ? G.q_vecs : 0) + r * svecs) * 16;
+    uint32_t lg = 2;
+    while (lg < svecs && lg < 64) lg <<= 1;
+    const uint32_t rps = 64 / lg;              // rows per step
+    const uint32_t trips = (svecs + lg - 1) / lg;
+    const uint32_t grp = lane / lg, li = lane % lg;
+    const uint32_t t0 = blk * kRowBlock;
+    const uint32_t rows = G.T - t0 < kRowBlock ? G.T - t0 : kRowBlock;
+    // descriptor over this block's rows (below 32 rows * 64 MiB = 2^31 bytes)
+    const Rsrc rs = make_rsrc(qkv + (uint64_t)t0 * G.ld_bytes,
+                              (uint64_t)(rows - 1) * G.ld_bytes + (uint64_t)(G.q_vecs + G.k_vecs) * 16);
+    float mine = 0.f;
+    for (uint32_t j0 = 0; j0 < rows; j0 += rps) {
+      const uint32_t j = j0 + grp;             // this lane group's row in the block
+      float acc = 0.f;
+      for (uint32_t k = 0; k < trips; ++k) {
+        const uint32_t v = li + k * lg;
+        float x[IO::kElems];
+        unpack<DT>(stream_load(rs, (j < rows && v < svecs)
+                                       ? (uint32_t)(j * G.ld_bytes) + shard_off + v * 16
+                                       : kOutOfRange), x);
+        acc = vec_sumsq<DT>(x, acc);
+      }
+      const float sum = group_sum_n(acc, lg);
+      for (uint32_t g = 0; g < rps; ++g) {
+        const float sg = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sum), g * lg));
+        mine = lane == j0 + g ? sg : mine;
+      }
+    }
+    if (lane < rows) (isk ? part_k : part_q)[(uint64_t)r * G.T + t0 + lane] = mine;
   }
 }
 
-// Phase C: one block per row (grid-stride), flat 16-byte vectors over Q then
-// K.  scale = rsq((sum over r < nparts of part[r*T + t]) / norm_w + eps).
+// Phase C.  A block takes kApplyRows consecutive rows.  First the rows'
+// scales: thread i < kApplyRows adds row t0+i's partials in order (r = 0 ..
+// nparts-1; each r one contiguous read across those threads), takes
+// rsq((sum)/norm_w + eps) and leaves it in LDS.  Then every row is applied
+// with flat 16-byte vectors over Q then K; thread tid takes vectors tid,
+// tid+512, ... of every row, so its gamma vectors stay in registers (VPT of
+// them) for all the block's rows.
+#ifndef QKNORM_APPLY_ROWS
+#define QKNORM_APPLY_ROWS 2        // rows per phase-C block
+#endif
+constexpr uint32_t kApplyRows = QKNORM_APPLY_ROWS;
+
+template <int VPT>
+__device__ __forceinline__ void apply_rows_load(Rsrc rs, uint32_t tid, uint32_t nt, uint32_t nv,
+                                                u32x4 (&x)[VPT]) {
+#pragma unroll
+  for (int k = 0; k < VPT; ++k) {
+    const uint32_t v = tid + k * nt;
+    x[k] = stream_load(rs, v < nv ? v * 16 : kOutOfRange);
+  }
+}
+
+template <int DT, int VPT>
+__device__ __forceinline__ void apply_rows_store(Rsrc rs, uint32_t tid, uint32_t nt,
+                                                 uint32_t q_vecs, uint32_t nv,
+                                                 const u32x4 (&x)[VPT], const u32x4 (&g)[VPT],
+                                                 float sq, float sk) {
+  using IO = IoTraits<DT>;
+#pragma unroll
+  for (int k = 0; k < VPT; ++k) {
+    const uint32_t v = tid + k * nt;
+    float xf[IO::kElems], gf[IO::kElems], y[IO::kElems];
+    unpack<DT>(x[k], xf);
+    unpack<DT>(g[k], gf);
+    const float sc = v < q_vecs ? sq : sk;
+#pragma unroll
+    for (int e = 0; e < IO::kElems; ++e) y[e] = (xf[e] * gf[e]) * sc;
+    stream_store(rs, v < nv ? v * 16 : kOutOfRange, pack<DT>(y));
+  }
+}
+
+template <int DT, int VPT>
+__global__ __launch_bounds__(512) void apply_scalar_kernel(
+    uint8_t* __restrict__ qkv, uint64_t ld_bytes, uint32_t T, uint32_t q_vecs, uint32_t k_vecs,
+    const float* __restrict__ part_q, const float* __restrict__ part_k, uint32_t nparts,
+    float inv_norm_wq, float inv_norm_wk, const uint8_t* __restrict__ gamma_q,
+    const uint8_t* __restrict__ gamma_k, float eps) {
+  using IO = IoTraits<DT>;
+  __shared__ float scale[2][kApplyRows];
+  const uint32_t tid = threadIdx.x, nt = blockDim.x;
+  const uint32_t nv = q_vecs + k_vecs;
+  u32x4 g[VPT];
+#pragma unroll
+  for (int k = 0; k < VPT; ++k) {
+    const uint32_t v = tid + k * nt;
+    g[k] = v < q_vecs ? load16(gamma_q + (uint64_t)v * 16)
+                      : (v < nv ? load16(gamma_k + (uint64_t)(v - q_vecs) * 16) : u32x4{0, 0, 0, 0});
+  }
+  for (uint32_t t0 = blockIdx.x * kApplyRows; t0 < T; t0 += gridDim.x * kApplyRows) {
+    const uint32_t rows = T - t0 < kApplyRows ? T - t0 : kApplyRows;
+    __syncthreads();                           // previous rows are done with `scale`
+    if (tid < rows) {
+      if (q_vecs) scale[0][tid] = rms_scale(combine(part_q + t0 + tid, nparts, T), inv_norm_wq, eps);
+      if (k_vecs) scale[1][tid] = rms_scale(combine(part_k + t0 + tid, nparts, T), inv_norm_wk, eps);
+    }
+    __syncthreads();
+    // rows alternate between two register sets: row j+1's loads are in
+    // flight while row j is scaled and stored
+    u32x4 xa[VPT], xb[VPT];
+    Rsrc ra = row_rsrc(qkv, ld_bytes, t0, nv), rb;
+    apply_rows_load<VPT>(ra, tid, nt, nv, xa);
+    for (uint32_t j = 0; j < rows; j += 2) {
+      const bool more1 = j + 1 < rows;
+      rb = row_rsrc(qkv, ld_bytes, more1 ? t0 + j + 1 : t0, more1 ? nv : 0);
+      apply_rows_load<VPT>(rb, tid, nt, nv, xb);
+      apply_rows_store<DT, VPT>(ra, tid, nt, q_vecs, nv, xa, g, scale[0][j], scale[1][j]);
+      if (!more1) break;
+      const bool more2 = j + 2 < rows;
+      ra = row_rsrc(qkv, ld_bytes, more2 ? t0 + j + 2 : t0, more2 ? nv : 0);
+      apply_rows_load<VPT>(ra, tid, nt, nv, xa);
+      apply_rows_store<DT, VPT>(rb, tid, nt, q_vecs, nv, xb, g, scale[0][j + 1], scale[1][j + 1]);
+    }
+  }
+}
+
+// Phase C for rows wider than 4 vectors per thread: one block per row, gamma
+// re-read for each row.
 template <int DT>
-__global__ __launch_bounds__(256) void apply_scalar_kernel(
+__global__ __launch_bounds__(256) void apply_scalar_wide_kernel(
     uint8_t* __restrict__ qkv, uint64_t ld_bytes, uint32_t T, uint32_t q_vecs, uint32_t k_vecs,
     const float* __restrict__ part_q, const float* __restrict__ part_k, uint32_t nparts,
     float inv_norm_wq, float inv_norm_wk, const uint8_t* __restrict__ gamma_q,
@@ -564,7 +695,7 @@ static hipError_t launch_per_head_t(const PerHeadArgs& a, hipStream_t s, int cus
   // the first head of qkv, at least one head long) so gamma reads stay valid.
   const void* gq = a.gamma_q ? a.gamma_q : (a.gamma_k ? a.gamma_k : a.qkv);
   const void* gk = a.gamma_k ? a.gamma_k : gq;
-  const bool gsgpr = kGammaSgpr && LPH <= 16;
+  const bool gsgpr = kGammaSgpr && contig && LPH <= 16;
   hipLaunchKernelGGL(kern, dim3((uint32_t)blocks), dim3(kBlock), 0, s, (uint8_t*)a.qkv,
                      (uint32_t)(a.ld * es), (uint32_t)a.T, (uint32_t)H, (uint32_t)a.hq,
                      (uint32_t)(H * a.head_dim * es),
@@ -672,7 +803,8 @@ hipError_t launch_layerwise(const LayerwiseArgs& a, hipStream_t s, int cus) {
 template <int DT>
 static hipError_t launch_partial_dt(const PartialArgs& a, hipStream_t s, int cus) {
   const RowGeom G = make_geom(a.T, a.ld, a.wq, a.wk, a.nshards, IoTraits<DT>::kBytes);
-  const uint64_t items = (uint64_t)a.T * a.nshards * ((a.wq > 0) + (a.wk > 0));
+  const uint64_t items = (uint64_t)((a.T + kRowBlock - 1) / kRowBlock) * a.nshards *
+                         ((a.wq > 0) + (a.wk > 0));
   uint64_t blocks = (items + 3) / 4;
   const uint64_t cap = (uint64_t)cus * (QKNORM_LW_WAVES_PER_CU / 4);
   if (blocks > cap) blocks = cap;
@@ -686,18 +818,38 @@ hipError_t launch_partial_sumsq(const PartialArgs& a, hipStream_t s, int cus) {
   return a.dtype == kBF16 ? launch_partial_dt<kBF16>(a, s, cus) : launch_partial_dt<kF32>(a, s, cus);
 }
 
+template <int DT, int VPT>
+static hipError_t launch_apply_rows(const ApplyArgs& a, hipStream_t s, int cus, uint32_t qv,
+                                    uint32_t kv, float iq, float ik) {
+  uint64_t blocks = ((uint64_t)a.T + kApplyRows - 1) / kApplyRows;
+  const uint64_t cap = (uint64_t)cus * (QKNORM_LW_WAVES_PER_CU / 8);
+  if (blocks > cap) blocks = cap;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL((apply_scalar_kernel<DT, VPT>), dim3((uint32_t)blocks), dim3(512), 0, s,
+                     (uint8_t*)a.qkv, (uint64_t)(a.ld * IoTraits<DT>::kBytes), (uint32_t)a.T, qv, kv,
+                     a.part_q, a.part_k, (uint32_t)a.nparts, iq, ik, (const uint8_t*)a.gamma_q,
+                     (const uint8_t*)a.gamma_k, a.eps);
+  return hipGetLastError();
+}
+
 template <int DT>
 static hipError_t launch_apply_dt(const ApplyArgs& a, hipStream_t s, int cus) {
   const int esize = IoTraits<DT>::kBytes;
+  const uint32_t qv = (uint32_t)(a.wq * esize / 16), kv = (uint32_t)(a.wk * esize / 16);
+  const float iq = a.norm_wq ? 1.0f / (float)a.norm_wq : 0.f;
+  const float ik = a.norm_wk ? 1.0f / (float)a.norm_wk : 0.f;
+  const uint32_t vpt = (qv + kv + 511) / 512;
+  if (vpt <= 1) return launch_apply_rows<DT, 1>(a, s, cus, qv, kv, iq, ik);
+  if (vpt <= 2) return launch_apply_rows<DT, 2>(a, s, cus, qv, kv, iq, ik);
+  if (vpt <= 3) return launch_apply_rows<DT, 3>(a, s, cus, qv, kv, iq, ik);
+  if (vpt <= 4) return launch_apply_rows<DT, 4>(a, s, cus, qv, kv, iq, ik);
   uint64_t blocks = a.T;
   const uint64_t cap = (uint64_t)cus * (QKNORM_LW_WAVES_PER_CU / 4);
   if (blocks > cap) blocks = cap;
   if (blocks < 1) blocks = 1;
-  hipLaunchKernelGGL((apply_scalar_kernel<DT>), dim3((uint32_t)blocks), dim3(256), 0, s,
-                     (uint8_t*)a.qkv, (uint64_t)(a.ld * esize), (uint32_t)a.T, (uint32_t)(a.wq * esize / 16),
-                     (uint32_t)(a.wk * esize / 16), a.part_q, a.part_k, (uint32_t)a.nparts,
-                     a.norm_wq ? 1.0f / (float)a.norm_wq : 0.f,
-                     a.norm_wk ? 1.0f / (float)a.norm_wk : 0.f, (const uint8_t*)a.gamma_q,
+  hipLaunchKernelGGL((apply_scalar_wide_kernel<DT>), dim3((uint32_t)blocks), dim3(256), 0, s,
+                     (uint8_t*)a.qkv, (uint64_t)(a.ld * esize), (uint32_t)a.T, qv, kv, a.part_q,
+                     a.part_k, (uint32_t)a.nparts, iq, ik, (const uint8_t*)a.gamma_q,
                      (const uint8_t*)a.gamma_k, a.eps);
   return hipGetLastError();
 }
