@@ -108,3 +108,24 @@ def ulp_histogram(got: np.ndarray, ref_rounded: np.ndarray, dtype):
 def assert_bytes_equal(a: np.ndarray, b: np.ndarray, label=""):
     if not np.array_equal(np.ascontiguousarray(a).view(np.uint8), np.ascontiguousarray(b).view(np.uint8)):
         raise AssertionError(f"{label}: bytes differ")
+
+
+def upload_rows(seed, T, ld, dtype, chunk=8192, **kw):
+    """A seeded [T, ld] input built chunk by chunk on the GPU (host memory stays
+    bounded); any row can be regenerated on its own with synth.make_x(row_start=...)."""
+    t = torch.empty((T, ld), dtype=torch_dtype(dtype), device="cuda")
+    for r0 in range(0, T, chunk):
+        n = min(chunk, T - r0)
+        t[r0:r0 + n].copy_(host_to_device(synth.make_x(seed, n, ld, dtype, row_start=r0, **kw), dtype))
+    return t
+
+
+def sample_rows(T, n=40, seed=11):
+    rng = np.random.default_rng(seed)
+    rows = set(rng.choice(T, size=min(n, T), replace=False).tolist()) | {0, T - 1}
+    return np.array(sorted(rows))
+
+
+def host_rows(seed, rows, ld, dtype, **kw):
+    """The same rows regenerated on the host."""
+    return np.concatenate([synth.make_x(seed, 1, ld, dtype, row_start=int(r), **kw) for r in rows])
