@@ -24,12 +24,12 @@ namespace qknorm {
 // =================================================================== per head
 //
 // A head of D values is LPH lanes x 16 bytes (bf16 D=128: 16 lanes, one DPP
-// row).  A wave covers 64/LPH consecutive heads per step and U steps per loop
-// trip, so each trip streams U contiguous 1 KiB runs (for bf16 D=128) and has
-// U independent 16-byte loads in flight per lane.  Heads are numbered
-// g = t*H + h over the Q and K heads of every row (H = hq + hkv); head h < hq
-// is a Q head with gamma_q, otherwise a K head with gamma_k.  (t, h) are kept
-// incrementally so the loop has no integer division.
+// row).  The heads are split into two regions, the Q heads of every row and
+// the K heads of every row; a block works in one region only, so each wave
+// has a single, uniform gamma.  Inside a region, heads are numbered
+// g = t*H + h (H heads per row), a wave covers 64/LPH consecutive heads per
+// step and U steps per trip, and (t, h) are kept incrementally, so the loop
+// has no integer division.
 
 #ifndef QKNORM_PH_GAMMA_SGPR
 #define QKNORM_PH_GAMMA_SGPR 1
@@ -52,72 +52,98 @@ __device__ __forceinline__ void gamma_to_lanes(const uint32_t* __restrict__ g, u
   }
 }
 
+// One region of heads: H per row, starting `col_bytes` into each row, with
+// its gamma; `blocks` blocks of the grid, which advance (stride_rows,
+// stride_heads) per trip.
+struct PhRegion {
+  const uint8_t* gamma;
+  uint32_t H;
+  uint32_t col_bytes;
+  uint32_t blocks;
+  uint32_t stride_rows, stride_heads;
+};
+
 // Addresses of one trip: U heads per lane group starting at the wave's head
-// (tw, hw).  CONTIG: rows are back to back with no padding, so the heads form
-// one flat array and no row wrap is needed.
+// (tw, hw) of the region.  CONTIG: rows hold just this region's heads, back
+// to back, so the heads form one flat array (tw = 0, hw = flat index).
 //
 // Loads and stores are issued unconditionally (straight-line code, so the
 // compiler can keep the next trip's loads in flight while this trip is being
 // computed).  The descriptor spans exactly the bytes this trip may touch; a
 // lane without a head gets an offset past that span, and a trip past the end
 // of the tensor gets an empty descriptor, so the hardware range check turns
-// those accesses into no-ops (loads return 0, stores are dropped).
+// those accesses into no-ops (loads return 0, stores are dropped).  Every
+// span is below 2^31 bytes (at most CH/H + 2 rows of at most 64 MiB).
 template <int LPH, int U, bool CONTIG>
 struct PerHeadTrip {
   Rsrc rs;
   uint32_t off[U];
-  bool isq[U];
 
   static constexpr uint32_t kNoHead = 0xFFFFFFF0u;
 
   __device__ __forceinline__ void setup(uint8_t* qkv, uint32_t ld_bytes, uint32_t T, uint32_t H,
-                                        uint32_t hq, uint32_t row_bytes, bool live, uint32_t tw,
-                                        uint32_t hw, uint32_t sub, uint32_t grp) {
+                                        uint32_t col_bytes, bool live, uint32_t tw, uint32_t hw,
+                                        uint32_t sub, uint32_t grp) {
     constexpr uint32_t HPW = 64 / LPH;
     constexpr uint32_t CH = HPW * U;
     constexpr uint32_t head_bytes = LPH * 16;
     tw = live ? tw : 0;
     hw = live ? hw : 0;
-    // bytes from the wave's first head to the end of the tensor (the last row
-    // ends with its K heads); CONTIG: tw = 0 and hw is the flat head index
-    const uint64_t first = (uint64_t)tw * ld_bytes + (CONTIG ? (uint64_t)hw * head_bytes : 0);
-    const uint64_t rest = CONTIG ? ((uint64_t)T * H - hw) * head_bytes
-                                 : (uint64_t)(T - 1 - tw) * ld_bytes + row_bytes;
-    // bytes this trip can reach: CH heads, possibly wrapping into later rows
-    uint64_t span;
-    if constexpr (CONTIG)
+    uint64_t first, rest, span;
+    if constexpr (CONTIG) {
+      first = (uint64_t)hw * head_bytes;
+      rest = ((uint64_t)T * H - hw) * head_bytes;
       span = (uint64_t)CH * head_bytes;
-    else
-      span = (uint64_t)((hw + CH - 1) / H) * ld_bytes + row_bytes;
+    } else {
+      // from the wave's first head to the end of the region in the last row
+      first = (uint64_t)tw * ld_bytes + col_bytes;
+      rest = (uint64_t)(T - 1 - tw) * ld_bytes + (uint64_t)H * head_bytes;
+      span = (uint64_t)((hw + CH - 1) / H) * ld_bytes + (uint64_t)H * head_bytes;
+    }
     rs = make_rsrc(qkv + first, live ? (span < rest ? span : rest) : 0);
 #pragma unroll
     for (uint32_t u = 0; u < U; ++u) {
       const uint32_t k = u * HPW + grp;      // head index from the wave's first head
       if constexpr (CONTIG) {
-        const bool ok = hw + k < T * H;
-        isq[u] = hq != 0;                    // one region only: all Q or all K heads
-        off[u] = ok ? k * head_bytes + sub * 16 : kNoHead;
+        off[u] = hw + k < T * H ? k * head_bytes + sub * 16 : kNoHead;
       } else {
         uint32_t hu = hw + k, dt = 0;
         if (hu >= H) {                       // wrap into the following row(s)
           dt = hu / H;
           hu -= dt * H;
         }
-        isq[u] = hu < hq;
         off[u] = tw + dt < T ? dt * ld_bytes + hu * head_bytes + sub * 16 : kNoHead;
       }
     }
   }
 };
 
-// Software-pipelined: the next trip's loads are issued before the current
-// trip's reduction and stores, so each lane keeps 2*U loads in flight and the
-// dependent arithmetic of one trip overlaps the memory latency of the next.
+template <int DT, int LPH, int U>
+__device__ __forceinline__ void per_head_apply(const u32x4 (&v)[U], const float (&g)[IoTraits<DT>::kElems],
+                                               float inv_d, float eps, Rsrc rs,
+                                               const uint32_t (&off)[U]) {
+  using IO = IoTraits<DT>;
+  constexpr int E = IO::kElems;
+#pragma unroll
+  for (uint32_t u = 0; u < U; ++u) {
+    float x[E];
+    unpack<DT>(v[u], x);
+    const float s = group_sum<LPH>(vec_sumsq<DT>(x, 0.f));
+    const float r = rms_scale(s, inv_d, eps);
+    float y[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) y[e] = (x[e] * g[e]) * r;
+    stream_store(rs, off[u], pack<DT>(y));
+  }
+}
+
+// ONE: the grid covers every head in one trip, so there is no loop.
+// Otherwise the loop is software-pipelined: the next trip's loads are issued
+// before the current trip's reduction and stores.
 template <int DT, int LPH, int U, bool CONTIG, bool ONE>
 __global__ __launch_bounds__(QKNORM_PH_THREADS) void per_head_kernel(
-    uint8_t* __restrict__ qkv, uint32_t ld_bytes, uint32_t T, uint32_t H, uint32_t hq,
-    uint32_t row_bytes, const uint8_t* __restrict__ gamma_q, const uint8_t* __restrict__ gamma_k,
-    float eps, float inv_d, uint32_t stride_rows, uint32_t stride_heads) {
+    uint8_t* __restrict__ qkv, uint32_t ld_bytes, uint32_t T, PhRegion r0, PhRegion r1,
+    float eps, float inv_d) {
   using IO = IoTraits<DT>;
   using Trip = PerHeadTrip<LPH, U, CONTIG>;
   constexpr int E = IO::kElems;
@@ -126,88 +152,65 @@ __global__ __launch_bounds__(QKNORM_PH_THREADS) void per_head_kernel(
   const uint32_t sub = lane % LPH;           // 16-byte slot inside the head
   const uint32_t grp = lane / LPH;           // head slot inside the wave step
 
+  // this block's region (uniform)
+  const bool second = blockIdx.x >= r0.blocks;
+  const uint8_t* gamma = second ? r1.gamma : r0.gamma;
+  const uint32_t H = second ? r1.H : r0.H;
+  const uint32_t col = second ? r1.col_bytes : r0.col_bytes;
+  const uint32_t stride_rows = second ? r1.stride_rows : r0.stride_rows;
+  const uint32_t stride_heads = second ? r1.stride_heads : r0.stride_heads;
+  const uint32_t lblock = blockIdx.x - (second ? r0.blocks : 0);
+
   // (tw, hw): row and head of the wave's first head this trip (wave-uniform).
-  // T*H < 2^31 is checked on the host, so 32-bit arithmetic suffices; a
-  // single-region tensor starts at row 0 with the flat head index in hw.
-  const uint32_t wave = uniform((blockIdx.x * blockDim.x + threadIdx.x) >> 6);
+  // T*H < 2^31 is checked on the host, so 32-bit arithmetic suffices.
+  const uint32_t wave = uniform(lblock * (blockDim.x >> 6) + (threadIdx.x >> 6));
   const uint32_t g0 = wave * CH;
   uint32_t tw = CONTIG ? 0 : g0 / H;
   uint32_t hw = CONTIG ? g0 : g0 - tw * H;
   const bool live = CONTIG ? hw < T * H : tw < T;
 
-  // first trip's loads go out before the barrier so it overlaps their latency
+  // first trip's loads go out before any gamma work
   Trip cur;
   u32x4 vc[U];
-  cur.setup(qkv, ld_bytes, T, H, hq, row_bytes, live, tw, hw, sub, grp);
+  cur.setup(qkv, ld_bytes, T, H, col, live, tw, hw, sub, grp);
 #pragma unroll
   for (uint32_t u = 0; u < U; ++u) vc[u] = stream_load(cur.rs, cur.off[u]);
   __builtin_amdgcn_sched_barrier(0);           // keep the row loads ahead of the gamma work
 
   // gamma: a vector load of the same few lines by every wave of the grid
-  // makes those lines an L2 hot spot.  A single-region tensor with short heads
-  // (LPH <= 16, at most 64 dwords of gamma) reads its one gamma with scalar
-  // loads through the scalar cache and hands each lane its 4 dwords with
-  // selects, which run while the row loads are in flight.  Otherwise (two
-  // gammas, or longer heads) gamma is staged once per block in LDS, which
-  // measured faster there.
-  float gq[E], gk[E];
-  if constexpr (kGammaSgpr && CONTIG && LPH <= 16) {
-    // the launcher stands in a readable address for a NULL gamma, so the
-    // loads are unconditional and stay behind the row loads
+  // makes those lines an L2 hot spot.  Short heads (LPH <= 16, at most 64
+  // dwords of gamma) read the region's gamma with scalar loads through the
+  // scalar cache and hand each lane its 4 dwords with selects, which run
+  // while the row loads are in flight; longer heads stage it once per block
+  // in LDS.
+  float g[E];
+  if constexpr (kGammaSgpr && LPH <= 16) {
     u32x4 w = {0, 0, 0, 0};
-    gamma_to_lanes<LPH>(reinterpret_cast<const uint32_t*>(hq ? gamma_q : gamma_k), sub, w);
-    unpack<DT>(w, gq);
-    unpack<DT>(w, gk);
+    gamma_to_lanes<LPH>(reinterpret_cast<const uint32_t*>(gamma), sub, w);
+    unpack<DT>(w, g);
   } else {
-    __shared__ u32x4 g_lds[2][LPH];
-    if (threadIdx.x < LPH) {
-      g_lds[0][threadIdx.x] = gamma_q ? load16(gamma_q + threadIdx.x * 16) : u32x4{0, 0, 0, 0};
-      g_lds[1][threadIdx.x] = gamma_k ? load16(gamma_k + threadIdx.x * 16) : u32x4{0, 0, 0, 0};
-    }
+    __shared__ u32x4 g_lds[LPH];
+    if (threadIdx.x < LPH) g_lds[threadIdx.x] = load16(gamma + threadIdx.x * 16);
     __syncthreads();
-    unpack<DT>(g_lds[0][sub], gq);
-    unpack<DT>(g_lds[1][sub], gk);
+    unpack<DT>(g_lds[sub], g);
   }
   if (!live) return;
 
   if constexpr (ONE) {
-    // the grid covers every head in one trip: no loop, no prefetch
-#pragma unroll
-    for (uint32_t u = 0; u < U; ++u) {
-      float x[E];
-      unpack<DT>(vc[u], x);
-      const float s = group_sum<LPH>(vec_sumsq<DT>(x, 0.f));
-      const float r = rms_scale(s, inv_d, eps);
-      float y[E];
-#pragma unroll
-      for (int e = 0; e < E; ++e) y[e] = (x[e] * (cur.isq[u] ? gq[e] : gk[e])) * r;
-      stream_store(cur.rs, cur.off[u], pack<DT>(y));
-    }
+    per_head_apply<DT, LPH, U>(vc, g, inv_d, eps, cur.rs, cur.off);
     return;
   }
-
   while (true) {
-    // next trip: advance by the whole grid (stride_rows rows, stride_heads heads;
-    // a flat index for single-region tensors)
+    // next trip: advance by the region's part of the grid
     uint32_t tn = tw + stride_rows, hn = hw + stride_heads;
     if (!CONTIG && hn >= H) { hn -= H; ++tn; }
     const bool more = CONTIG ? hn < T * H : tn < T;
     Trip nxt;
     u32x4 vn[U];
-    nxt.setup(qkv, ld_bytes, T, H, hq, row_bytes, more, tn, hn, sub, grp);
+    nxt.setup(qkv, ld_bytes, T, H, col, more, tn, hn, sub, grp);
 #pragma unroll
     for (uint32_t u = 0; u < U; ++u) vn[u] = stream_load(nxt.rs, nxt.off[u]);
-#pragma unroll
-    for (uint32_t u = 0; u < U; ++u) {
-      float x[E];
-      unpack<DT>(vc[u], x);
-      const float s = group_sum<LPH>(vec_sumsq<DT>(x, 0.f));
-      const float r = rms_scale(s, inv_d, eps);
-      float y[E];
-#pragma unroll
-      for (int e = 0; e < E; ++e) y[e] = (x[e] * (cur.isq[u] ? gq[e] : gk[e])) * r;
-      stream_store(cur.rs, cur.off[u], pack<DT>(y));
-    }
+    per_head_apply<DT, LPH, U>(vc, g, inv_d, eps, cur.rs, cur.off);
     if (!more) break;
     cur = nxt;
 #pragma unroll
@@ -678,31 +681,48 @@ static hipError_t launch_per_head_t(const PerHeadArgs& a, hipStream_t s, int cus
   constexpr int kBlock = QKNORM_PH_THREADS;
   constexpr uint64_t heads_per_block = CH * (kBlock / 64);
   const int es = IoTraits<DT>::kBytes;
-  const uint64_t H = (uint64_t)a.hq + a.hkv;
-  const uint64_t total = (uint64_t)a.T * H;
-  uint64_t blocks = (total + heads_per_block - 1) / heads_per_block;
+  const uint32_t head_bytes = (uint32_t)(a.head_dim * es);
   const uint64_t cap = (uint64_t)cus * QKNORM_PH_BLOCKS_PER_CU;
-  if (blocks > cap) blocks = cap;
-  if (blocks < 1) blocks = 1;
-  const uint64_t stride = blocks * heads_per_block;   // heads advanced per trip
-  const bool contig = a.hq == 0 || a.hkv == 0 ? (a.ld == (int64_t)H * a.head_dim) : false;
-  const bool one = stride >= total;             // a single trip covers every head
+  const uint64_t Htot = (uint64_t)a.hq + a.hkv;
+
+  // the non-empty regions, Q first; the grid cap is shared in proportion
+  PhRegion reg[2] = {};
+  int n = 0;
+  bool one = true;
+  const uint32_t heads[2] = {(uint32_t)a.hq, (uint32_t)a.hkv};
+  const void* gammas[2] = {a.gamma_q, a.gamma_k};
+  for (int i = 0; i < 2; ++i) {
+    if (heads[i] == 0) continue;
+    PhRegion& r = reg[n++];
+    r.gamma = (const uint8_t*)gammas[i];
+    r.H = heads[i];
+    r.col_bytes = i == 0 ? 0u : (uint32_t)a.hq * head_bytes;
+    const uint64_t total = (uint64_t)a.T * r.H;
+    uint64_t blocks = (total + heads_per_block - 1) / heads_per_block;
+    uint64_t rcap = cap * r.H / Htot;
+    if (rcap < 1) rcap = 1;
+    if (blocks > rcap) blocks = rcap;
+    if (blocks < 1) blocks = 1;
+    r.blocks = (uint32_t)blocks;
+    const uint64_t stride = blocks * heads_per_block;   // heads advanced per trip
+    one = one && stride >= total;
+    r.stride_rows = (uint32_t)(stride / r.H);
+    r.stride_heads = (uint32_t)(stride % r.H);
+  }
+  // a single region whose rows hold nothing else: one flat array of heads
+  const bool contig = n == 1 && reg[0].col_bytes == 0 &&
+                      a.ld == (int64_t)reg[0].H * a.head_dim;
+  if (contig) {
+    reg[0].stride_heads = reg[0].stride_rows * reg[0].H + reg[0].stride_heads;
+    reg[0].stride_rows = 0;
+  }
   auto kern = contig ? (one ? per_head_kernel<DT, LPH, U, true, true>
                             : per_head_kernel<DT, LPH, U, true, false>)
                      : (one ? per_head_kernel<DT, LPH, U, false, true>
                             : per_head_kernel<DT, LPH, U, false, false>);
-  // A NULL gamma serves a region without heads; stand in the other gamma (or
-  // the first head of qkv, at least one head long) so gamma reads stay valid.
-  const void* gq = a.gamma_q ? a.gamma_q : (a.gamma_k ? a.gamma_k : a.qkv);
-  const void* gk = a.gamma_k ? a.gamma_k : gq;
-  const bool gsgpr = kGammaSgpr && contig && LPH <= 16;
-  hipLaunchKernelGGL(kern, dim3((uint32_t)blocks), dim3(kBlock), 0, s, (uint8_t*)a.qkv,
-                     (uint32_t)(a.ld * es), (uint32_t)a.T, (uint32_t)H, (uint32_t)a.hq,
-                     (uint32_t)(H * a.head_dim * es),
-                     (const uint8_t*)(gsgpr ? gq : a.gamma_q),
-                     (const uint8_t*)(gsgpr ? gk : a.gamma_k), a.eps, 1.0f / (float)a.head_dim,
-                     contig ? 0u : (uint32_t)(stride / H),
-                     contig ? (uint32_t)stride : (uint32_t)(stride % H));
+  hipLaunchKernelGGL(kern, dim3(reg[0].blocks + reg[1].blocks), dim3(kBlock), 0, s,
+                     (uint8_t*)a.qkv, (uint32_t)(a.ld * es), (uint32_t)a.T, reg[0], reg[1], a.eps,
+                     1.0f / (float)a.head_dim);
   return hipGetLastError();
 }
 
