@@ -19,9 +19,10 @@
  *         (Lesson "Explain combined QKV projection and why it's faster than
  *         three separate projections?", section "With GQA": the fused output
  *         is Q heads, then K heads, then V heads, split by those widths.)
- *   dtype QKNORM_F32 or QKNORM_BF16; qkv and gamma share it.  Arithmetic is
- *         fp32 throughout; each output element is rounded once, to nearest
- *         even, to the I/O dtype.  Partial sums are always fp32.
+ *   dtype QKNORM_F32, QKNORM_BF16 or QKNORM_F16; qkv and gamma share it.
+ *         Arithmetic is fp32 throughout; each output element is rounded
+ *         once, to nearest even, to the I/O dtype.  Partial sums are always
+ *         fp32.
  *   eps   fp32, finite, >= 0; added to the mean square inside the root.
  *
  * Ownership, streams and threads
@@ -57,13 +58,14 @@ extern "C" {
 /* dtype codes */
 #define QKNORM_F32 0
 #define QKNORM_BF16 1
+#define QKNORM_F16 2
 
 /* return codes */
 #define QKNORM_OK 0
 #define QKNORM_E_NULLPTR -1     /* a pointer that would be used is NULL */
 #define QKNORM_E_SHAPE -2       /* negative size, ld too small, shard count does not divide */
 #define QKNORM_E_ALIGN -3       /* base, row pitch, head or shard not a multiple of 16 bytes */
-#define QKNORM_E_DTYPE -4       /* dtype not QKNORM_F32 / QKNORM_BF16 */
+#define QKNORM_E_DTYPE -4       /* dtype not QKNORM_F32 / QKNORM_BF16 / QKNORM_F16 */
 #define QKNORM_E_UNSUPPORTED -5 /* valid request this build does not implement (e.g. head_dim) */
 #define QKNORM_E_EPS -6         /* eps negative, NaN or infinite */
 #define QKNORM_E_HIP -7         /* the HIP runtime refused the launch or device query */
@@ -79,8 +81,9 @@ extern "C" {
  *  #13189, Motivation and Modifications: the QK norm is an RMSNorm whose
  *  hidden size is the head dimension, 128 in the benchmark tables.)
  *
- * Requires: head_dim in {64, 128, 256}; ld >= (hq+hkv)*head_dim; qkv, gamma
- * and ld*esize 16-byte aligned.
+ * Requires: a head of 64 to 1024 bytes, a power of two (bf16/fp16 head_dim
+ * 32..512, fp32 head_dim 16..256); ld >= (hq+hkv)*head_dim; qkv, gamma and
+ * ld*esize 16-byte aligned.
  */
 int qknorm_per_head(void *qkv, int64_t T, int64_t ld, int32_t hq, int32_t hkv,
                     int32_t head_dim, const void *gamma_q, const void *gamma_k,

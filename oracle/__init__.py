@@ -7,7 +7,7 @@ The arithmetic lives in ``qknorm_oracle.c`` (plain C, fp64, OpenMP over
 tokens); this module only marshals numpy arrays.  Every function returns the
 fp64 result ``y`` (V and padding columns copied through) and the result rounded
 once, to nearest-even, to the I/O dtype ``yr`` (same storage as the input:
-float32, or uint16 bf16 bit patterns).
+float32, or uint16 bf16 / fp16 bit patterns).
 
 Pins (tests/test_oracle_pins.py): unit RMS, scale invariance, the shard-sum
 identity, exact brute force on tiny inputs, closed-form rows, per-head vs
@@ -28,6 +28,7 @@ _LIB = os.path.join(_HERE, "liboracle.so")
 
 F32 = 0
 BF16 = 1
+F16 = 2
 
 _lib = None
 
@@ -70,7 +71,7 @@ def max_threads() -> int:
 def _storage(dtype: int):
     if dtype == F32:
         return np.float32
-    if dtype == BF16:
+    if dtype in (BF16, F16):
         return np.uint16
     raise ValueError(f"unknown dtype code {dtype}")
 
@@ -165,5 +166,7 @@ def decode(a, dtype):
     a = np.asarray(a)
     if dtype == F32:
         return a.astype(np.float64)
+    if dtype == F16:
+        return np.ascontiguousarray(a, dtype=np.uint16).view(np.float16).astype(np.float64)
     with np.errstate(invalid="ignore"):
         return (a.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)

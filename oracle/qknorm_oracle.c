@@ -40,7 +40,7 @@
  * are copied through unchanged; outputs are also given rounded once, to
  * nearest-even, to the I/O dtype.
  *
- * dtype codes: 0 = fp32, 1 = bf16 (stored as its 16-bit pattern).
+ * dtype codes: 0 = fp32, 1 = bf16, 2 = fp16 (both stored as 16-bit patterns).
  * Every function returns 0, or -1 on an argument it cannot use.
  */
 #include <math.h>
@@ -52,11 +52,27 @@
 
 /* ------------------------------------------------------------------ I/O -- */
 
-/* Exact value of element i of a stored fp32 or bf16 array. */
+/* Exact value of an IEEE binary16 pattern: 1 sign, 5 exponent, 10 fraction bits. */
+static double half_value(uint16_t h)
+{
+    int sign = h >> 15, e = (h >> 10) & 0x1F, m = h & 0x3FF;
+    double v;
+    if (e == 0)
+        v = ldexp((double)m, -24);                 /* zero and subnormals */
+    else if (e == 31)
+        v = m ? NAN : INFINITY;
+    else
+        v = ldexp((double)(1024 + m), e - 25);
+    return sign ? -v : v;
+}
+
+/* Exact value of element i of a stored fp32, bf16 or fp16 array. */
 static double load_value(const void *p, int dtype, int64_t i)
 {
     if (dtype == 0)
         return (double)((const float *)p)[i];
+    if (dtype == 2)
+        return half_value(((const uint16_t *)p)[i]);
     uint32_t bits = (uint32_t)((const uint16_t *)p)[i] << 16;
     float f;
     memcpy(&f, &bits, sizeof f);
@@ -87,10 +103,41 @@ static uint16_t round_to_bf16(double v)
     return (uint16_t)(bits >> 16);
 }
 
+/* Round v to the nearest binary16, ties to even, in a single step from fp64.
+ * 11 significant bits; below 2^-14 the spacing is fixed at 2^-24; anything
+ * that rounds past 65504 becomes infinity. */
+static uint16_t round_to_f16(double v)
+{
+    if (isnan(v))
+        return 0x7E00;
+    uint16_t sign = signbit(v) ? 0x8000 : 0;
+    double a = fabs(v);
+    if (isinf(a))
+        return sign | 0x7C00;
+    if (a == 0.0)
+        return sign;
+    int e;
+    frexp(a, &e);                          /* a = m * 2^e, 0.5 <= m < 1 */
+    if (e < -13)
+        e = -13;
+    double q = nearbyint(ldexp(a, 11 - e));  /* nearest, ties even */
+    double r = ldexp(q, e - 11);
+    if (r > 65504.0)
+        return sign | 0x7C00;
+    if (r < ldexp(1.0, -14))               /* subnormal (or a zero) */
+        return sign | (uint16_t)ldexp(r, 24);
+    int re;
+    double rm = frexp(r, &re);             /* r = rm * 2^re, rm in [0.5, 1) */
+    uint16_t frac = (uint16_t)(ldexp(rm, 11) - 1024.0);
+    return sign | (uint16_t)((re - 1 + 15) << 10) | frac;
+}
+
 static void store_rounded(void *p, int dtype, int64_t i, double v)
 {
     if (dtype == 0)
         ((float *)p)[i] = (float)v;          /* C conversion: nearest, ties even */
+    else if (dtype == 2)
+        ((uint16_t *)p)[i] = round_to_f16(v);
     else
         ((uint16_t *)p)[i] = round_to_bf16(v);
 }
@@ -157,7 +204,7 @@ static double sharded_total(const void *x, int dtype, int64_t off, int64_t width
     return S;
 }
 
-static int bad_dtype(int dtype) { return dtype != 0 && dtype != 1; }
+static int bad_dtype(int dtype) { return dtype != 0 && dtype != 1 && dtype != 2; }
 
 /* ------------------------------------------------------------ entry points -- */
 

@@ -27,6 +27,7 @@ LIB_PATH = os.path.join(HERE, "libqknorm.so")
 
 QKNORM_F32 = 0
 QKNORM_BF16 = 1
+QKNORM_F16 = 2
 QKNORM_OK = 0
 QKNORM_E_NULLPTR = -1
 QKNORM_E_SHAPE = -2
@@ -88,7 +89,9 @@ def _dtype_code(t) -> int:
         return QKNORM_F32
     if t.dtype == torch.bfloat16:
         return QKNORM_BF16
-    raise ValueError(f"QK-Norm supports float32 and bfloat16 tensors, not {t.dtype}")
+    if t.dtype == torch.float16:
+        return QKNORM_F16
+    raise ValueError(f"QK-Norm supports float32, bfloat16 and float16 tensors, not {t.dtype}")
 
 
 def _rows(qkv):
@@ -197,4 +200,4 @@ def qknorm_apply_scalar(qkv, wq: int, wk: int, part_q, part_k, norm_wq: int, nor
 
 
 __all__ = ["qknorm_per_head", "qknorm_layerwise", "qknorm_partial_sumsq", "qknorm_apply_scalar",
-           "strerror", "abi_version", "load", "QKNormError", "QKNORM_F32", "QKNORM_BF16"]
+           "strerror", "abi_version", "load", "QKNormError", "QKNORM_F32", "QKNORM_BF16", "QKNORM_F16"]

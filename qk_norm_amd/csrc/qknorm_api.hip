@@ -16,10 +16,14 @@ constexpr int64_t kMaxRows = (INT64_C(1) << 31) - (INT64_C(1) << 20);
 
 int esize_of(int32_t dtype) { return dtype == QKNORM_F32 ? 4 : 2; }
 
+bool known_dtype(int32_t dtype) {
+  return dtype == QKNORM_F32 || dtype == QKNORM_BF16 || dtype == QKNORM_F16;
+}
+
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 int check_common(int32_t dtype, float eps, int64_t T, int64_t ld) {
-  if (dtype != QKNORM_F32 && dtype != QKNORM_BF16) return QKNORM_E_DTYPE;
+  if (!known_dtype(dtype)) return QKNORM_E_DTYPE;
   if (!std::isfinite(eps) || eps < 0.f) return QKNORM_E_EPS;
   if (T < 0 || ld < 0) return QKNORM_E_SHAPE;
   if (T > kMaxRows) return QKNORM_E_UNSUPPORTED;
@@ -106,7 +110,10 @@ int qknorm_per_head(void* qkv, int64_t T, int64_t ld, int32_t hq, int32_t hkv, i
   if ((rc = check_region(qkv, T, ld, wq, wk, es))) return rc;
   if ((rc = check_gamma(gamma_q, wq, T))) return rc;
   if ((rc = check_gamma(gamma_k, wk, T))) return rc;
-  if (head_dim != 64 && head_dim != 128 && head_dim != 256) return QKNORM_E_UNSUPPORTED;
+  // a head is 4..64 lanes of 16 bytes, a power of two
+  const int64_t head_bytes = (int64_t)head_dim * es;
+  if (head_bytes < 64 || head_bytes > 1024 || (head_bytes & (head_bytes - 1)) != 0)
+    return QKNORM_E_UNSUPPORTED;
   if (T * ((int64_t)hq + hkv) >= kMaxHeadIndex) return QKNORM_E_UNSUPPORTED;
   if (T == 0 || hq + hkv == 0) return QKNORM_OK;
   int cus = 0;

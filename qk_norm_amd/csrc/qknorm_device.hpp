@@ -1,7 +1,7 @@
 // Device-side building blocks for the gfx950 QK-Norm kernels.
 //
-// Everything here works on 16-byte vectors (one global_load_dwordx4 /
-// global_store_dwordx4 per lane): 8 bf16 or 4 fp32 values.  Sums of squares
+// Everything here works on 16-byte vectors (one 16-byte load / store per
+// lane): 8 bf16 or fp16 values, or 4 fp32 values.  Sums of squares
 // are fp32; cross-lane reduction uses DPP row operations inside 16-lane rows
 // and the gfx950 permlane swaps across rows, so no LDS is touched.
 #pragma once
@@ -13,8 +13,9 @@ namespace qknorm {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
-enum : int { kF32 = 0, kBF16 = 1 };
+enum : int { kF32 = 0, kBF16 = 1, kF16 = 2 };
 
 template <int DT> struct IoTraits;
 template <> struct IoTraits<kF32> {
@@ -22,6 +23,10 @@ template <> struct IoTraits<kF32> {
   static constexpr int kBytes = 4;
 };
 template <> struct IoTraits<kBF16> {
+  static constexpr int kElems = 8;
+  static constexpr int kBytes = 2;
+};
+template <> struct IoTraits<kF16> {
   static constexpr int kElems = 8;
   static constexpr int kBytes = 2;
 };
@@ -84,13 +89,24 @@ __device__ __forceinline__ void unpack(u32x4 v, float (&f)[IoTraits<DT>::kElems]
       f[2 * i] = __uint_as_float(v[i] << 16);
       f[2 * i + 1] = __uint_as_float(v[i] & 0xFFFF0000u);
     }
+  } else if constexpr (DT == kF16) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      // copy the element out first: a bit_cast of the vector element itself
+      // reads element 0 whatever i is
+      const uint32_t w = v[i];
+      const f16x2 h = __builtin_bit_cast(f16x2, w);
+      f[2 * i] = (float)h[0];
+      f[2 * i + 1] = (float)h[1];
+    }
   } else {
 #pragma unroll
     for (int i = 0; i < 4; ++i) f[i] = __uint_as_float(v[i]);
   }
 }
 
-// Round fp32 to the I/O dtype (bf16: v_cvt_pk_bf16_f32, nearest-even) and pack.
+// Round fp32 to the I/O dtype (bf16: v_cvt_pk_bf16_f32; fp16: v_cvt_f16_f32;
+// both nearest-even) and pack.
 template <int DT>
 __device__ __forceinline__ u32x4 pack(const float (&f)[IoTraits<DT>::kElems]) {
   u32x4 v;
@@ -98,6 +114,12 @@ __device__ __forceinline__ u32x4 pack(const float (&f)[IoTraits<DT>::kElems]) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       bf16x2 h = {(__bf16)f[2 * i], (__bf16)f[2 * i + 1]};
+      v[i] = __builtin_bit_cast(uint32_t, h);
+    }
+  } else if constexpr (DT == kF16) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f16x2 h = {(_Float16)f[2 * i], (_Float16)f[2 * i + 1]};
       v[i] = __builtin_bit_cast(uint32_t, h);
     }
   } else {

@@ -730,6 +730,7 @@ template <int DT>
 static hipError_t launch_per_head_dt(const PerHeadArgs& a, hipStream_t s, int cus) {
   const int lph = a.head_dim * IoTraits<DT>::kBytes / 16;
   switch (lph) {
+    case 4: return launch_per_head_t<DT, 4>(a, s, cus);
     case 8: return launch_per_head_t<DT, 8>(a, s, cus);
     case 16: return launch_per_head_t<DT, 16>(a, s, cus);
     case 32: return launch_per_head_t<DT, 32>(a, s, cus);
@@ -739,8 +740,11 @@ static hipError_t launch_per_head_dt(const PerHeadArgs& a, hipStream_t s, int cu
 }
 
 hipError_t launch_per_head(const PerHeadArgs& a, hipStream_t s, int cus) {
-  return a.dtype == kBF16 ? launch_per_head_dt<kBF16>(a, s, cus)
-                          : launch_per_head_dt<kF32>(a, s, cus);
+  switch (a.dtype) {
+    case kBF16: return launch_per_head_dt<kBF16>(a, s, cus);
+    case kF16: return launch_per_head_dt<kF16>(a, s, cus);
+    default: return launch_per_head_dt<kF32>(a, s, cus);
+  }
 }
 
 static RowGeom make_geom(int64_t T, int64_t ld, int64_t wq, int64_t wk, int32_t nshards,
@@ -816,8 +820,11 @@ static hipError_t launch_layerwise_dt(const LayerwiseArgs& a, hipStream_t s, int
 }
 
 hipError_t launch_layerwise(const LayerwiseArgs& a, hipStream_t s, int cus) {
-  return a.dtype == kBF16 ? launch_layerwise_dt<kBF16>(a, s, cus)
-                          : launch_layerwise_dt<kF32>(a, s, cus);
+  switch (a.dtype) {
+    case kBF16: return launch_layerwise_dt<kBF16>(a, s, cus);
+    case kF16: return launch_layerwise_dt<kF16>(a, s, cus);
+    default: return launch_layerwise_dt<kF32>(a, s, cus);
+  }
 }
 
 template <int DT>
@@ -835,7 +842,11 @@ static hipError_t launch_partial_dt(const PartialArgs& a, hipStream_t s, int cus
 }
 
 hipError_t launch_partial_sumsq(const PartialArgs& a, hipStream_t s, int cus) {
-  return a.dtype == kBF16 ? launch_partial_dt<kBF16>(a, s, cus) : launch_partial_dt<kF32>(a, s, cus);
+  switch (a.dtype) {
+    case kBF16: return launch_partial_dt<kBF16>(a, s, cus);
+    case kF16: return launch_partial_dt<kF16>(a, s, cus);
+    default: return launch_partial_dt<kF32>(a, s, cus);
+  }
 }
 
 template <int DT, int VPT>
@@ -875,7 +886,11 @@ static hipError_t launch_apply_dt(const ApplyArgs& a, hipStream_t s, int cus) {
 }
 
 hipError_t launch_apply_scalar(const ApplyArgs& a, hipStream_t s, int cus) {
-  return a.dtype == kBF16 ? launch_apply_dt<kBF16>(a, s, cus) : launch_apply_dt<kF32>(a, s, cus);
+  switch (a.dtype) {
+    case kBF16: return launch_apply_dt<kBF16>(a, s, cus);
+    case kF16: return launch_apply_dt<kF16>(a, s, cus);
+    default: return launch_apply_dt<kF32>(a, s, cus);
+  }
 }
 
 }  // namespace qknorm

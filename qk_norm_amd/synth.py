@@ -24,9 +24,10 @@ Value structure (the workloads of the five benchmark cases):
   x[t, c] = round_to_dtype( z[t, c] * (20 if c is an outlier column else 1) * s_t )
 with z ~ N(0, 1), s_t ~ U(lo, hi) or 1, and gamma = round_to_dtype(U(0.5, 1.5)).
 Rounding to bf16 is round-to-nearest-even taken directly from the fp64 value
-(no intermediate fp32 step); fp32 uses numpy's own RNE cast.
+(no intermediate fp32 step); fp32 and fp16 use numpy's own RNE casts (numpy
+rounds fp64 to fp16 directly).
 
-bf16 arrays are returned as ``np.uint16`` bit patterns (numpy has no bf16).
+bf16 and fp16 arrays are returned as ``np.uint16`` bit patterns.
 """
 from __future__ import annotations
 
@@ -39,7 +40,8 @@ import numpy as np
 
 F32 = 0
 BF16 = 1
-DTYPE_NAMES = {F32: "f32", BF16: "bf16"}
+F16 = 2
+DTYPE_NAMES = {F32: "f32", BF16: "bf16", F16: "f16"}
 
 _GOLDEN = np.uint64(0x9E3779B97F4A7C15)
 _M1 = np.uint64(0xBF58476D1CE4E5B9)
@@ -140,6 +142,10 @@ def to_dtype(v: np.ndarray, dtype: int) -> np.ndarray:
         return np.asarray(v, dtype=np.float64).astype(np.float32)
     if dtype == BF16:
         return round_bf16_bits(v)
+    if dtype == F16:
+        # numpy rounds fp64 -> binary16 directly, nearest-even
+        with np.errstate(over="ignore"):
+            return np.asarray(v, dtype=np.float64).astype(np.float16).view(np.uint16)
     raise ValueError(f"unknown dtype code {dtype}")
 
 

@@ -8,13 +8,15 @@ import torch
 import oracle
 from qk_norm_amd import synth
 
-RTOL = {synth.F32: 1e-5, synth.BF16: 8e-3}
+RTOL = {synth.F32: 1e-5, synth.BF16: 8e-3, synth.F16: 1e-3}
+# fp16 outputs can be subnormal, where the spacing is fixed at 2^-24
+ATOL = {synth.F32: 0.0, synth.BF16: 0.0, synth.F16: 2.0 ** -24}
 GUARD_BYTES = 4096
 SENTINEL = 0xA5
 
 
 def torch_dtype(dtype):
-    return torch.float32 if dtype == synth.F32 else torch.bfloat16
+    return {synth.F32: torch.float32, synth.BF16: torch.bfloat16, synth.F16: torch.float16}[dtype]
 
 
 def host_to_device(a: np.ndarray, dtype, dev="cuda"):
@@ -22,7 +24,7 @@ def host_to_device(a: np.ndarray, dtype, dev="cuda"):
     if dtype == synth.F32:
         t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32))
     else:
-        t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint16).view(np.int16)).view(torch.bfloat16)
+        t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint16).view(np.int16)).view(torch_dtype(dtype))
     return t.to(dev)
 
 
@@ -74,15 +76,15 @@ def decode(a, dtype):
 
 
 def assert_close_to_oracle(got: np.ndarray, y64: np.ndarray, dtype, cols=None, label=""):
-    """|g - o| <= rtol |o| element by element (o the unrounded fp64 oracle value);
-    where o == 0 the GPU value must be a zero."""
+    """|g - o| <= rtol |o| (+ atol for fp16 subnormals) element by element (o the
+    unrounded fp64 oracle value); where o == 0 the GPU value must be a zero."""
     g = decode(got, dtype)
     if cols is not None:
         g = g[:, cols]
         y64 = y64[:, cols]
-    rtol = RTOL[dtype]
+    rtol, atol = RTOL[dtype], ATOL[dtype]
     err = np.abs(g - y64)
-    bad = err > rtol * np.abs(y64)
+    bad = (err > rtol * np.abs(y64) + atol) | ((y64 == 0) & (g != 0))
     if bad.any():
         idx = np.argwhere(bad)[:5]
         detail = ", ".join(f"[{i},{j}] gpu={g[i, j]!r} oracle={y64[i, j]!r}" for i, j in idx)
@@ -92,7 +94,7 @@ def assert_close_to_oracle(got: np.ndarray, y64: np.ndarray, dtype, cols=None, l
 
 
 def ordinal(bits: np.ndarray, dtype) -> np.ndarray:
-    if dtype == synth.BF16:
+    if dtype in (synth.BF16, synth.F16):
         b = bits.astype(np.int64)
         return np.where(b & 0x8000, -(b & 0x7FFF), b)
     b = bits.view(np.uint32).astype(np.int64)

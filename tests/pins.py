@@ -36,7 +36,8 @@ from qk_norm_amd import synth
 
 getcontext().prec = 60
 
-F32, BF16 = oracle.F32, oracle.BF16
+F32, BF16, F16 = oracle.F32, oracle.BF16, oracle.F16
+DTYPES = (F32, BF16, F16)
 
 
 # ------------------------------------------------------------------ helpers --
@@ -75,24 +76,33 @@ def _ulps(a: float, exact: Decimal) -> float:
     return abs(Decimal(a) - exact) / Decimal(math.ulp(e))
 
 
-def _bf16_value(bits: int) -> Fraction:
-    return Fraction(float(oracle.decode(np.array([bits], dtype=np.uint16), BF16)[0]))
+def _value16(bits: int, dtype) -> Fraction:
+    return Fraction(float(oracle.decode(np.array([bits], dtype=np.uint16), dtype)[0]))
 
 
-def _nearest_bf16(exact: Decimal) -> tuple[int, bool]:
-    """bf16 pattern nearest to an exact value (ties to even); also whether the
-    value lies so close to a rounding midpoint that an fp64 approximation of it
-    may legitimately round either way."""
+_NONFINITE = {BF16: 0x7F80, F16: 0x7C00}
+
+
+def _nearest16(exact: Decimal, dtype) -> tuple[int, bool]:
+    """bf16 / fp16 pattern nearest to an exact value (ties to even); also whether
+    the value lies so close to a rounding midpoint that an fp64 approximation of
+    it may legitimately round either way.  The first guess comes from a library
+    cast (torch for bf16, numpy for fp16); its neighbours are then compared
+    exactly."""
     import torch
     approx = float(exact)
-    b = int(torch.tensor([approx], dtype=torch.float32).to(torch.bfloat16).view(torch.int16)[0]) & 0xFFFF
+    if dtype == BF16:
+        b = int(torch.tensor([approx], dtype=torch.float32).to(torch.bfloat16).view(torch.int16)[0]) & 0xFFFF
+    else:
+        b = int(np.array([approx]).astype(np.float16).view(np.uint16)[0])
+    nf = _NONFINITE[dtype]
     cands = {b, (b + 1) & 0xFFFF, (b - 1) & 0xFFFF}
     ex = Fraction(exact)
     best = None
     for c in cands:
-        if (c & 0x7F80) == 0x7F80:      # inf / nan patterns
+        if (c & nf) == nf:              # inf / nan patterns
             continue
-        d = abs(_bf16_value(c) - ex)
+        d = abs(_value16(c, dtype) - ex)
         key = (d, c & 1)
         if best is None or key < best[0]:
             best = (key, c)
@@ -100,9 +110,9 @@ def _nearest_bf16(exact: Decimal) -> tuple[int, bool]:
     # distance to the nearest midpoint, in fp64 ulps of the value
     near_mid = False
     for n in ((c + 1) & 0xFFFF, (c - 1) & 0xFFFF):
-        if (n & 0x7F80) == 0x7F80:
+        if (n & nf) == nf:
             continue
-        mid = (_bf16_value(c) + _bf16_value(n)) / 2
+        mid = (_value16(c, dtype) + _value16(n, dtype)) / 2
         if approx != 0.0 and abs(mid - ex) <= 8 * Fraction(math.ulp(approx)):
             near_mid = True
     return c, near_mid
@@ -121,11 +131,11 @@ def _check_rows_exact(x, y, yr, dtype, groups, eps, label):
             got = float(y[t, c0 + j])
             u = _ulps(got, ex[j])
             assert u <= 4, f"{label}: row {t} col {c0 + j}: {got!r} vs exact {ex[j]} ({u} ulp)"
-            if dtype == BF16:
-                want, ambiguous = _nearest_bf16(ex[j])
+            if dtype in (BF16, F16):
+                want, ambiguous = _nearest16(ex[j], dtype)
                 gotb = int(yr[t, c0 + j])
                 assert gotb == want or ambiguous, \
-                    f"{label}: row {t} col {c0 + j}: bf16 {gotb:#06x} vs nearest {want:#06x}"
+                    f"{label}: row {t} col {c0 + j}: {gotb:#06x} vs nearest {want:#06x}"
             else:
                 want = np.float32(float(ex[j]))
                 assert yr[t, c0 + j] == want or abs(float(yr[t, c0 + j]) - float(want)) <= \
@@ -134,7 +144,7 @@ def _check_rows_exact(x, y, yr, dtype, groups, eps, label):
 
 def check_brute_force():
     seed = 100
-    for dtype in (F32, BF16):
+    for dtype in DTYPES:
         for D in (1, 2, 4, 8):
             for (hq, hkv, extra) in ((1, 0, 0), (3, 1, D), (2, 2, 3)):
                 T = 3
@@ -174,7 +184,7 @@ def check_apply_exact():
     slice is normalised with partials of the whole vector and the full-width
     divisor."""
     seed = 300
-    for dtype in (F32, BF16):
+    for dtype in DTYPES:
         T, W, N = 3, 48, 4          # full width 48 split over 4 "ranks" of 12
         seed += 1
         full = _rng_problem(seed, T, W, dtype)
@@ -200,7 +210,7 @@ def check_apply_exact():
 # -------------------------------------------------------------- invariants --
 
 def check_unit_rms():
-    for dtype in (F32, BF16):
+    for dtype in DTYPES:
         x = _rng_problem(7, 5, 3 * 128 + 64, dtype, scale=4.0)
         ones = synth.to_dtype(np.ones(128), dtype)
         y, _ = oracle.per_head(x, dtype, 2, 1, 128, ones, ones, 0.0)
@@ -218,7 +228,7 @@ def check_unit_rms():
 
 
 def check_eps_identity():
-    for dtype in (F32, BF16):
+    for dtype in DTYPES:
         x = _rng_problem(9, 4, 2 * 64, dtype, scale=0.01)
         ones = synth.to_dtype(np.ones(64), dtype)
         eps = synth.eps_f32(1e-4)
@@ -234,8 +244,13 @@ def check_eps_identity():
 
 
 def check_scale_pow2():
-    for dtype in (F32, BF16):
-        x = _rng_problem(10, 3, 3 * 32, dtype)
+    for dtype in DTYPES:
+        z = synth.normal(10, 0, 3 * 3 * 32).reshape(3, 3 * 32)
+        if dtype == F16:
+            # fp16 keeps full precision only above 2^-14: flush the small draws so
+            # that every 2^k below is exact (|z| < 8 stays under 65504 at k = 12)
+            z = np.where(np.abs(z) < 2.0 ** -6, 0.0, z)
+        x = synth.to_dtype(z, dtype)
         gq, gk = _gamma(10, 32, dtype, 3), _gamma(10, 32, dtype, 4)
         xd = oracle.decode(x, dtype)
         y0, _ = oracle.per_head(x, dtype, 2, 1, 32, gq, gk, 0.0)
@@ -260,11 +275,13 @@ def check_scale_pow2():
                 a = ya[t, h * 32:(h + 1) * 32]
                 b = yb[t, h * 32:(h + 1) * 32]
                 assert np.all(np.abs(a - b) <= bound * np.abs(a) + 1e-300), "eps scale bound"
-                assert np.all(np.abs(b) < np.abs(a)), "scaling down with eps > 0 must shrink |y|"
+                nz = a != 0
+                assert np.all(np.abs(b[nz]) < np.abs(a[nz])), "scaling down with eps > 0 must shrink |y|"
+                assert np.all(b[~nz] == 0)
 
 
 def check_shard_identity():
-    for dtype in (F32, BF16):
+    for dtype in DTYPES:
         for (wq, wk, R) in ((256, 64, 8), (96, 48, 3), (64, 64, 1)):
             T = 3
             x = _rng_problem(11 + R, T, wq + wk + 16, dtype, scale=5.0)
@@ -296,7 +313,7 @@ def check_closed_form():
     cases = [(128, 2, 8.0), (128, 8, 4.0), (128, 32, 2.0), (128, 128, 1.0),
              (4096, 1, 64.0), (4096, 4, 32.0), (4096, 16, 16.0), (1024, 1, 32.0),
              (8192, 2, 64.0), (8192, 8, 32.0)]
-    for dtype in (F32, BF16):
+    for dtype in DTYPES:
         for (n, k, root) in cases:
             for a in (1.0, 0.375, 3.0, 2.0 ** -20):
                 x = np.zeros((1, n))
@@ -319,7 +336,7 @@ def check_closed_form():
                 assert np.array_equal(yr[0], synth.to_dtype(want, dtype)), \
                     f"closed form rounded n={n} k={k} a={a}"
     # width-1 group: y = g x / sqrt(x^2 + eps); with eps = 0 just g * sign(x)
-    for dtype in (F32, BF16):
+    for dtype in DTYPES:
         x = synth.to_dtype(np.array([[3.0, -0.5, 1e-3]]), dtype)
         g = synth.to_dtype(np.array([1.25]), dtype)
         y, _ = oracle.per_head(x, dtype, 3, 0, 1, g, None, 0.0)
@@ -332,7 +349,7 @@ def check_closed_form():
 
 
 def check_identities():
-    for dtype in (F32, BF16):
+    for dtype in DTYPES:
         T, W = 4, 256
         x = _rng_problem(13, T, W + 40, dtype)
         g = _gamma(13, W, dtype)
@@ -359,7 +376,7 @@ def check_identities():
 
 def check_libraries():
     import torch
-    for dtype in (F32, BF16):
+    for dtype in DTYPES:
         T, H, D = 6, 5, 128
         x = _rng_problem(16, T, H * D, dtype, scale=2.0)
         g = _gamma(16, D, dtype)
@@ -421,8 +438,44 @@ def check_rounding():
     assert list(oracle.round_to(np.array([0.0, -0.0, 1e39, -1e39]), BF16)) == [0, 0x8000, 0x7F80, 0xFF80]
 
 
+def check_rounding_f16():
+    import torch
+    allh = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    vals = oracle.decode(allh, F16)
+    # the decode is the IEEE binary16 value: against numpy's own float16
+    assert np.array_equal(np.isnan(vals), np.isnan(allh.view(np.float16)))
+    fin = np.isfinite(vals)
+    assert np.array_equal(vals[fin], allh.view(np.float16)[fin].astype(np.float64))
+    # every finite pattern is a fixed point (signed zeros included)
+    assert np.array_equal(oracle.round_to(vals[fin], F16), allh[fin]), "fp16 fixed points"
+    # midpoints of every pair of neighbouring finite positives: ties to even
+    pos = allh[allh < 0x7BFF]
+    lo = oracle.decode(pos, F16)
+    hi = oracle.decode((pos + 1).astype(np.uint16), F16)
+    mid = (lo + hi) / 2
+    got = oracle.round_to(mid, F16)
+    want_even = np.where(pos % 2 == 0, pos, pos + 1).astype(np.uint16)
+    assert np.array_equal(got, want_even), "fp16 ties to even (normals and subnormals)"
+    assert np.array_equal(oracle.round_to(np.nextafter(mid, np.inf), F16), (pos + 1).astype(np.uint16))
+    assert np.array_equal(oracle.round_to(np.nextafter(mid, -np.inf), F16), pos)
+    # the range ends: 65504 is the largest finite value, the midpoint to the
+    # next binade (65520) and above become infinity; half of 2^-24 is a tie to 0
+    ends = np.array([65504.0, np.nextafter(65520.0, 0), 65520.0, 1e6, -1e6,
+                     2.0 ** -25, np.nextafter(2.0 ** -25, 1), 3 * 2.0 ** -25, -0.0])
+    assert [int(v) for v in oracle.round_to(ends, F16)] == \
+        [0x7BFF, 0x7BFF, 0x7C00, 0x7C00, 0xFC00, 0x0000, 0x0001, 0x0002, 0x8000]
+    # random values over a wide range: numpy (direct fp64 -> fp16) and torch
+    # (fp32 -> fp16, so on fp32-exact values) give the same patterns
+    v = synth.normal(79, 0, 200000) * np.exp(synth.normal(80, 0, 200000) * 4)
+    with np.errstate(over="ignore"):
+        assert np.array_equal(oracle.round_to(v, F16), v.astype(np.float16).view(np.uint16)), "vs numpy"
+        v32 = v.astype(np.float32).astype(np.float64)
+    tor = torch.from_numpy(v32).to(torch.float16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(oracle.round_to(v32, F16), tor), "fp32-exact values vs torch"
+
+
 def check_pass_through():
-    for dtype in (F32, BF16):
+    for dtype in DTYPES:
         hq, hkv, D, pad = 4, 2, 64, 24
         ld = (hq + 2 * hkv) * D + pad
         x = _rng_problem(18, 5, ld, dtype)
@@ -439,4 +492,4 @@ def check_pass_through():
 
 ALL_CHECKS = [check_brute_force, check_apply_exact, check_unit_rms, check_eps_identity,
               check_scale_pow2, check_shard_identity, check_closed_form, check_identities,
-              check_libraries, check_rounding, check_pass_through]
+              check_libraries, check_rounding, check_rounding_f16, check_pass_through]

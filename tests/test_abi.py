@@ -14,7 +14,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "qknorm.h")
 
 A16 = 0x10000          # a fake, 16-byte aligned "device" address (never dereferenced)
-BF16, F32 = q.QKNORM_BF16, q.QKNORM_F32
+BF16, F32, F16 = q.QKNORM_BF16, q.QKNORM_F32, q.QKNORM_F16
 
 
 def _declared():
@@ -85,8 +85,10 @@ def ap(lib, qkv=A16, T=4, ld=6144, wq=4096, wk=1024, pq=A16, pk=A16, n=8, nwq=40
 
 @pytest.mark.parametrize("call", [ph, lw, ps, ap], ids=["per_head", "layerwise", "partial", "apply"])
 def test_bad_dtype(lib, call):
-    assert call(lib, dt=2) == q.QKNORM_E_DTYPE
+    assert call(lib, dt=3) == q.QKNORM_E_DTYPE
     assert call(lib, dt=-1) == q.QKNORM_E_DTYPE
+    # fp16 is a valid code (T = 0: validated, nothing launched)
+    assert call(lib, dt=F16, T=0) == q.QKNORM_OK
 
 
 @pytest.mark.parametrize("call", [ph, lw, ap], ids=["per_head", "layerwise", "apply"])
@@ -152,9 +154,22 @@ def test_alignment(lib):
     assert ap(lib, wq=4092, nwq=4096) == q.QKNORM_E_ALIGN  # Q/K boundary off a 16 B vector
 
 
+@pytest.mark.parametrize("dt,D", [(F32, 16), (F32, 32), (F32, 64), (F32, 128), (F32, 256),
+                                  (BF16, 32), (BF16, 64), (BF16, 128), (BF16, 256), (BF16, 512),
+                                  (F16, 32), (F16, 128), (F16, 512)])
+def test_head_widths_accepted(lib, dt, D):
+    # a head is 64 to 1024 bytes, a power of two (T = 0: validated, nothing launched)
+    assert ph(lib, T=0, D=D, ld=20 * D, dt=dt) == q.QKNORM_OK
+
+
 def test_unsupported(lib):
     assert ph(lib, D=96, ld=20 * 96) == q.QKNORM_E_UNSUPPORTED
-    assert ph(lib, D=512, ld=20 * 512) == q.QKNORM_E_UNSUPPORTED
+    assert ph(lib, D=96, ld=20 * 96, T=0) == q.QKNORM_E_UNSUPPORTED   # checked before T == 0
+    assert ph(lib, D=512, ld=20 * 512) == q.QKNORM_E_UNSUPPORTED      # fp32: 2 KiB heads
+    assert ph(lib, D=8, ld=20 * 8) == q.QKNORM_E_UNSUPPORTED          # fp32: 32 B heads
+    assert ph(lib, D=16, ld=20 * 16, dt=BF16) == q.QKNORM_E_UNSUPPORTED
+    assert ph(lib, D=1024, ld=20 * 1024, dt=F16) == q.QKNORM_E_UNSUPPORTED
+    assert ph(lib, D=48, ld=20 * 48, dt=F16) == q.QKNORM_E_UNSUPPORTED
     assert lw(lib, R=2048, wq=4096 * 8, wk=2048 * 8, ld=6144 * 8) == q.QKNORM_E_UNSUPPORTED
     assert ap(lib, n=4096) == q.QKNORM_E_UNSUPPORTED
     # rows are addressed with 32-bit offsets: pitch above 64 MiB is refused

@@ -58,9 +58,9 @@ def check_against_oracle(p, got, label):
     qk = p.wq + p.wk
     assert_close_to_oracle(got[:, :qk], y64[:, :qk], p.dtype, label=label)
     assert_bytes_equal(got[:, qk:], p.x[:, qk:], f"{label}: V/padding columns")
-    if p.dtype == synth.BF16:
-        # one bf16 ulp is the tolerance itself: never more than 1 ulp from the
-        # oracle's own rounding (fp32 I/O is held to its 1e-5 relative bound)
+    if p.dtype in (synth.BF16, synth.F16):
+        # never more than one 16-bit ulp from the oracle's own rounding (fp32
+        # I/O is held to its 1e-5 relative bound)
         hist = ulp_histogram(got[:, :qk], yr[:, :qk], p.dtype)
         assert max(hist) <= 1, f"{label}: ulp histogram {hist}"
 
@@ -88,7 +88,7 @@ def test_cfg4_layerwise(T):
     full_check(synth.cfg4(T=T))
 
 
-@pytest.mark.parametrize("dtype", [synth.F32, synth.BF16])
+@pytest.mark.parametrize("dtype", [synth.F32, synth.BF16, synth.F16])
 @pytest.mark.parametrize("wq,wk,R,T", [
     (4096, 1024, 1, 33),       # one shard: register path, 8 slots per lane
     (4096, 1024, 2, 17),
@@ -157,6 +157,31 @@ def test_tensor_parallel_emulation_matches_fused():
     got = x.cpu().view(torch.int16).numpy().view(np.uint16)
     ref = fused(p)
     assert np.array_equal(got, ref), "rank-sliced two-phase differs from the fused kernel"
+
+
+def test_tensor_parallel_emulation_f16():
+    # the same rank-sliced two-phase form in fp16, against the fused kernel
+    # (bitwise) and the oracle
+    N, T, wq, wk = 8, 48, 4096, 1024
+    p = synth.layerwise_problem("tp_f16", 52, synth.F16, T, wq, wk, wq + 2 * wk, N,
+                                token_scale=(0.5, 2.0), outlier_frac=0.01)
+    sq, sk = wq // N, wk // N
+    x = host_to_device(p.x, p.dtype)
+    gq, gk = _gammas(p)
+    part_q = torch.empty(N, T, dtype=torch.float32, device="cuda")
+    part_k = torch.empty(N, T, dtype=torch.float32, device="cuda")
+    for r in range(N):
+        q.qknorm_partial_sumsq(x[:, r * sq:(r + 1) * sq], sq, 0, 1, part_q[r:r + 1], None)
+        q.qknorm_partial_sumsq(x[:, wq + r * sk:wq + (r + 1) * sk], sk, 0, 1, part_k[r:r + 1], None)
+    for r in range(N):
+        q.qknorm_apply_scalar(x[:, r * sq:(r + 1) * sq], sq, 0, part_q, None, wq, 0,
+                              gq[r * sq:(r + 1) * sq], None, p.eps)
+        q.qknorm_apply_scalar(x[:, wq + r * sk:wq + (r + 1) * sk], sk, 0, part_k, None, wk, 0,
+                              gk[r * sk:(r + 1) * sk], None, p.eps)
+    torch.cuda.synchronize()
+    got = x.cpu().view(torch.int16).numpy().view(np.uint16)
+    ref = full_check(p)
+    assert np.array_equal(got, ref), "rank-sliced fp16 two-phase differs from the fused kernel"
 
 
 def test_bitwise_deterministic():

@@ -26,10 +26,12 @@ def run_per_head(p: synth.Problem, check_ulp=True):
     qk = p.wq + p.wk
     relmax = assert_close_to_oracle(got[:, :qk], y64[:, :qk], p.dtype, label=p.name)
     assert_bytes_equal(got[:, qk:], p.x[:, qk:], f"{p.name}: V/padding columns")
-    if check_ulp and p.dtype == synth.BF16:
+    if check_ulp and p.dtype in (synth.BF16, synth.F16):
+        # fp32 arithmetic is far finer than a 16-bit ulp: at most one ulp from
+        # the oracle's own rounding, and nearly always none
         hist = ulp_histogram(got[:, :qk], yr[:, :qk], p.dtype)
         assert max(hist) <= 1, f"{p.name}: ulp histogram {hist}"
-        if p.dtype == synth.BF16 and qk * p.T > 10000:
+        if qk * p.T > 10000:
             assert hist.get(0, 0) / (qk * p.T) > 0.99, f"{p.name}: ulp histogram {hist}"
     return got, relmax
 
@@ -49,20 +51,26 @@ def test_cfg3_fused_gqa_bf16(T):
     run_per_head(synth.cfg3(T=T))
 
 
-@pytest.mark.parametrize("dtype", [synth.F32, synth.BF16])
-@pytest.mark.parametrize("D", [64, 128, 256])
+ALL_DTYPES = [synth.F32, synth.BF16, synth.F16]
+
+
+@pytest.mark.parametrize("dtype", ALL_DTYPES)
+@pytest.mark.parametrize("D", [16, 32, 64, 128, 256, 512])
 def test_head_dims(dtype, D):
-    # ragged: 37 rows x (5 Q + 3 K) heads, padding after V
+    # every head of 64 to 1024 bytes; ragged: 37 rows x (5 Q + 3 K) heads, padding after V
+    hb = D * (4 if dtype == synth.F32 else 2)
+    if hb < 64 or hb > 1024:
+        pytest.skip(f"{hb}-byte heads are outside the supported 64..1024 bytes")
     p = synth.per_head_problem(f"dims_D{D}", 21, dtype, 37, 5, 3, D, ld=(5 + 6) * D + 64,
                                token_scale=(0.1, 10.0))
     run_per_head(p)
 
 
-@pytest.mark.parametrize("dtype", [synth.F32, synth.BF16])
+@pytest.mark.parametrize("dtype", ALL_DTYPES)
 @pytest.mark.parametrize("T,hq,hkv", [(1, 1, 0), (3, 1, 1), (7, 0, 3), (129, 3, 1), (1000, 7, 2)])
 def test_ragged_head_counts(dtype, T, hq, hkv):
     p = synth.per_head_problem(f"ragged_T{T}_{hq}_{hkv}", 22, dtype, T, hq, hkv, 128,
-                               ld=(hq + 2 * hkv) * 128 + 8 * (dtype == synth.BF16) + 4 * (dtype == synth.F32))
+                               ld=(hq + 2 * hkv) * 128 + (4 if dtype == synth.F32 else 8))
     run_per_head(p)
 
 
@@ -85,7 +93,7 @@ def test_zero_rows_and_eps_zero_closed_forms():
         idx = np.arange(0, D, D // k)[:k]
         x[:, h * D + idx] = 0.75 * np.where(np.arange(k) % 2 == 0, 1.0, -1.0)
         roots[h] = (idx, np.sqrt(D / k))
-    for dtype in (synth.F32, synth.BF16):
+    for dtype in ALL_DTYPES:
         xs = synth.to_dtype(x, dtype)
         g = synth.make_gamma(3, 3, D, dtype)
         for eps in (0.0, synth.eps_f32(1e-6)):
@@ -104,7 +112,7 @@ def test_zero_rows_and_eps_zero_closed_forms():
                 want = np.zeros((T, H * D))
                 for h, (idx, root) in roots.items():
                     want[:, h * D + idx] = oracle.decode(g, dtype)[idx] * np.sign(x[:, h * D + idx]) * root
-                if dtype == synth.BF16:
+                if dtype != synth.F32:
                     assert np.array_equal(got[:, D:], synth.to_dtype(want, dtype)[:, D:]), \
                         "closed form, bit exact"
                 else:
@@ -123,6 +131,34 @@ def test_extreme_magnitudes():
                           synth.make_gamma(31, 3, D, dtype), None, synth.eps_f32(1e-6), hq=H,
                           hkv=0, head_dim=D)
         run_per_head(p, check_ulp=False)
+
+
+def test_extreme_magnitudes_f16():
+    # fp16 spans 2^-24 .. 65504: rows of subnormals, rows near the top of the
+    # range, and whole heads of the smallest and the largest finite value
+    T, H, D = 16, 4, 128
+    z = synth.normal(32, 0, T * H * D).reshape(T, H * D)
+    z *= (10.0 ** np.linspace(-5, 3.5, T))[:, None]
+    z[0, :D] = 2.0 ** -24
+    z[1, :D] = -65504.0
+    z[1, D:2 * D] = np.where(np.arange(D) % 2 == 0, 65504.0, 2.0 ** -24)
+    dtype = synth.F16
+    p = synth.Problem("extreme_f16", dtype, T, H * D, H * D, 0, synth.to_dtype(z, dtype),
+                      synth.make_gamma(32, 3, D, dtype), None, synth.eps_f32(0.0), hq=H,
+                      hkv=0, head_dim=D)
+    got, _ = run_per_head(p, check_ulp=False)
+    gd = oracle.decode(got, dtype)
+    g = oracle.decode(p.gamma_q, dtype)
+    assert np.array_equal(gd[0, :D], g), "a head of equal values normalises to gamma"
+    assert np.array_equal(gd[1, :D], -g)
+
+
+@pytest.mark.parametrize("T", [1, 333, 2048])
+def test_fused_gqa_f16(T):
+    # the fused GQA row of a Qwen3-8B-style layer (32 Q, 8 K, 8 V heads of 128) in fp16
+    p = synth.per_head_problem(f"gqa_f16_T{T}", 24, synth.F16, T, 32, 8, 128,
+                               token_scale=(0.25, 4.0), outlier_frac=0.01)
+    run_per_head(p)
 
 
 def test_bitwise_deterministic():
@@ -184,7 +220,7 @@ def test_graph_replay_matches_eager():
         assert torch.equal(work.view(torch.int16), eager.view(torch.int16))
 
 
-@pytest.mark.parametrize("dtype", [synth.F32, synth.BF16])
+@pytest.mark.parametrize("dtype", ALL_DTYPES)
 @pytest.mark.parametrize("hq,hkv", [(0, 5), (5, 0), (3, 2)])
 def test_rows_without_v_or_padding(dtype, hq, hkv):
     # ld == (hq + hkv) * D: rows back to back; single-region tensors take the

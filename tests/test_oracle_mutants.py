@@ -35,6 +35,15 @@ MUTANTS = {
                            "pass_through(x, dtype, row + wq + wk, ld - wq - wk - 1, y, yr);\n    }\n    return 0;\n}\n\n/* Layerwise"),
     "partials_transposed": ("part_q[(int64_t)r * T + t] = sum_of_squares",
                             "part_q[t * nshards + r] = sum_of_squares"),
+    "f16_exponent_bias_off_by_one": ("v = ldexp((double)(1024 + m), e - 25);",
+                                     "v = ldexp((double)(1024 + m), e - 24);"),
+    "f16_subnormals_flushed": ("v = ldexp((double)m, -24);", "v = 0.0 * m;"),
+    "f16_rounding_truncates": ("double q = nearbyint(ldexp(a, 11 - e));",
+                               "double q = trunc(ldexp(a, 11 - e));"),
+    "f16_overflow_saturates": ("if (r > 65504.0)\n        return sign | 0x7C00;",
+                               "if (r > 65504.0)\n        return sign | 0x7BFF;"),
+    "f16_stored_as_bf16": ("else if (dtype == 2)\n        ((uint16_t *)p)[i] = round_to_f16(v);",
+                           "else if (dtype == 2)\n        ((uint16_t *)p)[i] = round_to_bf16(v);"),
     "gamma_after_divide_by_rms_squared": ("double v = load_value(x, dtype, off + j) * load_value(g, dtype, goff + j) * inv;",
                                           "double v = load_value(x, dtype, off + j) * load_value(g, dtype, goff + j) * inv * inv;"),
 }
