@@ -19,10 +19,15 @@
  *         (Lesson "Explain combined QKV projection and why it's faster than
  *         three separate projections?", section "With GQA": the fused output
  *         is Q heads, then K heads, then V heads, split by those widths.)
- *   dtype QKNORM_F32, QKNORM_BF16 or QKNORM_F16; qkv and gamma share it.
+ *   dtype QKNORM_F32, QKNORM_BF16 or QKNORM_F16: qkv and gamma share it.
+ *         QKNORM_FP8_E4M3: qkv holds OCP FP8 E4M3 values (1 sign, 4 exponent
+ *         bits with bias 7, 3 fraction bits; no infinities; largest finite
+ *         448), unscaled, and gamma is bf16.  (SwiftQK verdict page, Section
+ *         IV-C / Fig. 2(b) and the summary: the activations are BF16 or
+ *         FP8-E4M3, and error is judged at that format.)
  *         Arithmetic is fp32 throughout; each output element is rounded
- *         once, to nearest even, to the I/O dtype.  Partial sums are always
- *         fp32.
+ *         once, to nearest even, to the I/O dtype; FP8 results beyond +-448
+ *         saturate to +-448 (a NaN stays NaN).  Partial sums are always fp32.
  *   eps   fp32, finite, >= 0; added to the mean square inside the root.
  *
  * Ownership, streams and threads
@@ -59,13 +64,14 @@ extern "C" {
 #define QKNORM_F32 0
 #define QKNORM_BF16 1
 #define QKNORM_F16 2
+#define QKNORM_FP8_E4M3 3
 
 /* return codes */
 #define QKNORM_OK 0
 #define QKNORM_E_NULLPTR -1     /* a pointer that would be used is NULL */
 #define QKNORM_E_SHAPE -2       /* negative size, ld too small, shard count does not divide */
 #define QKNORM_E_ALIGN -3       /* base, row pitch, head or shard not a multiple of 16 bytes */
-#define QKNORM_E_DTYPE -4       /* dtype not QKNORM_F32 / QKNORM_BF16 / QKNORM_F16 */
+#define QKNORM_E_DTYPE -4       /* dtype not one of the codes above */
 #define QKNORM_E_UNSUPPORTED -5 /* valid request this build does not implement (e.g. head_dim) */
 #define QKNORM_E_EPS -6         /* eps negative, NaN or infinite */
 #define QKNORM_E_HIP -7         /* the HIP runtime refused the launch or device query */
@@ -81,9 +87,9 @@ extern "C" {
  *  #13189, Motivation and Modifications: the QK norm is an RMSNorm whose
  *  hidden size is the head dimension, 128 in the benchmark tables.)
  *
- * Requires: a head of 64 to 1024 bytes, a power of two (bf16/fp16 head_dim
- * 32..512, fp32 head_dim 16..256); ld >= (hq+hkv)*head_dim; qkv, gamma and
- * ld*esize 16-byte aligned.
+ * Requires: a head of 64 to 1024 bytes, a power of two (FP8 head_dim
+ * 64..1024, bf16/fp16 32..512, fp32 16..256); ld >= (hq+hkv)*head_dim; qkv,
+ * gamma and ld*esize 16-byte aligned.
  */
 int qknorm_per_head(void *qkv, int64_t T, int64_t ld, int32_t hq, int32_t hkv,
                     int32_t head_dim, const void *gamma_q, const void *gamma_k,

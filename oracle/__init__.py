@@ -7,7 +7,8 @@ The arithmetic lives in ``qknorm_oracle.c`` (plain C, fp64, OpenMP over
 tokens); this module only marshals numpy arrays.  Every function returns the
 fp64 result ``y`` (V and padding columns copied through) and the result rounded
 once, to nearest-even, to the I/O dtype ``yr`` (same storage as the input:
-float32, or uint16 bf16 / fp16 bit patterns).
+float32, uint16 bf16 / fp16 bit patterns, or uint8 FP8 E4M3 bytes).  With
+FP8 E4M3 activations gamma is bf16.
 
 Pins (tests/test_oracle_pins.py): unit RMS, scale invariance, the shard-sum
 identity, exact brute force on tiny inputs, closed-form rows, per-head vs
@@ -29,6 +30,7 @@ _LIB = os.path.join(_HERE, "liboracle.so")
 F32 = 0
 BF16 = 1
 F16 = 2
+F8 = 3      # OCP FP8 E4M3 activations, bf16 gamma
 
 _lib = None
 
@@ -73,7 +75,14 @@ def _storage(dtype: int):
         return np.float32
     if dtype in (BF16, F16):
         return np.uint16
+    if dtype == F8:
+        return np.uint8
     raise ValueError(f"unknown dtype code {dtype}")
+
+
+def gamma_dtype(dtype: int) -> int:
+    """gamma shares the activations' dtype, except bf16 with FP8 E4M3."""
+    return BF16 if dtype == F8 else dtype
 
 
 def _arr(a, dtype):
@@ -103,8 +112,8 @@ def per_head(x, dtype, hq, hkv, head_dim, gamma_q, gamma_k, eps, want_y=True):
     """Per-head QK-Norm of fused rows x[T, ld] (Q heads, then K heads, then V)."""
     x, xp = _arr(x, dtype)
     T, ld = x.shape
-    gq_keep, gq = _arr(gamma_q, dtype)
-    gk_keep, gk = _opt(gamma_k, dtype)
+    gq_keep, gq = _arr(gamma_q, gamma_dtype(dtype))
+    gk_keep, gk = _opt(gamma_k, gamma_dtype(dtype))
     y, yr, yp, yrp = _outs(x.shape, dtype, want_y)
     _check(_load().oracle_per_head(xp, dtype, T, ld, hq, hkv, head_dim, gq, gk,
                                    float(eps), yp, yrp), "per_head")
@@ -115,8 +124,8 @@ def layerwise(x, dtype, wq, wk, gamma_q, gamma_k, eps, nshards=1, want_y=True):
     """Layerwise QK-Norm of fused rows over the full Q and K widths via shard sums."""
     x, xp = _arr(x, dtype)
     T, ld = x.shape
-    gq_keep, gq = _opt(gamma_q, dtype)
-    gk_keep, gk = _opt(gamma_k, dtype)
+    gq_keep, gq = _opt(gamma_q, gamma_dtype(dtype))
+    gk_keep, gk = _opt(gamma_k, gamma_dtype(dtype))
     y, yr, yp, yrp = _outs(x.shape, dtype, want_y)
     _check(_load().oracle_layerwise(xp, dtype, T, ld, wq, wk, gq, gk, float(eps), nshards,
                                     yp, yrp), "layerwise")
@@ -143,8 +152,8 @@ def apply(x, dtype, wq, wk, part_q, part_k, norm_wq, norm_wk, gamma_q, gamma_k, 
     pq = np.ascontiguousarray(part_q, dtype=np.float64)
     pk = np.ascontiguousarray(part_k, dtype=np.float64)
     nparts = pq.shape[0]
-    gq_keep, gq = _opt(gamma_q, dtype)
-    gk_keep, gk = _opt(gamma_k, dtype)
+    gq_keep, gq = _opt(gamma_q, gamma_dtype(dtype))
+    gk_keep, gk = _opt(gamma_k, gamma_dtype(dtype))
     y, yr, yp, yrp = _outs(x.shape, dtype, want_y)
     _check(_load().oracle_apply(xp, dtype, T, ld, wq, wk, pq.ctypes.data_as(ctypes.c_void_p),
                                 pk.ctypes.data_as(ctypes.c_void_p), nparts, float(norm_wq),
@@ -161,11 +170,25 @@ def round_to(v, dtype):
     return out
 
 
+def _e4m3_table() -> np.ndarray:
+    """fp64 value of every E4M3 byte, from its fields (bias 7, no infinity)."""
+    b = np.arange(256)
+    e, m = (b >> 3) & 0xF, b & 7
+    mag = np.where(e == 0, m * 2.0 ** -9, (8 + m) * np.exp2(e - 10.0))
+    mag = np.where((e == 15) & (m == 7), np.nan, mag)
+    return np.where(b & 0x80, -mag, mag)
+
+
+_E4M3 = _e4m3_table()
+
+
 def decode(a, dtype):
     """Exact fp64 values of stored elements (bf16 patterns widened)."""
     a = np.asarray(a)
     if dtype == F32:
         return a.astype(np.float64)
+    if dtype == F8:
+        return _E4M3[np.asarray(a, dtype=np.uint8)]
     if dtype == F16:
         return np.ascontiguousarray(a, dtype=np.uint16).view(np.float16).astype(np.float64)
     with np.errstate(invalid="ignore"):

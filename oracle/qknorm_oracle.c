@@ -40,7 +40,13 @@
  * are copied through unchanged; outputs are also given rounded once, to
  * nearest-even, to the I/O dtype.
  *
- * dtype codes: 0 = fp32, 1 = bf16, 2 = fp16 (both stored as 16-bit patterns).
+ * dtype codes: 0 = fp32, 1 = bf16, 2 = fp16 (both stored as 16-bit patterns),
+ * 3 = FP8 E4M3 activations (one byte each) with bf16 gamma.  The FP8 reading:
+ * the "SwiftQK" verdict page (Section IV-C / Fig. 2(b)) and its summary judge
+ * error at the activation format, BF16 or FP8-E4M3; the pages give no scale
+ * factor, so values are taken unscaled, and the weights keep bf16.  E4M3 has
+ * no infinity: results are rounded to nearest-even and anything beyond the
+ * largest finite value, 448, saturates to +-448.
  * Every function returns 0, or -1 on an argument it cannot use.
  */
 #include <math.h>
@@ -66,13 +72,31 @@ static double half_value(uint16_t h)
     return sign ? -v : v;
 }
 
-/* Exact value of element i of a stored fp32, bf16 or fp16 array. */
+/* Exact value of an FP8 E4M3 byte: 1 sign, 4 exponent bits (bias 7), 3
+ * fraction bits; exponent field 15 with fraction 7 is NaN, there is no
+ * infinity. */
+static double e4m3_value(uint8_t b)
+{
+    int sign = b >> 7, e = (b >> 3) & 0xF, m = b & 7;
+    double v;
+    if (e == 0)
+        v = ldexp((double)m, -9);                  /* zero and subnormals */
+    else if (e == 15 && m == 7)
+        v = NAN;
+    else
+        v = ldexp((double)(8 + m), e - 10);
+    return sign ? -v : v;
+}
+
+/* Exact value of element i of a stored fp32, bf16, fp16 or E4M3 array. */
 static double load_value(const void *p, int dtype, int64_t i)
 {
     if (dtype == 0)
         return (double)((const float *)p)[i];
     if (dtype == 2)
         return half_value(((const uint16_t *)p)[i]);
+    if (dtype == 3)
+        return e4m3_value(((const uint8_t *)p)[i]);
     uint32_t bits = (uint32_t)((const uint16_t *)p)[i] << 16;
     float f;
     memcpy(&f, &bits, sizeof f);
@@ -132,10 +156,42 @@ static uint16_t round_to_f16(double v)
     return sign | (uint16_t)((re - 1 + 15) << 10) | frac;
 }
 
+/* Round v to the nearest E4M3 value, ties to even, in one step from fp64:
+ * 4 significant bits, spacing fixed at 2^-9 below 2^-6, and saturation at
+ * +-448 (there is no infinity to overflow to). */
+static uint8_t round_to_e4m3(double v)
+{
+    if (isnan(v))
+        return 0x7F;
+    uint8_t sign = signbit(v) ? 0x80 : 0;
+    double a = fabs(v);
+    if (a == 0.0)
+        return sign;
+    if (a > 448.0)
+        return sign | 0x7E;                /* also infinities */
+    int e;
+    frexp(a, &e);                          /* a = m * 2^e, 0.5 <= m < 1 */
+    if (e < -5)
+        e = -5;
+    double q = nearbyint(ldexp(a, 4 - e));   /* nearest, ties even */
+    double r = ldexp(q, e - 4);              /* <= 448, which is representable */
+    if (r < ldexp(1.0, -6))                /* subnormal (or a zero) */
+        return sign | (uint8_t)ldexp(r, 9);
+    int re;
+    double rm = frexp(r, &re);             /* r = rm * 2^re, rm in [0.5, 1) */
+    uint8_t frac = (uint8_t)(ldexp(rm, 4) - 8.0);
+    return sign | (uint8_t)((re - 1 + 7) << 3) | frac;
+}
+
+/* gamma is stored in the activations' dtype, except bf16 with E4M3. */
+static int gamma_dtype(int dtype) { return dtype == 3 ? 1 : dtype; }
+
 static void store_rounded(void *p, int dtype, int64_t i, double v)
 {
     if (dtype == 0)
         ((float *)p)[i] = (float)v;          /* C conversion: nearest, ties even */
+    else if (dtype == 3)
+        ((uint8_t *)p)[i] = round_to_e4m3(v);
     else if (dtype == 2)
         ((uint16_t *)p)[i] = round_to_f16(v);
     else
@@ -146,6 +202,8 @@ static void copy_raw(void *dst, const void *src, int dtype, int64_t i)
 {
     if (dtype == 0)
         ((float *)dst)[i] = ((const float *)src)[i];
+    else if (dtype == 3)
+        ((uint8_t *)dst)[i] = ((const uint8_t *)src)[i];
     else
         ((uint16_t *)dst)[i] = ((const uint16_t *)src)[i];
 }
@@ -172,7 +230,7 @@ static void apply_group(const void *x, int dtype, int64_t off, int64_t width,
 {
     double inv = 1.0 / sqrt(S / n + eps);
     for (int64_t j = 0; j < width; ++j) {
-        double v = load_value(x, dtype, off + j) * load_value(g, dtype, goff + j) * inv;
+        double v = load_value(x, dtype, off + j) * load_value(g, gamma_dtype(dtype), goff + j) * inv;
         if (y)
             y[off + j] = v;
         if (yr)
@@ -204,7 +262,7 @@ static double sharded_total(const void *x, int dtype, int64_t off, int64_t width
     return S;
 }
 
-static int bad_dtype(int dtype) { return dtype != 0 && dtype != 1 && dtype != 2; }
+static int bad_dtype(int dtype) { return dtype < 0 || dtype > 3; }
 
 /* ------------------------------------------------------------ entry points -- */
 

@@ -12,7 +12,9 @@ The four entry points keep the C names and semantics (``include/qknorm.h``):
     qknorm_partial_sumsq(qkv, wq, wk, nshards, part_q, part_k)
     qknorm_apply_scalar(qkv, wq, wk, part_q, part_k, norm_wq, norm_wk, gamma_q, gamma_k, eps)
 
-``qkv`` is a [T, ...] tensor whose rows are contiguous within themselves
+``qkv`` is float32, bfloat16 or float16 with gamma of the same dtype, or
+float8_e4m3fn with bfloat16 gamma.  It is a [T, ...] tensor whose rows are
+contiguous within themselves
 (``stride(-1) == 1`` and each row packed); its row pitch is ``stride(0)``.
 All calls normalise in place and are enqueued on ``stream`` (default: torch's
 current stream).
@@ -28,6 +30,7 @@ LIB_PATH = os.path.join(HERE, "libqknorm.so")
 QKNORM_F32 = 0
 QKNORM_BF16 = 1
 QKNORM_F16 = 2
+QKNORM_FP8_E4M3 = 3
 QKNORM_OK = 0
 QKNORM_E_NULLPTR = -1
 QKNORM_E_SHAPE = -2
@@ -91,7 +94,10 @@ def _dtype_code(t) -> int:
         return QKNORM_BF16
     if t.dtype == torch.float16:
         return QKNORM_F16
-    raise ValueError(f"QK-Norm supports float32, bfloat16 and float16 tensors, not {t.dtype}")
+    if t.dtype == torch.float8_e4m3fn:
+        return QKNORM_FP8_E4M3
+    raise ValueError("QK-Norm supports float32, bfloat16, float16 and float8_e4m3fn tensors, "
+                     f"not {t.dtype}")
 
 
 def _rows(qkv):
@@ -119,10 +125,12 @@ def _ptr(t, dev=None):
 
 
 def _gamma(g, qkv):
+    import torch
     if g is None:
         return None
-    if g.dtype != qkv.dtype:
-        raise ValueError("gamma must have the dtype of qkv")
+    want = torch.bfloat16 if qkv.dtype == torch.float8_e4m3fn else qkv.dtype
+    if g.dtype != want:
+        raise ValueError(f"gamma must be {want} for {qkv.dtype} activations")
     if not g.is_contiguous():
         raise ValueError("gamma must be contiguous")
     return _ptr(g, qkv.device)
@@ -200,4 +208,5 @@ def qknorm_apply_scalar(qkv, wq: int, wk: int, part_q, part_k, norm_wq: int, nor
 
 
 __all__ = ["qknorm_per_head", "qknorm_layerwise", "qknorm_partial_sumsq", "qknorm_apply_scalar",
-           "strerror", "abi_version", "load", "QKNormError", "QKNORM_F32", "QKNORM_BF16", "QKNORM_F16"]
+           "strerror", "abi_version", "load", "QKNormError", "QKNORM_F32", "QKNORM_BF16", "QKNORM_F16",
+           "QKNORM_FP8_E4M3"]

@@ -14,10 +14,13 @@ constexpr int64_t kMaxPitchBytes = INT64_C(1) << 26;
 constexpr int64_t kMaxHeadIndex = INT64_C(1) << 31;   // T * heads must stay below this
 constexpr int64_t kMaxRows = (INT64_C(1) << 31) - (INT64_C(1) << 20);
 
-int esize_of(int32_t dtype) { return dtype == QKNORM_F32 ? 4 : 2; }
+int esize_of(int32_t dtype) {
+  return dtype == QKNORM_F32 ? 4 : (dtype == QKNORM_FP8_E4M3 ? 1 : 2);
+}
 
 bool known_dtype(int32_t dtype) {
-  return dtype == QKNORM_F32 || dtype == QKNORM_BF16 || dtype == QKNORM_F16;
+  return dtype == QKNORM_F32 || dtype == QKNORM_BF16 || dtype == QKNORM_F16 ||
+         dtype == QKNORM_FP8_E4M3;
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }

@@ -1,7 +1,7 @@
 // Device-side building blocks for the gfx950 QK-Norm kernels.
 //
 // Everything here works on 16-byte vectors (one 16-byte load / store per
-// lane): 8 bf16 or fp16 values, or 4 fp32 values.  Sums of squares
+// lane): 16 FP8-E4M3 values, 8 bf16 or fp16 values, or 4 fp32 values.  Sums of squares
 // are fp32; cross-lane reduction uses DPP row operations inside 16-lane rows
 // and the gfx950 permlane swaps across rows, so no LDS is touched.
 #pragma once
@@ -15,20 +15,39 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
-enum : int { kF32 = 0, kBF16 = 1, kF16 = 2 };
+enum : int { kF32 = 0, kBF16 = 1, kF16 = 2, kFP8 = 3 };
 
+// kGammaDt: the dtype gamma is stored in.  It is the activations' own dtype,
+// except that FP8 activations keep bf16 weights.
 template <int DT> struct IoTraits;
 template <> struct IoTraits<kF32> {
   static constexpr int kElems = 4;   // values per 16-byte vector
   static constexpr int kBytes = 4;
+  static constexpr int kGammaDt = kF32;
 };
 template <> struct IoTraits<kBF16> {
   static constexpr int kElems = 8;
   static constexpr int kBytes = 2;
+  static constexpr int kGammaDt = kBF16;
 };
 template <> struct IoTraits<kF16> {
   static constexpr int kElems = 8;
   static constexpr int kBytes = 2;
+  static constexpr int kGammaDt = kF16;
+};
+template <> struct IoTraits<kFP8> {
+  static constexpr int kElems = 16;
+  static constexpr int kBytes = 1;
+  static constexpr int kGammaDt = kBF16;
+};
+
+// The gamma values that pair with one 16-byte activation vector: one 16-byte
+// vector, or two when gamma is wider than the activations (FP8 with bf16).
+template <int DT>
+struct Gam {
+  static constexpr int kVecs =
+      IoTraits<DT>::kElems * IoTraits<IoTraits<DT>::kGammaDt>::kBytes / 16;
+  u32x4 v[kVecs];
 };
 
 // ----------------------------------------------------------------- memory --
@@ -75,15 +94,44 @@ __device__ __forceinline__ u32x4 load16(const void* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }
 
+// Gamma for activation vector `vec` (gamma element index = activation index).
+template <int DT>
+__device__ __forceinline__ Gam<DT> load_gamma(const uint8_t* __restrict__ gamma, uint64_t vec) {
+  Gam<DT> g;
+#pragma unroll
+  for (int i = 0; i < Gam<DT>::kVecs; ++i) g.v[i] = load16(gamma + (vec * Gam<DT>::kVecs + i) * 16);
+  return g;
+}
+
+template <int DT>
+__device__ __forceinline__ Gam<DT> zero_gamma() {
+  Gam<DT> g;
+#pragma unroll
+  for (int i = 0; i < Gam<DT>::kVecs; ++i) g.v[i] = u32x4{0, 0, 0, 0};
+  return g;
+}
+
 // Force a value the compiler cannot prove uniform into an SGPR.
 __device__ __forceinline__ uint32_t uniform(uint32_t v) { return __builtin_amdgcn_readfirstlane(v); }
 
 // ------------------------------------------------------------ conversions --
 
-// Widen one 16-byte vector to fp32 (exact for both dtypes).
+// Widen one 16-byte vector to fp32 (exact for every dtype).
 template <int DT>
 __device__ __forceinline__ void unpack(u32x4 v, float (&f)[IoTraits<DT>::kElems]) {
-  if constexpr (DT == kBF16) {
+  if constexpr (DT == kFP8) {
+    // v_cvt_pk_f32_fp8 decodes two OCP E4M3 bytes of a dword (low or high word)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int w = (int)v[i];
+      const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
+      const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
+      f[4 * i] = lo[0];
+      f[4 * i + 1] = lo[1];
+      f[4 * i + 2] = hi[0];
+      f[4 * i + 3] = hi[1];
+    }
+  } else if constexpr (DT == kBF16) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       f[2 * i] = __uint_as_float(v[i] << 16);
@@ -105,12 +153,29 @@ __device__ __forceinline__ void unpack(u32x4 v, float (&f)[IoTraits<DT>::kElems]
   }
 }
 
+// E4M3 has no infinity and its largest finite value is 448.  The hardware
+// conversion rounds nearest-even in range but turns magnitudes that round
+// past 448 into NaN; results are saturated to +-448 first instead (a NaN
+// fails the comparison and stays NaN).
+__device__ __forceinline__ float saturate_e4m3(float x) {
+  return __builtin_fabsf(x) > 448.f ? __builtin_copysignf(448.f, x) : x;
+}
+
 // Round fp32 to the I/O dtype (bf16: v_cvt_pk_bf16_f32; fp16: v_cvt_f16_f32;
-// both nearest-even) and pack.
+// FP8: v_cvt_pk_fp8_f32 after saturation; all nearest-even) and pack.
 template <int DT>
 __device__ __forceinline__ u32x4 pack(const float (&f)[IoTraits<DT>::kElems]) {
   u32x4 v;
-  if constexpr (DT == kBF16) {
+  if constexpr (DT == kFP8) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      int w = __builtin_amdgcn_cvt_pk_fp8_f32(saturate_e4m3(f[4 * i]), saturate_e4m3(f[4 * i + 1]),
+                                              0, false);
+      w = __builtin_amdgcn_cvt_pk_fp8_f32(saturate_e4m3(f[4 * i + 2]), saturate_e4m3(f[4 * i + 3]),
+                                          w, true);
+      v[i] = (uint32_t)w;
+    }
+  } else if constexpr (DT == kBF16) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       bf16x2 h = {(__bf16)f[2 * i], (__bf16)f[2 * i + 1]};
@@ -127,6 +192,20 @@ __device__ __forceinline__ u32x4 pack(const float (&f)[IoTraits<DT>::kElems]) {
     for (int i = 0; i < 4; ++i) v[i] = __float_as_uint(f[i]);
   }
   return v;
+}
+
+// Widen the gamma of one activation vector to fp32.
+template <int DT>
+__device__ __forceinline__ void unpack_gamma(const Gam<DT>& g, float (&f)[IoTraits<DT>::kElems]) {
+  constexpr int GD = IoTraits<DT>::kGammaDt;
+  constexpr int P = IoTraits<GD>::kElems;
+#pragma unroll
+  for (int i = 0; i < Gam<DT>::kVecs; ++i) {
+    float t[P];
+    unpack<GD>(g.v[i], t);
+#pragma unroll
+    for (int e = 0; e < P; ++e) f[i * P + e] = t[e];
+  }
 }
 
 // Sum of squares of one vector, left to right, one fused multiply-add each.

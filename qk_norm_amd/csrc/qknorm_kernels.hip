@@ -36,19 +36,23 @@ namespace qknorm {
 #endif
 static constexpr bool kGammaSgpr = QKNORM_PH_GAMMA_SGPR != 0;
 
-// The 4*LPH gamma dwords of a head, read at uniform addresses (scalar loads),
-// then lane group `sub` keeps dwords 4*sub .. 4*sub+3.
-template <int LPH>
+// The N = 4*GV*LPH gamma dwords of a head (GV 16-byte gamma vectors per
+// activation vector), read at uniform addresses (scalar loads); lane group
+// `sub` then keeps dwords N/LPH*sub .. N/LPH*(sub+1)-1.  `out` starts at zero.
+template <int DT, int LPH>
 __device__ __forceinline__ void gamma_to_lanes(const uint32_t* __restrict__ g, uint32_t sub,
-                                               u32x4& out) {
-  uint32_t w[4 * LPH];
+                                               Gam<DT>& out) {
+  constexpr int GV = Gam<DT>::kVecs;
+  uint32_t w[4 * GV * LPH];
 #pragma unroll
-  for (int k = 0; k < 4 * LPH; ++k) w[k] = g[k];   // all loads first (batched scalar loads)
+  for (int k = 0; k < 4 * GV * LPH; ++k) w[k] = g[k];   // all loads first (batched scalar loads)
 #pragma unroll
   for (uint32_t j = 0; j < LPH; ++j) {
     const uint32_t mask = 0u - (uint32_t)(sub == j);  // all ones in lane group j
 #pragma unroll
-    for (int i = 0; i < 4; ++i) out[i] |= w[j * 4 + i] & mask;
+    for (int q = 0; q < GV; ++q)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) out.v[q][i] |= w[(j * GV + q) * 4 + i] & mask;
   }
 }
 
@@ -178,21 +182,24 @@ __global__ __launch_bounds__(QKNORM_PH_THREADS) void per_head_kernel(
   __builtin_amdgcn_sched_barrier(0);           // keep the row loads ahead of the gamma work
 
   // gamma: a vector load of the same few lines by every wave of the grid
-  // makes those lines an L2 hot spot.  Short heads (LPH <= 16, at most 64
-  // dwords of gamma) read the region's gamma with scalar loads through the
-  // scalar cache and hand each lane its 4 dwords with selects, which run
-  // while the row loads are in flight; longer heads stage it once per block
-  // in LDS.
+  // makes those lines an L2 hot spot.  Heads with at most 64 dwords of gamma
+  // read the region's gamma with scalar loads through the scalar cache and
+  // hand each lane its dwords with selects, which run while the row loads are
+  // in flight; longer ones stage it once per block in LDS.
+  constexpr int GV = Gam<DT>::kVecs;
   float g[E];
-  if constexpr (kGammaSgpr && LPH <= 16) {
-    u32x4 w = {0, 0, 0, 0};
-    gamma_to_lanes<LPH>(reinterpret_cast<const uint32_t*>(gamma), sub, w);
-    unpack<DT>(w, g);
+  if constexpr (kGammaSgpr && 4 * GV * LPH <= 64) {
+    Gam<DT> w = zero_gamma<DT>();
+    gamma_to_lanes<DT, LPH>(reinterpret_cast<const uint32_t*>(gamma), sub, w);
+    unpack_gamma<DT>(w, g);
   } else {
-    __shared__ u32x4 g_lds[LPH];
-    if (threadIdx.x < LPH) g_lds[threadIdx.x] = load16(gamma + threadIdx.x * 16);
+    __shared__ u32x4 g_lds[LPH * GV];
+    if (threadIdx.x < LPH * GV) g_lds[threadIdx.x] = load16(gamma + threadIdx.x * 16);
     __syncthreads();
-    unpack<DT>(g_lds[sub], g);
+    Gam<DT> w;
+#pragma unroll
+    for (int q = 0; q < GV; ++q) w.v[q] = g_lds[sub * GV + q];
+    unpack_gamma<DT>(w, g);
   }
   if (!live) return;
 
@@ -251,23 +258,23 @@ __device__ __forceinline__ float combine(const float* __restrict__ p, uint32_t n
 // Slot j of a lane is shard wave + (j / trips)*nw, vector lane + (j % trips)*64.
 // The slot loops are fully unrolled so the kept vectors stay in VGPRs.
 
-template <int VPL>
+template <int DT, int VPL>
 struct Slots {
   u32x4 x[VPL];
-  u32x4 g[VPL];
+  Gam<DT> g[VPL];
 };
 
 template <int DT, int VPL>
 __device__ __forceinline__ void slots_load_gamma(const uint8_t* __restrict__ gamma, uint32_t svecs,
                                                  uint32_t R, uint32_t wave, uint32_t nw,
-                                                 uint32_t lane, Slots<VPL>& S) {
+                                                 uint32_t lane, Slots<DT, VPL>& S) {
   const uint32_t trips = (svecs + 63) / 64;
   uint32_t i = 0, k = 0;
 #pragma unroll
   for (int j = 0; j < VPL; ++j) {
     const uint32_t r = wave + i * nw, v = lane + k * 64;
-    S.g[j] = (r < R && v < svecs) ? load16(gamma + ((uint64_t)r * svecs + v) * 16)
-                                  : u32x4{0, 0, 0, 0};
+    S.g[j] = (r < R && v < svecs) ? load_gamma<DT>(gamma, (uint64_t)r * svecs + v)
+                                  : zero_gamma<DT>();
     if (++k == trips) { k = 0; ++i; }
   }
 }
@@ -280,7 +287,7 @@ constexpr uint32_t kOutOfRange = 0xFFFFFFF0u;
 template <int DT, int VPL>
 __device__ __forceinline__ void slots_load(Rsrc rs, uint32_t reg_off, uint32_t svecs, uint32_t R,
                                            uint32_t wave, uint32_t nw, uint32_t lane,
-                                           Slots<VPL>& S) {
+                                           Slots<DT, VPL>& S) {
   const uint32_t trips = (svecs + 63) / 64;
   uint32_t i = 0, k = 0;
 #pragma unroll
@@ -293,7 +300,7 @@ __device__ __forceinline__ void slots_load(Rsrc rs, uint32_t reg_off, uint32_t s
 
 template <int DT, int VPL>
 __device__ __forceinline__ void slots_partials(uint32_t svecs, uint32_t R, uint32_t wave,
-                                               uint32_t nw, uint32_t lane, const Slots<VPL>& S,
+                                               uint32_t nw, uint32_t lane, const Slots<DT, VPL>& S,
                                                float* __restrict__ part) {
   using IO = IoTraits<DT>;
   const uint32_t trips = (svecs + 63) / 64;
@@ -319,7 +326,7 @@ __device__ __forceinline__ void slots_partials(uint32_t svecs, uint32_t R, uint3
 template <int DT, int VPL>
 __device__ __forceinline__ void slots_apply(Rsrc rs, uint32_t reg_off, uint32_t svecs, uint32_t R,
                                             uint32_t wave, uint32_t nw, uint32_t lane,
-                                            const Slots<VPL>& S, float scale) {
+                                            const Slots<DT, VPL>& S, float scale) {
   using IO = IoTraits<DT>;
   const uint32_t trips = (svecs + 63) / 64;
   uint32_t i = 0, k = 0;
@@ -328,7 +335,7 @@ __device__ __forceinline__ void slots_apply(Rsrc rs, uint32_t reg_off, uint32_t 
     const uint32_t r = wave + i * nw, v = lane + k * 64;
     float x[IO::kElems], g[IO::kElems], y[IO::kElems];
     unpack<DT>(S.x[j], x);
-    unpack<DT>(S.g[j], g);
+    unpack_gamma<DT>(S.g[j], g);
 #pragma unroll
     for (int e = 0; e < IO::kElems; ++e) y[e] = (x[e] * g[e]) * scale;
     stream_store(rs, (r < R && v < svecs) ? reg_off + (r * svecs + v) * 16 : kOutOfRange,
@@ -362,7 +369,7 @@ __device__ __forceinline__ void apply_stream(Rsrc rs, uint32_t reg_off,
   for (uint32_t v = tid; v < nvecs; v += nthreads) {
     float x[IO::kElems], g[IO::kElems], y[IO::kElems];
     unpack<DT>(stream_load(rs, reg_off + v * 16), x);
-    unpack<DT>(load16(gamma + (uint64_t)v * 16), g);
+    unpack_gamma<DT>(load_gamma<DT>(gamma, v), g);
 #pragma unroll
     for (int e = 0; e < IO::kElems; ++e) y[e] = (x[e] * g[e]) * scale;
     stream_store(rs, reg_off + v * 16, pack<DT>(y));
@@ -381,16 +388,16 @@ __device__ __forceinline__ Rsrc row_rsrc(const uint8_t* qkv, uint64_t ld_bytes, 
 // reduced, combined and stored, the next row's loads are already in flight in
 // the other set (no register copies between them, so nothing forces a wait on
 // the previous row's stores).
-template <int QV, int KV>
+template <int DT, int QV, int KV>
 struct LwRow {
-  Slots<QV> q;
-  Slots<KV> k;
+  Slots<DT, QV> q;
+  Slots<DT, KV> k;
 };
 
 template <int DT, int QV, int KV>
 __device__ __forceinline__ void lw_issue(uint8_t* qkv, const RowGeom& G, uint32_t t, bool live,
                                          uint32_t Rq, uint32_t Rk, uint32_t wave, uint32_t nw,
-                                         uint32_t lane, Rsrc& rs, LwRow<QV, KV>& row) {
+                                         uint32_t lane, Rsrc& rs, LwRow<DT, QV, KV>& row) {
   rs = row_rsrc(qkv, G.ld_bytes, live ? t : 0, live ? G.q_vecs + G.k_vecs : 0);
   slots_load<DT, QV>(rs, 0, G.q_svecs, Rq, wave, nw, lane, row.q);
   slots_load<DT, KV>(rs, G.q_vecs * 16, G.k_svecs, Rk, wave, nw, lane, row.k);
@@ -399,7 +406,7 @@ __device__ __forceinline__ void lw_issue(uint8_t* qkv, const RowGeom& G, uint32_
 template <int DT, int QV, int KV>
 __device__ __forceinline__ void lw_finish(const RowGeom& G, Rsrc rs, uint32_t Rq, uint32_t Rk,
                                           uint32_t wave, uint32_t nw, uint32_t lane, float eps,
-                                          LwRow<QV, KV>& row, const LwRow<QV, KV>& gam,
+                                          LwRow<DT, QV, KV>& row, const LwRow<DT, QV, KV>& gam,
                                           float* __restrict__ part) {
   const uint32_t R = G.nshards;
   float* pq = part;
@@ -431,7 +438,7 @@ __global__ __launch_bounds__(512) void layerwise_regs_kernel(
   const uint32_t stride = gridDim.x;
 
   uint32_t t = blockIdx.x;
-  LwRow<QV, KV> a, b, gam;
+  LwRow<DT, QV, KV> a, b, gam;
   Rsrc ra, rb;
   lw_issue<DT, QV, KV>(qkv, G, t, t < G.T, Rq, Rk, wave, nw, lane, ra, a);
   slots_load_gamma<DT, QV>(gamma_q, G.q_svecs, Rq, wave, nw, lane, gam.q);
@@ -593,7 +600,7 @@ __device__ __forceinline__ void apply_rows_load(Rsrc rs, uint32_t tid, uint32_t 
 template <int DT, int VPT>
 __device__ __forceinline__ void apply_rows_store(Rsrc rs, uint32_t tid, uint32_t nt,
                                                  uint32_t q_vecs, uint32_t nv,
-                                                 const u32x4 (&x)[VPT], const u32x4 (&g)[VPT],
+                                                 const u32x4 (&x)[VPT], const Gam<DT> (&g)[VPT],
                                                  float sq, float sk) {
   using IO = IoTraits<DT>;
 #pragma unroll
@@ -601,7 +608,7 @@ __device__ __forceinline__ void apply_rows_store(Rsrc rs, uint32_t tid, uint32_t
     const uint32_t v = tid + k * nt;
     float xf[IO::kElems], gf[IO::kElems], y[IO::kElems];
     unpack<DT>(x[k], xf);
-    unpack<DT>(g[k], gf);
+    unpack_gamma<DT>(g[k], gf);
     const float sc = v < q_vecs ? sq : sk;
 #pragma unroll
     for (int e = 0; e < IO::kElems; ++e) y[e] = (xf[e] * gf[e]) * sc;
@@ -619,12 +626,12 @@ __global__ __launch_bounds__(512) void apply_scalar_kernel(
   __shared__ float scale[2][kApplyRows];
   const uint32_t tid = threadIdx.x, nt = blockDim.x;
   const uint32_t nv = q_vecs + k_vecs;
-  u32x4 g[VPT];
+  Gam<DT> g[VPT];
 #pragma unroll
   for (int k = 0; k < VPT; ++k) {
     const uint32_t v = tid + k * nt;
-    g[k] = v < q_vecs ? load16(gamma_q + (uint64_t)v * 16)
-                      : (v < nv ? load16(gamma_k + (uint64_t)(v - q_vecs) * 16) : u32x4{0, 0, 0, 0});
+    g[k] = v < q_vecs ? load_gamma<DT>(gamma_q, v)
+                      : (v < nv ? load_gamma<DT>(gamma_k, v - q_vecs) : zero_gamma<DT>());
   }
   for (uint32_t t0 = blockIdx.x * kApplyRows; t0 < T; t0 += gridDim.x * kApplyRows) {
     const uint32_t rows = T - t0 < kApplyRows ? T - t0 : kApplyRows;
@@ -743,6 +750,7 @@ hipError_t launch_per_head(const PerHeadArgs& a, hipStream_t s, int cus) {
   switch (a.dtype) {
     case kBF16: return launch_per_head_dt<kBF16>(a, s, cus);
     case kF16: return launch_per_head_dt<kF16>(a, s, cus);
+    case kFP8: return launch_per_head_dt<kFP8>(a, s, cus);
     default: return launch_per_head_dt<kF32>(a, s, cus);
   }
 }
@@ -789,13 +797,27 @@ static hipError_t launch_lw_regs(const RowGeom& G, uint32_t nw, const LayerwiseA
 
 static int slot_class(uint32_t n) { return n <= 1 ? 1 : n <= 2 ? 2 : n <= 4 ? 4 : 0; }
 
+// Rows too wide for the register slots.
+template <int DT>
+static hipError_t launch_lw_stream(const RowGeom& G, uint32_t nw, const LayerwiseArgs& a,
+                                   hipStream_t s, int cus) {
+  hipLaunchKernelGGL((layerwise_stream_kernel<DT>), dim3(row_blocks(G.T, nw, cus)), dim3(nw * 64),
+                     (size_t)4 * G.nshards * sizeof(float), s, (uint8_t*)a.qkv, G,
+                     (const uint8_t*)a.gamma_q, (const uint8_t*)a.gamma_k, a.eps);
+  return hipGetLastError();
+}
+
 template <int DT, int QV>
 static hipError_t launch_lw_regs_k(const RowGeom& G, uint32_t nw, int kc, const LayerwiseArgs& a,
                                    hipStream_t s, int cus) {
   switch (kc) {
     case 1: return launch_lw_regs<DT, QV, 1>(G, nw, a, s, cus);
     case 2: return launch_lw_regs<DT, QV, 2>(G, nw, a, s, cus);
-    default: return launch_lw_regs<DT, QV, 4>(G, nw, a, s, cus);
+    default:
+      // FP8 slots carry two gamma vectors each: four Q and four K slots would
+      // not fit in registers
+      if constexpr (DT == kFP8 && QV == 4) return launch_lw_stream<DT>(G, nw, a, s, cus);
+      else return launch_lw_regs<DT, QV, 4>(G, nw, a, s, cus);
   }
 }
 
@@ -812,17 +834,14 @@ static hipError_t launch_layerwise_dt(const LayerwiseArgs& a, hipStream_t s, int
       default: return launch_lw_regs_k<DT, 4>(G, nw, kc, a, s, cus);
     }
   }
-  // rows too wide for the register slots
-  hipLaunchKernelGGL((layerwise_stream_kernel<DT>), dim3(row_blocks(G.T, nw, cus)), dim3(nw * 64),
-                     (size_t)4 * G.nshards * sizeof(float), s, (uint8_t*)a.qkv, G,
-                     (const uint8_t*)a.gamma_q, (const uint8_t*)a.gamma_k, a.eps);
-  return hipGetLastError();
+  return launch_lw_stream<DT>(G, nw, a, s, cus);
 }
 
 hipError_t launch_layerwise(const LayerwiseArgs& a, hipStream_t s, int cus) {
   switch (a.dtype) {
     case kBF16: return launch_layerwise_dt<kBF16>(a, s, cus);
     case kF16: return launch_layerwise_dt<kF16>(a, s, cus);
+    case kFP8: return launch_layerwise_dt<kFP8>(a, s, cus);
     default: return launch_layerwise_dt<kF32>(a, s, cus);
   }
 }
@@ -845,6 +864,7 @@ hipError_t launch_partial_sumsq(const PartialArgs& a, hipStream_t s, int cus) {
   switch (a.dtype) {
     case kBF16: return launch_partial_dt<kBF16>(a, s, cus);
     case kF16: return launch_partial_dt<kF16>(a, s, cus);
+    case kFP8: return launch_partial_dt<kFP8>(a, s, cus);
     default: return launch_partial_dt<kF32>(a, s, cus);
   }
 }
@@ -889,6 +909,7 @@ hipError_t launch_apply_scalar(const ApplyArgs& a, hipStream_t s, int cus) {
   switch (a.dtype) {
     case kBF16: return launch_apply_dt<kBF16>(a, s, cus);
     case kF16: return launch_apply_dt<kF16>(a, s, cus);
+    case kFP8: return launch_apply_dt<kFP8>(a, s, cus);
     default: return launch_apply_dt<kF32>(a, s, cus);
   }
 }

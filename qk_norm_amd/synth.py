@@ -27,7 +27,8 @@ Rounding to bf16 is round-to-nearest-even taken directly from the fp64 value
 (no intermediate fp32 step); fp32 and fp16 use numpy's own RNE casts (numpy
 rounds fp64 to fp16 directly).
 
-bf16 and fp16 arrays are returned as ``np.uint16`` bit patterns.
+bf16 and fp16 arrays are returned as ``np.uint16`` bit patterns, FP8 E4M3 as
+``np.uint8`` bytes (nearest-even, magnitudes past 448 saturate to 448).
 """
 from __future__ import annotations
 
@@ -41,7 +42,17 @@ import numpy as np
 F32 = 0
 BF16 = 1
 F16 = 2
-DTYPE_NAMES = {F32: "f32", BF16: "bf16", F16: "f16"}
+F8 = 3      # OCP FP8 E4M3 activations; gamma stays bf16
+DTYPE_NAMES = {F32: "f32", BF16: "bf16", F16: "f16", F8: "fp8e4m3"}
+
+
+def gamma_dtype(dtype: int) -> int:
+    """Storage dtype of gamma: the activations' own, except bf16 with FP8."""
+    return BF16 if dtype == F8 else dtype
+
+
+def esize(dtype: int) -> int:
+    return {F32: 4, BF16: 2, F16: 2, F8: 1}[dtype]
 
 _GOLDEN = np.uint64(0x9E3779B97F4A7C15)
 _M1 = np.uint64(0xBF58476D1CE4E5B9)
@@ -137,6 +148,22 @@ def round_bf16_bits(v: np.ndarray) -> np.ndarray:
     return (f.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
 
 
+def round_e4m3_bits(v: np.ndarray) -> np.ndarray:
+    """fp64 -> OCP E4M3 bytes: nearest, ties to even, in one step; 4 significant
+    bits, fixed spacing 2^-9 below 2^-6, saturation at +-448 (no infinity)."""
+    v = np.asarray(v, dtype=np.float64)
+    a = np.minimum(np.abs(v), 512.0)         # anything above 448 saturates below
+    _, e = np.frexp(a)                       # a = m * 2**e, 0.5 <= m < 1
+    e = np.maximum(e, -5)
+    r = np.minimum(np.ldexp(np.rint(np.ldexp(a, 4 - e)), e - 4), 448.0)
+    rm, re = np.frexp(r)
+    normal = (re - 1 + 7) * 8 + (np.ldexp(rm, 4) - 8)
+    code = np.where(r < 2.0 ** -6, np.ldexp(r, 9), normal).astype(np.int64)
+    code = np.where(np.signbit(v), code | 0x80, code)
+    code = np.where(np.isnan(v), 0x7F, code)
+    return code.astype(np.uint8)
+
+
 def to_dtype(v: np.ndarray, dtype: int) -> np.ndarray:
     if dtype == F32:
         return np.asarray(v, dtype=np.float64).astype(np.float32)
@@ -146,6 +173,8 @@ def to_dtype(v: np.ndarray, dtype: int) -> np.ndarray:
         # numpy rounds fp64 -> binary16 directly, nearest-even
         with np.errstate(over="ignore"):
             return np.asarray(v, dtype=np.float64).astype(np.float16).view(np.uint16)
+    if dtype == F8:
+        return round_e4m3_bits(v)
     raise ValueError(f"unknown dtype code {dtype}")
 
 
@@ -189,7 +218,7 @@ class Problem:
 
     @property
     def esize(self) -> int:
-        return 4 if self.dtype == F32 else 2
+        return esize(self.dtype)
 
 
 def make_x(seed: int, T: int, ncols: int, dtype: int, *, token_scale=None,
@@ -208,7 +237,8 @@ def make_x(seed: int, T: int, ncols: int, dtype: int, *, token_scale=None,
 
 
 def make_gamma(seed: int, stream: int, n: int, dtype: int) -> np.ndarray:
-    return to_dtype(0.5 + uniform(seed, stream, n), dtype)
+    """gamma = U(0.5, 1.5), stored in the gamma dtype that goes with `dtype`."""
+    return to_dtype(0.5 + uniform(seed, stream, n), gamma_dtype(dtype))
 
 
 def eps_f32(eps: float) -> float:

@@ -8,21 +8,26 @@ import torch
 import oracle
 from qk_norm_amd import synth
 
-RTOL = {synth.F32: 1e-5, synth.BF16: 8e-3, synth.F16: 1e-3}
-# fp16 outputs can be subnormal, where the spacing is fixed at 2^-24
-ATOL = {synth.F32: 0.0, synth.BF16: 0.0, synth.F16: 2.0 ** -24}
+RTOL = {synth.F32: 1e-5, synth.BF16: 8e-3, synth.F16: 1e-3, synth.F8: 0.125}
+# fp16 and E4M3 outputs can be subnormal, where the spacing is fixed
+# (2^-24 and 2^-9)
+ATOL = {synth.F32: 0.0, synth.BF16: 0.0, synth.F16: 2.0 ** -24, synth.F8: 2.0 ** -9}
 GUARD_BYTES = 4096
 SENTINEL = 0xA5
 
 
 def torch_dtype(dtype):
-    return {synth.F32: torch.float32, synth.BF16: torch.bfloat16, synth.F16: torch.float16}[dtype]
+    return {synth.F32: torch.float32, synth.BF16: torch.bfloat16, synth.F16: torch.float16,
+            synth.F8: torch.float8_e4m3fn}[dtype]
 
 
 def host_to_device(a: np.ndarray, dtype, dev="cuda"):
-    """numpy storage (float32 or uint16 bf16 bits) -> torch tensor of dtype on the GPU."""
+    """numpy storage (float32, uint16 bf16/fp16 bits or uint8 E4M3 bytes) -> torch
+    tensor of dtype on the GPU."""
     if dtype == synth.F32:
         t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32))
+    elif dtype == synth.F8:
+        t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint8)).view(torch.float8_e4m3fn)
     else:
         t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint16).view(np.int16)).view(torch_dtype(dtype))
     return t.to(dev)
@@ -32,6 +37,8 @@ def device_to_host(t, dtype) -> np.ndarray:
     t = t.detach().cpu().contiguous()
     if dtype == synth.F32:
         return t.numpy().copy()
+    if dtype == synth.F8:
+        return t.view(torch.uint8).numpy().copy()
     return t.view(torch.int16).numpy().view(np.uint16).copy()
 
 
@@ -40,7 +47,7 @@ class Guarded:
 
     def __init__(self, host: np.ndarray, dtype, dev="cuda"):
         self.dtype = dtype
-        es = 4 if dtype == synth.F32 else 2
+        es = synth.esize(dtype)
         rows, cols = host.shape
         g = GUARD_BYTES // es
         n = rows * cols
@@ -93,7 +100,15 @@ def assert_close_to_oracle(got: np.ndarray, y64: np.ndarray, dtype, cols=None, l
     return float((err[nz] / np.abs(y64[nz])).max()) if nz.any() else 0.0
 
 
+def gamma_to_device(g, dtype, dev="cuda"):
+    """gamma in the storage dtype that goes with activations of `dtype`."""
+    return None if g is None else host_to_device(g, synth.gamma_dtype(dtype), dev)
+
+
 def ordinal(bits: np.ndarray, dtype) -> np.ndarray:
+    if dtype == synth.F8:
+        b = bits.astype(np.int64)
+        return np.where(b & 0x80, -(b & 0x7F), b)
     if dtype in (synth.BF16, synth.F16):
         b = bits.astype(np.int64)
         return np.where(b & 0x8000, -(b & 0x7FFF), b)

@@ -36,8 +36,9 @@ from qk_norm_amd import synth
 
 getcontext().prec = 60
 
-F32, BF16, F16 = oracle.F32, oracle.BF16, oracle.F16
-DTYPES = (F32, BF16, F16)
+F32, BF16, F16, F8 = oracle.F32, oracle.BF16, oracle.F16, oracle.F8
+DTYPES = (F32, BF16, F16, F8)
+GD = oracle.gamma_dtype     # gamma's storage dtype (bf16 with FP8 activations)
 
 
 # ------------------------------------------------------------------ helpers --
@@ -80,39 +81,47 @@ def _value16(bits: int, dtype) -> Fraction:
     return Fraction(float(oracle.decode(np.array([bits], dtype=np.uint16), dtype)[0]))
 
 
-_NONFINITE = {BF16: 0x7F80, F16: 0x7C00}
+def _value8(bits: int) -> Fraction:
+    return Fraction(float(oracle.decode(np.array([bits], dtype=np.uint8), F8)[0]))
+
+
+_NONFINITE = {BF16: 0x7F80, F16: 0x7C00, F8: 0x7F}
 
 
 def _nearest16(exact: Decimal, dtype) -> tuple[int, bool]:
-    """bf16 / fp16 pattern nearest to an exact value (ties to even); also whether
-    the value lies so close to a rounding midpoint that an fp64 approximation of
-    it may legitimately round either way.  The first guess comes from a library
-    cast (torch for bf16, numpy for fp16); its neighbours are then compared
-    exactly."""
+    """bf16 / fp16 / E4M3 pattern nearest to an exact value (ties to even); also
+    whether the value lies so close to a rounding midpoint that an fp64
+    approximation of it may legitimately round either way.  The first guess
+    comes from a library cast (torch for bf16 and E4M3, numpy for fp16); its
+    neighbours are then compared exactly."""
     import torch
     approx = float(exact)
     if dtype == BF16:
         b = int(torch.tensor([approx], dtype=torch.float32).to(torch.bfloat16).view(torch.int16)[0]) & 0xFFFF
+    elif dtype == F8:
+        b = int(torch.tensor([approx], dtype=torch.float32).to(torch.float8_e4m3fn).view(torch.uint8)[0])
     else:
         b = int(np.array([approx]).astype(np.float16).view(np.uint16)[0])
     nf = _NONFINITE[dtype]
-    cands = {b, (b + 1) & 0xFFFF, (b - 1) & 0xFFFF}
+    mask = 0xFF if dtype == F8 else 0xFFFF
+    value = _value8 if dtype == F8 else (lambda c: _value16(c, dtype))
+    cands = {b, (b + 1) & mask, (b - 1) & mask}
     ex = Fraction(exact)
     best = None
     for c in cands:
         if (c & nf) == nf:              # inf / nan patterns
             continue
-        d = abs(_value16(c, dtype) - ex)
+        d = abs(value(c) - ex)
         key = (d, c & 1)
         if best is None or key < best[0]:
             best = (key, c)
     c = best[1]
     # distance to the nearest midpoint, in fp64 ulps of the value
     near_mid = False
-    for n in ((c + 1) & 0xFFFF, (c - 1) & 0xFFFF):
+    for n in ((c + 1) & mask, (c - 1) & mask):
         if (n & nf) == nf:
             continue
-        mid = (_value16(c, dtype) + _value16(n, dtype)) / 2
+        mid = (value(c) + value(n)) / 2
         if approx != 0.0 and abs(mid - ex) <= 8 * Fraction(math.ulp(approx)):
             near_mid = True
     return c, near_mid
@@ -124,14 +133,14 @@ def _check_rows_exact(x, y, yr, dtype, groups, eps, label):
     """groups: list of (row, col0, n, gamma_array, shard_count, divisor)."""
     for (t, c0, n, g, R, div) in groups:
         xs = _exact(x[t, c0:c0 + n], dtype)
-        gs = _exact(g[:n], dtype)
+        gs = _exact(g[:n], GD(dtype))
         S = sum((v * v for v in xs), Fraction(0))
         ex = _exact_group(xs, gs, S, div, eps)
         for j in range(n):
             got = float(y[t, c0 + j])
             u = _ulps(got, ex[j])
             assert u <= 4, f"{label}: row {t} col {c0 + j}: {got!r} vs exact {ex[j]} ({u} ulp)"
-            if dtype in (BF16, F16):
+            if dtype in (BF16, F16, F8):
                 want, ambiguous = _nearest16(ex[j], dtype)
                 gotb = int(yr[t, c0 + j])
                 assert gotb == want or ambiguous, \
@@ -200,7 +209,7 @@ def check_apply_exact():
                                  g[r * sw:(r + 1) * sw], None, eps)
             for t in range(T):
                 xe = _exact(xs[t], dtype)
-                ge = _exact(g[r * sw:(r + 1) * sw], dtype)
+                ge = _exact(g[r * sw:(r + 1) * sw], GD(dtype))
                 S = sum((Fraction(p) for p in parts[:, t]), Fraction(0))
                 ex = _exact_group(xe, ge, S, W, eps)
                 for j in range(sw):
@@ -212,15 +221,15 @@ def check_apply_exact():
 def check_unit_rms():
     for dtype in DTYPES:
         x = _rng_problem(7, 5, 3 * 128 + 64, dtype, scale=4.0)
-        ones = synth.to_dtype(np.ones(128), dtype)
+        ones = synth.to_dtype(np.ones(128), GD(dtype))
         y, _ = oracle.per_head(x, dtype, 2, 1, 128, ones, ones, 0.0)
         for t in range(5):
             for h in range(3):
                 m = np.mean(y[t, h * 128:(h + 1) * 128] ** 2)
                 assert abs(m - 1.0) <= 1e-14, f"unit RMS per-head: {m!r}"
         xl = _rng_problem(8, 4, 512 + 256 + 8, dtype)
-        y, _ = oracle.layerwise(xl, dtype, 512, 256, synth.to_dtype(np.ones(512), dtype),
-                                synth.to_dtype(np.ones(256), dtype), 0.0, nshards=8)
+        y, _ = oracle.layerwise(xl, dtype, 512, 256, synth.to_dtype(np.ones(512), GD(dtype)),
+                                synth.to_dtype(np.ones(256), GD(dtype)), 0.0, nshards=8)
         for t in range(4):
             for (c0, n) in ((0, 512), (512, 256)):
                 m = np.mean(y[t, c0:c0 + n] ** 2)
@@ -230,7 +239,7 @@ def check_unit_rms():
 def check_eps_identity():
     for dtype in DTYPES:
         x = _rng_problem(9, 4, 2 * 64, dtype, scale=0.01)
-        ones = synth.to_dtype(np.ones(64), dtype)
+        ones = synth.to_dtype(np.ones(64), GD(dtype))
         eps = synth.eps_f32(1e-4)
         y, _ = oracle.per_head(x, dtype, 1, 1, 64, ones, ones, eps)
         xd = oracle.decode(x, dtype)
@@ -246,16 +255,21 @@ def check_eps_identity():
 def check_scale_pow2():
     for dtype in DTYPES:
         z = synth.normal(10, 0, 3 * 3 * 32).reshape(3, 3 * 32)
+        ks = (-7, -1, 3, 12)
         if dtype == F16:
             # fp16 keeps full precision only above 2^-14: flush the small draws so
             # that every 2^k below is exact (|z| < 8 stays under 65504 at k = 12)
             z = np.where(np.abs(z) < 2.0 ** -6, 0.0, z)
+        if dtype == F8:
+            # E4M3 is exact from 2^-6 to 448: keep |z| in [1/8, 8) and k in -2..3
+            z = np.where(np.abs(z) < 0.125, 0.0, z)
+            ks = (-2, -1, 1, 3)
         x = synth.to_dtype(z, dtype)
         gq, gk = _gamma(10, 32, dtype, 3), _gamma(10, 32, dtype, 4)
         xd = oracle.decode(x, dtype)
         y0, _ = oracle.per_head(x, dtype, 2, 1, 32, gq, gk, 0.0)
         l0, _ = oracle.layerwise(x, dtype, 64, 32, _gamma(10, 64, dtype), gk, 0.0, nshards=4)
-        for k in (-7, -1, 3, 12):
+        for k in ks:
             xs = synth.to_dtype(xd * 2.0 ** k, dtype)
             assert np.array_equal(oracle.decode(xs, dtype), xd * 2.0 ** k)
             y1, _ = oracle.per_head(xs, dtype, 2, 1, 32, gq, gk, 0.0)
@@ -315,20 +329,21 @@ def check_closed_form():
              (8192, 2, 64.0), (8192, 8, 32.0)]
     for dtype in DTYPES:
         for (n, k, root) in cases:
-            for a in (1.0, 0.375, 3.0, 2.0 ** -20):
+            tiny = 2.0 ** -8 if dtype == F8 else 2.0 ** -20   # representable in the dtype
+            for a in (1.0, 0.375, 3.0, tiny):
                 x = np.zeros((1, n))
                 idx = np.arange(0, n, n // k)[:k]
                 x[0, idx] = a * np.where(np.arange(k) % 2 == 0, 1.0, -1.0)
                 xs = synth.to_dtype(x, dtype)
                 g = _gamma(n + k, n, dtype)
-                gd = oracle.decode(g, dtype)
+                gd = oracle.decode(g, GD(dtype))
                 if n <= 128:
                     y, yr = oracle.per_head(xs, dtype, 1, 0, n, g, None, 0.0)
                 else:
                     y, yr = oracle.layerwise(xs, dtype, n, 0, g, None, 0.0, nshards=8)
                 want = np.zeros(n)
                 want[idx] = gd[idx] * np.sign(x[0, idx]) * root
-                if a == 1.0 or a == 2.0 ** -20:
+                if a == 1.0 or a == tiny:
                     assert np.array_equal(y[0], want), f"closed form exact n={n} k={k} a={a}"
                 else:
                     assert np.all(np.abs(y[0] - want) <= 4 * np.spacing(np.abs(want))), \
@@ -338,7 +353,7 @@ def check_closed_form():
     # width-1 group: y = g x / sqrt(x^2 + eps); with eps = 0 just g * sign(x)
     for dtype in DTYPES:
         x = synth.to_dtype(np.array([[3.0, -0.5, 1e-3]]), dtype)
-        g = synth.to_dtype(np.array([1.25]), dtype)
+        g = synth.to_dtype(np.array([1.25]), GD(dtype))
         y, _ = oracle.per_head(x, dtype, 3, 0, 1, g, None, 0.0)
         assert np.array_equal(y[0], 1.25 * np.sign(oracle.decode(x, dtype)[0]))
         eps = 0.5
@@ -383,7 +398,7 @@ def check_libraries():
         eps = synth.eps_f32(1e-6)
         y, _ = oracle.per_head(x, dtype, H, 0, D, g, None, eps)
         xd = oracle.decode(x, dtype).reshape(T, H, D)
-        gd = oracle.decode(g, dtype)
+        gd = oracle.decode(g, GD(dtype))
         ref = xd / np.sqrt(np.mean(xd ** 2, axis=-1, keepdims=True) + eps) * gd
         assert np.all(np.abs(y.reshape(T, H, D) - ref) <= 1e-14 * np.abs(ref) + 1e-300), "numpy"
         tref = torch.nn.functional.rms_norm(torch.from_numpy(xd), (D,), torch.from_numpy(gd),
@@ -397,7 +412,7 @@ def check_libraries():
         xd = oracle.decode(x, dtype)
         for (c0, w, gg) in ((0, wq, gq), (wq, wk, gk)):
             tref = torch.nn.functional.rms_norm(torch.from_numpy(xd[:, c0:c0 + w].copy()), (w,),
-                                                torch.from_numpy(oracle.decode(gg, dtype)),
+                                                torch.from_numpy(oracle.decode(gg, GD(dtype))),
                                                 eps=eps).numpy()
             assert np.all(np.abs(y[:, c0:c0 + w] - tref) <= 1e-14 * np.abs(tref) + 1e-300)
 
@@ -474,6 +489,39 @@ def check_rounding_f16():
     assert np.array_equal(oracle.round_to(v32, F16), tor), "fp32-exact values vs torch"
 
 
+def check_rounding_e4m3():
+    import torch
+    allb = np.arange(256, dtype=np.uint8)
+    vals = oracle.decode(allb, F8)
+    # the decode is OCP E4M3: against torch's float8_e4m3fn
+    tor = torch.from_numpy(allb.copy()).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert np.array_equal(np.isnan(vals), np.isnan(tor))
+    fin = np.isfinite(vals)
+    assert np.array_equal(vals[fin], tor[fin]), "E4M3 decode vs torch"
+    assert np.nanmax(vals) == 448.0 and vals[1] == 2.0 ** -9 and vals[8] == 2.0 ** -6
+    # every finite byte is a fixed point (signed zeros included)
+    assert np.array_equal(oracle.round_to(vals[fin], F8), allb[fin]), "E4M3 fixed points"
+    # midpoints of neighbouring positives (subnormal and normal): ties to even
+    pos = allb[allb < 0x7E]
+    lo = oracle.decode(pos, F8)
+    hi = oracle.decode((pos + 1).astype(np.uint8), F8)
+    mid = (lo + hi) / 2
+    want_even = np.where(pos % 2 == 0, pos, pos + 1).astype(np.uint8)
+    assert np.array_equal(oracle.round_to(mid, F8), want_even), "E4M3 ties to even"
+    assert np.array_equal(oracle.round_to(np.nextafter(mid, np.inf), F8), (pos + 1).astype(np.uint8))
+    assert np.array_equal(oracle.round_to(np.nextafter(mid, -np.inf), F8), pos)
+    assert np.array_equal(oracle.round_to(-mid, F8), (want_even | 0x80).astype(np.uint8))
+    # saturation: everything beyond 448 (including infinity) becomes +-448
+    big = np.array([448.0, 460.0, 464.0, 470.0, 1e6, np.inf, -500.0, -np.inf])
+    assert [int(v) for v in oracle.round_to(big, F8)] == [0x7E] * 6 + [0xFE] * 2
+    # random values in range: torch's fp32 -> E4M3 cast on fp32-exact values
+    v = synth.normal(81, 0, 200000) * np.exp(synth.normal(82, 0, 200000) * 3)
+    v32 = v.astype(np.float32).astype(np.float64)
+    m = np.abs(v32) <= 448.0
+    tor = torch.from_numpy(v32[m]).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(oracle.round_to(v32[m], F8), tor), "in-range values vs torch"
+
+
 def check_pass_through():
     for dtype in DTYPES:
         hq, hkv, D, pad = 4, 2, 64, 24
@@ -492,4 +540,5 @@ def check_pass_through():
 
 ALL_CHECKS = [check_brute_force, check_apply_exact, check_unit_rms, check_eps_identity,
               check_scale_pow2, check_shard_identity, check_closed_form, check_identities,
-              check_libraries, check_rounding, check_rounding_f16, check_pass_through]
+              check_libraries, check_rounding, check_rounding_f16, check_rounding_e4m3,
+              check_pass_through]

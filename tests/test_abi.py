@@ -14,7 +14,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "qknorm.h")
 
 A16 = 0x10000          # a fake, 16-byte aligned "device" address (never dereferenced)
-BF16, F32, F16 = q.QKNORM_BF16, q.QKNORM_F32, q.QKNORM_F16
+BF16, F32, F16, F8 = q.QKNORM_BF16, q.QKNORM_F32, q.QKNORM_F16, q.QKNORM_FP8_E4M3
 
 
 def _declared():
@@ -85,10 +85,11 @@ def ap(lib, qkv=A16, T=4, ld=6144, wq=4096, wk=1024, pq=A16, pk=A16, n=8, nwq=40
 
 @pytest.mark.parametrize("call", [ph, lw, ps, ap], ids=["per_head", "layerwise", "partial", "apply"])
 def test_bad_dtype(lib, call):
-    assert call(lib, dt=3) == q.QKNORM_E_DTYPE
+    assert call(lib, dt=4) == q.QKNORM_E_DTYPE
     assert call(lib, dt=-1) == q.QKNORM_E_DTYPE
-    # fp16 is a valid code (T = 0: validated, nothing launched)
+    # fp16 and E4M3 are valid codes (T = 0: validated, nothing launched)
     assert call(lib, dt=F16, T=0) == q.QKNORM_OK
+    assert call(lib, dt=F8, T=0) == q.QKNORM_OK
 
 
 @pytest.mark.parametrize("call", [ph, lw, ap], ids=["per_head", "layerwise", "apply"])
@@ -152,11 +153,17 @@ def test_alignment(lib):
     assert ps(lib, pq=A16 + 1) == q.QKNORM_E_ALIGN
     assert ap(lib, pk=A16 + 2) == q.QKNORM_E_ALIGN
     assert ap(lib, wq=4092, nwq=4096) == q.QKNORM_E_ALIGN  # Q/K boundary off a 16 B vector
+    # E4M3: one byte per element, so 16-byte rules count 16 elements
+    assert lw(lib, ld=6152, dt=F8) == q.QKNORM_E_ALIGN     # pitch 6152 B
+    assert lw(lib, wq=4096 + 8, ld=6160, R=1, dt=F8) == q.QKNORM_E_ALIGN
+    assert lw(lib, wq=4096, wk=1024, R=128, dt=F8) == q.QKNORM_E_ALIGN   # 8-byte K shards
+    assert lw(lib, T=0, ld=6160, dt=F8) == q.QKNORM_OK
 
 
 @pytest.mark.parametrize("dt,D", [(F32, 16), (F32, 32), (F32, 64), (F32, 128), (F32, 256),
                                   (BF16, 32), (BF16, 64), (BF16, 128), (BF16, 256), (BF16, 512),
-                                  (F16, 32), (F16, 128), (F16, 512)])
+                                  (F16, 32), (F16, 128), (F16, 512),
+                                  (F8, 64), (F8, 128), (F8, 256), (F8, 512), (F8, 1024)])
 def test_head_widths_accepted(lib, dt, D):
     # a head is 64 to 1024 bytes, a power of two (T = 0: validated, nothing launched)
     assert ph(lib, T=0, D=D, ld=20 * D, dt=dt) == q.QKNORM_OK
@@ -170,6 +177,8 @@ def test_unsupported(lib):
     assert ph(lib, D=16, ld=20 * 16, dt=BF16) == q.QKNORM_E_UNSUPPORTED
     assert ph(lib, D=1024, ld=20 * 1024, dt=F16) == q.QKNORM_E_UNSUPPORTED
     assert ph(lib, D=48, ld=20 * 48, dt=F16) == q.QKNORM_E_UNSUPPORTED
+    assert ph(lib, D=32, ld=20 * 32, dt=F8) == q.QKNORM_E_UNSUPPORTED        # 32 B heads
+    assert ph(lib, D=2048, ld=20 * 2048, dt=F8) == q.QKNORM_E_UNSUPPORTED
     assert lw(lib, R=2048, wq=4096 * 8, wk=2048 * 8, ld=6144 * 8) == q.QKNORM_E_UNSUPPORTED
     assert ap(lib, n=4096) == q.QKNORM_E_UNSUPPORTED
     # rows are addressed with 32-bit offsets: pitch above 64 MiB is refused

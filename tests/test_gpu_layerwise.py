@@ -7,8 +7,8 @@ import torch
 import oracle
 import qk_norm_amd as q
 from qk_norm_amd import synth
-from gpu_util import (Guarded, assert_bytes_equal, assert_close_to_oracle, guarded_f32,
-                      host_to_device, raw_guards_intact, ulp_histogram)
+from gpu_util import (Guarded, gamma_to_device, assert_bytes_equal, assert_close_to_oracle, guarded_f32,
+                      device_to_host, host_to_device, raw_guards_intact, ulp_histogram)
 
 pytestmark = pytest.mark.gpu
 
@@ -16,8 +16,8 @@ PART_RTOL = 1e-5
 
 
 def _gammas(p):
-    gq = host_to_device(p.gamma_q, p.dtype) if p.gamma_q is not None else None
-    gk = host_to_device(p.gamma_k, p.dtype) if p.gamma_k is not None else None
+    gq = gamma_to_device(p.gamma_q, p.dtype)
+    gk = gamma_to_device(p.gamma_k, p.dtype)
     return gq, gk
 
 
@@ -58,9 +58,9 @@ def check_against_oracle(p, got, label):
     qk = p.wq + p.wk
     assert_close_to_oracle(got[:, :qk], y64[:, :qk], p.dtype, label=label)
     assert_bytes_equal(got[:, qk:], p.x[:, qk:], f"{label}: V/padding columns")
-    if p.dtype in (synth.BF16, synth.F16):
-        # never more than one 16-bit ulp from the oracle's own rounding (fp32
-        # I/O is held to its 1e-5 relative bound)
+    if p.dtype in (synth.BF16, synth.F16, synth.F8):
+        # never more than one ulp from the oracle's own rounding (fp32 I/O is
+        # held to its 1e-5 relative bound)
         hist = ulp_histogram(got[:, :qk], yr[:, :qk], p.dtype)
         assert max(hist) <= 1, f"{label}: ulp histogram {hist}"
 
@@ -88,7 +88,7 @@ def test_cfg4_layerwise(T):
     full_check(synth.cfg4(T=T))
 
 
-@pytest.mark.parametrize("dtype", [synth.F32, synth.BF16, synth.F16])
+@pytest.mark.parametrize("dtype", [synth.F32, synth.BF16, synth.F16, synth.F8])
 @pytest.mark.parametrize("wq,wk,R,T", [
     (4096, 1024, 1, 33),       # one shard: register path, 8 slots per lane
     (4096, 1024, 2, 17),
@@ -102,11 +102,9 @@ def test_cfg4_layerwise(T):
     (1536, 384, 3, 21),        # shard count not a power of two
 ])
 def test_layerwise_shapes(dtype, wq, wk, R, T):
-    es = 4 if dtype == synth.F32 else 2
+    es = synth.esize(dtype)
     if ((wq // R) * es) % 16 or ((wk // R) * es) % 16:
         pytest.skip("shard not a multiple of 16 bytes in this dtype")
-    if dtype == synth.F32 and R == 1024:
-        pytest.skip("shard below 16 bytes in fp32")
     ld = wq + 2 * wk + 64
     p = synth.layerwise_problem(f"lw_{wq}_{wk}_R{R}", 41 + R, dtype, T, wq, wk, ld, R,
                                 token_scale=(0.1, 10.0), outlier_frac=0.01)
@@ -159,12 +157,13 @@ def test_tensor_parallel_emulation_matches_fused():
     assert np.array_equal(got, ref), "rank-sliced two-phase differs from the fused kernel"
 
 
-def test_tensor_parallel_emulation_f16():
-    # the same rank-sliced two-phase form in fp16, against the fused kernel
-    # (bitwise) and the oracle
+@pytest.mark.parametrize("dtype", [synth.F16, synth.F8])
+def test_tensor_parallel_emulation_other_dtypes(dtype):
+    # the same rank-sliced two-phase form in fp16 and E4M3, against the fused
+    # kernel (bitwise) and the oracle
     N, T, wq, wk = 8, 48, 4096, 1024
-    p = synth.layerwise_problem("tp_f16", 52, synth.F16, T, wq, wk, wq + 2 * wk, N,
-                                token_scale=(0.5, 2.0), outlier_frac=0.01)
+    p = synth.layerwise_problem(f"tp_{synth.DTYPE_NAMES[dtype]}", 52, dtype, T, wq, wk,
+                                wq + 2 * wk, N, token_scale=(0.5, 2.0), outlier_frac=0.01)
     sq, sk = wq // N, wk // N
     x = host_to_device(p.x, p.dtype)
     gq, gk = _gammas(p)
@@ -179,9 +178,9 @@ def test_tensor_parallel_emulation_f16():
         q.qknorm_apply_scalar(x[:, wq + r * sk:wq + (r + 1) * sk], sk, 0, part_k, None, wk, 0,
                               gk[r * sk:(r + 1) * sk], None, p.eps)
     torch.cuda.synchronize()
-    got = x.cpu().view(torch.int16).numpy().view(np.uint16)
+    got = device_to_host(x, dtype)
     ref = full_check(p)
-    assert np.array_equal(got, ref), "rank-sliced fp16 two-phase differs from the fused kernel"
+    assert np.array_equal(got, ref), "rank-sliced two-phase differs from the fused kernel"
 
 
 def test_bitwise_deterministic():
@@ -245,8 +244,8 @@ def test_cfg5_full_size_both_modes(cfg5_input):
     # per-head
     print("[cfg5] per-head full size", flush=True)
     x = x0.clone()
-    q.qknorm_per_head(x, ph.hq, ph.hkv, ph.head_dim, host_to_device(ph.gamma_q, p.dtype),
-                      host_to_device(ph.gamma_k, p.dtype), p.eps)
+    q.qknorm_per_head(x, ph.hq, ph.hkv, ph.head_dim, gamma_to_device(ph.gamma_q, p.dtype),
+                      gamma_to_device(ph.gamma_k, p.dtype), p.eps)
     torch.cuda.synchronize()
     assert torch.equal(x[:, qk:].view(torch.int16), x0[:, qk:].view(torch.int16)), "V changed"
     got = x[torch.from_numpy(rows).cuda()].cpu().view(torch.int16).numpy().view(np.uint16)

@@ -6,7 +6,7 @@ import torch
 import oracle
 import qk_norm_amd as q
 from qk_norm_amd import synth
-from gpu_util import (Guarded, assert_bytes_equal, assert_close_to_oracle, host_to_device,
+from gpu_util import (Guarded, gamma_to_device, assert_bytes_equal, assert_close_to_oracle, host_to_device,
                       ulp_histogram)
 
 pytestmark = pytest.mark.gpu
@@ -16,8 +16,8 @@ def run_per_head(p: synth.Problem, check_ulp=True):
     """Run the GPU per-head path on problem p and check it against the oracle."""
     print(f"[per_head] {p.name} T={p.T} ld={p.ld} hq={p.hq} hkv={p.hkv} D={p.head_dim}", flush=True)
     buf = Guarded(p.x, p.dtype)
-    gq = host_to_device(p.gamma_q, p.dtype)
-    gk = host_to_device(p.gamma_k, p.dtype) if p.gamma_k is not None else None
+    gq = gamma_to_device(p.gamma_q, p.dtype)
+    gk = gamma_to_device(p.gamma_k, p.dtype)
     q.qknorm_per_head(buf.t, p.hq, p.hkv, p.head_dim, gq, gk, p.eps)
     torch.cuda.synchronize()
     got = buf.host()
@@ -26,7 +26,7 @@ def run_per_head(p: synth.Problem, check_ulp=True):
     qk = p.wq + p.wk
     relmax = assert_close_to_oracle(got[:, :qk], y64[:, :qk], p.dtype, label=p.name)
     assert_bytes_equal(got[:, qk:], p.x[:, qk:], f"{p.name}: V/padding columns")
-    if check_ulp and p.dtype in (synth.BF16, synth.F16):
+    if check_ulp and p.dtype in (synth.BF16, synth.F16, synth.F8):
         # fp32 arithmetic is far finer than a 16-bit ulp: at most one ulp from
         # the oracle's own rounding, and nearly always none
         hist = ulp_histogram(got[:, :qk], yr[:, :qk], p.dtype)
@@ -51,14 +51,14 @@ def test_cfg3_fused_gqa_bf16(T):
     run_per_head(synth.cfg3(T=T))
 
 
-ALL_DTYPES = [synth.F32, synth.BF16, synth.F16]
+ALL_DTYPES = [synth.F32, synth.BF16, synth.F16, synth.F8]
 
 
 @pytest.mark.parametrize("dtype", ALL_DTYPES)
-@pytest.mark.parametrize("D", [16, 32, 64, 128, 256, 512])
+@pytest.mark.parametrize("D", [16, 32, 64, 128, 256, 512, 1024])
 def test_head_dims(dtype, D):
     # every head of 64 to 1024 bytes; ragged: 37 rows x (5 Q + 3 K) heads, padding after V
-    hb = D * (4 if dtype == synth.F32 else 2)
+    hb = D * synth.esize(dtype)
     if hb < 64 or hb > 1024:
         pytest.skip(f"{hb}-byte heads are outside the supported 64..1024 bytes")
     p = synth.per_head_problem(f"dims_D{D}", 21, dtype, 37, 5, 3, D, ld=(5 + 6) * D + 64,
@@ -70,7 +70,7 @@ def test_head_dims(dtype, D):
 @pytest.mark.parametrize("T,hq,hkv", [(1, 1, 0), (3, 1, 1), (7, 0, 3), (129, 3, 1), (1000, 7, 2)])
 def test_ragged_head_counts(dtype, T, hq, hkv):
     p = synth.per_head_problem(f"ragged_T{T}_{hq}_{hkv}", 22, dtype, T, hq, hkv, 128,
-                               ld=(hq + 2 * hkv) * 128 + (4 if dtype == synth.F32 else 8))
+                               ld=(hq + 2 * hkv) * 128 + 16 // synth.esize(dtype))
     run_per_head(p)
 
 
@@ -98,7 +98,7 @@ def test_zero_rows_and_eps_zero_closed_forms():
         g = synth.make_gamma(3, 3, D, dtype)
         for eps in (0.0, synth.eps_f32(1e-6)):
             buf = Guarded(xs, dtype)
-            q.qknorm_per_head(buf.t, H, 0, D, host_to_device(g, dtype), None, eps)
+            q.qknorm_per_head(buf.t, H, 0, D, gamma_to_device(g, dtype), None, eps)
             torch.cuda.synchronize()
             got = buf.host()
             gd = oracle.decode(got, dtype)
@@ -111,10 +111,17 @@ def test_zero_rows_and_eps_zero_closed_forms():
             if eps == 0.0:
                 want = np.zeros((T, H * D))
                 for h, (idx, root) in roots.items():
-                    want[:, h * D + idx] = oracle.decode(g, dtype)[idx] * np.sign(x[:, h * D + idx]) * root
-                if dtype != synth.F32:
+                    want[:, h * D + idx] = (oracle.decode(g, synth.gamma_dtype(dtype))[idx] *
+                                            np.sign(x[:, h * D + idx]) * root)
+                # exact in bf16 and fp16 (gamma times a power of two); with E4M3
+                # output a bf16 gamma times 2^k can sit on a rounding midpoint,
+                # where an fp32 ulp decides, so E4M3 keeps the tolerance checks
+                if dtype in (synth.BF16, synth.F16):
                     assert np.array_equal(got[:, D:], synth.to_dtype(want, dtype)[:, D:]), \
                         "closed form, bit exact"
+                elif dtype == synth.F8:
+                    hist = ulp_histogram(got[:, D:], synth.to_dtype(want, dtype)[:, D:], dtype)
+                    assert max(hist) <= 1, f"closed form within one E4M3 ulp: {hist}"
                 else:
                     assert np.all(np.abs(gd[:, D:] - want[:, D:]) <= 1e-5 * np.abs(want[:, D:]))
             y64, _ = oracle.per_head(xs, dtype, H, 0, D, g, None, eps)
@@ -153,12 +160,54 @@ def test_extreme_magnitudes_f16():
     assert np.array_equal(gd[1, :D], -g)
 
 
+@pytest.mark.parametrize("dtype", [synth.F16, synth.F8])
 @pytest.mark.parametrize("T", [1, 333, 2048])
-def test_fused_gqa_f16(T):
-    # the fused GQA row of a Qwen3-8B-style layer (32 Q, 8 K, 8 V heads of 128) in fp16
-    p = synth.per_head_problem(f"gqa_f16_T{T}", 24, synth.F16, T, 32, 8, 128,
+def test_fused_gqa_16bit_and_fp8(dtype, T):
+    # the fused GQA row of a Qwen3-8B-style layer (32 Q, 8 K, 8 V heads of 128)
+    p = synth.per_head_problem(f"gqa_{synth.DTYPE_NAMES[dtype]}_T{T}", 24, dtype, T, 32, 8, 128,
                                token_scale=(0.25, 4.0), outlier_frac=0.01)
     run_per_head(p)
+
+
+def test_extreme_magnitudes_e4m3():
+    # E4M3 spans 2^-9 .. 448: rows of subnormals, rows near the top, a head of
+    # the smallest value and a head of the largest
+    T, H, D = 16, 4, 128
+    dtype = synth.F8
+    z = synth.normal(33, 0, T * H * D).reshape(T, H * D)
+    z *= (2.0 ** np.linspace(-9, 6, T))[:, None]
+    z[0, :D] = 2.0 ** -9
+    z[1, :D] = -448.0
+    z[1, D:2 * D] = np.where(np.arange(D) % 2 == 0, 448.0, 2.0 ** -9)
+    p = synth.Problem("extreme_e4m3", dtype, T, H * D, H * D, 0, synth.to_dtype(z, dtype),
+                      synth.make_gamma(33, 3, D, dtype), None, synth.eps_f32(0.0), hq=H,
+                      hkv=0, head_dim=D)
+    got, _ = run_per_head(p, check_ulp=False)
+    _, yr = oracle.per_head(p.x, dtype, H, 0, D, p.gamma_q, None, p.eps)
+    # a head of equal values normalises to gamma, rounded to E4M3: within one
+    # ulp of the oracle's rounding (a bf16 gamma can sit on an E4M3 midpoint)
+    hist = ulp_histogram(got, yr, dtype)
+    assert max(hist) <= 1, hist
+
+
+def test_e4m3_saturates_at_448():
+    # gamma = 96 and one nonzero per head: y = 96 * sqrt(128) ~ 1086 > 448, so
+    # +-448 (never NaN); the rest of the head is exactly zero
+    T, H, D = 8, 6, 128
+    dtype = synth.F8
+    x = np.zeros((T, H * D))
+    x[:, ::D] = np.where(np.arange(T)[:, None] % 2 == 0, 1.5, -0.25) * np.ones((T, H))
+    g = synth.to_dtype(np.full(D, 96.0), synth.BF16)
+    p = synth.Problem("saturate_e4m3", dtype, T, H * D, H * D, 0, synth.to_dtype(x, dtype), g, None,
+                      synth.eps_f32(0.0), hq=H, hkv=0, head_dim=D)
+    buf = Guarded(p.x, dtype)
+    q.qknorm_per_head(buf.t, H, 0, D, gamma_to_device(g, dtype), None, p.eps)
+    torch.cuda.synchronize()
+    got = buf.host()
+    assert buf.guards_intact()
+    _, yr = oracle.per_head(p.x, dtype, H, 0, D, g, None, p.eps)
+    assert np.array_equal(got, yr), "saturated E4M3 bytes"
+    assert set(np.unique(got[:, ::D]).tolist()) == {0x7E, 0xFE}
 
 
 def test_bitwise_deterministic():
@@ -171,7 +220,7 @@ def test_bitwise_deterministic():
 def test_standalone_3d_tensor_and_side_stream():
     p = synth.cfg2(T=256, H=32)
     x = host_to_device(p.x, p.dtype).view(256, 32, 128)
-    g = host_to_device(p.gamma_q, p.dtype)
+    g = gamma_to_device(p.gamma_q, p.dtype)
     s = torch.cuda.Stream()
     with torch.cuda.stream(s):
         q.qknorm_per_head(x, 32, 0, 128, g, None, p.eps)
@@ -186,8 +235,8 @@ def test_rows_with_pitch_view():
     p = synth.cfg3(T=64)
     full = host_to_device(p.x, p.dtype)
     view = full[:, : p.wq + p.wk]
-    q.qknorm_per_head(view, p.hq, p.hkv, p.head_dim, host_to_device(p.gamma_q, p.dtype),
-                      host_to_device(p.gamma_k, p.dtype), p.eps)
+    q.qknorm_per_head(view, p.hq, p.hkv, p.head_dim, gamma_to_device(p.gamma_q, p.dtype),
+                      gamma_to_device(p.gamma_k, p.dtype), p.eps)
     torch.cuda.synchronize()
     got = full.cpu().view(torch.int16).numpy().view(np.uint16)
     y64, _ = oracle.per_head(p.x, p.dtype, p.hq, p.hkv, p.head_dim, p.gamma_q, p.gamma_k, p.eps)
@@ -199,7 +248,7 @@ def test_graph_replay_matches_eager():
     p = synth.cfg3(T=64)
     src = host_to_device(p.x, p.dtype)
     work = src.clone()
-    gq, gk = host_to_device(p.gamma_q, p.dtype), host_to_device(p.gamma_k, p.dtype)
+    gq, gk = gamma_to_device(p.gamma_q, p.dtype), gamma_to_device(p.gamma_k, p.dtype)
     q.qknorm_per_head(work, p.hq, p.hkv, p.head_dim, gq, gk, p.eps)
     torch.cuda.synchronize()
     eager = work.clone()

@@ -20,7 +20,7 @@ MUTANTS = {
                          "double inv = 1.0 / (sqrt(S / n) + eps);"),
     "divide_by_shard_width": ("apply_group(x, dtype, row, wq, S, (double)wq,",
                               "apply_group(x, dtype, row, wq, S, (double)(wq / nshards),"),
-    "gamma_not_indexed": ("load_value(g, dtype, goff + j)", "load_value(g, dtype, goff)"),
+    "gamma_not_indexed": ("load_value(g, gamma_dtype(dtype), goff + j)", "load_value(g, gamma_dtype(dtype), goff)"),
     "k_heads_use_gamma_q": ("apply_group(x, dtype, off, D, S, (double)D, gamma_k, 0, eps, y, yr);",
                             "apply_group(x, dtype, off, D, S, (double)D, gamma_q, 0, eps, y, yr);"),
     "k_heads_wrong_offset": ("int64_t off = row + wq + (int64_t)h * D;",
@@ -44,8 +44,16 @@ MUTANTS = {
                                "if (r > 65504.0)\n        return sign | 0x7BFF;"),
     "f16_stored_as_bf16": ("else if (dtype == 2)\n        ((uint16_t *)p)[i] = round_to_f16(v);",
                            "else if (dtype == 2)\n        ((uint16_t *)p)[i] = round_to_bf16(v);"),
-    "gamma_after_divide_by_rms_squared": ("double v = load_value(x, dtype, off + j) * load_value(g, dtype, goff + j) * inv;",
-                                          "double v = load_value(x, dtype, off + j) * load_value(g, dtype, goff + j) * inv * inv;"),
+    "e4m3_exponent_bias_off_by_one": ("v = ldexp((double)(8 + m), e - 10);",
+                                      "v = ldexp((double)(8 + m), e - 9);"),
+    "e4m3_rounding_truncates": ("double q = nearbyint(ldexp(a, 4 - e));",
+                                "double q = trunc(ldexp(a, 4 - e));"),
+    "e4m3_overflow_to_nan": ("if (a > 448.0)\n        return sign | 0x7E;",
+                             "if (a > 448.0)\n        return sign | 0x7F;"),
+    "e4m3_gamma_read_as_fp8": ("static int gamma_dtype(int dtype) { return dtype == 3 ? 1 : dtype; }",
+                               "static int gamma_dtype(int dtype) { return dtype; }"),
+    "gamma_after_divide_by_rms_squared": ("double v = load_value(x, dtype, off + j) * load_value(g, gamma_dtype(dtype), goff + j) * inv;",
+                                          "double v = load_value(x, dtype, off + j) * load_value(g, gamma_dtype(dtype), goff + j) * inv * inv;"),
 }
 
 
