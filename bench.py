@@ -70,11 +70,21 @@ def read_traffic(bytes_alg: float):
 # ----------------------------------------------------------------- devices --
 
 def to_device(a, dtype, torch, dev):
+    """numpy storage (float32, 16-bit patterns, E4M3 bytes) -> tensor of dtype on dev."""
     import numpy as np
     from qk_norm_amd import synth
     if dtype == synth.F32:
         return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
-    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+    if dtype == synth.F8:
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint8)).view(torch.float8_e4m3fn).to(dev)
+    tdt = torch.float16 if dtype == synth.F16 else torch.bfloat16
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(tdt).to(dev)
+
+
+def sizes(p):
+    """(activation, gamma) bytes per element of problem p."""
+    from qk_norm_amd import synth
+    return synth.esize(p.dtype), synth.esize(synth.gamma_dtype(p.dtype))
 
 
 class Timer:
@@ -127,13 +137,16 @@ def pool_count(buf_bytes: int, min_copies=2) -> int:
 # ------------------------------------------------------------------- cases --
 
 def bench_per_head(q, torch, dev, p, steps, warmup, label):
+    from qk_norm_amd import synth
     lib = q.load()
-    n = pool_count(p.T * p.ld * 2)
+    es, ges = sizes(p)
+    n = pool_count(p.T * p.ld * es)
     base = to_device(p.x, p.dtype, torch, dev)
     pool = [base.clone() for _ in range(n)]
     del base
-    gq = to_device(p.gamma_q, p.dtype, torch, dev)
-    gk = to_device(p.gamma_k, p.dtype, torch, dev) if p.gamma_k is not None else None
+    gd = synth.gamma_dtype(p.dtype)
+    gq = to_device(p.gamma_q, gd, torch, dev)
+    gk = to_device(p.gamma_k, gd, torch, dev) if p.gamma_k is not None else None
     stream = torch.cuda.current_stream(dev).cuda_stream
     args = [(t.data_ptr(), p.T, p.ld, p.hq, p.hkv, p.head_dim, gq.data_ptr(),
              gk.data_ptr() if gk is not None else None, p.eps, p.dtype, stream) for t in pool]
@@ -148,7 +161,7 @@ def bench_per_head(q, torch, dev, p, steps, warmup, label):
     timer = Timer(torch)
     wall, mean_us = timer.run(steps, launch, first=warmup)
     spread = timer.spread(min(steps, 200), launch, first=warmup + steps)
-    bytes_alg = 2 * p.T * (p.wq + p.wk) * 2 + (p.head_dim * 2) * (1 + (p.hkv > 0))
+    bytes_alg = 2 * p.T * (p.wq + p.wk) * es + (p.head_dim * ges) * (1 + (p.hkv > 0))
     del pool
     torch.cuda.empty_cache()
     log(f"{label}: {mean_us:.2f} us/launch, {bytes_alg / mean_us / 1e3:.0f} GB/s")
@@ -156,14 +169,16 @@ def bench_per_head(q, torch, dev, p, steps, warmup, label):
             "mean_us": mean_us, **spread, "gbs": bytes_alg / (mean_us * 1e-6) / 1e9}
 
 
-def bench_layerwise(q, torch, dev, p, steps, warmup):
+def bench_layerwise(q, torch, dev, p, steps, warmup, label="cfg5"):
+    from qk_norm_amd import synth
     lib = q.load()
-    n = pool_count(p.T * p.ld * 2)
+    es, ges = sizes(p)
+    n = pool_count(p.T * p.ld * es)
     base = to_device(p.x, p.dtype, torch, dev)
     pool = [base.clone() for _ in range(n)]
     del base
-    gq = to_device(p.gamma_q, p.dtype, torch, dev)
-    gk = to_device(p.gamma_k, p.dtype, torch, dev)
+    gq = to_device(p.gamma_q, synth.gamma_dtype(p.dtype), torch, dev)
+    gk = to_device(p.gamma_k, synth.gamma_dtype(p.dtype), torch, dev)
     pq = torch.empty(p.nshards, p.T, dtype=torch.float32, device=dev)
     pk = torch.empty(p.nshards, p.T, dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev).cuda_stream
@@ -191,8 +206,8 @@ def bench_layerwise(q, torch, dev, p, steps, warmup):
         if rc:
             raise RuntimeError(q.strerror(rc))
 
-    qk_bytes = p.T * (p.wq + p.wk) * 2
-    g_bytes = (p.wq + p.wk) * 2
+    qk_bytes = p.T * (p.wq + p.wk) * es
+    g_bytes = (p.wq + p.wk) * ges
     out = {}
     for name, fn, nbytes in (("layerwise_fused", fused, 2 * qk_bytes + g_bytes),
                              ("partial_sumsq", partial, qk_bytes + 2 * R * p.T * 4),
@@ -201,7 +216,7 @@ def bench_layerwise(q, torch, dev, p, steps, warmup):
             fn(i)
         wall, mean_us = Timer(torch).run(steps, fn, first=warmup)
         out[name] = {"bytes": nbytes, "mean_us": mean_us, "gbs": nbytes / (mean_us * 1e-6) / 1e9}
-        log(f"cfg5 {name}: {mean_us:.2f} us/launch, {out[name]['gbs']:.0f} GB/s")
+        log(f"{label} {name}: {mean_us:.2f} us/launch, {out[name]['gbs']:.0f} GB/s")
     two = out["partial_sumsq"]["mean_us"] + out["apply_scalar"]["mean_us"]
     out["two_phase_total"] = {"mean_us": two, "bytes": 3 * qk_bytes + g_bytes + 4 * R * p.T * 4,
                               "gbs_vs_fused_alg_bytes": (2 * qk_bytes + g_bytes) / (two * 1e-6) / 1e9}
@@ -274,7 +289,8 @@ def main():
     ap.add_argument("--quick", action="store_true", help="headline case only")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--case", default="headline",
-                    choices=["headline", "cfg5_layerwise", "cfg5_per_head", "copy"],
+                    choices=["headline", "cfg5_layerwise", "cfg5_per_head", "fp8_per_head",
+                             "fp8_cfg5_layerwise", "copy"],
                     help="single case for profiling runs")
     args = ap.parse_args()
 
@@ -305,6 +321,16 @@ def main():
     if args.case == "cfg5_layerwise":
         p = synth.cfg5(T=32768)
         print(json.dumps({"case": "cfg5_layerwise", **bench_layerwise(q, torch, dev, p, args.steps, args.warmup)}))
+        return
+    if args.case == "fp8_per_head":
+        p = synth.cfg2(T=4096, H=48, dtype=synth.F8)
+        print(json.dumps({"case": "fp8_per_head",
+                          **bench_per_head(q, torch, dev, p, args.steps, args.warmup, "fp8 per-head")}))
+        return
+    if args.case == "fp8_cfg5_layerwise":
+        p = synth.cfg5(T=32768, dtype=synth.F8)
+        print(json.dumps({"case": "fp8_cfg5_layerwise",
+                          **bench_layerwise(q, torch, dev, p, args.steps, args.warmup, "fp8 cfg5")}))
         return
     if args.case == "cfg5_per_head":
         p = synth.cfg5(T=32768, mode="per_head")
@@ -348,6 +374,15 @@ def main():
         del p5h
         c = bench_per_head(q, torch, dev, synth.cfg3(T=8192), 100, 10, "cfg3 fused GQA T=8192")
         cases["cfg3_T8192_per_head"] = {k: c[k] for k in ("bytes", "mean_us", "gbs")}
+        for dt in (synth.F16, synth.F8):
+            name = synth.DTYPE_NAMES[dt]
+            c = bench_per_head(q, torch, dev, synth.cfg2(T=4096, H=48, dtype=dt), 400, 40,
+                               f"{name} per-head [4096, 48, 128]")
+            cases[f"{name}_T4096_H48_per_head"] = {k: c[k] for k in ("bytes", "mean_us", "gbs")}
+        p8 = synth.cfg5(T=32768, dtype=synth.F8)
+        cases["fp8e4m3_cfg5_T32768_layerwise"] = bench_layerwise(q, torch, dev, p8, 50, 5,
+                                                                 "fp8e4m3 [32768, 10240]")
+        del p8
         cases["decode_floor"] = [bench_decode_floor(q, torch, dev, T, 48) for T in (1, 16, 128)]
         result["cases"] = cases
     if not args.no_cpu:

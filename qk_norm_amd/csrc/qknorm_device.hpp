@@ -162,17 +162,34 @@ __device__ __forceinline__ float saturate_e4m3(float x) {
 }
 
 // Round fp32 to the I/O dtype (bf16: v_cvt_pk_bf16_f32; fp16: v_cvt_f16_f32;
-// FP8: v_cvt_pk_fp8_f32 after saturation; all nearest-even) and pack.
+// FP8: v_cvt_pk_fp8_f32, saturated; all nearest-even) and pack.
+//
+// FP8 `may_exceed`: false only when the caller has shown that no value can
+// round past 448 (see e4m3_may_exceed); then the conversion alone already
+// gives the saturated result.  Otherwise the vector's largest magnitude is
+// tested first and only a vector above 448 takes the saturating selects (a
+// NaN is ignored by max, reaches the conversion unchanged and stays NaN).
 template <int DT>
-__device__ __forceinline__ u32x4 pack(const float (&f)[IoTraits<DT>::kElems]) {
+__device__ __forceinline__ u32x4 pack(const float (&f)[IoTraits<DT>::kElems],
+                                      bool may_exceed = true) {
   u32x4 v;
   if constexpr (DT == kFP8) {
+    float g[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) g[e] = f[e];
+    if (may_exceed) {
+      float m = 0.f;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) m = __builtin_fmaxf(m, __builtin_fabsf(g[e]));
+      if (m > 448.f) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) g[e] = saturate_e4m3(g[e]);
+      }
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      int w = __builtin_amdgcn_cvt_pk_fp8_f32(saturate_e4m3(f[4 * i]), saturate_e4m3(f[4 * i + 1]),
-                                              0, false);
-      w = __builtin_amdgcn_cvt_pk_fp8_f32(saturate_e4m3(f[4 * i + 2]), saturate_e4m3(f[4 * i + 3]),
-                                          w, true);
+      int w = __builtin_amdgcn_cvt_pk_fp8_f32(g[4 * i], g[4 * i + 1], 0, false);
+      w = __builtin_amdgcn_cvt_pk_fp8_f32(g[4 * i + 2], g[4 * i + 3], w, true);
       v[i] = (uint32_t)w;
     }
   } else if constexpr (DT == kBF16) {
@@ -192,6 +209,26 @@ __device__ __forceinline__ u32x4 pack(const float (&f)[IoTraits<DT>::kElems]) {
     for (int i = 0; i < 4; ++i) v[i] = __float_as_uint(f[i]);
   }
   return v;
+}
+
+// Whether any output of this wave could exceed the E4M3 range.  For a group
+// of width n normalised with sums computed from its own values,
+// |x_j| / sqrt(S/n + eps) <= sqrt(n) because S >= x_j^2, so |y_j| <=
+// |gamma_j| sqrt(n); fp32 rounding of the sum, the scale and the two products
+// adds at most about (n + 6) * 2^-24 relative (under 1e-3 for n <= 8192).  If
+// every gamma of the wave satisfies |gamma| sqrt(n) <= 448 the outputs stay
+// below 464, where the conversion rounds to at most 448 by itself.  The test
+// is wave-uniform (a ballot), so the saturating path is a scalar branch.
+__device__ __forceinline__ bool e4m3_may_exceed(float gmax, float inv_n) {
+  const bool mine = gmax * gmax > 200704.f * inv_n;      // 448^2 / n
+  return __builtin_amdgcn_ballot_w64(mine) != 0;
+}
+
+template <int E>
+__device__ __forceinline__ float abs_max(const float (&g)[E], float m) {
+#pragma unroll
+  for (int e = 0; e < E; ++e) m = __builtin_fmaxf(m, __builtin_fabsf(g[e]));
+  return m;
 }
 
 // Widen the gamma of one activation vector to fp32.

@@ -124,7 +124,7 @@ struct PerHeadTrip {
 
 template <int DT, int LPH, int U>
 __device__ __forceinline__ void per_head_apply(const u32x4 (&v)[U], const float (&g)[IoTraits<DT>::kElems],
-                                               float inv_d, float eps, Rsrc rs,
+                                               float inv_d, float eps, bool may_exceed, Rsrc rs,
                                                const uint32_t (&off)[U]) {
   using IO = IoTraits<DT>;
   constexpr int E = IO::kElems;
@@ -137,7 +137,7 @@ __device__ __forceinline__ void per_head_apply(const u32x4 (&v)[U], const float 
     float y[E];
 #pragma unroll
     for (int e = 0; e < E; ++e) y[e] = (x[e] * g[e]) * r;
-    stream_store(rs, off[u], pack<DT>(y));
+    stream_store(rs, off[u], pack<DT>(y, may_exceed));
   }
 }
 
@@ -201,10 +201,14 @@ __global__ __launch_bounds__(QKNORM_PH_THREADS) void per_head_kernel(
     for (int q = 0; q < GV; ++q) w.v[q] = g_lds[sub * GV + q];
     unpack_gamma<DT>(w, g);
   }
+  // FP8: whether this wave's outputs can leave the E4M3 range (all lanes
+  // take part in the ballot, so before the early exit)
+  bool may_exceed = true;
+  if constexpr (DT == kFP8) may_exceed = e4m3_may_exceed(abs_max<E>(g, 0.f), inv_d);
   if (!live) return;
 
   if constexpr (ONE) {
-    per_head_apply<DT, LPH, U>(vc, g, inv_d, eps, cur.rs, cur.off);
+    per_head_apply<DT, LPH, U>(vc, g, inv_d, eps, may_exceed, cur.rs, cur.off);
     return;
   }
   while (true) {
@@ -217,7 +221,7 @@ __global__ __launch_bounds__(QKNORM_PH_THREADS) void per_head_kernel(
     nxt.setup(qkv, ld_bytes, T, H, col, more, tn, hn, sub, grp);
 #pragma unroll
     for (uint32_t u = 0; u < U; ++u) vn[u] = stream_load(nxt.rs, nxt.off[u]);
-    per_head_apply<DT, LPH, U>(vc, g, inv_d, eps, cur.rs, cur.off);
+    per_head_apply<DT, LPH, U>(vc, g, inv_d, eps, may_exceed, cur.rs, cur.off);
     if (!more) break;
     cur = nxt;
 #pragma unroll
@@ -264,25 +268,45 @@ struct Slots {
   Gam<DT> g[VPL];
 };
 
+constexpr uint32_t kOutOfRange = 0xFFFFFFF0u;
+
+// Straight-line buffer loads (cached policy); an empty slot reads zeros
+// through an offset past the descriptor.
 template <int DT, int VPL>
 __device__ __forceinline__ void slots_load_gamma(const uint8_t* __restrict__ gamma, uint32_t svecs,
                                                  uint32_t R, uint32_t wave, uint32_t nw,
                                                  uint32_t lane, Slots<DT, VPL>& S) {
+  constexpr uint32_t GV = Gam<DT>::kVecs;
+  const Rsrc gr = make_rsrc(gamma, (uint64_t)R * svecs * GV * 16);
   const uint32_t trips = (svecs + 63) / 64;
   uint32_t i = 0, k = 0;
 #pragma unroll
   for (int j = 0; j < VPL; ++j) {
     const uint32_t r = wave + i * nw, v = lane + k * 64;
-    S.g[j] = (r < R && v < svecs) ? load_gamma<DT>(gamma, (uint64_t)r * svecs + v)
-                                  : zero_gamma<DT>();
+    const bool ok = r < R && v < svecs;
+#pragma unroll
+    for (uint32_t q = 0; q < GV; ++q)
+      S.g[j].v[q] = cached_load(gr, ok ? ((r * svecs + v) * GV + q) * 16 : kOutOfRange);
     if (++k == trips) { k = 0; ++i; }
   }
+}
+
+// Largest |gamma| over a lane's slots (its zero slots included).
+template <int DT, int VPL>
+__device__ __forceinline__ float slots_gamma_max(const Slots<DT, VPL>& S) {
+  float m = 0.f;
+#pragma unroll
+  for (int j = 0; j < VPL; ++j) {
+    float g[IoTraits<DT>::kElems];
+    unpack_gamma<DT>(S.g[j], g);
+    m = abs_max(g, m);
+  }
+  return m;
 }
 
 // Loads are unconditional (an invalid slot gets an offset past the row's
 // descriptor and reads 0), so a whole row's loads can stay in flight while the
 // previous row is being reduced.
-constexpr uint32_t kOutOfRange = 0xFFFFFFF0u;
 
 template <int DT, int VPL>
 __device__ __forceinline__ void slots_load(Rsrc rs, uint32_t reg_off, uint32_t svecs, uint32_t R,
@@ -326,7 +350,8 @@ __device__ __forceinline__ void slots_partials(uint32_t svecs, uint32_t R, uint3
 template <int DT, int VPL>
 __device__ __forceinline__ void slots_apply(Rsrc rs, uint32_t reg_off, uint32_t svecs, uint32_t R,
                                             uint32_t wave, uint32_t nw, uint32_t lane,
-                                            const Slots<DT, VPL>& S, float scale) {
+                                            const Slots<DT, VPL>& S, float scale,
+                                            bool may_exceed) {
   using IO = IoTraits<DT>;
   const uint32_t trips = (svecs + 63) / 64;
   uint32_t i = 0, k = 0;
@@ -339,7 +364,7 @@ __device__ __forceinline__ void slots_apply(Rsrc rs, uint32_t reg_off, uint32_t 
 #pragma unroll
     for (int e = 0; e < IO::kElems; ++e) y[e] = (x[e] * g[e]) * scale;
     stream_store(rs, (r < R && v < svecs) ? reg_off + (r * svecs + v) * 16 : kOutOfRange,
-                 pack<DT>(y));
+                 pack<DT>(y, may_exceed));
     if (++k == trips) { k = 0; ++i; }
   }
 }
@@ -407,7 +432,7 @@ template <int DT, int QV, int KV>
 __device__ __forceinline__ void lw_finish(const RowGeom& G, Rsrc rs, uint32_t Rq, uint32_t Rk,
                                           uint32_t wave, uint32_t nw, uint32_t lane, float eps,
                                           LwRow<DT, QV, KV>& row, const LwRow<DT, QV, KV>& gam,
-                                          float* __restrict__ part) {
+                                          bool exceed_q, bool exceed_k, float* __restrict__ part) {
   const uint32_t R = G.nshards;
   float* pq = part;
   float* pk = part + R;
@@ -419,9 +444,9 @@ __device__ __forceinline__ void lw_finish(const RowGeom& G, Rsrc rs, uint32_t Rq
 #pragma unroll
   for (int j = 0; j < KV; ++j) row.k.g[j] = gam.k.g[j];
   if (Rq) slots_apply<DT, QV>(rs, 0, G.q_svecs, Rq, wave, nw, lane, row.q,
-                              rms_scale(combine(pq, R, 1), G.inv_wq, eps));
+                              rms_scale(combine(pq, R, 1), G.inv_wq, eps), exceed_q);
   if (Rk) slots_apply<DT, KV>(rs, G.q_vecs * 16, G.k_svecs, Rk, wave, nw, lane, row.k,
-                              rms_scale(combine(pk, R, 1), G.inv_wk, eps));
+                              rms_scale(combine(pk, R, 1), G.inv_wk, eps), exceed_k);
 }
 
 // QV / KV: register slots per lane for Q and for K (a lane's shard vectors).
@@ -438,12 +463,19 @@ __global__ __launch_bounds__(512) void layerwise_regs_kernel(
   const uint32_t stride = gridDim.x;
 
   uint32_t t = blockIdx.x;
+  if (t >= G.T) return;                        // whole block: no barrier is skipped by part of it
   LwRow<DT, QV, KV> a, b, gam;
   Rsrc ra, rb;
-  lw_issue<DT, QV, KV>(qkv, G, t, t < G.T, Rq, Rk, wave, nw, lane, ra, a);
+  // gamma first (straight-line loads): the FP8 range test below then waits
+  // for gamma only, while the first row's loads stay in flight
   slots_load_gamma<DT, QV>(gamma_q, G.q_svecs, Rq, wave, nw, lane, gam.q);
   slots_load_gamma<DT, KV>(gamma_k, G.k_svecs, Rk, wave, nw, lane, gam.k);
-  if (t >= G.T) return;                        // whole block: no barrier is skipped by part of it
+  lw_issue<DT, QV, KV>(qkv, G, t, true, Rq, Rk, wave, nw, lane, ra, a);
+  bool exceed_q = true, exceed_k = true;
+  if constexpr (DT == kFP8) {
+    exceed_q = e4m3_may_exceed(slots_gamma_max(gam.q), G.inv_wq);
+    exceed_k = e4m3_may_exceed(slots_gamma_max(gam.k), G.inv_wk);
+  }
 
   // LDS partials alternate between two buffers, one per register set: a
   // buffer is written again only after every thread has passed the barrier of
@@ -452,12 +484,13 @@ __global__ __launch_bounds__(512) void layerwise_regs_kernel(
     const uint32_t t1 = t + stride;
     const bool more1 = t1 < G.T;
     lw_issue<DT, QV, KV>(qkv, G, t1, more1, Rq, Rk, wave, nw, lane, rb, b);
-    lw_finish<DT, QV, KV>(G, ra, Rq, Rk, wave, nw, lane, eps, a, gam, lds);
+    lw_finish<DT, QV, KV>(G, ra, Rq, Rk, wave, nw, lane, eps, a, gam, exceed_q, exceed_k, lds);
     if (!more1) break;
     const uint32_t t2 = t1 + stride;
     const bool more2 = t2 < G.T;
     lw_issue<DT, QV, KV>(qkv, G, t2, more2, Rq, Rk, wave, nw, lane, ra, a);
-    lw_finish<DT, QV, KV>(G, rb, Rq, Rk, wave, nw, lane, eps, b, gam, lds + 2 * R);
+    lw_finish<DT, QV, KV>(G, rb, Rq, Rk, wave, nw, lane, eps, b, gam, exceed_q, exceed_k,
+                          lds + 2 * R);
     if (!more2) break;
     t = t2;
   }
@@ -580,8 +613,9 @@ __global__ __launch_bounds__(256) void partial_sumsq_kernel(const uint8_t* __res
 // nparts-1; each r one contiguous read across those threads), takes
 // rsq((sum)/norm_w + eps) and leaves it in LDS.  Then every row is applied
 // with flat 16-byte vectors over Q then K; thread tid takes vectors tid,
-// tid+512, ... of every row, so its gamma vectors stay in registers (VPT of
-// them) for all the block's rows.
+// tid+nt, ... of every row (nt threads), so its gamma vectors stay in
+// registers (VPT of them) for all the block's rows.  The launcher picks VPT
+// and nt <= 512 that leave the fewest (thread, vector) slots idle.
 #ifndef QKNORM_APPLY_ROWS
 #define QKNORM_APPLY_ROWS 2        // rows per phase-C block
 #endif
@@ -871,12 +905,12 @@ hipError_t launch_partial_sumsq(const PartialArgs& a, hipStream_t s, int cus) {
 
 template <int DT, int VPT>
 static hipError_t launch_apply_rows(const ApplyArgs& a, hipStream_t s, int cus, uint32_t qv,
-                                    uint32_t kv, float iq, float ik) {
+                                    uint32_t kv, float iq, float ik, uint32_t threads) {
   uint64_t blocks = ((uint64_t)a.T + kApplyRows - 1) / kApplyRows;
-  const uint64_t cap = (uint64_t)cus * (QKNORM_LW_WAVES_PER_CU / 8);
+  const uint64_t cap = (uint64_t)cus * (QKNORM_LW_WAVES_PER_CU / (threads / 64));
   if (blocks > cap) blocks = cap;
   if (blocks < 1) blocks = 1;
-  hipLaunchKernelGGL((apply_scalar_kernel<DT, VPT>), dim3((uint32_t)blocks), dim3(512), 0, s,
+  hipLaunchKernelGGL((apply_scalar_kernel<DT, VPT>), dim3((uint32_t)blocks), dim3(threads), 0, s,
                      (uint8_t*)a.qkv, (uint64_t)(a.ld * IoTraits<DT>::kBytes), (uint32_t)a.T, qv, kv,
                      a.part_q, a.part_k, (uint32_t)a.nparts, iq, ik, (const uint8_t*)a.gamma_q,
                      (const uint8_t*)a.gamma_k, a.eps);
@@ -889,11 +923,24 @@ static hipError_t launch_apply_dt(const ApplyArgs& a, hipStream_t s, int cus) {
   const uint32_t qv = (uint32_t)(a.wq * esize / 16), kv = (uint32_t)(a.wk * esize / 16);
   const float iq = a.norm_wq ? 1.0f / (float)a.norm_wq : 0.f;
   const float ik = a.norm_wk ? 1.0f / (float)a.norm_wk : 0.f;
-  const uint32_t vpt = (qv + kv + 511) / 512;
-  if (vpt <= 1) return launch_apply_rows<DT, 1>(a, s, cus, qv, kv, iq, ik);
-  if (vpt <= 2) return launch_apply_rows<DT, 2>(a, s, cus, qv, kv, iq, ik);
-  if (vpt <= 3) return launch_apply_rows<DT, 3>(a, s, cus, qv, kv, iq, ik);
-  if (vpt <= 4) return launch_apply_rows<DT, 4>(a, s, cus, qv, kv, iq, ik);
+  // vectors per thread and block size: at most 512 threads, as few idle
+  // (thread, vector) slots as possible, fewer vectors per thread on a tie
+  const uint32_t nv = qv + kv;
+  uint32_t vpt = 0, threads = 512;
+  uint64_t best = ~0ull;
+  for (uint32_t c = 1; c <= 4; ++c) {
+    const uint32_t t = ((nv + c - 1) / c + 63) / 64 * 64;
+    if (t > 512) continue;
+    const uint64_t idle = (uint64_t)t * c - nv;
+    if (idle < best) { best = idle; vpt = c; threads = t; }
+  }
+  switch (vpt) {
+    case 1: return launch_apply_rows<DT, 1>(a, s, cus, qv, kv, iq, ik, threads);
+    case 2: return launch_apply_rows<DT, 2>(a, s, cus, qv, kv, iq, ik, threads);
+    case 3: return launch_apply_rows<DT, 3>(a, s, cus, qv, kv, iq, ik, threads);
+    case 4: return launch_apply_rows<DT, 4>(a, s, cus, qv, kv, iq, ik, threads);
+    default: break;
+  }
   uint64_t blocks = a.T;
   const uint64_t cap = (uint64_t)cus * (QKNORM_LW_WAVES_PER_CU / 4);
   if (blocks > cap) blocks = cap;

@@ -277,10 +277,10 @@ def cfg1(seed: int = 1) -> Problem:
     return per_head_problem("cfg1_per_head_f32", seed, F32, 4, 16, 4, 128)
 
 
-def cfg2(T: int = 4096, H: int = 48, seed: int = 2) -> Problem:
+def cfg2(T: int = 4096, H: int = 48, seed: int = 2, dtype: int = BF16) -> Problem:
     """Per-head, bf16, standalone [T, H, 128]; N(0,1) times per-token U(0.1, 10)."""
-    return per_head_problem(f"cfg2_per_head_bf16_T{T}_H{H}", seed, BF16, T, H, 0, 128,
-                            token_scale=(0.1, 10.0))
+    return per_head_problem(f"cfg2_per_head_{DTYPE_NAMES[dtype]}_T{T}_H{H}", seed, dtype, T, H, 0,
+                            128, token_scale=(0.1, 10.0))
 
 
 def cfg3(T: int = 8192, seed: int = 3) -> Problem:
@@ -294,15 +294,17 @@ def cfg4(T: int = 256, seed: int = 4) -> Problem:
                              outlier_frac=0.01)
 
 
-def cfg5(T: int = 32768, seed: int = 5, mode: str = "layerwise", row_start: int = 0) -> Problem:
+def cfg5(T: int = 32768, seed: int = 5, mode: str = "layerwise", row_start: int = 0,
+         dtype: int = BF16) -> Problem:
     """Large prefill: [T, 10240], Hq=64, Hkv=8, D=128; outliers x20 and per-token U(0.1, 10).
 
     Per-head and layerwise share x (same seed); only the gamma widths differ.
     """
+    name = DTYPE_NAMES[dtype]
     if mode == "per_head":
-        return per_head_problem(f"cfg5_per_head_bf16_T{T}", seed, BF16, T, 64, 8, 128,
+        return per_head_problem(f"cfg5_per_head_{name}_T{T}", seed, dtype, T, 64, 8, 128,
                                 token_scale=(0.1, 10.0), outlier_frac=0.01, row_start=row_start)
-    return layerwise_problem(f"cfg5_layerwise_bf16_T{T}", seed, BF16, T, 8192, 1024, 10240, 8,
+    return layerwise_problem(f"cfg5_layerwise_{name}_T{T}", seed, dtype, T, 8192, 1024, 10240, 8,
                              token_scale=(0.1, 10.0), outlier_frac=0.01, row_start=row_start)
 
 

@@ -183,6 +183,31 @@ def test_tensor_parallel_emulation_other_dtypes(dtype):
     assert np.array_equal(got, ref), "rank-sliced two-phase differs from the fused kernel"
 
 
+def test_e4m3_saturation_fused_and_two_phase():
+    # K's gamma of 96 lets |y| reach 96 * sqrt(1024) = 3072 (saturated to 448);
+    # Q's small gamma never leaves the range.  Fused and two-phase must both
+    # give the oracle's bytes exactly (no NaN).
+    T, wq, wk = 40, 4096, 1024
+    dtype = synth.F8
+    x = synth.normal(61, 0, T * (wq + 2 * wk)).reshape(T, wq + 2 * wk)
+    x[:, wq:wq + wk] = 0.0
+    x[:, wq + 5] = np.where(np.arange(T) % 2 == 0, 3.0, -0.5)      # one nonzero in K
+    x[:, wq + 700] = 0.25
+    gq = synth.make_gamma(61, 3, wq, dtype)
+    gk = synth.to_dtype(np.full(wk, 96.0), synth.BF16)
+    p = synth.Problem("e4m3_saturate_lw", dtype, T, wq + 2 * wk, wq, wk, synth.to_dtype(x, dtype),
+                      gq, gk, synth.eps_f32(1e-6), nshards=8)
+    a = fused(p)
+    b, _, _ = two_phase(p)
+    _, yr = oracle.layerwise(p.x, dtype, wq, wk, gq, gk, p.eps, 8)
+    assert np.array_equal(a[:, wq:], yr[:, wq:]), "fused: K bytes"
+    assert np.array_equal(b[:, wq:], yr[:, wq:]), "two-phase: K bytes"
+    assert set(np.unique(a[:, wq + 5]).tolist()) == {0x7E, 0xFE}
+    y64, _ = oracle.layerwise(p.x, dtype, wq, wk, gq, gk, p.eps, 8)
+    assert_close_to_oracle(a[:, :wq], y64[:, :wq], dtype, label="Q region")
+    assert np.array_equal(a, b)
+
+
 def test_bitwise_deterministic():
     p = synth.cfg4(T=256)
     assert np.array_equal(fused(p), fused(p))

@@ -210,6 +210,30 @@ def test_e4m3_saturates_at_448():
     assert set(np.unique(got[:, ::D]).tolist()) == {0x7E, 0xFE}
 
 
+@pytest.mark.parametrize("gval", [39.5, 40.0, 41.0, 42.0])
+def test_e4m3_range_boundary(gval):
+    # one nonzero per head gives |y| = gamma * sqrt(128): 447 (no saturation
+    # needed, the range test lets the conversion alone round it), 452.5 and
+    # 463.8 (round to 448 either way) and 475 (NaN without saturation).  Q uses
+    # this gamma, K a small one, so the two regions take different paths.
+    T, hq, hkv, D = 16, 4, 2, 128
+    dtype = synth.F8
+    x = np.zeros((T, (hq + 2 * hkv) * D))
+    x[:, : (hq + hkv) * D: D] = np.where(np.arange(T)[:, None] % 3 == 0, -2.0, 0.375)
+    gq = synth.to_dtype(np.full(D, gval), synth.BF16)
+    gk = synth.make_gamma(34, 4, D, dtype)
+    p = synth.Problem(f"e4m3_boundary_{gval}", dtype, T, x.shape[1], hq * D, hkv * D,
+                      synth.to_dtype(x, dtype), gq, gk, synth.eps_f32(0.0), hq=hq, hkv=hkv, head_dim=D)
+    buf = Guarded(p.x, dtype)
+    q.qknorm_per_head(buf.t, hq, hkv, D, gamma_to_device(gq, dtype), gamma_to_device(gk, dtype), p.eps)
+    torch.cuda.synchronize()
+    got = buf.host()
+    assert buf.guards_intact()
+    _, yr = oracle.per_head(p.x, dtype, hq, hkv, D, gq, gk, p.eps)
+    assert np.array_equal(got, yr), f"E4M3 bytes at gamma {gval}"
+    assert set(np.unique(got[:, : hq * D: D]).tolist()) <= {0x7E, 0xFE}
+
+
 def test_bitwise_deterministic():
     p = synth.cfg3(T=512)
     a, _ = run_per_head(p)
