@@ -87,9 +87,16 @@ extern "C" {
  *  #13189, Motivation and Modifications: the QK norm is an RMSNorm whose
  *  hidden size is the head dimension, 128 in the benchmark tables.)
  *
- * Requires: a head of 64 to 1024 bytes, a power of two (FP8 head_dim
- * 64..1024, bf16/fp16 32..512, fp32 16..256); ld >= (hq+hkv)*head_dim; qkv,
- * gamma and ld*esize 16-byte aligned.
+ * Serves any RMSNorm whose width is a head (the PR routes every RMSNorm of
+ * hidden size <= 128 to it): a plain [T, hidden] RMSNorm is hq = 1, hkv = 0,
+ * head_dim = ld = hidden.
+ *
+ * Requires: head_dim*esize a multiple of 16 bytes (else QKNORM_E_ALIGN) and
+ * at most 1024 bytes (FP8 head_dim 16..1024 in steps of 16, bf16/fp16 8..512
+ * in steps of 8, fp32 4..256 in steps of 4); ld >= (hq+hkv)*head_dim; qkv,
+ * gamma and ld*esize 16-byte aligned.  QKNORM_E_UNSUPPORTED also when one
+ * launch step over the smallest heads (16 or 32 bytes) would span 2 GiB of
+ * rows (a tiny head in rows of tens of MiB).
  */
 int qknorm_per_head(void *qkv, int64_t T, int64_t ld, int32_t hq, int32_t hkv,
                     int32_t head_dim, const void *gamma_q, const void *gamma_k,

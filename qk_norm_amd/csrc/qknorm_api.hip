@@ -113,15 +113,16 @@ int qknorm_per_head(void* qkv, int64_t T, int64_t ld, int32_t hq, int32_t hkv, i
   if ((rc = check_region(qkv, T, ld, wq, wk, es))) return rc;
   if ((rc = check_gamma(gamma_q, wq, T))) return rc;
   if ((rc = check_gamma(gamma_k, wk, T))) return rc;
-  // a head is 4..64 lanes of 16 bytes, a power of two
+  // a head is 1..64 vectors of 16 bytes
   const int64_t head_bytes = (int64_t)head_dim * es;
-  if (head_bytes < 64 || head_bytes > 1024 || (head_bytes & (head_bytes - 1)) != 0)
-    return QKNORM_E_UNSUPPORTED;
+  if (head_bytes % 16 != 0) return QKNORM_E_ALIGN;
+  if (head_bytes > 1024) return QKNORM_E_UNSUPPORTED;
   if (T * ((int64_t)hq + hkv) >= kMaxHeadIndex) return QKNORM_E_UNSUPPORTED;
+  qknorm::PerHeadArgs a{qkv, T, ld, hq, hkv, head_dim, gamma_q, gamma_k, eps, dtype};
+  if (!qknorm::per_head_span_ok(a)) return QKNORM_E_UNSUPPORTED;
   if (T == 0 || hq + hkv == 0) return QKNORM_OK;
   int cus = 0;
   if ((rc = device_cus(&cus))) return rc;
-  qknorm::PerHeadArgs a{qkv, T, ld, hq, hkv, head_dim, gamma_q, gamma_k, eps, dtype};
   return finish(qknorm::launch_per_head(a, static_cast<hipStream_t>(stream), cus));
 }
 

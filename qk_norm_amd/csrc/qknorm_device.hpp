@@ -265,11 +265,12 @@ __device__ __forceinline__ float dpp_add(float v) {
                                            0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
 }
 
-// Sum over aligned groups of LANES consecutive lanes (LANES in 2..64).
+// Sum over aligned groups of LANES consecutive lanes (LANES in 1..64).
 template <int LANES>
 __device__ __forceinline__ float group_sum(float v) {
-  static_assert(LANES == 2 || LANES == 4 || LANES == 8 || LANES == 16 || LANES == 32 ||
-                    LANES == 64, "group must be a power of two up to the wave");
+  static_assert(LANES == 1 || LANES == 2 || LANES == 4 || LANES == 8 || LANES == 16 ||
+                    LANES == 32 || LANES == 64, "group must be a power of two up to the wave");
+  if constexpr (LANES == 1) return v;
   v = dpp_add<0xB1>(v);                       // quad_perm [1,0,3,2]: pairs
   if constexpr (LANES >= 4) v = dpp_add<0x4E>(v);   // quad_perm [2,3,0,1]: quads
   if constexpr (LANES >= 8) v = dpp_add<0x141>(v);  // row_half_mirror: half-rows of 8

@@ -70,6 +70,8 @@ struct PhRegion {
 // Addresses of one trip: U heads per lane group starting at the wave's head
 // (tw, hw) of the region.  CONTIG: rows hold just this region's heads, back
 // to back, so the heads form one flat array (tw = 0, hw = flat index).
+// A head is hv 16-byte vectors (hb = 16*hv bytes); the group has LPH >= hv
+// lanes and lanes sub >= hv hold no part of it.
 //
 // Loads and stores are issued unconditionally (straight-line code, so the
 // compiler can keep the next trip's loads in flight while this trip is being
@@ -77,7 +79,8 @@ struct PhRegion {
 // lane without a head gets an offset past that span, and a trip past the end
 // of the tensor gets an empty descriptor, so the hardware range check turns
 // those accesses into no-ops (loads return 0, stores are dropped).  Every
-// span is below 2^31 bytes (at most CH/H + 2 rows of at most 64 MiB).
+// span is below 2^31 bytes: per_head_span_ok() checks the largest one on the
+// host before any launch.
 template <int LPH, int U, bool CONTIG>
 struct PerHeadTrip {
   Rsrc rs;
@@ -87,10 +90,11 @@ struct PerHeadTrip {
 
   __device__ __forceinline__ void setup(uint8_t* qkv, uint32_t ld_bytes, uint32_t T, uint32_t H,
                                         uint32_t col_bytes, bool live, uint32_t tw, uint32_t hw,
-                                        uint32_t sub, uint32_t grp) {
+                                        uint32_t sub, uint32_t grp, uint32_t hv) {
     constexpr uint32_t HPW = 64 / LPH;
     constexpr uint32_t CH = HPW * U;
-    constexpr uint32_t head_bytes = LPH * 16;
+    const uint32_t head_bytes = hv * 16;
+    const bool mine = sub < hv;              // this lane holds part of its head
     tw = live ? tw : 0;
     hw = live ? hw : 0;
     uint64_t first, rest, span;
@@ -109,14 +113,14 @@ struct PerHeadTrip {
     for (uint32_t u = 0; u < U; ++u) {
       const uint32_t k = u * HPW + grp;      // head index from the wave's first head
       if constexpr (CONTIG) {
-        off[u] = hw + k < T * H ? k * head_bytes + sub * 16 : kNoHead;
+        off[u] = mine && hw + k < T * H ? k * head_bytes + sub * 16 : kNoHead;
       } else {
         uint32_t hu = hw + k, dt = 0;
         if (hu >= H) {                       // wrap into the following row(s)
           dt = hu / H;
           hu -= dt * H;
         }
-        off[u] = tw + dt < T ? dt * ld_bytes + hu * head_bytes + sub * 16 : kNoHead;
+        off[u] = mine && tw + dt < T ? dt * ld_bytes + hu * head_bytes + sub * 16 : kNoHead;
       }
     }
   }
@@ -144,14 +148,17 @@ __device__ __forceinline__ void per_head_apply(const u32x4 (&v)[U], const float 
 // ONE: the grid covers every head in one trip, so there is no loop.
 // Otherwise the loop is software-pipelined: the next trip's loads are issued
 // before the current trip's reduction and stores.
-template <int DT, int LPH, int U, bool CONTIG, bool ONE>
+// EXACT: a head is exactly LPH vectors (a power of two); otherwise it is
+// hvec < LPH vectors and the group's last LPH - hvec lanes stay idle.
+template <int DT, int LPH, int U, bool CONTIG, bool ONE, bool EXACT>
 __global__ __launch_bounds__(QKNORM_PH_THREADS) void per_head_kernel(
     uint8_t* __restrict__ qkv, uint32_t ld_bytes, uint32_t T, PhRegion r0, PhRegion r1,
-    float eps, float inv_d) {
+    float eps, float inv_d, uint32_t hvec) {
   using IO = IoTraits<DT>;
   using Trip = PerHeadTrip<LPH, U, CONTIG>;
   constexpr int E = IO::kElems;
   constexpr uint32_t CH = (64 / LPH) * U;    // heads per wave per trip
+  const uint32_t hv = EXACT ? (uint32_t)LPH : hvec;
   const uint32_t lane = threadIdx.x & 63;
   const uint32_t sub = lane % LPH;           // 16-byte slot inside the head
   const uint32_t grp = lane / LPH;           // head slot inside the wave step
@@ -176,7 +183,7 @@ __global__ __launch_bounds__(QKNORM_PH_THREADS) void per_head_kernel(
   // first trip's loads go out before any gamma work
   Trip cur;
   u32x4 vc[U];
-  cur.setup(qkv, ld_bytes, T, H, col, live, tw, hw, sub, grp);
+  cur.setup(qkv, ld_bytes, T, H, col, live, tw, hw, sub, grp, hv);
 #pragma unroll
   for (uint32_t u = 0; u < U; ++u) vc[u] = stream_load(cur.rs, cur.off[u]);
   __builtin_amdgcn_sched_barrier(0);           // keep the row loads ahead of the gamma work
@@ -185,16 +192,19 @@ __global__ __launch_bounds__(QKNORM_PH_THREADS) void per_head_kernel(
   // makes those lines an L2 hot spot.  Heads with at most 64 dwords of gamma
   // read the region's gamma with scalar loads through the scalar cache and
   // hand each lane its dwords with selects, which run while the row loads are
-  // in flight; longer ones stage it once per block in LDS.
+  // in flight; longer ones, and heads that do not fill their lane group (the
+  // scalar loads would read past gamma), stage it once per block in LDS.
   constexpr int GV = Gam<DT>::kVecs;
   float g[E];
-  if constexpr (kGammaSgpr && 4 * GV * LPH <= 64) {
+  if constexpr (kGammaSgpr && EXACT && 4 * GV * LPH <= 64) {
     Gam<DT> w = zero_gamma<DT>();
     gamma_to_lanes<DT, LPH>(reinterpret_cast<const uint32_t*>(gamma), sub, w);
     unpack_gamma<DT>(w, g);
   } else {
     __shared__ u32x4 g_lds[LPH * GV];
-    if (threadIdx.x < LPH * GV) g_lds[threadIdx.x] = load16(gamma + threadIdx.x * 16);
+    if (threadIdx.x < LPH * GV)
+      g_lds[threadIdx.x] = threadIdx.x < hv * GV ? load16(gamma + threadIdx.x * 16)
+                                                 : u32x4{0, 0, 0, 0};
     __syncthreads();
     Gam<DT> w;
 #pragma unroll
@@ -218,7 +228,7 @@ __global__ __launch_bounds__(QKNORM_PH_THREADS) void per_head_kernel(
     const bool more = CONTIG ? hn < T * H : tn < T;
     Trip nxt;
     u32x4 vn[U];
-    nxt.setup(qkv, ld_bytes, T, H, col, more, tn, hn, sub, grp);
+    nxt.setup(qkv, ld_bytes, T, H, col, more, tn, hn, sub, grp, hv);
 #pragma unroll
     for (uint32_t u = 0; u < U; ++u) vn[u] = stream_load(nxt.rs, nxt.off[u]);
     per_head_apply<DT, LPH, U>(vc, g, inv_d, eps, may_exceed, cur.rs, cur.off);
@@ -723,6 +733,8 @@ static hipError_t launch_per_head_t(const PerHeadArgs& a, hipStream_t s, int cus
   constexpr uint64_t heads_per_block = CH * (kBlock / 64);
   const int es = IoTraits<DT>::kBytes;
   const uint32_t head_bytes = (uint32_t)(a.head_dim * es);
+  const uint32_t hvec = head_bytes / 16;
+  const bool exact = hvec == (uint32_t)LPH;
   const uint64_t cap = (uint64_t)cus * QKNORM_PH_BLOCKS_PER_CU;
   const uint64_t Htot = (uint64_t)a.hq + a.hkv;
 
@@ -751,26 +763,52 @@ static hipError_t launch_per_head_t(const PerHeadArgs& a, hipStream_t s, int cus
     r.stride_heads = (uint32_t)(stride % r.H);
   }
   // a single region whose rows hold nothing else: one flat array of heads
-  const bool contig = n == 1 && reg[0].col_bytes == 0 &&
+  // (heads of a power-of-two size only; others take the row-wise kernel)
+  const bool contig = exact && n == 1 && reg[0].col_bytes == 0 &&
                       a.ld == (int64_t)reg[0].H * a.head_dim;
   if (contig) {
     reg[0].stride_heads = reg[0].stride_rows * reg[0].H + reg[0].stride_heads;
     reg[0].stride_rows = 0;
   }
-  auto kern = contig ? (one ? per_head_kernel<DT, LPH, U, true, true>
-                            : per_head_kernel<DT, LPH, U, true, false>)
-                     : (one ? per_head_kernel<DT, LPH, U, false, true>
-                            : per_head_kernel<DT, LPH, U, false, false>);
+  auto kern = !exact ? (one ? per_head_kernel<DT, LPH, U, false, true, false>
+                            : per_head_kernel<DT, LPH, U, false, false, false>)
+              : contig ? (one ? per_head_kernel<DT, LPH, U, true, true, true>
+                              : per_head_kernel<DT, LPH, U, true, false, true>)
+                       : (one ? per_head_kernel<DT, LPH, U, false, true, true>
+                              : per_head_kernel<DT, LPH, U, false, false, true>);
   hipLaunchKernelGGL(kern, dim3(reg[0].blocks + reg[1].blocks), dim3(kBlock), 0, s,
                      (uint8_t*)a.qkv, (uint32_t)(a.ld * es), (uint32_t)a.T, reg[0], reg[1], a.eps,
-                     1.0f / (float)a.head_dim);
+                     1.0f / (float)a.head_dim, hvec);
   return hipGetLastError();
+}
+
+// Lanes per head: the head's 16-byte vectors rounded up to a power of two.
+static uint32_t lanes_per_head(uint32_t hvec) {
+  uint32_t l = 1;
+  while (l < hvec) l <<= 1;
+  return l;
+}
+
+bool per_head_span_ok(const PerHeadArgs& a) {
+  // the largest descriptor span of a trip: from a wave's first head (at most
+  // H-1 into its row) over CH heads, plus the region, must stay below 2^31
+  const int es = a.dtype == kF32 ? 4 : (a.dtype == kFP8 ? 1 : 2);
+  const uint64_t hb = (uint64_t)a.head_dim * es;
+  const uint64_t ch = (64 / lanes_per_head((uint32_t)(hb / 16))) * (uint64_t)QKNORM_PH_UNROLL;
+  const uint64_t ld_bytes = (uint64_t)a.ld * es;
+  for (int64_t H : {(int64_t)a.hq, (int64_t)a.hkv}) {
+    if (H <= 0) continue;
+    const uint64_t span = ((uint64_t)H + ch - 2) / (uint64_t)H * ld_bytes + (uint64_t)H * hb;
+    if (span >= (UINT64_C(1) << 31)) return false;
+  }
+  return true;
 }
 
 template <int DT>
 static hipError_t launch_per_head_dt(const PerHeadArgs& a, hipStream_t s, int cus) {
-  const int lph = a.head_dim * IoTraits<DT>::kBytes / 16;
-  switch (lph) {
+  switch (lanes_per_head((uint32_t)(a.head_dim * IoTraits<DT>::kBytes / 16))) {
+    case 1: return launch_per_head_t<DT, 1>(a, s, cus);
+    case 2: return launch_per_head_t<DT, 2>(a, s, cus);
     case 4: return launch_per_head_t<DT, 4>(a, s, cus);
     case 8: return launch_per_head_t<DT, 8>(a, s, cus);
     case 16: return launch_per_head_t<DT, 16>(a, s, cus);

@@ -49,6 +49,8 @@ struct ApplyArgs {
 };
 
 // `cus` is the compute-unit count of the current device (grid sizing).
+// Whether every per-head trip's buffer span stays below 2^31 bytes.
+bool per_head_span_ok(const PerHeadArgs& a);
 hipError_t launch_per_head(const PerHeadArgs& a, hipStream_t s, int cus);
 hipError_t launch_layerwise(const LayerwiseArgs& a, hipStream_t s, int cus);
 hipError_t launch_partial_sumsq(const PartialArgs& a, hipStream_t s, int cus);

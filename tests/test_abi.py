@@ -160,25 +160,30 @@ def test_alignment(lib):
     assert lw(lib, T=0, ld=6160, dt=F8) == q.QKNORM_OK
 
 
-@pytest.mark.parametrize("dt,D", [(F32, 16), (F32, 32), (F32, 64), (F32, 128), (F32, 256),
-                                  (BF16, 32), (BF16, 64), (BF16, 128), (BF16, 256), (BF16, 512),
-                                  (F16, 32), (F16, 128), (F16, 512),
-                                  (F8, 64), (F8, 128), (F8, 256), (F8, 512), (F8, 1024)])
+@pytest.mark.parametrize("dt,D", [(F32, 4), (F32, 12), (F32, 16), (F32, 100), (F32, 256),
+                                  (BF16, 8), (BF16, 24), (BF16, 96), (BF16, 128), (BF16, 504),
+                                  (BF16, 512), (F16, 40), (F16, 128), (F16, 512),
+                                  (F8, 16), (F8, 48), (F8, 128), (F8, 1008), (F8, 1024)])
 def test_head_widths_accepted(lib, dt, D):
-    # a head is 64 to 1024 bytes, a power of two (T = 0: validated, nothing launched)
+    # any head of 16 to 1024 bytes in 16-byte steps (T = 0: validated, nothing launched)
     assert ph(lib, T=0, D=D, ld=20 * D, dt=dt) == q.QKNORM_OK
 
 
+def test_head_bytes_not_a_multiple_of_16(lib):
+    assert ph(lib, T=0, D=100, ld=20 * 100, dt=BF16) == q.QKNORM_E_ALIGN   # 200-byte heads
+    assert ph(lib, D=100, ld=20 * 100, dt=BF16) == q.QKNORM_E_ALIGN
+    assert ph(lib, D=2, hq=8, hkv=0, ld=16, dt=F32) == q.QKNORM_E_ALIGN    # 8-byte heads
+    assert ph(lib, D=20, hq=4, hkv=0, ld=80, dt=F8) == q.QKNORM_E_ALIGN
+
+
 def test_unsupported(lib):
-    assert ph(lib, D=96, ld=20 * 96) == q.QKNORM_E_UNSUPPORTED
-    assert ph(lib, D=96, ld=20 * 96, T=0) == q.QKNORM_E_UNSUPPORTED   # checked before T == 0
     assert ph(lib, D=512, ld=20 * 512) == q.QKNORM_E_UNSUPPORTED      # fp32: 2 KiB heads
-    assert ph(lib, D=8, ld=20 * 8) == q.QKNORM_E_UNSUPPORTED          # fp32: 32 B heads
-    assert ph(lib, D=16, ld=20 * 16, dt=BF16) == q.QKNORM_E_UNSUPPORTED
+    assert ph(lib, D=512, ld=20 * 512, T=0) == q.QKNORM_E_UNSUPPORTED  # checked before T == 0
     assert ph(lib, D=1024, ld=20 * 1024, dt=F16) == q.QKNORM_E_UNSUPPORTED
-    assert ph(lib, D=48, ld=20 * 48, dt=F16) == q.QKNORM_E_UNSUPPORTED
-    assert ph(lib, D=32, ld=20 * 32, dt=F8) == q.QKNORM_E_UNSUPPORTED        # 32 B heads
     assert ph(lib, D=2048, ld=20 * 2048, dt=F8) == q.QKNORM_E_UNSUPPORTED
+    # one 16-byte head per 32 MiB row: a trip of 128 heads would span 4 GiB
+    assert ph(lib, D=8, hq=1, hkv=0, ld=1 << 24, dt=BF16, T=0) == q.QKNORM_E_UNSUPPORTED
+    assert ph(lib, D=8, hq=1, hkv=0, ld=1 << 20, dt=BF16, T=0) == q.QKNORM_OK
     assert lw(lib, R=2048, wq=4096 * 8, wk=2048 * 8, ld=6144 * 8) == q.QKNORM_E_UNSUPPORTED
     assert ap(lib, n=4096) == q.QKNORM_E_UNSUPPORTED
     # rows are addressed with 32-bit offsets: pitch above 64 MiB is refused

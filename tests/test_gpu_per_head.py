@@ -74,6 +74,41 @@ def test_ragged_head_counts(dtype, T, hq, hkv):
     run_per_head(p)
 
 
+# head widths that are not a power of two, and the smallest ones (16 and 32
+# bytes): in each dtype, through the lane groups that leave lanes idle
+ODD_WIDTHS = [(synth.F32, 4), (synth.F32, 12), (synth.F32, 20), (synth.F32, 100), (synth.F32, 252),
+              (synth.BF16, 8), (synth.BF16, 16), (synth.BF16, 24), (synth.BF16, 40),
+              (synth.BF16, 48), (synth.BF16, 80), (synth.BF16, 96), (synth.BF16, 112),
+              (synth.BF16, 136), (synth.BF16, 192), (synth.BF16, 320), (synth.BF16, 504),
+              (synth.F16, 8), (synth.F16, 96), (synth.F16, 200),
+              (synth.F8, 16), (synth.F8, 32), (synth.F8, 48), (synth.F8, 80), (synth.F8, 96),
+              (synth.F8, 112), (synth.F8, 144), (synth.F8, 1008)]
+
+
+@pytest.mark.parametrize("dtype,D", ODD_WIDTHS, ids=[f"{synth.DTYPE_NAMES[d]}-D{D}" for d, D in ODD_WIDTHS])
+def test_head_widths_any_multiple_of_16_bytes(dtype, D):
+    # fused rows with padding (row-wise kernel) and a ragged token count
+    pad = 16 // synth.esize(dtype)
+    p = synth.per_head_problem(f"odd_D{D}", 25, dtype, 53, 5, 3, D, ld=(5 + 6) * D + pad,
+                               token_scale=(0.1, 10.0))
+    run_per_head(p)
+    # the same heads packed back to back (a standalone [T, H, D] tensor)
+    p = synth.per_head_problem(f"odd_packed_D{D}", 26, dtype, 37, 7, 0, D)
+    run_per_head(p)
+
+
+@pytest.mark.parametrize("dtype", ALL_DTYPES)
+@pytest.mark.parametrize("hidden", [16, 32, 48, 64, 80, 96, 112, 128])
+def test_plain_rmsnorm_small_hidden(dtype, hidden):
+    # a plain RMSNorm over [T, hidden] rows with hidden <= 128 (the sizes the
+    # PR routes to the head-sized kernel): one head per row
+    if (hidden * synth.esize(dtype)) % 16:
+        pytest.skip("row not a multiple of 16 bytes")
+    p = synth.per_head_problem(f"rms_h{hidden}", 27, dtype, 1001, 1, 0, hidden,
+                               token_scale=(0.5, 2.0))
+    run_per_head(p)
+
+
 def test_t0_is_a_noop():
     x = torch.randn(0, 6144, device="cuda").to(torch.bfloat16)
     g = torch.ones(128, device="cuda", dtype=torch.bfloat16)
