@@ -86,60 +86,79 @@ def abi_version() -> int:
 
 # ----------------------------------------------------------------- marshal --
 
-def _dtype_code(t) -> int:
+# Everything below runs on every call, so it sticks to cheap tensor
+# attributes (shape, stride, dtype, device index) and the raw stream handle.
+
+_CODES = None           # torch dtype -> (dtype code, gamma dtype)
+_raw_stream = None      # device index -> current hipStream_t as an int
+
+
+def _torch_tables():
+    global _CODES, _raw_stream
     import torch
-    if t.dtype == torch.float32:
-        return QKNORM_F32
-    if t.dtype == torch.bfloat16:
-        return QKNORM_BF16
-    if t.dtype == torch.float16:
-        return QKNORM_F16
-    if t.dtype == torch.float8_e4m3fn:
-        return QKNORM_FP8_E4M3
-    raise ValueError("QK-Norm supports float32, bfloat16, float16 and float8_e4m3fn tensors, "
-                     f"not {t.dtype}")
+    _CODES = {torch.float32: (QKNORM_F32, torch.float32),
+              torch.bfloat16: (QKNORM_BF16, torch.bfloat16),
+              torch.float16: (QKNORM_F16, torch.float16),
+              torch.float8_e4m3fn: (QKNORM_FP8_E4M3, torch.bfloat16)}
+    raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+    _raw_stream = raw if raw is not None else (lambda i: torch.cuda.current_stream(i).cuda_stream)
+
+
+def _dtype_code(t) -> int:
+    if _CODES is None:
+        _torch_tables()
+    try:
+        return _CODES[t.dtype][0]
+    except KeyError:
+        raise ValueError("QK-Norm supports float32, bfloat16, float16 and float8_e4m3fn tensors, "
+                         f"not {t.dtype}") from None
 
 
 def _rows(qkv):
-    """(T, ld) of a [T, ...] tensor whose rows are packed."""
+    """(T, ld, device index) of a [T, ...] GPU tensor whose rows are packed."""
     if not qkv.is_cuda:
         raise ValueError("qkv must be a GPU tensor (the library has no CPU path)")
-    if qkv.dim() < 2:
+    shape, stride = qkv.shape, qkv.stride()
+    if len(shape) < 2:
         raise ValueError("qkv must have a leading token dimension and at least one more")
-    T = qkv.shape[0]
-    row = qkv[0] if T > 0 else qkv.new_empty(qkv.shape[1:])
-    if T > 0 and not row.is_contiguous():
-        raise ValueError("each qkv row must be contiguous")
-    ld = qkv.stride(0) if T > 1 else max(qkv.stride(0), row.numel())
-    return T, ld, row.numel()
+    T = shape[0]
+    row = 1                      # elements per row, and the check that they are packed
+    for n, st in zip(reversed(shape[1:]), reversed(stride[1:])):
+        if T > 0 and n != 1 and st != row:
+            raise ValueError("each qkv row must be contiguous")
+        row *= n
+    ld = stride[0] if T > 1 else max(stride[0], row)
+    return T, ld, qkv.get_device()
 
 
-def _ptr(t, dev=None):
+def _ptr(t, dev):
     if t is None:
         return None
     if not t.is_cuda:
         raise ValueError("all tensors must be on the GPU")
-    if dev is not None and t.device != dev:
+    if t.get_device() != dev:
         raise ValueError("all tensors must be on the same GPU")
     return t.data_ptr()
 
 
-def _gamma(g, qkv):
-    import torch
+def _gamma(g, qkv, dev):
     if g is None:
         return None
-    want = torch.bfloat16 if qkv.dtype == torch.float8_e4m3fn else qkv.dtype
+    if _CODES is None:
+        _torch_tables()
+    want = _CODES[qkv.dtype][1] if qkv.dtype in _CODES else qkv.dtype
     if g.dtype != want:
         raise ValueError(f"gamma must be {want} for {qkv.dtype} activations")
     if not g.is_contiguous():
         raise ValueError("gamma must be contiguous")
-    return _ptr(g, qkv.device)
+    return _ptr(g, dev)
 
 
 def _stream(stream, dev):
     if stream is None:
-        import torch
-        return torch.cuda.current_stream(dev).cuda_stream
+        if _raw_stream is None:
+            _torch_tables()
+        return _raw_stream(dev)
     return getattr(stream, "cuda_stream", stream)
 
 
@@ -156,39 +175,39 @@ def _raise(rc: int, what: str):
 def qknorm_per_head(qkv, hq: int, hkv: int, head_dim: int, gamma_q, gamma_k=None,
                     eps: float = 1e-6, stream=None) -> None:
     """Per-head RMSNorm of the hq Q heads and hkv K heads of each row, in place."""
-    T, ld, _ = _rows(qkv)
-    rc = load().qknorm_per_head(_ptr(qkv), T, ld, hq, hkv, head_dim, _gamma(gamma_q, qkv),
-                                _gamma(gamma_k, qkv), eps, _dtype_code(qkv),
-                                _stream(stream, qkv.device))
+    T, ld, dev = _rows(qkv)
+    rc = (_lib or load()).qknorm_per_head(qkv.data_ptr(), T, ld, hq, hkv, head_dim,
+                                          _gamma(gamma_q, qkv, dev), _gamma(gamma_k, qkv, dev),
+                                          eps, _dtype_code(qkv), _stream(stream, dev))
     _raise(rc, "qknorm_per_head")
 
 
 def qknorm_layerwise(qkv, wq: int, wk: int, gamma_q, gamma_k=None, eps: float = 1e-6,
                      nshards: int = 1, stream=None) -> None:
     """Layerwise RMSNorm over the whole Q and K widths via nshards partials, in place."""
-    T, ld, _ = _rows(qkv)
-    rc = load().qknorm_layerwise(_ptr(qkv), T, ld, wq, wk, _gamma(gamma_q, qkv),
-                                 _gamma(gamma_k, qkv), eps, nshards, _dtype_code(qkv),
-                                 _stream(stream, qkv.device))
+    T, ld, dev = _rows(qkv)
+    rc = (_lib or load()).qknorm_layerwise(qkv.data_ptr(), T, ld, wq, wk, _gamma(gamma_q, qkv, dev),
+                                           _gamma(gamma_k, qkv, dev), eps, nshards,
+                                           _dtype_code(qkv), _stream(stream, dev))
     _raise(rc, "qknorm_layerwise")
 
 
-def _partials(p, qkv):
+def _partials(p, dev):
     import torch
     if p is None:
         return None
     if p.dtype != torch.float32 or not p.is_contiguous():
         raise ValueError("partials must be contiguous float32 [nshards, T]")
-    return _ptr(p, qkv.device)
+    return _ptr(p, dev)
 
 
 def qknorm_partial_sumsq(qkv, wq: int, wk: int, nshards: int, part_q, part_k,
                          stream=None) -> None:
     """Shard partial sums of squares into part_q / part_k, float32 [nshards, T]."""
-    T, ld, _ = _rows(qkv)
-    rc = load().qknorm_partial_sumsq(_ptr(qkv), T, ld, wq, wk, nshards, _partials(part_q, qkv),
-                                     _partials(part_k, qkv), _dtype_code(qkv),
-                                     _stream(stream, qkv.device))
+    T, ld, dev = _rows(qkv)
+    rc = (_lib or load()).qknorm_partial_sumsq(qkv.data_ptr(), T, ld, wq, wk, nshards,
+                                               _partials(part_q, dev), _partials(part_k, dev),
+                                               _dtype_code(qkv), _stream(stream, dev))
     _raise(rc, "qknorm_partial_sumsq")
 
 
@@ -196,14 +215,15 @@ def qknorm_apply_scalar(qkv, wq: int, wk: int, part_q, part_k, norm_wq: int, nor
                         gamma_q, gamma_k=None, eps: float = 1e-6, nparts: int | None = None,
                         stream=None) -> None:
     """Combine nparts partials per token and apply, in place."""
-    T, ld, _ = _rows(qkv)
+    T, ld, dev = _rows(qkv)
     if nparts is None:
         ref = part_q if part_q is not None else part_k
         nparts = ref.shape[0] if ref is not None else 1
-    rc = load().qknorm_apply_scalar(_ptr(qkv), T, ld, wq, wk, _partials(part_q, qkv),
-                                    _partials(part_k, qkv), nparts, norm_wq, norm_wk,
-                                    _gamma(gamma_q, qkv), _gamma(gamma_k, qkv), eps,
-                                    _dtype_code(qkv), _stream(stream, qkv.device))
+    rc = (_lib or load()).qknorm_apply_scalar(qkv.data_ptr(), T, ld, wq, wk,
+                                              _partials(part_q, dev), _partials(part_k, dev),
+                                              nparts, norm_wq, norm_wk, _gamma(gamma_q, qkv, dev),
+                                              _gamma(gamma_k, qkv, dev), eps, _dtype_code(qkv),
+                                              _stream(stream, dev))
     _raise(rc, "qknorm_apply_scalar")
 
 
