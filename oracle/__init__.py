@@ -193,3 +193,40 @@ def decode(a, dtype):
         return np.ascontiguousarray(a, dtype=np.uint16).view(np.float16).astype(np.float64)
     with np.errstate(invalid="ignore"):
         return (a.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+
+
+def qkv_proj_per_head(x, w, dtype, hq, hkv, head_dim, gamma_q, gamma_k, eps, norm=True):
+    """The QKV projection followed by per-head QK-Norm, in fp64.
+
+    x is [T, K] and w is [N, K] (the projection's weight, one row per output
+    column), N = (hq + 2*hkv) * head_dim, both in the storage of `dtype`.
+    acc = x @ w^T is taken with numpy's fp64 matmul of the exactly decoded
+    values; each Q head (columns h*D, gamma_q) and each K head (columns
+    hq*D + h*D, gamma_k) of every row is then normalised over its D values,
+    y = acc * gamma / sqrt(sum(acc^2)/D + eps), and the V columns are acc
+    itself.  norm=False gives the plain projection.  Returns (y, y rounded
+    once to dtype).
+
+    The normalisation is the per-head RMSNorm of per_head() (sglang PR
+    "Add turbomind_rms_norm ...", #13189: an RMSNorm over the head dimension),
+    applied to the projection's output before any rounding: the fused form
+    of the QKV projection ("Explain combined QKV projection ..." lesson,
+    "With GQA": one matmul, split into Q, K and V heads).
+    """
+    xd = decode(x, dtype)
+    wd = decode(w, dtype)
+    T, N = xd.shape[0], wd.shape[0]
+    D = head_dim
+    if N != (hq + 2 * hkv) * D:
+        raise ValueError("w must have (hq + 2*hkv) * head_dim rows")
+    acc = xd @ wd.T
+    y = acc.copy()
+    if norm:
+        gd = gamma_dtype(dtype)
+        for c0, nh, g in ((0, hq, gamma_q), (hq * D, hkv, gamma_k)):
+            if nh == 0:
+                continue
+            seg = acc[:, c0:c0 + nh * D].reshape(T, nh, D)
+            ms = np.sum(seg * seg, axis=-1, keepdims=True) / D
+            y[:, c0:c0 + nh * D] = (seg * decode(g, gd) / np.sqrt(ms + eps)).reshape(T, nh * D)
+    return y, round_to(y, dtype)

@@ -538,7 +538,98 @@ def check_pass_through():
         assert np.array_equal(yr[:, c:].view(np.uint8), np.ascontiguousarray(x[:, c:]).view(np.uint8))
 
 
+# ------------------------------------------------ projection + per-head --
+
+def _proj_case(seed, dtype, T, K, hq, hkv, D, scale=1.0):
+    x = synth.to_dtype(synth.normal(seed, 0, T * K).reshape(T, K) * scale, dtype)
+    N = (hq + 2 * hkv) * D
+    w = synth.to_dtype(synth.normal(seed + 1, 0, N * K).reshape(N, K) / math.sqrt(K), dtype)
+    return x, w, _gamma(seed, D, dtype, 3), _gamma(seed, D, dtype, 4)
+
+
+def check_proj_selection():
+    """A weight that selects columns of x makes the projection exact, so the
+    fused result must be the per-head oracle applied to those columns."""
+    rng = np.random.default_rng(5)
+    for dtype in DTYPES:
+        for (hq, hkv, D) in ((4, 2, 16), (3, 1, 32), (2, 0, 8)):
+            N = (hq + 2 * hkv) * D
+            K = N + 24
+            T = 5
+            x = _rng_problem(400 + D, T, K, dtype, scale=2.0)
+            perm = rng.permutation(K)[:N]
+            wd = np.zeros((N, K))
+            wd[np.arange(N), perm] = 1.0
+            w = synth.to_dtype(wd, dtype)
+            gq, gk = _gamma(401, D, dtype, 3), _gamma(401, D, dtype, 4)
+            eps = synth.eps_f32(1e-6)
+            y, yr = oracle.qkv_proj_per_head(x, w, dtype, hq, hkv, D, gq, gk if hkv else None, eps)
+            xs = np.ascontiguousarray(x[:, perm])
+            ref, refr = oracle.per_head(xs, dtype, hq, hkv, D, gq, gk if hkv else None, eps)
+            assert np.all(np.abs(y - ref) <= 1e-14 * np.abs(ref)), f"selection {dtype} D={D}"
+            assert np.array_equal(yr, refr), f"selection rounded {dtype} D={D}"
+
+
+def check_proj_brute_force():
+    """Exact rational sums of the products, then the exact normalisation."""
+    for dtype in DTYPES:
+        hq, hkv, D, K, T = 1, 1, 4, 16, 3
+        x, w, gq, gk = _proj_case(410 + dtype, dtype, T, K, hq, hkv, D, scale=1.5)
+        eps = synth.eps_f32(1e-6)
+        y, _ = oracle.qkv_proj_per_head(x, w, dtype, hq, hkv, D, gq, gk, eps)
+        N = w.shape[0]
+        for t in range(T):
+            xe = _exact(x[t], dtype)
+            acc = [sum((a * b for a, b in zip(xe, _exact(w[n], dtype))), Fraction(0)) for n in range(N)]
+            for (c0, g) in ((0, gq), (D, gk)):
+                seg = acc[c0:c0 + D]
+                ex = _exact_group(seg, _exact(g, GD(dtype)), sum((v * v for v in seg), Fraction(0)), D, eps)
+                for j in range(D):
+                    assert _ulps(float(y[t, c0 + j]), ex[j]) <= 4 * K, f"proj brute force {dtype}"
+            for n in range((hq + hkv) * D, N):                      # V: the projection itself
+                assert abs(Fraction(float(y[t, n])) - acc[n]) <= Fraction(K, 2 ** 53) * \
+                    sum((abs(a * b) for a, b in zip(xe, _exact(w[n], dtype))), Fraction(0)), "proj V"
+
+
+def check_proj_plain_and_unit_rms():
+    for dtype in DTYPES:
+        hq, hkv, D = 3, 2, 32
+        x, w, gq, gk = _proj_case(420 + dtype, dtype, 6, 96, hq, hkv, D)
+        acc = oracle.decode(x, dtype) @ oracle.decode(w, dtype).T
+        p, _ = oracle.qkv_proj_per_head(x, w, dtype, hq, hkv, D, gq, gk, 0.0, norm=False)
+        assert np.array_equal(p, acc), "plain projection"
+        ones = synth.to_dtype(np.ones(D), GD(dtype))
+        y, _ = oracle.qkv_proj_per_head(x, w, dtype, hq, hkv, D, ones, ones, 0.0)
+        assert np.array_equal(y[:, (hq + hkv) * D:], acc[:, (hq + hkv) * D:]), "V columns untouched"
+        for h in range(hq + hkv):
+            m = np.mean(y[:, h * D:(h + 1) * D] ** 2, axis=1)
+            assert np.all(np.abs(m - 1.0) <= 1e-14), "unit RMS per head"
+        # K heads use gamma_k: with gamma_q = 1 and gamma_k = 2 the K heads double
+        twos = synth.to_dtype(np.full(D, 2.0), GD(dtype))
+        y2, _ = oracle.qkv_proj_per_head(x, w, dtype, hq, hkv, D, ones, twos, 0.0)
+        assert np.array_equal(y2[:, :hq * D], y[:, :hq * D])
+        assert np.array_equal(y2[:, hq * D:(hq + hkv) * D], 2 * y[:, hq * D:(hq + hkv) * D])
+
+
+def check_proj_head_scale():
+    """Scaling the weight rows of one head by 2^k leaves that head's output
+    unchanged (eps = 0) and scales nothing else."""
+    for dtype in (F32, BF16, F16):
+        hq, hkv, D = 2, 1, 16
+        x, w, gq, gk = _proj_case(430 + dtype, dtype, 4, 64, hq, hkv, D)
+        y, _ = oracle.qkv_proj_per_head(x, w, dtype, hq, hkv, D, gq, gk, 0.0)
+        wd = oracle.decode(w, dtype)
+        for h, k in ((0, 3), (2, 1)):   # upward: no value drops below the normal range
+            ws = wd.copy()
+            ws[h * D:(h + 1) * D] *= 2.0 ** k
+            y2, _ = oracle.qkv_proj_per_head(x, synth.to_dtype(ws, dtype), dtype, hq, hkv, D, gq, gk, 0.0)
+            assert np.array_equal(y2, y), f"head {h} scale 2^{k}"
+
+
+PROJ_CHECKS = [check_proj_selection, check_proj_brute_force, check_proj_plain_and_unit_rms,
+               check_proj_head_scale]
+
 ALL_CHECKS = [check_brute_force, check_apply_exact, check_unit_rms, check_eps_identity,
               check_scale_pow2, check_shard_identity, check_closed_form, check_identities,
               check_libraries, check_rounding, check_rounding_f16, check_rounding_e4m3,
-              check_pass_through]
+              check_pass_through] + PROJ_CHECKS
