@@ -159,6 +159,36 @@ int qknorm_apply_scalar(void *qkv, int64_t T, int64_t ld, int64_t wq, int64_t wk
                         int64_t norm_wq, int64_t norm_wk, const void *gamma_q,
                         const void *gamma_k, float eps, int32_t dtype, void *stream);
 
+/*
+ * QKV projection with per-head QK-Norm fused into its epilogue.
+ * qkv[t, n] = sum_k x[t, k] * w[n, k] for n < N = (hq + 2*hkv)*head_dim,
+ * accumulated in fp32; then, unless flags has QKNORM_PROJ_PLAIN, each Q head
+ * (columns h*head_dim, gamma_q) and each K head (columns hq*head_dim +
+ * h*head_dim, gamma_k) of every row is normalised as by qknorm_per_head, but
+ * on the fp32 accumulator before any rounding; V columns are stored as
+ * computed.  One pass replaces a projection that writes qkv and a norm that
+ * reads and rewrites it.
+ * (Lesson "Explain combined QKV projection and why it's faster than three
+ *  separate projections?", section "With GQA": one projection whose output is
+ *  split into Q, K and V heads; sglang PR #13189: the QK norm is an RMSNorm
+ *  over the head dimension.)
+ *
+ * x   [T, hidden], row pitch ldx (elements); w [N, hidden], the projection
+ *     weight with one row per output column, pitch ldw; qkv [T, ld] output,
+ *     columns >= N not written.  bf16 only (dtype QKNORM_BF16; others give
+ *     QKNORM_E_UNSUPPORTED).  flags: 0, or QKNORM_PROJ_PLAIN for the plain
+ *     projection (gamma and eps unused).
+ * Requires: hidden a multiple of 64 and head_dim 64 or 128 (else
+ * QKNORM_E_UNSUPPORTED); ldx, ldw >= hidden and ld >= N; x, w, qkv and gamma
+ * 16-byte aligned, pitches*2 multiples of 16 bytes; 128 rows of x or of w
+ * below 2 GiB.  x, w and gamma must not overlap qkv.
+ */
+#define QKNORM_PROJ_PLAIN 1
+int qknorm_qkv_proj_per_head(const void *x, int64_t ldx, const void *w, int64_t ldw, void *qkv,
+                             int64_t ld, int64_t T, int64_t hidden, int32_t hq, int32_t hkv,
+                             int32_t head_dim, const void *gamma_q, const void *gamma_k,
+                             float eps, int32_t flags, int32_t dtype, void *stream);
+
 /* Static description of a return code; never NULL. */
 const char *qknorm_strerror(int code);
 

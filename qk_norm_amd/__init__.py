@@ -40,8 +40,11 @@ QKNORM_E_UNSUPPORTED = -5
 QKNORM_E_EPS = -6
 QKNORM_E_HIP = -7
 
+QKNORM_PROJ_PLAIN = 1
+
 EXPORTED = ("qknorm_per_head", "qknorm_layerwise", "qknorm_partial_sumsq",
-            "qknorm_apply_scalar", "qknorm_strerror", "qknorm_abi_version")
+            "qknorm_apply_scalar", "qknorm_qkv_proj_per_head", "qknorm_strerror",
+            "qknorm_abi_version")
 
 _lib = None
 
@@ -66,8 +69,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.qknorm_layerwise.argtypes = [P, I64, I64, I64, I64, P, P, F, I32, I32, P]
     lib.qknorm_partial_sumsq.argtypes = [P, I64, I64, I64, I64, I32, P, P, I32, P]
     lib.qknorm_apply_scalar.argtypes = [P, I64, I64, I64, I64, P, P, I32, I64, I64, P, P, F, I32, P]
+    lib.qknorm_qkv_proj_per_head.argtypes = [P, I64, P, I64, P, I64, I64, I64, I32, I32, I32, P, P,
+                                             F, I32, I32, P]
     for name in ("qknorm_per_head", "qknorm_layerwise", "qknorm_partial_sumsq",
-                 "qknorm_apply_scalar", "qknorm_abi_version"):
+                 "qknorm_apply_scalar", "qknorm_qkv_proj_per_head", "qknorm_abi_version"):
         getattr(lib, name).restype = I32
     lib.qknorm_strerror.argtypes = [ctypes.c_int]
     lib.qknorm_strerror.restype = ctypes.c_char_p
@@ -227,6 +232,38 @@ def qknorm_apply_scalar(qkv, wq: int, wk: int, part_q, part_k, norm_wq: int, nor
     _raise(rc, "qknorm_apply_scalar")
 
 
-__all__ = ["qknorm_per_head", "qknorm_layerwise", "qknorm_partial_sumsq", "qknorm_apply_scalar",
+def _matrix(t, dev, what):
+    """(pointer, row pitch) of a 2-d GPU tensor with contiguous rows."""
+    if t.dim() != 2 or (t.shape[1] > 1 and t.stride(1) != 1):
+        raise ValueError(f"{what} must be a 2-d tensor with contiguous rows")
+    return _ptr(t, dev), t.stride(0) if t.shape[0] > 1 else max(t.stride(0), t.shape[1])
+
+
+def qknorm_qkv_proj_per_head(x, w, qkv, hq: int, hkv: int, head_dim: int, gamma_q=None,
+                             gamma_k=None, eps: float = 1e-6, plain: bool = False,
+                             stream=None) -> None:
+    """qkv[:, :N] = x @ w.T with each Q and K head RMS-normalised in the epilogue.
+
+    x [T, hidden], w [N, hidden] (N = (hq + 2*hkv) * head_dim) and qkv [T, >= N],
+    all bfloat16 on one GPU; plain=True gives the projection alone.
+    """
+    if not qkv.is_cuda:
+        raise ValueError("qkv must be a GPU tensor (the library has no CPU path)")
+    dev = qkv.get_device()
+    xp, ldx = _matrix(x, dev, "x")
+    wp, ldw = _matrix(w, dev, "w")
+    op, ld = _matrix(qkv, dev, "qkv")
+    if x.dtype != qkv.dtype or w.dtype != qkv.dtype:
+        raise ValueError("x, w and qkv must share the dtype")
+    if x.shape[0] != qkv.shape[0] or x.shape[1] != w.shape[1]:
+        raise ValueError("x [T, hidden], w [N, hidden] and qkv [T, >= N] do not match")
+    rc = (_lib or load()).qknorm_qkv_proj_per_head(
+        xp, ldx, wp, ldw, op, ld, x.shape[0], x.shape[1], hq, hkv, head_dim,
+        None if plain else _gamma(gamma_q, qkv, dev), None if plain else _gamma(gamma_k, qkv, dev),
+        eps, QKNORM_PROJ_PLAIN if plain else 0, _dtype_code(qkv), _stream(stream, dev))
+    _raise(rc, "qknorm_qkv_proj_per_head")
+
+
+__all__ = ["qknorm_per_head", "qknorm_qkv_proj_per_head", "qknorm_layerwise", "qknorm_partial_sumsq", "qknorm_apply_scalar",
            "strerror", "abi_version", "load", "QKNormError", "QKNORM_F32", "QKNORM_BF16", "QKNORM_F16",
            "QKNORM_FP8_E4M3"]

@@ -15,7 +15,8 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
-SOURCES = [os.path.join(CSRC, "qknorm_api.hip"), os.path.join(CSRC, "qknorm_kernels.hip")]
+SOURCES = [os.path.join(CSRC, "qknorm_api.hip"), os.path.join(CSRC, "qknorm_kernels.hip"),
+           os.path.join(CSRC, "qknorm_proj.hip")]
 LIB = os.path.join(HERE, "libqknorm.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

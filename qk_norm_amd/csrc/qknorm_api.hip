@@ -189,3 +189,31 @@ int qknorm_apply_scalar(void* qkv, int64_t T, int64_t ld, int64_t wq, int64_t wk
 }
 
 }  // extern "C"
+
+int qknorm_qkv_proj_per_head(const void* x, int64_t ldx, const void* w, int64_t ldw, void* qkv,
+                             int64_t ld, int64_t T, int64_t hidden, int32_t hq, int32_t hkv,
+                             int32_t head_dim, const void* gamma_q, const void* gamma_k, float eps,
+                             int32_t flags, int32_t dtype, void* stream) {
+  int rc = check_common(dtype, eps, T, ld);
+  if (rc) return rc;
+  if (dtype != QKNORM_BF16) return QKNORM_E_UNSUPPORTED;
+  if ((flags & ~QKNORM_PROJ_PLAIN) != 0) return QKNORM_E_UNSUPPORTED;
+  if (hidden <= 0 || hq < 0 || hkv < 0 || head_dim <= 0 || ldx < hidden || ldw < hidden)
+    return QKNORM_E_SHAPE;
+  const int64_t N = ((int64_t)hq + 2 * (int64_t)hkv) * head_dim;
+  if (ld < N) return QKNORM_E_SHAPE;
+  const bool norm = (flags & QKNORM_PROJ_PLAIN) == 0;
+  const bool touched = T > 0 && N > 0;
+  if (touched && (x == nullptr || w == nullptr || qkv == nullptr)) return QKNORM_E_NULLPTR;
+  if (norm && (rc = check_gamma(gamma_q, hq, T))) return rc;
+  if (norm && (rc = check_gamma(gamma_k, hkv, T))) return rc;
+  if (touched && (!aligned16(x) || !aligned16(w) || !aligned16(qkv))) return QKNORM_E_ALIGN;
+  if ((ldx * 2) % 16 != 0 || (ldw * 2) % 16 != 0 || (ld * 2) % 16 != 0) return QKNORM_E_ALIGN;
+  if (ld * 2 > kMaxPitchBytes || T * (ld + 1) > (INT64_C(1) << 46) || N >= (INT64_C(1) << 24))
+    return QKNORM_E_UNSUPPORTED;
+  qknorm::ProjArgs a{x, ldx, w, ldw, qkv, ld, T, hidden, hq, hkv, head_dim, gamma_q, gamma_k,
+                     eps, flags};
+  if (!qknorm::proj_shape_ok(a)) return QKNORM_E_UNSUPPORTED;
+  if (!touched) return QKNORM_OK;
+  return finish(qknorm::launch_qkv_proj(a, static_cast<hipStream_t>(stream)));
+}

@@ -48,12 +48,30 @@ struct ApplyArgs {
   int32_t dtype;
 };
 
-// `cus` is the compute-unit count of the current device (grid sizing).
+struct ProjArgs {
+  const void* x;
+  int64_t ldx;
+  const void* w;
+  int64_t ldw;
+  void* qkv;
+  int64_t ld, T, hidden;
+  int32_t hq, hkv, head_dim;
+  const void* gamma_q;
+  const void* gamma_k;
+  float eps;
+  int32_t flags;
+};
+
 // Whether every per-head trip's buffer span stays below 2^31 bytes.
 bool per_head_span_ok(const PerHeadArgs& a);
+// Whether the projection kernel takes this shape (tile offsets, K step, head_dim).
+bool proj_shape_ok(const ProjArgs& a);
+
+// `cus` is the compute-unit count of the current device (grid sizing).
 hipError_t launch_per_head(const PerHeadArgs& a, hipStream_t s, int cus);
 hipError_t launch_layerwise(const LayerwiseArgs& a, hipStream_t s, int cus);
 hipError_t launch_partial_sumsq(const PartialArgs& a, hipStream_t s, int cus);
 hipError_t launch_apply_scalar(const ApplyArgs& a, hipStream_t s, int cus);
+hipError_t launch_qkv_proj(const ProjArgs& a, hipStream_t s);
 
 }  // namespace qknorm

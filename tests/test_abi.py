@@ -204,3 +204,32 @@ def test_binding_refuses_cpu_tensors():
 def test_missing_library_fails_loudly(tmp_path):
     with pytest.raises(RuntimeError, match="not built"):
         q.load(str(tmp_path / "nope.so"))
+
+
+def pj(lib, x=A16, ldx=256, w=A16, ldw=256, out=A16, ld=768, T=4, hidden=256, hq=2, hkv=2,
+       D=128, gq=A16, gk=A16, eps=1e-6, flags=0, dt=BF16):
+    return lib.qknorm_qkv_proj_per_head(x, ldx, w, ldw, out, ld, T, hidden, hq, hkv, D, gq, gk,
+                                        eps, flags, dt, None)
+
+
+def test_projection_validation(lib):
+    # everything valid with T = 0: validated, nothing launched
+    assert pj(lib, T=0) == q.QKNORM_OK
+    assert pj(lib, T=0, D=64, ld=384) == q.QKNORM_OK
+    assert pj(lib, T=0, flags=q.QKNORM_PROJ_PLAIN, gq=None, gk=None) == q.QKNORM_OK
+    assert pj(lib, dt=F32) == q.QKNORM_E_UNSUPPORTED          # bf16 only
+    assert pj(lib, dt=7) == q.QKNORM_E_DTYPE
+    assert pj(lib, flags=2) == q.QKNORM_E_UNSUPPORTED
+    assert pj(lib, hidden=96, ldx=96, ldw=96) == q.QKNORM_E_UNSUPPORTED     # K step of 64
+    assert pj(lib, D=96, ld=576) == q.QKNORM_E_UNSUPPORTED                 # head_dim 64 or 128
+    assert pj(lib, ld=767) == q.QKNORM_E_SHAPE                             # ld < N = 768
+    assert pj(lib, ldx=128) == q.QKNORM_E_SHAPE                            # ldx < hidden
+    assert pj(lib, hidden=0) == q.QKNORM_E_SHAPE
+    assert pj(lib, hq=-1) == q.QKNORM_E_SHAPE
+    assert pj(lib, x=None) == q.QKNORM_E_NULLPTR
+    assert pj(lib, out=None) == q.QKNORM_E_NULLPTR
+    assert pj(lib, gk=None) == q.QKNORM_E_NULLPTR
+    assert pj(lib, w=A16 + 2) == q.QKNORM_E_ALIGN
+    assert pj(lib, ld=772) == q.QKNORM_E_ALIGN                             # 1544-byte pitch
+    assert pj(lib, eps=-1.0) == q.QKNORM_E_EPS
+    assert pj(lib, ldx=(1 << 23) + 8, T=0) == q.QKNORM_E_UNSUPPORTED       # 128 rows over 2 GiB

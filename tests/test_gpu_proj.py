@@ -1,0 +1,190 @@
+"""QKV projection with per-head QK-Norm in its epilogue: the HIP kernel
+against the fp64 oracle, through the C ABI.
+
+Tolerance.  The kernel accumulates the K products of each output in fp32
+(MFMA, order fixed by the hardware), the oracle in fp64.  The fp32 sum is
+within K * 2^-24 * A of the exact one, A = sum_k |x_k w_k| of that output.
+  V (and plain) columns: |g - o| <= 8e-3 |o| + 2 K 2^-24 A
+  normalised heads: that error passes through y = acc * gamma / rms(acc):
+      |g - o| <= 8e-3 |o| + 2 K 2^-24 (|gamma| A / rms + |o| ||A||_2 / ||acc||_2)
+  (8e-3 is one bf16 ulp, as for the norm alone; the factor 2 covers the
+  norm's own fp32 arithmetic, which is orders of magnitude smaller.)
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import qk_norm_amd as q
+from qk_norm_amd import synth
+from gpu_util import GUARD_BYTES, Guarded, assert_bytes_equal, gamma_to_device, host_to_device
+
+pytestmark = pytest.mark.gpu
+U = 2.0 ** -24
+BF16 = synth.BF16
+
+
+def make(seed, T, hidden, hq, hkv, D, token_scale=(0.25, 4.0)):
+    """x ~ N(0,1) times a per-token scale; w ~ N(0, 1/hidden) (unit-variance
+    outputs); gamma ~ U(0.5, 1.5)."""
+    N = (hq + 2 * hkv) * D
+    x = synth.make_x(seed, T, hidden, BF16, token_scale=token_scale)
+    w = synth.to_dtype(synth.normal(seed + 7, 0, N * hidden).reshape(N, hidden) / np.sqrt(hidden), BF16)
+    return x, w, synth.make_gamma(seed, 3, D, BF16), synth.make_gamma(seed, 4, D, BF16)
+
+
+def tolerance(x, w, y64, gq, gk, hq, hkv, D, norm=True):
+    """Per-element bound (see the module docstring)."""
+    xd, wd = np.abs(oracle.decode(x, BF16)), np.abs(oracle.decode(w, BF16))
+    A = xd @ wd.T
+    K = x.shape[1]
+    acc = oracle.decode(x, BF16) @ oracle.decode(w, BF16).T
+    tol = 8e-3 * np.abs(y64) + 2 * K * U * A
+    if norm:
+        T = x.shape[0]
+        for c0, nh, g in ((0, hq, gq), (hq * D, hkv, gk)):
+            if nh == 0:
+                continue
+            sl = slice(c0, c0 + nh * D)
+            a = acc[:, sl].reshape(T, nh, D)
+            rms = np.sqrt(np.mean(a * a, axis=-1, keepdims=True))
+            An = np.linalg.norm(A[:, sl].reshape(T, nh, D), axis=-1, keepdims=True)
+            an = np.linalg.norm(a, axis=-1, keepdims=True)
+            gd = np.abs(oracle.decode(g, BF16))
+            yo = np.abs(y64[:, sl].reshape(T, nh, D))
+            extra = 2 * K * U * (gd * A[:, sl].reshape(T, nh, D) / rms + yo * An / an)
+            tol[:, sl] = 8e-3 * yo.reshape(T, nh * D) + extra.reshape(T, nh * D)
+    return tol
+
+
+def run_proj(x, w, hq, hkv, D, gq, gk, eps, ld=None, plain=False, label=""):
+    T, hidden = x.shape
+    N = w.shape[0]
+    ld = ld or N
+    print(f"[proj] {label} T={T} hidden={hidden} hq={hq} hkv={hkv} D={D} ld={ld} plain={plain}",
+          flush=True)
+    xt, wt = host_to_device(x, BF16), host_to_device(w, BF16)
+    fill = np.full((T, ld), 0x7FC0, dtype=np.uint16)            # NaN: must be overwritten or kept
+    out = Guarded(fill, BF16)
+    q.qknorm_qkv_proj_per_head(xt, wt, out.t, hq, hkv, D, gamma_to_device(gq, BF16),
+                               gamma_to_device(gk, BF16) if hkv else None, eps, plain=plain)
+    torch.cuda.synchronize()
+    got = out.host()
+    assert out.guards_intact(), "write outside the output"
+    assert_bytes_equal(got[:, N:], fill[:, N:], f"{label}: columns past N")
+    return got[:, :N]
+
+
+def check(x, w, hq, hkv, D, gq, gk, eps, got, plain=False, label=""):
+    y64, yr = oracle.qkv_proj_per_head(x, w, BF16, hq, hkv, D, gq, gk if hkv else None, eps,
+                                       norm=not plain)
+    g = oracle.decode(got, BF16)
+    tol = tolerance(x, w, y64, gq, gk, hq, hkv, D, norm=not plain)
+    bad = ~(np.abs(g - y64) <= tol)
+    if bad.any():
+        i, j = np.argwhere(bad)[0]
+        raise AssertionError(f"{label}: {int(bad.sum())} elements beyond the bound, e.g. [{i},{j}] "
+                             f"gpu={g[i, j]!r} oracle={y64[i, j]!r} tol={tol[i, j]!r}")
+    exact = np.mean(got == yr)
+    assert exact > 0.97, f"{label}: only {exact:.4f} of outputs equal the oracle's rounding"
+    return exact
+
+
+@pytest.mark.parametrize("T,hidden,hq,hkv,D", [
+    (1, 64, 2, 1, 128),          # one token, one K step
+    (100, 192, 4, 2, 128),       # ragged rows, three K steps
+    (333, 512, 3, 1, 64),        # D = 64: N = 320, a half tile of columns
+    (130, 256, 32, 8, 128),      # the Qwen3-8B head layout, two row tiles
+    (64, 128, 0, 2, 64),         # K heads only
+    (48, 64, 5, 0, 64),          # no K or V
+])
+def test_fused_projection_against_oracle(T, hidden, hq, hkv, D):
+    x, w, gq, gk = make(70 + T, T, hidden, hq, hkv, D)
+    eps = synth.eps_f32(1e-6)
+    got = run_proj(x, w, hq, hkv, D, gq, gk, eps, label="fused")
+    check(x, w, hq, hkv, D, gq, gk, eps, got, label=f"fused T={T} K={hidden}")
+
+
+def test_plain_projection_and_padding():
+    T, hidden, hq, hkv, D = 77, 320, 4, 2, 128
+    x, w, gq, gk = make(80, T, hidden, hq, hkv, D)
+    N = w.shape[0]
+    got = run_proj(x, w, hq, hkv, D, gq, gk, 0.0, ld=N + 40, plain=True, label="plain")
+    check(x, w, hq, hkv, D, gq, gk, 0.0, got, plain=True, label="plain")
+    got = run_proj(x, w, hq, hkv, D, gq, gk, synth.eps_f32(1e-6), ld=N + 40, label="fused padded")
+    check(x, w, hq, hkv, D, gq, gk, synth.eps_f32(1e-6), got, label="fused padded")
+
+
+def test_fused_equals_unfused_up_to_the_intermediate_rounding():
+    # projection, then qknorm_per_head on its bf16 output: the fused kernel
+    # skips that rounding, so the two agree to within a bf16 ulp or two
+    T, hidden, hq, hkv, D = 256, 512, 8, 2, 128
+    x, w, gq, gk = make(81, T, hidden, hq, hkv, D)
+    eps = synth.eps_f32(1e-6)
+    fused = run_proj(x, w, hq, hkv, D, gq, gk, eps, label="fused")
+    plain = run_proj(x, w, hq, hkv, D, gq, gk, eps, plain=True, label="plain")
+    t = host_to_device(plain, BF16)
+    q.qknorm_per_head(t, hq, hkv, D, gamma_to_device(gq, BF16), gamma_to_device(gk, BF16), eps)
+    torch.cuda.synchronize()
+    unfused = t.cpu().view(torch.int16).numpy().view(np.uint16)
+    a, b = oracle.decode(fused, BF16), oracle.decode(unfused, BF16)
+    assert np.all(np.abs(a - b) <= 2 * 2.0 ** -7 * np.maximum(np.abs(a), np.abs(b)) + 1e-30)
+    assert np.array_equal(fused[:, (hq + hkv) * D:], unfused[:, (hq + hkv) * D:]), "V identical"
+
+
+def test_deterministic_and_graph_replay():
+    T, hidden, hq, hkv, D = 200, 256, 4, 1, 128
+    x, w, gq, gk = make(82, T, hidden, hq, hkv, D)
+    xt, wt = host_to_device(x, BF16), host_to_device(w, BF16)
+    g1, g2 = gamma_to_device(gq, BF16), gamma_to_device(gk, BF16)
+    out = torch.empty(T, w.shape[0], dtype=torch.bfloat16, device="cuda")
+    q.qknorm_qkv_proj_per_head(xt, wt, out, hq, hkv, D, g1, g2, 1e-6)
+    torch.cuda.synchronize()
+    eager = out.clone()
+    graph = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(graph, stream=s):
+            q.qknorm_qkv_proj_per_head(xt, wt, out, hq, hkv, D, g1, g2, 1e-6)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        out.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), eager.view(torch.int16))
+
+
+def test_full_size_qwen3_8b_prefill_sampled_rows():
+    # [4096, 4096] x [6144, 4096]^T, 32 Q + 8 K + 8 V heads of 128: the full
+    # output is checked on sampled rows (the oracle recomputes only those)
+    T, hidden, hq, hkv, D = 4096, 4096, 32, 8, 128
+    x, w, gq, gk = make(83, T, hidden, hq, hkv, D)
+    eps = synth.eps_f32(1e-6)
+    print(f"[proj] full size T={T} hidden={hidden}", flush=True)
+    xt, wt = host_to_device(x, BF16), host_to_device(w, BF16)
+    out = torch.empty(T, w.shape[0], dtype=torch.bfloat16, device="cuda")
+    q.qknorm_qkv_proj_per_head(xt, wt, out, hq, hkv, D, gamma_to_device(gq, BF16),
+                               gamma_to_device(gk, BF16), eps)
+    torch.cuda.synchronize()
+    got = out.cpu().view(torch.int16).numpy().view(np.uint16)
+    rows = np.unique(np.concatenate([np.random.default_rng(3).choice(T, 40, replace=False),
+                                     [0, 127, 128, T - 1]]))
+    check(x[rows], w, hq, hkv, D, gq, gk, eps, got[rows], label="full size, sampled rows")
+    assert not np.isnan(oracle.decode(got, BF16)).any()
+
+
+def test_rejected_shapes_launch_nothing():
+    x = torch.zeros(4, 96, dtype=torch.bfloat16, device="cuda")       # hidden not a multiple of 64
+    w = torch.zeros(512, 96, dtype=torch.bfloat16, device="cuda")
+    out = torch.zeros(4, 512, dtype=torch.bfloat16, device="cuda")
+    g = torch.ones(128, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(ValueError, match="unsupported"):
+        q.qknorm_qkv_proj_per_head(x, w, out, 2, 1, 128, g, g)
+    x = torch.zeros(4, 128, dtype=torch.bfloat16, device="cuda")
+    w = torch.zeros(4 * 96, 128, dtype=torch.bfloat16, device="cuda")   # head_dim 96
+    with pytest.raises(ValueError, match="unsupported"):
+        q.qknorm_qkv_proj_per_head(x, w, out[:, :384], 2, 1, 96, g[:96], g[:96])
+    torch.cuda.synchronize()
+    assert int(out.view(torch.int16).abs().sum()) == 0
