@@ -225,6 +225,72 @@ def bench_layerwise(q, torch, dev, p, steps, warmup, label="cfg5"):
     return out
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def bench_proj(q, torch, dev, steps, warmup, T=4096, hidden=4096, hq=32, hkv=8, D=128):
+    """QKV projection of a Qwen3-8B-sized layer ([T, 4096] x [6144, 4096]^T,
+    32 Q + 8 K + 8 V heads of 128): fused with per-head QK-Norm, the plain
+    projection (same kernel), torch's mm (hipBLASLt), and mm + qknorm_per_head.
+    x and w stay resident (48 MB of weight is reused call after call, as in
+    serving)."""
+    import numpy as np
+    from qk_norm_amd import synth
+    N = (hq + 2 * hkv) * D
+    x = to_device(synth.make_x(90, T, hidden, synth.BF16, token_scale=(0.25, 4.0)), synth.BF16, torch, dev)
+    w = to_device(synth.to_dtype(synth.normal(91, 0, N * hidden).reshape(N, hidden) / np.sqrt(hidden),
+                                 synth.BF16), synth.BF16, torch, dev)
+    gq = to_device(synth.make_gamma(90, 3, D, synth.BF16), synth.BF16, torch, dev)
+    gk = to_device(synth.make_gamma(90, 4, D, synth.BF16), synth.BF16, torch, dev)
+    out = torch.empty(T, N, dtype=torch.bfloat16, device=dev)
+    out2 = torch.empty(T, N, dtype=torch.bfloat16, device=dev)
+    lib = q.load()
+    stream = torch.cuda.current_stream(dev).cuda_stream
+
+    def proj(flags):
+        def f(_i):
+            rc = lib.qknorm_qkv_proj_per_head(x.data_ptr(), hidden, w.data_ptr(), hidden, out.data_ptr(),
+                                              N, T, hidden, hq, hkv, D, gq.data_ptr(), gk.data_ptr(),
+                                              1e-6, flags, synth.BF16, stream)
+            if rc:
+                raise RuntimeError(q.strerror(rc))
+        return f
+
+    def mm(_i):
+        torch.mm(x, w.t(), out=out2)
+
+    def mm_norm(_i):
+        torch.mm(x, w.t(), out=out2)
+        rc = lib.qknorm_per_head(out2.data_ptr(), T, N, hq, hkv, D, gq.data_ptr(), gk.data_ptr(), 1e-6,
+                                 synth.BF16, stream)
+        if rc:
+            raise RuntimeError(q.strerror(rc))
+
+    flops = 2.0 * T * hidden * N
+    res = {"shape": {"T": T, "hidden": hidden, "N": N, "hq": hq, "hkv": hkv, "head_dim": D},
+           "flops": flops}
+    variants = (("fused_proj_qknorm", proj(0)), ("plain_proj", proj(1)),
+                ("torch_mm", mm), ("torch_mm_then_qknorm", mm_norm))
+    # compute-bound kernels: warm every variant first (clocks), then take the
+    # better of two timed rounds of each
+    for _, fn in variants:
+        for i in range(warmup):
+            fn(i)
+    best = {}
+    for _ in range(2):
+        for name, fn in variants:
+            _, us = Timer(torch).run(steps, fn, first=warmup)
+            best[name] = min(us, best.get(name, us))
+    for name, _ in variants:
+        us = best[name]
+        res[name] = {"mean_us": us, "tflops": flops / (us * 1e-6) / 1e12,
+                     "frac_of_mfma_peak": flops / (us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS}
+        log(f"proj T={T} {name}: {us:.1f} us, {res[name]['tflops']:.0f} TFLOP/s")
+    del x, w, out, out2
+    torch.cuda.empty_cache()
+    return res
+
+
 def bench_decode_floor(q, torch, dev, T, H, reps=200):
     """Per-launch time of a tiny per-head call: eager (events) and hipGraph replay."""
     from qk_norm_amd import synth
@@ -290,7 +356,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--case", default="headline",
                     choices=["headline", "cfg5_layerwise", "cfg5_per_head", "fp8_per_head",
-                             "fp8_cfg5_layerwise", "copy"],
+                             "fp8_cfg5_layerwise", "proj", "copy"],
                     help="single case for profiling runs")
     args = ap.parse_args()
 
@@ -331,6 +397,9 @@ def main():
         p = synth.cfg5(T=32768, dtype=synth.F8)
         print(json.dumps({"case": "fp8_cfg5_layerwise",
                           **bench_layerwise(q, torch, dev, p, args.steps, args.warmup, "fp8 cfg5")}))
+        return
+    if args.case == "proj":
+        print(json.dumps({"case": "proj", **bench_proj(q, torch, dev, args.steps, args.warmup, T=8192)}))
         return
     if args.case == "cfg5_per_head":
         p = synth.cfg5(T=32768, mode="per_head")
@@ -384,6 +453,8 @@ def main():
                                                                  "fp8e4m3 [32768, 10240]")
         del p8
         cases["decode_floor"] = [bench_decode_floor(q, torch, dev, T, 48) for T in (1, 16, 128)]
+        for T in (4096, 8192):
+            cases[f"qkv_proj_T{T}_qwen3_8b"] = bench_proj(q, torch, dev, 30, 5, T=T)
         result["cases"] = cases
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(p)

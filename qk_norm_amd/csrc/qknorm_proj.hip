@@ -25,176 +25,220 @@ namespace qknorm {
 
 namespace {
 
-constexpr int kBM = 128, kBN = 128, kBK = 64;
-constexpr int kThreads = 256;
-constexpr int kLdsRow = kBK + 8;               // bf16 elements per padded LDS row
-constexpr int kCRow = kBN + 4;                 // fp32 elements per LDS row of the C tile
-constexpr int kTileElems = kBM * kLdsRow;      // one A (or B) buffer, bf16 elements
-constexpr int kLdsBytes = 4 * kTileElems * 2;  // A and B, two buffers each
-static_assert(kBM * kCRow * 4 <= kLdsBytes, "the C tile reuses the operand buffers");
-constexpr int kChunks = kBM * kBK * 2 / 16 / kThreads;   // 16-byte loads per thread per operand
-
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-// Global -> registers: chunk c = tid + i*256 of the tile is row c/8, columns
-// 8*(c%8) .. +8 of this K step.  Rows past the operand's end read zeros (the
-// descriptor covers only the valid rows).
+// Tile geometry.  A block of WM x WN waves owns a BM x BN output tile; each
+// wave a (BM/WM) x (BN/WN) slab of 32 x 32 MFMA blocks.  K advances BK at a
+// time through two LDS stages whose rows are padded by 16 bytes (the 16-byte
+// fragment reads of 32 consecutive rows then hit distinct banks).
+template <int BM_, int BN_, int WM_, int WN_, int BK_>
+struct Tile {
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, BK = BK_;
+  static constexpr int kThreads = 64 * WM * WN;
+  static constexpr int kWaveM = BM / WM, kWaveN = BN / WN;
+  static constexpr int MB = kWaveM / 32, NB = kWaveN / 32;
+  static constexpr int kLdsRow = BK + 8;                   // bf16 per padded row
+  static constexpr int kATile = BM * kLdsRow, kBTile = BN * kLdsRow;
+  static constexpr int kStage = kATile + kBTile;           // bf16 elements
+  static constexpr int kORow = BN + 8;                     // bf16 per output staging row
+  // two operand stages, or the bf16 output tile if that is larger (it reuses them)
+  static constexpr int kLdsBytes = 2 * kStage * 2 > BM * kORow * 2 ? 2 * kStage * 2 : BM * kORow * 2;
+  static constexpr int kRowChunks = BK * 2 / 16;           // 16-byte chunks per operand row
+  static constexpr int kAChunks = BM * kRowChunks / kThreads;
+  static constexpr int kBChunks = BN * kRowChunks / kThreads;
+  static_assert(BM * kRowChunks % kThreads == 0 && BN * kRowChunks % kThreads == 0, "");
+};
+
+// Global -> registers: chunk c = tid + i*threads of the tile is row
+// c / kRowChunks, 16 bytes at column chunk c % kRowChunks of this K step.
+// Rows past the operand's end read zeros (the descriptor covers only the
+// valid rows).
+template <class G, int CH>
 __device__ __forceinline__ void load_tile(Rsrc rs, uint32_t pitch_bytes, uint32_t k_bytes,
-                                          uint32_t tid, u32x4 (&r)[kChunks]) {
+                                          uint32_t tid, u32x4 (&r)[CH]) {
 #pragma unroll
-  for (int i = 0; i < kChunks; ++i) {
-    const uint32_t c = tid + i * kThreads;
-    r[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, (c / 8) * pitch_bytes + k_bytes + (c % 8) * 16,
-                                                 0, 0);
+  for (int i = 0; i < CH; ++i) {
+    const uint32_t c = tid + i * G::kThreads;
+    r[i] = __builtin_amdgcn_raw_buffer_load_b128(
+        rs, (c / G::kRowChunks) * pitch_bytes + k_bytes + (c % G::kRowChunks) * 16, 0, 0);
   }
 }
 
-__device__ __forceinline__ void store_tile(__bf16* lds, uint32_t tid, const u32x4 (&r)[kChunks]) {
+template <class G, int CH>
+__device__ __forceinline__ void store_tile(__bf16* lds, uint32_t tid, const u32x4 (&r)[CH]) {
 #pragma unroll
-  for (int i = 0; i < kChunks; ++i) {
-    const uint32_t c = tid + i * kThreads;
-    *reinterpret_cast<u32x4*>(lds + (c / 8) * kLdsRow + (c % 8) * 8) = r[i];
+  for (int i = 0; i < CH; ++i) {
+    const uint32_t c = tid + i * G::kThreads;
+    *reinterpret_cast<u32x4*>(lds + (c / G::kRowChunks) * G::kLdsRow + (c % G::kRowChunks) * 8) = r[i];
   }
 }
 
+template <class G>
 __device__ __forceinline__ bf16x8 frag(const __bf16* lds, uint32_t row, uint32_t k) {
-  return *reinterpret_cast<const bf16x8*>(lds + row * kLdsRow + k);
+  return *reinterpret_cast<const bf16x8*>(lds + row * G::kLdsRow + k);
 }
 
-// Epilogue for one tile: C (fp32, in LDS) -> normalised bf16 rows.  Lane l
-// of a wave takes row (step*4 + l/16) of its rows and columns 8*(l%16) ..
-// +8, so a head of D columns is D/8 consecutive lanes: its sum of squares is
-// the lanes' fma chains, then a D/8-lane reduction.
-template <int D>
-__device__ __forceinline__ void epilogue(const float* C, uint8_t* __restrict__ out,
-                                         uint64_t ld_bytes, uint32_t T, uint32_t N, uint32_t m0,
-                                         uint32_t n0, uint32_t hq, uint32_t hkv,
-                                         const uint8_t* __restrict__ gamma_q,
-                                         const uint8_t* __restrict__ gamma_k, float eps,
-                                         float inv_d, bool norm, uint32_t wave, uint32_t lane) {
-  constexpr uint32_t LG = D / 8;               // lanes per head
-  const uint32_t col = (lane % 16) * 8;        // column inside the tile
-  const uint32_t n = n0 + col;                 // global column of this lane's first value
-  const uint32_t head = n / D;
-  const bool is_q = head < hq, is_k = !is_q && head < hq + hkv;
-  const bool normed = norm && (is_q || is_k) && n < N;
-  float g[8];
-  if (normed) {
-    const uint8_t* gp = (is_q ? gamma_q : gamma_k) + (uint64_t)(n % D) * 2;
-    unpack<kBF16>(load16(gp), g);
-  }
-  const uint32_t valid_cols = N - n0 < (uint32_t)kBN ? N - n0 : (uint32_t)kBN;
-  for (uint32_t step = 0; step < kBM / 4 / 4; ++step) {   // 4 waves x 4 rows per step
-    const uint32_t r = (step * 4 + wave) * 4 + lane / 16;  // row inside the tile
-    const uint32_t t = m0 + r;
-    float v[8];
-    const float4 lo = *reinterpret_cast<const float4*>(C + r * kCRow + col);
-    const float4 hi = *reinterpret_cast<const float4*>(C + r * kCRow + col + 4);
-    v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w;
-    v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
-    float s = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) s = __builtin_fmaf(v[e], v[e], s);
-    s = group_sum<LG>(s);
-    if (normed) {
-      const float sc = rms_scale(s, inv_d, eps);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = (v[e] * g[e]) * sc;
-    }
-    // the row's valid columns only; rows past T store nothing
-    const Rsrc rs = make_rsrc(out + (uint64_t)(t < T ? t : 0) * ld_bytes + (uint64_t)n0 * 2,
-                              t < T ? valid_cols * 2 : 0);
-    stream_store(rs, col * 2, pack<kBF16>(v));
-  }
-}
-
-template <int D>
-__global__ __launch_bounds__(kThreads) void qkv_proj_kernel(
+template <class G, int D>
+__global__ __launch_bounds__(G::kThreads) void qkv_proj_kernel(
     const uint8_t* __restrict__ x, uint32_t ldx_bytes, const uint8_t* __restrict__ w,
     uint32_t ldw_bytes, uint8_t* __restrict__ out, uint64_t ld_bytes, uint32_t T, uint32_t K,
     uint32_t N, uint32_t hq, uint32_t hkv, const uint8_t* __restrict__ gamma_q,
     const uint8_t* __restrict__ gamma_k, float eps, float inv_d, uint32_t norm) {
+  constexpr int MB = G::MB, NB = G::NB, BK = G::BK;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  __bf16* As = reinterpret_cast<__bf16*>(smem);              // [2][BM][kLdsRow]
-  __bf16* Bs = As + 2 * kTileElems;                          // [2][BN][kLdsRow]
+  __bf16* As = reinterpret_cast<__bf16*>(smem);   // stage s: A at s*kStage, B after it
   const uint32_t tid = threadIdx.x, lane = tid & 63;
   const uint32_t wave = uniform(tid >> 6);
-  const uint32_t wm = wave >> 1, wn = wave & 1;              // the wave's 64 x 64 quarter
-  const uint32_t n0 = blockIdx.x * kBN, m0 = blockIdx.y * kBM;
+  const uint32_t wm = wave / G::WN, wn = wave % G::WN;
+  const uint32_t n0 = blockIdx.x * G::BN, m0 = blockIdx.y * G::BM;
 
-  // operand descriptors: the tile's rows that exist
-  const uint32_t a_rows = T - m0 < (uint32_t)kBM ? T - m0 : (uint32_t)kBM;
-  const uint32_t b_rows = N - n0 < (uint32_t)kBN ? N - n0 : (uint32_t)kBN;
+  const uint32_t a_rows = T - m0 < (uint32_t)G::BM ? T - m0 : (uint32_t)G::BM;
+  const uint32_t b_rows = N - n0 < (uint32_t)G::BN ? N - n0 : (uint32_t)G::BN;
   const Rsrc ra = make_rsrc(x + (uint64_t)m0 * ldx_bytes, (uint64_t)(a_rows - 1) * ldx_bytes + K * 2);
   const Rsrc rb = make_rsrc(w + (uint64_t)n0 * ldw_bytes, (uint64_t)(b_rows - 1) * ldw_bytes + K * 2);
 
-  f32x16 acc[2][2];
+  f32x16 acc[MB][NB];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < MB; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < NB; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-  const uint32_t ksteps = K / kBK;
-  u32x4 pa[kChunks], pb[kChunks];
-  load_tile(ra, ldx_bytes, 0, tid, pa);
-  load_tile(rb, ldw_bytes, 0, tid, pb);
-  store_tile(As, tid, pa);
-  store_tile(Bs, tid, pb);
+  // K steps alternate between two LDS stages; the global loads of step k+2
+  // are issued while step k computes, into the register set that step k's
+  // data came from, so each set's loads have a whole step of MFMAs to arrive
+  // before they are written to LDS.  Loads are unconditional (past the last
+  // step they fetch it again, unused), so the wait before each LDS write
+  // counts only the older set.
+  const uint32_t ksteps = K / BK;
+  const uint32_t last = (ksteps - 1) * BK * 2;
+  auto kbytes = [&](uint32_t k) { return k < ksteps ? k * BK * 2 : last; };
+  u32x4 pa0[G::kAChunks], pb0[G::kBChunks], pa1[G::kAChunks], pb1[G::kBChunks];
+  load_tile<G>(ra, ldx_bytes, 0, tid, pa0);
+  load_tile<G>(rb, ldw_bytes, 0, tid, pb0);
+  load_tile<G>(ra, ldx_bytes, kbytes(1), tid, pa1);
+  load_tile<G>(rb, ldw_bytes, kbytes(1), tid, pb1);
+  store_tile<G>(As, tid, pa0);
+  store_tile<G>(As + G::kATile, tid, pb0);
   __syncthreads();
 
   // a lane's fragment: row (lane % 32) of a 32-row block, 8 consecutive k
   // starting at 8*(lane/32) of each 16-wide MFMA step; A and B use the same
   // k order, so the products pair correctly whatever order the hardware sums
   const uint32_t fr = lane % 32, fk = 8 * (lane / 32);
-  for (uint32_t ks = 0; ks < ksteps; ++ks) {
-    const uint32_t buf = ks & 1;
-    const bool more = ks + 1 < ksteps;
-    if (more) {
-      load_tile(ra, ldx_bytes, (ks + 1) * kBK * 2, tid, pa);
-      load_tile(rb, ldw_bytes, (ks + 1) * kBK * 2, tid, pb);
-    }
-    const __bf16* Ab = As + buf * kTileElems;
-    const __bf16* Bb = Bs + buf * kTileElems;
-#pragma unroll
-    for (uint32_t kk = 0; kk < kBK; kk += 16) {
-      bf16x8 a[2], b[2];
-#pragma unroll
-      for (int i = 0; i < 2; ++i) a[i] = frag(Ab, wm * 64 + i * 32 + fr, kk + fk);
-#pragma unroll
-      for (int j = 0; j < 2; ++j) b[j] = frag(Bb, wn * 64 + j * 32 + fr, kk + fk);
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
-    }
-    if (more) {
-      store_tile(As + (buf ^ 1) * kTileElems, tid, pa);
-      store_tile(Bs + (buf ^ 1) * kTileElems, tid, pb);
+  const uint32_t arow = wm * G::kWaveM + fr, brow = wn * G::kWaveN + fr;
+#define QKNORM_PROJ_COMPUTE(STAGE)                                                         \
+  {                                                                                       \
+    const __bf16* Ab = As + (STAGE) * G::kStage;                                          \
+    const __bf16* Bb = Ab + G::kATile;                                                    \
+    _Pragma("unroll") for (uint32_t kk = 0; kk < (uint32_t)BK; kk += 16) {                \
+      bf16x8 a[MB], b[NB];                                                                \
+      _Pragma("unroll") for (int i = 0; i < MB; ++i) a[i] = frag<G>(Ab, arow + i * 32, kk + fk); \
+      _Pragma("unroll") for (int j = 0; j < NB; ++j) b[j] = frag<G>(Bb, brow + j * 32, kk + fk); \
+      _Pragma("unroll") for (int i = 0; i < MB; ++i)                                     \
+        _Pragma("unroll") for (int j = 0; j < NB; ++j)                                   \
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0); \
+    }                                                                                     \
+  }
+  for (uint32_t ks = 0; ks < ksteps; ks += 2) {
+    // even step ks: set 0 is free (its data is in stage 0), set 1 holds ks+1
+    load_tile<G>(ra, ldx_bytes, kbytes(ks + 2), tid, pa0);
+    load_tile<G>(rb, ldw_bytes, kbytes(ks + 2), tid, pb0);
+    QKNORM_PROJ_COMPUTE(0)
+    if (ks + 1 < ksteps) {
+      store_tile<G>(As + G::kStage, tid, pa1);
+      store_tile<G>(As + G::kStage + G::kATile, tid, pb1);
     }
     __syncthreads();
+    if (ks + 1 < ksteps) {
+      // odd step ks+1: set 1 is free, set 0 holds ks+2
+      load_tile<G>(ra, ldx_bytes, kbytes(ks + 3), tid, pa1);
+      load_tile<G>(rb, ldw_bytes, kbytes(ks + 3), tid, pb1);
+      QKNORM_PROJ_COMPUTE(1)
+      if (ks + 2 < ksteps) {
+        store_tile<G>(As, tid, pa0);
+        store_tile<G>(As + G::kATile, tid, pb0);
+      }
+      __syncthreads();
+    }
   }
+#undef QKNORM_PROJ_COMPUTE
 
-  // accumulators -> LDS (fp32): block (i, j) of the wave, value e of lane l
-  // is row 8*(e/4) + 4*(l/32) + e%4 and column l%32 of that 32 x 32 block
-  float* C = reinterpret_cast<float*>(smem);
+  // Epilogue.  Value e of block (i, j) in lane l is row i*32 + 8*(e/4) +
+  // 4*(l/32) + e%4 of the wave's slab and column j*32 + l%32.  A head of D
+  // columns is D/32 consecutive blocks j (a wave's columns are whole heads):
+  // its row sum of squares is the lane's fma chain over those blocks, then
+  // the 32-lane sum of the half-wave that holds the row.
+  constexpr int JH = D / 32;                    // blocks per head
+  static_assert(NB % JH == 0, "a wave's columns must be whole heads");
+  if (norm) {
+    float g[NB];
+    bool normed[NB];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+    for (int j = 0; j < NB; ++j) {
+      const uint32_t n = n0 + wn * G::kWaveN + j * 32 + lane % 32;
+      const uint32_t head = n / D;
+      const bool is_q = head < hq;
+      normed[j] = (is_q || head < hq + hkv) && n < N;
+      const __bf16* gp = reinterpret_cast<const __bf16*>(is_q ? gamma_q : gamma_k);
+      g[j] = normed[j] ? (float)gp[n % D] : 1.f;
+    }
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+      for (int h = 0; h < NB / JH; ++h) {
+        // the same for every lane and every block of one head (heads lie in
+        // one region and the tile's columns past N are whole heads)
+        if (!normed[h * JH]) continue;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          float s = 0.f;
+#pragma unroll
+          for (int jj = 0; jj < JH; ++jj)
+            s = __builtin_fmaf(acc[i][h * JH + jj][e], acc[i][h * JH + jj][e], s);
+          s = group_sum<32>(s);
+          const float sc = rms_scale(s, inv_d, eps);
+#pragma unroll
+          for (int jj = 0; jj < JH; ++jj)
+            acc[i][h * JH + jj][e] = (acc[i][h * JH + jj][e] * g[h * JH + jj]) * sc;
+        }
+      }
+  }
+  // the bf16 tile goes through LDS so rows leave as 16-byte stores
+  __syncthreads();                              // (stage buffers are reused)
+  __bf16* O = reinterpret_cast<__bf16*>(smem);
+#pragma unroll
+  for (int i = 0; i < MB; ++i)
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const uint32_t r = wm * 64 + i * 32 + 8 * (e / 4) + 4 * (lane / 32) + e % 4;
-        const uint32_t c = wn * 64 + j * 32 + lane % 32;
-        C[r * kCRow + c] = acc[i][j][e];
+        const uint32_t r = wm * G::kWaveM + i * 32 + 8 * (e / 4) + 4 * (lane / 32) + e % 4;
+        O[r * G::kORow + wn * G::kWaveN + j * 32 + lane % 32] = (__bf16)acc[i][j][e];
       }
   __syncthreads();
-  epilogue<D>(C, out, ld_bytes, T, N, m0, n0, hq, hkv, gamma_q, gamma_k, eps, inv_d, norm != 0,
-              wave, lane);
+  const uint32_t valid_cols = N - n0 < (uint32_t)G::BN ? N - n0 : (uint32_t)G::BN;
+  constexpr uint32_t kCols = G::BN / 8;         // 16-byte chunks per output row
+  constexpr uint32_t kRowsPerPass = G::kThreads / kCols;
+  for (uint32_t r0 = 0; r0 < (uint32_t)G::BM; r0 += kRowsPerPass) {
+    const uint32_t r = r0 + tid / kCols, c = (tid % kCols) * 8;
+    const uint32_t t = m0 + r;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(O + r * G::kORow + c);
+    const Rsrc rs = make_rsrc(out + (uint64_t)(t < T ? t : 0) * ld_bytes + (uint64_t)n0 * 2,
+                              t < T ? valid_cols * 2 : 0);
+    stream_store(rs, c * 2, v);
+  }
 }
+
+// 256 x 256 tiles of 8 waves (4 along M, 2 along N), each wave 64 x 128:
+// 0.75 fragment reads per MFMA and 131 flop per byte of operand staged, the
+// best of the shapes measured on MI355X (128 x 128 / 64 x 64 waves, 256 x 128
+// and 128 x 256 with 4 waves, 256 x 128 with BK = 32).
+using Geo = Tile<256, 256, 4, 2, 64>;
+constexpr int kBM = Geo::BM, kBN = Geo::BN, kBK = Geo::BK, kThreads = Geo::kThreads;
+constexpr int kLdsBytes = Geo::kLdsBytes;
 
 }  // namespace
 
@@ -209,7 +253,7 @@ bool proj_shape_ok(const ProjArgs& a) {
 hipError_t launch_qkv_proj(const ProjArgs& a, hipStream_t s) {
   const uint32_t N = (uint32_t)((a.hq + 2 * a.hkv) * a.head_dim);
   const dim3 grid((N + kBN - 1) / kBN, (uint32_t)((a.T + kBM - 1) / kBM));
-  auto kern = a.head_dim == 64 ? qkv_proj_kernel<64> : qkv_proj_kernel<128>;
+  auto kern = a.head_dim == 64 ? qkv_proj_kernel<Geo, 64> : qkv_proj_kernel<Geo, 128>;
   // more than the default 64 KiB of dynamic LDS (gfx950 has 160 KiB per CU);
   // a host-side attribute, set on every call (no shared state between threads)
   const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),

@@ -232,4 +232,5 @@ def test_projection_validation(lib):
     assert pj(lib, w=A16 + 2) == q.QKNORM_E_ALIGN
     assert pj(lib, ld=772) == q.QKNORM_E_ALIGN                             # 1544-byte pitch
     assert pj(lib, eps=-1.0) == q.QKNORM_E_EPS
-    assert pj(lib, ldx=(1 << 23) + 8, T=0) == q.QKNORM_E_UNSUPPORTED       # 128 rows over 2 GiB
+    assert pj(lib, ldx=(1 << 22) + 8, T=0) == q.QKNORM_E_UNSUPPORTED       # 256 rows over 2 GiB
+    assert pj(lib, ldw=(1 << 22) + 8, T=0) == q.QKNORM_E_UNSUPPORTED
