@@ -37,8 +37,9 @@ METRIC = "QK-Norm µs/call + achieved HBM GB/s (% of peak), 4096 tok×48 heads×
 HBM_PEAK_GBS = 8000.0
 POOL_BYTES = 1 << 30
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "per_head_bf16_T4096_H48_D128.pmc.md")
+# the per-head kernel's code and launch configuration
 KERNEL_SOURCES = [os.path.join(ROOT, "qk_norm_amd", "csrc", f) for f in
-                  ("qknorm_kernels.hip", "qknorm_device.hpp", "qknorm_api.hip", "qknorm_launch.hpp")]
+                  ("qknorm_kernels.hip", "qknorm_device.hpp")]
 
 
 def log(*a):

@@ -29,54 +29,53 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 // Tile geometry.  A block of WM x WN waves owns a BM x BN output tile; each
-// wave a (BM/WM) x (BN/WN) slab of 32 x 32 MFMA blocks.  K advances BK at a
-// time through two LDS stages whose rows are padded by 16 bytes (the 16-byte
-// fragment reads of 32 consecutive rows then hit distinct banks).
-template <int BM_, int BN_, int WM_, int WN_, int BK_>
+// wave a (BM/WM) x (BN/WN) slab of 32 x 32 MFMA blocks; K advances BK = 64
+// at a time through two LDS stages.  Operand rows are 128 bytes with no
+// padding; the 16-byte chunk c of row r is stored in slot c ^ (r % 8), so the
+// fragment reads of 8 consecutive rows hit 8 different slots.  Global loads
+// go straight into LDS (buffer_load_dwordx4 ... lds: lane i of a wave writes
+// 16 bytes at the instruction's LDS base + 16*i), so lane i of an
+// instruction covering rows R .. R+7 fetches row R + i/8, chunk
+// (i % 8) ^ (i / 8): no staging registers and no LDS write instructions.
+template <int BM_, int BN_, int WM_, int WN_>
 struct Tile {
-  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, BK = BK_;
-  static constexpr int kThreads = 64 * WM * WN;
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, BK = 64;
+  static constexpr int kThreads = 64 * WM * WN, kWaves = WM * WN;
   static constexpr int kWaveM = BM / WM, kWaveN = BN / WN;
   static constexpr int MB = kWaveM / 32, NB = kWaveN / 32;
-  static constexpr int kLdsRow = BK + 8;                   // bf16 per padded row
-  static constexpr int kATile = BM * kLdsRow, kBTile = BN * kLdsRow;
-  static constexpr int kStage = kATile + kBTile;           // bf16 elements
-  static constexpr int kORow = BN + 8;                     // bf16 per output staging row
-  // two operand stages, or the bf16 output tile if that is larger (it reuses them)
-  static constexpr int kLdsBytes = 2 * kStage * 2 > BM * kORow * 2 ? 2 * kStage * 2 : BM * kORow * 2;
-  static constexpr int kRowChunks = BK * 2 / 16;           // 16-byte chunks per operand row
-  static constexpr int kAChunks = BM * kRowChunks / kThreads;
-  static constexpr int kBChunks = BN * kRowChunks / kThreads;
-  static_assert(BM * kRowChunks % kThreads == 0 && BN * kRowChunks % kThreads == 0, "");
+  static constexpr int kRowBytes = 128;
+  static constexpr int kStageBytes = (BM + BN) * kRowBytes;
+  static constexpr int kORow = BN + 8;
+  static constexpr int kLdsBytes = 2 * kStageBytes > BM * kORow * 2 ? 2 * kStageBytes : BM * kORow * 2;
+  static constexpr int kAInst = BM / 8 / kWaves, kBInst = BN / 8 / kWaves;   // per wave per K step
+  static_assert(BM % (8 * kWaves) == 0 && BN % (8 * kWaves) == 0, "");
 };
 
-// Global -> registers: chunk c = tid + i*threads of the tile is row
-// c / kRowChunks, 16 bytes at column chunk c % kRowChunks of this K step.
-// Rows past the operand's end read zeros (the descriptor covers only the
-// valid rows).
-template <class G, int CH>
-__device__ __forceinline__ void load_tile(Rsrc rs, uint32_t pitch_bytes, uint32_t k_bytes,
-                                          uint32_t tid, u32x4 (&r)[CH]) {
+template <class G>
+__device__ __forceinline__ void dma_tile(Rsrc ra, uint32_t ldx_bytes, Rsrc rb, uint32_t ldw_bytes,
+                                         uint32_t k_bytes, uint8_t* stage, uint32_t wave,
+                                         uint32_t lane) {
+  const uint32_t sub = lane / 8, chunk = (lane % 8) ^ sub;
 #pragma unroll
-  for (int i = 0; i < CH; ++i) {
-    const uint32_t c = tid + i * G::kThreads;
-    r[i] = __builtin_amdgcn_raw_buffer_load_b128(
-        rs, (c / G::kRowChunks) * pitch_bytes + k_bytes + (c % G::kRowChunks) * 16, 0, 0);
+  for (int j = 0; j < G::kAInst; ++j) {
+    const uint32_t R = (wave * G::kAInst + j) * 8;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        ra, (__attribute__((address_space(3))) void*)(stage + R * G::kRowBytes), 16,
+        (R + sub) * ldx_bytes + k_bytes + chunk * 16, 0, 0, 0);
   }
-}
-
-template <class G, int CH>
-__device__ __forceinline__ void store_tile(__bf16* lds, uint32_t tid, const u32x4 (&r)[CH]) {
 #pragma unroll
-  for (int i = 0; i < CH; ++i) {
-    const uint32_t c = tid + i * G::kThreads;
-    *reinterpret_cast<u32x4*>(lds + (c / G::kRowChunks) * G::kLdsRow + (c % G::kRowChunks) * 8) = r[i];
+  for (int j = 0; j < G::kBInst; ++j) {
+    const uint32_t R = (wave * G::kBInst + j) * 8;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rb, (__attribute__((address_space(3))) void*)(stage + (G::BM + R) * G::kRowBytes), 16,
+        (R + sub) * ldw_bytes + k_bytes + chunk * 16, 0, 0, 0);
   }
 }
 
 template <class G>
-__device__ __forceinline__ bf16x8 frag(const __bf16* lds, uint32_t row, uint32_t k) {
-  return *reinterpret_cast<const bf16x8*>(lds + row * G::kLdsRow + k);
+__device__ __forceinline__ bf16x8 sfrag(const uint8_t* base, uint32_t row, uint32_t k) {
+  const uint32_t c = k / 8;
+  return *reinterpret_cast<const bf16x8*>(base + row * G::kRowBytes + ((c ^ (row % 8)) * 16));
 }
 
 template <class G, int D>
@@ -87,7 +86,6 @@ __global__ __launch_bounds__(G::kThreads) void qkv_proj_kernel(
     const uint8_t* __restrict__ gamma_k, float eps, float inv_d, uint32_t norm) {
   constexpr int MB = G::MB, NB = G::NB, BK = G::BK;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  __bf16* As = reinterpret_cast<__bf16*>(smem);   // stage s: A at s*kStage, B after it
   const uint32_t tid = threadIdx.x, lane = tid & 63;
   const uint32_t wave = uniform(tid >> 6);
   const uint32_t wm = wave / G::WN, wn = wave % G::WN;
@@ -106,65 +104,41 @@ __global__ __launch_bounds__(G::kThreads) void qkv_proj_kernel(
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-  // K steps alternate between two LDS stages; the global loads of step k+2
-  // are issued while step k computes, into the register set that step k's
-  // data came from, so each set's loads have a whole step of MFMAs to arrive
-  // before they are written to LDS.  Loads are unconditional (past the last
-  // step they fetch it again, unused), so the wait before each LDS write
-  // counts only the older set.
+  // K steps alternate between the two stages: step k+1's loads go into the
+  // other stage while step k computes; a full wait and a barrier then make
+  // every wave's loads visible before that stage is read.
   const uint32_t ksteps = K / BK;
-  const uint32_t last = (ksteps - 1) * BK * 2;
-  auto kbytes = [&](uint32_t k) { return k < ksteps ? k * BK * 2 : last; };
-  u32x4 pa0[G::kAChunks], pb0[G::kBChunks], pa1[G::kAChunks], pb1[G::kBChunks];
-  load_tile<G>(ra, ldx_bytes, 0, tid, pa0);
-  load_tile<G>(rb, ldw_bytes, 0, tid, pb0);
-  load_tile<G>(ra, ldx_bytes, kbytes(1), tid, pa1);
-  load_tile<G>(rb, ldw_bytes, kbytes(1), tid, pb1);
-  store_tile<G>(As, tid, pa0);
-  store_tile<G>(As + G::kATile, tid, pb0);
-  __syncthreads();
+  dma_tile<G>(ra, ldx_bytes, rb, ldw_bytes, 0, smem, wave, lane);
+  __builtin_amdgcn_s_waitcnt(0);                // this wave's loads have landed
+  __syncthreads();                              // and everyone's
 
   // a lane's fragment: row (lane % 32) of a 32-row block, 8 consecutive k
   // starting at 8*(lane/32) of each 16-wide MFMA step; A and B use the same
   // k order, so the products pair correctly whatever order the hardware sums
   const uint32_t fr = lane % 32, fk = 8 * (lane / 32);
-  const uint32_t arow = wm * G::kWaveM + fr, brow = wn * G::kWaveN + fr;
-#define QKNORM_PROJ_COMPUTE(STAGE)                                                         \
-  {                                                                                       \
-    const __bf16* Ab = As + (STAGE) * G::kStage;                                          \
-    const __bf16* Bb = Ab + G::kATile;                                                    \
-    _Pragma("unroll") for (uint32_t kk = 0; kk < (uint32_t)BK; kk += 16) {                \
-      bf16x8 a[MB], b[NB];                                                                \
-      _Pragma("unroll") for (int i = 0; i < MB; ++i) a[i] = frag<G>(Ab, arow + i * 32, kk + fk); \
-      _Pragma("unroll") for (int j = 0; j < NB; ++j) b[j] = frag<G>(Bb, brow + j * 32, kk + fk); \
-      _Pragma("unroll") for (int i = 0; i < MB; ++i)                                     \
-        _Pragma("unroll") for (int j = 0; j < NB; ++j)                                   \
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0); \
-    }                                                                                     \
-  }
-  for (uint32_t ks = 0; ks < ksteps; ks += 2) {
-    // even step ks: set 0 is free (its data is in stage 0), set 1 holds ks+1
-    load_tile<G>(ra, ldx_bytes, kbytes(ks + 2), tid, pa0);
-    load_tile<G>(rb, ldw_bytes, kbytes(ks + 2), tid, pb0);
-    QKNORM_PROJ_COMPUTE(0)
-    if (ks + 1 < ksteps) {
-      store_tile<G>(As + G::kStage, tid, pa1);
-      store_tile<G>(As + G::kStage + G::kATile, tid, pb1);
+  const uint32_t arow = wm * G::kWaveM + fr, brow = G::BM + wn * G::kWaveN + fr;
+  for (uint32_t ks = 0; ks < ksteps; ++ks) {
+    const uint8_t* st = smem + (ks & 1) * G::kStageBytes;
+    // the other stage was last read in step ks-1, finished at its barrier
+    if (ks + 1 < ksteps)
+      dma_tile<G>(ra, ldx_bytes, rb, ldw_bytes, (ks + 1) * BK * 2,
+                  smem + ((ks + 1) & 1) * G::kStageBytes, wave, lane);
+#pragma unroll
+    for (uint32_t kk = 0; kk < (uint32_t)BK; kk += 16) {
+      bf16x8 a[MB], b[NB];
+#pragma unroll
+      for (int i = 0; i < MB; ++i) a[i] = sfrag<G>(st, arow + i * 32, kk + fk);
+#pragma unroll
+      for (int j = 0; j < NB; ++j) b[j] = sfrag<G>(st, brow + j * 32, kk + fk);
+#pragma unroll
+      for (int i = 0; i < MB; ++i)
+#pragma unroll
+        for (int j = 0; j < NB; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
     }
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (ks + 1 < ksteps) {
-      // odd step ks+1: set 1 is free, set 0 holds ks+2
-      load_tile<G>(ra, ldx_bytes, kbytes(ks + 3), tid, pa1);
-      load_tile<G>(rb, ldw_bytes, kbytes(ks + 3), tid, pb1);
-      QKNORM_PROJ_COMPUTE(1)
-      if (ks + 2 < ksteps) {
-        store_tile<G>(As, tid, pa0);
-        store_tile<G>(As + G::kATile, tid, pb0);
-      }
-      __syncthreads();
-    }
   }
-#undef QKNORM_PROJ_COMPUTE
 
   // Epilogue.  Value e of block (i, j) in lane l is row i*32 + 8*(e/4) +
   // 4*(l/32) + e%4 of the wave's slab and column j*32 + l%32.  A head of D
@@ -206,8 +180,8 @@ __global__ __launch_bounds__(G::kThreads) void qkv_proj_kernel(
         }
       }
   }
-  // the bf16 tile goes through LDS so rows leave as 16-byte stores
-  __syncthreads();                              // (stage buffers are reused)
+  // the bf16 tile goes through LDS (the stages are free after the loop's last
+  // barrier) so rows leave as 16-byte stores
   __bf16* O = reinterpret_cast<__bf16*>(smem);
 #pragma unroll
   for (int i = 0; i < MB; ++i)
@@ -220,7 +194,7 @@ __global__ __launch_bounds__(G::kThreads) void qkv_proj_kernel(
       }
   __syncthreads();
   const uint32_t valid_cols = N - n0 < (uint32_t)G::BN ? N - n0 : (uint32_t)G::BN;
-  constexpr uint32_t kCols = G::BN / 8;         // 16-byte chunks per output row
+  constexpr uint32_t kCols = G::BN / 8;
   constexpr uint32_t kRowsPerPass = G::kThreads / kCols;
   for (uint32_t r0 = 0; r0 < (uint32_t)G::BM; r0 += kRowsPerPass) {
     const uint32_t r = r0 + tid / kCols, c = (tid % kCols) * 8;
@@ -234,9 +208,10 @@ __global__ __launch_bounds__(G::kThreads) void qkv_proj_kernel(
 
 // 256 x 256 tiles of 8 waves (4 along M, 2 along N), each wave 64 x 128:
 // 0.75 fragment reads per MFMA and 131 flop per byte of operand staged, the
-// best of the shapes measured on MI355X (128 x 128 / 64 x 64 waves, 256 x 128
-// and 128 x 256 with 4 waves, 256 x 128 with BK = 32).
-using Geo = Tile<256, 256, 4, 2, 64>;
+// best of the shapes measured on MI355X (128 x 128 with 64 x 64 waves,
+// 256 x 128 and 128 x 256 with 4 waves, 256 x 128 with BK = 32); loading
+// straight into LDS beat staging through registers by 3-4 %.
+using Geo = Tile<256, 256, 4, 2>;
 constexpr int kBM = Geo::BM, kBN = Geo::BN, kBK = Geo::BK, kThreads = Geo::kThreads;
 constexpr int kLdsBytes = Geo::kLdsBytes;
 
