@@ -180,8 +180,8 @@ int qknorm_apply_scalar(void *qkv, int64_t T, int64_t ld, int64_t wq, int64_t wk
  *     projection (gamma and eps unused).
  * Requires: hidden a multiple of 64 and head_dim 64 or 128 (else
  * QKNORM_E_UNSUPPORTED); ldx, ldw >= hidden and ld >= N; x, w, qkv and gamma
- * 16-byte aligned, pitches*2 multiples of 16 bytes; 256 rows of x and 256
- * rows of w each below 2 GiB.  x, w and gamma must not overlap qkv.
+ * 16-byte aligned, pitches*2 multiples of 16 bytes; 256 rows of x, of w and
+ * of qkv each below 2 GiB.  x, w and gamma must not overlap qkv.
  */
 #define QKNORM_PROJ_PLAIN 1
 int qknorm_qkv_proj_per_head(const void *x, int64_t ldx, const void *w, int64_t ldw, void *qkv,

@@ -29,54 +29,87 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 // Tile geometry.  A block of WM x WN waves owns a BM x BN output tile; each
-// wave a (BM/WM) x (BN/WN) slab of 32 x 32 MFMA blocks; K advances BK = 64
-// at a time through two LDS stages.  Operand rows are 128 bytes with no
-// padding; the 16-byte chunk c of row r is stored in slot c ^ (r % 8), so the
-// fragment reads of 8 consecutive rows hit 8 different slots.  Global loads
+// wave a (BM/WM) x (BN/WN) slab of 32 x 32 MFMA blocks; K advances BK at a
+// time through S LDS stages.  Operand rows are BK*2 bytes with no padding:
+// the 16-byte chunk c of row r sits in slot c ^ ((r / RPB) % CPR) (CPR chunks
+// per row, RPB rows per 256 bytes), so the 16 rows read by 16 lanes at once
+// land in 16 different 16-byte slots of a 256-byte bank line.  Global loads
 // go straight into LDS (buffer_load_dwordx4 ... lds: lane i of a wave writes
 // 16 bytes at the instruction's LDS base + 16*i), so lane i of an
-// instruction covering rows R .. R+7 fetches row R + i/8, chunk
-// (i % 8) ^ (i / 8): no staging registers and no LDS write instructions.
-template <int BM_, int BN_, int WM_, int WN_>
+// instruction covering rows R .. R+1024/(BK*2)-1 fetches row R + i / CPR and
+// the chunk whose slot is i % CPR: no staging registers and no LDS write
+// instructions.
+template <int BM_, int BN_, int WM_, int WN_, int BK_, int S_>
 struct Tile {
-  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, BK = 64;
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, BK = BK_, S = S_;
   static constexpr int kThreads = 64 * WM * WN, kWaves = WM * WN;
   static constexpr int kWaveM = BM / WM, kWaveN = BN / WN;
   static constexpr int MB = kWaveM / 32, NB = kWaveN / 32;
-  static constexpr int kRowBytes = 128;
+  static constexpr int kRowBytes = BK * 2;
+  static constexpr int CPR = kRowBytes / 16, RPB = 256 / kRowBytes;
+  static constexpr int kInstRows = 1024 / kRowBytes;         // rows one load instruction fills
   static constexpr int kStageBytes = (BM + BN) * kRowBytes;
   static constexpr int kORow = BN + 8;
-  static constexpr int kLdsBytes = 2 * kStageBytes > BM * kORow * 2 ? 2 * kStageBytes : BM * kORow * 2;
-  static constexpr int kAInst = BM / 8 / kWaves, kBInst = BN / 8 / kWaves;   // per wave per K step
-  static_assert(BM % (8 * kWaves) == 0 && BN % (8 * kWaves) == 0, "");
+  static constexpr int kLdsBytes = S * kStageBytes > BM * kORow * 2 ? S * kStageBytes : BM * kORow * 2;
+  static constexpr int kAInst = BM / kInstRows / kWaves, kBInst = BN / kInstRows / kWaves;
+  static constexpr int kLoads = kAInst + kBInst;              // per wave per K step
+  static_assert(BM % (kInstRows * kWaves) == 0 && BN % (kInstRows * kWaves) == 0, "");
+  static_assert(RPB * CPR == 16, "a 256-byte line holds 16 chunks");
 };
+
+template <class G>
+__device__ __forceinline__ uint32_t lds_slot(uint32_t row, uint32_t chunk) {
+  return chunk ^ ((row / G::RPB) % G::CPR);
+}
 
 template <class G>
 __device__ __forceinline__ void dma_tile(Rsrc ra, uint32_t ldx_bytes, Rsrc rb, uint32_t ldw_bytes,
                                          uint32_t k_bytes, uint8_t* stage, uint32_t wave,
                                          uint32_t lane) {
-  const uint32_t sub = lane / 8, chunk = (lane % 8) ^ sub;
+  constexpr uint32_t kRows = G::kInstRows, kRowBytes = G::kRowBytes, kBM = G::BM;
+  constexpr uint32_t kCpr = G::CPR, kRpb = G::RPB;
+  constexpr int kInst = G::kAInst;
+  static_assert(G::kAInst == G::kBInst, "one A and one B load per step of the loop");
+  const uint32_t sub = lane / kCpr, s = lane % kCpr;
 #pragma unroll
-  for (int j = 0; j < G::kAInst; ++j) {
-    const uint32_t R = (wave * G::kAInst + j) * 8;
+  for (int j = 0; j < kInst; ++j) {
+    const uint32_t R = (wave * kInst + j) * kRows, r = R + sub;
+    const uint32_t a_off = r * ldx_bytes + k_bytes + (s ^ ((r / kRpb) % kCpr)) * 16;
+    const uint32_t b_off = r * ldw_bytes + k_bytes + (s ^ (((kBM + r) / kRpb) % kCpr)) * 16;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        ra, (__attribute__((address_space(3))) void*)(stage + R * G::kRowBytes), 16,
-        (R + sub) * ldx_bytes + k_bytes + chunk * 16, 0, 0, 0);
-  }
-#pragma unroll
-  for (int j = 0; j < G::kBInst; ++j) {
-    const uint32_t R = (wave * G::kBInst + j) * 8;
+        ra, (__attribute__((address_space(3))) void*)(stage + R * kRowBytes), 16, a_off, 0, 0, 0);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        rb, (__attribute__((address_space(3))) void*)(stage + (G::BM + R) * G::kRowBytes), 16,
-        (R + sub) * ldw_bytes + k_bytes + chunk * 16, 0, 0, 0);
+        rb, (__attribute__((address_space(3))) void*)(stage + (kBM + R) * kRowBytes), 16, b_off, 0,
+        0, 0);
   }
 }
 
 template <class G>
 __device__ __forceinline__ bf16x8 sfrag(const uint8_t* base, uint32_t row, uint32_t k) {
-  const uint32_t c = k / 8;
-  return *reinterpret_cast<const bf16x8*>(base + row * G::kRowBytes + ((c ^ (row % 8)) * 16));
+  return *reinterpret_cast<const bf16x8*>(base + row * G::kRowBytes + lds_slot<G>(row, k / 8) * 16);
 }
+
+// Byte offset of K step k, or of the last step for k past it.
+template <class G>
+__device__ __forceinline__ uint32_t step_bytes(uint32_t k, uint32_t ksteps) {
+  return (k < ksteps ? k : ksteps - 1) * G::BK * 2;
+}
+
+// s_waitcnt with vmcnt(N) and the other counters left alone (gfx9 encoding:
+// vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// A workgroup barrier with no release fence: __syncthreads() would make the
+// compiler wait for every outstanding load into LDS (vmcnt(0)), including the
+// ones meant to stay in flight.  The "memory" clobber keeps the compiler from
+// moving LDS accesses across it; the loads that must have landed are waited
+// for explicitly before it, and the fragment reads of the stage about to be
+// refilled have all completed (their MFMAs consumed them).
+__device__ __forceinline__ void stage_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
 template <class G, int D>
 __global__ __launch_bounds__(G::kThreads) void qkv_proj_kernel(
@@ -104,25 +137,32 @@ __global__ __launch_bounds__(G::kThreads) void qkv_proj_kernel(
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-  // K steps alternate between the two stages: step k+1's loads go into the
-  // other stage while step k computes; a full wait and a barrier then make
-  // every wave's loads visible before that stage is read.
+  // K steps rotate through S stages: while step k computes, the loads of
+  // steps k+1 .. k+S-1 are in flight (step k+S-1's issued at the top of step
+  // k, into the stage step k-1 used).  Before the barrier that ends step k a
+  // wave waits until at most (S-2) steps of its loads are outstanding, i.e.
+  // step k+1's have landed; the barrier makes everyone's visible.  Loads past
+  // the last step fetch the last step again (unused), so the count is exact.
   const uint32_t ksteps = K / BK;
-  dma_tile<G>(ra, ldx_bytes, rb, ldw_bytes, 0, smem, wave, lane);
-  __builtin_amdgcn_s_waitcnt(0);                // this wave's loads have landed
-  __syncthreads();                              // and everyone's
+#pragma unroll
+  for (int st = 0; st < G::S - 1; ++st)
+    dma_tile<G>(ra, ldx_bytes, rb, ldw_bytes, step_bytes<G>(st, ksteps), smem + st * G::kStageBytes,
+                wave, lane);
+  wait_vmcnt<(G::S - 2) * G::kLoads>();         // step 0 has landed (this wave)
+  stage_barrier();                              // (and everyone's)
 
   // a lane's fragment: row (lane % 32) of a 32-row block, 8 consecutive k
   // starting at 8*(lane/32) of each 16-wide MFMA step; A and B use the same
   // k order, so the products pair correctly whatever order the hardware sums
   const uint32_t fr = lane % 32, fk = 8 * (lane / 32);
   const uint32_t arow = wm * G::kWaveM + fr, brow = G::BM + wn * G::kWaveN + fr;
+  uint32_t cur = 0;                             // stage of step ks
   for (uint32_t ks = 0; ks < ksteps; ++ks) {
-    const uint8_t* st = smem + (ks & 1) * G::kStageBytes;
-    // the other stage was last read in step ks-1, finished at its barrier
-    if (ks + 1 < ksteps)
-      dma_tile<G>(ra, ldx_bytes, rb, ldw_bytes, (ks + 1) * BK * 2,
-                  smem + ((ks + 1) & 1) * G::kStageBytes, wave, lane);
+    const uint8_t* st = smem + cur * G::kStageBytes;
+    // step ks+S-1 goes into the stage step ks-1 used (read before its barrier)
+    const uint32_t nxt = cur == 0 ? G::S - 1 : cur - 1;
+    dma_tile<G>(ra, ldx_bytes, rb, ldw_bytes, step_bytes<G>(ks + G::S - 1, ksteps),
+                smem + nxt * G::kStageBytes, wave, lane);
 #pragma unroll
     for (uint32_t kk = 0; kk < (uint32_t)BK; kk += 16) {
       bf16x8 a[MB], b[NB];
@@ -136,9 +176,13 @@ __global__ __launch_bounds__(G::kThreads) void qkv_proj_kernel(
         for (int j = 0; j < NB; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
     }
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+    wait_vmcnt<(G::S - 2) * G::kLoads>();
+    stage_barrier();
+    cur = cur + 1 == (uint32_t)G::S ? 0 : cur + 1;
   }
+  // the output tile reuses the stages: every load into LDS must be done
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
 
   // Epilogue.  Value e of block (i, j) in lane l is row i*32 + 8*(e/4) +
   // 4*(l/32) + e%4 of the wave's slab and column j*32 + l%32.  A head of D
@@ -193,25 +237,33 @@ __global__ __launch_bounds__(G::kThreads) void qkv_proj_kernel(
         O[r * G::kORow + wn * G::kWaveN + j * 32 + lane % 32] = (__bf16)acc[i][j][e];
       }
   __syncthreads();
+  // one descriptor over the tile's rows (wave-uniform); rows past T and
+  // columns past N get an offset outside it
   const uint32_t valid_cols = N - n0 < (uint32_t)G::BN ? N - n0 : (uint32_t)G::BN;
+  const Rsrc ro = make_rsrc(out + (uint64_t)m0 * ld_bytes + (uint64_t)n0 * 2,
+                            (uint64_t)(a_rows - 1) * ld_bytes + valid_cols * 2);
   constexpr uint32_t kCols = G::BN / 8;
   constexpr uint32_t kRowsPerPass = G::kThreads / kCols;
   for (uint32_t r0 = 0; r0 < (uint32_t)G::BM; r0 += kRowsPerPass) {
     const uint32_t r = r0 + tid / kCols, c = (tid % kCols) * 8;
-    const uint32_t t = m0 + r;
     const u32x4 v = *reinterpret_cast<const u32x4*>(O + r * G::kORow + c);
-    const Rsrc rs = make_rsrc(out + (uint64_t)(t < T ? t : 0) * ld_bytes + (uint64_t)n0 * 2,
-                              t < T ? valid_cols * 2 : 0);
-    stream_store(rs, c * 2, v);
+    stream_store(ro, r < a_rows && c < valid_cols ? r * (uint32_t)ld_bytes + c * 2 : 0xFFFFFFF0u, v);
   }
 }
 
 // 256 x 256 tiles of 8 waves (4 along M, 2 along N), each wave 64 x 128:
 // 0.75 fragment reads per MFMA and 131 flop per byte of operand staged, the
 // best of the shapes measured on MI355X (128 x 128 with 64 x 64 waves,
-// 256 x 128 and 128 x 256 with 4 waves, 256 x 128 with BK = 32); loading
-// straight into LDS beat staging through registers by 3-4 %.
-using Geo = Tile<256, 256, 4, 2>;
+// 256 x 128 and 128 x 256 with 4 waves, 256 x 128 with BK = 32).  Among the
+// pipelines measured, BK = 64 with two stages beat BK = 32 with three or four
+// (fewer barriers outweigh the shorter prefetch).
+#ifndef QKNORM_PROJ_BK
+#define QKNORM_PROJ_BK 64
+#endif
+#ifndef QKNORM_PROJ_STAGES
+#define QKNORM_PROJ_STAGES 2
+#endif
+using Geo = Tile<256, 256, 4, 2, QKNORM_PROJ_BK, QKNORM_PROJ_STAGES>;
 constexpr int kBM = Geo::BM, kBN = Geo::BN, kBK = Geo::BK, kThreads = Geo::kThreads;
 constexpr int kLdsBytes = Geo::kLdsBytes;
 
@@ -221,7 +273,8 @@ bool proj_shape_ok(const ProjArgs& a) {
   // buffer offsets inside one tile's rows stay below 2^31
   const uint64_t es = 2;
   return (uint64_t)kBM * a.ldx * es < (UINT64_C(1) << 31) &&
-         (uint64_t)kBN * a.ldw * es < (UINT64_C(1) << 31) && a.hidden % kBK == 0 &&
+         (uint64_t)kBN * a.ldw * es < (UINT64_C(1) << 31) &&
+         (uint64_t)kBM * a.ld * es < (UINT64_C(1) << 31) && a.hidden % 64 == 0 &&
          (a.head_dim == 64 || a.head_dim == 128);
 }
 
