@@ -292,41 +292,61 @@ def bench_proj(q, torch, dev, steps, warmup, T=4096, hidden=4096, hq=32, hkv=8, 
     return res
 
 
-def bench_decode_floor(q, torch, dev, T, H, reps=200):
-    """Per-launch time of a tiny per-head call: eager (events) and hipGraph replay."""
+def bench_decode(q, torch, dev, reps=200):
+    """Decode-sized launches: per-head [T, 48, 128] bf16 for T in {1, 8, 16, 64, 128}
+    and layerwise [T, 6144] (Q 4096 + K 1024, 8 shards) for T in {1, 4, 32, 256}.
+    For each: host time per eager call through the binding, GPU time per launch
+    from one event pair around `reps` back-to-back launches, and per launch in a
+    replayed hipGraph of `reps` launches."""
     from qk_norm_amd import synth
-    p = synth.cfg2(T=T, H=H)
-    x = to_device(p.x, p.dtype, torch, dev)
-    g = to_device(p.gamma_q, p.dtype, torch, dev)
+    out = []
 
-    def launch(_i=0):
-        q.qknorm_per_head(x, H, 0, 128, g, None, p.eps)
-
-    for _ in range(20):
-        launch()
-    timer = Timer(torch)
-    _, mean_us = timer.run(reps, launch)
-    st = timer.spread(reps, launch)
-    # graph of 100 launches: per-launch floor without host overhead
-    graph = torch.cuda.CUDAGraph()
-    s = torch.cuda.Stream()
-    s.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(s):
-        with torch.cuda.graph(graph, stream=s):
-            for _ in range(100):
-                launch()
-    torch.cuda.synchronize()
-    graph.replay()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(5):
+    def measure(launch):
+        for _ in range(20):
+            launch()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            launch()
+        host_us = (time.perf_counter() - t0) / reps * 1e6
+        torch.cuda.synchronize()
+        _, gpu_us = Timer(torch).run(reps, lambda _i: launch())
+        graph = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            with torch.cuda.graph(graph, stream=s):
+                for _ in range(reps):
+                    launch()
+        torch.cuda.synchronize()
         graph.replay()
-    e1.record()
-    torch.cuda.synchronize()
-    floor = e0.elapsed_time(e1) * 1e3 / 500
-    return {"T": T, "H": H, "eager_back_to_back_us": mean_us, "event_pair_p50_us": st["p50_us"],
-            "graph_per_launch_us": floor}
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return host_us, gpu_us, e0.elapsed_time(e1) * 1e3 / reps
+
+    for T in (1, 8, 16, 64, 128):
+        p = synth.cfg2(T=T, H=48)
+        x = to_device(p.x, p.dtype, torch, dev)
+        g = to_device(p.gamma_q, p.dtype, torch, dev)
+        h, gpu, gr = measure(lambda: q.qknorm_per_head(x, 48, 0, 128, g, None, p.eps))
+        out.append({"mode": "per_head", "T": T, "H": 48, "host_us_per_eager_call": h,
+                    "gpu_us_per_launch_back_to_back": gpu, "graph_us_per_launch": gr})
+        log(f"decode per-head T={T}: host {h:.2f} us, back-to-back {gpu:.2f} us, graph {gr:.2f} us")
+    for T in (1, 4, 32, 256):
+        p = synth.cfg4(T=T)
+        x = to_device(p.x, p.dtype, torch, dev)
+        gq = to_device(p.gamma_q, p.dtype, torch, dev)
+        gk = to_device(p.gamma_k, p.dtype, torch, dev)
+        h, gpu, gr = measure(lambda: q.qknorm_layerwise(x, p.wq, p.wk, gq, gk, p.eps, p.nshards))
+        out.append({"mode": "layerwise", "T": T, "wq": p.wq, "wk": p.wk, "nshards": p.nshards,
+                    "host_us_per_eager_call": h, "gpu_us_per_launch_back_to_back": gpu,
+                    "graph_us_per_launch": gr})
+        log(f"decode layerwise T={T}: host {h:.2f} us, back-to-back {gpu:.2f} us, graph {gr:.2f} us")
+    return out
 
 
 def cpu_baseline(p, budget_s=10.0):
@@ -357,7 +377,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--case", default="headline",
                     choices=["headline", "cfg5_layerwise", "cfg5_per_head", "fp8_per_head",
-                             "fp8_cfg5_layerwise", "proj", "copy"],
+                             "fp8_cfg5_layerwise", "proj", "decode", "copy"],
                     help="single case for profiling runs")
     args = ap.parse_args()
 
@@ -398,6 +418,9 @@ def main():
         p = synth.cfg5(T=32768, dtype=synth.F8)
         print(json.dumps({"case": "fp8_cfg5_layerwise",
                           **bench_layerwise(q, torch, dev, p, args.steps, args.warmup, "fp8 cfg5")}))
+        return
+    if args.case == "decode":
+        print(json.dumps({"case": "decode", "launches": bench_decode(q, torch, dev)}))
         return
     if args.case == "proj":
         print(json.dumps({"case": "proj", **bench_proj(q, torch, dev, args.steps, args.warmup, T=8192)}))
@@ -453,7 +476,7 @@ def main():
         cases["fp8e4m3_cfg5_T32768_layerwise"] = bench_layerwise(q, torch, dev, p8, 50, 5,
                                                                  "fp8e4m3 [32768, 10240]")
         del p8
-        cases["decode_floor"] = [bench_decode_floor(q, torch, dev, T, 48) for T in (1, 16, 128)]
+        cases["decode"] = bench_decode(q, torch, dev)
         for T in (4096, 8192):
             cases[f"qkv_proj_T{T}_qwen3_8b"] = bench_proj(q, torch, dev, 30, 5, T=T)
         result["cases"] = cases
