@@ -7,14 +7,15 @@
 // the V columns are stored as they are.  One pass instead of a projection
 // that writes qkv and a normalisation that reads and writes it again.
 //
-// Tiling: a block of 256 threads (2 x 2 waves) owns a BM x BN = 128 x 128
-// output tile; each wave a 64 x 64 quarter, as 2 x 2 v_mfma_f32_32x32x16
-// blocks.  K advances in BK = 64 steps through two LDS buffers (rows padded
-// to 144 bytes, so the 16-byte fragment reads of 32 consecutive rows hit
-// distinct banks): the next step's global loads are in flight in registers
-// while the current step's MFMAs run.  Because BN is a multiple of head_dim
-// and tiles start at multiples of BN, a tile holds whole heads, and the
-// epilogue can normalise them without leaving the block.
+// Tiling: a block of 512 threads (4 x 2 waves, two per SIMD) owns a 256 x 256
+// output tile; each wave a 64 x 128 slab of 2 x 4 v_mfma_f32_32x32x16_bf16
+// blocks.  K advances 64 at a time through two LDS stages filled straight
+// from global memory (buffer loads into LDS, no staging registers), with
+// the operand rows XOR-swizzled so that fragment reads hit distinct banks.
+// Tiles are ordered so the blocks each XCD holds at once share operand
+// panels in its L2.  Because the tile width is a multiple of head_dim and
+// tiles start at multiples of it, a tile holds whole heads, and the epilogue
+// normalises them in registers without leaving the block.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -57,30 +58,63 @@ struct Tile {
   static_assert(RPB * CPR == 16, "a 256-byte line holds 16 chunks");
 };
 
+#ifndef QKNORM_PROJ_XCD
+#define QKNORM_PROJ_XCD 1
+#endif
+#ifndef QKNORM_PROJ_GM
+#define QKNORM_PROJ_GM 4
+#endif
+constexpr bool kXcdRemap = QKNORM_PROJ_XCD != 0;
+constexpr uint32_t kGroupM = QKNORM_PROJ_GM;
+
 template <class G>
 __device__ __forceinline__ uint32_t lds_slot(uint32_t row, uint32_t chunk) {
   return chunk ^ ((row / G::RPB) % G::CPR);
 }
 
+// Per-lane byte offsets of a wave's operand loads within a K step: A rows in
+// off[0..kAInst), B rows after them.  They do not change with the step (the
+// step's byte offset travels in the instruction's scalar offset).
 template <class G>
-__device__ __forceinline__ void dma_tile(Rsrc ra, uint32_t ldx_bytes, Rsrc rb, uint32_t ldw_bytes,
-                                         uint32_t k_bytes, uint8_t* stage, uint32_t wave,
-                                         uint32_t lane) {
-  constexpr uint32_t kRows = G::kInstRows, kRowBytes = G::kRowBytes, kBM = G::BM;
-  constexpr uint32_t kCpr = G::CPR, kRpb = G::RPB;
+struct DmaOffsets {
+  uint32_t a[G::kAInst], b[G::kBInst];
+};
+
+template <class G>
+__device__ __forceinline__ DmaOffsets<G> dma_offsets(uint32_t ldx_bytes, uint32_t ldw_bytes,
+                                                     uint32_t wave, uint32_t lane) {
+  constexpr uint32_t kRows = G::kInstRows, kBM = G::BM, kCpr = G::CPR, kRpb = G::RPB;
   constexpr int kInst = G::kAInst;
-  static_assert(G::kAInst == G::kBInst, "one A and one B load per step of the loop");
+  static_assert(G::kAInst == G::kBInst, "as many A as B loads");
   const uint32_t sub = lane / kCpr, s = lane % kCpr;
+  DmaOffsets<G> o;
 #pragma unroll
   for (int j = 0; j < kInst; ++j) {
-    const uint32_t R = (wave * kInst + j) * kRows, r = R + sub;
-    const uint32_t a_off = r * ldx_bytes + k_bytes + (s ^ ((r / kRpb) % kCpr)) * 16;
-    const uint32_t b_off = r * ldw_bytes + k_bytes + (s ^ (((kBM + r) / kRpb) % kCpr)) * 16;
+    const uint32_t r = (wave * kInst + j) * kRows + sub;
+    o.a[j] = r * ldx_bytes + (s ^ ((r / kRpb) % kCpr)) * 16;
+    o.b[j] = r * ldw_bytes + (s ^ (((kBM + r) / kRpb) % kCpr)) * 16;
+  }
+  return o;
+}
+
+// One K step of the block's A and B tiles into a stage, this wave's share.
+// Rows past the end of x or w fall outside their descriptors (the row's own
+// offset already does, whatever the step's) and arrive as zeros.
+template <class G>
+__device__ __forceinline__ void dma_tile(Rsrc ra, Rsrc rb, const DmaOffsets<G>& o,
+                                         uint32_t k_bytes, uint8_t* stage, uint32_t wave) {
+  constexpr uint32_t kRows = G::kInstRows, kRowBytes = G::kRowBytes, kBM = G::BM;
+  constexpr int kInst = G::kAInst;
+#pragma unroll
+  for (int j = 0; j < kInst; ++j) {
+    const uint32_t R = (wave * kInst + j) * kRows;
+    const uint32_t va = o.a[j], vb = o.b[j];     // (locals: the host pass rejects members here)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        ra, (__attribute__((address_space(3))) void*)(stage + R * kRowBytes), 16, a_off, 0, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        rb, (__attribute__((address_space(3))) void*)(stage + (kBM + R) * kRowBytes), 16, b_off, 0,
+        ra, (__attribute__((address_space(3))) void*)(stage + R * kRowBytes), 16, va, k_bytes,
         0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rb, (__attribute__((address_space(3))) void*)(stage + (kBM + R) * kRowBytes), 16, vb,
+        k_bytes, 0, 0);
   }
 }
 
@@ -103,13 +137,55 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// A workgroup barrier with no release fence: __syncthreads() would make the
-// compiler wait for every outstanding load into LDS (vmcnt(0)), including the
-// ones meant to stay in flight.  The "memory" clobber keeps the compiler from
-// moving LDS accesses across it; the loads that must have landed are waited
-// for explicitly before it, and the fragment reads of the stage about to be
-// refilled have all completed (their MFMAs consumed them).
-__device__ __forceinline__ void stage_barrier() { asm volatile("s_barrier" ::: "memory"); }
+// A workgroup barrier that waits for this wave's LDS reads but not for its
+// loads into LDS: __syncthreads() would make the compiler wait for every
+// outstanding load (vmcnt(0)), including the ones meant to stay in flight.
+// The loads that must have landed are waited for explicitly before it.  The
+// lgkmcnt(0) matters: a fragment read still in flight at the barrier could
+// otherwise meet another wave's refill of the same stage issued after it.
+// The "memory" clobber keeps the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void stage_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+template <class G>
+__device__ __forceinline__ void read_frags(const uint8_t* st, uint32_t arow, uint32_t brow,
+                                           uint32_t k, bf16x8 (&a)[G::MB], bf16x8 (&b)[G::NB]) {
+#pragma unroll
+  for (int i = 0; i < G::MB; ++i) a[i] = sfrag<G>(st, arow + i * 32, k);
+#pragma unroll
+  for (int j = 0; j < G::NB; ++j) b[j] = sfrag<G>(st, brow + j * 32, k);
+}
+
+template <class G>
+__device__ __forceinline__ void mfma_step(f32x16 (&acc)[G::MB][G::NB], const bf16x8 (&a)[G::MB],
+                                          const bf16x8 (&b)[G::NB]) {
+#pragma unroll
+  for (int i = 0; i < G::MB; ++i)
+#pragma unroll
+    for (int j = 0; j < G::NB; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+}
+
+// Instruction order for the scheduler (sched_group_barrier masks: 0x008
+// MFMA, 0x020 vector memory read, 0x100 LDS read).  One MFMA, then R LDS
+// reads and V loads, NP times; then the remaining M MFMAs back to back.  With
+// one wave per SIMD nothing else hides a read's latency, so the reads feeding
+// the next sub-step go between this sub-step's MFMAs.
+template <int NP, int R, int V>
+__device__ __forceinline__ void sched_interleave() {
+  if constexpr (NP > 0) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if constexpr (R > 0) __builtin_amdgcn_sched_group_barrier(0x100, R, 0);
+    if constexpr (V > 0) __builtin_amdgcn_sched_group_barrier(0x020, V, 0);
+    sched_interleave<NP - 1, R, V>();
+  }
+}
+
+template <int M>
+__device__ __forceinline__ void sched_mfmas() {
+  if constexpr (M > 0) __builtin_amdgcn_sched_group_barrier(0x008, M, 0);
+}
 
 template <class G, int D>
 __global__ __launch_bounds__(G::kThreads) void qkv_proj_kernel(
@@ -122,7 +198,20 @@ __global__ __launch_bounds__(G::kThreads) void qkv_proj_kernel(
   const uint32_t tid = threadIdx.x, lane = tid & 63;
   const uint32_t wave = uniform(tid >> 6);
   const uint32_t wm = wave / G::WN, wn = wave % G::WN;
-  const uint32_t n0 = blockIdx.x * G::BN, m0 = blockIdx.y * G::BM;
+  // Tile order.  Workgroups go to the 8 XCDs round robin (id % 8), each XCD
+  // with its own L2; the remap gives each XCD a contiguous run of tiles, and
+  // the runs walk the output in bands of GM tile rows, columns outer, so the
+  // blocks an XCD holds at once share a few A and B panels in its L2.
+  const uint32_t n_tiles = (N + G::BN - 1) / G::BN, m_tiles = (T + G::BM - 1) / G::BM;
+  uint32_t id = blockIdx.x;
+  if (kXcdRemap) {
+    const uint32_t q = gridDim.x / 8, r = gridDim.x % 8, xcd = id % 8;
+    id = xcd * q + (xcd < r ? xcd : r) + id / 8;
+  }
+  const uint32_t band = id / (kGroupM * n_tiles), first_m = band * kGroupM;
+  const uint32_t gm = m_tiles - first_m < kGroupM ? m_tiles - first_m : kGroupM;
+  const uint32_t within = id - band * kGroupM * n_tiles;
+  const uint32_t n0 = (within / gm) * G::BN, m0 = (first_m + within % gm) * G::BM;
 
   const uint32_t a_rows = T - m0 < (uint32_t)G::BM ? T - m0 : (uint32_t)G::BM;
   const uint32_t b_rows = N - n0 < (uint32_t)G::BN ? N - n0 : (uint32_t)G::BN;
@@ -137,48 +226,60 @@ __global__ __launch_bounds__(G::kThreads) void qkv_proj_kernel(
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-  // K steps rotate through S stages: while step k computes, the loads of
-  // steps k+1 .. k+S-1 are in flight (step k+S-1's issued at the top of step
-  // k, into the stage step k-1 used).  Before the barrier that ends step k a
-  // wave waits until at most (S-2) steps of its loads are outstanding, i.e.
-  // step k+1's have landed; the barrier makes everyone's visible.  Loads past
-  // the last step fetch the last step again (unused), so the count is exact.
+  // Two LDS stages; K step ks computes from stage ks % 2.  Fragments are
+  // double-buffered in registers: the reads of sub-step kk+1 are issued
+  // before the MFMAs of sub-step kk.  Before the last sub-step of a step the
+  // wave waits for its loads of step ks+1 (into the other stage) and meets
+  // the barrier; after it, the stage just finished is free (every wave's
+  // reads of it have completed), so the loads of step ks+2 go there, and the
+  // first fragments of step ks+1 are read while the last MFMAs of step ks
+  // run.  Loads past the last step fetch the last step again (unused).
+  static_assert(G::S == 2 && BK % 32 == 0, "two stages, an even number of 16-wide sub-steps");
+  constexpr int KK = BK / 16;
   const uint32_t ksteps = K / BK;
-#pragma unroll
-  for (int st = 0; st < G::S - 1; ++st)
-    dma_tile<G>(ra, ldx_bytes, rb, ldw_bytes, step_bytes<G>(st, ksteps), smem + st * G::kStageBytes,
-                wave, lane);
-  wait_vmcnt<(G::S - 2) * G::kLoads>();         // step 0 has landed (this wave)
-  stage_barrier();                              // (and everyone's)
-
   // a lane's fragment: row (lane % 32) of a 32-row block, 8 consecutive k
   // starting at 8*(lane/32) of each 16-wide MFMA step; A and B use the same
   // k order, so the products pair correctly whatever order the hardware sums
   const uint32_t fr = lane % 32, fk = 8 * (lane / 32);
   const uint32_t arow = wm * G::kWaveM + fr, brow = G::BM + wn * G::kWaveN + fr;
-  uint32_t cur = 0;                             // stage of step ks
+  uint8_t* const stage0 = smem;
+  uint8_t* const stage1 = smem + G::kStageBytes;
+
+  const DmaOffsets<G> doff = dma_offsets<G>(ldx_bytes, ldw_bytes, wave, lane);
+  dma_tile<G>(ra, rb, doff, step_bytes<G>(0, ksteps), stage0, wave);
+  wait_vmcnt<0>();
+  stage_barrier();
+  dma_tile<G>(ra, rb, doff, step_bytes<G>(1, ksteps), stage1, wave);
+  bf16x8 fa[2][MB], fb[2][NB];
+  read_frags<G>(stage0, arow, brow, fk, fa[0], fb[0]);
+
+  constexpr int kReads = MB + NB, kMfma = MB * NB;
+  static_assert(kMfma > kReads && G::kLoads % (kMfma - kReads) == 0, "");
   for (uint32_t ks = 0; ks < ksteps; ++ks) {
-    const uint8_t* st = smem + cur * G::kStageBytes;
-    // step ks+S-1 goes into the stage step ks-1 used (read before its barrier)
-    const uint32_t nxt = cur == 0 ? G::S - 1 : cur - 1;
-    dma_tile<G>(ra, ldx_bytes, rb, ldw_bytes, step_bytes<G>(ks + G::S - 1, ksteps),
-                smem + nxt * G::kStageBytes, wave, lane);
+    uint8_t* const st = (ks & 1) ? stage1 : stage0;
+    uint8_t* const nx = (ks & 1) ? stage0 : stage1;
 #pragma unroll
-    for (uint32_t kk = 0; kk < (uint32_t)BK; kk += 16) {
-      bf16x8 a[MB], b[NB];
-#pragma unroll
-      for (int i = 0; i < MB; ++i) a[i] = sfrag<G>(st, arow + i * 32, kk + fk);
-#pragma unroll
-      for (int j = 0; j < NB; ++j) b[j] = sfrag<G>(st, brow + j * 32, kk + fk);
-#pragma unroll
-      for (int i = 0; i < MB; ++i)
-#pragma unroll
-        for (int j = 0; j < NB; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+    for (int kk = 0; kk < KK - 1; ++kk) {
+      read_frags<G>(st, arow, brow, (kk + 1) * 16 + fk, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
+      mfma_step<G>(acc, fa[kk & 1], fb[kk & 1]);
+      sched_interleave<kReads, 1, 0>();
+      sched_mfmas<kMfma - kReads>();
+      __builtin_amdgcn_sched_barrier(0);
     }
-    wait_vmcnt<(G::S - 2) * G::kLoads>();
-    stage_barrier();
-    cur = cur + 1 == (uint32_t)G::S ? 0 : cur + 1;
+    wait_vmcnt<0>();                            // step ks+1 has landed (this wave)
+    stage_barrier();                            // (and everyone's); stage st is free
+    __builtin_amdgcn_sched_barrier(0);
+    // the reads come first: the compiler cannot tell that the loads into
+    // stage st do not overlap stage nx, so it keeps them in source order
+    read_frags<G>(nx, arow, brow, fk, fa[0], fb[0]);
+    dma_tile<G>(ra, rb, doff, step_bytes<G>(ks + 2, ksteps), st, wave);
+    mfma_step<G>(acc, fa[1], fb[1]);
+    sched_interleave<kReads, 1, 0>();
+    sched_interleave<kMfma - kReads, 0, G::kLoads / (kMfma - kReads)>();
+    // keeps the reads above in this iteration: without it the compiler merges
+    // them with the reads before the loop into one read at the top of the
+    // loop, which then waits for its result before the first MFMA
+    asm volatile("" ::: "memory");
   }
   // the output tile reuses the stages: every load into LDS must be done
   __builtin_amdgcn_s_waitcnt(0);
@@ -253,18 +354,24 @@ __global__ __launch_bounds__(G::kThreads) void qkv_proj_kernel(
 
 // 256 x 256 tiles of 8 waves (4 along M, 2 along N), each wave 64 x 128:
 // 0.75 fragment reads per MFMA and 131 flop per byte of operand staged, the
-// best of the shapes measured on MI355X (128 x 128 with 64 x 64 waves,
-// 256 x 128 and 128 x 256 with 4 waves, 256 x 128 with BK = 32).  Among the
-// pipelines measured, BK = 64 with two stages beat BK = 32 with three or four
-// (fewer barriers outweigh the shorter prefetch).
+// best of the shapes measured on MI355X.  The others measured: 128 x 128 with
+// 64 x 64 waves; 256 x 128 and 128 x 256 with 4 waves; 256 x 256 with 4
+// waves of 128 x 128 (one wave per SIMD, 0.5 reads per MFMA, but about 7 %
+// slower: with no second wave on the SIMD every latency shows); BK = 32 with
+// three or four stages (more barriers outweigh the longer prefetch).  An L2
+// prefetch of later K steps (a 4-byte load per operand row) cost about 9 %:
+// it doubles the vector-memory requests per step.
 #ifndef QKNORM_PROJ_BK
 #define QKNORM_PROJ_BK 64
 #endif
-#ifndef QKNORM_PROJ_STAGES
-#define QKNORM_PROJ_STAGES 2
+#ifndef QKNORM_PROJ_WM
+#define QKNORM_PROJ_WM 4
 #endif
-using Geo = Tile<256, 256, 4, 2, QKNORM_PROJ_BK, QKNORM_PROJ_STAGES>;
-constexpr int kBM = Geo::BM, kBN = Geo::BN, kBK = Geo::BK, kThreads = Geo::kThreads;
+#ifndef QKNORM_PROJ_WN
+#define QKNORM_PROJ_WN 2
+#endif
+using Geo = Tile<256, 256, QKNORM_PROJ_WM, QKNORM_PROJ_WN, QKNORM_PROJ_BK, 2>;
+constexpr int kBM = Geo::BM, kBN = Geo::BN, kThreads = Geo::kThreads;
 constexpr int kLdsBytes = Geo::kLdsBytes;
 
 }  // namespace
@@ -275,12 +382,17 @@ bool proj_shape_ok(const ProjArgs& a) {
   return (uint64_t)kBM * a.ldx * es < (UINT64_C(1) << 31) &&
          (uint64_t)kBN * a.ldw * es < (UINT64_C(1) << 31) &&
          (uint64_t)kBM * a.ld * es < (UINT64_C(1) << 31) && a.hidden % 64 == 0 &&
+         // the tiles are numbered in one grid dimension, whose size in
+         // threads must fit 32 bits
+         (uint64_t)((a.T + kBM - 1) / kBM) * (uint64_t)(((a.hq + 2 * a.hkv) * a.head_dim + kBN - 1) / kBN) *
+                 (uint64_t)kThreads <
+             (UINT64_C(1) << 32) &&
          (a.head_dim == 64 || a.head_dim == 128);
 }
 
 hipError_t launch_qkv_proj(const ProjArgs& a, hipStream_t s) {
   const uint32_t N = (uint32_t)((a.hq + 2 * a.hkv) * a.head_dim);
-  const dim3 grid((N + kBN - 1) / kBN, (uint32_t)((a.T + kBM - 1) / kBM));
+  const dim3 grid((uint32_t)(((N + kBN - 1) / kBN) * ((a.T + kBM - 1) / kBM)));
   auto kern = a.head_dim == 64 ? qkv_proj_kernel<Geo, 64> : qkv_proj_kernel<Geo, 128>;
   // more than the default 64 KiB of dynamic LDS (gfx950 has 160 KiB per CU);
   // a host-side attribute, set on every call (no shared state between threads)
