@@ -584,6 +584,153 @@ __global__ __launch_bounds__(512) void layerwise_stream_kernel(
   }
 }
 
+// --- one wave per row (fused layerwise, regular shard geometry) -------------
+//
+// A region of 64*NS vectors is NS slots of 64 consecutive vectors: lane l
+// holds vector 64*j + l in slot j, so each slot is one coalesced 1 KiB load.
+// A shard of svecs vectors is either a run of m = svecs/64 whole slots, or,
+// when svecs divides 64, one of G = 64/svecs lane groups of a slot.  Either
+// way the lanes of a shard hold the vectors that lanes 0..svecs-1 hold in the
+// block kernel, in the same order, and the reduction is the same tree (a
+// narrow shard's group sum is the block kernel's 64-lane sum with zero lanes
+// left out), so the partials, their in-order combine and the outputs are the
+// same bits.  No barrier and no LDS traffic between waves: gamma is staged
+// once per block in LDS and every wave then walks its own rows.
+
+struct WaveShards {
+  uint32_t m;       // slots per shard (1 when shards are narrower than a slot)
+  uint32_t svecs;   // vectors per shard
+  uint32_t G;       // shards per slot (1 when a shard spans whole slots)
+};
+
+// Sum over aligned groups of lg lanes, lg = 1, 2, 4, .., 64 (wave-uniform).
+__device__ __forceinline__ float group_sum_n(float v, uint32_t lg) {
+  switch (lg) {
+    case 1: return v;
+    case 2: return group_sum<2>(v);
+    case 4: return group_sum<4>(v);
+    case 8: return group_sum<8>(v);
+    case 16: return group_sum<16>(v);
+    case 32: return group_sum<32>(v);
+    default: return group_sum<64>(v);
+  }
+}
+
+// The region's sum of squares: shard partials combined in shard order,
+// ((p0 + p1) + p2) + ..., wave-uniform.
+template <int DT, int NS>
+__device__ __forceinline__ float wave_region_sumsq(const u32x4 (&x)[NS], WaveShards w) {
+  using IO = IoTraits<DT>;
+  const uint32_t lanes = w.svecs < 64 ? w.svecs : 64;
+  float s = 0.f, acc = 0.f;
+  uint32_t k = 0;                              // slot within the current shard
+#pragma unroll
+  for (int j = 0; j < NS; ++j) {
+    float f[IO::kElems];
+    unpack<DT>(x[j], f);
+    acc = vec_sumsq<DT>(f, k == 0 ? 0.f : acc);
+    if (++k == w.m) {
+      const float ps = group_sum_n(acc, lanes);
+      for (uint32_t g = 0; g < w.G; ++g)
+        s += __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ps),
+                                                                 (int)(g * w.svecs)));
+      k = 0;
+    }
+  }
+  return s;
+}
+
+// Apply to slot j of the row in `rs` and store it, then load slot j of the
+// next row (descriptor `rn`, empty past the last row) into the same registers,
+// so the next row's loads go out while this row is still being written.
+template <int DT, int NS>
+__device__ __forceinline__ void wave_region_apply(Rsrc rs, Rsrc rn, uint32_t reg_off, u32x4 (&x)[NS],
+                                                  const u32x4* __restrict__ g_lds, uint32_t lane,
+                                                  float scale, bool may_exceed) {
+  using IO = IoTraits<DT>;
+  constexpr int GV = Gam<DT>::kVecs;
+#pragma unroll
+  for (int j = 0; j < NS; ++j) {
+    const uint32_t v = j * 64 + lane;
+    Gam<DT> gw;
+#pragma unroll
+    for (int q = 0; q < GV; ++q) gw.v[q] = g_lds[v * GV + q];
+    float f[IO::kElems], g[IO::kElems], y[IO::kElems];
+    unpack<DT>(x[j], f);
+    unpack_gamma<DT>(gw, g);
+#pragma unroll
+    for (int e = 0; e < IO::kElems; ++e) y[e] = (f[e] * g[e]) * scale;
+    stream_store(rs, reg_off + v * 16, pack<DT>(y, may_exceed));
+    x[j] = stream_load(rn, reg_off + v * 16);
+  }
+}
+
+// Largest |gamma| over this lane's vectors of a region.
+template <int DT, int NS>
+__device__ __forceinline__ float wave_gamma_max(const u32x4* __restrict__ g_lds, uint32_t lane) {
+  constexpr int GV = Gam<DT>::kVecs;
+  float m = 0.f;
+#pragma unroll
+  for (int j = 0; j < NS; ++j) {
+    Gam<DT> gw;
+#pragma unroll
+    for (int q = 0; q < GV; ++q) gw.v[q] = g_lds[(j * 64 + lane) * GV + q];
+    float g[IoTraits<DT>::kElems];
+    unpack_gamma<DT>(gw, g);
+    m = abs_max(g, m);
+  }
+  return m;
+}
+
+#ifndef QKNORM_LWW_BLOCK
+#define QKNORM_LWW_BLOCK 256         // threads per block of the one-wave-per-row kernel
+#endif
+
+// NQ, NK: slots of Q and of K (64 vectors each).  Rows: wave w of the grid
+// takes rows w, w + (waves in the grid), ...
+template <int DT, int NQ, int NK>
+__global__ __launch_bounds__(QKNORM_LWW_BLOCK) void layerwise_wave_kernel(
+    uint8_t* __restrict__ qkv, RowGeom G, WaveShards wq, WaveShards wk,
+    const uint8_t* __restrict__ gamma_q, const uint8_t* __restrict__ gamma_k, float eps) {
+  constexpr uint32_t GV = Gam<DT>::kVecs;
+  constexpr uint32_t kQg = NQ * 64 * GV, kKg = NK * 64 * GV;   // 16-byte gamma vectors
+  extern __shared__ u32x4 g_lds[];             // gamma_q, then gamma_k
+  const uint32_t lane = threadIdx.x & 63;
+  for (uint32_t i = threadIdx.x; i < kQg; i += blockDim.x) g_lds[i] = load16(gamma_q + i * 16);
+  for (uint32_t i = threadIdx.x; i < kKg; i += blockDim.x) g_lds[kQg + i] = load16(gamma_k + i * 16);
+  __syncthreads();
+  bool exceed_q = true, exceed_k = true;
+  if constexpr (DT == kFP8) {
+    exceed_q = e4m3_may_exceed(wave_gamma_max<DT, NQ>(g_lds, lane), G.inv_wq);
+    exceed_k = e4m3_may_exceed(wave_gamma_max<DT, NK>(g_lds + kQg, lane), G.inv_wk);
+  }
+  const uint32_t waves = gridDim.x * (blockDim.x >> 6);
+  const uint32_t k_off = G.q_vecs * 16;
+  const uint32_t qk_vecs = G.q_vecs + G.k_vecs;
+  uint32_t t = uniform(blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6));
+  Rsrc rs = row_rsrc(qkv, G.ld_bytes, t < G.T ? t : 0, t < G.T ? qk_vecs : 0);
+  u32x4 xq[NQ], xk[NK];
+#pragma unroll
+  for (int j = 0; j < NQ; ++j) xq[j] = stream_load(rs, (j * 64 + lane) * 16);
+#pragma unroll
+  for (int j = 0; j < NK; ++j) xk[j] = stream_load(rs, k_off + (j * 64 + lane) * 16);
+  for (; t < G.T; t += waves) {
+    const uint32_t tn = t + waves;
+    const Rsrc rn = row_rsrc(qkv, G.ld_bytes, tn < G.T ? tn : 0, tn < G.T ? qk_vecs : 0);
+    const float rq = rms_scale(wave_region_sumsq<DT, NQ>(xq, wq), G.inv_wq, eps);
+    const float rk = rms_scale(wave_region_sumsq<DT, NK>(xk, wk), G.inv_wk, eps);
+    // keep the row packed between the two passes: without these the compiler
+    // reuses the first pass's widened values and holds the whole row in fp32
+#pragma unroll
+    for (int j = 0; j < NQ; ++j) asm volatile("" : "+v"(xq[j]));
+#pragma unroll
+    for (int j = 0; j < NK; ++j) asm volatile("" : "+v"(xk[j]));
+    wave_region_apply<DT, NQ>(rs, rn, 0, xq, g_lds, lane, rq, exceed_q);
+    wave_region_apply<DT, NK>(rs, rn, k_off, xk, g_lds + kQg, lane, rk, exceed_k);
+    rs = rn;
+  }
+}
+
 // Phase A.  A wave takes one shard of one region (Q or K) over a block of 32
 // consecutive rows and ends with lane j holding the partial of row t0 + j,
 // stored with one coalesced 128-byte write at part[r*T + t0 ...].  (32 rows
@@ -596,16 +743,6 @@ __global__ __launch_bounds__(512) void layerwise_stream_kernel(
 // 64/LG rows per step; lane i of a group takes vector i, and the LG-lane sum
 // equals the 64-lane sum of the fused kernel bit for bit, because the lanes it
 // leaves out hold exact zeros (x + 0 == x).
-__device__ __forceinline__ float group_sum_n(float v, uint32_t lg) {
-  switch (lg) {                                // wave-uniform
-    case 2: return group_sum<2>(v);
-    case 4: return group_sum<4>(v);
-    case 8: return group_sum<8>(v);
-    case 16: return group_sum<16>(v);
-    case 32: return group_sum<32>(v);
-    default: return group_sum<64>(v);
-  }
-}
 
 constexpr uint32_t kRowBlock = 32;
 
@@ -950,9 +1087,78 @@ static hipError_t launch_lw_regs_k(const RowGeom& G, uint32_t nw, int kc, const 
   }
 }
 
+// The one-wave-per-row kernel serves FP8 rows: on the [32768, 10240] prefill
+// rows it takes 101 us against the block kernel's 112 us.  For bf16 rows it
+// measured 213-226 us against 198 us (at 8 to 128 waves per CU, with or
+// without the next row's loads overlapping the stores), so 16- and 32-bit rows
+// keep the block kernel.  One row per wave measured best (128 waves per CU).
+#ifndef QKNORM_LWW_WAVES_PER_CU
+#define QKNORM_LWW_WAVES_PER_CU 128  // grid cap of the one-wave-per-row kernel
+#endif
+#ifndef QKNORM_LWW
+#define QKNORM_LWW 1                 // 0: FP8 rows take the block-per-row kernels too
+#endif
+static constexpr bool kLwWave = QKNORM_LWW != 0;
+
+// The shard layout of a region for the one-wave-per-row kernel, if it has one.
+static bool wave_shards(uint32_t vecs, uint32_t svecs, WaveShards* w) {
+  if (vecs == 0 || vecs % 64 != 0) return false;
+  if (svecs % 64 == 0) {
+    *w = WaveShards{svecs / 64, svecs, 1};
+    return true;
+  }
+  if (64 % svecs == 0) {
+    *w = WaveShards{1, svecs, 64 / svecs};
+    return true;
+  }
+  return false;
+}
+
+template <int DT, int NQ, int NK>
+static hipError_t launch_lw_wave(const RowGeom& G, WaveShards wq, WaveShards wk,
+                                 const LayerwiseArgs& a, hipStream_t s, int cus) {
+  constexpr uint32_t kWaves = QKNORM_LWW_BLOCK / 64;
+  uint64_t waves = (uint64_t)cus * QKNORM_LWW_WAVES_PER_CU;
+  if (waves > G.T) waves = G.T;
+  const uint32_t blocks = (uint32_t)((waves + kWaves - 1) / kWaves);
+  const size_t lds = (size_t)(NQ + NK) * 64 * Gam<DT>::kVecs * 16;
+  hipLaunchKernelGGL((layerwise_wave_kernel<DT, NQ, NK>), dim3(blocks), dim3(QKNORM_LWW_BLOCK), lds,
+                     s, (uint8_t*)a.qkv, G, wq, wk, (const uint8_t*)a.gamma_q,
+                     (const uint8_t*)a.gamma_k, a.eps);
+  return hipGetLastError();
+}
+
+// The slot counts (Q, K) the one-wave-per-row kernel is built for.
+#define QKNORM_LWW_SHAPES(X) X(4, 1) X(8, 1) X(8, 2) X(16, 2) X(16, 4)
+
+// Whether the one-wave-per-row kernel takes this geometry.
+static bool lw_wave_fits(const RowGeom& G, WaveShards* wq, WaveShards* wk) {
+  if (!wave_shards(G.q_vecs, G.q_svecs, wq) || !wave_shards(G.k_vecs, G.k_svecs, wk)) return false;
+  const uint32_t nq = G.q_vecs / 64, nk = G.k_vecs / 64;
+#define QKNORM_LWW_FITS(Q, K) if (nq == Q && nk == K) return true;
+  QKNORM_LWW_SHAPES(QKNORM_LWW_FITS)
+#undef QKNORM_LWW_FITS
+  return false;
+}
+
+template <int DT>
+static hipError_t launch_lw_wave_dt(const RowGeom& G, WaveShards wq, WaveShards wk,
+                                    const LayerwiseArgs& a, hipStream_t s, int cus) {
+  const uint32_t nq = G.q_vecs / 64, nk = G.k_vecs / 64;
+#define QKNORM_LWW_LAUNCH(Q, K) \
+  if (nq == Q && nk == K) return launch_lw_wave<DT, Q, K>(G, wq, wk, a, s, cus);
+  QKNORM_LWW_SHAPES(QKNORM_LWW_LAUNCH)
+#undef QKNORM_LWW_LAUNCH
+  return hipErrorInvalidValue;                 // not reached: lw_wave_fits() was checked
+}
+
 template <int DT>
 static hipError_t launch_layerwise_dt(const LayerwiseArgs& a, hipStream_t s, int cus) {
   const RowGeom G = make_geom(a.T, a.ld, a.wq, a.wk, a.nshards, IoTraits<DT>::kBytes);
+  if constexpr (DT == kFP8 && kLwWave) {
+    WaveShards wq, wk;
+    if (lw_wave_fits(G, &wq, &wk)) return launch_lw_wave_dt<DT>(G, wq, wk, a, s, cus);
+  }
   uint32_t nw, qv, kv;
   layerwise_shape(G, &nw, &qv, &kv);
   const int qc = slot_class(qv), kc = slot_class(kv);

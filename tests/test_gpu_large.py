@@ -9,14 +9,17 @@ import torch
 import oracle
 import qk_norm_amd as q
 from qk_norm_amd import synth
-from gpu_util import (assert_bytes_equal, assert_close_to_oracle, device_to_host, host_rows,
-                      host_to_device, sample_rows, upload_rows)
+from gpu_util import (assert_bytes_equal, assert_close_to_oracle, device_to_host, gamma_to_device,
+                      host_rows, host_to_device, sample_rows, upload_rows)
 
 pytestmark = pytest.mark.gpu
 
 
 def _gather(t, rows, dtype):
-    return device_to_host(t[torch.from_numpy(rows).cuda()], dtype)
+    # index a same-size integer view (row gathers of float8 tensors are not
+    # implemented everywhere)
+    view = {1: torch.uint8, 2: torch.int16, 4: torch.int32}[t.element_size()]
+    return device_to_host(t.view(view)[torch.from_numpy(rows).cuda()].view(t.dtype), dtype)
 
 
 @pytest.mark.parametrize("layout", ["standalone", "fused"])
@@ -46,17 +49,23 @@ def test_per_head_multi_trip(layout):
         assert torch.equal(x[:, qk:].view(torch.int16), v0.view(torch.int16)), "V changed"
 
 
-def test_layerwise_many_rows_per_block_and_partials_grid_stride():
+@pytest.mark.parametrize("dtype,T,wq,wk,ld,R", [
     # 262144 rows of [Q 1024 | K 128 | V 128]: the fused kernel's blocks walk
     # ~21 rows each, and phase A has more row blocks than waves in its grid
-    dtype, T, wq, wk, ld, R = synth.BF16, 262144, 1024, 128, 1280, 8
+    (synth.BF16, 262144, 1024, 128, 1280, 8),
+    # FP8 rows of [Q 4096 | K 1024 | V 1024]: more rows than the one-wave-per-row
+    # kernel has waves on MI355X (32768), so waves take a second row, loaded
+    # while the first is stored
+    (synth.F8, 40000, 4096, 1024, 6144, 8),
+])
+def test_layerwise_many_rows_per_block_and_partials_grid_stride(dtype, T, wq, wk, ld, R):
     seed = 62
-    print(f"[large layerwise] T={T} wq={wq} wk={wk} R={R}", flush=True)
+    print(f"[large layerwise] {synth.DTYPE_NAMES[dtype]} T={T} wq={wq} wk={wk} R={R}", flush=True)
     x0 = upload_rows(seed, T, ld, dtype, outlier_frac=0.01)
     gq = synth.make_gamma(seed, 3, wq, dtype)
     gk = synth.make_gamma(seed, 4, wk, dtype)
     eps = synth.eps_f32(1e-6)
-    dq, dk = host_to_device(gq, dtype), host_to_device(gk, dtype)
+    dq, dk = gamma_to_device(gq, dtype), gamma_to_device(gk, dtype)
     rows = sample_rows(T)
     xs = host_rows(seed, rows, ld, dtype, outlier_frac=0.01)
     # fused
@@ -66,7 +75,7 @@ def test_layerwise_many_rows_per_block_and_partials_grid_stride():
     y64, _ = oracle.layerwise(xs, dtype, wq, wk, gq, gk, eps, R)
     assert_close_to_oracle(_gather(x, rows, dtype)[:, :wq + wk], y64[:, :wq + wk], dtype,
                            label="large layerwise fused")
-    assert torch.equal(x[:, wq + wk:].view(torch.int16), x0[:, wq + wk:].view(torch.int16))
+    assert torch.equal(x[:, wq + wk:].view(torch.uint8), x0[:, wq + wk:].view(torch.uint8))
     # two-phase: same bits everywhere, partials match the oracle on the sampled rows
     x2 = x0.clone()
     pq = torch.empty(R, T, dtype=torch.float32, device="cuda")
@@ -74,7 +83,7 @@ def test_layerwise_many_rows_per_block_and_partials_grid_stride():
     q.qknorm_partial_sumsq(x2, wq, wk, R, pq, pk)
     q.qknorm_apply_scalar(x2, wq, wk, pq, pk, wq, wk, dq, dk, eps)
     torch.cuda.synchronize()
-    assert torch.equal(x2.view(torch.int16), x.view(torch.int16)), "two-phase != fused"
+    assert torch.equal(x2.view(torch.uint8), x.view(torch.uint8)), "two-phase != fused"
     oq, ok = oracle.partials(xs, dtype, wq, wk, R)
     idx = torch.from_numpy(rows).cuda()
     for got, ref in ((pq[:, idx], oq), (pk[:, idx], ok)):
