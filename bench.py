@@ -17,8 +17,9 @@ Reported (one JSON line):
   cases          the T=32768 large-prefill case (layerwise fused, two-phase,
                  per-head), fused GQA T=8192, and decode-size launch floors
 
-Every case first keeps the GPU busy for 0.1 s of untimed launches (clock
-warm-up after idle), then runs its W warm-up steps, then times its K steps.
+Every bandwidth and projection case first keeps the GPU busy for 0.1 s of
+untimed launches (clock warm-up after idle), then runs its W warm-up steps,
+then times its K steps.
 
 Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--quick] [--no-cpu]
 """
@@ -136,8 +137,10 @@ class Timer:
 
 # After an idle spell MI355X runs this kernel about 3 % slower for the first
 # ~10 ms of continuous work (measured: 17.0-17.4 us per launch, settling at
-# 16.5-16.6 us).  Every case therefore keeps the GPU busy with untimed launches
-# for CLOCK_WARM_S of wall time before its W warm-up steps and K timed steps.
+# 16.5-16.6 us).  Every bandwidth and projection case therefore keeps the GPU
+# busy with untimed launches for CLOCK_WARM_S of wall time before its W
+# warm-up steps and K timed steps.  (The decode case measures single-launch
+# latency with fixed call counts and has no such phase.)
 CLOCK_WARM_S = 0.1
 
 
@@ -329,7 +332,6 @@ def bench_decode(q, torch, dev, reps=200):
     out = []
 
     def measure(launch):
-        warm_clocks(torch, lambda _i: launch())
         for _ in range(20):
             launch()
         torch.cuda.synchronize()
