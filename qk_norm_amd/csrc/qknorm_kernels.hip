@@ -16,7 +16,7 @@
 #define QKNORM_PH_BLOCKS_PER_CU 160 // per-head grid cap, blocks per CU (one trip for most sizes)
 #endif
 #ifndef QKNORM_LW_WAVES_PER_CU
-#define QKNORM_LW_WAVES_PER_CU 384   // layerwise grid cap, waves per CU
+#define QKNORM_LW_WAVES_PER_CU 512   // layerwise grid cap, waves per CU
 #endif
 
 namespace qknorm {
@@ -889,7 +889,6 @@ __global__ __launch_bounds__(512) void apply_scalar_kernel(
     const float* __restrict__ part_q, const float* __restrict__ part_k, uint32_t nparts,
     float inv_norm_wq, float inv_norm_wk, const uint8_t* __restrict__ gamma_q,
     const uint8_t* __restrict__ gamma_k, float eps) {
-  using IO = IoTraits<DT>;
   __shared__ float scale[2][kApplyRows];
   const uint32_t tid = threadIdx.x, nt = blockDim.x;
   const uint32_t nv = q_vecs + k_vecs;
