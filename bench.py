@@ -198,7 +198,7 @@ def bench_per_head(q, torch, dev, p, steps, warmup, label):
             "gbs": bytes_alg / (mean_us * 1e-6) / 1e9}
 
 
-def bench_layerwise(q, torch, dev, p, steps, warmup, label="cfg5"):
+def bench_layerwise(q, torch, dev, p, steps, warmup, label="prefill"):
     from qk_norm_amd import synth
     lib = q.load()
     es, ges = sizes(p)
@@ -359,7 +359,7 @@ def bench_decode(q, torch, dev, reps=200):
         return host_us, gpu_us, e0.elapsed_time(e1) * 1e3 / reps
 
     for T in (1, 8, 16, 64, 128):
-        p = synth.cfg2(T=T, H=48)
+        p = synth.standalone_heads(T=T, H=48)
         x = to_device(p.x, p.dtype, torch, dev)
         g = to_device(p.gamma_q, p.dtype, torch, dev)
         h, gpu, gr = measure(lambda: q.qknorm_per_head(x, 48, 0, 128, g, None, p.eps))
@@ -367,7 +367,7 @@ def bench_decode(q, torch, dev, reps=200):
                     "gpu_us_per_launch_back_to_back": gpu, "graph_us_per_launch": gr})
         log(f"decode per-head T={T}: host {h:.2f} us, back-to-back {gpu:.2f} us, graph {gr:.2f} us")
     for T in (1, 4, 32, 256):
-        p = synth.cfg4(T=T)
+        p = synth.layerwise_rows(T=T)
         x = to_device(p.x, p.dtype, torch, dev)
         gq = to_device(p.gamma_q, p.dtype, torch, dev)
         gk = to_device(p.gamma_k, p.dtype, torch, dev)
@@ -406,8 +406,8 @@ def main():
     ap.add_argument("--quick", action="store_true", help="headline case only")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--case", default="headline",
-                    choices=["headline", "cfg5_layerwise", "cfg5_per_head", "fp8_per_head",
-                             "fp8_cfg5_layerwise", "proj", "decode", "copy"],
+                    choices=["headline", "prefill_layerwise", "prefill_per_head", "fp8_per_head",
+                             "fp8_prefill_layerwise", "proj", "decode", "copy"],
                     help="single case for profiling runs")
     args = ap.parse_args()
 
@@ -435,19 +435,19 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"case": "copy", "bytes_read": n, "bytes_written": n}))
         return
-    if args.case == "cfg5_layerwise":
-        p = synth.cfg5(T=32768)
-        print(json.dumps({"case": "cfg5_layerwise", **bench_layerwise(q, torch, dev, p, args.steps, args.warmup)}))
+    if args.case == "prefill_layerwise":
+        p = synth.prefill_rows(T=32768)
+        print(json.dumps({"case": "prefill_layerwise", **bench_layerwise(q, torch, dev, p, args.steps, args.warmup)}))
         return
     if args.case == "fp8_per_head":
-        p = synth.cfg2(T=4096, H=48, dtype=synth.F8)
+        p = synth.standalone_heads(T=4096, H=48, dtype=synth.F8)
         print(json.dumps({"case": "fp8_per_head",
                           **bench_per_head(q, torch, dev, p, args.steps, args.warmup, "fp8 per-head")}))
         return
-    if args.case == "fp8_cfg5_layerwise":
-        p = synth.cfg5(T=32768, dtype=synth.F8)
-        print(json.dumps({"case": "fp8_cfg5_layerwise",
-                          **bench_layerwise(q, torch, dev, p, args.steps, args.warmup, "fp8 cfg5")}))
+    if args.case == "fp8_prefill_layerwise":
+        p = synth.prefill_rows(T=32768, dtype=synth.F8)
+        print(json.dumps({"case": "fp8_prefill_layerwise",
+                          **bench_layerwise(q, torch, dev, p, args.steps, args.warmup, "fp8 prefill [32768, 10240]")}))
         return
     if args.case == "decode":
         print(json.dumps({"case": "decode", "launches": bench_decode(q, torch, dev)}))
@@ -455,14 +455,14 @@ def main():
     if args.case == "proj":
         print(json.dumps({"case": "proj", **bench_proj(q, torch, dev, args.steps, args.warmup, T=8192)}))
         return
-    if args.case == "cfg5_per_head":
-        p = synth.cfg5(T=32768, mode="per_head")
-        print(json.dumps({"case": "cfg5_per_head",
-                          **bench_per_head(q, torch, dev, p, args.steps, args.warmup, "cfg5 per-head")}))
+    if args.case == "prefill_per_head":
+        p = synth.prefill_rows(T=32768, mode="per_head")
+        print(json.dumps({"case": "prefill_per_head",
+                          **bench_per_head(q, torch, dev, p, args.steps, args.warmup, "prefill [32768, 10240] per-head")}))
         return
 
     t_start = time.perf_counter()
-    p = synth.cfg2(T=4096, H=48)
+    p = synth.standalone_heads(T=4096, H=48)
     head = bench_per_head(q, torch, dev, p, args.steps, args.warmup, "headline per-head")
     bytes_alg = head["bytes"]
     value = bytes_alg * args.steps / head["wall_s"] / 1e9
@@ -490,22 +490,22 @@ def main():
     }
     if not args.quick:
         cases = {}
-        p5 = synth.cfg5(T=32768)
-        cases["cfg5_T32768_layerwise"] = bench_layerwise(q, torch, dev, p5, 50, 5)
-        p5h = synth.cfg5(T=32768, mode="per_head")
+        p5 = synth.prefill_rows(T=32768)
+        cases["prefill_T32768_layerwise"] = bench_layerwise(q, torch, dev, p5, 50, 5)
+        p5h = synth.prefill_rows(T=32768, mode="per_head")
         del p5
-        c = bench_per_head(q, torch, dev, p5h, 50, 5, "cfg5 per-head")
-        cases["cfg5_T32768_per_head"] = {k: c[k] for k in ("bytes", "mean_us", "gbs")}
+        c = bench_per_head(q, torch, dev, p5h, 50, 5, "prefill [32768, 10240] per-head")
+        cases["prefill_T32768_per_head"] = {k: c[k] for k in ("bytes", "mean_us", "gbs")}
         del p5h
-        c = bench_per_head(q, torch, dev, synth.cfg3(T=8192), 100, 10, "cfg3 fused GQA T=8192")
-        cases["cfg3_T8192_per_head"] = {k: c[k] for k in ("bytes", "mean_us", "gbs")}
+        c = bench_per_head(q, torch, dev, synth.fused_gqa_rows(T=8192), 100, 10, "fused GQA [8192, 6144] per-head")
+        cases["fused_gqa_T8192_per_head"] = {k: c[k] for k in ("bytes", "mean_us", "gbs")}
         for dt in (synth.F16, synth.F8):
             name = synth.DTYPE_NAMES[dt]
-            c = bench_per_head(q, torch, dev, synth.cfg2(T=4096, H=48, dtype=dt), 400, 40,
+            c = bench_per_head(q, torch, dev, synth.standalone_heads(T=4096, H=48, dtype=dt), 400, 40,
                                f"{name} per-head [4096, 48, 128]")
             cases[f"{name}_T4096_H48_per_head"] = {k: c[k] for k in ("bytes", "mean_us", "gbs")}
-        p8 = synth.cfg5(T=32768, dtype=synth.F8)
-        cases["fp8e4m3_cfg5_T32768_layerwise"] = bench_layerwise(q, torch, dev, p8, 50, 5,
+        p8 = synth.prefill_rows(T=32768, dtype=synth.F8)
+        cases["fp8e4m3_prefill_T32768_layerwise"] = bench_layerwise(q, torch, dev, p8, 50, 5,
                                                                  "fp8e4m3 [32768, 10240]")
         del p8
         cases["decode"] = bench_decode(q, torch, dev)

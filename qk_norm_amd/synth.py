@@ -272,43 +272,43 @@ def layerwise_problem(name, seed, dtype, T, wq, wk, ld, nshards, *, token_scale=
                    gamma_q=gq, gamma_k=gk, eps=eps_f32(eps), nshards=nshards, seed=seed)
 
 
-def cfg1(seed: int = 1) -> Problem:
+def small_fused_f32(seed: int = 1) -> Problem:
     """Per-head, fp32: [4, (16+2*4)*128], Hq=16, Hkv=4, D=128, N(0,1)."""
-    return per_head_problem("cfg1_per_head_f32", seed, F32, 4, 16, 4, 128)
+    return per_head_problem("fused_rows_per_head_f32_T4", seed, F32, 4, 16, 4, 128)
 
 
-def cfg2(T: int = 4096, H: int = 48, seed: int = 2, dtype: int = BF16) -> Problem:
+def standalone_heads(T: int = 4096, H: int = 48, seed: int = 2, dtype: int = BF16) -> Problem:
     """Per-head, bf16, standalone [T, H, 128]; N(0,1) times per-token U(0.1, 10)."""
-    return per_head_problem(f"cfg2_per_head_{DTYPE_NAMES[dtype]}_T{T}_H{H}", seed, dtype, T, H, 0,
-                            128, token_scale=(0.1, 10.0))
+    return per_head_problem(f"standalone_per_head_{DTYPE_NAMES[dtype]}_T{T}_H{H}", seed, dtype, T, H,
+                            0, 128, token_scale=(0.1, 10.0))
 
 
-def cfg3(T: int = 8192, seed: int = 3) -> Problem:
+def fused_gqa_rows(T: int = 8192, seed: int = 3) -> Problem:
     """Fused GQA per-head, bf16: [T, 6144] = Q 32x128 | K 8x128 | V 8x128."""
-    return per_head_problem(f"cfg3_fused_gqa_bf16_T{T}", seed, BF16, T, 32, 8, 128)
+    return per_head_problem(f"fused_gqa_per_head_bf16_T{T}", seed, BF16, T, 32, 8, 128)
 
 
-def cfg4(T: int = 256, seed: int = 4) -> Problem:
+def layerwise_rows(T: int = 256, seed: int = 4) -> Problem:
     """Layerwise via 8 shard partials, bf16: [T, 6144], Q 4096, K 1024, 1% outliers x20."""
-    return layerwise_problem(f"cfg4_layerwise_bf16_T{T}", seed, BF16, T, 4096, 1024, 6144, 8,
+    return layerwise_problem(f"layerwise_rows_bf16_T{T}", seed, BF16, T, 4096, 1024, 6144, 8,
                              outlier_frac=0.01)
 
 
-def cfg5(T: int = 32768, seed: int = 5, mode: str = "layerwise", row_start: int = 0,
-         dtype: int = BF16) -> Problem:
+def prefill_rows(T: int = 32768, seed: int = 5, mode: str = "layerwise", row_start: int = 0,
+                 dtype: int = BF16) -> Problem:
     """Large prefill: [T, 10240], Hq=64, Hkv=8, D=128; outliers x20 and per-token U(0.1, 10).
 
     Per-head and layerwise share x (same seed); only the gamma widths differ.
     """
     name = DTYPE_NAMES[dtype]
     if mode == "per_head":
-        return per_head_problem(f"cfg5_per_head_{name}_T{T}", seed, dtype, T, 64, 8, 128,
+        return per_head_problem(f"prefill_per_head_{name}_T{T}", seed, dtype, T, 64, 8, 128,
                                 token_scale=(0.1, 10.0), outlier_frac=0.01, row_start=row_start)
-    return layerwise_problem(f"cfg5_layerwise_{name}_T{T}", seed, dtype, T, 8192, 1024, 10240, 8,
+    return layerwise_problem(f"prefill_layerwise_{name}_T{T}", seed, dtype, T, 8192, 1024, 10240, 8,
                              token_scale=(0.1, 10.0), outlier_frac=0.01, row_start=row_start)
 
 
-CFG2_SWEEP_T = (1, 16, 128, 1024, 4096)
-CFG2_SWEEP_H = (16, 32, 48)
-CFG3_SWEEP_T = (1, 8, 64, 512, 8192)
-CFG4_SWEEP_T = (1, 4, 32, 256)
+STANDALONE_SWEEP_T = (1, 16, 128, 1024, 4096)
+STANDALONE_SWEEP_H = (16, 32, 48)
+FUSED_GQA_SWEEP_T = (1, 8, 64, 512, 8192)
+LAYERWISE_SWEEP_T = (1, 4, 32, 256)

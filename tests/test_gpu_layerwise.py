@@ -83,9 +83,9 @@ def full_check(p):
     return a
 
 
-@pytest.mark.parametrize("T", synth.CFG4_SWEEP_T)
-def test_cfg4_layerwise(T):
-    full_check(synth.cfg4(T=T))
+@pytest.mark.parametrize("T", synth.LAYERWISE_SWEEP_T)
+def test_layerwise_rows_sweep(T):
+    full_check(synth.layerwise_rows(T=T))
 
 
 @pytest.mark.parametrize("dtype", [synth.F32, synth.BF16, synth.F16, synth.F8])
@@ -113,7 +113,7 @@ def test_layerwise_shapes(dtype, wq, wk, R, T):
 
 def test_apply_scalar_alone_with_oracle_partials():
     # the apply phase on its own, fed fp32-rounded oracle partials
-    p = synth.cfg4(T=32)
+    p = synth.layerwise_rows(T=32)
     oq, ok = oracle.partials(p.x, p.dtype, p.wq, p.wk, p.nshards)
     fq, fk = oq.astype(np.float32), ok.astype(np.float32)
     buf = Guarded(p.x, p.dtype)
@@ -134,7 +134,7 @@ def test_tensor_parallel_emulation_matches_fused():
     its one-shard partial, the partials are gathered [N, T], and each rank applies
     with nparts = N and the full widths as divisors.  On one GPU this must equal
     the fused 8-shard kernel bit for bit."""
-    p = synth.cfg4(T=64)
+    p = synth.layerwise_rows(T=64)
     N, T = 8, p.T
     sq, sk = p.wq // N, p.wk // N
     x = host_to_device(p.x, p.dtype)
@@ -209,7 +209,7 @@ def test_e4m3_saturation_fused_and_two_phase():
 
 
 def test_bitwise_deterministic():
-    p = synth.cfg4(T=256)
+    p = synth.layerwise_rows(T=256)
     assert np.array_equal(fused(p), fused(p))
 
 
@@ -251,23 +251,23 @@ def _sample_rows(T, n=48, seed=7):
 
 
 @pytest.fixture(scope="module")
-def cfg5_input():
-    p = synth.cfg5(T=32768)
+def prefill_input():
+    p = synth.prefill_rows(T=32768)
     return p
 
 
-def test_cfg5_full_size_both_modes(cfg5_input):
+def test_prefill_full_size_both_modes(prefill_input):
     """T = 32768 x 10240 bf16, per-head and layerwise (fused and two-phase) on the same
     seeded input, in the launch configuration the bench times; sampled rows checked
     against the oracle, V checked over the whole tensor."""
-    p = cfg5_input
+    p = prefill_input
     rows = _sample_rows(p.T)
-    ph = synth.cfg5(T=p.T, mode="per_head")
+    ph = synth.prefill_rows(T=p.T, mode="per_head")
     x0 = host_to_device(p.x, p.dtype)
     qk = p.wq + p.wk
     sub = np.ascontiguousarray(p.x[rows])
     # per-head
-    print("[cfg5] per-head full size", flush=True)
+    print("[prefill] per-head full size", flush=True)
     x = x0.clone()
     q.qknorm_per_head(x, ph.hq, ph.hkv, ph.head_dim, gamma_to_device(ph.gamma_q, p.dtype),
                       gamma_to_device(ph.gamma_k, p.dtype), p.eps)
@@ -275,9 +275,9 @@ def test_cfg5_full_size_both_modes(cfg5_input):
     assert torch.equal(x[:, qk:].view(torch.int16), x0[:, qk:].view(torch.int16)), "V changed"
     got = x[torch.from_numpy(rows).cuda()].cpu().view(torch.int16).numpy().view(np.uint16)
     y64, _ = oracle.per_head(sub, p.dtype, ph.hq, ph.hkv, ph.head_dim, ph.gamma_q, ph.gamma_k, p.eps)
-    assert_close_to_oracle(got[:, :qk], y64[:, :qk], p.dtype, label="cfg5 per-head")
+    assert_close_to_oracle(got[:, :qk], y64[:, :qk], p.dtype, label="prefill [32768, 10240] per-head")
     # layerwise, fused
-    print("[cfg5] layerwise fused full size", flush=True)
+    print("[prefill] layerwise fused full size", flush=True)
     gq, gk = _gammas(p)
     x = x0.clone()
     q.qknorm_layerwise(x, p.wq, p.wk, gq, gk, p.eps, p.nshards)
@@ -285,10 +285,10 @@ def test_cfg5_full_size_both_modes(cfg5_input):
     assert torch.equal(x[:, qk:].view(torch.int16), x0[:, qk:].view(torch.int16)), "V changed"
     fused_rows = x[torch.from_numpy(rows).cuda()].cpu().view(torch.int16).numpy().view(np.uint16)
     y64, _ = oracle.layerwise(sub, p.dtype, p.wq, p.wk, p.gamma_q, p.gamma_k, p.eps, p.nshards)
-    assert_close_to_oracle(fused_rows[:, :qk], y64[:, :qk], p.dtype, label="cfg5 layerwise")
+    assert_close_to_oracle(fused_rows[:, :qk], y64[:, :qk], p.dtype, label="prefill layerwise")
     fused_all = x
     # layerwise, two-phase: same bits everywhere
-    print("[cfg5] layerwise two-phase full size", flush=True)
+    print("[prefill] layerwise two-phase full size", flush=True)
     x = x0.clone()
     pq = torch.empty(p.nshards, p.T, dtype=torch.float32, device="cuda")
     pk = torch.empty(p.nshards, p.T, dtype=torch.float32, device="cuda")

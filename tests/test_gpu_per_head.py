@@ -36,19 +36,19 @@ def run_per_head(p: synth.Problem, check_ulp=True):
     return got, relmax
 
 
-def test_cfg1_per_head_f32():
-    run_per_head(synth.cfg1())
+def test_small_fused_rows_f32():
+    run_per_head(synth.small_fused_f32())
 
 
-@pytest.mark.parametrize("H", synth.CFG2_SWEEP_H)
-@pytest.mark.parametrize("T", synth.CFG2_SWEEP_T)
-def test_cfg2_per_head_bf16_sweep(T, H):
-    run_per_head(synth.cfg2(T=T, H=H))
+@pytest.mark.parametrize("H", synth.STANDALONE_SWEEP_H)
+@pytest.mark.parametrize("T", synth.STANDALONE_SWEEP_T)
+def test_standalone_bf16_sweep(T, H):
+    run_per_head(synth.standalone_heads(T=T, H=H))
 
 
-@pytest.mark.parametrize("T", synth.CFG3_SWEEP_T)
-def test_cfg3_fused_gqa_bf16(T):
-    run_per_head(synth.cfg3(T=T))
+@pytest.mark.parametrize("T", synth.FUSED_GQA_SWEEP_T)
+def test_fused_gqa_bf16_sweep(T):
+    run_per_head(synth.fused_gqa_rows(T=T))
 
 
 ALL_DTYPES = [synth.F32, synth.BF16, synth.F16, synth.F8]
@@ -270,14 +270,14 @@ def test_e4m3_range_boundary(gval):
 
 
 def test_bitwise_deterministic():
-    p = synth.cfg3(T=512)
+    p = synth.fused_gqa_rows(T=512)
     a, _ = run_per_head(p)
     b, _ = run_per_head(p)
     assert np.array_equal(a, b)
 
 
 def test_standalone_3d_tensor_and_side_stream():
-    p = synth.cfg2(T=256, H=32)
+    p = synth.standalone_heads(T=256, H=32)
     x = host_to_device(p.x, p.dtype).view(256, 32, 128)
     g = gamma_to_device(p.gamma_q, p.dtype)
     s = torch.cuda.Stream()
@@ -291,7 +291,7 @@ def test_standalone_3d_tensor_and_side_stream():
 
 def test_rows_with_pitch_view():
     # a [T, (hq+hkv)*D] view into a wider buffer: pitch from stride(0)
-    p = synth.cfg3(T=64)
+    p = synth.fused_gqa_rows(T=64)
     full = host_to_device(p.x, p.dtype)
     view = full[:, : p.wq + p.wk]
     q.qknorm_per_head(view, p.hq, p.hkv, p.head_dim, gamma_to_device(p.gamma_q, p.dtype),
@@ -304,7 +304,7 @@ def test_rows_with_pitch_view():
 
 
 def test_graph_replay_matches_eager():
-    p = synth.cfg3(T=64)
+    p = synth.fused_gqa_rows(T=64)
     src = host_to_device(p.x, p.dtype)
     work = src.clone()
     gq, gk = gamma_to_device(p.gamma_q, p.dtype), gamma_to_device(p.gamma_k, p.dtype)

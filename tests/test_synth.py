@@ -56,12 +56,12 @@ def test_distributions():
 def test_outliers_and_token_scale():
     assert len(synth.outlier_columns(4, 6144, 0.01)) == 61
     assert len(synth.outlier_columns(5, 10240, 0.01)) == 102
-    p = synth.cfg4(T=32)
+    p = synth.layerwise_rows(T=32)
     x = oracle.decode(p.x, synth.BF16)
     cols = synth.outlier_columns(4, 6144, 0.01)
     others = np.setdiff1d(np.arange(6144), cols)
     assert np.abs(x[:, cols]).mean() > 10 * np.abs(x[:, others]).mean()
-    p2 = synth.cfg2(T=64, H=16)
+    p2 = synth.standalone_heads(T=64, H=16)
     rms = np.sqrt(np.mean(oracle.decode(p2.x, synth.BF16) ** 2, axis=1))
     assert rms.min() > 0.05 and rms.max() < 12 and rms.max() / rms.min() > 5
 
@@ -86,7 +86,7 @@ def _golden(name):
 
 def test_fused_gqa_layout_matches_the_lesson():
     g = _golden("gqa_fused_split.txt")
-    p = synth.cfg3(T=2)
+    p = synth.fused_gqa_rows(T=2)
     assert p.hq == g["q_heads"] and p.hkv == g["kv_heads"] and p.head_dim == g["head_dim"]
     assert p.wq == g["q_width"] and p.wk == g["k_width"]
     assert p.ld == g["fused_width"] == g["q_width"] + g["k_width"] + g["v_width"]
@@ -99,15 +99,15 @@ def test_fused_gqa_layout_matches_the_lesson():
 
 
 def test_config_shapes():
-    p = synth.cfg1()
+    p = synth.small_fused_f32()
     assert (p.T, p.ld, p.wq, p.wk, p.dtype) == (4, 3072, 2048, 512, synth.F32)
-    p = synth.cfg2(T=16, H=48)
+    p = synth.standalone_heads(T=16, H=48)
     assert (p.T, p.ld, p.wq, p.wk, p.hkv) == (16, 6144, 6144, 0, 0) and p.gamma_k is None
-    p = synth.cfg4(T=4)
+    p = synth.layerwise_rows(T=4)
     assert (p.ld, p.wq, p.wk, p.nshards) == (6144, 4096, 1024, 8)
-    p = synth.cfg5(T=3)
+    p = synth.prefill_rows(T=3)
     assert (p.ld, p.wq, p.wk, p.nshards) == (10240, 8192, 1024, 8)
-    ph = synth.cfg5(T=3, mode="per_head")
+    ph = synth.prefill_rows(T=3, mode="per_head")
     assert np.array_equal(ph.x, p.x)           # both modes on the same input
     assert (ph.hq, ph.hkv, ph.head_dim) == (64, 8, 128)
     assert p.eps == float(np.float32(1e-6))
