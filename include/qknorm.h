@@ -72,7 +72,7 @@ extern "C" {
 #define QKNORM_E_SHAPE -2       /* negative size, ld too small, shard count does not divide */
 #define QKNORM_E_ALIGN -3       /* base, row pitch, head or shard not a multiple of 16 bytes */
 #define QKNORM_E_DTYPE -4       /* dtype not one of the codes above */
-#define QKNORM_E_UNSUPPORTED -5 /* valid request this build does not implement (e.g. head_dim) */
+#define QKNORM_E_UNSUPPORTED -5 /* a valid request the library does not implement (e.g. head_dim) */
 #define QKNORM_E_EPS -6         /* eps negative, NaN or infinite */
 #define QKNORM_E_HIP -7         /* the HIP runtime refused the launch or device query */
 

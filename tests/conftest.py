@@ -16,7 +16,7 @@ def pytest_configure(config):
 
 
 def pytest_collection_modifyitems(config, items):
-    # Skip GPU tests cleanly where no GPU is visible; they are run on the GPU machine.
+    # Skip GPU tests cleanly where no GPU is visible; they run where one is.
     try:
         import torch
         have_gpu = torch.cuda.is_available()
