@@ -257,6 +257,23 @@ def bench_layerwise(q, torch, dev, p, steps, warmup, label="prefill"):
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 
+# The pages' own figures, on other hardware: context for the bench line, not
+# targets (the dtype of the per-head tables is not stated on the pages).
+PAGES_CONTEXT = {
+    "kind": "the pages' numbers on other hardware; context only, not a target",
+    "per_head_T4096_H48_D128_us": {
+        "source": "sglang PR 13189 (turbomind_rms_norm for QK norm), benchmark tables",
+        "H20": {"sglang_rmsnorm": 269.633, "turbomind_rms_norm": 69.378},
+        "H100": {"sglang_rmsnorm": 271.742, "turbomind_rms_norm": 73.303},
+    },
+    "layerwise_qknorm_latency_reduction_pct": {
+        "source": "SwiftQK (arXiv 2608.09160), abstract",
+        "range": [81.4, 93.9],
+        "setting": "multi-GPU tensor parallel: scalar sum-of-squares exchange against a full-vector "
+                   "all-gather; there is no single-GPU figure",
+    },
+}
+
 
 def bench_proj(q, torch, dev, steps, warmup, T=4096, hidden=4096, hq=32, hkv=8, D=128):
     """QKV projection of a Qwen3-8B-sized layer ([T, 4096] x [6144, 4096]^T,
@@ -512,6 +529,7 @@ def main():
         for T in (4096, 8192):
             cases[f"qkv_proj_T{T}_qwen3_8b"] = bench_proj(q, torch, dev, 30, 5, T=T)
         result["cases"] = cases
+    result["pages_context"] = PAGES_CONTEXT
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(p)
     result["bench_wall_s"] = round(time.perf_counter() - t_start, 1)
