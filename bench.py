@@ -396,6 +396,28 @@ def bench_decode(q, torch, dev, reps=200):
     return out
 
 
+def bench_d2d_copy(torch, dev, nbytes, steps=400, warmup=40):
+    """A device-to-device copy (hipMemcpyAsync through torch's copy_) that reads and
+    writes as many bytes as one headline launch: the practical ceiling the
+    runtime's own copy reaches.  Buffer pairs rotate through >= 1 GiB."""
+    n = pool_count(2 * nbytes)
+    src = [torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1) for _ in range(n)]
+    dst = [torch.empty(nbytes, dtype=torch.uint8, device=dev) for _ in range(n)]
+
+    def launch(i):
+        dst[i % n].copy_(src[i % n])
+
+    warm_clocks(torch, launch)
+    for i in range(warmup):
+        launch(i)
+    _, mean_us = Timer(torch).run(steps, launch, first=warmup)
+    del src, dst
+    torch.cuda.empty_cache()
+    log(f"d2d copy of {nbytes} bytes: {mean_us:.2f} us, {2 * nbytes / mean_us / 1e3:.0f} GB/s")
+    return {"bytes_read": nbytes, "bytes_written": nbytes, "mean_us": mean_us,
+            "gbs": 2 * nbytes / (mean_us * 1e-6) / 1e9}
+
+
 def cpu_baseline(p, budget_s=10.0):
     import oracle
     n = 0
@@ -526,6 +548,8 @@ def main():
                                                                  "fp8e4m3 [32768, 10240]")
         del p8
         cases["decode"] = bench_decode(q, torch, dev)
+        cp = bench_d2d_copy(torch, dev, p.T * (p.wq + p.wk) * 2)
+        cases["d2d_copy_headline_bytes"] = {**cp, "copy_time_over_headline_kernel_time": cp["mean_us"] / head["mean_us"]}
         for T in (4096, 8192):
             cases[f"qkv_proj_T{T}_qwen3_8b"] = bench_proj(q, torch, dev, 30, 5, T=T)
         result["cases"] = cases
