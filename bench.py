@@ -163,11 +163,13 @@ def pool_count(buf_bytes: int, min_copies=2) -> int:
 
 # ------------------------------------------------------------------- cases --
 
-def bench_per_head(q, torch, dev, p, steps, warmup, label):
+def bench_per_head(q, torch, dev, p, steps, warmup, label, max_copies=None, spread=True):
     from qk_norm_amd import synth
     lib = q.load()
     es, ges = sizes(p)
     n = pool_count(p.T * p.ld * es)
+    if max_copies is not None:
+        n = min(n, max_copies)
     base = to_device(p.x, p.dtype, torch, dev)
     pool = [base.clone() for _ in range(n)]
     del base
@@ -188,7 +190,7 @@ def bench_per_head(q, torch, dev, p, steps, warmup, label):
         launch(i)
     timer = Timer(torch)
     wall, mean_us = timer.run(steps, launch, first=warmup)
-    spread = timer.spread(min(steps, 200), launch, first=warmup + steps)
+    spread = timer.spread(min(steps, 200), launch, first=warmup + steps) if spread else {}
     bytes_alg = 2 * p.T * (p.wq + p.wk) * es + (p.head_dim * ges) * (1 + (p.hkv > 0))
     del pool
     torch.cuda.empty_cache()
@@ -396,6 +398,74 @@ def bench_decode(q, torch, dev, reps=200):
     return out
 
 
+# The grid of the sglang PR's per-head tables (head_dim 128), and its
+# turbomind_rms_norm column in us per call, as context (dtype not stated).
+PR_GRID_T = (1, 2, 4, 8, 16, 32, 64, 128, 256, 512, 1024, 2048, 4096)
+PR_TURBOMIND_US = {
+    "H20": {16: (2.401, 2.554, 2.554, 2.606, 2.623, 2.670, 2.768, 2.878, 3.171, 4.080, 5.538, 8.726, 15.672),
+            32: (2.553, 2.554, 2.609, 2.623, 2.670, 2.768, 2.862, 3.171, 4.080, 5.537, 8.731, 15.645, 44.130),
+            48: (2.548, 2.591, 2.612, 2.651, 2.723, 2.813, 3.288, 3.487, 4.873, 7.115, 11.958, 28.149, 69.378)},
+    "H100": {16: (2.644, 2.749, 2.758, 2.785, 2.903, 3.018, 3.067, 3.305, 3.481, 4.106, 5.459, 8.214, 16.025),
+             32: (2.760, 2.737, 2.813, 2.903, 3.021, 3.063, 3.286, 3.476, 4.112, 5.469, 8.206, 16.015, 46.956),
+             48: (2.732, 2.763, 2.831, 2.940, 2.998, 3.143, 3.355, 3.842, 4.792, 6.965, 11.216, 29.693, 73.303)},
+}
+
+
+def bench_sweep(q, torch, dev, reps=200):
+    """Per-head bf16 [T, H, 128] over the PR's grid (H in {16, 32, 48}, T = 1 ... 4096).
+    For each point: GPU time per launch of `reps` launches replayed from one
+    captured hipGraph (no host cost between launches), and of `reps` eager
+    launches through the C ABI (host-bound at small T).  Buffers rotate through
+    up to 64 copies, so the smaller sizes run out of the caches, as a serving
+    loop's would."""
+    from qk_norm_amd import synth
+    lib = q.load()
+    out = []
+    for H in (16, 32, 48):
+        for i, T in enumerate(PR_GRID_T):
+            p = synth.standalone_heads(T=T, H=H)
+            es, ges = sizes(p)
+            n = min(pool_count(p.T * p.ld * es), 64)
+            base = to_device(p.x, p.dtype, torch, dev)
+            pool = [base.clone() for _ in range(n)]
+            g = to_device(p.gamma_q, synth.gamma_dtype(p.dtype), torch, dev)
+            bytes_alg = 2 * p.T * p.wq * es + p.head_dim * ges
+
+            def launch(j, stream):
+                rc = lib.qknorm_per_head(pool[j % n].data_ptr(), p.T, p.ld, p.hq, 0, p.head_dim,
+                                         g.data_ptr(), None, p.eps, p.dtype, stream)
+                if rc:
+                    raise RuntimeError(q.strerror(rc))
+
+            cur = torch.cuda.current_stream(dev).cuda_stream
+            warm_clocks(torch, lambda j: launch(j, cur))
+            _, eager_us = Timer(torch).run(reps, lambda j: launch(j, cur))
+            graph = torch.cuda.CUDAGraph()
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                with torch.cuda.graph(graph, stream=side):
+                    for j in range(reps):
+                        launch(j, side.cuda_stream)
+            torch.cuda.synchronize()
+            graph.replay()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            graph.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            graph_us = e0.elapsed_time(e1) * 1e3 / reps
+            out.append({"H": H, "T": T, "graph_us": graph_us, "eager_us": eager_us,
+                        "gbs_graph": bytes_alg / (graph_us * 1e-6) / 1e9,
+                        "pct_of_hbm_peak_graph": 100 * bytes_alg / (graph_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                        "pool": n, "pages_turbomind_us": {k: v[H][i] for k, v in PR_TURBOMIND_US.items()}})
+            log(f"sweep H={H} T={T}: graph {graph_us:.2f} us, eager {eager_us:.2f} us")
+            del graph, pool, base
+            torch.cuda.empty_cache()
+    return out
+
+
 def bench_d2d_copy(torch, dev, nbytes, steps=400, warmup=40):
     """A device-to-device copy (hipMemcpyAsync through torch's copy_) that reads and
     writes as many bytes as one headline launch: the practical ceiling the
@@ -418,21 +488,51 @@ def bench_d2d_copy(torch, dev, nbytes, steps=400, warmup=40):
             "gbs": 2 * nbytes / (mean_us * 1e-6) / 1e9}
 
 
-def cpu_baseline(p, budget_s=10.0):
+def cpu_baseline(p, q, torch, dev, budget_s=10.0):
+    """The fp64 C oracle on the headline input, timed on the host's cores for about
+    budget_s of wall time.  Its first result also checks one fresh GPU launch on the
+    same input, element by element (the tolerance the tests use for bf16)."""
+    import numpy as np
     import oracle
+    from qk_norm_amd import synth
     n = 0
+    ref = None
     t0 = time.perf_counter()
     while True:
-        oracle.per_head(p.x, p.dtype, p.hq, p.hkv, p.head_dim, p.gamma_q, p.gamma_k, p.eps)
+        r = oracle.per_head(p.x, p.dtype, p.hq, p.hkv, p.head_dim, p.gamma_q, p.gamma_k, p.eps)
+        ref = ref or r
         n += 1
         el = time.perf_counter() - t0
         if el >= budget_s or el / n * (n + 1) > 3 * budget_s:
             break
     bytes_alg = 2 * p.T * (p.wq + p.wk) * 2 + p.head_dim * 2
+    # one launch on a fresh copy of the same input
+    x = to_device(p.x, p.dtype, torch, dev)
+    q.qknorm_per_head(x, p.hq, p.hkv, p.head_dim, to_device(p.gamma_q, p.dtype, torch, dev),
+                      None, p.eps)
+    torch.cuda.synchronize()
+    got = x.cpu().view(torch.int16).numpy().view(np.uint16)
+    y64, yr = ref
+    g = oracle.decode(got, p.dtype)
+    nz = y64 != 0
+    rel = np.abs(g[nz] - y64[nz]) / np.abs(y64[nz])
+
+    def ordinal(b):
+        b = b.astype(np.int64)
+        return np.where(b & 0x8000, -(b & 0x7FFF), b)
+
+    ulp = np.abs(ordinal(got) - ordinal(yr))
+    parity = {"elements": int(got.size), "max_rel_err": float(rel.max()),
+              "rtol": 8e-3, "zero_where_oracle_zero": bool(np.all(g[~nz] == 0)),
+              "ulp_0": int((ulp == 0).sum()), "ulp_1": int((ulp == 1).sum()),
+              "ulp_over_1": int((ulp > 1).sum())}
+    parity["pass"] = bool(parity["max_rel_err"] <= 8e-3 and parity["zero_where_oracle_zero"]
+                          and parity["ulp_over_1"] == 0)
     return {"value": bytes_alg * n / el / 1e9, "unit": "GB/s", "cores": oracle.max_threads(),
             "kind": "oracle",
             "sample": f"{n} full call(s) of the fp64 C oracle on the same [4096,48,128] bf16 input "
-                      f"({el:.1f} s)", "us_per_call": el / n * 1e6}
+                      f"({el:.1f} s)", "us_per_call": el / n * 1e6,
+            "parity_of_one_gpu_launch": parity}
 
 
 # -------------------------------------------------------------------- main --
@@ -446,7 +546,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--case", default="headline",
                     choices=["headline", "prefill_layerwise", "prefill_per_head", "fp8_per_head",
-                             "fp8_prefill_layerwise", "proj", "decode", "copy"],
+                             "fp8_prefill_layerwise", "proj", "decode", "sweep", "copy"],
                     help="single case for profiling runs")
     args = ap.parse_args()
 
@@ -487,6 +587,9 @@ def main():
         p = synth.prefill_rows(T=32768, dtype=synth.F8)
         print(json.dumps({"case": "fp8_prefill_layerwise",
                           **bench_layerwise(q, torch, dev, p, args.steps, args.warmup, "fp8 prefill [32768, 10240]")}))
+        return
+    if args.case == "sweep":
+        print(json.dumps({"case": "sweep", "per_head_bf16_D128": bench_sweep(q, torch, dev)}))
         return
     if args.case == "decode":
         print(json.dumps({"case": "decode", "launches": bench_decode(q, torch, dev)}))
@@ -555,7 +658,7 @@ def main():
         result["cases"] = cases
     result["pages_context"] = PAGES_CONTEXT
     if not args.no_cpu:
-        result["cpu_baseline"] = cpu_baseline(p)
+        result["cpu_baseline"] = cpu_baseline(p, q, torch, dev)
     result["bench_wall_s"] = round(time.perf_counter() - t_start, 1)
     print(json.dumps(result))
 
