@@ -362,7 +362,10 @@ __global__ __launch_bounds__(G::kThreads) void qkv_proj_kernel(
 // prefetch of later K steps (a 4-byte load per operand row) cost about 9 %:
 // it doubles the vector-memory requests per step.  4 waves of 128 x 128 with
 // the operands staged through registers (global loads two steps ahead, two
-// LDS stages) measured 11-17 % slower than this kernel.
+// LDS stages) measured 11-17 % slower than this kernel.  Reading fragments two
+// sub-steps ahead, accumulating in AGPRs, leaving the loads to one wave per
+// SIMD, or splitting a step's loads over two sub-steps (also with 4 waves of
+// 128 x 128) changed the time by 3 % or less.
 #ifndef QKNORM_PROJ_BK
 #define QKNORM_PROJ_BK 64
 #endif
