@@ -364,8 +364,10 @@ __global__ __launch_bounds__(G::kThreads) void qkv_proj_kernel(
 // the operands staged through registers (global loads two steps ahead, two
 // LDS stages) measured 11-17 % slower than this kernel.  Reading fragments two
 // sub-steps ahead, accumulating in AGPRs, leaving the loads to one wave per
-// SIMD, or splitting a step's loads over two sub-steps (also with 4 waves of
-// 128 x 128) changed the time by 3 % or less.
+// SIMD, splitting a step's loads over two sub-steps (also with 4 waves of
+// 128 x 128), an epilogue that stores from registers, or a persistent grid
+// that loads the next tile during the epilogue changed the time by 3 % or
+// less.
 #ifndef QKNORM_PROJ_BK
 #define QKNORM_PROJ_BK 64
 #endif
