@@ -301,3 +301,52 @@ def test_prefill_full_size_both_modes(prefill_input):
     gpq = pq[:, idx].cpu().numpy().astype(np.float64)
     gpk = pk[:, idx].cpu().numpy().astype(np.float64)
     assert np.all(np.abs(gpq - oq) <= PART_RTOL * oq) and np.all(np.abs(gpk - ok) <= PART_RTOL * ok)
+
+
+@pytest.mark.parametrize("dtype", [synth.BF16, synth.F8], ids=["bf16", "fp8"])
+def test_graph_replay_matches_eager(dtype):
+    """The fused call, and partial_sumsq followed by apply_scalar, captured in
+    graphs: every replay (with eager work and synchronisations between them)
+    leaves the bytes the eager calls leave, and the partials too."""
+    p = synth.layerwise_problem(f"graph_{synth.DTYPE_NAMES[dtype]}", 61, dtype, 96, 4096, 1024, 6144, 8,
+                                outlier_frac=0.01)
+    print(f"[layerwise graph] {p.name} T={p.T} R={p.nshards}", flush=True)
+    src = host_to_device(p.x, p.dtype)
+    gq, gk = _gammas(p)
+    R, T = p.nshards, p.T
+    pq = torch.empty(R, T, dtype=torch.float32, device="cuda")
+    pk = torch.empty(R, T, dtype=torch.float32, device="cuda")
+
+    def fused_call(t):
+        q.qknorm_layerwise(t, p.wq, p.wk, gq, gk, p.eps, R)
+
+    def two_phase_call(t):
+        q.qknorm_partial_sumsq(t, p.wq, p.wk, R, pq, pk)
+        q.qknorm_apply_scalar(t, p.wq, p.wk, pq, pk, p.wq, p.wk, gq, gk, p.eps)
+
+    for name, call in (("fused", fused_call), ("two-phase", two_phase_call)):
+        work = src.clone()
+        call(work)
+        torch.cuda.synchronize()
+        eager, eager_pq, eager_pk = work.clone(), pq.clone(), pk.clone()
+        work.copy_(src)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            with torch.cuda.graph(g, stream=s):
+                call(work)
+        torch.cuda.synchronize()
+        for i in range(4):
+            work.copy_(src)
+            pq.fill_(-1.0)
+            pk.fill_(-1.0)
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(work.view(torch.uint8), eager.view(torch.uint8)), f"{name}: replay {i}"
+            if name == "two-phase":
+                assert torch.equal(pq, eager_pq) and torch.equal(pk, eager_pk), f"{name}: partials, replay {i}"
+        got = device_to_host(work, p.dtype)
+        check_against_oracle(p, got, f"{p.name} {name} graph")
