@@ -234,3 +234,22 @@ def test_projection_validation(lib):
     assert pj(lib, eps=-1.0) == q.QKNORM_E_EPS
     assert pj(lib, ldx=(1 << 22) + 8, T=0) == q.QKNORM_E_UNSUPPORTED       # 256 rows over 2 GiB
     assert pj(lib, ldw=(1 << 22) + 8, T=0) == q.QKNORM_E_UNSUPPORTED
+
+
+def _c_program():
+    """tests/c_abi/closed_form, built with gcc here if it is not there yet."""
+    import importlib.util
+    path = os.path.join(ROOT, "tests", "c_abi", "build.py")
+    spec = importlib.util.spec_from_file_location("c_abi_build", path)
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod.BIN if os.path.exists(mod.BIN) else mod.build()
+
+
+def test_plain_c_program_gets_the_validation_codes():
+    # a C program linked against the library (no Python in between) gets every
+    # validation code before any HIP call; its GPU part runs in the GPU tests
+    res = subprocess.run([_c_program(), "--validation-only"], capture_output=True, text=True,
+                         timeout=60)
+    assert res.returncode == 0, res.stderr
+    assert "validation codes ok" in res.stdout
