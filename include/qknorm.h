@@ -175,9 +175,11 @@ int qknorm_apply_scalar(void *qkv, int64_t T, int64_t ld, int64_t wq, int64_t wk
  *
  * x   [T, hidden], row pitch ldx (elements); w [N, hidden], the projection
  *     weight with one row per output column, pitch ldw; qkv [T, ld] output,
- *     columns >= N not written.  bf16 only (dtype QKNORM_BF16; others give
- *     QKNORM_E_UNSUPPORTED).  flags: 0, or QKNORM_PROJ_PLAIN for the plain
- *     projection (gamma and eps unused).
+ *     columns >= N not written.  dtype QKNORM_BF16 or QKNORM_F16: x, w,
+ *     gamma and qkv share it (others give QKNORM_E_UNSUPPORTED); products are
+ *     accumulated in fp32 either way and rounded once, to nearest-even.
+ *     flags: 0, or QKNORM_PROJ_PLAIN for the plain projection (gamma and eps
+ *     unused).
  * Requires: hidden a multiple of 64 and head_dim 64 or 128 (else
  * QKNORM_E_UNSUPPORTED); ldx, ldw >= hidden and ld >= N; x, w, qkv and gamma
  * 16-byte aligned, pitches*2 multiples of 16 bytes; 256 rows of x, of w and

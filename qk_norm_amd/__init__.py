@@ -245,7 +245,8 @@ def qknorm_qkv_proj_per_head(x, w, qkv, hq: int, hkv: int, head_dim: int, gamma_
     """qkv[:, :N] = x @ w.T with each Q and K head RMS-normalised in the epilogue.
 
     x [T, hidden], w [N, hidden] (N = (hq + 2*hkv) * head_dim) and qkv [T, >= N],
-    all bfloat16 on one GPU; plain=True gives the projection alone.
+    all bfloat16 or all float16 (gamma too) on one GPU; plain=True gives the
+    projection alone.
     """
     if not qkv.is_cuda:
         raise ValueError("qkv must be a GPU tensor (the library has no CPU path)")

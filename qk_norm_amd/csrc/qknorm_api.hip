@@ -196,7 +196,7 @@ int qknorm_qkv_proj_per_head(const void* x, int64_t ldx, const void* w, int64_t 
                              int32_t flags, int32_t dtype, void* stream) {
   int rc = check_common(dtype, eps, T, ld);
   if (rc) return rc;
-  if (dtype != QKNORM_BF16) return QKNORM_E_UNSUPPORTED;
+  if (dtype != QKNORM_BF16 && dtype != QKNORM_F16) return QKNORM_E_UNSUPPORTED;
   if ((flags & ~QKNORM_PROJ_PLAIN) != 0) return QKNORM_E_UNSUPPORTED;
   if (hidden <= 0 || hq < 0 || hkv < 0 || head_dim <= 0 || ldx < hidden || ldw < hidden)
     return QKNORM_E_SHAPE;
@@ -212,7 +212,7 @@ int qknorm_qkv_proj_per_head(const void* x, int64_t ldx, const void* w, int64_t 
   if (ld * 2 > kMaxPitchBytes || T * (ld + 1) > (INT64_C(1) << 46) || N >= (INT64_C(1) << 24))
     return QKNORM_E_UNSUPPORTED;
   qknorm::ProjArgs a{x, ldx, w, ldw, qkv, ld, T, hidden, hq, hkv, head_dim, gamma_q, gamma_k,
-                     eps, flags};
+                     eps, flags, dtype};
   if (!qknorm::proj_shape_ok(a)) return QKNORM_E_UNSUPPORTED;
   if (!touched) return QKNORM_OK;
   return finish(qknorm::launch_qkv_proj(a, static_cast<hipStream_t>(stream)));

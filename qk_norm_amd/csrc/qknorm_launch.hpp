@@ -60,6 +60,7 @@ struct ProjArgs {
   const void* gamma_k;
   float eps;
   int32_t flags;
+  int32_t dtype;       // kBF16 or kF16: x, w, gamma and qkv share it
 };
 
 // Whether every per-head trip's buffer span stays below 2^31 bytes.

@@ -9,7 +9,7 @@
 //
 // Tiling: a block of 512 threads (4 x 2 waves, two per SIMD) owns a 256 x 256
 // output tile; each wave a 64 x 128 slab of 2 x 4 v_mfma_f32_32x32x16_bf16
-// blocks.  K advances 64 at a time through two LDS stages filled straight
+// blocks (v_mfma_f32_32x32x16_f16 for fp16, the same layout).  K advances 64 at a time through two LDS stages filled straight
 // from global memory (buffer loads into LDS, no staging registers), with
 // the operand rows XOR-swizzled so that fragment reads hit distinct banks.
 // Tiles are ordered so the blocks each XCD holds at once share operand
@@ -26,8 +26,28 @@ namespace qknorm {
 
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// The 16-bit element type: its 8-element fragment and the 32 x 32 x 16 MFMA
+// that takes it (fp32 accumulation either way).
+template <int DT>
+struct ProjElem;
+template <>
+struct ProjElem<kBF16> {
+  typedef __bf16 T;
+  typedef __bf16 V8 __attribute__((ext_vector_type(8)));
+  static __device__ __forceinline__ f32x16 mfma(V8 a, V8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+};
+template <>
+struct ProjElem<kF16> {
+  typedef _Float16 T;
+  typedef _Float16 V8 __attribute__((ext_vector_type(8)));
+  static __device__ __forceinline__ f32x16 mfma(V8 a, V8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+};
 
 // Tile geometry.  A block of WM x WN waves owns a BM x BN output tile; each
 // wave a (BM/WM) x (BN/WN) slab of 32 x 32 MFMA blocks; K advances BK at a
@@ -118,9 +138,10 @@ __device__ __forceinline__ void dma_tile(Rsrc ra, Rsrc rb, const DmaOffsets<G>& 
   }
 }
 
-template <class G>
-__device__ __forceinline__ bf16x8 sfrag(const uint8_t* base, uint32_t row, uint32_t k) {
-  return *reinterpret_cast<const bf16x8*>(base + row * G::kRowBytes + lds_slot<G>(row, k / 8) * 16);
+template <class G, int DT>
+__device__ __forceinline__ typename ProjElem<DT>::V8 sfrag(const uint8_t* base, uint32_t row, uint32_t k) {
+  return *reinterpret_cast<const typename ProjElem<DT>::V8*>(base + row * G::kRowBytes +
+                                                            lds_slot<G>(row, k / 8) * 16);
 }
 
 // Byte offset of K step k, or of the last step for k past it.
@@ -148,23 +169,24 @@ __device__ __forceinline__ void stage_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-template <class G>
+template <class G, int DT>
 __device__ __forceinline__ void read_frags(const uint8_t* st, uint32_t arow, uint32_t brow,
-                                           uint32_t k, bf16x8 (&a)[G::MB], bf16x8 (&b)[G::NB]) {
+                                           uint32_t k, typename ProjElem<DT>::V8 (&a)[G::MB],
+                                           typename ProjElem<DT>::V8 (&b)[G::NB]) {
 #pragma unroll
-  for (int i = 0; i < G::MB; ++i) a[i] = sfrag<G>(st, arow + i * 32, k);
+  for (int i = 0; i < G::MB; ++i) a[i] = sfrag<G, DT>(st, arow + i * 32, k);
 #pragma unroll
-  for (int j = 0; j < G::NB; ++j) b[j] = sfrag<G>(st, brow + j * 32, k);
+  for (int j = 0; j < G::NB; ++j) b[j] = sfrag<G, DT>(st, brow + j * 32, k);
 }
 
-template <class G>
-__device__ __forceinline__ void mfma_step(f32x16 (&acc)[G::MB][G::NB], const bf16x8 (&a)[G::MB],
-                                          const bf16x8 (&b)[G::NB]) {
+template <class G, int DT>
+__device__ __forceinline__ void mfma_step(f32x16 (&acc)[G::MB][G::NB],
+                                          const typename ProjElem<DT>::V8 (&a)[G::MB],
+                                          const typename ProjElem<DT>::V8 (&b)[G::NB]) {
 #pragma unroll
   for (int i = 0; i < G::MB; ++i)
 #pragma unroll
-    for (int j = 0; j < G::NB; ++j)
-      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+    for (int j = 0; j < G::NB; ++j) acc[i][j] = ProjElem<DT>::mfma(a[i], b[j], acc[i][j]);
 }
 
 // Instruction order for the scheduler (sched_group_barrier masks: 0x008
@@ -187,7 +209,7 @@ __device__ __forceinline__ void sched_mfmas() {
   if constexpr (M > 0) __builtin_amdgcn_sched_group_barrier(0x008, M, 0);
 }
 
-template <class G, int D>
+template <class G, int DT, int D>
 __global__ __launch_bounds__(G::kThreads) void qkv_proj_kernel(
     const uint8_t* __restrict__ x, uint32_t ldx_bytes, const uint8_t* __restrict__ w,
     uint32_t ldw_bytes, uint8_t* __restrict__ out, uint64_t ld_bytes, uint32_t T, uint32_t K,
@@ -250,8 +272,10 @@ __global__ __launch_bounds__(G::kThreads) void qkv_proj_kernel(
   wait_vmcnt<0>();
   stage_barrier();
   dma_tile<G>(ra, rb, doff, step_bytes<G>(1, ksteps), stage1, wave);
-  bf16x8 fa[2][MB], fb[2][NB];
-  read_frags<G>(stage0, arow, brow, fk, fa[0], fb[0]);
+  typedef typename ProjElem<DT>::V8 Frag;
+  typedef typename ProjElem<DT>::T Elem;
+  Frag fa[2][MB], fb[2][NB];
+  read_frags<G, DT>(stage0, arow, brow, fk, fa[0], fb[0]);
 
   constexpr int kReads = MB + NB, kMfma = MB * NB;
   static_assert(kMfma > kReads && G::kLoads % (kMfma - kReads) == 0, "");
@@ -260,8 +284,8 @@ __global__ __launch_bounds__(G::kThreads) void qkv_proj_kernel(
     uint8_t* const nx = (ks & 1) ? stage0 : stage1;
 #pragma unroll
     for (int kk = 0; kk < KK - 1; ++kk) {
-      read_frags<G>(st, arow, brow, (kk + 1) * 16 + fk, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
-      mfma_step<G>(acc, fa[kk & 1], fb[kk & 1]);
+      read_frags<G, DT>(st, arow, brow, (kk + 1) * 16 + fk, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
+      mfma_step<G, DT>(acc, fa[kk & 1], fb[kk & 1]);
       sched_interleave<kReads, 1, 0>();
       sched_mfmas<kMfma - kReads>();
       __builtin_amdgcn_sched_barrier(0);
@@ -271,9 +295,9 @@ __global__ __launch_bounds__(G::kThreads) void qkv_proj_kernel(
     __builtin_amdgcn_sched_barrier(0);
     // the reads come first: the compiler cannot tell that the loads into
     // stage st do not overlap stage nx, so it keeps them in source order
-    read_frags<G>(nx, arow, brow, fk, fa[0], fb[0]);
+    read_frags<G, DT>(nx, arow, brow, fk, fa[0], fb[0]);
     dma_tile<G>(ra, rb, doff, step_bytes<G>(ks + 2, ksteps), st, wave);
-    mfma_step<G>(acc, fa[1], fb[1]);
+    mfma_step<G, DT>(acc, fa[1], fb[1]);
     sched_interleave<kReads, 1, 0>();
     sched_interleave<kMfma - kReads, 0, G::kLoads / (kMfma - kReads)>();
     // keeps the reads above in this iteration: without it the compiler merges
@@ -301,7 +325,7 @@ __global__ __launch_bounds__(G::kThreads) void qkv_proj_kernel(
       const uint32_t head = n / D;
       const bool is_q = head < hq;
       normed[j] = (is_q || head < hq + hkv) && n < N;
-      const __bf16* gp = reinterpret_cast<const __bf16*>(is_q ? gamma_q : gamma_k);
+      const Elem* gp = reinterpret_cast<const Elem*>(is_q ? gamma_q : gamma_k);
       g[j] = normed[j] ? (float)gp[n % D] : 1.f;
     }
 #pragma unroll
@@ -327,7 +351,7 @@ __global__ __launch_bounds__(G::kThreads) void qkv_proj_kernel(
   }
   // the bf16 tile goes through LDS (the stages are free after the loop's last
   // barrier) so rows leave as 16-byte stores
-  __bf16* O = reinterpret_cast<__bf16*>(smem);
+  Elem* O = reinterpret_cast<Elem*>(smem);
 #pragma unroll
   for (int i = 0; i < MB; ++i)
 #pragma unroll
@@ -335,7 +359,7 @@ __global__ __launch_bounds__(G::kThreads) void qkv_proj_kernel(
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const uint32_t r = wm * G::kWaveM + i * 32 + 8 * (e / 4) + 4 * (lane / 32) + e % 4;
-        O[r * G::kORow + wn * G::kWaveN + j * 32 + lane % 32] = (__bf16)acc[i][j][e];
+        O[r * G::kORow + wn * G::kWaveN + j * 32 + lane % 32] = (Elem)acc[i][j][e];
       }
   __syncthreads();
   // one descriptor over the tile's rows (wave-uniform); rows past T and
@@ -400,7 +424,9 @@ bool proj_shape_ok(const ProjArgs& a) {
 hipError_t launch_qkv_proj(const ProjArgs& a, hipStream_t s) {
   const uint32_t N = (uint32_t)((a.hq + 2 * a.hkv) * a.head_dim);
   const dim3 grid((uint32_t)(((N + kBN - 1) / kBN) * ((a.T + kBM - 1) / kBM)));
-  auto kern = a.head_dim == 64 ? qkv_proj_kernel<Geo, 64> : qkv_proj_kernel<Geo, 128>;
+  auto kern = a.dtype == kF16
+                  ? (a.head_dim == 64 ? qkv_proj_kernel<Geo, kF16, 64> : qkv_proj_kernel<Geo, kF16, 128>)
+                  : (a.head_dim == 64 ? qkv_proj_kernel<Geo, kBF16, 64> : qkv_proj_kernel<Geo, kBF16, 128>);
   // more than the default 64 KiB of dynamic LDS (gfx950 has 160 KiB per CU);
   // a host-side attribute, set on every call (no shared state between threads)
   const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),

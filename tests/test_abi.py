@@ -217,7 +217,9 @@ def test_projection_validation(lib):
     assert pj(lib, T=0) == q.QKNORM_OK
     assert pj(lib, T=0, D=64, ld=384) == q.QKNORM_OK
     assert pj(lib, T=0, flags=q.QKNORM_PROJ_PLAIN, gq=None, gk=None) == q.QKNORM_OK
-    assert pj(lib, dt=F32) == q.QKNORM_E_UNSUPPORTED          # bf16 only
+    assert pj(lib, T=0, dt=F16) == q.QKNORM_OK                 # bf16 and fp16
+    assert pj(lib, dt=F32) == q.QKNORM_E_UNSUPPORTED
+    assert pj(lib, dt=F8) == q.QKNORM_E_UNSUPPORTED
     assert pj(lib, dt=7) == q.QKNORM_E_DTYPE
     assert pj(lib, flags=2) == q.QKNORM_E_UNSUPPORTED
     assert pj(lib, hidden=96, ldx=96, ldw=96) == q.QKNORM_E_UNSUPPORTED     # K step of 64

@@ -9,6 +9,8 @@ within K * 2^-24 * A of the exact one, A = sum_k |x_k w_k| of that output.
       |g - o| <= 8e-3 |o| + 2 K 2^-24 (|gamma| A / rms + |o| ||A||_2 / ||acc||_2)
   (8e-3 is one bf16 ulp, as for the norm alone; the factor 2 covers the
   norm's own fp32 arithmetic, which is orders of magnitude smaller.)
+For fp16 I/O the per-ulp term is 1e-3 |o| + 2^-24 (one fp16 ulp, subnormal
+results included), as for the fp16 norm; the accumulation terms are the same.
 """
 import numpy as np
 import pytest
@@ -22,24 +24,29 @@ from gpu_util import GUARD_BYTES, Guarded, assert_bytes_equal, gamma_to_device, 
 pytestmark = pytest.mark.gpu
 U = 2.0 ** -24
 BF16 = synth.BF16
+F16 = synth.F16
 
 
-def make(seed, T, hidden, hq, hkv, D, token_scale=(0.25, 4.0)):
+def make(seed, T, hidden, hq, hkv, D, token_scale=(0.25, 4.0), dtype=BF16):
     """x ~ N(0,1) times a per-token scale; w ~ N(0, 1/hidden) (unit-variance
     outputs); gamma ~ U(0.5, 1.5)."""
     N = (hq + 2 * hkv) * D
-    x = synth.make_x(seed, T, hidden, BF16, token_scale=token_scale)
-    w = synth.to_dtype(synth.normal(seed + 7, 0, N * hidden).reshape(N, hidden) / np.sqrt(hidden), BF16)
-    return x, w, synth.make_gamma(seed, 3, D, BF16), synth.make_gamma(seed, 4, D, BF16)
+    x = synth.make_x(seed, T, hidden, dtype, token_scale=token_scale)
+    w = synth.to_dtype(synth.normal(seed + 7, 0, N * hidden).reshape(N, hidden) / np.sqrt(hidden), dtype)
+    return x, w, synth.make_gamma(seed, 3, D, dtype), synth.make_gamma(seed, 4, D, dtype)
 
 
-def tolerance(x, w, y64, gq, gk, hq, hkv, D, norm=True):
+def _ulp_term(y, dtype):
+    return 8e-3 * np.abs(y) if dtype == BF16 else 1e-3 * np.abs(y) + U
+
+
+def tolerance(x, w, y64, gq, gk, hq, hkv, D, norm=True, dtype=BF16):
     """Per-element bound (see the module docstring)."""
-    xd, wd = np.abs(oracle.decode(x, BF16)), np.abs(oracle.decode(w, BF16))
+    xd, wd = np.abs(oracle.decode(x, dtype)), np.abs(oracle.decode(w, dtype))
     A = xd @ wd.T
     K = x.shape[1]
-    acc = oracle.decode(x, BF16) @ oracle.decode(w, BF16).T
-    tol = 8e-3 * np.abs(y64) + 2 * K * U * A
+    acc = oracle.decode(x, dtype) @ oracle.decode(w, dtype).T
+    tol = _ulp_term(y64, dtype) + 2 * K * U * A
     if norm:
         T = x.shape[0]
         for c0, nh, g in ((0, hq, gq), (hq * D, hkv, gk)):
@@ -50,24 +57,25 @@ def tolerance(x, w, y64, gq, gk, hq, hkv, D, norm=True):
             rms = np.sqrt(np.mean(a * a, axis=-1, keepdims=True))
             An = np.linalg.norm(A[:, sl].reshape(T, nh, D), axis=-1, keepdims=True)
             an = np.linalg.norm(a, axis=-1, keepdims=True)
-            gd = np.abs(oracle.decode(g, BF16))
+            gd = np.abs(oracle.decode(g, dtype))
             yo = np.abs(y64[:, sl].reshape(T, nh, D))
             extra = 2 * K * U * (gd * A[:, sl].reshape(T, nh, D) / rms + yo * An / an)
-            tol[:, sl] = 8e-3 * yo.reshape(T, nh * D) + extra.reshape(T, nh * D)
+            tol[:, sl] = _ulp_term(yo.reshape(T, nh * D), dtype) + extra.reshape(T, nh * D)
     return tol
 
 
-def run_proj(x, w, hq, hkv, D, gq, gk, eps, ld=None, plain=False, label=""):
+def run_proj(x, w, hq, hkv, D, gq, gk, eps, ld=None, plain=False, label="", dtype=BF16):
     T, hidden = x.shape
     N = w.shape[0]
     ld = ld or N
-    print(f"[proj] {label} T={T} hidden={hidden} hq={hq} hkv={hkv} D={D} ld={ld} plain={plain}",
-          flush=True)
-    xt, wt = host_to_device(x, BF16), host_to_device(w, BF16)
-    fill = np.full((T, ld), 0x7FC0, dtype=np.uint16)            # NaN: must be overwritten or kept
-    out = Guarded(fill, BF16)
-    q.qknorm_qkv_proj_per_head(xt, wt, out.t, hq, hkv, D, gamma_to_device(gq, BF16),
-                               gamma_to_device(gk, BF16) if hkv else None, eps, plain=plain)
+    print(f"[proj] {label} T={T} hidden={hidden} hq={hq} hkv={hkv} D={D} ld={ld} plain={plain} "
+          f"{synth.DTYPE_NAMES[dtype]}", flush=True)
+    xt, wt = host_to_device(x, dtype), host_to_device(w, dtype)
+    nan = 0x7FC0 if dtype == BF16 else 0x7E00
+    fill = np.full((T, ld), nan, dtype=np.uint16)               # NaN: must be overwritten or kept
+    out = Guarded(fill, dtype)
+    q.qknorm_qkv_proj_per_head(xt, wt, out.t, hq, hkv, D, gamma_to_device(gq, dtype),
+                               gamma_to_device(gk, dtype) if hkv else None, eps, plain=plain)
     torch.cuda.synchronize()
     got = out.host()
     assert out.guards_intact(), "write outside the output"
@@ -75,11 +83,11 @@ def run_proj(x, w, hq, hkv, D, gq, gk, eps, ld=None, plain=False, label=""):
     return got[:, :N]
 
 
-def check(x, w, hq, hkv, D, gq, gk, eps, got, plain=False, label=""):
-    y64, yr = oracle.qkv_proj_per_head(x, w, BF16, hq, hkv, D, gq, gk if hkv else None, eps,
+def check(x, w, hq, hkv, D, gq, gk, eps, got, plain=False, label="", dtype=BF16):
+    y64, yr = oracle.qkv_proj_per_head(x, w, dtype, hq, hkv, D, gq, gk if hkv else None, eps,
                                        norm=not plain)
-    g = oracle.decode(got, BF16)
-    tol = tolerance(x, w, y64, gq, gk, hq, hkv, D, norm=not plain)
+    g = oracle.decode(got, dtype)
+    tol = tolerance(x, w, y64, gq, gk, hq, hkv, D, norm=not plain, dtype=dtype)
     bad = ~(np.abs(g - y64) <= tol)
     if bad.any():
         i, j = np.argwhere(bad)[0]
@@ -113,6 +121,22 @@ def test_plain_projection_and_padding():
     check(x, w, hq, hkv, D, gq, gk, 0.0, got, plain=True, label="plain")
     got = run_proj(x, w, hq, hkv, D, gq, gk, synth.eps_f32(1e-6), ld=N + 40, label="fused padded")
     check(x, w, hq, hkv, D, gq, gk, synth.eps_f32(1e-6), got, label="fused padded")
+
+
+@pytest.mark.parametrize("T,hidden,hq,hkv,D", [
+    (100, 192, 4, 2, 128),       # ragged rows, three K steps
+    (333, 512, 3, 1, 64),        # D = 64, a half tile of columns
+    (300, 1024, 32, 8, 128),     # the Qwen3-8B head layout, two row tiles
+])
+def test_fp16_projection_against_oracle(T, hidden, hq, hkv, D):
+    # the same kernel with fp16 operands, gamma and output (v_mfma_f32_32x32x16_f16)
+    x, w, gq, gk = make(90 + T, T, hidden, hq, hkv, D, dtype=F16)
+    eps = synth.eps_f32(1e-6)
+    N = w.shape[0]
+    got = run_proj(x, w, hq, hkv, D, gq, gk, eps, ld=N + 24, label="fp16 fused", dtype=F16)
+    check(x, w, hq, hkv, D, gq, gk, eps, got, label=f"fp16 fused T={T} K={hidden}", dtype=F16)
+    got = run_proj(x, w, hq, hkv, D, gq, gk, eps, plain=True, label="fp16 plain", dtype=F16)
+    check(x, w, hq, hkv, D, gq, gk, eps, got, plain=True, label="fp16 plain", dtype=F16)
 
 
 def test_fused_equals_unfused_up_to_the_intermediate_rounding():
