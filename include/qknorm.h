@@ -180,7 +180,7 @@ int qknorm_apply_scalar(void *qkv, int64_t T, int64_t ld, int64_t wq, int64_t wk
  *     accumulated in fp32 either way and rounded once, to nearest-even.
  *     flags: 0, or QKNORM_PROJ_PLAIN for the plain projection (gamma and eps
  *     unused).
- * Requires: hidden a multiple of 64 and head_dim 64 or 128 (else
+ * Requires: hidden a multiple of 64 and head_dim 64, 128 or 256 (else
  * QKNORM_E_UNSUPPORTED); ldx, ldw >= hidden and ld >= N; x, w, qkv and gamma
  * 16-byte aligned, pitches*2 multiples of 16 bytes; 256 rows of x, of w and
  * of qkv each below 2 GiB.  x, w and gamma must not overlap qkv.

@@ -315,7 +315,6 @@ __global__ __launch_bounds__(G::kThreads) void qkv_proj_kernel(
   // its row sum of squares is the lane's fma chain over those blocks, then
   // the 32-lane sum of the half-wave that holds the row.
   constexpr int JH = D / 32;                    // blocks per head
-  static_assert(NB % JH == 0, "a wave's columns must be whole heads");
   if (norm) {
     float g[NB];
     bool normed[NB];
@@ -328,26 +327,59 @@ __global__ __launch_bounds__(G::kThreads) void qkv_proj_kernel(
       const Elem* gp = reinterpret_cast<const Elem*>(is_q ? gamma_q : gamma_k);
       g[j] = normed[j] ? (float)gp[n % D] : 1.f;
     }
+    if constexpr (JH <= NB) {
+      static_assert(NB % JH == 0, "a wave's columns must be whole heads");
 #pragma unroll
-    for (int i = 0; i < MB; ++i)
+      for (int i = 0; i < MB; ++i)
 #pragma unroll
-      for (int h = 0; h < NB / JH; ++h) {
-        // the same for every lane and every block of one head (heads lie in
-        // one region and the tile's columns past N are whole heads)
-        if (!normed[h * JH]) continue;
+        for (int h = 0; h < NB / JH; ++h) {
+          // the same for every lane and every block of one head (heads lie in
+          // one region and the tile's columns past N are whole heads)
+          if (!normed[h * JH]) continue;
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            float s = 0.f;
+#pragma unroll
+            for (int jj = 0; jj < JH; ++jj)
+              s = __builtin_fmaf(acc[i][h * JH + jj][e], acc[i][h * JH + jj][e], s);
+            s = group_sum<32>(s);
+            const float sc = rms_scale(s, inv_d, eps);
+#pragma unroll
+            for (int jj = 0; jj < JH; ++jj)
+              acc[i][h * JH + jj][e] = (acc[i][h * JH + jj][e] * g[h * JH + jj]) * sc;
+          }
+        }
+    } else {
+      // a head spans the tile's two column waves (D = 2 * kWaveN): each wave
+      // leaves its half-head row sums in LDS (the stages are free), and both
+      // add the two halves in the same order, so they scale with the same bits
+      static_assert(JH == 2 * NB && G::WN == 2 && G::BN == D, "one head across the two column waves");
+      float* half = reinterpret_cast<float*>(smem);   // [WN][BM]
+#pragma unroll
+      for (int i = 0; i < MB; ++i)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           float s = 0.f;
 #pragma unroll
-          for (int jj = 0; jj < JH; ++jj)
-            s = __builtin_fmaf(acc[i][h * JH + jj][e], acc[i][h * JH + jj][e], s);
+          for (int j = 0; j < NB; ++j) s = __builtin_fmaf(acc[i][j][e], acc[i][j][e], s);
           s = group_sum<32>(s);
-          const float sc = rms_scale(s, inv_d, eps);
-#pragma unroll
-          for (int jj = 0; jj < JH; ++jj)
-            acc[i][h * JH + jj][e] = (acc[i][h * JH + jj][e] * g[h * JH + jj]) * sc;
+          const uint32_t r = wm * G::kWaveM + i * 32 + 8 * (e / 4) + 4 * (lane / 32) + e % 4;
+          if (lane % 32 == 0) half[wn * G::BM + r] = s;
         }
+      __syncthreads();
+      if (normed[0]) {
+#pragma unroll
+        for (int i = 0; i < MB; ++i)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const uint32_t r = wm * G::kWaveM + i * 32 + 8 * (e / 4) + 4 * (lane / 32) + e % 4;
+            const float sc = rms_scale(half[r] + half[G::BM + r], inv_d, eps);
+#pragma unroll
+            for (int j = 0; j < NB; ++j) acc[i][j][e] = (acc[i][j][e] * g[j]) * sc;
+          }
       }
+      __syncthreads();                           // the output staging reuses the LDS
+    }
   }
   // the bf16 tile goes through LDS (the stages are free after the loop's last
   // barrier) so rows leave as 16-byte stores
@@ -418,15 +450,19 @@ bool proj_shape_ok(const ProjArgs& a) {
          (uint64_t)((a.T + kBM - 1) / kBM) * (uint64_t)(((a.hq + 2 * a.hkv) * a.head_dim + kBN - 1) / kBN) *
                  (uint64_t)kThreads <
              (UINT64_C(1) << 32) &&
-         (a.head_dim == 64 || a.head_dim == 128);
+         (a.head_dim == 64 || a.head_dim == 128 || a.head_dim == 256);
 }
 
 hipError_t launch_qkv_proj(const ProjArgs& a, hipStream_t s) {
   const uint32_t N = (uint32_t)((a.hq + 2 * a.hkv) * a.head_dim);
   const dim3 grid((uint32_t)(((N + kBN - 1) / kBN) * ((a.T + kBM - 1) / kBM)));
-  auto kern = a.dtype == kF16
-                  ? (a.head_dim == 64 ? qkv_proj_kernel<Geo, kF16, 64> : qkv_proj_kernel<Geo, kF16, 128>)
-                  : (a.head_dim == 64 ? qkv_proj_kernel<Geo, kBF16, 64> : qkv_proj_kernel<Geo, kBF16, 128>);
+  auto pick = [&](auto k64, auto k128, auto k256) {
+    return a.head_dim == 64 ? k64 : (a.head_dim == 128 ? k128 : k256);
+  };
+  auto kern = a.dtype == kF16 ? pick(qkv_proj_kernel<Geo, kF16, 64>, qkv_proj_kernel<Geo, kF16, 128>,
+                                     qkv_proj_kernel<Geo, kF16, 256>)
+                              : pick(qkv_proj_kernel<Geo, kBF16, 64>, qkv_proj_kernel<Geo, kBF16, 128>,
+                                     qkv_proj_kernel<Geo, kBF16, 256>);
   // more than the default 64 KiB of dynamic LDS (gfx950 has 160 KiB per CU);
   // a host-side attribute, set on every call (no shared state between threads)
   const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),

@@ -223,7 +223,9 @@ def test_projection_validation(lib):
     assert pj(lib, dt=7) == q.QKNORM_E_DTYPE
     assert pj(lib, flags=2) == q.QKNORM_E_UNSUPPORTED
     assert pj(lib, hidden=96, ldx=96, ldw=96) == q.QKNORM_E_UNSUPPORTED     # K step of 64
-    assert pj(lib, D=96, ld=576) == q.QKNORM_E_UNSUPPORTED                 # head_dim 64 or 128
+    assert pj(lib, T=0, D=256, ld=1536) == q.QKNORM_OK                     # head_dim 64, 128, 256
+    assert pj(lib, D=96, ld=576) == q.QKNORM_E_UNSUPPORTED
+    assert pj(lib, D=512, ld=3072) == q.QKNORM_E_UNSUPPORTED
     assert pj(lib, ld=767) == q.QKNORM_E_SHAPE                             # ld < N = 768
     assert pj(lib, ldx=128) == q.QKNORM_E_SHAPE                            # ldx < hidden
     assert pj(lib, hidden=0) == q.QKNORM_E_SHAPE

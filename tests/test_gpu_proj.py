@@ -105,6 +105,8 @@ def check(x, w, hq, hkv, D, gq, gk, eps, got, plain=False, label="", dtype=BF16)
     (130, 256, 32, 8, 128),      # the Qwen3-8B head layout, two row tiles
     (64, 128, 0, 2, 64),         # K heads only
     (48, 64, 5, 0, 64),          # no K or V
+    (150, 256, 4, 2, 256),       # D = 256: a head spans the tile's two column waves
+    (70, 192, 0, 3, 256),        # D = 256, K heads only
 ])
 def test_fused_projection_against_oracle(T, hidden, hq, hkv, D):
     x, w, gq, gk = make(70 + T, T, hidden, hq, hkv, D)
@@ -127,6 +129,7 @@ def test_plain_projection_and_padding():
     (100, 192, 4, 2, 128),       # ragged rows, three K steps
     (333, 512, 3, 1, 64),        # D = 64, a half tile of columns
     (300, 1024, 32, 8, 128),     # the Qwen3-8B head layout, two row tiles
+    (260, 512, 8, 4, 256),       # D = 256
 ])
 def test_fp16_projection_against_oracle(T, hidden, hq, hkv, D):
     # the same kernel with fp16 operands, gamma and output (v_mfma_f32_32x32x16_f16)
