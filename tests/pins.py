@@ -552,7 +552,7 @@ def check_proj_selection():
     fused result must be the per-head oracle applied to those columns."""
     rng = np.random.default_rng(5)
     for dtype in DTYPES:
-        for (hq, hkv, D) in ((4, 2, 16), (3, 1, 32), (2, 0, 8)):
+        for (hq, hkv, D) in ((4, 2, 16), (3, 1, 32), (2, 0, 8), (2, 1, 128), (1, 1, 256)):
             N = (hq + 2 * hkv) * D
             K = N + 24
             T = 5
