@@ -7,7 +7,7 @@
 #include "qknorm_launch.hpp"
 
 #ifndef QKNORM_PH_THREADS
-#define QKNORM_PH_THREADS 512      // threads per per-head block
+#define QKNORM_PH_THREADS 512      // threads per per-head block (16- and 32-bit heads)
 #endif
 #ifndef QKNORM_PH_UNROLL
 #define QKNORM_PH_UNROLL 2         // heads per lane group per loop trip
@@ -48,10 +48,17 @@ static constexpr bool kFp8GammaLds = QKNORM_PH_GAMMA_LDS_FP8 != 0;
 #ifndef QKNORM_PH_UNROLL_FP8
 #define QKNORM_PH_UNROLL_FP8 1
 #endif
+#ifndef QKNORM_PH_THREADS_FP8
+#define QKNORM_PH_THREADS_FP8 256  // FP8 heads: smaller blocks measured faster
+#endif
 
 // Heads per lane group per loop trip.
 template <int DT>
 constexpr int ph_unroll() { return DT == kFP8 ? QKNORM_PH_UNROLL_FP8 : QKNORM_PH_UNROLL; }
+
+// Threads per per-head block.
+template <int DT>
+constexpr int ph_threads() { return DT == kFP8 ? QKNORM_PH_THREADS_FP8 : QKNORM_PH_THREADS; }
 
 // A workgroup barrier after this wave's LDS accesses have completed, with no
 // wait for its outstanding vector-memory loads (__syncthreads() would wait for
@@ -197,7 +204,7 @@ __device__ __forceinline__ void per_head_apply(const u32x4 (&v)[U], const float 
 // EXACT: a head is exactly LPH vectors (a power of two); otherwise it is
 // hvec < LPH vectors and the group's last LPH - hvec lanes stay idle.
 template <int DT, int LPH, int U, bool CONTIG, bool ONE, bool EXACT, bool TWO>
-__global__ __launch_bounds__(QKNORM_PH_THREADS) void per_head_kernel(
+__global__ __launch_bounds__(ph_threads<DT>()) void per_head_kernel(
     uint8_t* __restrict__ qkv, uint32_t ld_bytes, uint32_t T, PhRegion r0, PhRegion r1, FastDiv byN,
     float eps, float inv_d, uint32_t hvec) {
   using IO = IoTraits<DT>;
@@ -265,7 +272,7 @@ __global__ __launch_bounds__(QKNORM_PH_THREADS) void per_head_kernel(
   if constexpr (kGammaSgpr && EXACT && 4 * GV * LPH <= 64 && DT == kFP8 && kFp8GammaLds) {
     // the head's LPH*GV 16-byte gamma chunks: chunk c comes from wave
     // c % waves, through its scalar cache and one lane, into LDS
-    constexpr uint32_t kChunks = LPH * GV, kWaves = QKNORM_PH_THREADS / 64;
+    constexpr uint32_t kChunks = LPH * GV, kWaves = ph_threads<DT>() / 64;
     __shared__ u32x4 g_lds[kChunks];
     const uint32_t wv = threadIdx.x >> 6;
     const uint32_t* g32 = reinterpret_cast<const uint32_t*>(gamma);
@@ -951,13 +958,14 @@ template <int DT, int LPH>
 static hipError_t launch_per_head_t(const PerHeadArgs& a, hipStream_t s, int cus) {
   constexpr int U = ph_unroll<DT>();
   constexpr uint64_t CH = (64 / LPH) * U;
-  constexpr int kBlock = QKNORM_PH_THREADS;
+  constexpr int kBlock = ph_threads<DT>();
   constexpr uint64_t heads_per_block = CH * (kBlock / 64);
   const int es = IoTraits<DT>::kBytes;
   const uint32_t head_bytes = (uint32_t)(a.head_dim * es);
   const uint32_t hvec = head_bytes / 16;
   const bool exact = hvec == (uint32_t)LPH;
-  const uint64_t cap = (uint64_t)cus * QKNORM_PH_BLOCKS_PER_CU;
+  // the cap in waves is the same for every block size
+  const uint64_t cap = (uint64_t)cus * QKNORM_PH_BLOCKS_PER_CU * QKNORM_PH_THREADS / kBlock;
   const uint64_t Htot = (uint64_t)a.hq + a.hkv;
 
   // the non-empty regions, Q first; the grid cap is shared in proportion
