@@ -739,11 +739,16 @@ __device__ __forceinline__ float wave_gamma_max(const u32x4* __restrict__ g_lds,
 #endif
 
 // NQ, NK: slots of Q and of K (64 vectors each).  Rows: wave w of the grid
-// takes rows w, w + (waves in the grid), ...
-template <int DT, int NQ, int NK>
+// takes rows w, w + (waves in the grid), ...  APPLY: the phase-C form -- each
+// row's scale comes from the caller's nparts partials, added in order exactly
+// as apply_scalar_kernel adds them (G.inv_wq / G.inv_wk then hold 1 / the
+// full widths), and FP8 results are range-checked vector by vector, since a
+// caller's scale carries no bound.
+template <int DT, int NQ, int NK, bool APPLY>
 __global__ __launch_bounds__(QKNORM_LWW_BLOCK) void layerwise_wave_kernel(
     uint8_t* __restrict__ qkv, RowGeom G, WaveShards wq, WaveShards wk,
-    const uint8_t* __restrict__ gamma_q, const uint8_t* __restrict__ gamma_k, float eps) {
+    const uint8_t* __restrict__ gamma_q, const uint8_t* __restrict__ gamma_k, float eps,
+    const float* __restrict__ part_q, const float* __restrict__ part_k, uint32_t nparts) {
   constexpr uint32_t GV = Gam<DT>::kVecs;
   constexpr uint32_t kQg = NQ * 64 * GV, kKg = NK * 64 * GV;   // 16-byte gamma vectors
   extern __shared__ u32x4 g_lds[];             // gamma_q, then gamma_k
@@ -752,7 +757,7 @@ __global__ __launch_bounds__(QKNORM_LWW_BLOCK) void layerwise_wave_kernel(
   for (uint32_t i = threadIdx.x; i < kKg; i += blockDim.x) g_lds[kQg + i] = load16(gamma_k + i * 16);
   __syncthreads();
   bool exceed_q = true, exceed_k = true;
-  if constexpr (DT == kFP8) {
+  if constexpr (DT == kFP8 && !APPLY) {
     exceed_q = e4m3_may_exceed(wave_gamma_max<DT, NQ>(g_lds, lane), G.inv_wq);
     exceed_k = e4m3_may_exceed(wave_gamma_max<DT, NK>(g_lds + kQg, lane), G.inv_wk);
   }
@@ -769,8 +774,14 @@ __global__ __launch_bounds__(QKNORM_LWW_BLOCK) void layerwise_wave_kernel(
   for (; t < G.T; t += waves) {
     const uint32_t tn = t + waves;
     const Rsrc rn = row_rsrc(qkv, G.ld_bytes, tn < G.T ? tn : 0, tn < G.T ? qk_vecs : 0);
-    const float rq = rms_scale(wave_region_sumsq<DT, NQ>(xq, wq), G.inv_wq, eps);
-    const float rk = rms_scale(wave_region_sumsq<DT, NK>(xk, wk), G.inv_wk, eps);
+    float rq, rk;
+    if constexpr (APPLY) {
+      rq = rms_scale(combine(part_q + t, nparts, G.T), G.inv_wq, eps);
+      rk = rms_scale(combine(part_k + t, nparts, G.T), G.inv_wk, eps);
+    } else {
+      rq = rms_scale(wave_region_sumsq<DT, NQ>(xq, wq), G.inv_wq, eps);
+      rk = rms_scale(wave_region_sumsq<DT, NK>(xk, wk), G.inv_wk, eps);
+    }
     // keep the row packed between the two passes: without these the compiler
     // reuses the first pass's widened values and holds the whole row in fp32
 #pragma unroll
@@ -1175,9 +1186,24 @@ static hipError_t launch_lw_wave(const RowGeom& G, WaveShards wq, WaveShards wk,
   if (waves > G.T) waves = G.T;
   const uint32_t blocks = (uint32_t)((waves + kWaves - 1) / kWaves);
   const size_t lds = (size_t)(NQ + NK) * 64 * Gam<DT>::kVecs * 16;
-  hipLaunchKernelGGL((layerwise_wave_kernel<DT, NQ, NK>), dim3(blocks), dim3(QKNORM_LWW_BLOCK), lds,
+  hipLaunchKernelGGL((layerwise_wave_kernel<DT, NQ, NK, false>), dim3(blocks), dim3(QKNORM_LWW_BLOCK), lds,
                      s, (uint8_t*)a.qkv, G, wq, wk, (const uint8_t*)a.gamma_q,
-                     (const uint8_t*)a.gamma_k, a.eps);
+                     (const uint8_t*)a.gamma_k, a.eps, (const float*)nullptr, (const float*)nullptr, 0u);
+  return hipGetLastError();
+}
+
+// Phase C through the one-wave-per-row kernel (G.inv_wq / inv_wk: 1 / the full widths).
+template <int DT, int NQ, int NK>
+static hipError_t launch_lw_wave_apply(const RowGeom& G, const ApplyArgs& a, hipStream_t s, int cus) {
+  constexpr uint32_t kWaves = QKNORM_LWW_BLOCK / 64;
+  uint64_t waves = (uint64_t)cus * QKNORM_LWW_WAVES_PER_CU;
+  if (waves > G.T) waves = G.T;
+  const uint32_t blocks = (uint32_t)((waves + kWaves - 1) / kWaves);
+  const size_t lds = (size_t)(NQ + NK) * 64 * Gam<DT>::kVecs * 16;
+  const WaveShards none{1, 64, 1};
+  hipLaunchKernelGGL((layerwise_wave_kernel<DT, NQ, NK, true>), dim3(blocks), dim3(QKNORM_LWW_BLOCK), lds,
+                     s, (uint8_t*)a.qkv, G, none, none, (const uint8_t*)a.gamma_q,
+                     (const uint8_t*)a.gamma_k, a.eps, a.part_q, a.part_k, (uint32_t)a.nparts);
   return hipGetLastError();
 }
 
@@ -1277,6 +1303,19 @@ static hipError_t launch_apply_dt(const ApplyArgs& a, hipStream_t s, int cus) {
   const uint32_t qv = (uint32_t)(a.wq * esize / 16), kv = (uint32_t)(a.wk * esize / 16);
   const float iq = a.norm_wq ? 1.0f / (float)a.norm_wq : 0.f;
   const float ik = a.norm_wk ? 1.0f / (float)a.norm_wk : 0.f;
+  if constexpr (DT == kFP8 && kLwWave) {
+    // FP8 rows of whole slots take the one-wave-per-row kernel, as in the fused call
+    if (qv % 64 == 0 && kv % 64 == 0) {
+      RowGeom G = make_geom(a.T, a.ld, a.wq, a.wk, 1, esize);
+      G.inv_wq = iq;
+      G.inv_wk = ik;
+      const uint32_t nq = qv / 64, nk = kv / 64;
+#define QKNORM_LWW_APPLY(Q, K) \
+  if (nq == Q && nk == K) return launch_lw_wave_apply<DT, Q, K>(G, a, s, cus);
+      QKNORM_LWW_SHAPES(QKNORM_LWW_APPLY)
+#undef QKNORM_LWW_APPLY
+    }
+  }
   // vectors per thread and block size: at most 512 threads, as few idle
   // (thread, vector) slots as possible, fewer vectors per thread on a tie
   const uint32_t nv = qv + kv;
