@@ -59,8 +59,10 @@ def _load():
         lib.oracle_apply.argtypes = [P, I32, I64, I64, I64, I64, P, P, I32, D, D, P, P, D, P, P]
         lib.oracle_round.argtypes = [P, I64, I32, P]
         for f in (lib.oracle_per_head, lib.oracle_layerwise, lib.oracle_partials,
-                  lib.oracle_apply, lib.oracle_round, lib.oracle_max_threads):
+                  lib.oracle_apply, lib.oracle_round, lib.oracle_max_threads,
+                  lib.oracle_set_threads):
             f.restype = I32
+        lib.oracle_set_threads.argtypes = [I32]
         _lib = lib
     return _lib
 
@@ -68,6 +70,12 @@ def _load():
 def max_threads() -> int:
     """OpenMP threads the oracle's parallel loops use."""
     return int(_load().oracle_max_threads())
+
+
+def set_threads(n: int) -> int:
+    """Use n OpenMP threads from now on (results do not depend on it); returns
+    the count in effect."""
+    return int(_load().oracle_set_threads(int(n)))
 
 
 def _storage(dtype: int):

@@ -275,6 +275,19 @@ int oracle_max_threads(void)
 #endif
 }
 
+/* Threads for the parallel loops that follow (timing at a chosen core count);
+ * the results do not depend on it: every token is computed the same way. */
+int oracle_set_threads(int n)
+{
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+    return omp_get_max_threads();
+#else
+    (void)n;
+    return 1;
+#endif
+}
+
 /* Per-head QK-Norm on fused rows x[T, ld]: Q heads 0..hq-1 at columns h*D with
  * gamma_q, K heads 0..hkv-1 at columns hq*D + h*D with gamma_k (both of length
  * D).  Writes the fp64 result to y[T*ld] and the dtype-rounded result to
