@@ -23,7 +23,10 @@ GIB4 = 1 << 32
 
 def _tiled(seed, T, ld, dtype, **kw):
     block = upload_rows(seed, BLOCK, ld, dtype, **kw)
-    big = block.repeat(T // BLOCK, 1)
+    # repeat through a same-size integer view (float8 repeats are not
+    # implemented everywhere)
+    view = {1: torch.uint8, 2: torch.int16, 4: torch.int32}[block.element_size()]
+    big = block.view(view).repeat(T // BLOCK, 1).view(block.dtype)
     del block
     return big
 
@@ -67,12 +70,15 @@ def test_per_head_past_4gib():
     _free()
 
 
-def test_layerwise_fused_and_two_phase_past_4gib():
-    dtype, T, wq, wk, ld, R = synth.BF16, 32 * BLOCK, 8192, 1024, 10240, 8
+@pytest.mark.parametrize("dtype", [synth.BF16, synth.F8], ids=["bf16", "fp8"])
+def test_layerwise_fused_and_two_phase_past_4gib(dtype):
+    es = synth.esize(dtype)
+    T, wq, wk, ld, R = (64 if es == 1 else 32) * BLOCK, 8192, 1024, 10240, 8
     seed = 72
-    print(f"[huge layerwise] T={T} ld={ld}: {T * ld * 2 / 2**30:.1f} GiB twice", flush=True)
+    print(f"[huge layerwise] {synth.DTYPE_NAMES[dtype]} T={T} ld={ld}: {T * ld * es / 2**30:.1f} GiB twice",
+          flush=True)
     a = _tiled(seed, T, ld, dtype, token_scale=(0.1, 10.0))
-    assert a.numel() * 2 > GIB4
+    assert a.numel() * es > GIB4
     b = a.clone()
     gq = synth.make_gamma(seed, 3, wq, dtype)
     gk = synth.make_gamma(seed, 4, wk, dtype)
@@ -84,7 +90,7 @@ def test_layerwise_fused_and_two_phase_past_4gib():
     q.qknorm_partial_sumsq(b, wq, wk, R, pq, pk)
     q.qknorm_apply_scalar(b, wq, wk, pq, pk, wq, wk, gqd, gkd, eps)
     torch.cuda.synchronize()
-    assert torch.equal(a.view(torch.int16), b.view(torch.int16)), "fused and two-phase differ"
+    assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), "fused and two-phase differ"
     del b, pq, pk
     _free()
     rows = _rows(T)
