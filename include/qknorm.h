@@ -108,7 +108,12 @@ int qknorm_per_head(void *qkv, int64_t T, int64_t ld, int32_t hq, int32_t hkv,
  * are each normalised over their whole width.  The sum of squares of each is
  * taken as nshards contiguous equal shard partials in fp32, which are added
  * in shard order; the mean divides by the FULL width.  Each element is read
- * from memory once and written once.
+ * from memory once and written once while each of Q and K is at most
+ * min(nshards, 8) x 4 KiB per row (bf16: 2048 values per shard-owning wave,
+ * so 16384 with 8 shards, 2048 with one; FP8: not both at that limit), and
+ * for FP8 also when Q is 4, 8 or 16 KiB and K a quarter or an eighth of it.
+ * Wider rows take a streamed kernel that reads the row a second time to
+ * apply the scale (that re-read is mostly served from L2).
  * (SwiftQK summary page, newx.sg, Abstract: the layerwise normalisation
  *  factor depends on the full hidden vector.  SwiftQK verdict page, key
  *  machinery: the per-shard factor over S_local,r is replaced by the global

@@ -188,8 +188,6 @@ int qknorm_apply_scalar(void* qkv, int64_t T, int64_t ld, int64_t wq, int64_t wk
   return finish(qknorm::launch_apply_scalar(a, static_cast<hipStream_t>(stream), cus));
 }
 
-}  // extern "C"
-
 int qknorm_qkv_proj_per_head(const void* x, int64_t ldx, const void* w, int64_t ldw, void* qkv,
                              int64_t ld, int64_t T, int64_t hidden, int32_t hq, int32_t hkv,
                              int32_t head_dim, const void* gamma_q, const void* gamma_k, float eps,
@@ -217,3 +215,5 @@ int qknorm_qkv_proj_per_head(const void* x, int64_t ldx, const void* w, int64_t 
   if (!touched) return QKNORM_OK;
   return finish(qknorm::launch_qkv_proj(a, static_cast<hipStream_t>(stream)));
 }
+
+}  // extern "C"

@@ -15,6 +15,9 @@
 #ifndef QKNORM_PH_BLOCKS_PER_CU
 #define QKNORM_PH_BLOCKS_PER_CU 160 // per-head grid cap, blocks per CU (one trip for most sizes)
 #endif
+#ifndef QKNORM_PH_WAVES_PER_CU_FP8
+#define QKNORM_PH_WAVES_PER_CU_FP8 (QKNORM_PH_BLOCKS_PER_CU * QKNORM_PH_THREADS / 64)
+#endif
 #ifndef QKNORM_LW_WAVES_PER_CU
 #define QKNORM_LW_WAVES_PER_CU 512   // layerwise grid cap, waves per CU
 #endif
@@ -106,6 +109,27 @@ static inline FastDiv make_fastdiv(uint32_t d) {
   while ((UINT64_C(1) << l) < d) ++l;
   const uint64_t p = UINT64_C(1) << (31 + l);
   return FastDiv{(uint32_t)((p + d - 1) / d), 31 + l};
+}
+
+// The same method for 64-bit dividends below 2^40 (divisor 1 <= d < 2^31):
+// m = ceil(2^(40+l) / d) <= 2^41 and floor(n / d) = floor(m * n / 2^(40+l)),
+// the product (below 2^81) taken as its high and low 64-bit words.
+struct FastDiv40 {
+  uint64_t m;
+  uint32_t sh;
+  __device__ __forceinline__ uint32_t div(uint64_t n) const {
+    const uint64_t hi = __umul64hi(m, n), lo = m * n;
+    return (uint32_t)(sh >= 64 ? hi >> (sh - 64) : (hi << (64 - sh)) | (lo >> sh));
+  }
+};
+
+static constexpr uint64_t kFastDiv40Limit = UINT64_C(1) << 40;
+
+static inline FastDiv40 make_fastdiv40(uint32_t d) {
+  uint32_t l = 0;
+  while ((UINT64_C(1) << l) < d) ++l;
+  const unsigned __int128 p = (unsigned __int128)1 << (40 + l);
+  return FastDiv40{(uint64_t)((p + d - 1) / d), 40 + l};
 }
 
 // One region of heads: H per row, starting `col_bytes` into each row, with
@@ -205,7 +229,7 @@ __device__ __forceinline__ void per_head_apply(const u32x4 (&v)[U], const float 
 // hvec < LPH vectors and the group's last LPH - hvec lanes stay idle.
 template <int DT, int LPH, int U, bool CONTIG, bool ONE, bool EXACT, bool TWO>
 __global__ __launch_bounds__(ph_threads<DT>()) void per_head_kernel(
-    uint8_t* __restrict__ qkv, uint32_t ld_bytes, uint32_t T, PhRegion r0, PhRegion r1, FastDiv byN,
+    uint8_t* __restrict__ qkv, uint32_t ld_bytes, uint32_t T, PhRegion r0, PhRegion r1, FastDiv40 byN,
     float eps, float inv_d, uint32_t hvec) {
   using IO = IoTraits<DT>;
   using Trip = PerHeadTrip<LPH, U, CONTIG>;
@@ -233,8 +257,8 @@ __global__ __launch_bounds__(ph_threads<DT>()) void per_head_kernel(
     second = blockIdx.x >= r0.blocks;
     lblock = blockIdx.x - (second ? r0.blocks : 0);
   } else {
-    const uint32_t c0 = byN.div(blockIdx.x * r1.blocks);
-    const uint32_t c1 = byN.div((blockIdx.x + 1) * r1.blocks);
+    const uint32_t c0 = byN.div((uint64_t)blockIdx.x * r1.blocks);
+    const uint32_t c1 = byN.div((uint64_t)(blockIdx.x + 1) * r1.blocks);
     second = c1 > c0;
     lblock = second ? c0 : blockIdx.x - c1;
   }
@@ -976,7 +1000,8 @@ static hipError_t launch_per_head_t(const PerHeadArgs& a, hipStream_t s, int cus
   const uint32_t hvec = head_bytes / 16;
   const bool exact = hvec == (uint32_t)LPH;
   // the cap in waves is the same for every block size
-  const uint64_t cap = (uint64_t)cus * QKNORM_PH_BLOCKS_PER_CU * QKNORM_PH_THREADS / kBlock;
+  const uint64_t cap = DT == kFP8 ? (uint64_t)cus * QKNORM_PH_WAVES_PER_CU_FP8 / (kBlock / 64)
+                                  : (uint64_t)cus * QKNORM_PH_BLOCKS_PER_CU * QKNORM_PH_THREADS / kBlock;
   const uint64_t Htot = (uint64_t)a.hq + a.hkv;
 
   // the non-empty regions, Q first; the grid cap is shared in proportion
@@ -1013,7 +1038,7 @@ static hipError_t launch_per_head_t(const PerHeadArgs& a, hipStream_t s, int cus
     reg[0].stride_rows = 0;
   }
   const bool two = n == 2;
-  void (*kern)(uint8_t*, uint32_t, uint32_t, PhRegion, PhRegion, FastDiv, float, float, uint32_t);
+  void (*kern)(uint8_t*, uint32_t, uint32_t, PhRegion, PhRegion, FastDiv40, float, float, uint32_t);
   if (contig)
     kern = one ? per_head_kernel<DT, LPH, U, true, true, true, false>
                : per_head_kernel<DT, LPH, U, true, false, true, false>;
@@ -1027,12 +1052,13 @@ static hipError_t launch_per_head_t(const PerHeadArgs& a, hipStream_t s, int cus
                       : per_head_kernel<DT, LPH, U, false, false, false, true>)
                : (one ? per_head_kernel<DT, LPH, U, false, true, false, false>
                       : per_head_kernel<DT, LPH, U, false, false, false, false>);
-  // interleave the two regions' blocks while (N + 1) * blocks1 stays a valid
-  // fast-division dividend (always, at up to 160 blocks per CU on 256 CUs)
+  // interleave the two regions' blocks: the largest dividend, N * blocks1,
+  // stays far below 2^40 for the capped grids used here (N is at most 320
+  // blocks per CU), so the interleave applies to every shape
   const uint64_t N = (uint64_t)reg[0].blocks + reg[1].blocks;
-  FastDiv byN{0, 0};
-  if (reg[1].blocks != 0 && (N + 1) * reg[1].blocks < (UINT64_C(1) << 31))
-    byN = make_fastdiv((uint32_t)N);
+  FastDiv40 byN{0, 0};
+  if (reg[1].blocks != 0 && N * reg[1].blocks < kFastDiv40Limit)
+    byN = make_fastdiv40((uint32_t)N);
   hipLaunchKernelGGL(kern, dim3((uint32_t)N), dim3(kBlock), 0, s, (uint8_t*)a.qkv,
                      (uint32_t)(a.ld * es), (uint32_t)a.T, reg[0], reg[1], byN, a.eps,
                      1.0f / (float)a.head_dim, hvec);
