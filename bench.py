@@ -95,29 +95,39 @@ def sizes(p):
 class Timer:
     """Times `steps` back-to-back launches on the launch stream.
 
-    One HIP event pair brackets the whole timed region (so no event sits
-    between two kernels); the mean launch duration is its elapsed time / steps.
-    Host wall time is taken over the same region between synchronisations.
-    A separate, shorter pass with an event pair around every launch gives the
-    spread (p10/p50/p90); those per-launch figures include the events' own
-    overhead (about 2 us each on this part) and are reported only as spread.
+    Host wall time covers exactly the `steps` launches, between two
+    synchronisations.  One HIP event pair brackets the launches after the
+    first LEAD of them: when the first event is stamped the GPU is already
+    running the lead launches, and the host stays ahead of the GPU from then
+    on, so the bracket holds back-to-back kernels only (no host submission
+    time of the first launch); the mean launch duration is its elapsed time
+    over the launches it holds.  A separate, shorter pass with an event pair
+    around every launch gives the spread (p10/p50/p90); those per-launch
+    figures include the events' own overhead (about 2 us each on this part)
+    and are reported only as spread.
     """
+
+    LEAD = 2
 
     def __init__(self, torch):
         self.torch = torch
 
     def run(self, steps, launch, first=0):
         torch = self.torch
+        lead = self.LEAD if steps > self.LEAD else 0
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        e0.record()
-        for i in range(first, first + steps):
+        if lead == 0:
+            e0.record()
+        for k, i in enumerate(range(first, first + steps)):
             launch(i)
+            if k + 1 == lead:
+                e0.record()
         e1.record()
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
-        return wall, e0.elapsed_time(e1) * 1e3 / steps
+        return wall, e0.elapsed_time(e1) * 1e3 / (steps - lead)
 
     def spread(self, steps, launch, first=0):
         torch = self.torch
@@ -163,7 +173,31 @@ def pool_count(buf_bytes: int, min_copies=2) -> int:
 
 # ------------------------------------------------------------------- cases --
 
-def bench_per_head(q, torch, dev, p, steps, warmup, label, max_copies=None, spread=True):
+def graph_replay_us(torch, launch, steps, first=0):
+    """Mean GPU time per launch of `steps` launches captured in one hipGraph and
+    replayed (no host work between the launches).  The graph is replayed once
+    untimed, then once between a HIP event pair."""
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            for i in range(first, first + steps):
+                launch(i, side.cuda_stream)
+    torch.cuda.synchronize()
+    graph.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / steps
+    del graph
+    return us
+
+
+def bench_per_head(q, torch, dev, p, steps, warmup, label, max_copies=None, spread=True, graph=False):
     from qk_norm_amd import synth
     lib = q.load()
     es, ges = sizes(p)
@@ -185,12 +219,20 @@ def bench_per_head(q, torch, dev, p, steps, warmup, label, max_copies=None, spre
         if rc:
             raise RuntimeError(f"qknorm_per_head: {q.strerror(rc)}")
 
+    def launch_on(i, s):
+        a = args[i % n]
+        rc = lib.qknorm_per_head(*a[:-1], s)
+        if rc:
+            raise RuntimeError(f"qknorm_per_head: {q.strerror(rc)}")
+
     warm = warm_clocks(torch, launch)
     for i in range(warmup):
         launch(i)
     timer = Timer(torch)
     wall, mean_us = timer.run(steps, launch, first=warmup)
     spread = timer.spread(min(steps, 200), launch, first=warmup + steps) if spread else {}
+    if graph:
+        spread["graph_replay_us"] = graph_replay_us(torch, launch_on, steps)
     bytes_alg = 2 * p.T * (p.wq + p.wk) * es + (p.head_dim * ges) * (1 + (p.hkv > 0))
     del pool
     torch.cuda.empty_cache()
@@ -488,24 +530,141 @@ def bench_d2d_copy(torch, dev, nbytes, steps=400, warmup=40):
             "gbs": 2 * nbytes / (mean_us * 1e-6) / 1e9}
 
 
-def cpu_baseline(p, q, torch, dev, budget_s=10.0):
-    """The fp64 C oracle on the headline input, timed on the host's cores for about
-    budget_s of wall time.  Its first result also checks one fresh GPU launch on the
-    same input, element by element (the tolerance the tests use for bf16)."""
+CEILING_LIB = os.path.join(ROOT, "qk_norm_amd", "libqknorm_ceiling.so")
+STREAM_MODES = {0: "in_place", 1: "read_only", 2: "write_only"}
+# (vectors per lane per trip, threads per block, grid cap in blocks per CU; 0 = one trip)
+STREAM_SHAPES = ((1, 256, 0), (2, 256, 0), (1, 512, 0), (2, 512, 0), (4, 512, 0),
+                 (1, 256, 16), (1, 256, 24), (2, 256, 8), (2, 256, 12), (2, 256, 16),
+                 (1, 512, 8), (1, 512, 12), (2, 512, 4), (2, 512, 6), (2, 512, 8),
+                 (1, 1024, 0), (2, 1024, 0))
+
+
+def bench_stream(torch, dev, nbytes, steps=200, warmup=20, modes=(0, 1, 2)):
+    """Trivial streams over `nbytes` per launch with the norms' access width and
+    cache policy (16-byte buffer loads/stores, nt sc1): in place (read and write
+    every byte once), read only, write only; each over STREAM_SHAPES, buffers
+    rotating through >= 1 GiB.  The fastest shape of each mode is the practical
+    ceiling for a kernel that moves those bytes."""
+    import ctypes
+    if not os.path.exists(CEILING_LIB):
+        raise RuntimeError(f"{CEILING_LIB} is missing: run __graft_entry__.build()")
+    lib = ctypes.CDLL(CEILING_LIB)
+    lib.qknorm_ceiling_stream.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                          ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
+    lib.qknorm_ceiling_stream.restype = ctypes.c_int32
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    n = pool_count(nbytes)
+    pool = [torch.ones(nbytes // 2, dtype=torch.bfloat16, device=dev) for _ in range(n)]
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    out = {"bytes_per_direction": nbytes, "pool": n}
+    for mode in modes:
+        moved = nbytes * (2 if mode == 0 else 1)
+        rows = []
+        for u, threads, cap in STREAM_SHAPES:
+            max_blocks = cus * cap
+
+            def launch(i, u=u, threads=threads, max_blocks=max_blocks):
+                rc = lib.qknorm_ceiling_stream(pool[i % n].data_ptr(), nbytes, mode, u, threads, max_blocks,
+                                               sink.data_ptr(), stream)
+                if rc:
+                    raise RuntimeError(f"ceiling probe rc={rc}")
+
+            warm_clocks(torch, launch)
+            for i in range(warmup):
+                launch(i)
+            _, us = Timer(torch).run(steps, launch, first=warmup)
+            rows.append({"u": u, "threads": threads, "blocks_per_cu_cap": cap, "mean_us": us,
+                         "gbs": moved / (us * 1e-6) / 1e9})
+        best = min(rows, key=lambda r: r["mean_us"])
+        out[STREAM_MODES[mode]] = {"best": best, "bytes_moved": moved, "shapes": rows}
+        log(f"stream {STREAM_MODES[mode]} {nbytes / 2**20:.0f} MiB: best {best['mean_us']:.2f} us "
+            f"({best['gbs']:.0f} GB/s) at u={best['u']} threads={best['threads']} cap={best['blocks_per_cu_cap']}")
+    del pool
+    torch.cuda.empty_cache()
+    return out
+
+
+def summarize_trace(path, kernel, skip=0, count=0, nbytes=0.0, workgroup=0, grid=0):
+    """Kernel-trace CSV of rocprofv3 -> durations of the dispatches of kernels
+    whose name contains `kernel` (and, if given, of that workgroup and grid size
+    in threads along x), in dispatch order: the window [skip, skip+count)
+    (count 0: to the end).  Returns a dict of statistics in us."""
+    import csv
+    rows = []
+    with open(path, newline="") as f:
+        for r in csv.DictReader(f):
+            if workgroup and int(r.get("Workgroup_Size_X") or r.get("Workgroup_Size") or 0) != workgroup:
+                continue
+            if grid and int(r.get("Grid_Size_X") or r.get("Grid_Size") or 0) != grid:
+                continue
+            if kernel in r["Kernel_Name"]:
+                rows.append((int(r.get("Dispatch_Id") or 0), int(r["Start_Timestamp"]),
+                             int(r["End_Timestamp"]), r["Kernel_Name"]))
+    rows.sort(key=lambda r: (r[1], r[0]))
+    total = len(rows)
+    win = rows[skip:skip + count] if count else rows[skip:]
+    if not win:
+        raise SystemExit(f"no dispatches of {kernel!r} in the window (found {total})")
+    d = sorted((e - b) / 1e3 for _, b, e, _ in win)
+    m = len(d)
+    avg = sum(d) / m
+    name = win[0][3]
+    name = name[:name.index(">(") + 1] if ">(" in name else name.split("(")[0]
+    res = {"kernel": name, "dispatches_of_kernel": total, "window": [skip, skip + m],
+           "launches": m, "avg_us": avg, "p10_us": d[int(0.1 * (m - 1))], "median_us": d[(m - 1) // 2],
+           "p90_us": d[int(0.9 * (m - 1))], "min_us": d[0], "max_us": d[-1]}
+    if nbytes:
+        res["gbs_at_avg"] = nbytes / (avg * 1e-6) / 1e9
+        res["pct_of_8tbs"] = 100 * res["gbs_at_avg"] / HBM_PEAK_GBS
+    return res
+
+
+def oracle_threads_all() -> tuple[int, int]:
+    """(threads for the all-cores leg, host CPUs visible to this process).
+    The all-cores leg uses every CPU in the affinity mask, capped by
+    OMP_NUM_THREADS when the environment sets it (a host shared between jobs
+    gives each job that many)."""
+    visible = len(os.sched_getaffinity(0))
+    try:
+        cap = int(os.environ.get("OMP_NUM_THREADS", "0") or 0)
+    except ValueError:
+        cap = 0
+    return (min(visible, cap) if cap > 0 else visible), visible
+
+
+def cpu_baseline(p, q, torch, dev, run_s=2.0):
+    """The fp64 C oracle on the headline input, at 1 thread and on all host
+    cores: three runs per leg of about run_s seconds each (whole calls), the
+    median run's time per call reported.  The oracle's first result also
+    checks one fresh GPU launch on the same input, element by element (the
+    tolerance the tests use for bf16)."""
     import numpy as np
     import oracle
-    from qk_norm_amd import synth
-    n = 0
-    ref = None
-    t0 = time.perf_counter()
-    while True:
-        r = oracle.per_head(p.x, p.dtype, p.hq, p.hkv, p.head_dim, p.gamma_q, p.gamma_k, p.eps)
-        ref = ref or r
-        n += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s or el / n * (n + 1) > 3 * budget_s:
-            break
     bytes_alg = 2 * p.T * (p.wq + p.wk) * 2 + p.head_dim * 2
+    all_threads, visible = oracle_threads_all()
+    ref = None
+    legs = {}
+    for leg, want in (("one_thread", 1), ("all_cores", all_threads)):
+        used = oracle.set_threads(want)
+        runs, calls = [], []
+        for _ in range(3):
+            n, t0 = 0, time.perf_counter()
+            while True:
+                r = oracle.per_head(p.x, p.dtype, p.hq, p.hkv, p.head_dim, p.gamma_q, p.gamma_k, p.eps,
+                                    want_y=ref is None)
+                ref = ref or r
+                n += 1
+                el = time.perf_counter() - t0
+                if el >= run_s:
+                    break
+            runs.append(el / n)
+            calls.append(n)
+        med = sorted(runs)[1]
+        legs[leg] = {"threads": used, "us_per_call_median_of_3": med * 1e6,
+                     "us_per_call_runs": [r * 1e6 for r in runs], "calls_per_run": calls,
+                     "gbs": bytes_alg / med / 1e9}
+    oracle.set_threads(all_threads)
     # one launch on a fresh copy of the same input
     x = to_device(p.x, p.dtype, torch, dev)
     q.qknorm_per_head(x, p.hq, p.hkv, p.head_dim, to_device(p.gamma_q, p.dtype, torch, dev),
@@ -528,11 +687,14 @@ def cpu_baseline(p, q, torch, dev, budget_s=10.0):
               "ulp_over_1": int((ulp > 1).sum())}
     parity["pass"] = bool(parity["max_rel_err"] <= 8e-3 and parity["zero_where_oracle_zero"]
                           and parity["ulp_over_1"] == 0)
-    return {"value": bytes_alg * n / el / 1e9, "unit": "GB/s", "cores": oracle.max_threads(),
-            "kind": "oracle",
-            "sample": f"{n} full call(s) of the fp64 C oracle on the same [4096,48,128] bf16 input "
-                      f"({el:.1f} s)", "us_per_call": el / n * 1e6,
-            "parity_of_one_gpu_launch": parity}
+    a, o = legs["all_cores"], legs["one_thread"]
+    return {"value": a["gbs"], "unit": "GB/s", "cores": a["threads"], "kind": "oracle",
+            "sample": f"whole calls of the fp64 C oracle on the same [4096,48,128] bf16 input, "
+                      f"3 runs of >= {run_s:.0f} s per leg, median run; all-cores leg "
+                      f"{a['threads']} threads ({visible} host CPUs visible), "
+                      f"one-thread leg {o['gbs']:.2f} GB/s",
+            "us_per_call": a["us_per_call_median_of_3"], "host_cpus_visible": visible,
+            "legs": legs, "parity_of_one_gpu_launch": parity}
 
 
 # -------------------------------------------------------------------- main --
@@ -546,9 +708,26 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--case", default="headline",
                     choices=["headline", "prefill_layerwise", "prefill_per_head", "fp8_per_head",
-                             "fp8_prefill_layerwise", "proj", "decode", "sweep", "copy"],
+                             "fp8_prefill_layerwise", "proj", "decode", "sweep", "copy", "stream",
+                             "wide_layerwise"],
                     help="single case for profiling runs")
+    ap.add_argument("--stream-shape", metavar="U,THREADS,CAP",
+                    help="with --case stream: one in-place shape only (CAP in blocks per CU, 0: one trip)")
+    ap.add_argument("--stream-mib", type=int, default=48, help="with --stream-shape: MiB per direction")
+    ap.add_argument("--summarize-trace", metavar="CSV",
+                    help="summarise a rocprofv3 kernel-trace CSV (no GPU use) and exit")
+    ap.add_argument("--kernel", default="per_head_kernel", help="with --summarize-trace: name substring")
+    ap.add_argument("--skip", type=int, default=0, help="with --summarize-trace: dispatches to skip")
+    ap.add_argument("--count", type=int, default=0, help="with --summarize-trace: dispatches to take")
+    ap.add_argument("--bytes", type=float, default=0.0, help="with --summarize-trace: bytes per launch")
+    ap.add_argument("--workgroup", type=int, default=0, help="with --summarize-trace: workgroup size")
+    ap.add_argument("--grid", type=int, default=0, help="with --summarize-trace: grid size in threads")
     args = ap.parse_args()
+
+    if args.summarize_trace:
+        print(json.dumps(summarize_trace(args.summarize_trace, args.kernel, args.skip, args.count,
+                                         args.bytes, args.workgroup, args.grid)))
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: this QK-Norm build has no multi-GPU path "
@@ -574,6 +753,28 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"case": "copy", "bytes_read": n, "bytes_written": n}))
         return
+    if args.case == "stream":
+        res = {"case": "stream"}
+        if args.stream_shape:
+            # one in-place shape at one size (for a kernel trace of the ceiling)
+            u, threads, cap = (int(v) for v in args.stream_shape.split(","))
+            global STREAM_SHAPES
+            STREAM_SHAPES = ((u, threads, cap),)
+            res[f"{args.stream_mib}MiB"] = bench_stream(torch, dev, args.stream_mib << 20, args.steps,
+                                                       args.warmup, modes=(0,))
+        else:
+            for mib in (24, 48, 288, 576):
+                res[f"{mib}MiB"] = bench_stream(torch, dev, mib << 20)
+        print(json.dumps(res))
+        return
+    if args.case == "wide_layerwise":
+        # rows too wide for the register-resident kernels: Q 32768 + K 4096
+        # bf16 columns, 8 shards (the streamed layerwise kernel)
+        p = synth.layerwise_problem("wide_layerwise", 71, synth.BF16, 4096, 32768, 4096, 32768 + 2 * 4096,
+                                    8, outlier_frac=0.01)
+        print(json.dumps({"case": "wide_layerwise", **bench_layerwise(q, torch, dev, p, args.steps,
+                                                                      args.warmup, "wide [4096, 40960]")}))
+        return
     if args.case == "prefill_layerwise":
         p = synth.prefill_rows(T=32768)
         print(json.dumps({"case": "prefill_layerwise", **bench_layerwise(q, torch, dev, p, args.steps, args.warmup)}))
@@ -581,7 +782,8 @@ def main():
     if args.case == "fp8_per_head":
         p = synth.standalone_heads(T=4096, H=48, dtype=synth.F8)
         print(json.dumps({"case": "fp8_per_head",
-                          **bench_per_head(q, torch, dev, p, args.steps, args.warmup, "fp8 per-head")}))
+                          **bench_per_head(q, torch, dev, p, args.steps, args.warmup, "fp8 per-head",
+                                           graph=True)}))
         return
     if args.case == "fp8_prefill_layerwise":
         p = synth.prefill_rows(T=32768, dtype=synth.F8)
@@ -606,6 +808,7 @@ def main():
     t_start = time.perf_counter()
     p = synth.standalone_heads(T=4096, H=48)
     head = bench_per_head(q, torch, dev, p, args.steps, args.warmup, "headline per-head")
+    lead = Timer.LEAD if args.steps > Timer.LEAD else 0
     bytes_alg = head["bytes"]
     value = bytes_alg * args.steps / head["wall_s"] / 1e9
     achieved = head["gbs"]
@@ -628,10 +831,23 @@ def main():
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": read_traffic(bytes_alg),
                      "kernel": "per_head_kernel<bf16, 16 lanes/head>",
-                     "bytes_per_launch": bytes_alg},
+                     "bytes_per_launch": bytes_alg,
+                     "timing": f"HIP event pair on the launch stream around the last "
+                               f"{args.steps - lead} of the {args.steps} timed launches"},
+        # where the timed launches sit among this kernel's dispatches in a
+        # rocprofv3 kernel trace of this run (for --summarize-trace)
+        "trace_window": {"kernel": "per_head_kernel<1, 16, 2, true, true, true, false>",
+                         "skip": head["clock_warm_launches"] + args.warmup + lead,
+                         "count": args.steps - lead},
     }
     if not args.quick:
         cases = {}
+        for mib, kern_us in ((48, head["mean_us"]), (24, None)):
+            st = bench_stream(torch, dev, mib << 20, modes=(0,))
+            best = st["in_place"]["best"]
+            cases[f"stream_ceiling_in_place_{mib}MiB"] = {"best": best, "shapes": st["in_place"]["shapes"]}
+            if kern_us is not None:
+                result["headline_frac_of_stream_ceiling_48MiB"] = round(best["mean_us"] / kern_us, 4)
         p5 = synth.prefill_rows(T=32768)
         cases["prefill_T32768_layerwise"] = bench_layerwise(q, torch, dev, p5, 50, 5)
         p5h = synth.prefill_rows(T=32768, mode="per_head")
@@ -644,8 +860,13 @@ def main():
         for dt in (synth.F16, synth.F8):
             name = synth.DTYPE_NAMES[dt]
             c = bench_per_head(q, torch, dev, synth.standalone_heads(T=4096, H=48, dtype=dt), 400, 40,
-                               f"{name} per-head [4096, 48, 128]")
+                               f"{name} per-head [4096, 48, 128]", graph=dt == synth.F8)
             cases[f"{name}_T4096_H48_per_head"] = {k: c[k] for k in ("bytes", "mean_us", "gbs")}
+            if "graph_replay_us" in c:
+                cases[f"{name}_T4096_H48_per_head"]["graph_replay_us"] = c["graph_replay_us"]
+            if dt == synth.F8:
+                ceil_us = cases["stream_ceiling_in_place_24MiB"]["best"]["mean_us"]
+                cases[f"{name}_T4096_H48_per_head"]["frac_of_stream_ceiling_24MiB"] = ceil_us / c["mean_us"]
         p8 = synth.prefill_rows(T=32768, dtype=synth.F8)
         cases["fp8e4m3_prefill_T32768_layerwise"] = bench_layerwise(q, torch, dev, p8, 50, 5,
                                                                  "fp8e4m3 [32768, 10240]")

@@ -1,4 +1,6 @@
-"""Build the gfx950 HIP library in-tree: qk_norm_amd/libqknorm.so.
+"""Build the gfx950 HIP libraries in-tree: qk_norm_amd/libqknorm.so (the
+QK-Norm C ABI) and qk_norm_amd/libqknorm_ceiling.so (the bench's bandwidth
+ceiling probes, loaded by bench.py only).
 
     python -m qk_norm_amd.build            # or __graft_entry__.build()
 
@@ -18,6 +20,8 @@ CSRC = os.path.join(HERE, "csrc")
 SOURCES = [os.path.join(CSRC, "qknorm_api.hip"), os.path.join(CSRC, "qknorm_kernels.hip"),
            os.path.join(CSRC, "qknorm_proj.hip")]
 LIB = os.path.join(HERE, "libqknorm.so")
+CEILING_SOURCES = [os.path.join(CSRC, "ceiling_probe.hip")]
+CEILING_LIB = os.path.join(HERE, "libqknorm_ceiling.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
@@ -29,11 +33,12 @@ FLAGS = [
 ]
 
 
-def build(out: str = LIB, defines: list[str] | None = None, verbose: bool = False) -> str:
+def build(out: str = LIB, defines: list[str] | None = None, verbose: bool = False,
+          sources: list[str] | None = None) -> str:
     defs = list(defines or [])
     defs += os.environ.get("QKNORM_DEFINES", "").split()
     tmp = out + ".tmp"
-    cmd = [HIPCC, *FLAGS, *[f"-D{d}" for d in defs], "-o", tmp, *SOURCES]
+    cmd = [HIPCC, *FLAGS, *[f"-D{d}" for d in defs], "-o", tmp, *(sources or SOURCES)]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -44,5 +49,10 @@ def build(out: str = LIB, defines: list[str] | None = None, verbose: bool = Fals
     return out
 
 
+def build_ceiling(verbose: bool = False) -> str:
+    return build(CEILING_LIB, verbose=verbose, sources=CEILING_SOURCES)
+
+
 if __name__ == "__main__":
     print(build(verbose=True))
+    print(build_ceiling(verbose=True))
