@@ -19,6 +19,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "qknorm_device.hpp"
 #include "qknorm_launch.hpp"
 
@@ -209,21 +211,12 @@ __device__ __forceinline__ void sched_mfmas() {
   if constexpr (M > 0) __builtin_amdgcn_sched_group_barrier(0x008, M, 0);
 }
 
-template <class G, int DT, int D>
-__global__ __launch_bounds__(G::kThreads) void qkv_proj_kernel(
-    const uint8_t* __restrict__ x, uint32_t ldx_bytes, const uint8_t* __restrict__ w,
-    uint32_t ldw_bytes, uint8_t* __restrict__ out, uint64_t ld_bytes, uint32_t T, uint32_t K,
-    uint32_t N, uint32_t hq, uint32_t hkv, const uint8_t* __restrict__ gamma_q,
-    const uint8_t* __restrict__ gamma_k, float eps, float inv_d, uint32_t norm) {
-  constexpr int MB = G::MB, NB = G::NB, BK = G::BK;
-  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  const uint32_t tid = threadIdx.x, lane = tid & 63;
-  const uint32_t wave = uniform(tid >> 6);
-  const uint32_t wm = wave / G::WN, wn = wave % G::WN;
-  // Tile order.  Workgroups go to the 8 XCDs round robin (id % 8), each XCD
-  // with its own L2; the remap gives each XCD a contiguous run of tiles, and
-  // the runs walk the output in bands of GM tile rows, columns outer, so the
-  // blocks an XCD holds at once share a few A and B panels in its L2.
+// Tile order.  Workgroups go to the 8 XCDs round robin (id % 8), each XCD
+// with its own L2; the remap gives each XCD a contiguous run of tiles, and
+// the runs walk the output in bands of GM tile rows, columns outer, so the
+// blocks an XCD holds at once share a few A and B panels in its L2.
+template <class G>
+__device__ __forceinline__ void tile_origin(uint32_t T, uint32_t N, uint32_t* m0, uint32_t* n0) {
   const uint32_t n_tiles = (N + G::BN - 1) / G::BN, m_tiles = (T + G::BM - 1) / G::BM;
   uint32_t id = blockIdx.x;
   if (kXcdRemap) {
@@ -233,82 +226,24 @@ __global__ __launch_bounds__(G::kThreads) void qkv_proj_kernel(
   const uint32_t band = id / (kGroupM * n_tiles), first_m = band * kGroupM;
   const uint32_t gm = m_tiles - first_m < kGroupM ? m_tiles - first_m : kGroupM;
   const uint32_t within = id - band * kGroupM * n_tiles;
-  const uint32_t n0 = (within / gm) * G::BN, m0 = (first_m + within % gm) * G::BM;
+  *n0 = (within / gm) * G::BN;
+  *m0 = (first_m + within % gm) * G::BM;
+}
 
-  const uint32_t a_rows = T - m0 < (uint32_t)G::BM ? T - m0 : (uint32_t)G::BM;
-  const uint32_t b_rows = N - n0 < (uint32_t)G::BN ? N - n0 : (uint32_t)G::BN;
-  const Rsrc ra = make_rsrc(x + (uint64_t)m0 * ldx_bytes, (uint64_t)(a_rows - 1) * ldx_bytes + K * 2);
-  const Rsrc rb = make_rsrc(w + (uint64_t)n0 * ldw_bytes, (uint64_t)(b_rows - 1) * ldw_bytes + K * 2);
-
-  f32x16 acc[MB][NB];
-#pragma unroll
-  for (int i = 0; i < MB; ++i)
-#pragma unroll
-    for (int j = 0; j < NB; ++j)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
-
-  // Two LDS stages; K step ks computes from stage ks % 2.  Fragments are
-  // double-buffered in registers: the reads of sub-step kk+1 are issued
-  // before the MFMAs of sub-step kk.  Before the last sub-step of a step the
-  // wave waits for its loads of step ks+1 (into the other stage) and meets
-  // the barrier; after it, the stage just finished is free (every wave's
-  // reads of it have completed), so the loads of step ks+2 go there, and the
-  // first fragments of step ks+1 are read while the last MFMAs of step ks
-  // run.  Loads past the last step fetch the last step again (unused).
-  static_assert(G::S == 2 && BK % 32 == 0, "two stages, an even number of 16-wide sub-steps");
-  constexpr int KK = BK / 16;
-  const uint32_t ksteps = K / BK;
-  // a lane's fragment: row (lane % 32) of a 32-row block, 8 consecutive k
-  // starting at 8*(lane/32) of each 16-wide MFMA step; A and B use the same
-  // k order, so the products pair correctly whatever order the hardware sums
-  const uint32_t fr = lane % 32, fk = 8 * (lane / 32);
-  const uint32_t arow = wm * G::kWaveM + fr, brow = G::BM + wn * G::kWaveN + fr;
-  uint8_t* const stage0 = smem;
-  uint8_t* const stage1 = smem + G::kStageBytes;
-
-  const DmaOffsets<G> doff = dma_offsets<G>(ldx_bytes, ldw_bytes, wave, lane);
-  dma_tile<G>(ra, rb, doff, step_bytes<G>(0, ksteps), stage0, wave);
-  wait_vmcnt<0>();
-  stage_barrier();
-  dma_tile<G>(ra, rb, doff, step_bytes<G>(1, ksteps), stage1, wave);
-  typedef typename ProjElem<DT>::V8 Frag;
+// Epilogue: per-head QK-Norm on the fp32 accumulators (unless `norm` is 0),
+// then the tile leaves through LDS as 16-byte row stores.  Every load into
+// LDS must have completed and every wave must have passed a barrier after
+// its last fragment read (the output staging reuses the stages).
+template <class G, int DT, int D>
+__device__ __forceinline__ void proj_epilogue(f32x16 (&acc)[G::MB][G::NB], uint8_t* smem, uint32_t tid,
+                                              uint32_t lane, uint32_t wm, uint32_t wn, uint32_t m0,
+                                              uint32_t n0, uint32_t a_rows, uint32_t N, uint32_t hq,
+                                              uint32_t hkv, const uint8_t* __restrict__ gamma_q,
+                                              const uint8_t* __restrict__ gamma_k, float eps,
+                                              float inv_d, uint32_t norm, uint8_t* __restrict__ out,
+                                              uint64_t ld_bytes) {
+  constexpr int MB = G::MB, NB = G::NB;
   typedef typename ProjElem<DT>::T Elem;
-  Frag fa[2][MB], fb[2][NB];
-  read_frags<G, DT>(stage0, arow, brow, fk, fa[0], fb[0]);
-
-  constexpr int kReads = MB + NB, kMfma = MB * NB;
-  static_assert(kMfma > kReads && G::kLoads % (kMfma - kReads) == 0, "");
-  for (uint32_t ks = 0; ks < ksteps; ++ks) {
-    uint8_t* const st = (ks & 1) ? stage1 : stage0;
-    uint8_t* const nx = (ks & 1) ? stage0 : stage1;
-#pragma unroll
-    for (int kk = 0; kk < KK - 1; ++kk) {
-      read_frags<G, DT>(st, arow, brow, (kk + 1) * 16 + fk, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
-      mfma_step<G, DT>(acc, fa[kk & 1], fb[kk & 1]);
-      sched_interleave<kReads, 1, 0>();
-      sched_mfmas<kMfma - kReads>();
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    wait_vmcnt<0>();                            // step ks+1 has landed (this wave)
-    stage_barrier();                            // (and everyone's); stage st is free
-    __builtin_amdgcn_sched_barrier(0);
-    // the reads come first: the compiler cannot tell that the loads into
-    // stage st do not overlap stage nx, so it keeps them in source order
-    read_frags<G, DT>(nx, arow, brow, fk, fa[0], fb[0]);
-    dma_tile<G>(ra, rb, doff, step_bytes<G>(ks + 2, ksteps), st, wave);
-    mfma_step<G, DT>(acc, fa[1], fb[1]);
-    sched_interleave<kReads, 1, 0>();
-    sched_interleave<kMfma - kReads, 0, G::kLoads / (kMfma - kReads)>();
-    // keeps the reads above in this iteration: without it the compiler merges
-    // them with the reads before the loop into one read at the top of the
-    // loop, which then waits for its result before the first MFMA
-    asm volatile("" ::: "memory");
-  }
-  // the output tile reuses the stages: every load into LDS must be done
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-
   // Epilogue.  Value e of block (i, j) in lane l is row i*32 + 8*(e/4) +
   // 4*(l/32) + e%4 of the wave's slab and column j*32 + l%32.  A head of D
   // columns is D/32 consecutive blocks j (a wave's columns are whole heads):
@@ -408,6 +343,236 @@ __global__ __launch_bounds__(G::kThreads) void qkv_proj_kernel(
   }
 }
 
+template <class G, int DT, int D>
+__global__ __launch_bounds__(G::kThreads) void qkv_proj_kernel(
+    const uint8_t* __restrict__ x, uint32_t ldx_bytes, const uint8_t* __restrict__ w,
+    uint32_t ldw_bytes, uint8_t* __restrict__ out, uint64_t ld_bytes, uint32_t T, uint32_t K,
+    uint32_t N, uint32_t hq, uint32_t hkv, const uint8_t* __restrict__ gamma_q,
+    const uint8_t* __restrict__ gamma_k, float eps, float inv_d, uint32_t norm) {
+  constexpr int MB = G::MB, NB = G::NB, BK = G::BK;
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  const uint32_t tid = threadIdx.x, lane = tid & 63;
+  const uint32_t wave = uniform(tid >> 6);
+  const uint32_t wm = wave / G::WN, wn = wave % G::WN;
+  uint32_t m0, n0;
+  tile_origin<G>(T, N, &m0, &n0);
+
+  const uint32_t a_rows = T - m0 < (uint32_t)G::BM ? T - m0 : (uint32_t)G::BM;
+  const uint32_t b_rows = N - n0 < (uint32_t)G::BN ? N - n0 : (uint32_t)G::BN;
+  const Rsrc ra = make_rsrc(x + (uint64_t)m0 * ldx_bytes, (uint64_t)(a_rows - 1) * ldx_bytes + K * 2);
+  const Rsrc rb = make_rsrc(w + (uint64_t)n0 * ldw_bytes, (uint64_t)(b_rows - 1) * ldw_bytes + K * 2);
+
+  f32x16 acc[MB][NB];
+#pragma unroll
+  for (int i = 0; i < MB; ++i)
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+  // Two LDS stages; K step ks computes from stage ks % 2.  Fragments are
+  // double-buffered in registers: the reads of sub-step kk+1 are issued
+  // before the MFMAs of sub-step kk.  Before the last sub-step of a step the
+  // wave waits for its loads of step ks+1 (into the other stage) and meets
+  // the barrier; after it, the stage just finished is free (every wave's
+  // reads of it have completed), so the loads of step ks+2 go there, and the
+  // first fragments of step ks+1 are read while the last MFMAs of step ks
+  // run.  Loads past the last step fetch the last step again (unused).
+  static_assert(G::S == 2 && BK % 32 == 0, "two stages, an even number of 16-wide sub-steps");
+  constexpr int KK = BK / 16;
+  const uint32_t ksteps = K / BK;
+  // a lane's fragment: row (lane % 32) of a 32-row block, 8 consecutive k
+  // starting at 8*(lane/32) of each 16-wide MFMA step; A and B use the same
+  // k order, so the products pair correctly whatever order the hardware sums
+  const uint32_t fr = lane % 32, fk = 8 * (lane / 32);
+  const uint32_t arow = wm * G::kWaveM + fr, brow = G::BM + wn * G::kWaveN + fr;
+  uint8_t* const stage0 = smem;
+  uint8_t* const stage1 = smem + G::kStageBytes;
+
+  const DmaOffsets<G> doff = dma_offsets<G>(ldx_bytes, ldw_bytes, wave, lane);
+  dma_tile<G>(ra, rb, doff, step_bytes<G>(0, ksteps), stage0, wave);
+  wait_vmcnt<0>();
+  stage_barrier();
+  dma_tile<G>(ra, rb, doff, step_bytes<G>(1, ksteps), stage1, wave);
+  typedef typename ProjElem<DT>::V8 Frag;
+  typedef typename ProjElem<DT>::T Elem;
+  Frag fa[2][MB], fb[2][NB];
+  read_frags<G, DT>(stage0, arow, brow, fk, fa[0], fb[0]);
+
+  constexpr int kReads = MB + NB, kMfma = MB * NB;
+  static_assert(kMfma > kReads && G::kLoads % (kMfma - kReads) == 0, "");
+  for (uint32_t ks = 0; ks < ksteps; ++ks) {
+    uint8_t* const st = (ks & 1) ? stage1 : stage0;
+    uint8_t* const nx = (ks & 1) ? stage0 : stage1;
+#pragma unroll
+    for (int kk = 0; kk < KK - 1; ++kk) {
+      read_frags<G, DT>(st, arow, brow, (kk + 1) * 16 + fk, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
+      mfma_step<G, DT>(acc, fa[kk & 1], fb[kk & 1]);
+      sched_interleave<kReads, 1, 0>();
+      sched_mfmas<kMfma - kReads>();
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    wait_vmcnt<0>();                            // step ks+1 has landed (this wave)
+    stage_barrier();                            // (and everyone's); stage st is free
+    __builtin_amdgcn_sched_barrier(0);
+    // the reads come first: the compiler cannot tell that the loads into
+    // stage st do not overlap stage nx, so it keeps them in source order
+    read_frags<G, DT>(nx, arow, brow, fk, fa[0], fb[0]);
+    dma_tile<G>(ra, rb, doff, step_bytes<G>(ks + 2, ksteps), st, wave);
+    mfma_step<G, DT>(acc, fa[1], fb[1]);
+    sched_interleave<kReads, 1, 0>();
+    sched_interleave<kMfma - kReads, 0, G::kLoads / (kMfma - kReads)>();
+    // keeps the reads above in this iteration: without it the compiler merges
+    // them with the reads before the loop into one read at the top of the
+    // loop, which then waits for its result before the first MFMA
+    asm volatile("" ::: "memory");
+  }
+  // the output tile reuses the stages: every load into LDS must be done
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  proj_epilogue<G, DT, D>(acc, smem, tid, lane, wm, wn, m0, n0, a_rows, N, hq, hkv, gamma_q, gamma_k,
+                          eps, inv_d, norm, out, ld_bytes);
+}
+
+// ------------------------------------------------------------- ping-pong --
+//
+// The same tile with a different schedule of its main loop.  The 8 waves
+// form two groups, waves 0-3 and 4-7, and the two waves that share a SIMD
+// (w and w+4) belong to different groups.  Each wave alternates a memory
+// phase M_j (issue the block's loads into LDS of step j+D -- group 0 only --
+// and read every fragment of step j into registers) and a compute phase C_j
+// (the step's MFMAs back to back), and group 1 runs one phase behind group 0,
+// with a workgroup barrier between phases:
+//
+//   slot:     0     1     2     3     4   ...
+//   group 0:  M_0   C_0   M_1   C_1   M_2
+//   group 1:  --    M_0   C_0   M_1   C_1
+//
+// so in every slot one wave of each SIMD issues MFMAs while the other does
+// its memory work, and the matrix core of the SIMD is fed by one wave at a
+// time.  S LDS stages hold steps j .. j+S-1; the loads of step j+D (D = S-1)
+// go into the stage that step j-1 used, whose last reads (group 1, M_{j-1})
+// ended before the barrier that opens M_j.  Group 0 waits for its loads of
+// step j+1 at the end of C_j, before the barrier that opens M_{j+1}.
+
+// Per-lane part of a loader wave's load offsets: row `sub` of the
+// instruction, chunk slot of lane % CPR.  Rows R of an instruction start at
+// multiples of kInstRows = 4 * RPB, so the swizzle of row R + sub is
+// ((4 * (R / kInstRows) + sub / RPB) % CPR): it depends on the instruction
+// index only through (4 * idx) % CPR, which is 0 or 4.
+template <class G>
+__device__ __forceinline__ uint32_t pp_lane_part(uint32_t ld_bytes, uint32_t lane, uint32_t phase) {
+  const uint32_t sub = lane / G::CPR, s = lane % G::CPR;
+  return sub * ld_bytes + (s ^ ((phase + sub / G::RPB) % G::CPR)) * 16;
+}
+
+// One K step of both operand tiles into `stage`, issued by the 4 loader waves
+// (group 0), kL instructions of A rows and kL of B rows each.  The row part of
+// each offset is added per instruction (it travels in the vector offset, so
+// rows past the end of x or w fall outside the descriptor and arrive as
+// zeros).
+template <class G>
+__device__ __forceinline__ void pp_dma(Rsrc ra, Rsrc rb, uint32_t ldx_bytes, uint32_t ldw_bytes,
+                                       const uint32_t (&pa)[2], const uint32_t (&pb)[2], uint32_t k_bytes,
+                                       uint8_t* stage, uint32_t lw) {
+  constexpr uint32_t kRows = G::kInstRows, kRowBytes = G::kRowBytes, kBM = G::BM;
+  constexpr uint32_t kL = G::BM / G::kInstRows / 4;
+  static_assert(G::BM == G::BN, "as many A as B loads");
+#pragma unroll
+  for (uint32_t j = 0; j < kL; ++j) {
+    const uint32_t idx = lw * kL + j;
+    const uint32_t R = idx * kRows;
+    const uint32_t ph = ((4 * idx) % G::CPR) / 4;       // kL is even: the parity of j
+    const uint32_t va = pa[ph] + (R * ldx_bytes + k_bytes);
+    const uint32_t vb = pb[ph] + (R * ldw_bytes + k_bytes);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        ra, (__attribute__((address_space(3))) void*)(stage + R * kRowBytes), 16, va, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rb, (__attribute__((address_space(3))) void*)(stage + (kBM + R) * kRowBytes), 16, vb, 0, 0, 0);
+  }
+}
+
+template <class G, int DT, int D>
+__global__ __launch_bounds__(G::kThreads) void qkv_proj_pp_kernel(
+    const uint8_t* __restrict__ x, uint32_t ldx_bytes, const uint8_t* __restrict__ w,
+    uint32_t ldw_bytes, uint8_t* __restrict__ out, uint64_t ld_bytes, uint32_t T, uint32_t K,
+    uint32_t N, uint32_t hq, uint32_t hkv, const uint8_t* __restrict__ gamma_q,
+    const uint8_t* __restrict__ gamma_k, float eps, float inv_d, uint32_t norm) {
+  constexpr int MB = G::MB, NB = G::NB, BK = G::BK, S = G::S, DIST = S - 1;
+  constexpr int KK = BK / 16;
+  constexpr uint32_t kL = G::BM / G::kInstRows / 4;           // loads per operand per loader wave
+  constexpr int kBatch = 2 * kL;                               // loads per loader wave per step
+  static_assert(G::kWaves == 8 && S >= 2 && (kL % 2 == 0 || G::CPR <= 4), "");
+  static_assert((DIST - 1) * kBatch < 64, "vmcnt range");
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  const uint32_t tid = threadIdx.x, lane = tid & 63;
+  const uint32_t wave = uniform(tid >> 6);
+  const uint32_t wm = wave / G::WN, wn = wave % G::WN;
+  const uint32_t grp = wave >> 2, lw = wave & 3;
+  uint32_t m0, n0;
+  tile_origin<G>(T, N, &m0, &n0);
+  const uint32_t a_rows = T - m0 < (uint32_t)G::BM ? T - m0 : (uint32_t)G::BM;
+  const uint32_t b_rows = N - n0 < (uint32_t)G::BN ? N - n0 : (uint32_t)G::BN;
+  const Rsrc ra = make_rsrc(x + (uint64_t)m0 * ldx_bytes, (uint64_t)(a_rows - 1) * ldx_bytes + K * 2);
+  const Rsrc rb = make_rsrc(w + (uint64_t)n0 * ldw_bytes, (uint64_t)(b_rows - 1) * ldw_bytes + K * 2);
+
+  f32x16 acc[MB][NB];
+#pragma unroll
+  for (int i = 0; i < MB; ++i)
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+  const uint32_t ksteps = K / BK;
+  const uint32_t fr = lane % 32, fk = 8 * (lane / 32);
+  const uint32_t arow = wm * G::kWaveM + fr, brow = G::BM + wn * G::kWaveN + fr;
+  const uint32_t pa[2] = {pp_lane_part<G>(ldx_bytes, lane, 0), pp_lane_part<G>(ldx_bytes, lane, 4)};
+  const uint32_t pb[2] = {pp_lane_part<G>(ldw_bytes, lane, 0), pp_lane_part<G>(ldw_bytes, lane, 4)};
+  auto stage = [&](uint32_t k) { return smem + (k % S) * G::kStageBytes; };
+
+  // prologue: steps 0 .. DIST-1 into their stages (group 0 loads)
+  if (grp == 0) {
+#pragma unroll
+    for (int d = 0; d < DIST; ++d)
+      if ((uint32_t)d < ksteps) pp_dma<G>(ra, rb, ldx_bytes, ldw_bytes, pa, pb, d * BK * 2, stage(d), lw);
+  }
+  wait_vmcnt<0>();
+  stage_barrier();
+  if (grp == 1) stage_barrier();               // group 1 starts one phase later
+
+  typedef typename ProjElem<DT>::V8 Frag;
+  Frag fa[KK][MB], fb[KK][NB];
+  for (uint32_t j = 0; j < ksteps; ++j) {
+    // M_j
+    __builtin_amdgcn_sched_barrier(0);
+    const bool load_next = j + DIST < ksteps;
+    if (grp == 0 && load_next)
+      pp_dma<G>(ra, rb, ldx_bytes, ldw_bytes, pa, pb, (j + DIST) * BK * 2, stage(j + DIST), lw);
+    const uint8_t* st = stage(j);
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) read_frags<G, DT>(st, arow, brow, kk * 16 + fk, fa[kk], fb[kk]);
+    stage_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    // C_j
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) mfma_step<G, DT>(acc, fa[kk], fb[kk]);
+    __builtin_amdgcn_sched_barrier(0);
+    if (grp == 0) {
+      // step j+1 has landed (the loads of later steps may stay in flight)
+      if (load_next) wait_vmcnt<(DIST - 1) * kBatch>();
+      else wait_vmcnt<0>();
+    }
+    stage_barrier();
+  }
+  if (grp == 0) stage_barrier();              // matches group 1's extra barrier
+  // the output tile reuses the stages: every load into LDS must be done
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  proj_epilogue<G, DT, D>(acc, smem, tid, lane, wm, wn, m0, n0, a_rows, N, hq, hkv, gamma_q, gamma_k,
+                          eps, inv_d, norm, out, ld_bytes);
+}
+
 // 256 x 256 tiles of 8 waves (4 along M, 2 along N), each wave 64 x 128:
 // 0.75 fragment reads per MFMA and 131 flop per byte of operand staged, the
 // best of the shapes measured on MI355X.  The others measured: 128 x 128 with
@@ -433,9 +598,27 @@ __global__ __launch_bounds__(G::kThreads) void qkv_proj_kernel(
 #ifndef QKNORM_PROJ_WN
 #define QKNORM_PROJ_WN 2
 #endif
-using Geo = Tile<256, 256, QKNORM_PROJ_WM, QKNORM_PROJ_WN, QKNORM_PROJ_BK, 2>;
+#ifndef QKNORM_PROJ_PP
+#define QKNORM_PROJ_PP 0           // 1: the ping-pong main loop
+#endif
+#ifndef QKNORM_PROJ_PP_BK
+#define QKNORM_PROJ_PP_BK 64
+#endif
+#ifndef QKNORM_PROJ_PP_S
+#define QKNORM_PROJ_PP_S 2
+#endif
+constexpr bool kPingPong = QKNORM_PROJ_PP != 0;
+using GeoIl = Tile<256, 256, QKNORM_PROJ_WM, QKNORM_PROJ_WN, QKNORM_PROJ_BK, 2>;
+using GeoPp = Tile<256, 256, 4, 2, QKNORM_PROJ_PP_BK, QKNORM_PROJ_PP_S>;
+using Geo = std::conditional_t<kPingPong, GeoPp, GeoIl>;
 constexpr int kBM = Geo::BM, kBN = Geo::BN, kThreads = Geo::kThreads;
 constexpr int kLdsBytes = Geo::kLdsBytes;
+
+template <int DT, int D>
+constexpr auto proj_kernel() {
+  if constexpr (kPingPong) return qkv_proj_pp_kernel<Geo, DT, D>;
+  else return qkv_proj_kernel<Geo, DT, D>;
+}
 
 }  // namespace
 
@@ -459,10 +642,10 @@ hipError_t launch_qkv_proj(const ProjArgs& a, hipStream_t s) {
   auto pick = [&](auto k64, auto k128, auto k256) {
     return a.head_dim == 64 ? k64 : (a.head_dim == 128 ? k128 : k256);
   };
-  auto kern = a.dtype == kF16 ? pick(qkv_proj_kernel<Geo, kF16, 64>, qkv_proj_kernel<Geo, kF16, 128>,
-                                     qkv_proj_kernel<Geo, kF16, 256>)
-                              : pick(qkv_proj_kernel<Geo, kBF16, 64>, qkv_proj_kernel<Geo, kBF16, 128>,
-                                     qkv_proj_kernel<Geo, kBF16, 256>);
+  auto kern = a.dtype == kF16 ? pick(proj_kernel<kF16, 64>(), proj_kernel<kF16, 128>(),
+                                     proj_kernel<kF16, 256>())
+                              : pick(proj_kernel<kBF16, 64>(), proj_kernel<kBF16, 128>(),
+                                     proj_kernel<kBF16, 256>());
   // more than the default 64 KiB of dynamic LDS (gfx950 has 160 KiB per CU);
   // a host-side attribute, set on every call (no shared state between threads)
   const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
