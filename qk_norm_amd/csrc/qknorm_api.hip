@@ -213,7 +213,9 @@ int qknorm_qkv_proj_per_head(const void* x, int64_t ldx, const void* w, int64_t 
                      eps, flags, dtype};
   if (!qknorm::proj_shape_ok(a)) return QKNORM_E_UNSUPPORTED;
   if (!touched) return QKNORM_OK;
-  return finish(qknorm::launch_qkv_proj(a, static_cast<hipStream_t>(stream)));
+  int cus = 0;
+  if ((rc = device_cus(&cus))) return rc;
+  return finish(qknorm::launch_qkv_proj(a, static_cast<hipStream_t>(stream), cus));
 }
 
 }  // extern "C"

@@ -73,6 +73,6 @@ hipError_t launch_per_head(const PerHeadArgs& a, hipStream_t s, int cus);
 hipError_t launch_layerwise(const LayerwiseArgs& a, hipStream_t s, int cus);
 hipError_t launch_partial_sumsq(const PartialArgs& a, hipStream_t s, int cus);
 hipError_t launch_apply_scalar(const ApplyArgs& a, hipStream_t s, int cus);
-hipError_t launch_qkv_proj(const ProjArgs& a, hipStream_t s);
+hipError_t launch_qkv_proj(const ProjArgs& a, hipStream_t s, int cus);
 
 }  // namespace qknorm

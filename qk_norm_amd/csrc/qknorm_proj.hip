@@ -8,14 +8,17 @@
 // that writes qkv and a normalisation that reads and writes it again.
 //
 // Tiling: a block of 512 threads (4 x 2 waves, two per SIMD) owns a 256 x 256
-// output tile; each wave a 64 x 128 slab of 2 x 4 v_mfma_f32_32x32x16_bf16
-// blocks (v_mfma_f32_32x32x16_f16 for fp16, the same layout).  K advances 64 at a time through two LDS stages filled straight
-// from global memory (buffer loads into LDS, no staging registers), with
-// the operand rows XOR-swizzled so that fragment reads hit distinct banks.
-// Tiles are ordered so the blocks each XCD holds at once share operand
-// panels in its L2.  Because the tile width is a multiple of head_dim and
-// tiles start at multiples of it, a tile holds whole heads, and the epilogue
-// normalises them in registers without leaving the block.
+// output tile; each wave a 64 x 128 slab of 4 x 8 v_mfma_f32_16x16x32_bf16
+// blocks (v_mfma_f32_16x16x32_f16 for fp16, the same layout).  K advances 64
+// at a time through two LDS stages filled straight from global memory
+// (buffer loads into LDS, no staging registers), with the operand rows
+// XOR-swizzled so that fragment reads hit distinct banks.  Where 256 x 256
+// tiles would leave a round of the chip's CUs half empty, the last columns
+// go to 256 x 128 tiles of the same launch.  Tiles are ordered so the blocks
+// each XCD holds at once share operand panels in its L2.  Because tile widths
+// are multiples of head_dim (or one head spans a tile's two column waves)
+// and tiles start at multiples of it, a tile holds whole heads, and the
+// epilogue normalises them in registers without leaving the block.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -29,9 +32,11 @@ namespace qknorm {
 namespace {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-// The 16-bit element type: its 8-element fragment and the 32 x 32 x 16 MFMA
-// that takes it (fp32 accumulation either way).
+// The 16-bit element type: its 8-element fragment and the MFMAs that take it
+// (fp32 accumulation either way): 32 x 32 x 16 (16 accumulators per lane) and
+// 16 x 16 x 32 (4 per lane).
 template <int DT>
 struct ProjElem;
 template <>
@@ -41,6 +46,9 @@ struct ProjElem<kBF16> {
   static __device__ __forceinline__ f32x16 mfma(V8 a, V8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
   }
+  static __device__ __forceinline__ f32x4 mfma(V8 a, V8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
 };
 template <>
 struct ProjElem<kF16> {
@@ -49,10 +57,30 @@ struct ProjElem<kF16> {
   static __device__ __forceinline__ f32x16 mfma(V8 a, V8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
   }
+  static __device__ __forceinline__ f32x4 mfma(V8 a, V8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  }
+};
+
+// MFMA block shape.  MS x MS output blocks, KS of K per instruction; lane l
+// holds A row (l % MS) and B column (l % MS) with 8 consecutive k starting
+// at 8 * (l / MS), and accumulator value e of the block at column l % MS and
+// row 8 * (e / 4) + 4 * (l / 32) + e % 4 (MS = 32) or 4 * (l / 16) + e (MS = 16).
+template <int MS>
+struct MfmaShape;
+template <>
+struct MfmaShape<32> {
+  static constexpr int KS = 16, NACC = 16;
+  typedef f32x16 Acc;
+};
+template <>
+struct MfmaShape<16> {
+  static constexpr int KS = 32, NACC = 4;
+  typedef f32x4 Acc;
 };
 
 // Tile geometry.  A block of WM x WN waves owns a BM x BN output tile; each
-// wave a (BM/WM) x (BN/WN) slab of 32 x 32 MFMA blocks; K advances BK at a
+// wave a (BM/WM) x (BN/WN) slab of MS x MS MFMA blocks; K advances BK at a
 // time through S LDS stages.  Operand rows are BK*2 bytes with no padding:
 // the 16-byte chunk c of row r sits in slot c ^ ((r / RPB) % CPR) (CPR chunks
 // per row, RPB rows per 256 bytes), so the 16 rows read by 16 lanes at once
@@ -62,12 +90,14 @@ struct ProjElem<kF16> {
 // instruction covering rows R .. R+1024/(BK*2)-1 fetches row R + i / CPR and
 // the chunk whose slot is i % CPR: no staging registers and no LDS write
 // instructions.
-template <int BM_, int BN_, int WM_, int WN_, int BK_, int S_>
+template <int BM_, int BN_, int WM_, int WN_, int BK_, int S_, int MS_ = 32>
 struct Tile {
-  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, BK = BK_, S = S_;
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, BK = BK_, S = S_, MS = MS_;
   static constexpr int kThreads = 64 * WM * WN, kWaves = WM * WN;
   static constexpr int kWaveM = BM / WM, kWaveN = BN / WN;
-  static constexpr int MB = kWaveM / 32, NB = kWaveN / 32;
+  static constexpr int MB = kWaveM / MS, NB = kWaveN / MS;
+  static constexpr int KS = MfmaShape<MS>::KS, KK = BK / KS;   // K per MFMA, MFMA steps per K step
+  typedef typename MfmaShape<MS>::Acc Acc;
   static constexpr int kRowBytes = BK * 2;
   static constexpr int CPR = kRowBytes / 16, RPB = 256 / kRowBytes;
   static constexpr int kInstRows = 1024 / kRowBytes;         // rows one load instruction fills
@@ -82,6 +112,9 @@ struct Tile {
 
 #ifndef QKNORM_PROJ_XCD
 #define QKNORM_PROJ_XCD 1
+#endif
+#ifndef QKNORM_PROJ_MPR
+#define QKNORM_PROJ_MPR 1          // MFMAs between the fragment reads of the next sub-step
 #endif
 #ifndef QKNORM_PROJ_GM
 #define QKNORM_PROJ_GM 4
@@ -106,14 +139,16 @@ template <class G>
 __device__ __forceinline__ DmaOffsets<G> dma_offsets(uint32_t ldx_bytes, uint32_t ldw_bytes,
                                                      uint32_t wave, uint32_t lane) {
   constexpr uint32_t kRows = G::kInstRows, kBM = G::BM, kCpr = G::CPR, kRpb = G::RPB;
-  constexpr int kInst = G::kAInst;
-  static_assert(G::kAInst == G::kBInst, "as many A as B loads");
   const uint32_t sub = lane / kCpr, s = lane % kCpr;
   DmaOffsets<G> o;
 #pragma unroll
-  for (int j = 0; j < kInst; ++j) {
-    const uint32_t r = (wave * kInst + j) * kRows + sub;
+  for (int j = 0; j < G::kAInst; ++j) {
+    const uint32_t r = (wave * G::kAInst + j) * kRows + sub;
     o.a[j] = r * ldx_bytes + (s ^ ((r / kRpb) % kCpr)) * 16;
+  }
+#pragma unroll
+  for (int j = 0; j < G::kBInst; ++j) {
+    const uint32_t r = (wave * G::kBInst + j) * kRows + sub;
     o.b[j] = r * ldw_bytes + (s ^ (((kBM + r) / kRpb) % kCpr)) * 16;
   }
   return o;
@@ -126,17 +161,24 @@ template <class G>
 __device__ __forceinline__ void dma_tile(Rsrc ra, Rsrc rb, const DmaOffsets<G>& o,
                                          uint32_t k_bytes, uint8_t* stage, uint32_t wave) {
   constexpr uint32_t kRows = G::kInstRows, kRowBytes = G::kRowBytes, kBM = G::BM;
-  constexpr int kInst = G::kAInst;
+  constexpr int kMax = G::kAInst > G::kBInst ? G::kAInst : G::kBInst;
+  // A and B loads alternate while both have some left
 #pragma unroll
-  for (int j = 0; j < kInst; ++j) {
-    const uint32_t R = (wave * kInst + j) * kRows;
-    const uint32_t va = o.a[j], vb = o.b[j];     // (locals: the host pass rejects members here)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        ra, (__attribute__((address_space(3))) void*)(stage + R * kRowBytes), 16, va, k_bytes,
-        0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        rb, (__attribute__((address_space(3))) void*)(stage + (kBM + R) * kRowBytes), 16, vb,
-        k_bytes, 0, 0);
+  for (int j = 0; j < kMax; ++j) {
+    if (j < G::kAInst) {
+      const uint32_t R = (wave * G::kAInst + j) * kRows;
+      const uint32_t va = o.a[j];                // (locals: the host pass rejects members here)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          ra, (__attribute__((address_space(3))) void*)(stage + R * kRowBytes), 16, va, k_bytes,
+          0, 0);
+    }
+    if (j < G::kBInst) {
+      const uint32_t R = (wave * G::kBInst + j) * kRows;
+      const uint32_t vb = o.b[j];
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rb, (__attribute__((address_space(3))) void*)(stage + (kBM + R) * kRowBytes), 16, vb,
+          k_bytes, 0, 0);
+    }
   }
 }
 
@@ -176,13 +218,13 @@ __device__ __forceinline__ void read_frags(const uint8_t* st, uint32_t arow, uin
                                            uint32_t k, typename ProjElem<DT>::V8 (&a)[G::MB],
                                            typename ProjElem<DT>::V8 (&b)[G::NB]) {
 #pragma unroll
-  for (int i = 0; i < G::MB; ++i) a[i] = sfrag<G, DT>(st, arow + i * 32, k);
+  for (int i = 0; i < G::MB; ++i) a[i] = sfrag<G, DT>(st, arow + i * G::MS, k);
 #pragma unroll
-  for (int j = 0; j < G::NB; ++j) b[j] = sfrag<G, DT>(st, brow + j * 32, k);
+  for (int j = 0; j < G::NB; ++j) b[j] = sfrag<G, DT>(st, brow + j * G::MS, k);
 }
 
 template <class G, int DT>
-__device__ __forceinline__ void mfma_step(f32x16 (&acc)[G::MB][G::NB],
+__device__ __forceinline__ void mfma_step(typename G::Acc (&acc)[G::MB][G::NB],
                                           const typename ProjElem<DT>::V8 (&a)[G::MB],
                                           const typename ProjElem<DT>::V8 (&b)[G::NB]) {
 #pragma unroll
@@ -196,13 +238,13 @@ __device__ __forceinline__ void mfma_step(f32x16 (&acc)[G::MB][G::NB],
 // reads and V loads, NP times; then the remaining M MFMAs back to back.  With
 // one wave per SIMD nothing else hides a read's latency, so the reads feeding
 // the next sub-step go between this sub-step's MFMAs.
-template <int NP, int R, int V>
+template <int NP, int R, int V, int M = 1>
 __device__ __forceinline__ void sched_interleave() {
   if constexpr (NP > 0) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, M, 0);
     if constexpr (R > 0) __builtin_amdgcn_sched_group_barrier(0x100, R, 0);
     if constexpr (V > 0) __builtin_amdgcn_sched_group_barrier(0x020, V, 0);
-    sched_interleave<NP - 1, R, V>();
+    sched_interleave<NP - 1, R, V, M>();
   }
 }
 
@@ -215,12 +257,14 @@ __device__ __forceinline__ void sched_mfmas() {
 // with its own L2; the remap gives each XCD a contiguous run of tiles, and
 // the runs walk the output in bands of GM tile rows, columns outer, so the
 // blocks an XCD holds at once share a few A and B panels in its L2.
+// `id` counts the blocks of one tile shape (0 .. count-1); blocks are numbered
+// so that id % 8 is the block's XCD.
 template <class G>
-__device__ __forceinline__ void tile_origin(uint32_t T, uint32_t N, uint32_t* m0, uint32_t* n0) {
+__device__ __forceinline__ void tile_origin(uint32_t T, uint32_t N, uint32_t id, uint32_t count,
+                                            uint32_t* m0, uint32_t* n0) {
   const uint32_t n_tiles = (N + G::BN - 1) / G::BN, m_tiles = (T + G::BM - 1) / G::BM;
-  uint32_t id = blockIdx.x;
   if (kXcdRemap) {
-    const uint32_t q = gridDim.x / 8, r = gridDim.x % 8, xcd = id % 8;
+    const uint32_t q = count / 8, r = count % 8, xcd = id % 8;
     id = xcd * q + (xcd < r ? xcd : r) + id / 8;
   }
   const uint32_t band = id / (kGroupM * n_tiles), first_m = band * kGroupM;
@@ -230,38 +274,61 @@ __device__ __forceinline__ void tile_origin(uint32_t T, uint32_t N, uint32_t* m0
   *m0 = (first_m + within % gm) * G::BM;
 }
 
+// The gamma value and whether it is normalised, for each of a lane's columns
+// (j * MS + lane % MS of the wave's slab, for each block j).  Loaded before
+// the main loop, so the loads' latency hides behind it.
+template <class G>
+struct EpiGamma {
+  float g[G::NB];
+  bool normed[G::NB];
+};
+
+// The loads are unconditional (a load behind a branch makes the compiler wait
+// for it at once): columns that take no gamma read a valid stand-in, `spare`
+// (the weight, at least head_dim elements long), and select 1 afterwards.
+template <class G, int DT, int D>
+__device__ __forceinline__ EpiGamma<G> epi_gamma(uint32_t lane, uint32_t wn, uint32_t n0, uint32_t N,
+                                                 uint32_t hq, uint32_t hkv,
+                                                 const uint8_t* __restrict__ gamma_q,
+                                                 const uint8_t* __restrict__ gamma_k,
+                                                 const uint8_t* __restrict__ spare, uint32_t norm) {
+  typedef typename ProjElem<DT>::T Elem;
+  EpiGamma<G> eg;
+#pragma unroll
+  for (int j = 0; j < G::NB; ++j) {
+    const uint32_t n = n0 + wn * G::kWaveN + j * G::MS + lane % G::MS;
+    const uint32_t head = n / D;
+    const bool is_q = head < hq;
+    eg.normed[j] = norm && (is_q || head < hq + hkv) && n < N;
+    const uint8_t* src = eg.normed[j] ? (is_q ? gamma_q : gamma_k) : spare;
+    const float v = (float)reinterpret_cast<const Elem*>(src)[n % D];
+    eg.g[j] = eg.normed[j] ? v : 1.f;
+  }
+  return eg;
+}
+
 // Epilogue: per-head QK-Norm on the fp32 accumulators (unless `norm` is 0),
 // then the tile leaves through LDS as 16-byte row stores.  Every load into
 // LDS must have completed and every wave must have passed a barrier after
 // its last fragment read (the output staging reuses the stages).
 template <class G, int DT, int D>
-__device__ __forceinline__ void proj_epilogue(f32x16 (&acc)[G::MB][G::NB], uint8_t* smem, uint32_t tid,
+__device__ __forceinline__ void proj_epilogue(typename G::Acc (&acc)[G::MB][G::NB], uint8_t* smem, uint32_t tid,
                                               uint32_t lane, uint32_t wm, uint32_t wn, uint32_t m0,
-                                              uint32_t n0, uint32_t a_rows, uint32_t N, uint32_t hq,
-                                              uint32_t hkv, const uint8_t* __restrict__ gamma_q,
-                                              const uint8_t* __restrict__ gamma_k, float eps,
-                                              float inv_d, uint32_t norm, uint8_t* __restrict__ out,
+                                              uint32_t n0, uint32_t a_rows, uint32_t N,
+                                              const EpiGamma<G>& eg, float eps, float inv_d,
+                                              uint32_t norm, uint8_t* __restrict__ out,
                                               uint64_t ld_bytes) {
-  constexpr int MB = G::MB, NB = G::NB;
+  constexpr int MB = G::MB, NB = G::NB, MS = G::MS, NACC = MfmaShape<MS>::NACC;
   typedef typename ProjElem<DT>::T Elem;
-  // Epilogue.  Value e of block (i, j) in lane l is row i*32 + 8*(e/4) +
-  // 4*(l/32) + e%4 of the wave's slab and column j*32 + l%32.  A head of D
-  // columns is D/32 consecutive blocks j (a wave's columns are whole heads):
-  // its row sum of squares is the lane's fma chain over those blocks, then
-  // the 32-lane sum of the half-wave that holds the row.
-  constexpr int JH = D / 32;                    // blocks per head
+  // Value e of block (i, j) in lane l is row i*MS + (its row in the block)
+  // of the wave's slab and column j*MS + l%MS.  A head of D columns is D/MS
+  // consecutive blocks j (a wave's columns are whole heads): its row sum of
+  // squares is the lane's fma chain over those blocks, then the sum over the
+  // MS lanes that hold the row.
+  constexpr int JH = D / MS;                    // blocks per head
   if (norm) {
-    float g[NB];
-    bool normed[NB];
-#pragma unroll
-    for (int j = 0; j < NB; ++j) {
-      const uint32_t n = n0 + wn * G::kWaveN + j * 32 + lane % 32;
-      const uint32_t head = n / D;
-      const bool is_q = head < hq;
-      normed[j] = (is_q || head < hq + hkv) && n < N;
-      const Elem* gp = reinterpret_cast<const Elem*>(is_q ? gamma_q : gamma_k);
-      g[j] = normed[j] ? (float)gp[n % D] : 1.f;
-    }
+    const float* g = eg.g;
+    const bool* normed = eg.normed;
     if constexpr (JH <= NB) {
       static_assert(NB % JH == 0, "a wave's columns must be whole heads");
 #pragma unroll
@@ -272,12 +339,12 @@ __device__ __forceinline__ void proj_epilogue(f32x16 (&acc)[G::MB][G::NB], uint8
           // one region and the tile's columns past N are whole heads)
           if (!normed[h * JH]) continue;
 #pragma unroll
-          for (int e = 0; e < 16; ++e) {
+          for (int e = 0; e < NACC; ++e) {
             float s = 0.f;
 #pragma unroll
             for (int jj = 0; jj < JH; ++jj)
               s = __builtin_fmaf(acc[i][h * JH + jj][e], acc[i][h * JH + jj][e], s);
-            s = group_sum<32>(s);
+            s = group_sum<MS>(s);
             const float sc = rms_scale(s, inv_d, eps);
 #pragma unroll
             for (int jj = 0; jj < JH; ++jj)
@@ -293,21 +360,21 @@ __device__ __forceinline__ void proj_epilogue(f32x16 (&acc)[G::MB][G::NB], uint8
 #pragma unroll
       for (int i = 0; i < MB; ++i)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
+        for (int e = 0; e < NACC; ++e) {
           float s = 0.f;
 #pragma unroll
           for (int j = 0; j < NB; ++j) s = __builtin_fmaf(acc[i][j][e], acc[i][j][e], s);
-          s = group_sum<32>(s);
-          const uint32_t r = wm * G::kWaveM + i * 32 + 8 * (e / 4) + 4 * (lane / 32) + e % 4;
-          if (lane % 32 == 0) half[wn * G::BM + r] = s;
+          s = group_sum<MS>(s);
+          const uint32_t r = wm * G::kWaveM + i * MS + (MS == 32 ? 8 * (e / 4) + 4 * (lane / 32) + e % 4 : 4 * (lane / 16) + e);
+          if (lane % MS == 0) half[wn * G::BM + r] = s;
         }
       __syncthreads();
       if (normed[0]) {
 #pragma unroll
         for (int i = 0; i < MB; ++i)
 #pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const uint32_t r = wm * G::kWaveM + i * 32 + 8 * (e / 4) + 4 * (lane / 32) + e % 4;
+          for (int e = 0; e < NACC; ++e) {
+            const uint32_t r = wm * G::kWaveM + i * MS + (MS == 32 ? 8 * (e / 4) + 4 * (lane / 32) + e % 4 : 4 * (lane / 16) + e);
             const float sc = rms_scale(half[r] + half[G::BM + r], inv_d, eps);
 #pragma unroll
             for (int j = 0; j < NB; ++j) acc[i][j][e] = (acc[i][j][e] * g[j]) * sc;
@@ -324,9 +391,9 @@ __device__ __forceinline__ void proj_epilogue(f32x16 (&acc)[G::MB][G::NB], uint8
 #pragma unroll
     for (int j = 0; j < NB; ++j)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const uint32_t r = wm * G::kWaveM + i * 32 + 8 * (e / 4) + 4 * (lane / 32) + e % 4;
-        O[r * G::kORow + wn * G::kWaveN + j * 32 + lane % 32] = (Elem)acc[i][j][e];
+      for (int e = 0; e < NACC; ++e) {
+        const uint32_t r = wm * G::kWaveM + i * MS + (MS == 32 ? 8 * (e / 4) + 4 * (lane / 32) + e % 4 : 4 * (lane / 16) + e);
+        O[r * G::kORow + wn * G::kWaveN + j * MS + lane % MS] = (Elem)acc[i][j][e];
       }
   __syncthreads();
   // one descriptor over the tile's rows (wave-uniform); rows past T and
@@ -343,32 +410,49 @@ __device__ __forceinline__ void proj_epilogue(f32x16 (&acc)[G::MB][G::NB], uint8
   }
 }
 
+// The kernel's arguments (one copy for both tile shapes).
+struct ProjKArgs {
+  const uint8_t* x;
+  const uint8_t* w;
+  uint8_t* out;
+  const uint8_t* gamma_q;
+  const uint8_t* gamma_k;
+  uint64_t ld_bytes;
+  uint32_t ldx_bytes, ldw_bytes, T, K, N, hq, hkv, norm;
+  float eps, inv_d;
+};
+
+// One output tile of shape G: rows m0 .. m0+BM-1, columns n0 .. n0+BN-1 of
+// the column range [n_begin, n_end) this tile shape covers.
 template <class G, int DT, int D>
-__global__ __launch_bounds__(G::kThreads) void qkv_proj_kernel(
-    const uint8_t* __restrict__ x, uint32_t ldx_bytes, const uint8_t* __restrict__ w,
-    uint32_t ldw_bytes, uint8_t* __restrict__ out, uint64_t ld_bytes, uint32_t T, uint32_t K,
-    uint32_t N, uint32_t hq, uint32_t hkv, const uint8_t* __restrict__ gamma_q,
-    const uint8_t* __restrict__ gamma_k, float eps, float inv_d, uint32_t norm) {
+__device__ __forceinline__ void proj_tile(const ProjKArgs& args, uint32_t id, uint32_t count,
+                                          uint32_t n_begin, uint32_t n_end, uint8_t* smem) {
   constexpr int MB = G::MB, NB = G::NB, BK = G::BK;
-  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  const uint8_t* __restrict__ x = args.x;
+  const uint8_t* __restrict__ w = args.w;
+  const uint32_t ldx_bytes = args.ldx_bytes, ldw_bytes = args.ldw_bytes;
+  const uint32_t T = args.T, K = args.K;
   const uint32_t tid = threadIdx.x, lane = tid & 63;
   const uint32_t wave = uniform(tid >> 6);
   const uint32_t wm = wave / G::WN, wn = wave % G::WN;
   uint32_t m0, n0;
-  tile_origin<G>(T, N, &m0, &n0);
+  tile_origin<G>(T, n_end - n_begin, id, count, &m0, &n0);
+  n0 += n_begin;
 
   const uint32_t a_rows = T - m0 < (uint32_t)G::BM ? T - m0 : (uint32_t)G::BM;
-  const uint32_t b_rows = N - n0 < (uint32_t)G::BN ? N - n0 : (uint32_t)G::BN;
+  const uint32_t b_rows = n_end - n0 < (uint32_t)G::BN ? n_end - n0 : (uint32_t)G::BN;
   const Rsrc ra = make_rsrc(x + (uint64_t)m0 * ldx_bytes, (uint64_t)(a_rows - 1) * ldx_bytes + K * 2);
   const Rsrc rb = make_rsrc(w + (uint64_t)n0 * ldw_bytes, (uint64_t)(b_rows - 1) * ldw_bytes + K * 2);
+  const EpiGamma<G> eg = epi_gamma<G, DT, D>(lane, wn, n0, n_end, args.hq, args.hkv, args.gamma_q,
+                                             args.gamma_k, w, args.norm);
 
-  f32x16 acc[MB][NB];
+  typename G::Acc acc[MB][NB];
 #pragma unroll
   for (int i = 0; i < MB; ++i)
 #pragma unroll
     for (int j = 0; j < NB; ++j)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+      for (int e = 0; e < MfmaShape<G::MS>::NACC; ++e) acc[i][j][e] = 0.f;
 
   // Two LDS stages; K step ks computes from stage ks % 2.  Fragments are
   // double-buffered in registers: the reads of sub-step kk+1 are issued
@@ -378,13 +462,13 @@ __global__ __launch_bounds__(G::kThreads) void qkv_proj_kernel(
   // reads of it have completed), so the loads of step ks+2 go there, and the
   // first fragments of step ks+1 are read while the last MFMAs of step ks
   // run.  Loads past the last step fetch the last step again (unused).
-  static_assert(G::S == 2 && BK % 32 == 0, "two stages, an even number of 16-wide sub-steps");
-  constexpr int KK = BK / 16;
+  static_assert(G::S == 2 && G::KK % 2 == 0, "two stages, an even number of MFMA steps");
+  constexpr int KK = G::KK;
   const uint32_t ksteps = K / BK;
-  // a lane's fragment: row (lane % 32) of a 32-row block, 8 consecutive k
-  // starting at 8*(lane/32) of each 16-wide MFMA step; A and B use the same
+  // a lane's fragment: row (lane % MS) of an MS-row block, 8 consecutive k
+  // starting at 8*(lane/MS) of each KS-wide MFMA step; A and B use the same
   // k order, so the products pair correctly whatever order the hardware sums
-  const uint32_t fr = lane % 32, fk = 8 * (lane / 32);
+  const uint32_t fr = lane % G::MS, fk = 8 * (lane / G::MS);
   const uint32_t arow = wm * G::kWaveM + fr, brow = G::BM + wn * G::kWaveN + fr;
   uint8_t* const stage0 = smem;
   uint8_t* const stage1 = smem + G::kStageBytes;
@@ -400,16 +484,21 @@ __global__ __launch_bounds__(G::kThreads) void qkv_proj_kernel(
   read_frags<G, DT>(stage0, arow, brow, fk, fa[0], fb[0]);
 
   constexpr int kReads = MB + NB, kMfma = MB * NB;
-  static_assert(kMfma > kReads && G::kLoads % (kMfma - kReads) == 0, "");
+  // the next sub-step's fragment reads go one after every kMfmaPerRead MFMAs
+  // (where there are MFMAs enough), the step's loads between the MFMAs after them
+  constexpr int kMfmaPerRead = QKNORM_PROJ_MPR * kReads < kMfma ? QKNORM_PROJ_MPR : 1;
+  constexpr int kLoadsPerMfma =
+      (G::kLoads + kMfma - kReads * kMfmaPerRead - 1) / (kMfma - kReads * kMfmaPerRead);
+  static_assert(kMfma > kReads, "");
   for (uint32_t ks = 0; ks < ksteps; ++ks) {
     uint8_t* const st = (ks & 1) ? stage1 : stage0;
     uint8_t* const nx = (ks & 1) ? stage0 : stage1;
 #pragma unroll
     for (int kk = 0; kk < KK - 1; ++kk) {
-      read_frags<G, DT>(st, arow, brow, (kk + 1) * 16 + fk, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
+      read_frags<G, DT>(st, arow, brow, (kk + 1) * G::KS + fk, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
       mfma_step<G, DT>(acc, fa[kk & 1], fb[kk & 1]);
-      sched_interleave<kReads, 1, 0>();
-      sched_mfmas<kMfma - kReads>();
+      sched_interleave<kReads, 1, 0, kMfmaPerRead>();
+      sched_mfmas<kMfma - kReads * kMfmaPerRead>();
       __builtin_amdgcn_sched_barrier(0);
     }
     wait_vmcnt<0>();                            // step ks+1 has landed (this wave)
@@ -420,8 +509,8 @@ __global__ __launch_bounds__(G::kThreads) void qkv_proj_kernel(
     read_frags<G, DT>(nx, arow, brow, fk, fa[0], fb[0]);
     dma_tile<G>(ra, rb, doff, step_bytes<G>(ks + 2, ksteps), st, wave);
     mfma_step<G, DT>(acc, fa[1], fb[1]);
-    sched_interleave<kReads, 1, 0>();
-    sched_interleave<kMfma - kReads, 0, G::kLoads / (kMfma - kReads)>();
+    sched_interleave<kReads, 1, 0, kMfmaPerRead>();
+    sched_interleave<kMfma - kReads * kMfmaPerRead, 0, kLoadsPerMfma>();
     // keeps the reads above in this iteration: without it the compiler merges
     // them with the reads before the loop into one read at the top of the
     // loop, which then waits for its result before the first MFMA
@@ -430,147 +519,26 @@ __global__ __launch_bounds__(G::kThreads) void qkv_proj_kernel(
   // the output tile reuses the stages: every load into LDS must be done
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  proj_epilogue<G, DT, D>(acc, smem, tid, lane, wm, wn, m0, n0, a_rows, N, hq, hkv, gamma_q, gamma_k,
-                          eps, inv_d, norm, out, ld_bytes);
+  proj_epilogue<G, DT, D>(acc, smem, tid, lane, wm, wn, m0, n0, a_rows, n_end, eg, args.eps, args.inv_d,
+                          args.norm, args.out, args.ld_bytes);
 }
 
-// ------------------------------------------------------------- ping-pong --
-//
-// The same tile with a different schedule of its main loop.  The 8 waves
-// form two groups, waves 0-3 and 4-7, and the two waves that share a SIMD
-// (w and w+4) belong to different groups.  Each wave alternates a memory
-// phase M_j (issue the block's loads into LDS of step j+D -- group 0 only --
-// and read every fragment of step j into registers) and a compute phase C_j
-// (the step's MFMAs back to back), and group 1 runs one phase behind group 0,
-// with a workgroup barrier between phases:
-//
-//   slot:     0     1     2     3     4   ...
-//   group 0:  M_0   C_0   M_1   C_1   M_2
-//   group 1:  --    M_0   C_0   M_1   C_1
-//
-// so in every slot one wave of each SIMD issues MFMAs while the other does
-// its memory work, and the matrix core of the SIMD is fed by one wave at a
-// time.  S LDS stages hold steps j .. j+S-1; the loads of step j+D (D = S-1)
-// go into the stage that step j-1 used, whose last reads (group 1, M_{j-1})
-// ended before the barrier that opens M_j.  Group 0 waits for its loads of
-// step j+1 at the end of C_j, before the barrier that opens M_{j+1}.
-
-// Per-lane part of a loader wave's load offsets: row `sub` of the
-// instruction, chunk slot of lane % CPR.  Rows R of an instruction start at
-// multiples of kInstRows = 4 * RPB, so the swizzle of row R + sub is
-// ((4 * (R / kInstRows) + sub / RPB) % CPR): it depends on the instruction
-// index only through (4 * idx) % CPR, which is 0 or 4.
-template <class G>
-__device__ __forceinline__ uint32_t pp_lane_part(uint32_t ld_bytes, uint32_t lane, uint32_t phase) {
-  const uint32_t sub = lane / G::CPR, s = lane % G::CPR;
-  return sub * ld_bytes + (s ^ ((phase + sub / G::RPB) % G::CPR)) * 16;
-}
-
-// One K step of both operand tiles into `stage`, issued by the 4 loader waves
-// (group 0), kL instructions of A rows and kL of B rows each.  The row part of
-// each offset is added per instruction (it travels in the vector offset, so
-// rows past the end of x or w fall outside the descriptor and arrive as
-// zeros).
-template <class G>
-__device__ __forceinline__ void pp_dma(Rsrc ra, Rsrc rb, uint32_t ldx_bytes, uint32_t ldw_bytes,
-                                       const uint32_t (&pa)[2], const uint32_t (&pb)[2], uint32_t k_bytes,
-                                       uint8_t* stage, uint32_t lw) {
-  constexpr uint32_t kRows = G::kInstRows, kRowBytes = G::kRowBytes, kBM = G::BM;
-  constexpr uint32_t kL = G::BM / G::kInstRows / 4;
-  static_assert(G::BM == G::BN, "as many A as B loads");
-#pragma unroll
-  for (uint32_t j = 0; j < kL; ++j) {
-    const uint32_t idx = lw * kL + j;
-    const uint32_t R = idx * kRows;
-    const uint32_t ph = ((4 * idx) % G::CPR) / 4;       // kL is even: the parity of j
-    const uint32_t va = pa[ph] + (R * ldx_bytes + k_bytes);
-    const uint32_t vb = pb[ph] + (R * ldw_bytes + k_bytes);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        ra, (__attribute__((address_space(3))) void*)(stage + R * kRowBytes), 16, va, 0, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        rb, (__attribute__((address_space(3))) void*)(stage + (kBM + R) * kRowBytes), 16, vb, 0, 0, 0);
-  }
-}
-
-template <class G, int DT, int D>
-__global__ __launch_bounds__(G::kThreads) void qkv_proj_pp_kernel(
-    const uint8_t* __restrict__ x, uint32_t ldx_bytes, const uint8_t* __restrict__ w,
-    uint32_t ldw_bytes, uint8_t* __restrict__ out, uint64_t ld_bytes, uint32_t T, uint32_t K,
-    uint32_t N, uint32_t hq, uint32_t hkv, const uint8_t* __restrict__ gamma_q,
-    const uint8_t* __restrict__ gamma_k, float eps, float inv_d, uint32_t norm) {
-  constexpr int MB = G::MB, NB = G::NB, BK = G::BK, S = G::S, DIST = S - 1;
-  constexpr int KK = BK / 16;
-  constexpr uint32_t kL = G::BM / G::kInstRows / 4;           // loads per operand per loader wave
-  constexpr int kBatch = 2 * kL;                               // loads per loader wave per step
-  static_assert(G::kWaves == 8 && S >= 2 && (kL % 2 == 0 || G::CPR <= 4), "");
-  static_assert((DIST - 1) * kBatch < 64, "vmcnt range");
+// Blocks 0 .. n_full-1 take full tiles (GF) of columns [0, n_split); the rest
+// take half-width tiles (GH) of columns [n_split, N).  The half-width tail
+// lets a launch fill whole rounds of the chip's CUs where full tiles alone
+// would leave a round half empty (384 tiles on 256 CUs at T = 4096).
+template <class GF, class GH, int DT, int D>
+__global__ __launch_bounds__(GF::kThreads) void qkv_proj_kernel(ProjKArgs args, uint32_t n_full,
+                                                                uint32_t n_split) {
+  static_assert(GF::kThreads == GH::kThreads, "one block size");
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  const uint32_t tid = threadIdx.x, lane = tid & 63;
-  const uint32_t wave = uniform(tid >> 6);
-  const uint32_t wm = wave / G::WN, wn = wave % G::WN;
-  const uint32_t grp = wave >> 2, lw = wave & 3;
-  uint32_t m0, n0;
-  tile_origin<G>(T, N, &m0, &n0);
-  const uint32_t a_rows = T - m0 < (uint32_t)G::BM ? T - m0 : (uint32_t)G::BM;
-  const uint32_t b_rows = N - n0 < (uint32_t)G::BN ? N - n0 : (uint32_t)G::BN;
-  const Rsrc ra = make_rsrc(x + (uint64_t)m0 * ldx_bytes, (uint64_t)(a_rows - 1) * ldx_bytes + K * 2);
-  const Rsrc rb = make_rsrc(w + (uint64_t)n0 * ldw_bytes, (uint64_t)(b_rows - 1) * ldw_bytes + K * 2);
-
-  f32x16 acc[MB][NB];
-#pragma unroll
-  for (int i = 0; i < MB; ++i)
-#pragma unroll
-    for (int j = 0; j < NB; ++j)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
-
-  const uint32_t ksteps = K / BK;
-  const uint32_t fr = lane % 32, fk = 8 * (lane / 32);
-  const uint32_t arow = wm * G::kWaveM + fr, brow = G::BM + wn * G::kWaveN + fr;
-  const uint32_t pa[2] = {pp_lane_part<G>(ldx_bytes, lane, 0), pp_lane_part<G>(ldx_bytes, lane, 4)};
-  const uint32_t pb[2] = {pp_lane_part<G>(ldw_bytes, lane, 0), pp_lane_part<G>(ldw_bytes, lane, 4)};
-  auto stage = [&](uint32_t k) { return smem + (k % S) * G::kStageBytes; };
-
-  // prologue: steps 0 .. DIST-1 into their stages (group 0 loads)
-  if (grp == 0) {
-#pragma unroll
-    for (int d = 0; d < DIST; ++d)
-      if ((uint32_t)d < ksteps) pp_dma<G>(ra, rb, ldx_bytes, ldw_bytes, pa, pb, d * BK * 2, stage(d), lw);
+  if (blockIdx.x < n_full) {
+    proj_tile<GF, DT, D>(args, blockIdx.x, n_full, 0, n_split, smem);
+  } else if constexpr (D <= GH::BN) {
+    // a half-width tile holds whole heads, or one head across its two column
+    // waves (head_dim 128); head_dim 256 never takes this path
+    proj_tile<GH, DT, D>(args, blockIdx.x - n_full, gridDim.x - n_full, n_split, args.N, smem);
   }
-  wait_vmcnt<0>();
-  stage_barrier();
-  if (grp == 1) stage_barrier();               // group 1 starts one phase later
-
-  typedef typename ProjElem<DT>::V8 Frag;
-  Frag fa[KK][MB], fb[KK][NB];
-  for (uint32_t j = 0; j < ksteps; ++j) {
-    // M_j
-    __builtin_amdgcn_sched_barrier(0);
-    const bool load_next = j + DIST < ksteps;
-    if (grp == 0 && load_next)
-      pp_dma<G>(ra, rb, ldx_bytes, ldw_bytes, pa, pb, (j + DIST) * BK * 2, stage(j + DIST), lw);
-    const uint8_t* st = stage(j);
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) read_frags<G, DT>(st, arow, brow, kk * 16 + fk, fa[kk], fb[kk]);
-    stage_barrier();
-    __builtin_amdgcn_sched_barrier(0);
-    // C_j
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) mfma_step<G, DT>(acc, fa[kk], fb[kk]);
-    __builtin_amdgcn_sched_barrier(0);
-    if (grp == 0) {
-      // step j+1 has landed (the loads of later steps may stay in flight)
-      if (load_next) wait_vmcnt<(DIST - 1) * kBatch>();
-      else wait_vmcnt<0>();
-    }
-    stage_barrier();
-  }
-  if (grp == 0) stage_barrier();              // matches group 1's extra barrier
-  // the output tile reuses the stages: every load into LDS must be done
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  proj_epilogue<G, DT, D>(acc, smem, tid, lane, wm, wn, m0, n0, a_rows, N, hq, hkv, gamma_q, gamma_k,
-                          eps, inv_d, norm, out, ld_bytes);
 }
 
 // 256 x 256 tiles of 8 waves (4 along M, 2 along N), each wave 64 x 128:
@@ -592,33 +560,20 @@ __global__ __launch_bounds__(G::kThreads) void qkv_proj_pp_kernel(
 #ifndef QKNORM_PROJ_BK
 #define QKNORM_PROJ_BK 64
 #endif
-#ifndef QKNORM_PROJ_WM
-#define QKNORM_PROJ_WM 4
+#ifndef QKNORM_PROJ_MS
+#define QKNORM_PROJ_MS 16          // MFMA block: 16 (16 x 16 x 32) or 32 (32 x 32 x 16)
 #endif
-#ifndef QKNORM_PROJ_WN
-#define QKNORM_PROJ_WN 2
+#ifndef QKNORM_PROJ_SPLIT
+#define QKNORM_PROJ_SPLIT 1        // 0: full tiles only
 #endif
-#ifndef QKNORM_PROJ_PP
-#define QKNORM_PROJ_PP 0           // 1: the ping-pong main loop
-#endif
-#ifndef QKNORM_PROJ_PP_BK
-#define QKNORM_PROJ_PP_BK 64
-#endif
-#ifndef QKNORM_PROJ_PP_S
-#define QKNORM_PROJ_PP_S 2
-#endif
-constexpr bool kPingPong = QKNORM_PROJ_PP != 0;
-using GeoIl = Tile<256, 256, QKNORM_PROJ_WM, QKNORM_PROJ_WN, QKNORM_PROJ_BK, 2>;
-using GeoPp = Tile<256, 256, 4, 2, QKNORM_PROJ_PP_BK, QKNORM_PROJ_PP_S>;
-using Geo = std::conditional_t<kPingPong, GeoPp, GeoIl>;
-constexpr int kBM = Geo::BM, kBN = Geo::BN, kThreads = Geo::kThreads;
-constexpr int kLdsBytes = Geo::kLdsBytes;
-
-template <int DT, int D>
-constexpr auto proj_kernel() {
-  if constexpr (kPingPong) return qkv_proj_pp_kernel<Geo, DT, D>;
-  else return qkv_proj_kernel<Geo, DT, D>;
-}
+// Full tiles: 256 x 256, 8 waves of 64 x 128.  Half-width tiles: 256 x 128,
+// 8 waves of 64 x 64.
+using GeoF = Tile<256, 256, 4, 2, QKNORM_PROJ_BK, 2, QKNORM_PROJ_MS>;
+// (32 x 32 blocks leave a 64 x 64 wave only 4 MFMAs per step: no tail then)
+using GeoH = std::conditional_t<QKNORM_PROJ_MS == 16, Tile<256, 128, 4, 2, QKNORM_PROJ_BK, 2, 16>, GeoF>;
+constexpr bool kSplit = QKNORM_PROJ_SPLIT != 0 && QKNORM_PROJ_MS == 16;
+constexpr int kBM = GeoF::BM, kBN = GeoF::BN, kThreads = GeoF::kThreads;
+constexpr int kLdsBytes = GeoF::kLdsBytes > GeoH::kLdsBytes ? GeoF::kLdsBytes : GeoH::kLdsBytes;
 
 }  // namespace
 
@@ -628,35 +583,75 @@ bool proj_shape_ok(const ProjArgs& a) {
   return (uint64_t)kBM * a.ldx * es < (UINT64_C(1) << 31) &&
          (uint64_t)kBN * a.ldw * es < (UINT64_C(1) << 31) &&
          (uint64_t)kBM * a.ld * es < (UINT64_C(1) << 31) && a.hidden % 64 == 0 &&
-         // the tiles are numbered in one grid dimension, whose size in
-         // threads must fit 32 bits
-         (uint64_t)((a.T + kBM - 1) / kBM) * (uint64_t)(((a.hq + 2 * a.hkv) * a.head_dim + kBN - 1) / kBN) *
+         // the tiles (full or half-width) are numbered in one grid
+         // dimension, whose size in threads must fit 32 bits
+         (uint64_t)((a.T + kBM - 1) / kBM) *
+                 (uint64_t)(((a.hq + 2 * a.hkv) * a.head_dim + GeoH::BN - 1) / GeoH::BN) *
                  (uint64_t)kThreads <
              (UINT64_C(1) << 32) &&
          (a.head_dim == 64 || a.head_dim == 128 || a.head_dim == 256);
 }
 
-hipError_t launch_qkv_proj(const ProjArgs& a, hipStream_t s) {
+// Where the half-width tail starts: the column n_split (a multiple of 256)
+// that minimises the estimated time in rounds of the chip's CUs, a full tile
+// costing 1 and a half-width tile kHalfCost; n_split = N means no tail.
+// Head dims above 128 never split (a half-width tile would cut a head).
+static uint32_t split_column(uint32_t T, uint32_t N, uint32_t head_dim, int cus) {
+  constexpr double kHalfCost = 0.6;
+  const uint64_t m_tiles = (T + kBM - 1) / kBM;
+  const uint64_t c = cus > 0 ? (uint64_t)cus : 1;
+  auto rounds = [&](uint64_t n) { return (double)((n + c - 1) / c); };
+  const uint64_t all = m_tiles * ((N + kBN - 1) / kBN);
+  uint32_t best = N;
+  double best_cost = rounds(all);
+  if (!kSplit || head_dim > (uint32_t)GeoH::BN) return best;
+  for (uint32_t n1 = 0; n1 < N; n1 += kBN) {
+    const uint64_t full = m_tiles * (n1 / kBN);
+    const uint64_t half = m_tiles * ((N - n1 + GeoH::BN - 1) / GeoH::BN);
+    const double cost = rounds(full) + kHalfCost * rounds(half);
+    if (cost < best_cost - 1e-9) { best_cost = cost; best = n1; }
+  }
+  return best;
+}
+
+hipError_t launch_qkv_proj(const ProjArgs& a, hipStream_t s, int cus) {
   const uint32_t N = (uint32_t)((a.hq + 2 * a.hkv) * a.head_dim);
-  const dim3 grid((uint32_t)(((N + kBN - 1) / kBN) * ((a.T + kBM - 1) / kBM)));
+  const uint32_t T = (uint32_t)a.T;
+  const uint32_t n_split = split_column(T, N, (uint32_t)a.head_dim, cus);
+  const uint32_t m_tiles = (T + kBM - 1) / kBM;
+  const uint32_t n_full = m_tiles * ((n_split + kBN - 1) / kBN);
+  const uint32_t n_half = n_split < N ? m_tiles * ((N - n_split + GeoH::BN - 1) / GeoH::BN) : 0;
   auto pick = [&](auto k64, auto k128, auto k256) {
     return a.head_dim == 64 ? k64 : (a.head_dim == 128 ? k128 : k256);
   };
-  auto kern = a.dtype == kF16 ? pick(proj_kernel<kF16, 64>(), proj_kernel<kF16, 128>(),
-                                     proj_kernel<kF16, 256>())
-                              : pick(proj_kernel<kBF16, 64>(), proj_kernel<kBF16, 128>(),
-                                     proj_kernel<kBF16, 256>());
+  auto kern = a.dtype == kF16
+                  ? pick(qkv_proj_kernel<GeoF, GeoH, kF16, 64>, qkv_proj_kernel<GeoF, GeoH, kF16, 128>,
+                         qkv_proj_kernel<GeoF, GeoH, kF16, 256>)
+                  : pick(qkv_proj_kernel<GeoF, GeoH, kBF16, 64>, qkv_proj_kernel<GeoF, GeoH, kBF16, 128>,
+                         qkv_proj_kernel<GeoF, GeoH, kBF16, 256>);
   // more than the default 64 KiB of dynamic LDS (gfx950 has 160 KiB per CU);
   // a host-side attribute, set on every call (no shared state between threads)
   const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, grid, dim3(kThreads), kLdsBytes, s, (const uint8_t*)a.x,
-                     (uint32_t)(a.ldx * 2), (const uint8_t*)a.w, (uint32_t)(a.ldw * 2),
-                     (uint8_t*)a.qkv, (uint64_t)a.ld * 2, (uint32_t)a.T, (uint32_t)a.hidden, N,
-                     (uint32_t)a.hq, (uint32_t)a.hkv, (const uint8_t*)a.gamma_q,
-                     (const uint8_t*)a.gamma_k, a.eps, 1.0f / (float)a.head_dim,
-                     (uint32_t)((a.flags & 1) == 0));
+  ProjKArgs k;
+  k.x = (const uint8_t*)a.x;
+  k.w = (const uint8_t*)a.w;
+  k.out = (uint8_t*)a.qkv;
+  k.gamma_q = (const uint8_t*)a.gamma_q;
+  k.gamma_k = (const uint8_t*)a.gamma_k;
+  k.ld_bytes = (uint64_t)a.ld * 2;
+  k.ldx_bytes = (uint32_t)(a.ldx * 2);
+  k.ldw_bytes = (uint32_t)(a.ldw * 2);
+  k.T = T;
+  k.K = (uint32_t)a.hidden;
+  k.N = N;
+  k.hq = (uint32_t)a.hq;
+  k.hkv = (uint32_t)a.hkv;
+  k.norm = (uint32_t)((a.flags & 1) == 0);
+  k.eps = a.eps;
+  k.inv_d = 1.0f / (float)a.head_dim;
+  hipLaunchKernelGGL(kern, dim3(n_full + n_half), dim3(kThreads), kLdsBytes, s, k, n_full, n_split);
   return hipGetLastError();
 }
 

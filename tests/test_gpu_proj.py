@@ -115,6 +115,25 @@ def test_fused_projection_against_oracle(T, hidden, hq, hkv, D):
     check(x, w, hq, hkv, D, gq, gk, eps, got, label=f"fused T={T} K={hidden}")
 
 
+# Which tile shapes a launch uses depends on the grid: a tail of half-width
+# (256 x 128) tiles is added where it fills the chip's CUs better (for
+# head_dim <= 128).  On MI355X's 256 CUs these shapes take, in turn: only
+# half-width tiles (small T), only full tiles, and full tiles for the first
+# columns with a half-width tail (N = 6144: from column 4864 at T = 6000, from
+# column 4096 at T = 4096).
+@pytest.mark.parametrize("T,hidden,hq,hkv,D", [
+    (500, 256, 32, 8, 128),      # 2 row tiles x 48 half-width tiles: one round
+    (2048, 256, 32, 8, 128),     # 8 x 24 full tiles: one round, no tail
+    (6000, 256, 32, 8, 128),     # 24 x 19 full tiles, then a tail of 24 x 10 half-width
+    (4096, 192, 64, 16, 64),     # head_dim 64: 16 x 16 full tiles, then 16 x 16 half-width
+])
+def test_full_and_half_width_tiles(T, hidden, hq, hkv, D):
+    x, w, gq, gk = make(95 + T, T, hidden, hq, hkv, D)
+    eps = synth.eps_f32(1e-6)
+    got = run_proj(x, w, hq, hkv, D, gq, gk, eps, label="tile shapes")
+    check(x, w, hq, hkv, D, gq, gk, eps, got, label=f"tile shapes T={T} K={hidden} D={D}")
+
+
 def test_plain_projection_and_padding():
     T, hidden, hq, hkv, D = 77, 320, 4, 2, 128
     x, w, gq, gk = make(80, T, hidden, hq, hkv, D)
@@ -132,7 +151,7 @@ def test_plain_projection_and_padding():
     (260, 512, 8, 4, 256),       # D = 256
 ])
 def test_fp16_projection_against_oracle(T, hidden, hq, hkv, D):
-    # the same kernel with fp16 operands, gamma and output (v_mfma_f32_32x32x16_f16)
+    # the same kernel with fp16 operands, gamma and output (v_mfma_f32_16x16x32_f16)
     x, w, gq, gk = make(90 + T, T, hidden, hq, hkv, D, dtype=F16)
     eps = synth.eps_f32(1e-6)
     N = w.shape[0]
