@@ -81,6 +81,50 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     return lib
 
 
+_calls_mod = None       # the CPython call module (or its ctypes stand-in)
+
+
+class _CtypesCalls:
+    """The call module's functions through ctypes, for a tree where the module
+    is not built (the same library calls, only slower to make)."""
+
+    def __init__(self, lib):
+        self.per_head = lib.qknorm_per_head
+        self.layerwise = lib.qknorm_layerwise
+        self.partial_sumsq = lib.qknorm_partial_sumsq
+        self.apply_scalar = lib.qknorm_apply_scalar
+        self.qkv_proj_per_head = lib.qknorm_qkv_proj_per_head
+
+    @staticmethod
+    def per_head_t(*_):
+        return None
+
+    @staticmethod
+    def layerwise_t(*_):
+        return None
+
+
+def _calls():
+    """The functions that call the C ABI: `_qknorm_fast` (qk_norm_amd/csrc/pyfast.c),
+    which converts the Python ints and floats itself and, for the common case of
+    contiguous GPU tensors, reads the tensors itself too; or ctypes."""
+    global _calls_mod
+    if _calls_mod is None:
+        lib = load()
+        try:
+            from . import _qknorm_fast as mod
+        except ImportError:
+            mod = _CtypesCalls(lib)
+        else:
+            import torch
+            if _CODES is None:
+                _torch_tables()
+            dts = (torch.float32, torch.bfloat16, torch.float16, torch.float8_e4m3fn)
+            mod.setup(dts, tuple(_CODES[d][1] for d in dts), _raw_stream)
+        _calls_mod = mod
+    return _calls_mod
+
+
 def strerror(code: int) -> str:
     return load().qknorm_strerror(int(code)).decode()
 
@@ -123,6 +167,10 @@ def _rows(qkv):
     """(T, ld, device index) of a [T, ...] GPU tensor whose rows are packed."""
     if not qkv.is_cuda:
         raise ValueError("qkv must be a GPU tensor (the library has no CPU path)")
+    if qkv.is_contiguous() and qkv.dim() >= 2:
+        T = qkv.shape[0]
+        if T > 0:                # rows back to back: the pitch is the row's size
+            return T, qkv.numel() // T, qkv.get_device()
     shape, stride = qkv.shape, qkv.stride()
     if len(shape) < 2:
         raise ValueError("qkv must have a leading token dimension and at least one more")
@@ -180,21 +228,27 @@ def _raise(rc: int, what: str):
 def qknorm_per_head(qkv, hq: int, hkv: int, head_dim: int, gamma_q, gamma_k=None,
                     eps: float = 1e-6, stream=None) -> None:
     """Per-head RMSNorm of the hq Q heads and hkv K heads of each row, in place."""
-    T, ld, dev = _rows(qkv)
-    rc = (_lib or load()).qknorm_per_head(qkv.data_ptr(), T, ld, hq, hkv, head_dim,
-                                          _gamma(gamma_q, qkv, dev), _gamma(gamma_k, qkv, dev),
-                                          eps, _dtype_code(qkv), _stream(stream, dev))
-    _raise(rc, "qknorm_per_head")
+    c = _calls_mod or _calls()
+    rc = c.per_head_t(qkv, hq, hkv, head_dim, gamma_q, gamma_k, eps, stream)
+    if rc is None:               # not the common case: the full checks, in Python
+        T, ld, dev = _rows(qkv)
+        rc = c.per_head(qkv.data_ptr(), T, ld, hq, hkv, head_dim, _gamma(gamma_q, qkv, dev),
+                        _gamma(gamma_k, qkv, dev), eps, _dtype_code(qkv), _stream(stream, dev))
+    if rc:
+        _raise(rc, "qknorm_per_head")
 
 
 def qknorm_layerwise(qkv, wq: int, wk: int, gamma_q, gamma_k=None, eps: float = 1e-6,
                      nshards: int = 1, stream=None) -> None:
     """Layerwise RMSNorm over the whole Q and K widths via nshards partials, in place."""
-    T, ld, dev = _rows(qkv)
-    rc = (_lib or load()).qknorm_layerwise(qkv.data_ptr(), T, ld, wq, wk, _gamma(gamma_q, qkv, dev),
-                                           _gamma(gamma_k, qkv, dev), eps, nshards,
-                                           _dtype_code(qkv), _stream(stream, dev))
-    _raise(rc, "qknorm_layerwise")
+    c = _calls_mod or _calls()
+    rc = c.layerwise_t(qkv, wq, wk, gamma_q, gamma_k, eps, nshards, stream)
+    if rc is None:               # not the common case: the full checks, in Python
+        T, ld, dev = _rows(qkv)
+        rc = c.layerwise(qkv.data_ptr(), T, ld, wq, wk, _gamma(gamma_q, qkv, dev),
+                         _gamma(gamma_k, qkv, dev), eps, nshards, _dtype_code(qkv), _stream(stream, dev))
+    if rc:
+        _raise(rc, "qknorm_layerwise")
 
 
 def _partials(p, dev):
@@ -210,7 +264,7 @@ def qknorm_partial_sumsq(qkv, wq: int, wk: int, nshards: int, part_q, part_k,
                          stream=None) -> None:
     """Shard partial sums of squares into part_q / part_k, float32 [nshards, T]."""
     T, ld, dev = _rows(qkv)
-    rc = (_lib or load()).qknorm_partial_sumsq(qkv.data_ptr(), T, ld, wq, wk, nshards,
+    rc = _calls().partial_sumsq(qkv.data_ptr(), T, ld, wq, wk, nshards,
                                                _partials(part_q, dev), _partials(part_k, dev),
                                                _dtype_code(qkv), _stream(stream, dev))
     _raise(rc, "qknorm_partial_sumsq")
@@ -224,7 +278,7 @@ def qknorm_apply_scalar(qkv, wq: int, wk: int, part_q, part_k, norm_wq: int, nor
     if nparts is None:
         ref = part_q if part_q is not None else part_k
         nparts = ref.shape[0] if ref is not None else 1
-    rc = (_lib or load()).qknorm_apply_scalar(qkv.data_ptr(), T, ld, wq, wk,
+    rc = _calls().apply_scalar(qkv.data_ptr(), T, ld, wq, wk,
                                               _partials(part_q, dev), _partials(part_k, dev),
                                               nparts, norm_wq, norm_wk, _gamma(gamma_q, qkv, dev),
                                               _gamma(gamma_k, qkv, dev), eps, _dtype_code(qkv),
@@ -258,7 +312,7 @@ def qknorm_qkv_proj_per_head(x, w, qkv, hq: int, hkv: int, head_dim: int, gamma_
         raise ValueError("x, w and qkv must share the dtype")
     if x.shape[0] != qkv.shape[0] or x.shape[1] != w.shape[1]:
         raise ValueError("x [T, hidden], w [N, hidden] and qkv [T, >= N] do not match")
-    rc = (_lib or load()).qknorm_qkv_proj_per_head(
+    rc = _calls().qkv_proj_per_head(
         xp, ldx, wp, ldw, op, ld, x.shape[0], x.shape[1], hq, hkv, head_dim,
         None if plain else _gamma(gamma_q, qkv, dev), None if plain else _gamma(gamma_k, qkv, dev),
         eps, QKNORM_PROJ_PLAIN if plain else 0, _dtype_code(qkv), _stream(stream, dev))

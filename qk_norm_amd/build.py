@@ -1,6 +1,7 @@
 """Build the gfx950 HIP libraries in-tree: qk_norm_amd/libqknorm.so (the
 QK-Norm C ABI) and qk_norm_amd/libqknorm_ceiling.so (the bench's bandwidth
-ceiling probes, loaded by bench.py only).
+ceiling probes, loaded by bench.py only); and the CPython module
+qk_norm_amd/_qknorm_fast*.so that the binding calls the C ABI through.
 
     python -m qk_norm_amd.build            # or __graft_entry__.build()
 
@@ -21,6 +22,7 @@ SOURCES = [os.path.join(CSRC, "qknorm_api.hip"), os.path.join(CSRC, "qknorm_kern
            os.path.join(CSRC, "qknorm_proj.hip")]
 LIB = os.path.join(HERE, "libqknorm.so")
 CEILING_SOURCES = [os.path.join(CSRC, "ceiling_probe.hip")]
+FAST_SOURCE = os.path.join(CSRC, "pyfast.c")
 CEILING_LIB = os.path.join(HERE, "libqknorm_ceiling.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -38,7 +40,10 @@ def build(out: str = LIB, defines: list[str] | None = None, verbose: bool = Fals
     defs = list(defines or [])
     defs += os.environ.get("QKNORM_DEFINES", "").split()
     tmp = out + ".tmp"
-    cmd = [HIPCC, *FLAGS, *[f"-D{d}" for d in defs], "-o", tmp, *(sources or SOURCES)]
+    # the library's own file name as its SONAME: one copy in a process whether it
+    # is opened by path (ctypes) or found by name (the Python call module)
+    cmd = [HIPCC, *FLAGS, f"-Wl,-soname,{os.path.basename(out)}", *[f"-D{d}" for d in defs], "-o", tmp,
+           *(sources or SOURCES)]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -53,6 +58,31 @@ def build_ceiling(verbose: bool = False) -> str:
     return build(CEILING_LIB, verbose=verbose, sources=CEILING_SOURCES)
 
 
+def fast_module_path() -> str:
+    import sysconfig
+    return os.path.join(HERE, "_qknorm_fast" + sysconfig.get_config_var("EXT_SUFFIX"))
+
+
+def build_fast(verbose: bool = False) -> str:
+    """The CPython module that calls the C ABI directly (host C, gcc), linked
+    against libqknorm.so in the same directory."""
+    import sysconfig
+    out = fast_module_path()
+    tmp = out + ".tmp"
+    cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-Wall", "-Wextra", "-Wno-unused-parameter",
+           "-I", sysconfig.get_paths()["include"], "-I", os.path.join(ROOT, "include"),
+           "-o", tmp, FAST_SOURCE, "-L", HERE, "-l:libqknorm.so", "-Wl,-rpath,$ORIGIN"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        sys.stderr.write(res.stdout + res.stderr)
+        raise RuntimeError("gcc failed building the QK-Norm Python call module")
+    os.replace(tmp, out)
+    return out
+
+
 if __name__ == "__main__":
     print(build(verbose=True))
     print(build_ceiling(verbose=True))
+    print(build_fast(verbose=True))

@@ -257,3 +257,27 @@ def test_plain_c_program_gets_the_validation_codes():
                          timeout=60)
     assert res.returncode == 0, res.stderr
     assert "validation codes ok" in res.stdout
+
+
+def test_python_call_module_forwards_to_the_same_library(lib):
+    # the binding's call path (qk_norm_amd/csrc/pyfast.c) converts the Python
+    # arguments itself and calls the same extern "C" functions: the library's
+    # validation codes come back unchanged, and the process holds one copy of
+    # the library whichever way it was opened
+    from qk_norm_amd import _qknorm_fast as f
+    assert f.per_head(A16, 4, 6144, 48, 0, 128, A16, None, 1e-6, 99, None) == q.QKNORM_E_DTYPE
+    assert f.per_head(0, 4, 6144, 48, 0, 128, A16, None, 1e-6, BF16, None) == q.QKNORM_E_NULLPTR
+    assert f.layerwise(A16, 4, 6144, 4096, 1024, A16, A16, 1e-6, 3, BF16, None) == q.QKNORM_E_SHAPE
+    assert f.partial_sumsq(A16, 4, 6144, 4096, 1024, 0, A16, A16, BF16, None) == q.QKNORM_E_SHAPE
+    assert f.apply_scalar(A16, 4, 6144, 4096, 1024, None, None, 8, 4096, 1024, A16, A16, 1e-6, BF16,
+                          None) == q.QKNORM_E_NULLPTR
+    assert f.qkv_proj_per_head(A16, 4096, A16, 4096, A16, 6144, 16, 4096, 32, 8, 128, A16, A16, 1e-6, 0,
+                               F32, None) == q.QKNORM_E_UNSUPPORTED
+    assert f.per_head(A16, 0, 6144, 48, 0, 128, A16, None, float("nan"), BF16, None) == q.QKNORM_E_EPS
+    with pytest.raises(TypeError):
+        f.per_head(A16, 4)
+    with pytest.raises(OverflowError):
+        f.per_head(A16, 4, 6144, 1 << 40, 0, 128, A16, None, 1e-6, BF16, None)
+    assert q._calls() is f
+    maps = {line.split()[-1] for line in open("/proc/self/maps") if "libqknorm.so" in line}
+    assert maps == {os.path.realpath(q.LIB_PATH)}, maps

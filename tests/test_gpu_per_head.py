@@ -339,3 +339,48 @@ def test_rows_without_v_or_padding(dtype, hq, hkv):
     if p.gamma_k is None:
         p.gamma_k = synth.make_gamma(23, 4, D, dtype)
     run_per_head(p)
+
+
+def test_tensor_calls_take_the_c_marshalling_path():
+    # The binding hands contiguous row-major tensors to the call module's
+    # per_head_t / layerwise_t, which read the tensors from C.  For those it
+    # must launch (return 0, not None) and give the same bytes as the
+    # pointer-level call; other layouts must return None (Python path).
+    c = q._calls()
+    assert type(c).__name__ == "module", "the compiled call module was not loaded"
+    p = synth.fused_gqa_rows(T=96)
+    src = host_to_device(p.x, p.dtype)
+    gq, gk = gamma_to_device(p.gamma_q, p.dtype), gamma_to_device(p.gamma_k, p.dtype)
+    a, b = src.clone(), src.clone()
+    side = torch.cuda.Stream()
+    for stream in (None, side, side.cuda_stream):
+        a.copy_(src)
+        torch.cuda.synchronize()
+        assert c.per_head_t(a, p.hq, p.hkv, p.head_dim, gq, gk, p.eps, stream) == 0
+        torch.cuda.synchronize()
+        b.copy_(src)
+        assert c.per_head(b.data_ptr(), p.T, p.ld, p.hq, p.hkv, p.head_dim, gq.data_ptr(), gk.data_ptr(),
+                          p.eps, q._dtype_code(b), torch.cuda.current_stream().cuda_stream) == 0
+        torch.cuda.synchronize()
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16)), f"stream {stream!r}"
+    # layouts the C side leaves to Python
+    assert c.per_head_t(a[:, : p.wq + p.wk], p.hq, p.hkv, p.head_dim, gq, gk, p.eps, None) is None
+    assert c.per_head_t(a, p.hq, p.hkv, p.head_dim, gq.float(), gk, p.eps, None) is None
+    assert c.per_head_t(a.cpu(), p.hq, p.hkv, p.head_dim, gq, gk, p.eps, None) is None
+    assert c.per_head_t(a[0], p.hq, p.hkv, p.head_dim, gq, gk, p.eps, None) is None
+    # rejected arguments come back as the library's error code, nothing launched
+    a.copy_(src)
+    torch.cuda.synchronize()
+    assert c.per_head_t(a, -1, p.hkv, p.head_dim, gq, gk, p.eps, None) != 0
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), src.view(torch.int16))
+    # layerwise on the same rows: tensor call and pointer call agree bit for bit
+    lw = synth.layerwise_rows(T=96)
+    ls = host_to_device(lw.x, lw.dtype)
+    lgq, lgk = gamma_to_device(lw.gamma_q, lw.dtype), gamma_to_device(lw.gamma_k, lw.dtype)
+    la, lb = ls.clone(), ls.clone()
+    assert c.layerwise_t(la, lw.wq, lw.wk, lgq, lgk, lw.eps, lw.nshards, None) == 0
+    assert c.layerwise(lb.data_ptr(), lw.T, lw.ld, lw.wq, lw.wk, lgq.data_ptr(), lgk.data_ptr(), lw.eps, lw.nshards,
+                       q._dtype_code(lb), torch.cuda.current_stream().cuda_stream) == 0
+    torch.cuda.synchronize()
+    assert torch.equal(la.view(torch.int16), lb.view(torch.int16))
