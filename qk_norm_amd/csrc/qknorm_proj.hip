@@ -541,22 +541,23 @@ __global__ __launch_bounds__(GF::kThreads) void qkv_proj_kernel(ProjKArgs args, 
   }
 }
 
-// 256 x 256 tiles of 8 waves (4 along M, 2 along N), each wave 64 x 128:
-// 0.75 fragment reads per MFMA and 131 flop per byte of operand staged, the
-// best of the shapes measured on MI355X.  The others measured: 128 x 128 with
-// 64 x 64 waves; 256 x 128 and 128 x 256 with 4 waves; 256 x 256 with 4
-// waves of 128 x 128 (one wave per SIMD, 0.5 reads per MFMA, but about 7 %
-// slower: with no second wave on the SIMD every latency shows); BK = 32 with
-// three or four stages (more barriers outweigh the longer prefetch).  An L2
-// prefetch of later K steps (a 4-byte load per operand row) cost about 9 %:
-// it doubles the vector-memory requests per step.  4 waves of 128 x 128 with
-// the operands staged through registers (global loads two steps ahead, two
-// LDS stages) measured 11-17 % slower than this kernel.  Reading fragments two
-// sub-steps ahead, accumulating in AGPRs, leaving the loads to one wave per
-// SIMD, splitting a step's loads over two sub-steps (also with 4 waves of
-// 128 x 128), an epilogue that stores from registers, or a persistent grid
-// that loads the next tile during the epilogue changed the time by 3 % or
-// less.
+// 256 x 256 tiles of 8 waves (4 along M, 2 along N), each wave 64 x 128 as
+// 4 x 8 blocks of 16 x 16: 12 fragment reads per 32 MFMAs and 131 flop per
+// byte of operand staged, the best of the shapes measured on MI355X.  The
+// others measured: 128 x 128 with 64 x 64 waves; 256 x 128 and 128 x 256
+// with 4 waves; 256 x 256 with 4 waves of 128 x 128 (one wave per SIMD, 16
+// reads per 64 MFMAs, the accumulators in AGPRs): the same time for the
+// plain product and a slower norm epilogue; BK = 32 with three or four
+// stages (more barriers outweigh the longer prefetch).  32 x 32 x 16 MFMAs do
+// the same work from the same fragments but run the chip at a lower clock
+// (about 9 % slower).  An L2 prefetch of later K steps (a 4-byte load per
+// operand row) cost about 9 %: it doubles the vector-memory requests per
+// step.  Operands staged through registers instead of loaded straight into
+// LDS measured 11-17 % slower.  Reading fragments two sub-steps ahead,
+// leaving the loads to one wave per SIMD, splitting a step's loads over two
+// sub-steps, an epilogue that stores from registers, a persistent grid that
+// loads the next tile during the epilogue, or a ping-pong schedule of two
+// wave groups changed the time by 3 % or less, or made it slower.
 #ifndef QKNORM_PROJ_BK
 #define QKNORM_PROJ_BK 64
 #endif
