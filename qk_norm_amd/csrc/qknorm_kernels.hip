@@ -384,6 +384,20 @@ __device__ __forceinline__ float combine(const float* __restrict__ p, uint32_t n
   return s;
 }
 
+// Two such sums side by side (the Q and K partials of one row), each in the
+// same order as combine(): both regions' reads go out together, so a row
+// waits for one round of LDS reads instead of two.
+__device__ __forceinline__ void combine2(const float* __restrict__ p, const float* __restrict__ q,
+                                         uint32_t n, float* sp, float* sq) {
+  float a = 0.f, b = 0.f;
+  for (uint32_t r = 0; r < n; ++r) {
+    a += p[r];
+    b += q[r];
+  }
+  *sp = a;
+  *sq = b;
+}
+
 // --- register-resident slots (fused kernel, MODE 0) -------------------------
 //
 // Slot j of a lane is shard wave + (j / trips)*nw, vector lane + (j % trips)*64.
@@ -570,10 +584,13 @@ __device__ __forceinline__ void lw_finish(const RowGeom& G, Rsrc rs, uint32_t Rq
   for (int j = 0; j < QV; ++j) row.q.g[j] = gam.q.g[j];
 #pragma unroll
   for (int j = 0; j < KV; ++j) row.k.g[j] = gam.k.g[j];
+  // (a region without vectors reads partials nobody wrote and ignores them)
+  float sq, sk;
+  combine2(pq, pk, R, &sq, &sk);
   if (Rq) slots_apply<DT, QV>(rs, 0, G.q_svecs, Rq, wave, nw, lane, row.q,
-                              rms_scale(combine(pq, R, 1), G.inv_wq, eps), exceed_q);
+                              rms_scale(sq, G.inv_wq, eps), exceed_q);
   if (Rk) slots_apply<DT, KV>(rs, G.q_vecs * 16, G.k_svecs, Rk, wave, nw, lane, row.k,
-                              rms_scale(combine(pk, R, 1), G.inv_wk, eps), exceed_k);
+                              rms_scale(sk, G.inv_wk, eps), exceed_k);
 }
 
 // QV / KV: register slots per lane for Q and for K (a lane's shard vectors).
