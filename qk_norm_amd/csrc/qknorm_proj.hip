@@ -70,7 +70,7 @@ template <int MS>
 struct MfmaShape;
 template <>
 struct MfmaShape<32> {
-  static constexpr int KS = 16, NACC = 16;
+  [[maybe_unused]] static constexpr int KS = 16, NACC = 16;
   typedef f32x16 Acc;
 };
 template <>
@@ -312,7 +312,7 @@ __device__ __forceinline__ EpiGamma<G> epi_gamma(uint32_t lane, uint32_t wn, uin
 // LDS must have completed and every wave must have passed a barrier after
 // its last fragment read (the output staging reuses the stages).
 template <class G, int DT, int D>
-__device__ __forceinline__ void proj_epilogue(typename G::Acc (&acc)[G::MB][G::NB], uint8_t* smem, uint32_t tid,
+__device__ __forceinline__ void proj_epilogue(const typename G::Acc (&acc)[G::MB][G::NB], uint8_t* smem, uint32_t tid,
                                               uint32_t lane, uint32_t wm, uint32_t wn, uint32_t m0,
                                               uint32_t n0, uint32_t a_rows, uint32_t N,
                                               const EpiGamma<G>& eg, float eps, float inv_d,
@@ -326,36 +326,39 @@ __device__ __forceinline__ void proj_epilogue(typename G::Acc (&acc)[G::MB][G::N
   // squares is the lane's fma chain over those blocks, then the sum over the
   // MS lanes that hold the row.
   constexpr int JH = D / MS;                    // blocks per head
-  if (norm) {
-    const float* g = eg.g;
-    const bool* normed = eg.normed;
-    if constexpr (JH <= NB) {
-      static_assert(NB % JH == 0, "a wave's columns must be whole heads");
+  constexpr int NH = JH <= NB ? NB / JH : 1;     // heads in a wave's columns (or one half-head)
+  // the RMS scale of row (i, e) of head h; the scaled values (acc * g) * sc
+  // are formed once, as they go to LDS, so the accumulators are only read
+  float sc[MB][NH][NACC];
+  bool scaled[NH];
+  const float* g = eg.g;
+  const bool* normed = eg.normed;
+  if constexpr (JH <= NB) {
+    static_assert(NB % JH == 0, "a wave's columns must be whole heads");
+#pragma unroll
+    for (int h = 0; h < NH; ++h) {
+      // the same for every lane and every block of one head (heads lie in
+      // one region and the tile's columns past N are whole heads)
+      scaled[h] = norm && normed[h * JH];
+      if (!scaled[h]) continue;
 #pragma unroll
       for (int i = 0; i < MB; ++i)
 #pragma unroll
-        for (int h = 0; h < NB / JH; ++h) {
-          // the same for every lane and every block of one head (heads lie in
-          // one region and the tile's columns past N are whole heads)
-          if (!normed[h * JH]) continue;
+        for (int e = 0; e < NACC; ++e) {
+          float s = 0.f;
 #pragma unroll
-          for (int e = 0; e < NACC; ++e) {
-            float s = 0.f;
-#pragma unroll
-            for (int jj = 0; jj < JH; ++jj)
-              s = __builtin_fmaf(acc[i][h * JH + jj][e], acc[i][h * JH + jj][e], s);
-            s = group_sum<MS>(s);
-            const float sc = rms_scale(s, inv_d, eps);
-#pragma unroll
-            for (int jj = 0; jj < JH; ++jj)
-              acc[i][h * JH + jj][e] = (acc[i][h * JH + jj][e] * g[h * JH + jj]) * sc;
-          }
+          for (int jj = 0; jj < JH; ++jj)
+            s = __builtin_fmaf(acc[i][h * JH + jj][e], acc[i][h * JH + jj][e], s);
+          sc[i][h][e] = rms_scale(group_sum<MS>(s), inv_d, eps);
         }
-    } else {
-      // a head spans the tile's two column waves (D = 2 * kWaveN): each wave
-      // leaves its half-head row sums in LDS (the stages are free), and both
-      // add the two halves in the same order, so they scale with the same bits
-      static_assert(JH == 2 * NB && G::WN == 2 && G::BN == D, "one head across the two column waves");
+    }
+  } else {
+    // a head spans the tile's two column waves (D = 2 * kWaveN): each wave
+    // leaves its half-head row sums in LDS (the stages are free), and both
+    // add the two halves in the same order, so they scale with the same bits
+    static_assert(JH == 2 * NB && G::WN == 2 && G::BN == D, "one head across the two column waves");
+    scaled[0] = norm && normed[0];
+    if (norm) {
       float* half = reinterpret_cast<float*>(smem);   // [WN][BM]
 #pragma unroll
       for (int i = 0; i < MB; ++i)
@@ -369,15 +372,13 @@ __device__ __forceinline__ void proj_epilogue(typename G::Acc (&acc)[G::MB][G::N
           if (lane % MS == 0) half[wn * G::BM + r] = s;
         }
       __syncthreads();
-      if (normed[0]) {
+      if (scaled[0]) {
 #pragma unroll
         for (int i = 0; i < MB; ++i)
 #pragma unroll
           for (int e = 0; e < NACC; ++e) {
             const uint32_t r = wm * G::kWaveM + i * MS + (MS == 32 ? 8 * (e / 4) + 4 * (lane / 32) + e % 4 : 4 * (lane / 16) + e);
-            const float sc = rms_scale(half[r] + half[G::BM + r], inv_d, eps);
-#pragma unroll
-            for (int j = 0; j < NB; ++j) acc[i][j][e] = (acc[i][j][e] * g[j]) * sc;
+            sc[i][0][e] = rms_scale(half[r] + half[G::BM + r], inv_d, eps);
           }
       }
       __syncthreads();                           // the output staging reuses the LDS
@@ -392,8 +393,11 @@ __device__ __forceinline__ void proj_epilogue(typename G::Acc (&acc)[G::MB][G::N
     for (int j = 0; j < NB; ++j)
 #pragma unroll
       for (int e = 0; e < NACC; ++e) {
+        const int h = JH <= NB ? j / JH : 0;
+        float v = acc[i][j][e];
+        if (scaled[h]) v = (v * g[j]) * sc[i][h][e];
         const uint32_t r = wm * G::kWaveM + i * MS + (MS == 32 ? 8 * (e / 4) + 4 * (lane / 32) + e % 4 : 4 * (lane / 16) + e);
-        O[r * G::kORow + wn * G::kWaveN + j * MS + lane % MS] = (Elem)acc[i][j][e];
+        O[r * G::kORow + wn * G::kWaveN + j * MS + lane % MS] = (Elem)v;
       }
   __syncthreads();
   // one descriptor over the tile's rows (wave-uniform); rows past T and
@@ -479,7 +483,6 @@ __device__ __forceinline__ void proj_tile(const ProjKArgs& args, uint32_t id, ui
   stage_barrier();
   dma_tile<G>(ra, rb, doff, step_bytes<G>(1, ksteps), stage1, wave);
   typedef typename ProjElem<DT>::V8 Frag;
-  typedef typename ProjElem<DT>::T Elem;
   Frag fa[2][MB], fb[2][NB];
   read_frags<G, DT>(stage0, arow, brow, fk, fa[0], fb[0]);
 
