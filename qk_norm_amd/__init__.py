@@ -120,7 +120,7 @@ def _calls():
             if _CODES is None:
                 _torch_tables()
             dts = (torch.float32, torch.bfloat16, torch.float16, torch.float8_e4m3fn)
-            mod.setup(dts, tuple(_CODES[d][1] for d in dts), _raw_stream)
+            mod.setup(dts, tuple(_CODES[d][1] for d in dts), _raw_stream, torch.Tensor)
         _calls_mod = mod
     return _calls_mod
 

@@ -1,12 +1,16 @@
 /* Python entry points of the QK-Norm C ABI with no argument-conversion layer.
  *
- * The Python binding (qk_norm_amd/__init__.py) gathers device pointers,
- * sizes and the stream from torch tensors; this module only converts those
- * Python ints and floats to C values and calls the library's extern "C"
- * functions (libqknorm.so) with them, returning the library's int status.
- * It replaces ctypes on the call path because ctypes' per-call conversion of
- * eleven or more arguments costs about a microsecond, which is a third of a
- * decode-sized launch.  Pointers are Python ints (0 or None for NULL).
+ * Two kinds of call, both argument marshalling only (every step of the work
+ * runs in libqknorm.so):
+ * - per_head, layerwise, partial_sumsq, apply_scalar, qkv_proj_per_head take
+ *   the C ABI's arguments as Python ints and floats (pointers as ints, 0 or
+ *   None for NULL), convert them to C values and call the library's
+ *   extern "C" function, returning its int status.  They replace ctypes,
+ *   whose per-call conversion of eleven or more arguments costs about a
+ *   microsecond, a third of a decode-sized launch.
+ * - per_head_t and layerwise_t take the binding's own arguments (torch
+ *   tensors) and read from them, in C, what the binding's Python path would:
+ *   the common case only, and None for anything else (see below).
  */
 #define PY_SSIZE_T_CLEAN
 #include <Python.h>
@@ -139,34 +143,32 @@ static PyObject* f_qkv_proj_per_head(PyObject* self, PyObject* const* a, Py_ssiz
 
 /* ------------------------------------------------------------------------
  * The common case of the binding's marshalling, on torch tensors: qkv a
- * contiguous [T, ...] GPU tensor (T > 0) of a dtype the library takes, gamma
+ * contiguous [T, ...] GPU torch.Tensor (T > 0; not a subclass) of a dtype the
+ * library takes, gamma
  * None or contiguous on the same GPU in the dtype that goes with qkv's.  The
  * same reads of the tensors the Python binding makes (is_cuda, dtype,
  * contiguity, device, data pointer), made from C.  Anything else returns
  * None, and the binding's Python path handles it (views with a row pitch,
  * and every error, with its message).  `setup` hands over the four torch
- * dtypes with their codes and gamma dtypes, and torch's current-raw-stream
- * function. */
+ * dtypes with their codes and gamma dtypes, torch's current-raw-stream
+ * function and the torch.Tensor type. */
 
 static PyObject* g_dtypes[4];       /* torch dtype objects, indexed by code */
 static PyObject* g_gdtypes[4];      /* gamma dtype for each */
-static PyObject* g_raw_stream;      /* torch._C._cuda_getCurrentRawStream */
+static PyObject* g_tensor;          /* torch.Tensor: only that exact type takes the C path */
+static PyObject* g_raw_stream;      /* torch._C._cuda_getCurrentRawStream; set last, so that
+                                       its presence means the rest is ready */
 static PyObject *s_is_cuda, *s_dtype, *s_is_contiguous, *s_dim, *s_size, *s_numel, *s_get_device,
     *s_data_ptr;
 
 static PyObject* f_setup(PyObject* self, PyObject* const* a, Py_ssize_t n) {
   (void)self;
-  if (!nargs_ok(n, 3, "setup")) return NULL;
+  if (!nargs_ok(n, 4, "setup")) return NULL;
   if (!PyTuple_Check(a[0]) || PyTuple_GET_SIZE(a[0]) != 4 || !PyTuple_Check(a[1]) ||
-      PyTuple_GET_SIZE(a[1]) != 4) {
-    PyErr_SetString(PyExc_TypeError, "setup(dtypes[4], gamma_dtypes[4], raw_stream)");
+      PyTuple_GET_SIZE(a[1]) != 4 || !PyType_Check(a[3])) {
+    PyErr_SetString(PyExc_TypeError, "setup(dtypes[4], gamma_dtypes[4], raw_stream, tensor_type)");
     return NULL;
   }
-  for (int i = 0; i < 4; ++i) {
-    Py_XSETREF(g_dtypes[i], Py_NewRef(PyTuple_GET_ITEM(a[0], i)));
-    Py_XSETREF(g_gdtypes[i], Py_NewRef(PyTuple_GET_ITEM(a[1], i)));
-  }
-  Py_XSETREF(g_raw_stream, Py_NewRef(a[2]));
 #define INTERN(v, txt) \
   if (!v && !(v = PyUnicode_InternFromString(txt))) return NULL;
   INTERN(s_is_cuda, "is_cuda")
@@ -178,8 +180,16 @@ static PyObject* f_setup(PyObject* self, PyObject* const* a, Py_ssize_t n) {
   INTERN(s_get_device, "get_device")
   INTERN(s_data_ptr, "data_ptr")
 #undef INTERN
+  for (int i = 0; i < 4; ++i) {
+    Py_XSETREF(g_dtypes[i], Py_NewRef(PyTuple_GET_ITEM(a[0], i)));
+    Py_XSETREF(g_gdtypes[i], Py_NewRef(PyTuple_GET_ITEM(a[1], i)));
+  }
+  Py_XSETREF(g_tensor, Py_NewRef(a[3]));
+  Py_XSETREF(g_raw_stream, Py_NewRef(a[2]));
   Py_RETURN_NONE;
 }
+
+static int is_tensor(PyObject* o) { return (PyObject*)Py_TYPE(o) == g_tensor; }
 
 /* 1 true, 0 false, -1 error (a Python exception is set) */
 static int attr_true(PyObject* o, PyObject* name) {
@@ -221,6 +231,7 @@ static int dtype_code(PyObject* o) {
 
 /* qkv: 1 and (T, ld, dev, ptr, code) for the common case, 0 otherwise, -1 on error */
 static int qkv_rows(PyObject* t, int64_t* T, int64_t* ld, int64_t* dev, void** ptr, int* code) {
+  if (!is_tensor(t)) return 0;
   int r = attr_true(t, s_is_cuda);
   if (r <= 0) return r;
   if ((*code = dtype_code(t)) < 0) return -1;
@@ -249,6 +260,7 @@ static int gamma_ptr(PyObject* g, int code, int64_t dev, void** ptr) {
     *ptr = NULL;
     return 1;
   }
+  if (!is_tensor(g)) return 0;
   PyObject* d = PyObject_GetAttr(g, s_dtype);
   if (!d) return -1;
   const int same = d == g_gdtypes[code];

@@ -281,3 +281,25 @@ def test_python_call_module_forwards_to_the_same_library(lib):
     assert q._calls() is f
     maps = {line.split()[-1] for line in open("/proc/self/maps") if "libqknorm.so" in line}
     assert maps == {os.path.realpath(q.LIB_PATH)}, maps
+
+
+def test_tensor_calls_leave_other_inputs_to_the_python_path(lib):
+    # per_head_t / layerwise_t take the common case only (a plain
+    # torch.Tensor on the GPU); for anything else they return None without
+    # touching the library, and the binding's Python path raises its own error
+    import numpy as np
+    import torch
+    c = q._calls()
+    x = torch.zeros(4, 256, dtype=torch.bfloat16)
+    g = torch.ones(128, dtype=torch.bfloat16)
+
+    class Sub(torch.Tensor):
+        pass
+
+    for obj in (x, np.zeros((4, 256), np.float32), x.as_subclass(Sub), [[0.0] * 256] * 4, None):
+        assert c.per_head_t(obj, 2, 0, 128, g, None, 1e-6, None) is None
+        assert c.layerwise_t(obj, 128, 128, g, g, 1e-6, 1, None) is None
+    with pytest.raises(ValueError, match="GPU tensor"):
+        q.qknorm_per_head(x, 2, 0, 128, g)
+    with pytest.raises(TypeError):
+        c.per_head_t(x, 2, 0)
