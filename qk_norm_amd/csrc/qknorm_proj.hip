@@ -18,7 +18,11 @@
 // each XCD holds at once share operand panels in its L2.  Because tile widths
 // are multiples of head_dim (or one head spans a tile's two column waves)
 // and tiles start at multiples of it, a tile holds whole heads, and the
-// epilogue normalises them in registers without leaving the block.
+// epilogue normalises them in registers without leaving the block.  The
+// MFMAs take the weight's fragment as their first operand, so a lane's
+// accumulators are four consecutive columns of one token: one lane swap
+// then gives each lane eight consecutive outputs, stored as one 16-byte
+// write straight from registers.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -34,18 +38,14 @@ namespace {
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-// The 16-bit element type: its 8-element fragment and the MFMAs that take it
-// (fp32 accumulation either way): 32 x 32 x 16 (16 accumulators per lane) and
-// 16 x 16 x 32 (4 per lane).
+// The 16-bit element type: its 8-element fragment and the 16 x 16 x 32 MFMA
+// that takes it (fp32 accumulation, 4 accumulators per lane).
 template <int DT>
 struct ProjElem;
 template <>
 struct ProjElem<kBF16> {
   typedef __bf16 T;
   typedef __bf16 V8 __attribute__((ext_vector_type(8)));
-  static __device__ __forceinline__ f32x16 mfma(V8 a, V8 b, f32x16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-  }
   static __device__ __forceinline__ f32x4 mfma(V8 a, V8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
   }
@@ -54,30 +54,24 @@ template <>
 struct ProjElem<kF16> {
   typedef _Float16 T;
   typedef _Float16 V8 __attribute__((ext_vector_type(8)));
-  static __device__ __forceinline__ f32x16 mfma(V8 a, V8 b, f32x16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
-  }
   static __device__ __forceinline__ f32x4 mfma(V8 a, V8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
   }
 };
 
-// MFMA block shape.  MS x MS output blocks, KS of K per instruction; lane l
-// holds A row (l % MS) and B column (l % MS) with 8 consecutive k starting
-// at 8 * (l / MS), and accumulator value e of the block at column l % MS and
-// row 8 * (e / 4) + 4 * (l / 32) + e % 4 (MS = 32) or 4 * (l / 16) + e (MS = 16).
-template <int MS>
-struct MfmaShape;
-template <>
-struct MfmaShape<32> {
-  [[maybe_unused]] static constexpr int KS = 16, NACC = 16;
-  typedef f32x16 Acc;
-};
-template <>
-struct MfmaShape<16> {
-  static constexpr int KS = 32, NACC = 4;
-  typedef f32x4 Acc;
-};
+// Two fp32 values rounded once (to nearest even) to the element type and
+// packed into one dword, the first in the low half (the lower address).
+template <int DT>
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+  typedef typename ProjElem<DT>::T Elem;
+  const Elem ea = (Elem)a, eb = (Elem)b;
+  return (uint32_t)__builtin_bit_cast(uint16_t, ea) | ((uint32_t)__builtin_bit_cast(uint16_t, eb) << 16);
+}
+
+// MFMA block: 16 x 16 outputs, 32 of K per instruction.  Lane l supplies row
+// l % 16 of each operand's fragment (8 consecutive k from 8 * (l / 16)), and
+// holds accumulator e of the block at row 4 * (l / 16) + e of the first
+// operand and row l % 16 of the second.
 
 // Tile geometry.  A block of WM x WN waves owns a BM x BN output tile; each
 // wave a (BM/WM) x (BN/WN) slab of MS x MS MFMA blocks; K advances BK at a
@@ -90,20 +84,19 @@ struct MfmaShape<16> {
 // instruction covering rows R .. R+1024/(BK*2)-1 fetches row R + i / CPR and
 // the chunk whose slot is i % CPR: no staging registers and no LDS write
 // instructions.
-template <int BM_, int BN_, int WM_, int WN_, int BK_, int S_, int MS_ = 32>
+template <int BM_, int BN_, int WM_, int WN_, int BK_, int S_>
 struct Tile {
-  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, BK = BK_, S = S_, MS = MS_;
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, BK = BK_, S = S_, MS = 16;
   static constexpr int kThreads = 64 * WM * WN, kWaves = WM * WN;
   static constexpr int kWaveM = BM / WM, kWaveN = BN / WN;
   static constexpr int MB = kWaveM / MS, NB = kWaveN / MS;
-  static constexpr int KS = MfmaShape<MS>::KS, KK = BK / KS;   // K per MFMA, MFMA steps per K step
-  typedef typename MfmaShape<MS>::Acc Acc;
+  static constexpr int KS = 32, KK = BK / KS;                 // K per MFMA, MFMA steps per K step
+  typedef f32x4 Acc;
   static constexpr int kRowBytes = BK * 2;
   static constexpr int CPR = kRowBytes / 16, RPB = 256 / kRowBytes;
   static constexpr int kInstRows = 1024 / kRowBytes;         // rows one load instruction fills
   static constexpr int kStageBytes = (BM + BN) * kRowBytes;
-  static constexpr int kORow = BN + 8;
-  static constexpr int kLdsBytes = S * kStageBytes > BM * kORow * 2 ? S * kStageBytes : BM * kORow * 2;
+  static constexpr int kStagesBytes = S * kStageBytes;
   static constexpr int kAInst = BM / kInstRows / kWaves, kBInst = BN / kInstRows / kWaves;
   static constexpr int kLoads = kAInst + kBInst;              // per wave per K step
   static_assert(BM % (kInstRows * kWaves) == 0 && BN % (kInstRows * kWaves) == 0, "");
@@ -223,6 +216,9 @@ __device__ __forceinline__ void read_frags(const uint8_t* st, uint32_t arow, uin
   for (int j = 0; j < G::NB; ++j) b[j] = sfrag<G, DT>(st, brow + j * G::MS, k);
 }
 
+// One MFMA per block, the weight's fragment first: block (i, j) accumulates
+// rows j*16.. of w against rows i*16.. of x, so its lanes hold output
+// columns 4*(l/16) + e of token l%16 (the layout the epilogue stores from).
 template <class G, int DT>
 __device__ __forceinline__ void mfma_step(typename G::Acc (&acc)[G::MB][G::NB],
                                           const typename ProjElem<DT>::V8 (&a)[G::MB],
@@ -230,7 +226,7 @@ __device__ __forceinline__ void mfma_step(typename G::Acc (&acc)[G::MB][G::NB],
 #pragma unroll
   for (int i = 0; i < G::MB; ++i)
 #pragma unroll
-    for (int j = 0; j < G::NB; ++j) acc[i][j] = ProjElem<DT>::mfma(a[i], b[j], acc[i][j]);
+    for (int j = 0; j < G::NB; ++j) acc[i][j] = ProjElem<DT>::mfma(b[j], a[i], acc[i][j]);
 }
 
 // Instruction order for the scheduler (sched_group_barrier masks: 0x008
@@ -274,143 +270,138 @@ __device__ __forceinline__ void tile_origin(uint32_t T, uint32_t N, uint32_t id,
   *m0 = (first_m + within % gm) * G::BM;
 }
 
-// The gamma value and whether it is normalised, for each of a lane's columns
-// (j * MS + lane % MS of the wave's slab, for each block j).  Loaded before
-// the main loop, so the loads' latency hides behind it.
-template <class G>
-struct EpiGamma {
-  float g[G::NB];
-  bool normed[G::NB];
-};
+// LDS beyond the operand stages: gamma_q and gamma_k as fp32 (head_dim
+// values each, at most 256), then the half-head row sums of head_dim 256
+// ([2 column waves][256 rows]).
+constexpr int kGammaFloats = 2 * 256;
+constexpr int kHalfFloats = 2 * 256;
 
-// The loads are unconditional (a load behind a branch makes the compiler wait
-// for it at once): columns that take no gamma read a valid stand-in, `spare`
-// (the weight, at least head_dim elements long), and select 1 afterwards.
-template <class G, int DT, int D>
-__device__ __forceinline__ EpiGamma<G> epi_gamma(uint32_t lane, uint32_t wn, uint32_t n0, uint32_t N,
-                                                 uint32_t hq, uint32_t hkv,
-                                                 const uint8_t* __restrict__ gamma_q,
-                                                 const uint8_t* __restrict__ gamma_k,
-                                                 const uint8_t* __restrict__ spare, uint32_t norm) {
+// gamma_q and gamma_k into the block's table, once per block (threads below
+// head_dim; a missing gamma reads as 1, and is only used where normalised).
+template <int DT, int D>
+__device__ __forceinline__ void stage_gamma(float* gtab, const uint8_t* __restrict__ gamma_q,
+                                            const uint8_t* __restrict__ gamma_k, uint32_t tid) {
   typedef typename ProjElem<DT>::T Elem;
-  EpiGamma<G> eg;
-#pragma unroll
-  for (int j = 0; j < G::NB; ++j) {
-    const uint32_t n = n0 + wn * G::kWaveN + j * G::MS + lane % G::MS;
-    const uint32_t head = n / D;
-    const bool is_q = head < hq;
-    eg.normed[j] = norm && (is_q || head < hq + hkv) && n < N;
-    const uint8_t* src = eg.normed[j] ? (is_q ? gamma_q : gamma_k) : spare;
-    const float v = (float)reinterpret_cast<const Elem*>(src)[n % D];
-    eg.g[j] = eg.normed[j] ? v : 1.f;
+  if (tid < (uint32_t)D) {
+    gtab[tid] = gamma_q ? (float)reinterpret_cast<const Elem*>(gamma_q)[tid] : 1.f;
+    gtab[D + tid] = gamma_k ? (float)reinterpret_cast<const Elem*>(gamma_k)[tid] : 1.f;
   }
-  return eg;
+}
+
+// Sum over the four lanes that hold one token (l, l ^ 16, l ^ 32, l ^ 48):
+// every lane gets the same value (each step adds a pair in either order).
+__device__ __forceinline__ float token_sum(float v) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  auto r2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r2[0]) + __uint_as_float(r2[1]);
 }
 
 // Epilogue: per-head QK-Norm on the fp32 accumulators (unless `norm` is 0),
-// then the tile leaves through LDS as 16-byte row stores.  Every load into
-// LDS must have completed and every wave must have passed a barrier after
-// its last fragment read (the output staging reuses the stages).
+// then 16-byte stores straight from registers.  Block (i, j) of a wave holds
+// token i*16 + l%16 of the wave's rows and columns j*16 + 4*(l/16) + e,
+// e = 0..3 (the weight's fragment is the MFMA's first operand).  A head of
+// D columns is D/16 consecutive blocks j (a wave's columns are whole heads,
+// or half of one for head_dim 256): a token's sum of squares is each lane's
+// fma chain over its 4 values of each block, then the sum over the 4 lanes
+// that hold the token.  For the stores, blocks 2p and 2p+1 are paired: one
+// v_permlane16_swap per dword moves the even rows' block-2p+1 values and the
+// odd rows' block-2p values across, which leaves each lane 8 consecutive
+// columns of its token.
 template <class G, int DT, int D>
-__device__ __forceinline__ void proj_epilogue(const typename G::Acc (&acc)[G::MB][G::NB], uint8_t* smem, uint32_t tid,
-                                              uint32_t lane, uint32_t wm, uint32_t wn, uint32_t m0,
-                                              uint32_t n0, uint32_t a_rows, uint32_t N,
-                                              const EpiGamma<G>& eg, float eps, float inv_d,
+__device__ __forceinline__ void proj_epilogue(const f32x4 (&acc)[G::MB][G::NB], const float* gtab,
+                                              float* half, uint32_t lane, uint32_t wm, uint32_t wn,
+                                              uint32_t m0, uint32_t n0, uint32_t a_rows, uint32_t N,
+                                              uint32_t hq, uint32_t hkv, float eps, float inv_d,
                                               uint32_t norm, uint8_t* __restrict__ out,
                                               uint64_t ld_bytes) {
-  constexpr int MB = G::MB, NB = G::NB, MS = G::MS, NACC = MfmaShape<MS>::NACC;
-  typedef typename ProjElem<DT>::T Elem;
-  // Value e of block (i, j) in lane l is row i*MS + (its row in the block)
-  // of the wave's slab and column j*MS + l%MS.  A head of D columns is D/MS
-  // consecutive blocks j (a wave's columns are whole heads): its row sum of
-  // squares is the lane's fma chain over those blocks, then the sum over the
-  // MS lanes that hold the row.
-  constexpr int JH = D / MS;                    // blocks per head
+  constexpr int MB = G::MB, NB = G::NB;
+  constexpr int JH = D / 16;                     // blocks per head
   constexpr int NH = JH <= NB ? NB / JH : 1;     // heads in a wave's columns (or one half-head)
-  // the RMS scale of row (i, e) of head h; the scaled values (acc * g) * sc
-  // are formed once, as they go to LDS, so the accumulators are only read
-  float sc[MB][NH][NACC];
-  bool scaled[NH];
-  const float* g = eg.g;
-  const bool* normed = eg.normed;
-  if constexpr (JH <= NB) {
-    static_assert(NB % JH == 0, "a wave's columns must be whole heads");
+  static_assert(NB % 2 == 0, "blocks are stored in pairs");
+  const uint32_t q4 = lane / 16, tl = lane % 16;
+  const uint32_t c_wave = n0 + wn * G::kWaveN;   // the wave's first column
+  // each block's columns lie in one head, so whether it is normalised (and
+  // its gamma table) is the same for the whole block
+  bool normed[NB];
+  float g[NB][4];
 #pragma unroll
-    for (int h = 0; h < NH; ++h) {
-      // the same for every lane and every block of one head (heads lie in
-      // one region and the tile's columns past N are whole heads)
-      scaled[h] = norm && normed[h * JH];
-      if (!scaled[h]) continue;
+  for (int j = 0; j < NB; ++j) {
+    const uint32_t nb = c_wave + j * 16;
+    const uint32_t head = nb / D;
+    normed[j] = norm && head < hq + hkv && nb < N;
+    const float4 gv = *reinterpret_cast<const float4*>(gtab + (head < hq ? 0 : D) + nb % D + 4 * q4);
+    g[j][0] = gv.x;
+    g[j][1] = gv.y;
+    g[j][2] = gv.z;
+    g[j][3] = gv.w;
+  }
+  float sc[MB][NH];
+  if (norm) {
+    if constexpr (JH <= NB) {
+      static_assert(NB % JH == 0, "a wave's columns must be whole heads");
 #pragma unroll
-      for (int i = 0; i < MB; ++i)
+      for (int h = 0; h < NH; ++h) {
+        if (!normed[h * JH]) continue;           // the same for the whole head
 #pragma unroll
-        for (int e = 0; e < NACC; ++e) {
+        for (int i = 0; i < MB; ++i) {
           float s = 0.f;
 #pragma unroll
           for (int jj = 0; jj < JH; ++jj)
-            s = __builtin_fmaf(acc[i][h * JH + jj][e], acc[i][h * JH + jj][e], s);
-          sc[i][h][e] = rms_scale(group_sum<MS>(s), inv_d, eps);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) s = __builtin_fmaf(acc[i][h * JH + jj][e], acc[i][h * JH + jj][e], s);
+          sc[i][h] = rms_scale(token_sum(s), inv_d, eps);
         }
-    }
-  } else {
-    // a head spans the tile's two column waves (D = 2 * kWaveN): each wave
-    // leaves its half-head row sums in LDS (the stages are free), and both
-    // add the two halves in the same order, so they scale with the same bits
-    static_assert(JH == 2 * NB && G::WN == 2 && G::BN == D, "one head across the two column waves");
-    scaled[0] = norm && normed[0];
-    if (norm) {
-      float* half = reinterpret_cast<float*>(smem);   // [WN][BM]
-#pragma unroll
-      for (int i = 0; i < MB; ++i)
-#pragma unroll
-        for (int e = 0; e < NACC; ++e) {
-          float s = 0.f;
-#pragma unroll
-          for (int j = 0; j < NB; ++j) s = __builtin_fmaf(acc[i][j][e], acc[i][j][e], s);
-          s = group_sum<MS>(s);
-          const uint32_t r = wm * G::kWaveM + i * MS + (MS == 32 ? 8 * (e / 4) + 4 * (lane / 32) + e % 4 : 4 * (lane / 16) + e);
-          if (lane % MS == 0) half[wn * G::BM + r] = s;
-        }
-      __syncthreads();
-      if (scaled[0]) {
-#pragma unroll
-        for (int i = 0; i < MB; ++i)
-#pragma unroll
-          for (int e = 0; e < NACC; ++e) {
-            const uint32_t r = wm * G::kWaveM + i * MS + (MS == 32 ? 8 * (e / 4) + 4 * (lane / 32) + e % 4 : 4 * (lane / 16) + e);
-            sc[i][0][e] = rms_scale(half[r] + half[G::BM + r], inv_d, eps);
-          }
       }
-      __syncthreads();                           // the output staging reuses the LDS
+    } else {
+      // a head spans the tile's two column waves (D = 2 * kWaveN): each wave
+      // leaves its half-head sums in LDS, and both add the two halves in the
+      // same order, so they scale with the same bits
+      static_assert(JH == 2 * NB && G::WN == 2 && G::BN == D, "one head across the two column waves");
+#pragma unroll
+      for (int i = 0; i < MB; ++i) {
+        float s = 0.f;
+#pragma unroll
+        for (int j = 0; j < NB; ++j)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) s = __builtin_fmaf(acc[i][j][e], acc[i][j][e], s);
+        s = token_sum(s);
+        if (q4 == 0) half[wn * G::BM + wm * G::kWaveM + i * 16 + tl] = s;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < MB; ++i) {
+        const uint32_t r = wm * G::kWaveM + i * 16 + tl;
+        sc[i][0] = rms_scale(half[r] + half[G::BM + r], inv_d, eps);
+      }
     }
   }
-  // the bf16 tile goes through LDS (the stages are free after the loop's last
-  // barrier) so rows leave as 16-byte stores
-  Elem* O = reinterpret_cast<Elem*>(smem);
-#pragma unroll
-  for (int i = 0; i < MB; ++i)
-#pragma unroll
-    for (int j = 0; j < NB; ++j)
-#pragma unroll
-      for (int e = 0; e < NACC; ++e) {
-        const int h = JH <= NB ? j / JH : 0;
-        float v = acc[i][j][e];
-        if (scaled[h]) v = (v * g[j]) * sc[i][h][e];
-        const uint32_t r = wm * G::kWaveM + i * MS + (MS == 32 ? 8 * (e / 4) + 4 * (lane / 32) + e % 4 : 4 * (lane / 16) + e);
-        O[r * G::kORow + wn * G::kWaveN + j * MS + lane % MS] = (Elem)v;
-      }
-  __syncthreads();
   // one descriptor over the tile's rows (wave-uniform); rows past T and
   // columns past N get an offset outside it
   const uint32_t valid_cols = N - n0 < (uint32_t)G::BN ? N - n0 : (uint32_t)G::BN;
   const Rsrc ro = make_rsrc(out + (uint64_t)m0 * ld_bytes + (uint64_t)n0 * 2,
                             (uint64_t)(a_rows - 1) * ld_bytes + valid_cols * 2);
-  constexpr uint32_t kCols = G::BN / 8;
-  constexpr uint32_t kRowsPerPass = G::kThreads / kCols;
-  for (uint32_t r0 = 0; r0 < (uint32_t)G::BM; r0 += kRowsPerPass) {
-    const uint32_t r = r0 + tid / kCols, c = (tid % kCols) * 8;
-    const u32x4 v = *reinterpret_cast<const u32x4*>(O + r * G::kORow + c);
-    stream_store(ro, r < a_rows && c < valid_cols ? r * (uint32_t)ld_bytes + c * 2 : 0xFFFFFFF0u, v);
+  auto value = [&](int i, int j, int e) {
+    const float v = acc[i][j][e];
+    return normed[j] ? (v * g[j][e]) * sc[i][JH <= NB ? j / JH : 0] : v;
+  };
+#pragma unroll
+  for (int i = 0; i < MB; ++i) {
+    const uint32_t r = wm * G::kWaveM + i * 16 + tl;
+#pragma unroll
+    for (int p = 0; p < NB / 2; ++p) {
+      const uint32_t a01 = pack2<DT>(value(i, 2 * p, 0), value(i, 2 * p, 1));
+      const uint32_t a23 = pack2<DT>(value(i, 2 * p, 2), value(i, 2 * p, 3));
+      const uint32_t b01 = pack2<DT>(value(i, 2 * p + 1, 0), value(i, 2 * p + 1, 1));
+      const uint32_t b23 = pack2<DT>(value(i, 2 * p + 1, 2), value(i, 2 * p + 1, 3));
+      auto s01 = __builtin_amdgcn_permlane16_swap(a01, b01, false, false);
+      auto s23 = __builtin_amdgcn_permlane16_swap(a23, b23, false, false);
+      // even rows (q4 0, 2): block 2p, columns 4*q4 .. +7; odd rows: block 2p+1,
+      // columns 4*(q4-1) .. +7
+      const uint32_t c = wn * G::kWaveN + 32 * p + (q4 & 1) * 16 + (q4 >> 1) * 8;
+      const u32x4 v = {s01[0], s23[0], s01[1], s23[1]};
+      stream_store(ro, r < a_rows && c < valid_cols ? r * (uint32_t)ld_bytes + c * 2 : 0xFFFFFFF0u, v);
+    }
   }
 }
 
@@ -430,7 +421,8 @@ struct ProjKArgs {
 // the column range [n_begin, n_end) this tile shape covers.
 template <class G, int DT, int D>
 __device__ __forceinline__ void proj_tile(const ProjKArgs& args, uint32_t id, uint32_t count,
-                                          uint32_t n_begin, uint32_t n_end, uint8_t* smem) {
+                                          uint32_t n_begin, uint32_t n_end, uint8_t* smem,
+                                          const float* gtab, float* half) {
   constexpr int MB = G::MB, NB = G::NB, BK = G::BK;
   const uint8_t* __restrict__ x = args.x;
   const uint8_t* __restrict__ w = args.w;
@@ -447,8 +439,6 @@ __device__ __forceinline__ void proj_tile(const ProjKArgs& args, uint32_t id, ui
   const uint32_t b_rows = n_end - n0 < (uint32_t)G::BN ? n_end - n0 : (uint32_t)G::BN;
   const Rsrc ra = make_rsrc(x + (uint64_t)m0 * ldx_bytes, (uint64_t)(a_rows - 1) * ldx_bytes + K * 2);
   const Rsrc rb = make_rsrc(w + (uint64_t)n0 * ldw_bytes, (uint64_t)(b_rows - 1) * ldw_bytes + K * 2);
-  const EpiGamma<G> eg = epi_gamma<G, DT, D>(lane, wn, n0, n_end, args.hq, args.hkv, args.gamma_q,
-                                             args.gamma_k, w, args.norm);
 
   typename G::Acc acc[MB][NB];
 #pragma unroll
@@ -456,7 +446,7 @@ __device__ __forceinline__ void proj_tile(const ProjKArgs& args, uint32_t id, ui
 #pragma unroll
     for (int j = 0; j < NB; ++j)
 #pragma unroll
-      for (int e = 0; e < MfmaShape<G::MS>::NACC; ++e) acc[i][j][e] = 0.f;
+      for (int e = 0; e < 4; ++e) acc[i][j][e] = 0.f;
 
   // Two LDS stages; K step ks computes from stage ks % 2.  Fragments are
   // double-buffered in registers: the reads of sub-step kk+1 are issued
@@ -519,11 +509,12 @@ __device__ __forceinline__ void proj_tile(const ProjKArgs& args, uint32_t id, ui
     // loop, which then waits for its result before the first MFMA
     asm volatile("" ::: "memory");
   }
-  // the output tile reuses the stages: every load into LDS must be done
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  proj_epilogue<G, DT, D>(acc, smem, tid, lane, wm, wn, m0, n0, a_rows, n_end, eg, args.eps, args.inv_d,
-                          args.norm, args.out, args.ld_bytes);
+  // the last step's spare loads into LDS must land before the block ends
+  // (its LDS may then go to another block); waiting here, before the
+  // stores, leaves the stores out of the wait
+  wait_vmcnt<0>();
+  proj_epilogue<G, DT, D>(acc, gtab, half, lane, wm, wn, m0, n0, a_rows, n_end, args.hq, args.hkv,
+                          args.eps, args.inv_d, args.norm, args.out, args.ld_bytes);
 }
 
 // Blocks 0 .. n_full-1 take full tiles (GF) of columns [0, n_split); the rest
@@ -535,12 +526,17 @@ __global__ __launch_bounds__(GF::kThreads) void qkv_proj_kernel(ProjKArgs args, 
                                                                 uint32_t n_split) {
   static_assert(GF::kThreads == GH::kThreads, "one block size");
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  constexpr int kStages = GF::kStagesBytes > GH::kStagesBytes ? GF::kStagesBytes : GH::kStagesBytes;
+  float* gtab = reinterpret_cast<float*>(smem + kStages);
+  float* half = gtab + kGammaFloats;
+  // made visible by the first barrier of the tile's main loop
+  stage_gamma<DT, D>(gtab, args.gamma_q, args.gamma_k, threadIdx.x);
   if (blockIdx.x < n_full) {
-    proj_tile<GF, DT, D>(args, blockIdx.x, n_full, 0, n_split, smem);
+    proj_tile<GF, DT, D>(args, blockIdx.x, n_full, 0, n_split, smem, gtab, half);
   } else if constexpr (D <= GH::BN) {
     // a half-width tile holds whole heads, or one head across its two column
     // waves (head_dim 128); head_dim 256 never takes this path
-    proj_tile<GH, DT, D>(args, blockIdx.x - n_full, gridDim.x - n_full, n_split, args.N, smem);
+    proj_tile<GH, DT, D>(args, blockIdx.x - n_full, gridDim.x - n_full, n_split, args.N, smem, gtab, half);
   }
 }
 
@@ -558,26 +554,25 @@ __global__ __launch_bounds__(GF::kThreads) void qkv_proj_kernel(ProjKArgs args, 
 // step.  Operands staged through registers instead of loaded straight into
 // LDS measured 11-17 % slower.  Reading fragments two sub-steps ahead,
 // leaving the loads to one wave per SIMD, splitting a step's loads over two
-// sub-steps, an epilogue that stores from registers, a persistent grid that
-// loads the next tile during the epilogue, or a ping-pong schedule of two
-// wave groups changed the time by 3 % or less, or made it slower.
+// sub-steps, a persistent grid that loads the next tile during the
+// epilogue, or a ping-pong schedule of two wave groups changed the time by
+// 3 % or less, or made it slower.  Storing straight from registers (the
+// swapped MFMA operands above) instead of through LDS saves about 3 %: the
+// LDS round trip of the output tile cost about 6 us of 290 at T = 8192.
 #ifndef QKNORM_PROJ_BK
 #define QKNORM_PROJ_BK 64
-#endif
-#ifndef QKNORM_PROJ_MS
-#define QKNORM_PROJ_MS 16          // MFMA block: 16 (16 x 16 x 32) or 32 (32 x 32 x 16)
 #endif
 #ifndef QKNORM_PROJ_SPLIT
 #define QKNORM_PROJ_SPLIT 1        // 0: full tiles only
 #endif
 // Full tiles: 256 x 256, 8 waves of 64 x 128.  Half-width tiles: 256 x 128,
 // 8 waves of 64 x 64.
-using GeoF = Tile<256, 256, 4, 2, QKNORM_PROJ_BK, 2, QKNORM_PROJ_MS>;
-// (32 x 32 blocks leave a 64 x 64 wave only 4 MFMAs per step: no tail then)
-using GeoH = std::conditional_t<QKNORM_PROJ_MS == 16, Tile<256, 128, 4, 2, QKNORM_PROJ_BK, 2, 16>, GeoF>;
-constexpr bool kSplit = QKNORM_PROJ_SPLIT != 0 && QKNORM_PROJ_MS == 16;
+using GeoF = Tile<256, 256, 4, 2, QKNORM_PROJ_BK, 2>;
+using GeoH = Tile<256, 128, 4, 2, QKNORM_PROJ_BK, 2>;
+constexpr bool kSplit = QKNORM_PROJ_SPLIT != 0;
 constexpr int kBM = GeoF::BM, kBN = GeoF::BN, kThreads = GeoF::kThreads;
-constexpr int kLdsBytes = GeoF::kLdsBytes > GeoH::kLdsBytes ? GeoF::kLdsBytes : GeoH::kLdsBytes;
+constexpr int kLdsBytes = (GeoF::kStagesBytes > GeoH::kStagesBytes ? GeoF::kStagesBytes : GeoH::kStagesBytes) +
+                          (kGammaFloats + kHalfFloats) * 4;
 
 }  // namespace
 
