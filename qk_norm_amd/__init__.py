@@ -105,7 +105,7 @@ class _CtypesCalls:
 
 
 def _calls():
-    """The functions that call the C ABI: `_qknorm_fast` (qk_norm_amd/csrc/pyfast.c),
+    """The functions that call the C ABI: `_qknorm_fast` (qk_norm_amd/csrc/pyfast.cpp),
     which converts the Python ints and floats itself and, for the common case of
     contiguous GPU tensors, reads the tensors itself too; or ctypes."""
     global _calls_mod
@@ -119,8 +119,7 @@ def _calls():
             import torch
             if _CODES is None:
                 _torch_tables()
-            dts = (torch.float32, torch.bfloat16, torch.float16, torch.float8_e4m3fn)
-            mod.setup(dts, tuple(_CODES[d][1] for d in dts), _raw_stream, torch.Tensor)
+            mod.setup(_raw_stream, torch.Tensor)
         _calls_mod = mod
     return _calls_mod
 

@@ -22,7 +22,7 @@ SOURCES = [os.path.join(CSRC, "qknorm_api.hip"), os.path.join(CSRC, "qknorm_kern
            os.path.join(CSRC, "qknorm_proj.hip")]
 LIB = os.path.join(HERE, "libqknorm.so")
 CEILING_SOURCES = [os.path.join(CSRC, "ceiling_probe.hip")]
-FAST_SOURCE = os.path.join(CSRC, "pyfast.c")
+FAST_SOURCE = os.path.join(CSRC, "pyfast.cpp")
 CEILING_LIB = os.path.join(HERE, "libqknorm_ceiling.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -64,20 +64,28 @@ def fast_module_path() -> str:
 
 
 def build_fast(verbose: bool = False) -> str:
-    """The CPython module that calls the C ABI directly (host C, gcc), linked
-    against libqknorm.so in the same directory."""
+    """The CPython module that calls the C ABI directly (host C++, g++), linked
+    against libqknorm.so in the same directory and against torch's libraries
+    (it reads torch tensors through torch's C++ API)."""
     import sysconfig
+    import torch
+    import torch.utils.cpp_extension as ce
     out = fast_module_path()
     tmp = out + ".tmp"
-    cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-Wall", "-Wextra", "-Wno-unused-parameter",
-           "-I", sysconfig.get_paths()["include"], "-I", os.path.join(ROOT, "include"),
-           "-o", tmp, FAST_SOURCE, "-L", HERE, "-l:libqknorm.so", "-Wl,-rpath,$ORIGIN"]
+    abi = int(torch._C._GLIBCXX_USE_CXX11_ABI)
+    inc = [f for p in ce.include_paths() for f in ("-I", p)]
+    libdir = ce.library_paths()[0]
+    cmd = ["g++", "-O2", "-std=c++17", "-fPIC", "-shared", "-Wall", "-Wextra", "-Wno-unused-parameter",
+           f"-D_GLIBCXX_USE_CXX11_ABI={abi}",
+           "-I", sysconfig.get_paths()["include"], "-I", os.path.join(ROOT, "include"), *inc,
+           "-o", tmp, FAST_SOURCE, "-L", HERE, "-l:libqknorm.so", "-L", libdir, "-ltorch_python", "-ltorch",
+           "-lc10", f"-Wl,-rpath,$ORIGIN:{libdir}"]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
-        raise RuntimeError("gcc failed building the QK-Norm Python call module")
+        raise RuntimeError("g++ failed building the QK-Norm Python call module")
     os.replace(tmp, out)
     return out
 

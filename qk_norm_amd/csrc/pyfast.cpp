@@ -9,12 +9,16 @@
  *   whose per-call conversion of eleven or more arguments costs about a
  *   microsecond, a third of a decode-sized launch.
  * - per_head_t and layerwise_t take the binding's own arguments (torch
- *   tensors) and read from them, in C, what the binding's Python path would:
- *   the common case only, and None for anything else (see below).
+ *   tensors) and read from them what the binding's Python path would, through
+ *   torch's C++ tensor API (no Python-level attribute calls, each of which
+ *   costs about 0.1 us): the common case only, and None for anything else
+ *   (see below).
  */
 #define PY_SSIZE_T_CLEAN
 #include <Python.h>
 #include <stdint.h>
+
+#include <torch/csrc/autograd/python_variable.h>
 
 #include "../../include/qknorm.h"
 
@@ -144,136 +148,71 @@ static PyObject* f_qkv_proj_per_head(PyObject* self, PyObject* const* a, Py_ssiz
 /* ------------------------------------------------------------------------
  * The common case of the binding's marshalling, on torch tensors: qkv a
  * contiguous [T, ...] GPU torch.Tensor (T > 0; not a subclass) of a dtype the
- * library takes, gamma
- * None or contiguous on the same GPU in the dtype that goes with qkv's.  The
- * same reads of the tensors the Python binding makes (is_cuda, dtype,
- * contiguity, device, data pointer), made from C.  Anything else returns
- * None, and the binding's Python path handles it (views with a row pitch,
- * and every error, with its message).  `setup` hands over the four torch
- * dtypes with their codes and gamma dtypes, torch's current-raw-stream
- * function and the torch.Tensor type. */
+ * library takes, gamma None or a contiguous torch.Tensor on the same GPU in
+ * the dtype that goes with qkv's.  The same facts the Python binding reads
+ * (device, dtype, contiguity, rows, data pointer), read from the tensor's
+ * C++ object.  Anything else returns None, and the binding's Python path
+ * handles it (views with a row pitch, and every error, with its message).
+ * `setup` hands over torch's current-raw-stream function and the
+ * torch.Tensor type. */
 
-static PyObject* g_dtypes[4];       /* torch dtype objects, indexed by code */
-static PyObject* g_gdtypes[4];      /* gamma dtype for each */
-static PyObject* g_tensor;          /* torch.Tensor: only that exact type takes the C path */
+static PyObject* g_tensor;          /* torch.Tensor: only that exact type takes the C++ path */
 static PyObject* g_raw_stream;      /* torch._C._cuda_getCurrentRawStream; set last, so that
                                        its presence means the rest is ready */
-static PyObject *s_is_cuda, *s_dtype, *s_is_contiguous, *s_dim, *s_size, *s_numel, *s_get_device,
-    *s_data_ptr;
 
 static PyObject* f_setup(PyObject* self, PyObject* const* a, Py_ssize_t n) {
   (void)self;
-  if (!nargs_ok(n, 4, "setup")) return NULL;
-  if (!PyTuple_Check(a[0]) || PyTuple_GET_SIZE(a[0]) != 4 || !PyTuple_Check(a[1]) ||
-      PyTuple_GET_SIZE(a[1]) != 4 || !PyType_Check(a[3])) {
-    PyErr_SetString(PyExc_TypeError, "setup(dtypes[4], gamma_dtypes[4], raw_stream, tensor_type)");
+  if (!nargs_ok(n, 2, "setup")) return NULL;
+  if (!PyType_Check(a[1])) {
+    PyErr_SetString(PyExc_TypeError, "setup(raw_stream, tensor_type)");
     return NULL;
   }
-#define INTERN(v, txt) \
-  if (!v && !(v = PyUnicode_InternFromString(txt))) return NULL;
-  INTERN(s_is_cuda, "is_cuda")
-  INTERN(s_dtype, "dtype")
-  INTERN(s_is_contiguous, "is_contiguous")
-  INTERN(s_dim, "dim")
-  INTERN(s_size, "size")
-  INTERN(s_numel, "numel")
-  INTERN(s_get_device, "get_device")
-  INTERN(s_data_ptr, "data_ptr")
-#undef INTERN
-  for (int i = 0; i < 4; ++i) {
-    Py_XSETREF(g_dtypes[i], Py_NewRef(PyTuple_GET_ITEM(a[0], i)));
-    Py_XSETREF(g_gdtypes[i], Py_NewRef(PyTuple_GET_ITEM(a[1], i)));
-  }
-  Py_XSETREF(g_tensor, Py_NewRef(a[3]));
-  Py_XSETREF(g_raw_stream, Py_NewRef(a[2]));
+  Py_XSETREF(g_tensor, Py_NewRef(a[1]));
+  Py_XSETREF(g_raw_stream, Py_NewRef(a[0]));
   Py_RETURN_NONE;
 }
 
-static int is_tensor(PyObject* o) { return (PyObject*)Py_TYPE(o) == g_tensor; }
-
-/* 1 true, 0 false, -1 error (a Python exception is set) */
-static int attr_true(PyObject* o, PyObject* name) {
-  PyObject* v = PyObject_GetAttr(o, name);
-  if (!v) return -1;
-  const int r = PyObject_IsTrue(v);
-  Py_DECREF(v);
-  return r;
+/* The tensor inside o when o is exactly a torch.Tensor, else NULL. */
+static const at::Tensor* tensor_of(PyObject* o) {
+  if ((PyObject*)Py_TYPE(o) != g_tensor) return NULL;
+  return &THPVariable_Unpack(o);
 }
 
-static int call_true(PyObject* o, PyObject* name) {
-  PyObject* v = PyObject_CallMethodNoArgs(o, name);
-  if (!v) return -1;
-  const int r = PyObject_IsTrue(v);
-  Py_DECREF(v);
-  return r;
+/* The library's dtype code of a tensor, or -1 for another dtype. */
+static int dtype_code(const at::Tensor& t) {
+  switch (t.scalar_type()) {
+    case c10::ScalarType::Float: return QKNORM_F32;
+    case c10::ScalarType::BFloat16: return QKNORM_BF16;
+    case c10::ScalarType::Half: return QKNORM_F16;
+    case c10::ScalarType::Float8_e4m3fn: return QKNORM_FP8_E4M3;
+    default: return -1;
+  }
 }
 
-static int call_i64(PyObject* o, PyObject* name, PyObject* arg, int64_t* out) {
-  PyObject* v = arg ? PyObject_CallMethodOneArg(o, name, arg) : PyObject_CallMethodNoArgs(o, name);
-  if (!v) return -1;
-  const long long r = PyLong_AsLongLong(v);
-  Py_DECREF(v);
-  if (r == -1 && PyErr_Occurred()) return -1;
-  *out = r;
-  return 0;
-}
-
-/* The dtype code of o (0..3), 4 for another dtype, -1 on error. */
-static int dtype_code(PyObject* o) {
-  PyObject* d = PyObject_GetAttr(o, s_dtype);
-  if (!d) return -1;
-  int code = 4;
-  for (int i = 0; i < 4; ++i)
-    if (d == g_dtypes[i]) code = i;
-  Py_DECREF(d);
-  return code;
-}
-
-/* qkv: 1 and (T, ld, dev, ptr, code) for the common case, 0 otherwise, -1 on error */
-static int qkv_rows(PyObject* t, int64_t* T, int64_t* ld, int64_t* dev, void** ptr, int* code) {
-  if (!is_tensor(t)) return 0;
-  int r = attr_true(t, s_is_cuda);
-  if (r <= 0) return r;
-  if ((*code = dtype_code(t)) < 0) return -1;
-  if (*code > 3) return 0;
-  if ((r = call_true(t, s_is_contiguous)) <= 0) return r;
-  int64_t dim, numel;
-  if (call_i64(t, s_dim, NULL, &dim)) return -1;
-  if (dim < 2) return 0;
-  PyObject* zero = PyLong_FromLong(0);
-  if (!zero) return -1;
-  r = call_i64(t, s_size, zero, T);
-  Py_DECREF(zero);
-  if (r) return -1;
+/* qkv: 1 and (T, ld, dev, ptr, code) for the common case, 0 otherwise */
+static int qkv_rows(PyObject* o, int64_t* T, int64_t* ld, int64_t* dev, void** ptr, int* code) {
+  const at::Tensor* t = tensor_of(o);
+  if (!t || !t->is_cuda() || (*code = dtype_code(*t)) < 0 || !t->is_contiguous() || t->dim() < 2) return 0;
+  *T = t->size(0);
   if (*T <= 0) return 0;
-  if (call_i64(t, s_numel, NULL, &numel) || call_i64(t, s_get_device, NULL, dev)) return -1;
-  *ld = numel / *T;
-  int64_t p;
-  if (call_i64(t, s_data_ptr, NULL, &p)) return -1;
-  *ptr = (void*)(uintptr_t)p;
+  *ld = t->numel() / *T;
+  *dev = t->get_device();
+  *ptr = t->data_ptr();
   return 1;
 }
 
-/* gamma: 1 and its pointer (NULL for None) for the common case, 0 otherwise, -1 on error */
+/* gamma: 1 and its pointer (NULL for None) for the common case, 0 otherwise;
+ * the dtype that goes with qkv's is its own, bf16 for FP8 */
 static int gamma_ptr(PyObject* g, int code, int64_t dev, void** ptr) {
   if (g == Py_None) {
     *ptr = NULL;
     return 1;
   }
-  if (!is_tensor(g)) return 0;
-  PyObject* d = PyObject_GetAttr(g, s_dtype);
-  if (!d) return -1;
-  const int same = d == g_gdtypes[code];
-  Py_DECREF(d);
-  if (!same) return 0;
-  int r;
-  if ((r = call_true(g, s_is_contiguous)) <= 0) return r;
-  if ((r = attr_true(g, s_is_cuda)) <= 0) return r;
-  int64_t gd, p;
-  if (call_i64(g, s_get_device, NULL, &gd)) return -1;
-  if (gd != dev) return 0;
-  if (call_i64(g, s_data_ptr, NULL, &p)) return -1;
-  *ptr = (void*)(uintptr_t)p;
+  const at::Tensor* t = tensor_of(g);
+  const int want = code == QKNORM_FP8_E4M3 ? QKNORM_BF16 : code;
+  if (!t || dtype_code(*t) != want || !t->is_contiguous() || !t->is_cuda() || t->get_device() != dev)
+    return 0;
+  *ptr = t->data_ptr();
   return 1;
 }
 
@@ -304,17 +243,12 @@ static PyObject* f_per_head_t(PyObject* self, PyObject* const* a, Py_ssize_t n) 
   if (!g_raw_stream) Py_RETURN_NONE;
   int64_t T, ld, dev;
   void *qkv, *gq, *gk, *st;
-  int code, r;
+  int code;
   int32_t hq, hkv, d;
   float eps;
-  if ((r = qkv_rows(a[0], &T, &ld, &dev, &qkv, &code)) <= 0) {
-    if (r < 0) return NULL;
+  if (!qkv_rows(a[0], &T, &ld, &dev, &qkv, &code) || !gamma_ptr(a[4], code, dev, &gq) ||
+      !gamma_ptr(a[5], code, dev, &gk))
     Py_RETURN_NONE;
-  }
-  if ((r = gamma_ptr(a[4], code, dev, &gq)) <= 0 || (r = gamma_ptr(a[5], code, dev, &gk)) <= 0) {
-    if (r < 0) return NULL;
-    Py_RETURN_NONE;
-  }
   if (as_i32(a[1], &hq) || as_i32(a[2], &hkv) || as_i32(a[3], &d) || as_f32(a[6], &eps) ||
       stream_ptr(a[7], dev, &st))
     return NULL;
@@ -328,17 +262,12 @@ static PyObject* f_layerwise_t(PyObject* self, PyObject* const* a, Py_ssize_t n)
   if (!g_raw_stream) Py_RETURN_NONE;
   int64_t T, ld, dev, wq, wk;
   void *qkv, *gq, *gk, *st;
-  int code, r;
+  int code;
   int32_t ns;
   float eps;
-  if ((r = qkv_rows(a[0], &T, &ld, &dev, &qkv, &code)) <= 0) {
-    if (r < 0) return NULL;
+  if (!qkv_rows(a[0], &T, &ld, &dev, &qkv, &code) || !gamma_ptr(a[3], code, dev, &gq) ||
+      !gamma_ptr(a[4], code, dev, &gk))
     Py_RETURN_NONE;
-  }
-  if ((r = gamma_ptr(a[3], code, dev, &gq)) <= 0 || (r = gamma_ptr(a[4], code, dev, &gk)) <= 0) {
-    if (r < 0) return NULL;
-    Py_RETURN_NONE;
-  }
   if (as_i64(a[1], &wq) || as_i64(a[2], &wk) || as_f32(a[5], &eps) || as_i32(a[6], &ns) ||
       stream_ptr(a[7], dev, &st))
     return NULL;

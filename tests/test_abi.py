@@ -260,7 +260,7 @@ def test_plain_c_program_gets_the_validation_codes():
 
 
 def test_python_call_module_forwards_to_the_same_library(lib):
-    # the binding's call path (qk_norm_amd/csrc/pyfast.c) converts the Python
+    # the binding's call path (qk_norm_amd/csrc/pyfast.cpp) converts the Python
     # arguments itself and calls the same extern "C" functions: the library's
     # validation codes come back unchanged, and the process holds one copy of
     # the library whichever way it was opened
