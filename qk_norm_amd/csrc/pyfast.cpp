@@ -275,7 +275,8 @@ static PyObject* f_layerwise_t(PyObject* self, PyObject* const* a, Py_ssize_t n)
 }
 
 static PyMethodDef kMethods[] = {
-    {"setup", (PyCFunction)(void (*)(void))f_setup, METH_FASTCALL, "hand over torch's dtypes and stream query"},
+    {"setup", (PyCFunction)(void (*)(void))f_setup, METH_FASTCALL,
+     "hand over torch's current-raw-stream function and the torch.Tensor type"},
     {"per_head_t", (PyCFunction)(void (*)(void))f_per_head_t, METH_FASTCALL,
      "qknorm_per_head on torch tensors (common case; None: use the Python path)"},
     {"layerwise_t", (PyCFunction)(void (*)(void))f_layerwise_t, METH_FASTCALL,
