@@ -25,7 +25,9 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "qknorm_oracle.c")
-_LIB = os.path.join(_HERE, "liboracle.so")
+# QKNORM_ORACLE_LIB names another build of the same source to load instead
+# (for instance one built with sanitizers, to run the CPU pins under them)
+_LIB = os.environ.get("QKNORM_ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
 
 F32 = 0
 BF16 = 1
