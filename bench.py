@@ -453,59 +453,90 @@ PR_TURBOMIND_US = {
 }
 
 
+def _graph_and_eager(torch, dev, launch, reps):
+    """GPU time per launch of `reps` eager launches (event pair, after the
+    clock warm-up) and of `reps` launches replayed from one captured hipGraph.
+    `launch(j, stream)` launches call j on the given raw stream."""
+    cur = torch.cuda.current_stream(dev).cuda_stream
+    warm_clocks(torch, lambda j: launch(j, cur))
+    _, eager_us = Timer(torch).run(reps, lambda j: launch(j, cur))
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            for j in range(reps):
+                launch(j, side.cuda_stream)
+    torch.cuda.synchronize()
+    graph.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    graph_us = e0.elapsed_time(e1) * 1e3 / reps
+    del graph
+    return graph_us, eager_us
+
+
+def _per_head_points(q, torch, dev, problems, reps, label):
+    """Graph-replay and eager time per launch for each per-head problem, its
+    buffers rotating through up to 64 copies (so the smaller sizes run out of
+    the caches, as a serving loop's would)."""
+    from qk_norm_amd import synth
+    lib = q.load()
+    out = []
+    for p in problems:
+        es, ges = sizes(p)
+        n = min(pool_count(p.T * p.ld * es), 64)
+        base = to_device(p.x, p.dtype, torch, dev)
+        pool = [base.clone() for _ in range(n)]
+        gq = to_device(p.gamma_q, synth.gamma_dtype(p.dtype), torch, dev)
+        gk = to_device(p.gamma_k, synth.gamma_dtype(p.dtype), torch, dev) if p.hkv else None
+        bytes_alg = 2 * p.T * (p.wq + p.wk) * es + p.head_dim * ges * (2 if p.hkv else 1)
+
+        def launch(j, stream):
+            rc = lib.qknorm_per_head(pool[j % n].data_ptr(), p.T, p.ld, p.hq, p.hkv, p.head_dim,
+                                     gq.data_ptr(), gk.data_ptr() if gk is not None else None, p.eps,
+                                     p.dtype, stream)
+            if rc:
+                raise RuntimeError(q.strerror(rc))
+
+        graph_us, eager_us = _graph_and_eager(torch, dev, launch, reps)
+        gbs = bytes_alg / (graph_us * 1e-6) / 1e9
+        out.append({"hq": p.hq, "hkv": p.hkv, "T": p.T, "ld": p.ld, "graph_us": graph_us,
+                    "eager_us": eager_us, "gbs_graph": gbs, "pct_of_hbm_peak_graph": 100 * gbs / HBM_PEAK_GBS,
+                    "pool": n})
+        log(f"{label} hq={p.hq} hkv={p.hkv} T={p.T}: graph {graph_us:.2f} us, eager {eager_us:.2f} us")
+        del pool, base
+        torch.cuda.empty_cache()
+    return out
+
+
 def bench_sweep(q, torch, dev, reps=200):
     """Per-head bf16 [T, H, 128] over the PR's grid (H in {16, 32, 48}, T = 1 ... 4096).
     For each point: GPU time per launch of `reps` launches replayed from one
     captured hipGraph (no host cost between launches), and of `reps` eager
-    launches through the C ABI (host-bound at small T).  Buffers rotate through
-    up to 64 copies, so the smaller sizes run out of the caches, as a serving
-    loop's would."""
+    launches through the C ABI (host-bound at small T)."""
     from qk_norm_amd import synth
-    lib = q.load()
     out = []
     for H in (16, 32, 48):
-        for i, T in enumerate(PR_GRID_T):
-            p = synth.standalone_heads(T=T, H=H)
-            es, ges = sizes(p)
-            n = min(pool_count(p.T * p.ld * es), 64)
-            base = to_device(p.x, p.dtype, torch, dev)
-            pool = [base.clone() for _ in range(n)]
-            g = to_device(p.gamma_q, synth.gamma_dtype(p.dtype), torch, dev)
-            bytes_alg = 2 * p.T * p.wq * es + p.head_dim * ges
-
-            def launch(j, stream):
-                rc = lib.qknorm_per_head(pool[j % n].data_ptr(), p.T, p.ld, p.hq, 0, p.head_dim,
-                                         g.data_ptr(), None, p.eps, p.dtype, stream)
-                if rc:
-                    raise RuntimeError(q.strerror(rc))
-
-            cur = torch.cuda.current_stream(dev).cuda_stream
-            warm_clocks(torch, lambda j: launch(j, cur))
-            _, eager_us = Timer(torch).run(reps, lambda j: launch(j, cur))
-            graph = torch.cuda.CUDAGraph()
-            side = torch.cuda.Stream()
-            side.wait_stream(torch.cuda.current_stream())
-            with torch.cuda.stream(side):
-                with torch.cuda.graph(graph, stream=side):
-                    for j in range(reps):
-                        launch(j, side.cuda_stream)
-            torch.cuda.synchronize()
-            graph.replay()
-            torch.cuda.synchronize()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            graph.replay()
-            e1.record()
-            torch.cuda.synchronize()
-            graph_us = e0.elapsed_time(e1) * 1e3 / reps
-            out.append({"H": H, "T": T, "graph_us": graph_us, "eager_us": eager_us,
-                        "gbs_graph": bytes_alg / (graph_us * 1e-6) / 1e9,
-                        "pct_of_hbm_peak_graph": 100 * bytes_alg / (graph_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
-                        "pool": n, "pages_turbomind_us": {k: v[H][i] for k, v in PR_TURBOMIND_US.items()}})
-            log(f"sweep H={H} T={T}: graph {graph_us:.2f} us, eager {eager_us:.2f} us")
-            del graph, pool, base
-            torch.cuda.empty_cache()
+        pts = _per_head_points(q, torch, dev, [synth.standalone_heads(T=T, H=H) for T in PR_GRID_T], reps,
+                               "sweep")
+        for i, r in enumerate(pts):
+            out.append({"H": H, "T": r["T"], "graph_us": r["graph_us"], "eager_us": r["eager_us"],
+                        "gbs_graph": r["gbs_graph"], "pct_of_hbm_peak_graph": r["pct_of_hbm_peak_graph"],
+                        "pool": r["pool"], "pages_turbomind_us": {k: v[H][i] for k, v in PR_TURBOMIND_US.items()}})
     return out
+
+
+def bench_gqa_sweep(q, torch, dev, reps=200):
+    """Per-head on fused GQA rows [T, 6144] (Q 32 + K 8 heads of 128, V 8 heads
+    untouched), bf16, T in {1, 8, 64, 512, 8192}: the same two timings."""
+    from qk_norm_amd import synth
+    return _per_head_points(q, torch, dev, [synth.fused_gqa_rows(T=T) for T in (1, 8, 64, 512, 8192)], reps,
+                            "fused GQA")
 
 
 def bench_d2d_copy(torch, dev, nbytes, steps=400, warmup=40):
@@ -791,7 +822,8 @@ def main():
                           **bench_layerwise(q, torch, dev, p, args.steps, args.warmup, "fp8 prefill [32768, 10240]")}))
         return
     if args.case == "sweep":
-        print(json.dumps({"case": "sweep", "per_head_bf16_D128": bench_sweep(q, torch, dev)}))
+        print(json.dumps({"case": "sweep", "per_head_bf16_D128": bench_sweep(q, torch, dev),
+                          "fused_gqa_rows_bf16": bench_gqa_sweep(q, torch, dev)}))
         return
     if args.case == "decode":
         print(json.dumps({"case": "decode", "launches": bench_decode(q, torch, dev)}))
