@@ -822,8 +822,11 @@ def main():
                           **bench_layerwise(q, torch, dev, p, args.steps, args.warmup, "fp8 prefill [32768, 10240]")}))
         return
     if args.case == "sweep":
+        from qk_norm_amd import synth
         print(json.dumps({"case": "sweep", "per_head_bf16_D128": bench_sweep(q, torch, dev),
-                          "fused_gqa_rows_bf16": bench_gqa_sweep(q, torch, dev)}))
+                          "fused_gqa_rows_bf16": bench_gqa_sweep(q, torch, dev),
+                          "fused_rows_f32_T4": _per_head_points(q, torch, dev, [synth.small_fused_f32()], 200,
+                                                                "fp32 fused rows")}))
         return
     if args.case == "decode":
         print(json.dumps({"case": "decode", "launches": bench_decode(q, torch, dev)}))
