@@ -35,13 +35,15 @@ int check_common(int32_t dtype, float eps, int64_t T, int64_t ld) {
 
 // Q+K region and row pitch: ld >= wq + wk, pitch a multiple of 16 bytes,
 // base 16-byte aligned when anything is touched.
+// (ld >= 0 and T <= kMaxRows are checked before; every product below is
+// formed only once its factors are bounded, so no input overflows int64.)
 int check_region(const void* qkv, int64_t T, int64_t ld, int64_t wq, int64_t wk, int es) {
   if (wq < 0 || wk < 0) return QKNORM_E_SHAPE;
-  if (ld < wq + wk) return QKNORM_E_SHAPE;
+  if (wq > ld || wk > ld - wq) return QKNORM_E_SHAPE;       // ld < wq + wk
   const bool touched = T > 0 && wq + wk > 0;
   if (touched && qkv == nullptr) return QKNORM_E_NULLPTR;
   // rows are addressed with 32-bit buffer offsets: pitch at most 64 MiB
-  if (ld * es > kMaxPitchBytes || T * (ld + 1) > (INT64_C(1) << 46)) return QKNORM_E_UNSUPPORTED;
+  if (ld > kMaxPitchBytes / es || T * (ld + 1) > (INT64_C(1) << 46)) return QKNORM_E_UNSUPPORTED;
   if (touched && (!aligned16(qkv) || (ld * es) % 16 != 0)) return QKNORM_E_ALIGN;
   if ((wq * es) % 16 != 0 || (wk * es) % 16 != 0) return QKNORM_E_ALIGN;
   return QKNORM_OK;
@@ -198,16 +200,22 @@ int qknorm_qkv_proj_per_head(const void* x, int64_t ldx, const void* w, int64_t 
   if ((flags & ~QKNORM_PROJ_PLAIN) != 0) return QKNORM_E_UNSUPPORTED;
   if (hidden <= 0 || hq < 0 || hkv < 0 || head_dim <= 0 || ldx < hidden || ldw < hidden)
     return QKNORM_E_SHAPE;
-  const int64_t N = ((int64_t)hq + 2 * (int64_t)hkv) * head_dim;
-  if (ld < N) return QKNORM_E_SHAPE;
+  // N of any int32 head counts and head_dim fits 128 bits; N <= ld then fits int64
+  const __int128 n_wide = ((__int128)hq + 2 * (__int128)hkv) * head_dim;
+  if (n_wide > ld) return QKNORM_E_SHAPE;
+  const int64_t N = (int64_t)n_wide;
   const bool norm = (flags & QKNORM_PROJ_PLAIN) == 0;
   const bool touched = T > 0 && N > 0;
   if (touched && (x == nullptr || w == nullptr || qkv == nullptr)) return QKNORM_E_NULLPTR;
   if (norm && (rc = check_gamma(gamma_q, hq, T))) return rc;
   if (norm && (rc = check_gamma(gamma_k, hkv, T))) return rc;
   if (touched && (!aligned16(x) || !aligned16(w) || !aligned16(qkv))) return QKNORM_E_ALIGN;
-  if ((ldx * 2) % 16 != 0 || (ldw * 2) % 16 != 0 || (ld * 2) % 16 != 0) return QKNORM_E_ALIGN;
-  if (ld * 2 > kMaxPitchBytes || T * (ld + 1) > (INT64_C(1) << 46) || N >= (INT64_C(1) << 24))
+  // 16-byte row pitches: a multiple of 8 two-byte elements
+  if (ldx % 8 != 0 || ldw % 8 != 0 || ld % 8 != 0) return QKNORM_E_ALIGN;
+  // every pitch within 64 MiB before any product is formed from it (the
+  // kernel's own limits, checked next, are tighter still)
+  if (ld > kMaxPitchBytes / 2 || ldx > kMaxPitchBytes / 2 || ldw > kMaxPitchBytes / 2 ||
+      T * (ld + 1) > (INT64_C(1) << 46) || N >= (INT64_C(1) << 24))
     return QKNORM_E_UNSUPPORTED;
   qknorm::ProjArgs a{x, ldx, w, ldw, qkv, ld, T, hidden, hq, hkv, head_dim, gamma_q, gamma_k,
                      eps, flags, dtype};

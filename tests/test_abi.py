@@ -240,6 +240,27 @@ def test_projection_validation(lib):
     assert pj(lib, ldw=(1 << 22) + 8, T=0) == q.QKNORM_E_UNSUPPORTED
 
 
+def test_sizes_whose_products_overflow_64_bits_are_rejected(lib):
+    # pitches, widths and head counts near the int64 / int32 limits: each is
+    # rejected by value, before any product of it is formed (a product that
+    # wrapped could pass a bound and reach a kernel with truncated offsets)
+    big = 1 << 62
+    assert lw(lib, ld=big, wq=big, wk=big) == q.QKNORM_E_SHAPE            # wq + wk > ld
+    assert ps(lib, ld=big, wq=big - 1024, wk=2048, R=1) == q.QKNORM_E_SHAPE
+    assert lw(lib, ld=big, wq=4096, wk=1024) == q.QKNORM_E_UNSUPPORTED     # pitch past 64 MiB
+    assert ph(lib, ld=big, dt=F32) == q.QKNORM_E_UNSUPPORTED                # ld * 4 would wrap to 0
+    assert ph(lib, ld=(1 << 63) - 16, dt=BF16) == q.QKNORM_E_UNSUPPORTED
+    assert ap(lib, ld=big, wq=4096, wk=1024) == q.QKNORM_E_UNSUPPORTED
+    # projection: 256 rows of a 2^61-element pitch wrap a 64-bit byte count to 0
+    assert pj(lib, ldx=1 << 61) == q.QKNORM_E_UNSUPPORTED
+    assert pj(lib, ldw=1 << 61) == q.QKNORM_E_UNSUPPORTED
+    assert pj(lib, ld=1 << 61) == q.QKNORM_E_UNSUPPORTED
+    # (hq + 2 hkv) * head_dim past int64 from int32 arguments
+    m = (1 << 31) - 1
+    assert pj(lib, hq=m, hkv=m, D=m, ld=big) == q.QKNORM_E_SHAPE           # N > ld
+    assert pj(lib, hq=m, hkv=m, D=128, ld=big) == q.QKNORM_E_UNSUPPORTED
+
+
 def _c_program():
     """tests/c_abi/closed_form, built with gcc here if it is not there yet."""
     import importlib.util
