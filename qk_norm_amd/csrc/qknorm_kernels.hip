@@ -384,6 +384,38 @@ __device__ __forceinline__ float combine(const float* __restrict__ p, uint32_t n
   return s;
 }
 
+// The same sums for the Q and K partials of one row read from global memory
+// (a caller's [nparts][T] arrays, column t): the loads go out eight shards at
+// a time for both regions, so a row waits for one memory round trip per
+// eight shards instead of one per shard, and the adds still take the shards
+// in order, ((p0 + p1) + p2) + ..., the bits of combine().  Both pointers
+// must be readable: a caller without one region passes the other's.
+__device__ __forceinline__ void combine_cols(const float* __restrict__ p, const float* __restrict__ q,
+                                             uint32_t n, int64_t stride, float* sp, float* sq) {
+  constexpr uint32_t kBatch = 8;
+  float a = 0.f, b = 0.f;
+  uint32_t r = 0;
+  for (; r + kBatch <= n; r += kBatch) {
+    float u[kBatch], v[kBatch];
+#pragma unroll
+    for (uint32_t i = 0; i < kBatch; ++i) {
+      u[i] = p[(int64_t)(r + i) * stride];
+      v[i] = q[(int64_t)(r + i) * stride];
+    }
+#pragma unroll
+    for (uint32_t i = 0; i < kBatch; ++i) {
+      a += u[i];
+      b += v[i];
+    }
+  }
+  for (; r < n; ++r) {
+    a += p[(int64_t)r * stride];
+    b += q[(int64_t)r * stride];
+  }
+  *sp = a;
+  *sq = b;
+}
+
 // Two such sums side by side (the Q and K partials of one row), each in the
 // same order as combine(): both regions' reads go out together, so a row
 // waits for one round of LDS reads instead of two.
@@ -817,8 +849,12 @@ __global__ __launch_bounds__(QKNORM_LWW_BLOCK) void layerwise_wave_kernel(
     const Rsrc rn = row_rsrc(qkv, G.ld_bytes, tn < G.T ? tn : 0, tn < G.T ? qk_vecs : 0);
     float rq, rk;
     if constexpr (APPLY) {
-      rq = rms_scale(combine(part_q + t, nparts, G.T), G.inv_wq, eps);
-      rk = rms_scale(combine(part_k + t, nparts, G.T), G.inv_wk, eps);
+      const float* pq = G.q_vecs ? part_q + t : part_k + t;
+      const float* pk = G.k_vecs ? part_k + t : part_q + t;
+      float sq, sk;
+      combine_cols(pq, pk, nparts, G.T, &sq, &sk);
+      rq = rms_scale(sq, G.inv_wq, eps);
+      rk = rms_scale(sk, G.inv_wk, eps);
     } else {
       rq = rms_scale(wave_region_sumsq<DT, NQ>(xq, wq), G.inv_wq, eps);
       rk = rms_scale(wave_region_sumsq<DT, NK>(xk, wk), G.inv_wk, eps);
@@ -948,7 +984,9 @@ __global__ __launch_bounds__(512) void apply_scalar_kernel(
     const float* __restrict__ part_q, const float* __restrict__ part_k, uint32_t nparts,
     float inv_norm_wq, float inv_norm_wk, const uint8_t* __restrict__ gamma_q,
     const uint8_t* __restrict__ gamma_k, float eps) {
-  __shared__ float scale[2][kApplyRows];
+  // the rows' scales, two buffers used in turn: a buffer is written again
+  // only after every thread has passed the barrier of the rows in between
+  __shared__ float scale[2][2][kApplyRows];
   const uint32_t tid = threadIdx.x, nt = blockDim.x;
   const uint32_t nv = q_vecs + k_vecs;
   Gam<DT> g[VPT];
@@ -958,29 +996,36 @@ __global__ __launch_bounds__(512) void apply_scalar_kernel(
     g[k] = v < q_vecs ? load_gamma<DT>(gamma_q, v)
                       : (v < nv ? load_gamma<DT>(gamma_k, v - q_vecs) : zero_gamma<DT>());
   }
-  for (uint32_t t0 = blockIdx.x * kApplyRows; t0 < T; t0 += gridDim.x * kApplyRows) {
+  uint32_t buf = 0;
+  for (uint32_t t0 = blockIdx.x * kApplyRows; t0 < T; t0 += gridDim.x * kApplyRows, buf ^= 1) {
     const uint32_t rows = T - t0 < kApplyRows ? T - t0 : kApplyRows;
-    __syncthreads();                           // previous rows are done with `scale`
-    if (tid < rows) {
-      if (q_vecs) scale[0][tid] = rms_scale(combine(part_q + t0 + tid, nparts, T), inv_norm_wq, eps);
-      if (k_vecs) scale[1][tid] = rms_scale(combine(part_k + t0 + tid, nparts, T), inv_norm_wk, eps);
-    }
-    __syncthreads();
-    // rows alternate between two register sets: row j+1's loads are in
-    // flight while row j is scaled and stored
+    // the first row's loads go out before the partials are read (they do not
+    // need the scales), so the two reads' latencies overlap; the barrier
+    // below waits for LDS only, not for these loads
     u32x4 xa[VPT], xb[VPT];
     Rsrc ra = row_rsrc(qkv, ld_bytes, t0, nv), rb;
     apply_rows_load<VPT>(ra, tid, nt, nv, xa);
+    float (&sc)[2][kApplyRows] = scale[buf];
+    if (tid < rows) {
+      float sq, sk;
+      combine_cols((q_vecs ? part_q : part_k) + t0 + tid, (k_vecs ? part_k : part_q) + t0 + tid, nparts,
+                   T, &sq, &sk);
+      sc[0][tid] = rms_scale(sq, inv_norm_wq, eps);   // (a region without vectors never reads its scale)
+      sc[1][tid] = rms_scale(sk, inv_norm_wk, eps);
+    }
+    lds_barrier();
+    // rows alternate between two register sets: row j+1's loads are in
+    // flight while row j is scaled and stored
     for (uint32_t j = 0; j < rows; j += 2) {
       const bool more1 = j + 1 < rows;
       rb = row_rsrc(qkv, ld_bytes, more1 ? t0 + j + 1 : t0, more1 ? nv : 0);
       apply_rows_load<VPT>(rb, tid, nt, nv, xb);
-      apply_rows_store<DT, VPT>(ra, tid, nt, q_vecs, nv, xa, g, scale[0][j], scale[1][j]);
+      apply_rows_store<DT, VPT>(ra, tid, nt, q_vecs, nv, xa, g, sc[0][j], sc[1][j]);
       if (!more1) break;
       const bool more2 = j + 2 < rows;
       ra = row_rsrc(qkv, ld_bytes, more2 ? t0 + j + 2 : t0, more2 ? nv : 0);
       apply_rows_load<VPT>(ra, tid, nt, nv, xa);
-      apply_rows_store<DT, VPT>(rb, tid, nt, q_vecs, nv, xb, g, scale[0][j + 1], scale[1][j + 1]);
+      apply_rows_store<DT, VPT>(rb, tid, nt, q_vecs, nv, xb, g, sc[0][j + 1], sc[1][j + 1]);
     }
   }
 }
@@ -995,12 +1040,13 @@ __global__ __launch_bounds__(256) void apply_scalar_wide_kernel(
     const uint8_t* __restrict__ gamma_k, float eps) {
   for (uint32_t t = blockIdx.x; t < T; t += gridDim.x) {
     const Rsrc rs = row_rsrc(qkv, ld_bytes, t, q_vecs + k_vecs);
+    float sq, sk;
+    combine_cols((q_vecs ? part_q : part_k) + t, (k_vecs ? part_k : part_q) + t, nparts, T, &sq, &sk);
     if (q_vecs)
-      apply_stream<DT>(rs, 0, gamma_q, q_vecs, threadIdx.x, blockDim.x,
-                       rms_scale(combine(part_q + t, nparts, T), inv_norm_wq, eps));
+      apply_stream<DT>(rs, 0, gamma_q, q_vecs, threadIdx.x, blockDim.x, rms_scale(sq, inv_norm_wq, eps));
     if (k_vecs)
       apply_stream<DT>(rs, q_vecs * 16, gamma_k, k_vecs, threadIdx.x, blockDim.x,
-                       rms_scale(combine(part_k + t, nparts, T), inv_norm_wk, eps));
+                       rms_scale(sk, inv_norm_wk, eps));
   }
 }
 
