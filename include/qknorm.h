@@ -24,7 +24,7 @@
  *         bits with bias 7, 3 fraction bits; no infinities; largest finite
  *         448), unscaled, and gamma is bf16.  (SwiftQK verdict page, Section
  *         IV-C / Fig. 2(b) and the summary: the activations are BF16 or
- *         FP8-E4M3, and error is judged at that format.)
+ *         FP8-E4M3, and error is measured at that format.)
  *         Arithmetic is fp32 throughout; each output element is rounded
  *         once, to nearest even, to the I/O dtype; FP8 results beyond +-448
  *         saturate to +-448 (a NaN stays NaN).  Partial sums are always fp32.

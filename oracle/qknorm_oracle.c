@@ -42,7 +42,7 @@
  *
  * dtype codes: 0 = fp32, 1 = bf16, 2 = fp16 (both stored as 16-bit patterns),
  * 3 = FP8 E4M3 activations (one byte each) with bf16 gamma.  The FP8 reading:
- * the "SwiftQK" verdict page (Section IV-C / Fig. 2(b)) and its summary judge
+ * the "SwiftQK" verdict page (Section IV-C / Fig. 2(b)) and its summary measure
  * error at the activation format, BF16 or FP8-E4M3; the pages give no scale
  * factor, so values are taken unscaled, and the weights keep bf16.  E4M3 has
  * no infinity: results are rounded to nearest-even and anything beyond the
