@@ -739,7 +739,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--case", default="headline",
                     choices=["headline", "prefill_layerwise", "prefill_per_head", "fp8_per_head",
-                             "fp8_prefill_layerwise", "proj", "decode", "sweep", "copy", "stream",
+                             "fp8_prefill_layerwise", "proj", "proj_tokens", "decode", "sweep", "copy", "stream",
                              "wide_layerwise"],
                     help="single case for profiling runs")
     ap.add_argument("--stream-shape", metavar="U,THREADS,CAP",
@@ -833,6 +833,16 @@ def main():
         return
     if args.case == "proj":
         print(json.dumps({"case": "proj", **bench_proj(q, torch, dev, args.steps, args.warmup, T=8192)}))
+        return
+    if args.case == "proj_tokens":
+        # the Qwen3-8B projection from decode sizes to prefill (one kernel per
+        # size range: one block per head up to 32 tokens, tiles above)
+        pts = {}
+        for T in (1, 8, 32, 64, 128, 256, 512, 1024, 2048, 4096):
+            r = bench_proj(q, torch, dev, args.steps, args.warmup, T=T)
+            pts[str(T)] = {k: round(r[k]["mean_us"], 2) for k in
+                           ("fused_proj_qknorm", "plain_proj", "torch_mm", "torch_mm_then_qknorm")}
+        print(json.dumps({"case": "proj_tokens", "us_per_call": pts}))
         return
     if args.case == "prefill_per_head":
         p = synth.prefill_rows(T=32768, mode="per_head")

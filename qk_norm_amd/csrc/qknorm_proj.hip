@@ -540,6 +540,126 @@ __global__ __launch_bounds__(GF::kThreads) void qkv_proj_kernel(ProjKArgs args, 
   }
 }
 
+// Decode sizes (T <= 32 tokens).  256 x 256 tiles would leave all but a few
+// of the CUs idle and spend their MFMAs on empty rows, while the time is in
+// reading the weight (N x K, each element once).  Here one block of 8 waves
+// takes one head (D columns) for all T tokens: WN groups of 64 columns times
+// WK = 8 / WN groups of 32-wide K chunks.  Each wave accumulates its 64
+// columns x 16*TB tokens over its chunks with the tiled kernel's MFMA (the
+// weight's fragment first), its fragments loaded straight from global memory
+// PF - 1 chunks ahead.  The WK partial sums then meet in LDS, one block of
+// 16 tokens at a time, and are added in K-group order; each token's head is
+// normalised on those fp32 sums (per-head QK-Norm, as in the tiled kernel)
+// and stored, four outputs (8 bytes) per thread.  Rows past T read zeros
+// (their offsets fall outside the activations' descriptor) and are not
+// stored.  A block reads the weight at 30-50 GB/s, so one block per head (48
+// for a Qwen3-8B layer) bounds this path near 2 TB/s.
+template <int DT, int D, int TB>
+__global__ __launch_bounds__(512) void qkv_proj_decode_kernel(ProjKArgs args) {
+  constexpr int WN = D / 64, WK = 8 / WN, JB = 4, PF = 4;
+  constexpr int kPitch = D + 4;                  // floats per token row (padding spreads the banks)
+  static_assert(WN * WK == 8 && TB >= 1 && TB <= 4, "");
+  __shared__ __attribute__((aligned(16))) float part[WK][16][kPitch];
+  typedef typename ProjElem<DT>::T Elem;
+  typedef typename ProjElem<DT>::V8 Frag;
+  const uint32_t tid = threadIdx.x, lane = tid & 63, wave = uniform(tid >> 6);
+  const uint32_t wn = wave % WN, wk = wave / WN;
+  const uint32_t head = blockIdx.x, n0 = head * D;
+  const uint32_t T = args.T, K = args.K;
+  const uint32_t nk = K / 32;                    // K chunks; this wave takes [c0, c1)
+  const uint32_t c0 = wk * nk / WK, c1 = (wk + 1) * nk / WK;
+  const uint32_t fr = lane % 16, fk = 8 * (lane / 16);
+  const Rsrc rw = make_rsrc(args.w + (uint64_t)(n0 + wn * 64) * args.ldw_bytes,
+                            (uint64_t)63 * args.ldw_bytes + K * 2);
+  const Rsrc rx = make_rsrc(args.x, (uint64_t)(T - 1) * args.ldx_bytes + K * 2);
+  uint32_t woff[JB], xoff[TB];
+#pragma unroll
+  for (int j = 0; j < JB; ++j) woff[j] = (j * 16 + fr) * args.ldw_bytes + fk * 2;
+#pragma unroll
+  for (int t = 0; t < TB; ++t) xoff[t] = (t * 16 + fr) * args.ldx_bytes + fk * 2;
+
+  f32x4 acc[TB][JB];
+#pragma unroll
+  for (int t = 0; t < TB; ++t)
+#pragma unroll
+    for (int j = 0; j < JB; ++j) acc[t][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (c0 < c1) {
+    // a ring of PF fragment sets; loads past the last chunk fetch the last
+    // chunk again (unused) so that every slot is loaded the same way
+    Frag wf[PF][JB], xf[PF][TB];
+    auto load = [&](Frag (&w)[JB], Frag (&x)[TB], uint32_t c) {
+      const uint32_t so = (c < c1 ? c : c1 - 1) * 64;
+#pragma unroll
+      for (int j = 0; j < JB; ++j)
+        w[j] = __builtin_bit_cast(Frag, __builtin_amdgcn_raw_buffer_load_b128(rw, woff[j], so, 0));
+#pragma unroll
+      for (int t = 0; t < TB; ++t)
+        x[t] = __builtin_bit_cast(Frag, __builtin_amdgcn_raw_buffer_load_b128(rx, xoff[t], so, 0));
+    };
+#pragma unroll
+    for (int p = 0; p < PF - 1; ++p) load(wf[p], xf[p], c0 + p);
+    for (uint32_t c = c0; c < c1; c += PF) {
+#pragma unroll
+      for (int p = 0; p < PF; ++p) {
+        const int kNext = (p + PF - 1) % PF;       // (constant once the loop is unrolled)
+        load(wf[kNext], xf[kNext], c + p + PF - 1);
+        if (c + p < c1) {
+#pragma unroll
+          for (int t = 0; t < TB; ++t)
+#pragma unroll
+            for (int j = 0; j < JB; ++j) acc[t][j] = ProjElem<DT>::mfma(wf[p][j], xf[p][t], acc[t][j]);
+        }
+      }
+    }
+  }
+
+  // per token block: each wave's partial into LDS, then thread tid takes
+  // four consecutive columns (4 * q4 ...) of token tt of the block
+  constexpr int kQuads = D / 4;                  // threads per token
+  constexpr int kTokPerPass = 512 / kQuads;      // 32, 16, 8
+  constexpr int kPasses = kTokPerPass >= 16 ? 1 : 16 / kTokPerPass;
+  const uint32_t q4 = tid % kQuads, tt = tid / kQuads;
+  const bool normed = args.norm && head < args.hq + args.hkv;
+  float g[4] = {1.f, 1.f, 1.f, 1.f};
+  if (normed) {
+    const Elem* gs = reinterpret_cast<const Elem*>(head < args.hq ? args.gamma_q : args.gamma_k);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) g[e] = (float)gs[4 * q4 + e];
+  }
+  const Rsrc ro = make_rsrc(args.out + (uint64_t)n0 * 2, (uint64_t)(T - 1) * args.ld_bytes + D * 2);
+#pragma unroll
+  for (int t = 0; t < TB; ++t) {
+    __syncthreads();                             // the previous block's sums have been read
+#pragma unroll
+    for (int j = 0; j < JB; ++j)
+      *reinterpret_cast<f32x4*>(&part[wk][fr][wn * 64 + j * 16 + 4 * (lane / 16)]) = acc[t][j];
+    __syncthreads();
+#pragma unroll
+    for (int ps = 0; ps < kPasses; ++ps) {
+      const uint32_t tok = ps * kTokPerPass + tt;    // (head_dim 64: the last 4 waves have none)
+      if (tok < 16) {
+        f32x4 v = *reinterpret_cast<const f32x4*>(&part[0][tok][4 * q4]);
+#pragma unroll
+        for (int w = 1; w < WK; ++w) v += *reinterpret_cast<const f32x4*>(&part[w][tok][4 * q4]);
+        const uint32_t row = t * 16 + tok;
+        float y[4] = {v[0], v[1], v[2], v[3]};
+        if (normed) {
+          float ss = 0.f;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) ss = __builtin_fmaf(y[e], y[e], ss);
+          const float sc = rms_scale(group_sum<kQuads>(ss), args.inv_d, args.eps);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) y[e] = (y[e] * g[e]) * sc;
+        }
+        typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+        const u32x2 o = {pack2<DT>(y[0], y[1]), pack2<DT>(y[2], y[3])};
+        __builtin_amdgcn_raw_buffer_store_b64(o, ro, row < T ? row * (uint32_t)args.ld_bytes + q4 * 8 : 0xFFFFFFF0u,
+                                              0, kStorePolicy);
+      }
+    }
+  }
+}
+
 // 256 x 256 tiles of 8 waves (4 along M, 2 along N), each wave 64 x 128 as
 // 4 x 8 blocks of 16 x 16: 12 fragment reads per 32 MFMAs and 131 flop per
 // byte of operand staged, the best of the shapes measured on MI355X.  The
@@ -613,7 +733,57 @@ static uint32_t split_column(uint32_t T, uint32_t N, uint32_t head_dim, int cus)
   return best;
 }
 
+// The kernel arguments of one call (both kernels take them).
+static ProjKArgs kernel_args(const ProjArgs& a) {
+  ProjKArgs k;
+  k.x = (const uint8_t*)a.x;
+  k.w = (const uint8_t*)a.w;
+  k.out = (uint8_t*)a.qkv;
+  k.gamma_q = (const uint8_t*)a.gamma_q;
+  k.gamma_k = (const uint8_t*)a.gamma_k;
+  k.ld_bytes = (uint64_t)a.ld * 2;
+  k.ldx_bytes = (uint32_t)(a.ldx * 2);
+  k.ldw_bytes = (uint32_t)(a.ldw * 2);
+  k.T = (uint32_t)a.T;
+  k.K = (uint32_t)a.hidden;
+  k.N = (uint32_t)((a.hq + 2 * a.hkv) * a.head_dim);
+  k.hq = (uint32_t)a.hq;
+  k.hkv = (uint32_t)a.hkv;
+  k.norm = (uint32_t)((a.flags & 1) == 0);
+  k.eps = a.eps;
+  k.inv_d = 1.0f / (float)a.head_dim;
+  return k;
+}
+
+#ifndef QKNORM_PROJ_DECODE_T
+#define QKNORM_PROJ_DECODE_T 32    // token counts up to this take one block per head
+#endif
+static_assert(QKNORM_PROJ_DECODE_T <= 64, "the decode kernel holds at most 4 blocks of 16 tokens");
+
+template <int DT>
+static auto decode_kernel(int head_dim, uint32_t tb) {
+  auto by_tb = [&](auto k1, auto k2, auto k3, auto k4) {
+    return tb == 1 ? k1 : (tb == 2 ? k2 : (tb == 3 ? k3 : k4));
+  };
+  return head_dim == 64
+             ? by_tb(qkv_proj_decode_kernel<DT, 64, 1>, qkv_proj_decode_kernel<DT, 64, 2>,
+                     qkv_proj_decode_kernel<DT, 64, 3>, qkv_proj_decode_kernel<DT, 64, 4>)
+         : head_dim == 128
+             ? by_tb(qkv_proj_decode_kernel<DT, 128, 1>, qkv_proj_decode_kernel<DT, 128, 2>,
+                     qkv_proj_decode_kernel<DT, 128, 3>, qkv_proj_decode_kernel<DT, 128, 4>)
+             : by_tb(qkv_proj_decode_kernel<DT, 256, 1>, qkv_proj_decode_kernel<DT, 256, 2>,
+                     qkv_proj_decode_kernel<DT, 256, 3>, qkv_proj_decode_kernel<DT, 256, 4>);
+}
+
+static hipError_t launch_qkv_proj_decode(const ProjArgs& a, hipStream_t s) {
+  const uint32_t tb = (uint32_t)((a.T + 15) / 16);
+  auto kern = a.dtype == kF16 ? decode_kernel<kF16>(a.head_dim, tb) : decode_kernel<kBF16>(a.head_dim, tb);
+  hipLaunchKernelGGL(kern, dim3((uint32_t)(a.hq + 2 * a.hkv)), dim3(512), 0, s, kernel_args(a));
+  return hipGetLastError();
+}
+
 hipError_t launch_qkv_proj(const ProjArgs& a, hipStream_t s, int cus) {
+  if (a.T <= QKNORM_PROJ_DECODE_T) return launch_qkv_proj_decode(a, s);
   const uint32_t N = (uint32_t)((a.hq + 2 * a.hkv) * a.head_dim);
   const uint32_t T = (uint32_t)a.T;
   const uint32_t n_split = split_column(T, N, (uint32_t)a.head_dim, cus);
@@ -633,24 +803,8 @@ hipError_t launch_qkv_proj(const ProjArgs& a, hipStream_t s, int cus) {
   const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
   if (e != hipSuccess) return e;
-  ProjKArgs k;
-  k.x = (const uint8_t*)a.x;
-  k.w = (const uint8_t*)a.w;
-  k.out = (uint8_t*)a.qkv;
-  k.gamma_q = (const uint8_t*)a.gamma_q;
-  k.gamma_k = (const uint8_t*)a.gamma_k;
-  k.ld_bytes = (uint64_t)a.ld * 2;
-  k.ldx_bytes = (uint32_t)(a.ldx * 2);
-  k.ldw_bytes = (uint32_t)(a.ldw * 2);
-  k.T = T;
-  k.K = (uint32_t)a.hidden;
-  k.N = N;
-  k.hq = (uint32_t)a.hq;
-  k.hkv = (uint32_t)a.hkv;
-  k.norm = (uint32_t)((a.flags & 1) == 0);
-  k.eps = a.eps;
-  k.inv_d = 1.0f / (float)a.head_dim;
-  hipLaunchKernelGGL(kern, dim3(n_full + n_half), dim3(kThreads), kLdsBytes, s, k, n_full, n_split);
+  hipLaunchKernelGGL(kern, dim3(n_full + n_half), dim3(kThreads), kLdsBytes, s, kernel_args(a), n_full,
+                     n_split);
   return hipGetLastError();
 }
 

@@ -178,8 +178,36 @@ def test_fused_equals_unfused_up_to_the_intermediate_rounding():
     assert np.array_equal(fused[:, (hq + hkv) * D:], unfused[:, (hq + hkv) * D:]), "V identical"
 
 
-def test_deterministic_and_graph_replay():
-    T, hidden, hq, hkv, D = 200, 256, 4, 1, 128
+# Decode sizes (T <= 32) take the one-block-per-head kernel: every head_dim,
+# token counts on and off its 16-token blocks, K chunks that do not divide
+# evenly among its K groups (or number fewer than them), and each head
+# layout; 33 to 64 tokens take the tiled kernel again.
+@pytest.mark.parametrize("dtype", [BF16, F16], ids=["bf16", "fp16"])
+@pytest.mark.parametrize("T,hidden,hq,hkv,D", [
+    (1, 4096, 32, 8, 128),       # a Qwen3-8B decode step
+    (8, 4096, 32, 8, 128),
+    (32, 4096, 32, 8, 128),
+    (17, 320, 4, 2, 128),        # 10 K chunks over 4 K groups
+    (2, 64, 3, 1, 64),           # 2 K chunks over 8 K groups: most waves have none
+    (31, 192, 5, 0, 64),         # no K or V heads
+    (15, 448, 0, 3, 64),         # K heads only
+    (16, 256, 2, 1, 256),        # head_dim 256
+    (29, 576, 1, 2, 256),
+    (48, 128, 6, 2, 128),        # (tiled)
+])
+def test_decode_size_projection(dtype, T, hidden, hq, hkv, D):
+    x, w, gq, gk = make(110 + T + D, T, hidden, hq, hkv, D, dtype=dtype)
+    eps = synth.eps_f32(1e-6)
+    N = w.shape[0]
+    got = run_proj(x, w, hq, hkv, D, gq, gk, eps, ld=N + 16, label="decode", dtype=dtype)
+    check(x, w, hq, hkv, D, gq, gk, eps, got, label=f"decode T={T} K={hidden} D={D}", dtype=dtype)
+    got = run_proj(x, w, hq, hkv, D, gq, gk, eps, plain=True, label="decode plain", dtype=dtype)
+    check(x, w, hq, hkv, D, gq, gk, eps, got, plain=True, label=f"decode plain T={T} D={D}", dtype=dtype)
+
+
+@pytest.mark.parametrize("T", [200, 8], ids=["tiled", "decode"])
+def test_deterministic_and_graph_replay(T):
+    hidden, hq, hkv, D = 256, 4, 1, 128
     x, w, gq, gk = make(82, T, hidden, hq, hkv, D)
     xt, wt = host_to_device(x, BF16), host_to_device(w, BF16)
     g1, g2 = gamma_to_device(gq, BF16), gamma_to_device(gk, BF16)
