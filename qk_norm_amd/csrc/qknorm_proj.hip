@@ -758,21 +758,25 @@ static ProjKArgs kernel_args(const ProjArgs& a) {
 #ifndef QKNORM_PROJ_DECODE_T
 #define QKNORM_PROJ_DECODE_T 32    // token counts up to this take one block per head
 #endif
-static_assert(QKNORM_PROJ_DECODE_T <= 64, "the decode kernel holds at most 4 blocks of 16 tokens");
+static_assert(QKNORM_PROJ_DECODE_T >= 1 && QKNORM_PROJ_DECODE_T <= 64,
+              "the decode kernel holds 1 to 4 blocks of 16 tokens");
+
+// The decode kernel for TB blocks of 16 tokens (only the TB the threshold
+// allows are built).
+typedef void (*ProjKernel)(ProjKArgs);
+template <int DT, int D>
+static ProjKernel decode_kernel_d(uint32_t tb) {
+  constexpr uint32_t kMaxTb = (QKNORM_PROJ_DECODE_T + 15) / 16;
+  if constexpr (kMaxTb >= 4) if (tb == 4) return qkv_proj_decode_kernel<DT, D, 4>;
+  if constexpr (kMaxTb >= 3) if (tb == 3) return qkv_proj_decode_kernel<DT, D, 3>;
+  if constexpr (kMaxTb >= 2) if (tb == 2) return qkv_proj_decode_kernel<DT, D, 2>;
+  return qkv_proj_decode_kernel<DT, D, 1>;
+}
 
 template <int DT>
-static auto decode_kernel(int head_dim, uint32_t tb) {
-  auto by_tb = [&](auto k1, auto k2, auto k3, auto k4) {
-    return tb == 1 ? k1 : (tb == 2 ? k2 : (tb == 3 ? k3 : k4));
-  };
-  return head_dim == 64
-             ? by_tb(qkv_proj_decode_kernel<DT, 64, 1>, qkv_proj_decode_kernel<DT, 64, 2>,
-                     qkv_proj_decode_kernel<DT, 64, 3>, qkv_proj_decode_kernel<DT, 64, 4>)
-         : head_dim == 128
-             ? by_tb(qkv_proj_decode_kernel<DT, 128, 1>, qkv_proj_decode_kernel<DT, 128, 2>,
-                     qkv_proj_decode_kernel<DT, 128, 3>, qkv_proj_decode_kernel<DT, 128, 4>)
-             : by_tb(qkv_proj_decode_kernel<DT, 256, 1>, qkv_proj_decode_kernel<DT, 256, 2>,
-                     qkv_proj_decode_kernel<DT, 256, 3>, qkv_proj_decode_kernel<DT, 256, 4>);
+static ProjKernel decode_kernel(int head_dim, uint32_t tb) {
+  return head_dim == 64 ? decode_kernel_d<DT, 64>(tb)
+                        : (head_dim == 128 ? decode_kernel_d<DT, 128>(tb) : decode_kernel_d<DT, 256>(tb));
 }
 
 static hipError_t launch_qkv_proj_decode(const ProjArgs& a, hipStream_t s) {
