@@ -478,11 +478,13 @@ __device__ __forceinline__ void proj_tile(const ProjKArgs& args, uint32_t id, ui
 
   constexpr int kReads = MB + NB, kMfma = MB * NB;
   // the next sub-step's fragment reads go one after every kMfmaPerRead MFMAs
-  // (where there are MFMAs enough), the step's loads between the MFMAs after them
-  constexpr int kMfmaPerRead = QKNORM_PROJ_MPR * kReads < kMfma ? QKNORM_PROJ_MPR : 1;
-  constexpr int kLoadsPerMfma =
-      (G::kLoads + kMfma - kReads * kMfmaPerRead - 1) / (kMfma - kReads * kMfmaPerRead);
-  static_assert(kMfma > kReads, "");
+  // (where there are MFMAs enough), the step's loads between the MFMAs after
+  // them; slabs with fewer MFMAs than reads (one 16-row block) leave the
+  // order to the compiler
+  constexpr bool kSched = kMfma > kReads;
+  constexpr int kMfmaPerRead = kSched && QKNORM_PROJ_MPR * kReads < kMfma ? QKNORM_PROJ_MPR : 1;
+  constexpr int kFreeMfma = kSched ? kMfma - kReads * kMfmaPerRead : 1;
+  constexpr int kLoadsPerMfma = (G::kLoads + kFreeMfma - 1) / kFreeMfma;
   for (uint32_t ks = 0; ks < ksteps; ++ks) {
     uint8_t* const st = (ks & 1) ? stage1 : stage0;
     uint8_t* const nx = (ks & 1) ? stage0 : stage1;
@@ -490,8 +492,10 @@ __device__ __forceinline__ void proj_tile(const ProjKArgs& args, uint32_t id, ui
     for (int kk = 0; kk < KK - 1; ++kk) {
       read_frags<G, DT>(st, arow, brow, (kk + 1) * G::KS + fk, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
       mfma_step<G, DT>(acc, fa[kk & 1], fb[kk & 1]);
-      sched_interleave<kReads, 1, 0, kMfmaPerRead>();
-      sched_mfmas<kMfma - kReads * kMfmaPerRead>();
+      if constexpr (kSched) {
+        sched_interleave<kReads, 1, 0, kMfmaPerRead>();
+        sched_mfmas<kMfma - kReads * kMfmaPerRead>();
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
     wait_vmcnt<0>();                            // step ks+1 has landed (this wave)
@@ -502,8 +506,10 @@ __device__ __forceinline__ void proj_tile(const ProjKArgs& args, uint32_t id, ui
     read_frags<G, DT>(nx, arow, brow, fk, fa[0], fb[0]);
     dma_tile<G>(ra, rb, doff, step_bytes<G>(ks + 2, ksteps), st, wave);
     mfma_step<G, DT>(acc, fa[1], fb[1]);
-    sched_interleave<kReads, 1, 0, kMfmaPerRead>();
-    sched_interleave<kMfma - kReads * kMfmaPerRead, 0, kLoadsPerMfma>();
+    if constexpr (kSched) {
+      sched_interleave<kReads, 1, 0, kMfmaPerRead>();
+      sched_interleave<kMfma - kReads * kMfmaPerRead, 0, kLoadsPerMfma>();
+    }
     // keeps the reads above in this iteration: without it the compiler merges
     // them with the reads before the loop into one read at the top of the
     // loop, which then waits for its result before the first MFMA
@@ -540,7 +546,7 @@ __global__ __launch_bounds__(GF::kThreads) void qkv_proj_kernel(ProjKArgs args, 
   }
 }
 
-// Decode sizes (T <= 32 tokens).  256 x 256 tiles would leave all but a few
+// Decode sizes (T <= 16 tokens).  256 x 256 tiles would leave all but a few
 // of the CUs idle and spend their MFMAs on empty rows, while the time is in
 // reading the weight (N x K, each element once).  Here one block of 8 waves
 // takes one head (D columns) for all T tokens: WN groups of 64 columns times
@@ -756,10 +762,10 @@ static ProjKArgs kernel_args(const ProjArgs& a) {
 }
 
 #ifndef QKNORM_PROJ_DECODE_T
-#define QKNORM_PROJ_DECODE_T 32    // token counts up to this take one block per head
+#define QKNORM_PROJ_DECODE_T 16    // token counts up to this take one block per head
 #endif
-static_assert(QKNORM_PROJ_DECODE_T >= 1 && QKNORM_PROJ_DECODE_T <= 64,
-              "the decode kernel holds 1 to 4 blocks of 16 tokens");
+static_assert(QKNORM_PROJ_DECODE_T >= 0 && QKNORM_PROJ_DECODE_T <= 64,
+              "the decode kernel holds at most 4 blocks of 16 tokens");
 
 // The decode kernel for TB blocks of 16 tokens (only the TB the threshold
 // allows are built).
@@ -786,8 +792,41 @@ static hipError_t launch_qkv_proj_decode(const ProjArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+#ifndef QKNORM_PROJ_SMALL_T
+#define QKNORM_PROJ_SMALL_T 256    // token counts up to this (above the decode range) take 64-row tiles
+#endif
+// 64-row tiles for small token counts: one head wide (or two heads of 64),
+// 8 waves of 16 x 64 (a head of 128 spans the two column waves), or 256
+// wide for head_dim 256; 48 KiB of LDS, so several blocks share a CU.  For
+// 17 to 256 tokens they take 38-39 us on the Qwen3-8B layer against 50-56 us
+// for 256-row tiles, which spend their MFMAs on empty rows; from about 512
+// tokens the 256-row tiles' lower operand traffic wins (56 against 76 us).
+using GeoS = Tile<64, 128, 4, 2, 64, 2>;
+using GeoS256 = Tile<64, 256, 4, 2, 64, 2>;
+
+static hipError_t launch_qkv_proj_small(const ProjArgs& a, hipStream_t s) {
+  const uint32_t N = (uint32_t)((a.hq + 2 * a.hkv) * a.head_dim);
+  const uint32_t m_tiles = (uint32_t)((a.T + GeoS::BM - 1) / GeoS::BM);
+  const uint32_t bn = a.head_dim == 256 ? GeoS256::BN : GeoS::BN;
+  const uint32_t tiles = m_tiles * ((N + bn - 1) / bn);
+  auto kern = a.dtype == kF16
+                  ? (a.head_dim == 64    ? qkv_proj_kernel<GeoS, GeoS, kF16, 64>
+                     : a.head_dim == 128 ? qkv_proj_kernel<GeoS, GeoS, kF16, 128>
+                                         : qkv_proj_kernel<GeoS256, GeoS256, kF16, 256>)
+                  : (a.head_dim == 64    ? qkv_proj_kernel<GeoS, GeoS, kBF16, 64>
+                     : a.head_dim == 128 ? qkv_proj_kernel<GeoS, GeoS, kBF16, 128>
+                                         : qkv_proj_kernel<GeoS256, GeoS256, kBF16, 256>);
+  constexpr int kSmallLds = GeoS256::kStagesBytes + (kGammaFloats + kHalfFloats) * 4;
+  const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, kSmallLds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kern, dim3(tiles), dim3(GeoS::kThreads), kSmallLds, s, kernel_args(a), tiles, N);
+  return hipGetLastError();
+}
+
 hipError_t launch_qkv_proj(const ProjArgs& a, hipStream_t s, int cus) {
   if (a.T <= QKNORM_PROJ_DECODE_T) return launch_qkv_proj_decode(a, s);
+  if (a.T <= QKNORM_PROJ_SMALL_T) return launch_qkv_proj_small(a, s);
   const uint32_t N = (uint32_t)((a.hq + 2 * a.hkv) * a.head_dim);
   const uint32_t T = (uint32_t)a.T;
   const uint32_t n_split = split_column(T, N, (uint32_t)a.head_dim, cus);

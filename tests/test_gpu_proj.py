@@ -178,10 +178,10 @@ def test_fused_equals_unfused_up_to_the_intermediate_rounding():
     assert np.array_equal(fused[:, (hq + hkv) * D:], unfused[:, (hq + hkv) * D:]), "V identical"
 
 
-# Decode sizes (T <= 32) take the one-block-per-head kernel: every head_dim,
-# token counts on and off its 16-token blocks, K chunks that do not divide
-# evenly among its K groups (or number fewer than them), and each head
-# layout; 33 to 64 tokens take the tiled kernel again.
+# Small token counts: up to 16 the one-block-per-head kernel, 17 to 256 the
+# 64-row tiles.  Every head_dim, token counts on and off the 16-token blocks,
+# K chunks that do not divide evenly among the decode kernel's K groups (or
+# number fewer than them), and each head layout.
 @pytest.mark.parametrize("dtype", [BF16, F16], ids=["bf16", "fp16"])
 @pytest.mark.parametrize("T,hidden,hq,hkv,D", [
     (1, 4096, 32, 8, 128),       # a Qwen3-8B decode step
@@ -193,7 +193,9 @@ def test_fused_equals_unfused_up_to_the_intermediate_rounding():
     (15, 448, 0, 3, 64),         # K heads only
     (16, 256, 2, 1, 256),        # head_dim 256
     (29, 576, 1, 2, 256),
-    (48, 128, 6, 2, 128),        # (tiled)
+    (48, 128, 6, 2, 128),
+    (200, 320, 5, 1, 64),        # 64-row tiles: ragged last tile, two heads of 64 per tile
+    (256, 256, 2, 2, 256),
 ])
 def test_decode_size_projection(dtype, T, hidden, hq, hkv, D):
     x, w, gq, gk = make(110 + T + D, T, hidden, hq, hkv, D, dtype=dtype)
