@@ -804,29 +804,43 @@ static hipError_t launch_qkv_proj_decode(const ProjArgs& a, hipStream_t s) {
 using GeoS = Tile<64, 128, 4, 2, 64, 2>;
 using GeoS256 = Tile<64, 256, 4, 2, 64, 2>;
 
-static hipError_t launch_qkv_proj_small(const ProjArgs& a, hipStream_t s) {
+// One launch of geometry G (G256 for head_dim 256), every block a full tile.
+template <class G, class G256>
+static hipError_t launch_qkv_proj_tiles(const ProjArgs& a, hipStream_t s) {
   const uint32_t N = (uint32_t)((a.hq + 2 * a.hkv) * a.head_dim);
-  const uint32_t m_tiles = (uint32_t)((a.T + GeoS::BM - 1) / GeoS::BM);
-  const uint32_t bn = a.head_dim == 256 ? GeoS256::BN : GeoS::BN;
+  const uint32_t m_tiles = (uint32_t)((a.T + G::BM - 1) / G::BM);
+  const uint32_t bn = a.head_dim == 256 ? G256::BN : G::BN;
   const uint32_t tiles = m_tiles * ((N + bn - 1) / bn);
   auto kern = a.dtype == kF16
-                  ? (a.head_dim == 64    ? qkv_proj_kernel<GeoS, GeoS, kF16, 64>
-                     : a.head_dim == 128 ? qkv_proj_kernel<GeoS, GeoS, kF16, 128>
-                                         : qkv_proj_kernel<GeoS256, GeoS256, kF16, 256>)
-                  : (a.head_dim == 64    ? qkv_proj_kernel<GeoS, GeoS, kBF16, 64>
-                     : a.head_dim == 128 ? qkv_proj_kernel<GeoS, GeoS, kBF16, 128>
-                                         : qkv_proj_kernel<GeoS256, GeoS256, kBF16, 256>);
-  constexpr int kSmallLds = GeoS256::kStagesBytes + (kGammaFloats + kHalfFloats) * 4;
+                  ? (a.head_dim == 64    ? qkv_proj_kernel<G, G, kF16, 64>
+                     : a.head_dim == 128 ? qkv_proj_kernel<G, G, kF16, 128>
+                                         : qkv_proj_kernel<G256, G256, kF16, 256>)
+                  : (a.head_dim == 64    ? qkv_proj_kernel<G, G, kBF16, 64>
+                     : a.head_dim == 128 ? qkv_proj_kernel<G, G, kBF16, 128>
+                                         : qkv_proj_kernel<G256, G256, kBF16, 256>);
+  constexpr int kLds = G256::kStagesBytes + (kGammaFloats + kHalfFloats) * 4;
   const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, kSmallLds);
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, dim3(tiles), dim3(GeoS::kThreads), kSmallLds, s, kernel_args(a), tiles, N);
+  hipLaunchKernelGGL(kern, dim3(tiles), dim3(G::kThreads), kLds, s, kernel_args(a), tiles, N);
   return hipGetLastError();
 }
 
+// 128-row tiles for 257 to 512 tokens: one head wide, 8 waves of 32 x 64 (a
+// head of 128 across the two column waves), or 256 wide for head_dim 256.
+// At 384 and 512 tokens 44-45 us against 56-57 us for 256-row tiles on the
+// Qwen3-8B layer; from 768 tokens the 256-row tiles are faster (57 against
+// 88 us).
+#ifndef QKNORM_PROJ_MID_T
+#define QKNORM_PROJ_MID_T 512      // token counts up to this (above the 64-row range) take 128-row tiles
+#endif
+using GeoM = Tile<128, 128, 4, 2, 64, 2>;
+using GeoM256 = Tile<128, 256, 4, 2, 64, 2>;
+
 hipError_t launch_qkv_proj(const ProjArgs& a, hipStream_t s, int cus) {
   if (a.T <= QKNORM_PROJ_DECODE_T) return launch_qkv_proj_decode(a, s);
-  if (a.T <= QKNORM_PROJ_SMALL_T) return launch_qkv_proj_small(a, s);
+  if (a.T <= QKNORM_PROJ_SMALL_T) return launch_qkv_proj_tiles<GeoS, GeoS256>(a, s);
+  if (a.T <= QKNORM_PROJ_MID_T) return launch_qkv_proj_tiles<GeoM, GeoM256>(a, s);
   const uint32_t N = (uint32_t)((a.hq + 2 * a.hkv) * a.head_dim);
   const uint32_t T = (uint32_t)a.T;
   const uint32_t n_split = split_column(T, N, (uint32_t)a.head_dim, cus);
