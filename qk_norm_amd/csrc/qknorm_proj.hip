@@ -23,6 +23,11 @@
 // accumulators are four consecutive columns of one token: one lane swap
 // then gives each lane eight consecutive outputs, stored as one 16-byte
 // write straight from registers.
+//
+// Fewer tokens take narrower launches of the same kernel (128-row tiles one
+// head wide up to 512 tokens, 64-row tiles up to 256), and up to 16 tokens
+// a separate kernel gives each head one block that reads its weight rows
+// once (qkv_proj_decode_kernel).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
