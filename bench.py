@@ -319,18 +319,22 @@ PAGES_CONTEXT = {
 }
 
 
-def bench_proj(q, torch, dev, steps, warmup, T=4096, hidden=4096, hq=32, hkv=8, D=128):
+def bench_proj(q, torch, dev, steps, warmup, T=4096, hidden=4096, hq=32, hkv=8, D=128, copies=1):
     """QKV projection of a Qwen3-8B-sized layer ([T, 4096] x [6144, 4096]^T,
     32 Q + 8 K + 8 V heads of 128): fused with per-head QK-Norm, the plain
-    projection (same kernel), torch's mm (hipBLASLt), and mm + qknorm_per_head.
-    x and w stay resident (48 MB of weight is reused call after call, as in
-    serving)."""
+    projection (same kernel), torch's mm (hipBLASLt), and mm + qknorm_per_head;
+    at decode sizes also the fused projection through a workspace.  x and w
+    stay resident; with copies > 1 the calls rotate through that many copies
+    of the 48 MB weight, so that the 256 MB Infinity Cache cannot hold it from
+    one call to the next (in a served model the other layers' weights come
+    between two calls of one layer)."""
     import numpy as np
     from qk_norm_amd import synth
     N = (hq + 2 * hkv) * D
     x = to_device(synth.make_x(90, T, hidden, synth.BF16, token_scale=(0.25, 4.0)), synth.BF16, torch, dev)
-    w = to_device(synth.to_dtype(synth.normal(91, 0, N * hidden).reshape(N, hidden) / np.sqrt(hidden),
-                                 synth.BF16), synth.BF16, torch, dev)
+    w0 = to_device(synth.to_dtype(synth.normal(91, 0, N * hidden).reshape(N, hidden) / np.sqrt(hidden),
+                                  synth.BF16), synth.BF16, torch, dev)
+    ws = [w0] + [w0.clone() for _ in range(copies - 1)]
     gq = to_device(synth.make_gamma(90, 3, D, synth.BF16), synth.BF16, torch, dev)
     gk = to_device(synth.make_gamma(90, 4, D, synth.BF16), synth.BF16, torch, dev)
     out = torch.empty(T, N, dtype=torch.bfloat16, device=dev)
@@ -338,20 +342,31 @@ def bench_proj(q, torch, dev, steps, warmup, T=4096, hidden=4096, hq=32, hkv=8, 
     lib = q.load()
     stream = torch.cuda.current_stream(dev).cuda_stream
 
+    need = q.qknorm_qkv_proj_workspace_bytes(T, hq, hkv, D)
+    space = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    wptr = [t.data_ptr() for t in ws]
+
     def proj(flags):
-        def f(_i):
-            rc = lib.qknorm_qkv_proj_per_head(x.data_ptr(), hidden, w.data_ptr(), hidden, out.data_ptr(),
+        def f(i):
+            rc = lib.qknorm_qkv_proj_per_head(x.data_ptr(), hidden, wptr[i % copies], hidden, out.data_ptr(),
                                               N, T, hidden, hq, hkv, D, gq.data_ptr(), gk.data_ptr(),
                                               1e-6, flags, synth.BF16, stream)
             if rc:
                 raise RuntimeError(q.strerror(rc))
         return f
 
-    def mm(_i):
-        torch.mm(x, w.t(), out=out2)
+    def proj_ws(i):
+        rc = lib.qknorm_qkv_proj_per_head_ws(x.data_ptr(), hidden, wptr[i % copies], hidden, out.data_ptr(),
+                                             N, T, hidden, hq, hkv, D, gq.data_ptr(), gk.data_ptr(),
+                                             1e-6, 0, synth.BF16, space.data_ptr(), need, stream)
+        if rc:
+            raise RuntimeError(q.strerror(rc))
 
-    def mm_norm(_i):
-        torch.mm(x, w.t(), out=out2)
+    def mm(i):
+        torch.mm(x, ws[i % copies].t(), out=out2)
+
+    def mm_norm(i):
+        torch.mm(x, ws[i % copies].t(), out=out2)
         rc = lib.qknorm_per_head(out2.data_ptr(), T, N, hq, hkv, D, gq.data_ptr(), gk.data_ptr(), 1e-6,
                                  synth.BF16, stream)
         if rc:
@@ -359,9 +374,11 @@ def bench_proj(q, torch, dev, steps, warmup, T=4096, hidden=4096, hq=32, hkv=8, 
 
     flops = 2.0 * T * hidden * N
     res = {"shape": {"T": T, "hidden": hidden, "N": N, "hq": hq, "hkv": hkv, "head_dim": D},
-           "flops": flops}
+           "flops": flops, "weight_copies": copies}
     variants = (("fused_proj_qknorm", proj(0)), ("plain_proj", proj(1)),
                 ("torch_mm", mm), ("torch_mm_then_qknorm", mm_norm))
+    if need:
+        variants += (("fused_proj_qknorm_ws", proj_ws),)
     # compute-bound kernels: warm every variant first (clocks), then take the
     # better of two timed rounds of each
     for _, fn in variants:
@@ -378,7 +395,7 @@ def bench_proj(q, torch, dev, steps, warmup, T=4096, hidden=4096, hq=32, hkv=8, 
         res[name] = {"mean_us": us, "tflops": flops / (us * 1e-6) / 1e12,
                      "frac_of_mfma_peak": flops / (us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS}
         log(f"proj T={T} {name}: {us:.1f} us, {res[name]['tflops']:.0f} TFLOP/s")
-    del x, w, out, out2
+    del x, w0, ws, out, out2, space
     torch.cuda.empty_cache()
     return res
 
@@ -836,13 +853,16 @@ def main():
         return
     if args.case == "proj_tokens":
         # the Qwen3-8B projection from decode sizes to prefill (one kernel per
-        # size range: one block per head up to 32 tokens, tiles above)
+        # size range: one block per head up to 16 tokens, or the split kernels
+        # through a workspace; tiles above), the weight rotating through 6
+        # copies (300 MB)
         pts = {}
-        for T in (1, 8, 32, 64, 128, 256, 512, 1024, 2048, 4096):
-            r = bench_proj(q, torch, dev, args.steps, args.warmup, T=T)
+        for T in (1, 4, 8, 16, 32, 64, 128, 256, 512, 1024, 2048, 4096):
+            r = bench_proj(q, torch, dev, args.steps, args.warmup, T=T, copies=6)
             pts[str(T)] = {k: round(r[k]["mean_us"], 2) for k in
-                           ("fused_proj_qknorm", "plain_proj", "torch_mm", "torch_mm_then_qknorm")}
-        print(json.dumps({"case": "proj_tokens", "us_per_call": pts}))
+                           ("fused_proj_qknorm", "fused_proj_qknorm_ws", "plain_proj", "torch_mm",
+                            "torch_mm_then_qknorm") if k in r}
+        print(json.dumps({"case": "proj_tokens", "weight_copies": 6, "us_per_call": pts}))
         return
     if args.case == "prefill_per_head":
         p = synth.prefill_rows(T=32768, mode="per_head")

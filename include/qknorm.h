@@ -196,6 +196,48 @@ int qknorm_qkv_proj_per_head(const void *x, int64_t ldx, const void *w, int64_t 
                              int32_t head_dim, const void *gamma_q, const void *gamma_k,
                              float eps, int32_t flags, int32_t dtype, void *stream);
 
+/*
+ * Workspace bytes qknorm_qkv_proj_per_head_ws needs for T tokens of these
+ * heads: for 1 <= T <= 16, 16*T*N bytes up to 8 tokens and 32*T*N up to 16
+ * (N = (hq + 2*hkv)*head_dim; rounded up to a multiple of 256); 0 for other
+ * T, which need none.  Negative on error: QKNORM_E_SHAPE for a negative T,
+ * hq or hkv or head_dim <= 0, QKNORM_E_UNSUPPORTED for T or N beyond the
+ * projection's limits.  Host only; no HIP call.
+ */
+int64_t qknorm_qkv_proj_workspace_bytes(int64_t T, int32_t hq, int32_t hkv, int32_t head_dim);
+
+/*
+ * qknorm_qkv_proj_per_head with a workspace, for decode sizes.
+ * At 1 <= T <= 16 the projection is a stream over the weight (N x hidden,
+ * each element read once), and one block per head cannot read it at the
+ * chip's rate.  With a workspace the weight is cut into narrow column groups
+ * by slices of hidden, one block each, which leave fp32 partial sums in the
+ * workspace; a second launch on the same stream adds each output's partials
+ * in slice order, normalises each Q and K head of every row and stores.
+ * The result has the definition of qknorm_qkv_proj_per_head (fp32
+ * accumulation, per-head QK-Norm on the fp32 sums, one rounding); the fp32
+ * additions come in another order, so the two calls may differ in the last
+ * bit.  For any other T the call is qknorm_qkv_proj_per_head and the
+ * workspace is not used (it may be NULL).
+ * (Lesson "Explain combined QKV projection and why it's faster than three
+ *  separate projections?", sections "With GQA" and "Why it is faster": one
+ *  projection split into Q, K and V heads; at decode sizes it is bound by
+ *  memory traffic, not arithmetic.)
+ *
+ * workspace: device memory owned by the caller, 16-byte aligned, at least
+ * qknorm_qkv_proj_workspace_bytes(T, hq, hkv, head_dim) bytes, given in
+ * workspace_bytes (less: QKNORM_E_SHAPE; NULL: QKNORM_E_NULLPTR; misaligned:
+ * QKNORM_E_ALIGN).  Its contents on entry do not matter and afterwards hold
+ * partial sums.  It must not overlap x, w, gamma or qkv, and must not serve
+ * two calls that can run at the same time (calls on different streams).
+ * All other arguments and errors as for qknorm_qkv_proj_per_head.
+ */
+int qknorm_qkv_proj_per_head_ws(const void *x, int64_t ldx, const void *w, int64_t ldw, void *qkv,
+                                int64_t ld, int64_t T, int64_t hidden, int32_t hq, int32_t hkv,
+                                int32_t head_dim, const void *gamma_q, const void *gamma_k,
+                                float eps, int32_t flags, int32_t dtype, void *workspace,
+                                int64_t workspace_bytes, void *stream);
+
 /* Static description of a return code; never NULL. */
 const char *qknorm_strerror(int code);
 

@@ -43,8 +43,8 @@ QKNORM_E_HIP = -7
 QKNORM_PROJ_PLAIN = 1
 
 EXPORTED = ("qknorm_per_head", "qknorm_layerwise", "qknorm_partial_sumsq",
-            "qknorm_apply_scalar", "qknorm_qkv_proj_per_head", "qknorm_strerror",
-            "qknorm_abi_version")
+            "qknorm_apply_scalar", "qknorm_qkv_proj_per_head", "qknorm_qkv_proj_workspace_bytes",
+            "qknorm_qkv_proj_per_head_ws", "qknorm_strerror", "qknorm_abi_version")
 
 _lib = None
 
@@ -71,8 +71,13 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.qknorm_apply_scalar.argtypes = [P, I64, I64, I64, I64, P, P, I32, I64, I64, P, P, F, I32, P]
     lib.qknorm_qkv_proj_per_head.argtypes = [P, I64, P, I64, P, I64, I64, I64, I32, I32, I32, P, P,
                                              F, I32, I32, P]
+    lib.qknorm_qkv_proj_workspace_bytes.argtypes = [I64, I32, I32, I32]
+    lib.qknorm_qkv_proj_workspace_bytes.restype = I64
+    lib.qknorm_qkv_proj_per_head_ws.argtypes = [P, I64, P, I64, P, I64, I64, I64, I32, I32, I32, P, P,
+                                                F, I32, I32, P, I64, P]
     for name in ("qknorm_per_head", "qknorm_layerwise", "qknorm_partial_sumsq",
-                 "qknorm_apply_scalar", "qknorm_qkv_proj_per_head", "qknorm_abi_version"):
+                 "qknorm_apply_scalar", "qknorm_qkv_proj_per_head", "qknorm_qkv_proj_per_head_ws",
+                 "qknorm_abi_version"):
         getattr(lib, name).restype = I32
     lib.qknorm_strerror.argtypes = [ctypes.c_int]
     lib.qknorm_strerror.restype = ctypes.c_char_p
@@ -94,6 +99,7 @@ class _CtypesCalls:
         self.partial_sumsq = lib.qknorm_partial_sumsq
         self.apply_scalar = lib.qknorm_apply_scalar
         self.qkv_proj_per_head = lib.qknorm_qkv_proj_per_head
+        self.qkv_proj_per_head_ws = lib.qknorm_qkv_proj_per_head_ws
 
     @staticmethod
     def per_head_t(*_):
@@ -292,15 +298,9 @@ def _matrix(t, dev, what):
     return _ptr(t, dev), t.stride(0) if t.shape[0] > 1 else max(t.stride(0), t.shape[1])
 
 
-def qknorm_qkv_proj_per_head(x, w, qkv, hq: int, hkv: int, head_dim: int, gamma_q=None,
-                             gamma_k=None, eps: float = 1e-6, plain: bool = False,
-                             stream=None) -> None:
-    """qkv[:, :N] = x @ w.T with each Q and K head RMS-normalised in the epilogue.
-
-    x [T, hidden], w [N, hidden] (N = (hq + 2*hkv) * head_dim) and qkv [T, >= N],
-    all bfloat16 or all float16 (gamma too) on one GPU; plain=True gives the
-    projection alone.
-    """
+def _proj_args(x, w, qkv, hq, hkv, head_dim, gamma_q, gamma_k, eps, plain):
+    """The C ABI's arguments of a projection call up to `dtype` (the stream is
+    added by the caller)."""
     if not qkv.is_cuda:
         raise ValueError("qkv must be a GPU tensor (the library has no CPU path)")
     dev = qkv.get_device()
@@ -311,13 +311,51 @@ def qknorm_qkv_proj_per_head(x, w, qkv, hq: int, hkv: int, head_dim: int, gamma_
         raise ValueError("x, w and qkv must share the dtype")
     if x.shape[0] != qkv.shape[0] or x.shape[1] != w.shape[1]:
         raise ValueError("x [T, hidden], w [N, hidden] and qkv [T, >= N] do not match")
-    rc = _calls().qkv_proj_per_head(
-        xp, ldx, wp, ldw, op, ld, x.shape[0], x.shape[1], hq, hkv, head_dim,
-        None if plain else _gamma(gamma_q, qkv, dev), None if plain else _gamma(gamma_k, qkv, dev),
-        eps, QKNORM_PROJ_PLAIN if plain else 0, _dtype_code(qkv), _stream(stream, dev))
+    return dev, (xp, ldx, wp, ldw, op, ld, x.shape[0], x.shape[1], hq, hkv, head_dim,
+                 None if plain else _gamma(gamma_q, qkv, dev), None if plain else _gamma(gamma_k, qkv, dev),
+                 eps, QKNORM_PROJ_PLAIN if plain else 0, _dtype_code(qkv))
+
+
+def qknorm_qkv_proj_per_head(x, w, qkv, hq: int, hkv: int, head_dim: int, gamma_q=None,
+                             gamma_k=None, eps: float = 1e-6, plain: bool = False,
+                             stream=None) -> None:
+    """qkv[:, :N] = x @ w.T with each Q and K head RMS-normalised in the epilogue.
+
+    x [T, hidden], w [N, hidden] (N = (hq + 2*hkv) * head_dim) and qkv [T, >= N],
+    all bfloat16 or all float16 (gamma too) on one GPU; plain=True gives the
+    projection alone.
+    """
+    dev, args = _proj_args(x, w, qkv, hq, hkv, head_dim, gamma_q, gamma_k, eps, plain)
+    rc = _calls().qkv_proj_per_head(*args, _stream(stream, dev))
     _raise(rc, "qknorm_qkv_proj_per_head")
 
 
-__all__ = ["qknorm_per_head", "qknorm_qkv_proj_per_head", "qknorm_layerwise", "qknorm_partial_sumsq", "qknorm_apply_scalar",
+def qknorm_qkv_proj_workspace_bytes(T: int, hq: int, hkv: int, head_dim: int) -> int:
+    """Bytes of workspace qknorm_qkv_proj_per_head_ws needs (0: none)."""
+    n = int(load().qknorm_qkv_proj_workspace_bytes(int(T), int(hq), int(hkv), int(head_dim)))
+    if n < 0:
+        _raise(n, "qknorm_qkv_proj_workspace_bytes")
+    return n
+
+
+def qknorm_qkv_proj_per_head_ws(x, w, qkv, hq: int, hkv: int, head_dim: int, gamma_q=None,
+                                gamma_k=None, eps: float = 1e-6, plain: bool = False,
+                                workspace=None, stream=None) -> None:
+    """qknorm_qkv_proj_per_head with a workspace: a GPU tensor of at least
+    qknorm_qkv_proj_workspace_bytes(T, hq, hkv, head_dim) bytes, contiguous, on
+    qkv's device, that no other call uses meanwhile (None where that is 0)."""
+    dev, args = _proj_args(x, w, qkv, hq, hkv, head_dim, gamma_q, gamma_k, eps, plain)
+    if workspace is None:
+        wsp, nbytes = None, 0
+    else:
+        if not workspace.is_contiguous():
+            raise ValueError("workspace must be contiguous")
+        wsp, nbytes = _ptr(workspace, dev), workspace.numel() * workspace.element_size()
+    rc = _calls().qkv_proj_per_head_ws(*args, wsp, nbytes, _stream(stream, dev))
+    _raise(rc, "qknorm_qkv_proj_per_head_ws")
+
+
+__all__ = ["qknorm_per_head", "qknorm_qkv_proj_per_head", "qknorm_qkv_proj_per_head_ws",
+           "qknorm_qkv_proj_workspace_bytes", "qknorm_layerwise", "qknorm_partial_sumsq", "qknorm_apply_scalar",
            "strerror", "abi_version", "load", "QKNormError", "QKNORM_F32", "QKNORM_BF16", "QKNORM_F16",
            "QKNORM_FP8_E4M3"]

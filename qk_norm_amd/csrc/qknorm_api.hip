@@ -82,6 +82,43 @@ int device_cus(int* cus) {
   return QKNORM_OK;
 }
 
+// Everything qknorm_qkv_proj_per_head and its workspace form check before
+// any HIP call; on success *a holds the launch arguments and *n the output
+// column count N.
+int check_proj(const void* x, int64_t ldx, const void* w, int64_t ldw, void* qkv, int64_t ld,
+               int64_t T, int64_t hidden, int32_t hq, int32_t hkv, int32_t head_dim,
+               const void* gamma_q, const void* gamma_k, float eps, int32_t flags, int32_t dtype,
+               qknorm::ProjArgs* a, int64_t* n) {
+  int rc = check_common(dtype, eps, T, ld);
+  if (rc) return rc;
+  if (dtype != QKNORM_BF16 && dtype != QKNORM_F16) return QKNORM_E_UNSUPPORTED;
+  if ((flags & ~QKNORM_PROJ_PLAIN) != 0) return QKNORM_E_UNSUPPORTED;
+  if (hidden <= 0 || hq < 0 || hkv < 0 || head_dim <= 0 || ldx < hidden || ldw < hidden)
+    return QKNORM_E_SHAPE;
+  // N of any int32 head counts and head_dim fits 128 bits; N <= ld then fits int64
+  const __int128 n_wide = ((__int128)hq + 2 * (__int128)hkv) * head_dim;
+  if (n_wide > ld) return QKNORM_E_SHAPE;
+  const int64_t N = (int64_t)n_wide;
+  const bool norm = (flags & QKNORM_PROJ_PLAIN) == 0;
+  const bool touched = T > 0 && N > 0;
+  if (touched && (x == nullptr || w == nullptr || qkv == nullptr)) return QKNORM_E_NULLPTR;
+  if (norm && (rc = check_gamma(gamma_q, hq, T))) return rc;
+  if (norm && (rc = check_gamma(gamma_k, hkv, T))) return rc;
+  if (touched && (!aligned16(x) || !aligned16(w) || !aligned16(qkv))) return QKNORM_E_ALIGN;
+  // 16-byte row pitches: a multiple of 8 two-byte elements
+  if (ldx % 8 != 0 || ldw % 8 != 0 || ld % 8 != 0) return QKNORM_E_ALIGN;
+  // every pitch within 64 MiB before any product is formed from it (the
+  // kernel's own limits, checked next, are tighter still)
+  if (ld > kMaxPitchBytes / 2 || ldx > kMaxPitchBytes / 2 || ldw > kMaxPitchBytes / 2 ||
+      T * (ld + 1) > (INT64_C(1) << 46) || N >= (INT64_C(1) << 24))
+    return QKNORM_E_UNSUPPORTED;
+  *a = qknorm::ProjArgs{x, ldx, w, ldw, qkv, ld, T, hidden, hq, hkv, head_dim, gamma_q, gamma_k,
+                        eps, flags, dtype};
+  if (!qknorm::proj_shape_ok(*a)) return QKNORM_E_UNSUPPORTED;
+  *n = N;
+  return QKNORM_OK;
+}
+
 int finish(hipError_t e) { return e == hipSuccess ? QKNORM_OK : QKNORM_E_HIP; }
 
 }  // namespace
@@ -194,33 +231,44 @@ int qknorm_qkv_proj_per_head(const void* x, int64_t ldx, const void* w, int64_t 
                              int64_t ld, int64_t T, int64_t hidden, int32_t hq, int32_t hkv,
                              int32_t head_dim, const void* gamma_q, const void* gamma_k, float eps,
                              int32_t flags, int32_t dtype, void* stream) {
-  int rc = check_common(dtype, eps, T, ld);
+  qknorm::ProjArgs a;
+  int64_t N = 0;
+  int rc = check_proj(x, ldx, w, ldw, qkv, ld, T, hidden, hq, hkv, head_dim, gamma_q, gamma_k, eps,
+                      flags, dtype, &a, &N);
   if (rc) return rc;
-  if (dtype != QKNORM_BF16 && dtype != QKNORM_F16) return QKNORM_E_UNSUPPORTED;
-  if ((flags & ~QKNORM_PROJ_PLAIN) != 0) return QKNORM_E_UNSUPPORTED;
-  if (hidden <= 0 || hq < 0 || hkv < 0 || head_dim <= 0 || ldx < hidden || ldw < hidden)
-    return QKNORM_E_SHAPE;
-  // N of any int32 head counts and head_dim fits 128 bits; N <= ld then fits int64
+  if (T == 0 || N == 0) return QKNORM_OK;
+  int cus = 0;
+  if ((rc = device_cus(&cus))) return rc;
+  return finish(qknorm::launch_qkv_proj(a, static_cast<hipStream_t>(stream), cus));
+}
+
+int64_t qknorm_qkv_proj_workspace_bytes(int64_t T, int32_t hq, int32_t hkv, int32_t head_dim) {
+  if (T < 0 || hq < 0 || hkv < 0 || head_dim <= 0) return QKNORM_E_SHAPE;
+  if (T > kMaxRows) return QKNORM_E_UNSUPPORTED;
   const __int128 n_wide = ((__int128)hq + 2 * (__int128)hkv) * head_dim;
-  if (n_wide > ld) return QKNORM_E_SHAPE;
-  const int64_t N = (int64_t)n_wide;
-  const bool norm = (flags & QKNORM_PROJ_PLAIN) == 0;
-  const bool touched = T > 0 && N > 0;
-  if (touched && (x == nullptr || w == nullptr || qkv == nullptr)) return QKNORM_E_NULLPTR;
-  if (norm && (rc = check_gamma(gamma_q, hq, T))) return rc;
-  if (norm && (rc = check_gamma(gamma_k, hkv, T))) return rc;
-  if (touched && (!aligned16(x) || !aligned16(w) || !aligned16(qkv))) return QKNORM_E_ALIGN;
-  // 16-byte row pitches: a multiple of 8 two-byte elements
-  if (ldx % 8 != 0 || ldw % 8 != 0 || ld % 8 != 0) return QKNORM_E_ALIGN;
-  // every pitch within 64 MiB before any product is formed from it (the
-  // kernel's own limits, checked next, are tighter still)
-  if (ld > kMaxPitchBytes / 2 || ldx > kMaxPitchBytes / 2 || ldw > kMaxPitchBytes / 2 ||
-      T * (ld + 1) > (INT64_C(1) << 46) || N >= (INT64_C(1) << 24))
-    return QKNORM_E_UNSUPPORTED;
-  qknorm::ProjArgs a{x, ldx, w, ldw, qkv, ld, T, hidden, hq, hkv, head_dim, gamma_q, gamma_k,
-                     eps, flags, dtype};
-  if (!qknorm::proj_shape_ok(a)) return QKNORM_E_UNSUPPORTED;
-  if (!touched) return QKNORM_OK;
+  if (n_wide >= (INT64_C(1) << 24)) return QKNORM_E_UNSUPPORTED;
+  return qknorm::proj_workspace_bytes(T, (int64_t)n_wide);
+}
+
+int qknorm_qkv_proj_per_head_ws(const void* x, int64_t ldx, const void* w, int64_t ldw, void* qkv,
+                                int64_t ld, int64_t T, int64_t hidden, int32_t hq, int32_t hkv,
+                                int32_t head_dim, const void* gamma_q, const void* gamma_k,
+                                float eps, int32_t flags, int32_t dtype, void* workspace,
+                                int64_t workspace_bytes, void* stream) {
+  qknorm::ProjArgs a;
+  int64_t N = 0;
+  int rc = check_proj(x, ldx, w, ldw, qkv, ld, T, hidden, hq, hkv, head_dim, gamma_q, gamma_k, eps,
+                      flags, dtype, &a, &N);
+  if (rc) return rc;
+  if (workspace_bytes < 0) return QKNORM_E_SHAPE;
+  const int64_t need = qknorm::proj_workspace_bytes(T, N);
+  if (need > 0) {
+    if (workspace == nullptr) return QKNORM_E_NULLPTR;
+    if (!aligned16(workspace)) return QKNORM_E_ALIGN;
+    if (workspace_bytes < need) return QKNORM_E_SHAPE;
+  }
+  if (T == 0 || N == 0) return QKNORM_OK;
+  if (need > 0) return finish(qknorm::launch_qkv_proj_split(a, workspace, static_cast<hipStream_t>(stream)));
   int cus = 0;
   if ((rc = device_cus(&cus))) return rc;
   return finish(qknorm::launch_qkv_proj(a, static_cast<hipStream_t>(stream), cus));

@@ -75,4 +75,14 @@ hipError_t launch_partial_sumsq(const PartialArgs& a, hipStream_t s, int cus);
 hipError_t launch_apply_scalar(const ApplyArgs& a, hipStream_t s, int cus);
 hipError_t launch_qkv_proj(const ProjArgs& a, hipStream_t s, int cus);
 
+// Token counts up to this take the split projection when the caller gives a
+// workspace (or the library's own scratch).
+constexpr int64_t kProjSplitMaxT = 16;
+// Bytes of fp32 partials the split projection needs for T tokens and N
+// output columns (0 where T is outside 1..kProjSplitMaxT).
+int64_t proj_workspace_bytes(int64_t T, int64_t N);
+// The split projection: partial sums into `workspace`, then one block per
+// head adds them and normalises (two launches on `s`).
+hipError_t launch_qkv_proj_split(const ProjArgs& a, void* workspace, hipStream_t s);
+
 }  // namespace qknorm

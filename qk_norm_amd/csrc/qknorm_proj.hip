@@ -671,6 +671,130 @@ __global__ __launch_bounds__(512) void qkv_proj_decode_kernel(ProjKArgs args) {
   }
 }
 
+// Decode sizes through a workspace (T <= 16).  The kernel above gives a
+// head's D columns to one block, and one block reads at most 30-50 GB/s.
+// Here the weight is cut into 16 * JB columns by KS slices of K, one block
+// of 4 waves each (for a Qwen3-8B layer 1536 blocks up to 8 tokens, 1536 of
+// 32 columns up to 16), so the whole chip streams it.  Each wave takes a
+// quarter of its block's slice with the same MFMA (the weight's fragment
+// first, fragments straight from global memory PF - 1 chunks ahead, none
+// past the slice's end); the four waves' sums meet in LDS and are added in
+// wave order; the block stores them as fp32 partials part[ks][t][n].  A
+// second kernel, one block per head, adds each output's KS partials in
+// slice order, normalises the head's rows and stores them.  Rows past T read
+// zeros and store nothing.  One kernel in which the last block of a head to
+// finish did the norm was measured slower: with agent-scope release fences
+// 5-20 times, and with the partials written and read through
+// device-coherent stores and loads ahead of a counter still 15-25 %, since
+// each block then waits for its writes to reach memory before its CU takes
+// the next block.
+template <int DT, int D, int KS, int JB, int PF>
+__global__ __launch_bounds__(256) void qkv_proj_split_kernel(ProjKArgs args, float* __restrict__ part) {
+  constexpr int CB = 16 * JB;                    // columns per block
+  static_assert(D % CB == 0 && PF >= 2, "");
+  __shared__ __attribute__((aligned(16))) float red[4][16][CB + 4];
+  typedef typename ProjElem<DT>::V8 Frag;
+  const uint32_t tid = threadIdx.x, lane = tid & 63, wave = uniform(tid >> 6);
+  const uint32_t ks = blockIdx.x % KS, n0 = blockIdx.x / KS * CB;
+  const uint32_t T = args.T, K = args.K, N = args.N;
+  const uint32_t nk = K / 32;                    // 32-wide K chunks; the block takes [b0, b1)
+  const uint32_t b0 = ks * nk / KS, b1 = (ks + 1) * nk / KS;
+  const uint32_t c0 = b0 + wave * (b1 - b0) / 4, c1 = b0 + (wave + 1) * (b1 - b0) / 4;
+  const uint32_t fr = lane % 16, fk = 8 * (lane / 16);
+  const Rsrc rw = make_rsrc(args.w + (uint64_t)n0 * args.ldw_bytes, (uint64_t)(CB - 1) * args.ldw_bytes + K * 2);
+  const Rsrc rx = make_rsrc(args.x, (uint64_t)(T - 1) * args.ldx_bytes + K * 2);
+  const uint32_t wo = fr * args.ldw_bytes + fk * 2, xo = fr * args.ldx_bytes + fk * 2;
+  f32x4 acc[JB];
+#pragma unroll
+  for (int j = 0; j < JB; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  {
+    Frag wf[PF][JB], xf[PF];
+    auto load = [&](int p, uint32_t c) {
+#pragma unroll
+      for (int j = 0; j < JB; ++j)
+        wf[p][j] = __builtin_bit_cast(
+            Frag, __builtin_amdgcn_raw_buffer_load_b128(rw, wo + j * 16 * args.ldw_bytes, c * 64, 0));
+      xf[p] = __builtin_bit_cast(Frag, __builtin_amdgcn_raw_buffer_load_b128(rx, xo, c * 64, 0));
+    };
+#pragma unroll
+    for (int p = 0; p < PF - 1; ++p)
+      if (c0 + p < c1) load(p, c0 + p);
+    for (uint32_t c = c0; c < c1; c += PF) {
+#pragma unroll
+      for (int p = 0; p < PF; ++p) {
+        if (c + p + PF - 1 < c1) load((p + PF - 1) % PF, c + p + PF - 1);
+        if (c + p < c1) {
+#pragma unroll
+          for (int j = 0; j < JB; ++j) acc[j] = ProjElem<DT>::mfma(wf[p][j], xf[p], acc[j]);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < JB; ++j) *reinterpret_cast<f32x4*>(&red[wave][fr][16 * j + 4 * (lane / 16)]) = acc[j];
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < JB; ++j) {
+    const uint32_t i = tid + 256 * j, tok = i / CB, col = i % CB;
+    if (tok < T)
+      part[((uint64_t)ks * T + tok) * N + n0 + col] =
+          ((red[0][tok][col] + red[1][tok][col]) + red[2][tok][col]) + red[3][tok][col];
+  }
+}
+
+// One block per head: 16 threads per token, E = D / 16 consecutive columns
+// each; the KS partials of a column are added in slice order, then the
+// token's head is normalised (Q and K heads, unless plain) and stored.
+template <int DT, int D, int KS>
+__global__ __launch_bounds__(256) void qkv_proj_split_finish_kernel(ProjKArgs args,
+                                                                     const float* __restrict__ part) {
+  constexpr int E = D / 16;
+  typedef typename ProjElem<DT>::T Elem;
+  const uint32_t tid = threadIdx.x, head = blockIdx.x, tok = tid / 16, q = tid % 16;
+  const uint32_t T = args.T, N = args.N, n = head * D + E * q;
+  float v[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) v[e] = 0.f;
+  if (tok < T) {
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const float* p = part + ((uint64_t)s * T + tok) * N + n;
+#pragma unroll
+      for (int e = 0; e < E; e += 4) {
+        const f32x4 f = *reinterpret_cast<const f32x4*>(p + e);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[e + i] += f[i];
+      }
+    }
+  }
+  if (args.norm && head < args.hq + args.hkv) {
+    // every lane of a token's 16 takes part, rows past T with zeros
+    const Elem* g = reinterpret_cast<const Elem*>(head < args.hq ? args.gamma_q : args.gamma_k) + E * q;
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) ss = __builtin_fmaf(v[e], v[e], ss);
+    const float sc = rms_scale(group_sum<16>(ss), args.inv_d, args.eps);
+#pragma unroll
+    for (int e = 0; e < E; ++e) v[e] = (v[e] * (float)g[e]) * sc;
+  }
+  if (tok < T) {
+    const Rsrc ro = make_rsrc(args.out + (uint64_t)head * D * 2, (uint64_t)(T - 1) * args.ld_bytes + D * 2);
+    const uint32_t off = tok * (uint32_t)args.ld_bytes + q * E * 2;
+    if constexpr (E == 4) {
+      typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+      const u32x2 o = {pack2<DT>(v[0], v[1]), pack2<DT>(v[2], v[3])};
+      __builtin_amdgcn_raw_buffer_store_b64(o, ro, off, 0, kStorePolicy);
+    } else {
+#pragma unroll
+      for (int e = 0; e < E; e += 8) {
+        const u32x4 o = {pack2<DT>(v[e], v[e + 1]), pack2<DT>(v[e + 2], v[e + 3]),
+                         pack2<DT>(v[e + 4], v[e + 5]), pack2<DT>(v[e + 6], v[e + 7])};
+        __builtin_amdgcn_raw_buffer_store_b128(o, ro, off + e * 2, 0, kStorePolicy);
+      }
+    }
+  }
+}
+
 // 256 x 256 tiles of 8 waves (4 along M, 2 along N), each wave 64 x 128 as
 // 4 x 8 blocks of 16 x 16: 12 fragment reads per 32 MFMAs and 131 flop per
 // byte of operand staged, the best of the shapes measured on MI355X.  The
@@ -841,6 +965,60 @@ static hipError_t launch_qkv_proj_tiles(const ProjArgs& a, hipStream_t s) {
 #endif
 using GeoM = Tile<128, 128, 4, 2, 64, 2>;
 using GeoM256 = Tile<128, 256, 4, 2, 64, 2>;
+
+// The split geometry for a decode-size token count: up to 8 tokens 16
+// columns by 4 slices of K (1536 blocks for the Qwen3-8B layer; with the
+// norm kernel 12.1 us per call at T = 1 and 14.8 us at T = 8, against 12.2
+// and 14.9 us with 8 slices), up to 16 tokens 32 columns by 8 slices, which
+// halves the activation fragments loaded per weight fragment (17.2 against
+// 18.5 us at T = 16).
+struct SplitGeo {
+  uint32_t ks, jb;
+};
+static SplitGeo split_geo(int64_t T) { return T <= 8 ? SplitGeo{4, 1} : SplitGeo{8, 2}; }
+
+int64_t proj_workspace_bytes(int64_t T, int64_t N) {
+  if (T <= 0 || T > kProjSplitMaxT || N <= 0) return 0;
+  const int64_t b = (int64_t)split_geo(T).ks * T * N * 4;
+  return (b + 255) & ~(int64_t)255;
+}
+
+typedef void (*SplitKernel)(ProjKArgs, float*);
+typedef void (*FinishKernel)(ProjKArgs, const float*);
+
+template <int DT, int D>
+static void split_kernels(uint32_t ks, SplitKernel* k1, FinishKernel* k2) {
+  if (ks == 4) {
+    *k1 = qkv_proj_split_kernel<DT, D, 4, 1, 8>;
+    *k2 = qkv_proj_split_finish_kernel<DT, D, 4>;
+  } else {
+    *k1 = qkv_proj_split_kernel<DT, D, 8, 2, 4>;
+    *k2 = qkv_proj_split_finish_kernel<DT, D, 8>;
+  }
+}
+
+template <int DT>
+static void split_kernels_dt(int head_dim, uint32_t ks, SplitKernel* k1, FinishKernel* k2) {
+  if (head_dim == 64) split_kernels<DT, 64>(ks, k1, k2);
+  else if (head_dim == 128) split_kernels<DT, 128>(ks, k1, k2);
+  else split_kernels<DT, 256>(ks, k1, k2);
+}
+
+hipError_t launch_qkv_proj_split(const ProjArgs& a, void* workspace, hipStream_t s) {
+  const SplitGeo g = split_geo(a.T);
+  const uint32_t N = (uint32_t)((a.hq + 2 * a.hkv) * a.head_dim);
+  SplitKernel k1;
+  FinishKernel k2;
+  if (a.dtype == kF16) split_kernels_dt<kF16>(a.head_dim, g.ks, &k1, &k2);
+  else split_kernels_dt<kBF16>(a.head_dim, g.ks, &k1, &k2);
+  const ProjKArgs k = kernel_args(a);
+  float* part = static_cast<float*>(workspace);
+  hipLaunchKernelGGL(k1, dim3(N / (16 * g.jb) * g.ks), dim3(256), 0, s, k, part);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k2, dim3(N / (uint32_t)a.head_dim), dim3(256), 0, s, k, (const float*)part);
+  return hipGetLastError();
+}
 
 hipError_t launch_qkv_proj(const ProjArgs& a, hipStream_t s, int cus) {
   if (a.T <= QKNORM_PROJ_DECODE_T) return launch_qkv_proj_decode(a, s);

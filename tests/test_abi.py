@@ -240,6 +240,40 @@ def test_projection_validation(lib):
     assert pj(lib, ldw=(1 << 22) + 8, T=0) == q.QKNORM_E_UNSUPPORTED
 
 
+def pjw(lib, ws=A16, wsb=1 << 30, x=A16, ldx=256, w=A16, ldw=256, out=A16, ld=768, T=4, hidden=256,
+        hq=2, hkv=2, D=128, gq=A16, gk=A16, eps=1e-6, flags=0, dt=BF16):
+    return lib.qknorm_qkv_proj_per_head_ws(x, ldx, w, ldw, out, ld, T, hidden, hq, hkv, D, gq, gk,
+                                           eps, flags, dt, ws, wsb, None)
+
+
+def test_projection_workspace_size_and_validation(lib):
+    f = lib.qknorm_qkv_proj_workspace_bytes
+    N = (32 + 2 * 8) * 128                                 # a Qwen3-8B layer
+    assert f(1, 32, 8, 128) == 4 * 1 * N * 4               # up to 8 tokens: 4 slices of K
+    assert f(8, 32, 8, 128) == 4 * 8 * N * 4
+    assert f(9, 32, 8, 128) == 8 * 9 * N * 4               # 9 to 16: 8 slices
+    assert f(16, 32, 8, 128) == 8 * 16 * N * 4
+    assert f(1, 1, 1, 1) == 256                            # 48 bytes, rounded up to 256
+    assert f(0, 32, 8, 128) == 0 and f(17, 32, 8, 128) == 0 and f(4096, 32, 8, 128) == 0
+    assert f(-1, 1, 0, 64) == q.QKNORM_E_SHAPE
+    assert f(1, -1, 0, 64) == q.QKNORM_E_SHAPE
+    assert f(1, 1, 0, 0) == q.QKNORM_E_SHAPE
+    m = (1 << 31) - 1
+    assert f(1, m, m, m) == q.QKNORM_E_UNSUPPORTED
+    assert f(1 << 40, 1, 0, 64) == q.QKNORM_E_UNSUPPORTED
+    # the workspace form: the projection's own checks first, then the workspace's
+    need = 4 * 4 * 768 * 4
+    assert pjw(lib, dt=F32) == q.QKNORM_E_UNSUPPORTED
+    assert pjw(lib, ld=767) == q.QKNORM_E_SHAPE
+    assert pjw(lib, x=None) == q.QKNORM_E_NULLPTR
+    assert pjw(lib, ws=None, wsb=need) == q.QKNORM_E_NULLPTR
+    assert pjw(lib, ws=A16 + 8, wsb=need) == q.QKNORM_E_ALIGN
+    assert pjw(lib, wsb=need - 1) == q.QKNORM_E_SHAPE
+    assert pjw(lib, wsb=-1) == q.QKNORM_E_SHAPE
+    assert pjw(lib, T=0, ws=None, wsb=0) == q.QKNORM_OK   # validated, nothing launched
+    assert pjw(lib, T=0, ws=None, wsb=-1) == q.QKNORM_E_SHAPE
+
+
 def test_sizes_whose_products_overflow_64_bits_are_rejected(lib):
     # pitches, widths and head counts near the int64 / int32 limits: each is
     # rejected by value, before any product of it is formed (a product that
@@ -295,6 +329,8 @@ def test_python_call_module_forwards_to_the_same_library(lib):
     assert f.qkv_proj_per_head(A16, 4096, A16, 4096, A16, 6144, 16, 4096, 32, 8, 128, A16, A16, 1e-6, 0,
                                F32, None) == q.QKNORM_E_UNSUPPORTED
     assert f.per_head(A16, 0, 6144, 48, 0, 128, A16, None, float("nan"), BF16, None) == q.QKNORM_E_EPS
+    assert f.qkv_proj_per_head_ws(A16, 4096, A16, 4096, A16, 6144, 16, 4096, 32, 8, 128, A16, A16, 1e-6,
+                                  0, BF16, None, 1 << 30, None) == q.QKNORM_E_NULLPTR
     with pytest.raises(TypeError):
         f.per_head(A16, 4)
     with pytest.raises(OverflowError):

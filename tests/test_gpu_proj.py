@@ -64,21 +64,32 @@ def tolerance(x, w, y64, gq, gk, hq, hkv, D, norm=True, dtype=BF16):
     return tol
 
 
-def run_proj(x, w, hq, hkv, D, gq, gk, eps, ld=None, plain=False, label="", dtype=BF16):
+def run_proj(x, w, hq, hkv, D, gq, gk, eps, ld=None, plain=False, label="", dtype=BF16, ws=False):
+    """One call through the C ABI; ws=True takes qknorm_qkv_proj_per_head_ws with
+    a workspace of exactly the size asked for, filled with NaN bytes, and
+    checks the bytes after it untouched."""
     T, hidden = x.shape
     N = w.shape[0]
     ld = ld or N
     print(f"[proj] {label} T={T} hidden={hidden} hq={hq} hkv={hkv} D={D} ld={ld} plain={plain} "
-          f"{synth.DTYPE_NAMES[dtype]}", flush=True)
+          f"ws={ws} {synth.DTYPE_NAMES[dtype]}", flush=True)
     xt, wt = host_to_device(x, dtype), host_to_device(w, dtype)
     nan = 0x7FC0 if dtype == BF16 else 0x7E00
     fill = np.full((T, ld), nan, dtype=np.uint16)               # NaN: must be overwritten or kept
     out = Guarded(fill, dtype)
-    q.qknorm_qkv_proj_per_head(xt, wt, out.t, hq, hkv, D, gamma_to_device(gq, dtype),
-                               gamma_to_device(gk, dtype) if hkv else None, eps, plain=plain)
+    g1, g2 = gamma_to_device(gq, dtype), gamma_to_device(gk, dtype) if hkv else None
+    if ws:
+        need = q.qknorm_qkv_proj_workspace_bytes(T, hq, hkv, D)
+        space = torch.full((need + GUARD_BYTES,), 0xFF, dtype=torch.uint8, device="cuda")
+        q.qknorm_qkv_proj_per_head_ws(xt, wt, out.t, hq, hkv, D, g1, g2, eps, plain=plain,
+                                      workspace=space[:need] if need else None)
+    else:
+        q.qknorm_qkv_proj_per_head(xt, wt, out.t, hq, hkv, D, g1, g2, eps, plain=plain)
     torch.cuda.synchronize()
     got = out.host()
     assert out.guards_intact(), "write outside the output"
+    if ws:
+        assert bool((space[need:] == 0xFF).all()), "write past the workspace"
     assert_bytes_equal(got[:, N:], fill[:, N:], f"{label}: columns past N")
     return got[:, :N]
 
@@ -207,22 +218,82 @@ def test_decode_size_projection(dtype, T, hidden, hq, hkv, D):
     check(x, w, hq, hkv, D, gq, gk, eps, got, plain=True, label=f"decode plain T={T} D={D}", dtype=dtype)
 
 
-@pytest.mark.parametrize("T", [200, 8], ids=["tiled", "decode"])
-def test_deterministic_and_graph_replay(T):
+# Small token counts through the workspace form: up to 8 tokens 16 columns by 4
+# slices of K, 9 to 16 tokens 32 columns by 8 slices; above 16 the call is the
+# plain one.  K chunks that leave some slices or waves empty, every head_dim
+# and head layout.
+@pytest.mark.parametrize("dtype", [BF16, F16], ids=["bf16", "fp16"])
+@pytest.mark.parametrize("T,hidden,hq,hkv,D", [
+    (1, 4096, 32, 8, 128),       # a Qwen3-8B decode step
+    (8, 4096, 32, 8, 128),
+    (12, 4096, 32, 8, 128),
+    (16, 4096, 32, 8, 128),
+    (3, 320, 4, 2, 128),         # 10 K chunks over 4 slices
+    (2, 64, 3, 1, 64),           # 2 K chunks over 4 slices: most waves have none
+    (9, 64, 1, 1, 64),           # 2 K chunks over 8 slices
+    (5, 192, 5, 0, 64),          # no K or V heads
+    (15, 448, 0, 3, 64),         # K heads only
+    (16, 256, 2, 1, 256),        # head_dim 256
+    (7, 576, 1, 2, 256),
+    (17, 320, 4, 2, 128),        # above the split range: the workspace is not used
+])
+def test_decode_size_projection_workspace(dtype, T, hidden, hq, hkv, D):
+    x, w, gq, gk = make(310 + T + D, T, hidden, hq, hkv, D, dtype=dtype)
+    eps = synth.eps_f32(1e-6)
+    N = w.shape[0]
+    got = run_proj(x, w, hq, hkv, D, gq, gk, eps, ld=N + 16, label="decode ws", dtype=dtype, ws=True)
+    check(x, w, hq, hkv, D, gq, gk, eps, got, label=f"decode ws T={T} K={hidden} D={D}", dtype=dtype)
+    got = run_proj(x, w, hq, hkv, D, gq, gk, eps, plain=True, label="decode ws plain", dtype=dtype, ws=True)
+    check(x, w, hq, hkv, D, gq, gk, eps, got, plain=True, label=f"decode ws plain T={T} D={D}", dtype=dtype)
+
+
+def test_workspace_size_and_errors_on_the_gpu():
+    # a workspace one 256-byte step short, or misaligned, is refused before any
+    # launch; the output keeps its fill
+    T, hidden, hq, hkv, D = 4, 256, 4, 1, 128
+    x, w, gq, gk = make(91, T, hidden, hq, hkv, D)
+    xt, wt = host_to_device(x, BF16), host_to_device(w, BF16)
+    g1, g2 = gamma_to_device(gq, BF16), gamma_to_device(gk, BF16)
+    need = q.qknorm_qkv_proj_workspace_bytes(T, hq, hkv, D)
+    assert need == 4 * T * w.shape[0] * 4
+    out = torch.zeros(T, w.shape[0], dtype=torch.bfloat16, device="cuda")
+    space = torch.empty(need + 256, dtype=torch.uint8, device="cuda")
+    for bad, code in ((space[:need - 256], q.QKNORM_E_SHAPE), (space[8:need + 8], q.QKNORM_E_ALIGN),
+                      (None, q.QKNORM_E_NULLPTR)):
+        with pytest.raises(ValueError, match=f"code {code}"):
+            q.qknorm_qkv_proj_per_head_ws(xt, wt, out, hq, hkv, D, g1, g2, 1e-6, workspace=bad)
+    torch.cuda.synchronize()
+    assert not out.view(torch.int16).any()
+
+
+@pytest.mark.parametrize("T,ws", [(200, False), (8, False), (8, True), (13, True)],
+                         ids=["tiled", "decode", "decode-ws", "decode-ws-32col"])
+def test_deterministic_and_graph_replay(T, ws):
     hidden, hq, hkv, D = 256, 4, 1, 128
     x, w, gq, gk = make(82, T, hidden, hq, hkv, D)
     xt, wt = host_to_device(x, BF16), host_to_device(w, BF16)
     g1, g2 = gamma_to_device(gq, BF16), gamma_to_device(gk, BF16)
     out = torch.empty(T, w.shape[0], dtype=torch.bfloat16, device="cuda")
-    q.qknorm_qkv_proj_per_head(xt, wt, out, hq, hkv, D, g1, g2, 1e-6)
+    space = torch.empty(max(q.qknorm_qkv_proj_workspace_bytes(T, hq, hkv, D), 1), dtype=torch.uint8,
+                        device="cuda")
+
+    def call():
+        if ws:
+            q.qknorm_qkv_proj_per_head_ws(xt, wt, out, hq, hkv, D, g1, g2, 1e-6, workspace=space)
+        else:
+            q.qknorm_qkv_proj_per_head(xt, wt, out, hq, hkv, D, g1, g2, 1e-6)
+    call()
     torch.cuda.synchronize()
     eager = out.clone()
+    call()                                       # the same bits again
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), eager.view(torch.int16))
     graph = torch.cuda.CUDAGraph()
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
         with torch.cuda.graph(graph, stream=s):
-            q.qknorm_qkv_proj_per_head(xt, wt, out, hq, hkv, D, g1, g2, 1e-6)
+            call()
     torch.cuda.synchronize()
     for _ in range(3):
         out.zero_()
