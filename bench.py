@@ -941,6 +941,11 @@ def main():
         cases["d2d_copy_headline_bytes"] = {**cp, "copy_time_over_headline_kernel_time": cp["mean_us"] / head["mean_us"]}
         for T in (4096, 8192):
             cases[f"qkv_proj_T{T}_qwen3_8b"] = bench_proj(q, torch, dev, 30, 5, T=T)
+        # the weight rotating through 6 copies (300 MB), cold in the Infinity
+        # Cache at each call as in a served model; decode sizes add the
+        # workspace form
+        for T in (1, 16, 4096, 8192):
+            cases[f"qkv_proj_T{T}_qwen3_8b_cold_weight"] = bench_proj(q, torch, dev, 30, 5, T=T, copies=6)
         result["cases"] = cases
     result["pages_context"] = PAGES_CONTEXT
     if not args.no_cpu:
