@@ -238,6 +238,28 @@ int qknorm_qkv_proj_per_head_ws(const void *x, int64_t ldx, const void *w, int64
                                 float eps, int32_t flags, int32_t dtype, void *workspace,
                                 int64_t workspace_bytes, void *stream);
 
+/*
+ * qknorm_qkv_proj_per_head_ws for callers that cannot allocate a workspace
+ * (code under HIP graph capture, serving loops that may not allocate,
+ * harnesses that forbid it): the same kernels, with the library's own
+ * scratch in place of the workspace.  The scratch is one array of 8 MiB per
+ * GPU, in the library's device memory from its load until the process ends;
+ * this call allocates and frees nothing.  Decode sizes whose workspace
+ * (qknorm_qkv_proj_workspace_bytes) would exceed 8 MiB get
+ * QKNORM_E_UNSUPPORTED before anything is enqueued (at 16 tokens N up to
+ * 16384).  Every call on one GPU shares that GPU's scratch: calls that can
+ * run at the same time on one GPU (different streams) race and must not
+ * overlap.  Nothing in the scratch needs clearing between calls.  Devices
+ * numbered 64 or higher get QKNORM_E_HIP.  Arguments, results and other
+ * errors as for qknorm_qkv_proj_per_head_ws (for the same inputs the two
+ * give the same bits).
+ */
+int qknorm_qkv_proj_per_head_noalloc(const void *x, int64_t ldx, const void *w, int64_t ldw,
+                                     void *qkv, int64_t ld, int64_t T, int64_t hidden, int32_t hq,
+                                     int32_t hkv, int32_t head_dim, const void *gamma_q,
+                                     const void *gamma_k, float eps, int32_t flags, int32_t dtype,
+                                     void *stream);
+
 /* Static description of a return code; never NULL. */
 const char *qknorm_strerror(int code);
 

@@ -44,7 +44,8 @@ QKNORM_PROJ_PLAIN = 1
 
 EXPORTED = ("qknorm_per_head", "qknorm_layerwise", "qknorm_partial_sumsq",
             "qknorm_apply_scalar", "qknorm_qkv_proj_per_head", "qknorm_qkv_proj_workspace_bytes",
-            "qknorm_qkv_proj_per_head_ws", "qknorm_strerror", "qknorm_abi_version")
+            "qknorm_qkv_proj_per_head_ws", "qknorm_qkv_proj_per_head_noalloc", "qknorm_strerror",
+            "qknorm_abi_version")
 
 _lib = None
 
@@ -75,9 +76,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.qknorm_qkv_proj_workspace_bytes.restype = I64
     lib.qknorm_qkv_proj_per_head_ws.argtypes = [P, I64, P, I64, P, I64, I64, I64, I32, I32, I32, P, P,
                                                 F, I32, I32, P, I64, P]
+    lib.qknorm_qkv_proj_per_head_noalloc.argtypes = lib.qknorm_qkv_proj_per_head.argtypes
     for name in ("qknorm_per_head", "qknorm_layerwise", "qknorm_partial_sumsq",
                  "qknorm_apply_scalar", "qknorm_qkv_proj_per_head", "qknorm_qkv_proj_per_head_ws",
-                 "qknorm_abi_version"):
+                 "qknorm_qkv_proj_per_head_noalloc", "qknorm_abi_version"):
         getattr(lib, name).restype = I32
     lib.qknorm_strerror.argtypes = [ctypes.c_int]
     lib.qknorm_strerror.restype = ctypes.c_char_p
@@ -100,6 +102,7 @@ class _CtypesCalls:
         self.apply_scalar = lib.qknorm_apply_scalar
         self.qkv_proj_per_head = lib.qknorm_qkv_proj_per_head
         self.qkv_proj_per_head_ws = lib.qknorm_qkv_proj_per_head_ws
+        self.qkv_proj_per_head_noalloc = lib.qknorm_qkv_proj_per_head_noalloc
 
     @staticmethod
     def per_head_t(*_):
@@ -355,7 +358,17 @@ def qknorm_qkv_proj_per_head_ws(x, w, qkv, hq: int, hkv: int, head_dim: int, gam
     _raise(rc, "qknorm_qkv_proj_per_head_ws")
 
 
+def qknorm_qkv_proj_per_head_noalloc(x, w, qkv, hq: int, hkv: int, head_dim: int, gamma_q=None,
+                                     gamma_k=None, eps: float = 1e-6, plain: bool = False,
+                                     stream=None) -> None:
+    """qknorm_qkv_proj_per_head_ws with the library's own per-GPU scratch in
+    place of a workspace (nothing allocated; calls that overlap on one GPU race)."""
+    dev, args = _proj_args(x, w, qkv, hq, hkv, head_dim, gamma_q, gamma_k, eps, plain)
+    rc = _calls().qkv_proj_per_head_noalloc(*args, _stream(stream, dev))
+    _raise(rc, "qknorm_qkv_proj_per_head_noalloc")
+
+
 __all__ = ["qknorm_per_head", "qknorm_qkv_proj_per_head", "qknorm_qkv_proj_per_head_ws",
-           "qknorm_qkv_proj_workspace_bytes", "qknorm_layerwise", "qknorm_partial_sumsq", "qknorm_apply_scalar",
+           "qknorm_qkv_proj_workspace_bytes", "qknorm_qkv_proj_per_head_noalloc", "qknorm_layerwise", "qknorm_partial_sumsq", "qknorm_apply_scalar",
            "strerror", "abi_version", "load", "QKNormError", "QKNORM_F32", "QKNORM_BF16", "QKNORM_F16",
            "QKNORM_FP8_E4M3"]

@@ -2,8 +2,8 @@
  *
  * Two kinds of call, both argument marshalling only (every step of the work
  * runs in libqknorm.so):
- * - per_head, layerwise, partial_sumsq, apply_scalar, qkv_proj_per_head and
- *   qkv_proj_per_head_ws take the C ABI's arguments as Python ints and floats
+ * - per_head, layerwise, partial_sumsq, apply_scalar and the qkv_proj_per_head
+ *   calls (plain, _ws, _noalloc) take the C ABI's arguments as Python ints and floats
  *   (pointers as ints, 0 or None for NULL), convert them to C values and call the library's
  *   extern "C" function, returning its int status.  They replace ctypes,
  *   whose per-call conversion of eleven or more arguments costs about a
@@ -143,6 +143,24 @@ static PyObject* f_qkv_proj_per_head(PyObject* self, PyObject* const* a, Py_ssiz
     return NULL;
   return PyLong_FromLong(
       qknorm_qkv_proj_per_head(x, ldx, w, ldw, qkv, ld, T, hidden, hq, hkv, d, gq, gk, eps, fl, dt, st));
+}
+
+/* qkv_proj_per_head_noalloc: the arguments of qkv_proj_per_head -> int */
+static PyObject* f_qkv_proj_per_head_noalloc(PyObject* self, PyObject* const* a, Py_ssize_t n) {
+  (void)self;
+  void *x, *w, *qkv, *gq, *gk, *st;
+  int64_t ldx, ldw, ld, T, hidden;
+  int32_t hq, hkv, d, fl, dt;
+  float eps;
+  if (!nargs_ok(n, 17, "qkv_proj_per_head_noalloc")) return NULL;
+  if (as_ptr(a[0], &x) || as_i64(a[1], &ldx) || as_ptr(a[2], &w) || as_i64(a[3], &ldw) ||
+      as_ptr(a[4], &qkv) || as_i64(a[5], &ld) || as_i64(a[6], &T) || as_i64(a[7], &hidden) ||
+      as_i32(a[8], &hq) || as_i32(a[9], &hkv) || as_i32(a[10], &d) || as_ptr(a[11], &gq) ||
+      as_ptr(a[12], &gk) || as_f32(a[13], &eps) || as_i32(a[14], &fl) || as_i32(a[15], &dt) ||
+      as_ptr(a[16], &st))
+    return NULL;
+  return PyLong_FromLong(qknorm_qkv_proj_per_head_noalloc(x, ldx, w, ldw, qkv, ld, T, hidden, hq, hkv,
+                                                          d, gq, gk, eps, fl, dt, st));
 }
 
 /* qkv_proj_per_head_ws(x, ldx, w, ldw, qkv, ld, T, hidden, hq, hkv, head_dim, gamma_q, gamma_k,
@@ -308,6 +326,8 @@ static PyMethodDef kMethods[] = {
      "qknorm_qkv_proj_per_head"},
     {"qkv_proj_per_head_ws", (PyCFunction)(void (*)(void))f_qkv_proj_per_head_ws, METH_FASTCALL,
      "qknorm_qkv_proj_per_head_ws"},
+    {"qkv_proj_per_head_noalloc", (PyCFunction)(void (*)(void))f_qkv_proj_per_head_noalloc,
+     METH_FASTCALL, "qknorm_qkv_proj_per_head_noalloc"},
     {NULL, NULL, 0, NULL}};
 
 static struct PyModuleDef kModule = {PyModuleDef_HEAD_INIT, "_qknorm_fast",

@@ -274,4 +274,27 @@ int qknorm_qkv_proj_per_head_ws(const void* x, int64_t ldx, const void* w, int64
   return finish(qknorm::launch_qkv_proj(a, static_cast<hipStream_t>(stream), cus));
 }
 
+int qknorm_qkv_proj_per_head_noalloc(const void* x, int64_t ldx, const void* w, int64_t ldw,
+                                     void* qkv, int64_t ld, int64_t T, int64_t hidden, int32_t hq,
+                                     int32_t hkv, int32_t head_dim, const void* gamma_q,
+                                     const void* gamma_k, float eps, int32_t flags, int32_t dtype,
+                                     void* stream) {
+  qknorm::ProjArgs a;
+  int64_t N = 0;
+  int rc = check_proj(x, ldx, w, ldw, qkv, ld, T, hidden, hq, hkv, head_dim, gamma_q, gamma_k, eps,
+                      flags, dtype, &a, &N);
+  if (rc) return rc;
+  const int64_t need = qknorm::proj_workspace_bytes(T, N);
+  if (need > qknorm::kProjScratchBytes) return QKNORM_E_UNSUPPORTED;
+  if (T == 0 || N == 0) return QKNORM_OK;
+  if (need > 0) {
+    void* scratch = nullptr;
+    if (qknorm::proj_scratch(&scratch) != hipSuccess) return QKNORM_E_HIP;
+    return finish(qknorm::launch_qkv_proj_split(a, scratch, static_cast<hipStream_t>(stream)));
+  }
+  int cus = 0;
+  if ((rc = device_cus(&cus))) return rc;
+  return finish(qknorm::launch_qkv_proj(a, static_cast<hipStream_t>(stream), cus));
+}
+
 }  // extern "C"

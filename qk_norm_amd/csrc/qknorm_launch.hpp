@@ -85,4 +85,11 @@ int64_t proj_workspace_bytes(int64_t T, int64_t N);
 // head adds them and normalises (two launches on `s`).
 hipError_t launch_qkv_proj_split(const ProjArgs& a, void* workspace, hipStream_t s);
 
+// The library's own scratch for the split projection (one array per GPU):
+// its size, and its device address on the current device (looked up once per
+// device).  Devices numbered kMaxScratchDevices or higher are not served.
+constexpr int64_t kProjScratchBytes = INT64_C(8) << 20;
+constexpr int kMaxScratchDevices = 64;
+hipError_t proj_scratch(void** ptr);
+
 }  // namespace qknorm

@@ -31,6 +31,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+#include <mutex>
 #include <type_traits>
 
 #include "qknorm_device.hpp"
@@ -1018,6 +1020,39 @@ hipError_t launch_qkv_proj_split(const ProjArgs& a, void* workspace, hipStream_t
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k2, dim3(N / (uint32_t)a.head_dim), dim3(256), 0, s, k, (const float*)part);
   return hipGetLastError();
+}
+
+// The split projection's partials for callers that cannot allocate a
+// workspace: one array per GPU, held from the library's load until the
+// process ends.  Host code never passes the array's name to a kernel (on the
+// host it names a stand-in, not device memory); the device address comes
+// from hipGetSymbolAddress, looked up once per device with that device
+// current and kept per device.  Every such call on one GPU shares the array,
+// so calls that can overlap on one GPU (different streams) race.  Nothing in
+// it needs clearing between calls: the first kernel writes every partial the
+// second one reads.
+static __device__ __align__(256) uint8_t scratch[kProjScratchBytes];
+
+static std::mutex g_scratch_mu;
+static std::atomic<void*> g_scratch_ptr[kMaxScratchDevices];
+
+hipError_t proj_scratch(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess || p == nullptr) return e != hipSuccess ? e : hipErrorInvalidSymbol;
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *ptr = p;
+  return hipSuccess;
 }
 
 hipError_t launch_qkv_proj(const ProjArgs& a, hipStream_t s, int cus) {
