@@ -198,22 +198,25 @@ int qknorm_qkv_proj_per_head(const void *x, int64_t ldx, const void *w, int64_t 
 
 /*
  * Workspace bytes qknorm_qkv_proj_per_head_ws needs for T tokens of these
- * heads: for 1 <= T <= 16, 16*T*N bytes up to 8 tokens and 32*T*N up to 16
- * (N = (hq + 2*hkv)*head_dim; rounded up to a multiple of 256); 0 for other
- * T, which need none.  Negative on error: QKNORM_E_SHAPE for a negative T,
- * hq or hkv or head_dim <= 0, QKNORM_E_UNSUPPORTED for T or N beyond the
- * projection's limits.  Host only; no HIP call.
+ * heads: for 1 <= T <= 64, 16*T*N bytes up to 8 tokens, 32*T*N from 9 to 32
+ * and 16*T*N from 33 to 64 (N = (hq + 2*hkv)*head_dim; rounded up to a
+ * multiple of 256); 0 for other T, which need none.  Negative on error:
+ * QKNORM_E_SHAPE for a negative T, hq or hkv or head_dim <= 0,
+ * QKNORM_E_UNSUPPORTED for T or N beyond the projection's limits.  Host only;
+ * no HIP call.
  */
 int64_t qknorm_qkv_proj_workspace_bytes(int64_t T, int32_t hq, int32_t hkv, int32_t head_dim);
 
 /*
- * qknorm_qkv_proj_per_head with a workspace, for decode sizes.
- * At 1 <= T <= 16 the projection is a stream over the weight (N x hidden,
- * each element read once), and one block per head cannot read it at the
- * chip's rate.  With a workspace the weight is cut into narrow column groups
- * by slices of hidden, one block each, which leave fp32 partial sums in the
- * workspace; a second launch on the same stream adds each output's partials
- * in slice order, normalises each Q and K head of every row and stores.
+ * qknorm_qkv_proj_per_head with a workspace, for decode and other small
+ * token counts.  At 1 <= T <= 64 the projection is mostly a stream over the
+ * weight (N x hidden, each element read once), and the few blocks of one
+ * head (or one row tile of a head) each cannot read it at the chip's rate.
+ * With a workspace the weight is cut into narrow column groups by slices of
+ * hidden, one block each for all T tokens, which leave fp32 partial sums in
+ * the workspace; a second launch on the same stream adds each output's
+ * partials in slice order, normalises each Q and K head of every row and
+ * stores.
  * The result has the definition of qknorm_qkv_proj_per_head (fp32
  * accumulation, per-head QK-Norm on the fp32 sums, one rounding); the fp32
  * additions come in another order, so the two calls may differ in the last
@@ -244,10 +247,10 @@ int qknorm_qkv_proj_per_head_ws(const void *x, int64_t ldx, const void *w, int64
  * harnesses that forbid it): the same kernels, with the library's own
  * scratch in place of the workspace.  The scratch is one array of 8 MiB per
  * GPU, in the library's device memory from its load until the process ends;
- * this call allocates and frees nothing.  Decode sizes whose workspace
+ * this call allocates and frees nothing.  Token counts whose workspace
  * (qknorm_qkv_proj_workspace_bytes) would exceed 8 MiB get
- * QKNORM_E_UNSUPPORTED before anything is enqueued (at 16 tokens N up to
- * 16384).  Every call on one GPU shares that GPU's scratch: calls that can
+ * QKNORM_E_UNSUPPORTED before anything is enqueued (N up to 16384 at 16
+ * tokens, up to 8192 at 32 or 64; a Qwen3-8B layer has N = 6144).  Every call on one GPU shares that GPU's scratch: calls that can
  * run at the same time on one GPU (different streams) race and must not
  * overlap.  Nothing in the scratch needs clearing between calls.  Devices
  * numbered 64 or higher get QKNORM_E_HIP.  Arguments, results and other

@@ -76,8 +76,8 @@ hipError_t launch_apply_scalar(const ApplyArgs& a, hipStream_t s, int cus);
 hipError_t launch_qkv_proj(const ProjArgs& a, hipStream_t s, int cus);
 
 // Token counts up to this take the split projection when the caller gives a
-// workspace (or the library's own scratch).
-constexpr int64_t kProjSplitMaxT = 16;
+// workspace (or the library's own scratch); larger ones take the tiles.
+constexpr int64_t kProjSplitMaxT = 64;
 // Bytes of fp32 partials the split projection needs for T tokens and N
 // output columns (0 where T is outside 1..kProjSplitMaxT).
 int64_t proj_workspace_bytes(int64_t T, int64_t N);

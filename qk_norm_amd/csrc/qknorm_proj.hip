@@ -27,7 +27,10 @@
 // Fewer tokens take narrower launches of the same kernel (128-row tiles one
 // head wide up to 512 tokens, 64-row tiles up to 256), and up to 16 tokens
 // a separate kernel gives each head one block that reads its weight rows
-// once (qkv_proj_decode_kernel).
+// once (qkv_proj_decode_kernel).  With a workspace, up to 64 tokens take two
+// other kernels instead: the weight split over many more blocks into fp32
+// partials, then one block per head adding them and normalising
+// (qkv_proj_split_kernel, qkv_proj_split_finish_kernel).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -673,28 +676,29 @@ __global__ __launch_bounds__(512) void qkv_proj_decode_kernel(ProjKArgs args) {
   }
 }
 
-// Decode sizes through a workspace (T <= 16).  The kernel above gives a
-// head's D columns to one block, and one block reads at most 30-50 GB/s.
-// Here the weight is cut into 16 * JB columns by KS slices of K, one block
-// of 4 waves each (for a Qwen3-8B layer 1536 blocks up to 8 tokens, 1536 of
-// 32 columns up to 16), so the whole chip streams it.  Each wave takes a
-// quarter of its block's slice with the same MFMA (the weight's fragment
-// first, fragments straight from global memory PF - 1 chunks ahead, none
-// past the slice's end); the four waves' sums meet in LDS and are added in
-// wave order; the block stores them as fp32 partials part[ks][t][n].  A
-// second kernel, one block per head, adds each output's KS partials in
-// slice order, normalises the head's rows and stores them.  Rows past T read
+// Small token counts through a workspace (T <= 64).  The kernels above give
+// a head's D columns (or a 64-row tile of them) to one block, and one block
+// reads at most 30-50 GB/s, less still when the weight comes from HBM rather
+// than the Infinity Cache.  Here the weight is cut into 16 * JB columns by KS
+// slices of K, one block of 4 waves each for all T tokens (TB blocks of 16),
+// so that the whole chip streams it.  Each wave takes a quarter of its
+// block's slice with the same MFMA (the weight's fragment first, fragments
+// straight from global memory PF - 1 chunks ahead, none past the slice's
+// end); the four waves' sums meet in LDS and are added in wave order; the
+// block stores them as fp32 partials part[ks][t][n].  A second kernel, one
+// block per head and 16 tokens, adds each output's KS partials in slice
+// order, normalises the head's rows and stores them.  Rows past T read
 // zeros and store nothing.  One kernel in which the last block of a head to
 // finish did the norm was measured slower: with agent-scope release fences
 // 5-20 times, and with the partials written and read through
 // device-coherent stores and loads ahead of a counter still 15-25 %, since
 // each block then waits for its writes to reach memory before its CU takes
 // the next block.
-template <int DT, int D, int KS, int JB, int PF>
+template <int DT, int D, int KS, int JB, int TB, int PF>
 __global__ __launch_bounds__(256) void qkv_proj_split_kernel(ProjKArgs args, float* __restrict__ part) {
   constexpr int CB = 16 * JB;                    // columns per block
-  static_assert(D % CB == 0 && PF >= 2, "");
-  __shared__ __attribute__((aligned(16))) float red[4][16][CB + 4];
+  static_assert(D % CB == 0 && PF >= 2 && TB >= 1 && TB <= 4, "");
+  __shared__ __attribute__((aligned(16))) float red[4][16 * TB][CB + 4];
   typedef typename ProjElem<DT>::V8 Frag;
   const uint32_t tid = threadIdx.x, lane = tid & 63, wave = uniform(tid >> 6);
   const uint32_t ks = blockIdx.x % KS, n0 = blockIdx.x / KS * CB;
@@ -706,17 +710,22 @@ __global__ __launch_bounds__(256) void qkv_proj_split_kernel(ProjKArgs args, flo
   const Rsrc rw = make_rsrc(args.w + (uint64_t)n0 * args.ldw_bytes, (uint64_t)(CB - 1) * args.ldw_bytes + K * 2);
   const Rsrc rx = make_rsrc(args.x, (uint64_t)(T - 1) * args.ldx_bytes + K * 2);
   const uint32_t wo = fr * args.ldw_bytes + fk * 2, xo = fr * args.ldx_bytes + fk * 2;
-  f32x4 acc[JB];
+  f32x4 acc[TB][JB];
 #pragma unroll
-  for (int j = 0; j < JB; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int t = 0; t < TB; ++t)
+#pragma unroll
+    for (int j = 0; j < JB; ++j) acc[t][j] = f32x4{0.f, 0.f, 0.f, 0.f};
   {
-    Frag wf[PF][JB], xf[PF];
+    Frag wf[PF][JB], xf[PF][TB];
     auto load = [&](int p, uint32_t c) {
 #pragma unroll
       for (int j = 0; j < JB; ++j)
         wf[p][j] = __builtin_bit_cast(
             Frag, __builtin_amdgcn_raw_buffer_load_b128(rw, wo + j * 16 * args.ldw_bytes, c * 64, 0));
-      xf[p] = __builtin_bit_cast(Frag, __builtin_amdgcn_raw_buffer_load_b128(rx, xo, c * 64, 0));
+#pragma unroll
+      for (int t = 0; t < TB; ++t)
+        xf[p][t] = __builtin_bit_cast(
+            Frag, __builtin_amdgcn_raw_buffer_load_b128(rx, xo + t * 16 * args.ldx_bytes, c * 64, 0));
     };
 #pragma unroll
     for (int p = 0; p < PF - 1; ++p)
@@ -727,32 +736,37 @@ __global__ __launch_bounds__(256) void qkv_proj_split_kernel(ProjKArgs args, flo
         if (c + p + PF - 1 < c1) load((p + PF - 1) % PF, c + p + PF - 1);
         if (c + p < c1) {
 #pragma unroll
-          for (int j = 0; j < JB; ++j) acc[j] = ProjElem<DT>::mfma(wf[p][j], xf[p], acc[j]);
+          for (int t = 0; t < TB; ++t)
+#pragma unroll
+            for (int j = 0; j < JB; ++j) acc[t][j] = ProjElem<DT>::mfma(wf[p][j], xf[p][t], acc[t][j]);
         }
       }
     }
   }
 #pragma unroll
-  for (int j = 0; j < JB; ++j) *reinterpret_cast<f32x4*>(&red[wave][fr][16 * j + 4 * (lane / 16)]) = acc[j];
+  for (int t = 0; t < TB; ++t)
+#pragma unroll
+    for (int j = 0; j < JB; ++j)
+      *reinterpret_cast<f32x4*>(&red[wave][16 * t + fr][16 * j + 4 * (lane / 16)]) = acc[t][j];
   __syncthreads();
 #pragma unroll
-  for (int j = 0; j < JB; ++j) {
-    const uint32_t i = tid + 256 * j, tok = i / CB, col = i % CB;
+  for (int m = 0; m < TB * JB; ++m) {
+    const uint32_t i = tid + 256 * m, tok = i / CB, col = i % CB;
     if (tok < T)
       part[((uint64_t)ks * T + tok) * N + n0 + col] =
           ((red[0][tok][col] + red[1][tok][col]) + red[2][tok][col]) + red[3][tok][col];
   }
 }
 
-// One block per head: 16 threads per token, E = D / 16 consecutive columns
-// each; the KS partials of a column are added in slice order, then the
+// One block per head and 16 tokens: 16 threads per token, E = D / 16
+// consecutive columns each; the KS partials of a column are added in slice order, then the
 // token's head is normalised (Q and K heads, unless plain) and stored.
 template <int DT, int D, int KS>
 __global__ __launch_bounds__(256) void qkv_proj_split_finish_kernel(ProjKArgs args,
                                                                      const float* __restrict__ part) {
   constexpr int E = D / 16;
   typedef typename ProjElem<DT>::T Elem;
-  const uint32_t tid = threadIdx.x, head = blockIdx.x, tok = tid / 16, q = tid % 16;
+  const uint32_t tid = threadIdx.x, head = blockIdx.x, tok = blockIdx.y * 16 + tid / 16, q = tid % 16;
   const uint32_t T = args.T, N = args.N, n = head * D + E * q;
   float v[E];
 #pragma unroll
@@ -968,16 +982,32 @@ static hipError_t launch_qkv_proj_tiles(const ProjArgs& a, hipStream_t s) {
 using GeoM = Tile<128, 128, 4, 2, 64, 2>;
 using GeoM256 = Tile<128, 256, 4, 2, 64, 2>;
 
-// The split geometry for a decode-size token count: up to 8 tokens 16
-// columns by 4 slices of K (1536 blocks for the Qwen3-8B layer; with the
-// norm kernel 12.1 us per call at T = 1 and 14.8 us at T = 8, against 12.2
-// and 14.9 us with 8 slices), up to 16 tokens 32 columns by 8 slices, which
-// halves the activation fragments loaded per weight fragment (17.2 against
-// 18.5 us at T = 16).
+// The split geometry for a token count: KS slices of K, blocks of 16 * JB
+// columns, TB blocks of 16 tokens.  Up to 8 tokens 16 columns by 4 slices
+// (1536 blocks for the Qwen3-8B layer; with the norm kernel 12.1 us per
+// call at T = 1 and 14.8 us at T = 8, against 12.2 and 14.9 us with 8
+// slices); from 9 tokens 32 columns, which halves the activation fragments
+// loaded per weight fragment (17.2 against 18.5 us at T = 16).  From 17
+// tokens two or four token blocks share each weight fragment; K slices
+// measured with the weight rotating through 6 copies: 8 slices 17.0, 18.0
+// and 19.9 us at 17, 24 and 32 tokens (4 slices 17.6, 18.7, 19.8; 16 slices
+// 18.2, 20.0, 21.9); 4 slices 23.4 and 25.8 us at 48 and 64 tokens (8
+// slices 24.0 and 27.3; 2 slices 26.7 and 30.1).
+#ifndef QKNORM_PROJ_SPLIT_KS32
+#define QKNORM_PROJ_SPLIT_KS32 8   // K slices for 17 to 32 tokens
+#endif
+#ifndef QKNORM_PROJ_SPLIT_KS64
+#define QKNORM_PROJ_SPLIT_KS64 4   // K slices for 33 to 64 tokens
+#endif
 struct SplitGeo {
-  uint32_t ks, jb;
+  uint32_t ks, jb, tb;
 };
-static SplitGeo split_geo(int64_t T) { return T <= 8 ? SplitGeo{4, 1} : SplitGeo{8, 2}; }
+static SplitGeo split_geo(int64_t T) {
+  if (T <= 8) return SplitGeo{4, 1, 1};
+  if (T <= 16) return SplitGeo{8, 2, 1};
+  if (T <= 32) return SplitGeo{QKNORM_PROJ_SPLIT_KS32, 2, 2};
+  return SplitGeo{QKNORM_PROJ_SPLIT_KS64, 2, 4};
+}
 
 int64_t proj_workspace_bytes(int64_t T, int64_t N) {
   if (T <= 0 || T > kProjSplitMaxT || N <= 0) return 0;
@@ -989,21 +1019,28 @@ typedef void (*SplitKernel)(ProjKArgs, float*);
 typedef void (*FinishKernel)(ProjKArgs, const float*);
 
 template <int DT, int D>
-static void split_kernels(uint32_t ks, SplitKernel* k1, FinishKernel* k2) {
-  if (ks == 4) {
-    *k1 = qkv_proj_split_kernel<DT, D, 4, 1, 8>;
+static void split_kernels(const SplitGeo& g, SplitKernel* k1, FinishKernel* k2) {
+  constexpr int S32 = QKNORM_PROJ_SPLIT_KS32, S64 = QKNORM_PROJ_SPLIT_KS64;
+  if (g.tb == 1 && g.jb == 1) {
+    *k1 = qkv_proj_split_kernel<DT, D, 4, 1, 1, 8>;
     *k2 = qkv_proj_split_finish_kernel<DT, D, 4>;
-  } else {
-    *k1 = qkv_proj_split_kernel<DT, D, 8, 2, 4>;
+  } else if (g.tb == 1) {
+    *k1 = qkv_proj_split_kernel<DT, D, 8, 2, 1, 4>;
     *k2 = qkv_proj_split_finish_kernel<DT, D, 8>;
+  } else if (g.tb == 2) {
+    *k1 = qkv_proj_split_kernel<DT, D, S32, 2, 2, 4>;
+    *k2 = qkv_proj_split_finish_kernel<DT, D, S32>;
+  } else {
+    *k1 = qkv_proj_split_kernel<DT, D, S64, 2, 4, 4>;
+    *k2 = qkv_proj_split_finish_kernel<DT, D, S64>;
   }
 }
 
 template <int DT>
-static void split_kernels_dt(int head_dim, uint32_t ks, SplitKernel* k1, FinishKernel* k2) {
-  if (head_dim == 64) split_kernels<DT, 64>(ks, k1, k2);
-  else if (head_dim == 128) split_kernels<DT, 128>(ks, k1, k2);
-  else split_kernels<DT, 256>(ks, k1, k2);
+static void split_kernels_dt(int head_dim, const SplitGeo& g, SplitKernel* k1, FinishKernel* k2) {
+  if (head_dim == 64) split_kernels<DT, 64>(g, k1, k2);
+  else if (head_dim == 128) split_kernels<DT, 128>(g, k1, k2);
+  else split_kernels<DT, 256>(g, k1, k2);
 }
 
 hipError_t launch_qkv_proj_split(const ProjArgs& a, void* workspace, hipStream_t s) {
@@ -1011,14 +1048,15 @@ hipError_t launch_qkv_proj_split(const ProjArgs& a, void* workspace, hipStream_t
   const uint32_t N = (uint32_t)((a.hq + 2 * a.hkv) * a.head_dim);
   SplitKernel k1;
   FinishKernel k2;
-  if (a.dtype == kF16) split_kernels_dt<kF16>(a.head_dim, g.ks, &k1, &k2);
-  else split_kernels_dt<kBF16>(a.head_dim, g.ks, &k1, &k2);
+  if (a.dtype == kF16) split_kernels_dt<kF16>(a.head_dim, g, &k1, &k2);
+  else split_kernels_dt<kBF16>(a.head_dim, g, &k1, &k2);
   const ProjKArgs k = kernel_args(a);
   float* part = static_cast<float*>(workspace);
   hipLaunchKernelGGL(k1, dim3(N / (16 * g.jb) * g.ks), dim3(256), 0, s, k, part);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k2, dim3(N / (uint32_t)a.head_dim), dim3(256), 0, s, k, (const float*)part);
+  hipLaunchKernelGGL(k2, dim3(N / (uint32_t)a.head_dim, (uint32_t)(a.T + 15) / 16), dim3(256), 0, s, k,
+                     (const float*)part);
   return hipGetLastError();
 }
 

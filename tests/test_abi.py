@@ -253,8 +253,10 @@ def test_projection_workspace_size_and_validation(lib):
     assert f(8, 32, 8, 128) == 4 * 8 * N * 4
     assert f(9, 32, 8, 128) == 8 * 9 * N * 4               # 9 to 16: 8 slices
     assert f(16, 32, 8, 128) == 8 * 16 * N * 4
+    assert f(17, 32, 8, 128) == 8 * 17 * N * 4             # 17 to 32: 8 slices
+    assert f(64, 32, 8, 128) == 4 * 64 * N * 4             # 33 to 64: 4 slices
     assert f(1, 1, 1, 1) == 256                            # 48 bytes, rounded up to 256
-    assert f(0, 32, 8, 128) == 0 and f(17, 32, 8, 128) == 0 and f(4096, 32, 8, 128) == 0
+    assert f(0, 32, 8, 128) == 0 and f(65, 32, 8, 128) == 0 and f(4096, 32, 8, 128) == 0
     assert f(-1, 1, 0, 64) == q.QKNORM_E_SHAPE
     assert f(1, -1, 0, 64) == q.QKNORM_E_SHAPE
     assert f(1, 1, 0, 0) == q.QKNORM_E_SHAPE

@@ -219,9 +219,10 @@ def test_decode_size_projection(dtype, T, hidden, hq, hkv, D):
 
 
 # Small token counts through the workspace form: up to 8 tokens 16 columns by 4
-# slices of K, 9 to 16 tokens 32 columns by 8 slices; above 16 the call is the
-# plain one.  K chunks that leave some slices or waves empty, every head_dim
-# and head layout.
+# slices of K, 9 to 16 tokens 32 columns by 8 slices, 17 to 32 and 33 to 64
+# tokens 32 columns with two and four blocks of 16 tokens; above 64 the call
+# is the plain one.  K chunks that leave some slices or waves empty, every
+# head_dim and head layout, token counts on and off the 16-token blocks.
 @pytest.mark.parametrize("dtype", [BF16, F16], ids=["bf16", "fp16"])
 @pytest.mark.parametrize("T,hidden,hq,hkv,D", [
     (1, 4096, 32, 8, 128),       # a Qwen3-8B decode step
@@ -235,7 +236,13 @@ def test_decode_size_projection(dtype, T, hidden, hq, hkv, D):
     (15, 448, 0, 3, 64),         # K heads only
     (16, 256, 2, 1, 256),        # head_dim 256
     (7, 576, 1, 2, 256),
-    (17, 320, 4, 2, 128),        # above the split range: the workspace is not used
+    (17, 320, 4, 2, 128),        # two token blocks, the second with one token
+    (32, 4096, 32, 8, 128),
+    (33, 4096, 32, 8, 128),      # four token blocks, the last three nearly empty
+    (64, 4096, 32, 8, 128),
+    (50, 64, 1, 1, 64),          # 2 K chunks over the slices
+    (40, 576, 1, 2, 256),
+    (65, 320, 4, 2, 128),        # above the split range: the workspace is not used
 ])
 def test_decode_size_projection_workspace(dtype, T, hidden, hq, hkv, D):
     x, w, gq, gk = make(310 + T + D, T, hidden, hq, hkv, D, dtype=dtype)
@@ -266,8 +273,8 @@ def test_workspace_size_and_errors_on_the_gpu():
     assert not out.view(torch.int16).any()
 
 
-@pytest.mark.parametrize("T,ws", [(200, False), (8, False), (8, True), (13, True)],
-                         ids=["tiled", "decode", "decode-ws", "decode-ws-32col"])
+@pytest.mark.parametrize("T,ws", [(200, False), (8, False), (8, True), (13, True), (45, True)],
+                         ids=["tiled", "decode", "decode-ws", "decode-ws-32col", "ws-4-token-blocks"])
 def test_deterministic_and_graph_replay(T, ws):
     hidden, hq, hkv, D = 256, 4, 1, 128
     x, w, gq, gk = make(82, T, hidden, hq, hkv, D)
