@@ -12,8 +12,12 @@
  * keep every fp32 step exact except the reciprocal square root, so each bf16
  * output is within one bf16 ulp of the closed form.
  *
- * Also: validation codes returned before any HIP call, and the fused
- * layerwise call equal, byte for byte, to partial sums then apply.
+ * Also: validation codes returned before any HIP call, the fused layerwise
+ * call equal, byte for byte, to partial sums then apply, and the QKV
+ * projection with a weight that selects columns of x (each output one exact
+ * product), so its Q and K heads take the closed form of the norm and its V
+ * heads copy x; the three projection calls (no workspace, a workspace, the
+ * library's scratch) give the same bytes.
  *
  * Exit status 0 when every check passes; the first failure is printed.
  * With --validation-only it stops after the checks that need no GPU.
@@ -106,6 +110,15 @@ static int validation(void) {
          "a shard count that does not divide the widths not rejected");
   for (int c = QKNORM_E_HIP; c <= QKNORM_OK; ++c)
     EXPECT(qknorm_strerror(c) != NULL && qknorm_strerror(c)[0] != '\0', "no text for code %d", c);
+  EXPECT(qknorm_qkv_proj_workspace_bytes(1, 32, 8, 128) == 4 * 6144 * 4, "workspace bytes at T = 1");
+  EXPECT(qknorm_qkv_proj_workspace_bytes(65, 32, 8, 128) == 0, "no workspace above 64 tokens");
+  EXPECT(qknorm_qkv_proj_workspace_bytes(-1, 32, 8, 128) == QKNORM_E_SHAPE, "negative T not rejected");
+  EXPECT(qknorm_qkv_proj_per_head_ws(g, 256, g, 256, (void*)g, 512, 4, 256, 2, 1, 128, g, g, 0.0f, 0,
+                                     QKNORM_BF16, NULL, 1 << 20, NULL) == QKNORM_E_NULLPTR,
+         "a missing workspace not rejected");
+  EXPECT(qknorm_qkv_proj_per_head_noalloc(g, 256, g, 256, (void*)g, 512, 4, 256, 2, 1, 128, g, g, 0.0f, 0,
+                                          QKNORM_F32, NULL) == QKNORM_E_UNSUPPORTED,
+         "fp32 projection not rejected");
   return 0;
 }
 
@@ -202,6 +215,70 @@ static int layerwise(void) {
   return 0;
 }
 
+static int projection(void) {
+  /* x [T, 256] bf16 holding two closed-form groups of 128 per row; w [512, 256]
+   * with w[n][n % 256] = 1 and zeros elsewhere, so qkv[t][n] = x[t][n % 256]:
+   * Q heads 0 and 1 are the two groups, the K head the first group again, the
+   * V head a copy of the second group */
+  enum { T = 5, HID = 256, HQ = 2, HKV = 1, D = 128, N = (HQ + 2 * HKV) * D };
+  uint16_t *x = malloc((size_t)T * HID * 2), *w = calloc((size_t)N * HID, 2), *g = malloc(D * 2);
+  uint16_t *y[3];
+  int k[T][2];
+  EXPECT(x && w && g, "host allocation");
+  for (int j = 0; j < D; ++j) g[j] = to_bf16(gamma_at(j));
+  for (int t = 0; t < T; ++t)
+    for (int h = 0; h < 2; ++h) k[t][h] = fill_group(x + (size_t)t * HID + h * D, D, (unsigned)(t * 17 + h * 5 + 1));
+  for (int n = 0; n < N; ++n) w[(size_t)n * HID + n % HID] = to_bf16(1.0f);
+  void *dx, *dw, *dg, *dy, *ws;
+  const int64_t need = qknorm_qkv_proj_workspace_bytes(T, HQ, HKV, D);
+  EXPECT(need == 4 * T * N * 4, "workspace bytes %lld", (long long)need);
+  HIP_OK(hipMalloc(&dx, (size_t)T * HID * 2));
+  HIP_OK(hipMalloc(&dw, (size_t)N * HID * 2));
+  HIP_OK(hipMalloc(&dg, D * 2));
+  HIP_OK(hipMalloc(&dy, (size_t)T * N * 2));
+  HIP_OK(hipMalloc(&ws, (size_t)need));
+  HIP_OK(hipMemcpy(dx, x, (size_t)T * HID * 2, hipMemcpyHostToDevice));
+  HIP_OK(hipMemcpy(dw, w, (size_t)N * HID * 2, hipMemcpyHostToDevice));
+  HIP_OK(hipMemcpy(dg, g, D * 2, hipMemcpyHostToDevice));
+  for (int c = 0; c < 3; ++c) {
+    y[c] = malloc((size_t)T * N * 2);
+    EXPECT(y[c], "host allocation");
+    HIP_OK(hipMemset(dy, 0xFF, (size_t)T * N * 2));
+    int rc;
+    if (c == 0)
+      rc = qknorm_qkv_proj_per_head(dx, HID, dw, HID, dy, N, T, HID, HQ, HKV, D, dg, dg, 0.0f, 0,
+                                    QKNORM_BF16, NULL);
+    else if (c == 1)
+      rc = qknorm_qkv_proj_per_head_ws(dx, HID, dw, HID, dy, N, T, HID, HQ, HKV, D, dg, dg, 0.0f, 0,
+                                       QKNORM_BF16, ws, need, NULL);
+    else
+      rc = qknorm_qkv_proj_per_head_noalloc(dx, HID, dw, HID, dy, N, T, HID, HQ, HKV, D, dg, dg, 0.0f, 0,
+                                            QKNORM_BF16, NULL);
+    EXPECT(rc == QKNORM_OK, "projection call %d: %s", c, qknorm_strerror(rc));
+    HIP_OK(hipDeviceSynchronize());
+    HIP_OK(hipMemcpy(y[c], dy, (size_t)T * N * 2, hipMemcpyDeviceToHost));
+    for (int t = 0; t < T; ++t) {
+      const uint16_t* r = y[c] + (size_t)t * N;
+      if (check_group(r, D, k[t][0], "projection Q head 0 of row", t)) return 1;
+      if (check_group(r + D, D, k[t][1], "projection Q head 1 of row", t)) return 1;
+      if (check_group(r + 2 * D, D, k[t][0], "projection K head of row", t)) return 1;
+      EXPECT(memcmp(r + 3 * D, x + (size_t)t * HID + D, D * 2) == 0, "call %d row %d: V head is not x", c, t);
+    }
+  }
+  EXPECT(memcmp(y[0], y[1], (size_t)T * N * 2) == 0, "workspace projection differs from the plain call");
+  EXPECT(memcmp(y[0], y[2], (size_t)T * N * 2) == 0, "no-alloc projection differs from the plain call");
+  HIP_OK(hipFree(dx));
+  HIP_OK(hipFree(dw));
+  HIP_OK(hipFree(dg));
+  HIP_OK(hipFree(dy));
+  HIP_OK(hipFree(ws));
+  for (int c = 0; c < 3; ++c) free(y[c]);
+  free(x);
+  free(w);
+  free(g);
+  return 0;
+}
+
 int main(int argc, char** argv) {
   if (validation()) return 1;
   printf("validation codes ok\n");
@@ -212,5 +289,8 @@ int main(int argc, char** argv) {
   fflush(stdout);
   if (layerwise()) return 1;
   printf("layerwise closed forms ok, fused == two-phase\n");
+  fflush(stdout);
+  if (projection()) return 1;
+  printf("projection closed forms ok, the three projection calls agree\n");
   return 0;
 }

@@ -16,5 +16,6 @@ def test_plain_c_program_closed_forms():
     print(f"[c-abi] {BIN}", flush=True)
     res = subprocess.run([BIN], capture_output=True, text=True, timeout=100)
     assert res.returncode == 0, f"exit {res.returncode}: {res.stderr.strip()}"
-    for line in ("validation codes ok", "per-head closed forms ok", "layerwise closed forms ok"):
+    for line in ("validation codes ok", "per-head closed forms ok", "layerwise closed forms ok",
+                 "projection closed forms ok"):
         assert line in res.stdout, res.stdout

@@ -60,3 +60,35 @@ def test_noalloc_rejects_partials_beyond_the_scratch():
         q.qknorm_qkv_proj_per_head_noalloc(x, w, out, hq, hkv, D, g, None, 1e-6)
     torch.cuda.synchronize()
     assert not out.view(torch.int16).any()
+
+
+def test_noalloc_in_a_replayed_graph_with_other_calls_between():
+    # captured once, replayed three times; before each replay an eager no-alloc
+    # call on other inputs rewrites the scratch, which the replay must not need
+    T, hidden, hq, hkv, D = 12, 256, 4, 1, 128
+    x, w, gq, gk = make(403, T, hidden, hq, hkv, D)
+    x2, w2, gq2, gk2 = make(404, 7, 320, 2, 2, D)
+    xt, wt = host_to_device(x, BF16), host_to_device(w, BF16)
+    g1, g2 = gamma_to_device(gq, BF16), gamma_to_device(gk, BF16)
+    xt2, wt2 = host_to_device(x2, BF16), host_to_device(w2, BF16)
+    h1, h2 = gamma_to_device(gq2, BF16), gamma_to_device(gk2, BF16)
+    out = torch.empty(T, w.shape[0], dtype=torch.bfloat16, device="cuda")
+    out2 = torch.empty(7, w2.shape[0], dtype=torch.bfloat16, device="cuda")
+    print("[noalloc] graph replay", flush=True)
+    q.qknorm_qkv_proj_per_head_noalloc(xt, wt, out, hq, hkv, D, g1, g2, 1e-6)
+    torch.cuda.synchronize()
+    eager = out.clone()
+    graph = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(graph, stream=s):
+            q.qknorm_qkv_proj_per_head_noalloc(xt, wt, out, hq, hkv, D, g1, g2, 1e-6)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        out.zero_()
+        q.qknorm_qkv_proj_per_head_noalloc(xt2, wt2, out2, 2, 2, D, h1, h2, 1e-6)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), eager.view(torch.int16))
