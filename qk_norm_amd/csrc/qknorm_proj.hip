@@ -122,6 +122,9 @@ struct Tile {
 #ifndef QKNORM_PROJ_GM
 #define QKNORM_PROJ_GM 4
 #endif
+#ifndef QKNORM_PROJ_STAGGER
+#define QKNORM_PROJ_STAGGER 1      // 0: every block walks K from step 0
+#endif
 constexpr bool kXcdRemap = QKNORM_PROJ_XCD != 0;
 constexpr uint32_t kGroupM = QKNORM_PROJ_GM;
 
@@ -191,10 +194,13 @@ __device__ __forceinline__ typename ProjElem<DT>::V8 sfrag(const uint8_t* base, 
                                                             lds_slot<G>(row, k / 8) * 16);
 }
 
-// Byte offset of K step k, or of the last step for k past it.
+// Byte offset of the block's K step k (or of its last step for k past it),
+// the block's walk through K starting `shift` steps in and wrapping round.
 template <class G>
-__device__ __forceinline__ uint32_t step_bytes(uint32_t k, uint32_t ksteps) {
-  return (k < ksteps ? k : ksteps - 1) * G::BK * 2;
+__device__ __forceinline__ uint32_t step_bytes(uint32_t k, uint32_t ksteps, uint32_t shift) {
+  uint32_t s = (k < ksteps ? k : ksteps - 1) + shift;
+  if (s >= ksteps) s -= ksteps;
+  return s * G::BK * 2;
 }
 
 // s_waitcnt with vmcnt(N) and the other counters left alone (gfx9 encoding:
@@ -477,11 +483,16 @@ __device__ __forceinline__ void proj_tile(const ProjKArgs& args, uint32_t id, ui
   uint8_t* const stage0 = smem;
   uint8_t* const stage1 = smem + G::kStageBytes;
 
+  // The blocks of each XCD start their walk through K at their own eighth of
+  // it: blocks on different XCDs that share weight columns then reach each
+  // K step at different times, so a step's weight comes from HBM for the
+  // first of them only and from the Infinity Cache for the rest.
+  const uint32_t shift = QKNORM_PROJ_STAGGER ? uniform(blockIdx.x % 8 * ksteps / 8) : 0;
   const DmaOffsets<G> doff = dma_offsets<G>(ldx_bytes, ldw_bytes, wave, lane);
-  dma_tile<G>(ra, rb, doff, step_bytes<G>(0, ksteps), stage0, wave);
+  dma_tile<G>(ra, rb, doff, step_bytes<G>(0, ksteps, shift), stage0, wave);
   wait_vmcnt<0>();
   stage_barrier();
-  dma_tile<G>(ra, rb, doff, step_bytes<G>(1, ksteps), stage1, wave);
+  dma_tile<G>(ra, rb, doff, step_bytes<G>(1, ksteps, shift), stage1, wave);
   typedef typename ProjElem<DT>::V8 Frag;
   Frag fa[2][MB], fb[2][NB];
   read_frags<G, DT>(stage0, arow, brow, fk, fa[0], fb[0]);
@@ -514,7 +525,7 @@ __device__ __forceinline__ void proj_tile(const ProjKArgs& args, uint32_t id, ui
     // the reads come first: the compiler cannot tell that the loads into
     // stage st do not overlap stage nx, so it keeps them in source order
     read_frags<G, DT>(nx, arow, brow, fk, fa[0], fb[0]);
-    dma_tile<G>(ra, rb, doff, step_bytes<G>(ks + 2, ksteps), st, wave);
+    dma_tile<G>(ra, rb, doff, step_bytes<G>(ks + 2, ksteps, shift), st, wave);
     mfma_step<G, DT>(acc, fa[1], fb[1]);
     if constexpr (kSched) {
       sched_interleave<kReads, 1, 0, kMfmaPerRead>();
