@@ -13,7 +13,7 @@ import qk_norm_amd as q
 from qk_norm_amd import synth
 from gpu_util import (assert_close_to_oracle, device_to_host, gamma_to_device, host_rows,
                       host_to_device, upload_rows)
-from test_gpu_proj import check as proj_check
+from test_gpu_proj import tolerance as proj_tolerance
 
 pytestmark = pytest.mark.gpu
 
@@ -119,14 +119,27 @@ def test_projection_output_past_4gib():
                                gamma_to_device(gq, synth.BF16), gamma_to_device(gk, synth.BF16), eps)
     torch.cuda.synchronize()
     del x
-    rows = _rows(T)
-    xs = host_rows(seed, rows % BLOCK, hidden, synth.BF16, token_scale=(0.25, 4.0))
-    # the same per-element bound as the projection's other parity tests
-    proj_check(xs, w, hq, hkv, D, gq, gk, eps, _gather(out, rows, synth.BF16),
-               label="projection past 4 GiB, sampled rows")
-    first = out[:BLOCK].clone()
-    for b in (1, T // BLOCK // 2, T // BLOCK - 1):
-        assert torch.equal(out[b * BLOCK:(b + 1) * BLOCK].view(torch.int16), first.view(torch.int16)), \
-            f"block {b} differs from block 0"
-    del out, first
+    # Each XCD's tiles start their walk through K at a different step, so two
+    # copies of a row can be summed in different orders: the copies are each
+    # held to the oracle's bound rather than to each other's bits.  The oracle
+    # is computed once per chunk of the repeated block and every row of four
+    # blocks is checked against it: the first two, one in the middle and the
+    # last, which lies past 4 GiB.
+    xs = host_rows(seed, np.arange(BLOCK), hidden, synth.BF16, token_scale=(0.25, 4.0))
+    blocks = (0, 1, T // BLOCK // 2, T // BLOCK - 1)
+    assert (T // BLOCK - 1) * BLOCK * N * 2 >= GIB4
+    got = {b: out[b * BLOCK:(b + 1) * BLOCK].cpu().view(torch.int16).numpy().view(np.uint16)
+           for b in blocks}
+    del out
     _free()
+    for r0 in range(0, BLOCK, 1024):
+        rows = slice(r0, r0 + 1024)
+        y64, yr = oracle.qkv_proj_per_head(xs[rows], w, synth.BF16, hq, hkv, D, gq, gk, eps)
+        tol = proj_tolerance(xs[rows], w, y64, gq, gk, hq, hkv, D)
+        for b in blocks:
+            g = oracle.decode(got[b][rows], synth.BF16)
+            bad = ~(np.abs(g - y64) <= tol)
+            assert not bad.any(), \
+                f"projection past 4 GiB: block {b} rows {r0}..: {int(bad.sum())} beyond the bound"
+            exact = np.mean(got[b][rows] == yr)
+            assert exact > 0.97, f"block {b} rows {r0}..: only {exact:.4f} equal the oracle's rounding"
