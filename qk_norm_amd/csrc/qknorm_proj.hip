@@ -10,11 +10,12 @@
 // Tiling: a block of 512 threads (4 x 2 waves, two per SIMD) owns a 256 x 256
 // output tile; each wave a 64 x 128 slab of 4 x 8 v_mfma_f32_16x16x32_bf16
 // blocks (v_mfma_f32_16x16x32_f16 for fp16, the same layout).  K advances 64
-// at a time through two LDS stages filled straight from global memory
-// (buffer loads into LDS, no staging registers), with the operand rows
-// XOR-swizzled so that fragment reads hit distinct banks.  Where 256 x 256
-// tiles would leave a round of the chip's CUs half empty, the last columns
-// go to 256 x 128 tiles of the same launch.  Tiles are ordered so the blocks
+// at a time through a ring of LDS stages (two for these tiles, three or four
+// for the smaller ones) filled straight from global memory (buffer loads
+// into LDS, no staging registers), with the operand rows XOR-swizzled so that
+// fragment reads hit distinct banks.  Where 256 x 256 tiles would leave a
+// round of the chip's CUs half empty, the last columns go to 256 x 128 tiles
+// of the same launch.  Tiles are ordered so the blocks
 // each XCD holds at once share operand panels in its L2.  Because tile widths
 // are multiples of head_dim (or one head spans a tile's two column waves)
 // and tiles start at multiples of it, a tile holds whole heads, and the
@@ -25,7 +26,8 @@
 // write straight from registers.
 //
 // Fewer tokens take narrower launches of the same kernel (128-row tiles one
-// head wide up to 512 tokens, 64-row tiles up to 256), and up to 16 tokens
+// head wide up to 512 tokens, or on to 1024 while they fit one round of the
+// CUs; 64-row tiles up to 256), and up to 16 tokens
 // a separate kernel gives each head one block that reads its weight rows
 // once (qkv_proj_decode_kernel).  With a workspace, up to 64 tokens take two
 // other kernels instead: the weight split over many more blocks into fp32
@@ -464,16 +466,20 @@ __device__ __forceinline__ void proj_tile(const ProjKArgs& args, uint32_t id, ui
 #pragma unroll
       for (int e = 0; e < 4; ++e) acc[i][j][e] = 0.f;
 
-  // Two LDS stages; K step ks computes from stage ks % 2.  Fragments are
-  // double-buffered in registers: the reads of sub-step kk+1 are issued
+  // S LDS stages in a ring; K step ks computes from stage ks % S.  Fragments
+  // are double-buffered in registers: the reads of sub-step kk+1 are issued
   // before the MFMAs of sub-step kk.  Before the last sub-step of a step the
-  // wave waits for its loads of step ks+1 (into the other stage) and meets
-  // the barrier; after it, the stage just finished is free (every wave's
-  // reads of it have completed), so the loads of step ks+2 go there, and the
-  // first fragments of step ks+1 are read while the last MFMAs of step ks
-  // run.  Loads past the last step fetch the last step again (unused).
-  static_assert(G::S == 2 && G::KK % 2 == 0, "two stages, an even number of MFMA steps");
-  constexpr int KK = G::KK;
+  // wave waits for its loads of step ks+1 (those of steps ks+2 .. ks+S-1 stay
+  // in flight: loads into LDS complete in the order they were issued) and
+  // meets the barrier; after it, the stage just finished is free (every
+  // wave's reads of it have completed), so the loads of step ks+S go there,
+  // and the first fragments of step ks+1 are read while the last MFMAs of
+  // step ks run.  Loads past the last step fetch the last step again
+  // (unused).  More stages keep more of the operands in flight per block,
+  // which is what bounds a launch of few blocks reading a cold weight.
+  constexpr int S = G::S, KK = G::KK, L = G::kLoads;
+  static_assert(S >= 2 && KK % 2 == 0, "two stages or more, an even number of MFMA steps");
+  static_assert((S - 1) * L < 64, "the loads in flight fit the vmcnt counter");
   const uint32_t ksteps = K / BK;
   // a lane's fragment: row (lane % MS) of an MS-row block, 8 consecutive k
   // starting at 8*(lane/MS) of each KS-wide MFMA step; A and B use the same
@@ -482,6 +488,7 @@ __device__ __forceinline__ void proj_tile(const ProjKArgs& args, uint32_t id, ui
   const uint32_t arow = wm * G::kWaveM + fr, brow = G::BM + wn * G::kWaveN + fr;
   uint8_t* const stage0 = smem;
   uint8_t* const stage1 = smem + G::kStageBytes;
+  auto stage = [&](uint32_t i) { return smem + i * G::kStageBytes; };
 
   // The blocks of each XCD start their walk through K at their own eighth of
   // it: blocks on different XCDs that share weight columns then reach each
@@ -489,10 +496,17 @@ __device__ __forceinline__ void proj_tile(const ProjKArgs& args, uint32_t id, ui
   // first of them only and from the Infinity Cache for the rest.
   const uint32_t shift = QKNORM_PROJ_STAGGER ? uniform(blockIdx.x % 8 * ksteps / 8) : 0;
   const DmaOffsets<G> doff = dma_offsets<G>(ldx_bytes, ldw_bytes, wave, lane);
-  dma_tile<G>(ra, rb, doff, step_bytes<G>(0, ksteps, shift), stage0, wave);
-  wait_vmcnt<0>();
-  stage_barrier();
-  dma_tile<G>(ra, rb, doff, step_bytes<G>(1, ksteps, shift), stage1, wave);
+  if constexpr (S == 2) {
+    dma_tile<G>(ra, rb, doff, step_bytes<G>(0, ksteps, shift), stage0, wave);
+    wait_vmcnt<0>();
+    stage_barrier();
+    dma_tile<G>(ra, rb, doff, step_bytes<G>(1, ksteps, shift), stage1, wave);
+  } else {
+#pragma unroll
+    for (int p = 0; p < S; ++p) dma_tile<G>(ra, rb, doff, step_bytes<G>(p, ksteps, shift), stage(p), wave);
+    wait_vmcnt<(S - 1) * L>();                 // step 0 has landed (this wave)
+    stage_barrier();
+  }
   typedef typename ProjElem<DT>::V8 Frag;
   Frag fa[2][MB], fb[2][NB];
   read_frags<G, DT>(stage0, arow, brow, fk, fa[0], fb[0]);
@@ -506,9 +520,11 @@ __device__ __forceinline__ void proj_tile(const ProjKArgs& args, uint32_t id, ui
   constexpr int kMfmaPerRead = kSched && QKNORM_PROJ_MPR * kReads < kMfma ? QKNORM_PROJ_MPR : 1;
   constexpr int kFreeMfma = kSched ? kMfma - kReads * kMfmaPerRead : 1;
   constexpr int kLoadsPerMfma = (G::kLoads + kFreeMfma - 1) / kFreeMfma;
+  uint32_t cur = 0;                             // the stage of step ks (S > 2)
   for (uint32_t ks = 0; ks < ksteps; ++ks) {
-    uint8_t* const st = (ks & 1) ? stage1 : stage0;
-    uint8_t* const nx = (ks & 1) ? stage0 : stage1;
+    const uint32_t nxt = cur + 1 == (uint32_t)S ? 0 : cur + 1;
+    uint8_t* const st = S == 2 ? ((ks & 1) ? stage1 : stage0) : stage(cur);
+    uint8_t* const nx = S == 2 ? ((ks & 1) ? stage0 : stage1) : stage(nxt);
 #pragma unroll
     for (int kk = 0; kk < KK - 1; ++kk) {
       read_frags<G, DT>(st, arow, brow, (kk + 1) * G::KS + fk, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
@@ -519,13 +535,13 @@ __device__ __forceinline__ void proj_tile(const ProjKArgs& args, uint32_t id, ui
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    wait_vmcnt<0>();                            // step ks+1 has landed (this wave)
+    wait_vmcnt<(S - 2) * L>();                  // step ks+1 has landed (this wave)
     stage_barrier();                            // (and everyone's); stage st is free
     __builtin_amdgcn_sched_barrier(0);
     // the reads come first: the compiler cannot tell that the loads into
     // stage st do not overlap stage nx, so it keeps them in source order
     read_frags<G, DT>(nx, arow, brow, fk, fa[0], fb[0]);
-    dma_tile<G>(ra, rb, doff, step_bytes<G>(ks + 2, ksteps, shift), st, wave);
+    dma_tile<G>(ra, rb, doff, step_bytes<G>(ks + S, ksteps, shift), st, wave);
     mfma_step<G, DT>(acc, fa[1], fb[1]);
     if constexpr (kSched) {
       sched_interleave<kReads, 1, 0, kMfmaPerRead>();
@@ -535,6 +551,7 @@ __device__ __forceinline__ void proj_tile(const ProjKArgs& args, uint32_t id, ui
     // them with the reads before the loop into one read at the top of the
     // loop, which then waits for its result before the first MFMA
     asm volatile("" ::: "memory");
+    cur = nxt;
   }
   // the last step's spare loads into LDS must land before the block ends
   // (its LDS may then go to another block); waiting here, before the
@@ -847,14 +864,22 @@ __global__ __launch_bounds__(256) void qkv_proj_split_finish_kernel(ProjKArgs ar
 #ifndef QKNORM_PROJ_SPLIT
 #define QKNORM_PROJ_SPLIT 1        // 0: full tiles only
 #endif
-// Full tiles: 256 x 256, 8 waves of 64 x 128.  Half-width tiles: 256 x 128,
-// 8 waves of 64 x 64.
+// Full tiles: 256 x 256, 8 waves of 64 x 128, two LDS stages (128 KiB).
+// Half-width tiles: 256 x 128, 8 waves of 64 x 64, three stages (144 KiB, the
+// kernel's LDS in either case): where a launch is all or mostly half-width
+// tiles (513 to 1280 tokens on a Qwen3-8B layer) the third stage takes a
+// quarter to a third off the time with the weight cold (52 against 73-75 us
+// at 768 and 1024 tokens).
+#ifndef QKNORM_PROJ_STAGES_H
+#define QKNORM_PROJ_STAGES_H 3     // LDS stages of the half-width tiles
+#endif
 using GeoF = Tile<256, 256, 4, 2, QKNORM_PROJ_BK, 2>;
-using GeoH = Tile<256, 128, 4, 2, QKNORM_PROJ_BK, 2>;
+using GeoH = Tile<256, 128, 4, 2, QKNORM_PROJ_BK, QKNORM_PROJ_STAGES_H>;
 constexpr bool kSplit = QKNORM_PROJ_SPLIT != 0;
 constexpr int kBM = GeoF::BM, kBN = GeoF::BN, kThreads = GeoF::kThreads;
 constexpr int kLdsBytes = (GeoF::kStagesBytes > GeoH::kStagesBytes ? GeoF::kStagesBytes : GeoH::kStagesBytes) +
                           (kGammaFloats + kHalfFloats) * 4;
+static_assert(kLdsBytes <= 160 * 1024, "the stages fit a CU's 160 KiB of LDS");
 
 }  // namespace
 
@@ -878,7 +903,10 @@ bool proj_shape_ok(const ProjArgs& a) {
 // costing 1 and a half-width tile kHalfCost; n_split = N means no tail.
 // Head dims above 128 never split (a half-width tile would cut a head).
 static uint32_t split_column(uint32_t T, uint32_t N, uint32_t head_dim, int cus) {
-  constexpr double kHalfCost = 0.6;
+#ifndef QKNORM_PROJ_HALF_COST
+#define QKNORM_PROJ_HALF_COST 0.6
+#endif
+  constexpr double kHalfCost = QKNORM_PROJ_HALF_COST;
   const uint64_t m_tiles = (T + kBM - 1) / kBM;
   const uint64_t c = cus > 0 ? (uint64_t)cus : 1;
   auto rounds = [&](uint64_t n) { return (double)((n + c - 1) / c); };
@@ -953,12 +981,17 @@ static hipError_t launch_qkv_proj_decode(const ProjArgs& a, hipStream_t s) {
 #endif
 // 64-row tiles for small token counts: one head wide (or two heads of 64),
 // 8 waves of 16 x 64 (a head of 128 spans the two column waves), or 256
-// wide for head_dim 256; 48 KiB of LDS, so several blocks share a CU.  For
-// 17 to 256 tokens they take 38-39 us on the Qwen3-8B layer against 50-56 us
-// for 256-row tiles, which spend their MFMAs on empty rows; from about 512
-// tokens the 256-row tiles' lower operand traffic wins (56 against 76 us).
-using GeoS = Tile<64, 128, 4, 2, 64, 2>;
-using GeoS256 = Tile<64, 256, 4, 2, 64, 2>;
+// wide for head_dim 256.  Such a launch has few blocks (96 to 192 on a
+// Qwen3-8B layer), each reading a whole weight panel, so what bounds it is
+// the operand bytes one block keeps in flight: four LDS stages (96 KiB; three,
+// 120 KiB, for head_dim 256) keep three K steps in flight.  With the weight
+// cold in the Infinity Cache, 26-28 us from 17 to 256 tokens on that layer,
+// against 50-52 us with two stages.
+#ifndef QKNORM_PROJ_STAGES_S
+#define QKNORM_PROJ_STAGES_S 4     // LDS stages of the 64-row tiles (3 at most for head_dim 256)
+#endif
+using GeoS = Tile<64, 128, 4, 2, 64, QKNORM_PROJ_STAGES_S>;
+using GeoS256 = Tile<64, 256, 4, 2, 64, (QKNORM_PROJ_STAGES_S < 3 ? QKNORM_PROJ_STAGES_S : 3)>;
 
 // One launch of geometry G (G256 for head_dim 256), every block a full tile.
 template <class G, class G256>
@@ -974,24 +1007,31 @@ static hipError_t launch_qkv_proj_tiles(const ProjArgs& a, hipStream_t s) {
                   : (a.head_dim == 64    ? qkv_proj_kernel<G, G, kBF16, 64>
                      : a.head_dim == 128 ? qkv_proj_kernel<G, G, kBF16, 128>
                                          : qkv_proj_kernel<G256, G256, kBF16, 256>);
-  constexpr int kLds = G256::kStagesBytes + (kGammaFloats + kHalfFloats) * 4;
+  const int lds = (a.head_dim == 256 ? G256::kStagesBytes : G::kStagesBytes) +
+                  (kGammaFloats + kHalfFloats) * 4;
+  static_assert(G::kStagesBytes + (kGammaFloats + kHalfFloats) * 4 <= 160 * 1024 &&
+                    G256::kStagesBytes + (kGammaFloats + kHalfFloats) * 4 <= 160 * 1024,
+                "the stages fit a CU's 160 KiB of LDS");
   const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, dim3(tiles), dim3(G::kThreads), kLds, s, kernel_args(a), tiles, N);
+  hipLaunchKernelGGL(kern, dim3(tiles), dim3(G::kThreads), lds, s, kernel_args(a), tiles, N);
   return hipGetLastError();
 }
 
-// 128-row tiles for 257 to 512 tokens: one head wide, 8 waves of 32 x 64 (a
-// head of 128 across the two column waves), or 256 wide for head_dim 256.
-// At 384 and 512 tokens 44-45 us against 56-57 us for 256-row tiles on the
-// Qwen3-8B layer; from 768 tokens the 256-row tiles are faster (57 against
-// 88 us).
+// 128-row tiles for 257 to 512 tokens (and on while they fit one round of
+// the CUs): one head wide, 8 waves of 32 x 64 (a head of 128 across the two
+// column waves), or 256 wide for head_dim 256; four LDS stages (128 KiB;
+// three, 144 KiB, for head_dim 256).  Weight cold: 36-37 us at 384 and 512
+// tokens on the Qwen3-8B layer, against 57-58 us with two stages.
 #ifndef QKNORM_PROJ_MID_T
 #define QKNORM_PROJ_MID_T 512      // token counts up to this (above the 64-row range) take 128-row tiles
 #endif
-using GeoM = Tile<128, 128, 4, 2, 64, 2>;
-using GeoM256 = Tile<128, 256, 4, 2, 64, 2>;
+#ifndef QKNORM_PROJ_STAGES_M
+#define QKNORM_PROJ_STAGES_M 4     // LDS stages of the 128-row tiles (3 at most for head_dim 256)
+#endif
+using GeoM = Tile<128, 128, 4, 2, 64, QKNORM_PROJ_STAGES_M>;
+using GeoM256 = Tile<128, 256, 4, 2, 64, (QKNORM_PROJ_STAGES_M < 3 ? QKNORM_PROJ_STAGES_M : 3)>;
 
 // The split geometry for a token count: KS slices of K, blocks of 16 * JB
 // columns, TB blocks of 16 tokens.  Up to 8 tokens 16 columns by 4 slices
@@ -1107,8 +1147,16 @@ hipError_t proj_scratch(void** ptr) {
 hipError_t launch_qkv_proj(const ProjArgs& a, hipStream_t s, int cus) {
   if (a.T <= QKNORM_PROJ_DECODE_T) return launch_qkv_proj_decode(a, s);
   if (a.T <= QKNORM_PROJ_SMALL_T) return launch_qkv_proj_tiles<GeoS, GeoS256>(a, s);
-  if (a.T <= QKNORM_PROJ_MID_T) return launch_qkv_proj_tiles<GeoM, GeoM256>(a, s);
   const uint32_t N = (uint32_t)((a.hq + 2 * a.hkv) * a.head_dim);
+  // 128-row tiles up to 512 tokens, and up to 1024 while they fit one round
+  // of the chip's CUs (on a Qwen3-8B layer up to 640 tokens: 36 against 43 us
+  // for the 256-row launch at 513 tokens, 60 against 52 us at 768, where a
+  // second round would hold 32 tiles)
+  const uint64_t bn_m = a.head_dim == 256 ? GeoM256::BN : GeoM::BN;
+  const uint64_t m_tiles_m = (uint64_t)(a.T + GeoM::BM - 1) / GeoM::BM;
+  if (a.T <= QKNORM_PROJ_MID_T ||
+      (a.T <= 2 * QKNORM_PROJ_MID_T && m_tiles_m * ((N + bn_m - 1) / bn_m) <= (uint64_t)(cus > 0 ? cus : 1)))
+    return launch_qkv_proj_tiles<GeoM, GeoM256>(a, s);
   const uint32_t T = (uint32_t)a.T;
   const uint32_t n_split = split_column(T, N, (uint32_t)a.head_dim, cus);
   const uint32_t m_tiles = (T + kBM - 1) / kBM;

@@ -126,14 +126,20 @@ def test_fused_projection_against_oracle(T, hidden, hq, hkv, D):
     check(x, w, hq, hkv, D, gq, gk, eps, got, label=f"fused T={T} K={hidden}")
 
 
-# Which tile shapes a launch uses depends on the grid: a tail of half-width
-# (256 x 128) tiles is added where it fills the chip's CUs better (for
-# head_dim <= 128).  On MI355X's 256 CUs these shapes take, in turn: only
-# half-width tiles (small T), only full tiles, and full tiles for the first
-# columns with a half-width tail (N = 6144: from column 4864 at T = 6000, from
-# column 4096 at T = 4096).
+# Which tile shapes a launch uses depends on the token count and the grid.
+# From 17 tokens: 64-row tiles one head wide (four LDS stages; three for
+# head_dim 256); above 256 tokens 128-row tiles (the same), up to 512 tokens
+# and on to 1024 while they fit one round of the chip's CUs.  Beyond, 256-row
+# tiles: a tail of half-width (256 x 128, three stages) tiles is added where
+# it fills the CUs better (for head_dim <= 128).  On MI355X's 256 CUs these
+# take, in turn: only half-width tiles, only full tiles, and full tiles for
+# the first columns with a half-width tail (N = 6144: from column 4864 at
+# T = 6000, from column 4096 at T = 4096).
 @pytest.mark.parametrize("T,hidden,hq,hkv,D", [
-    (500, 256, 32, 8, 128),      # 2 row tiles x 48 half-width tiles: one round
+    (640, 256, 32, 8, 128),      # 128-row tiles past 512 tokens: 5 x 48 fit one round
+    (400, 320, 8, 2, 256),       # head_dim 256 on 128-row tiles (three stages), five K steps
+    (200, 64, 16, 4, 128),       # 64-row tiles, one K step through the four-stage ring
+    (768, 256, 32, 8, 128),      # 3 row tiles x 48 half-width tiles: one round
     (2048, 256, 32, 8, 128),     # 8 x 24 full tiles: one round, no tail
     (6000, 256, 32, 8, 128),     # 24 x 19 full tiles, then a tail of 24 x 10 half-width
     (4096, 192, 64, 16, 64),     # head_dim 64: 16 x 16 full tiles, then 16 x 16 half-width
