@@ -852,10 +852,10 @@ def main():
         print(json.dumps({"case": "proj", **bench_proj(q, torch, dev, args.steps, args.warmup, T=8192)}))
         return
     if args.case == "proj_tokens":
-        # the Qwen3-8B projection from decode sizes to prefill (one kernel per
-        # size range: one block per head up to 16 tokens, or the split kernels
-        # through a workspace; tiles above), the weight rotating through 6
-        # copies (300 MB)
+        # the Qwen3-8B projection from decode sizes to prefill (tiles of 64,
+        # 128 or 256 rows by token count; up to 64 tokens also the split
+        # kernels through a workspace), the weight rotating through 6 copies
+        # (300 MB)
         pts = {}
         for T in (1, 4, 8, 16, 32, 64, 128, 256, 512, 1024, 2048, 4096):
             r = bench_proj(q, torch, dev, args.steps, args.warmup, T=T, copies=6)

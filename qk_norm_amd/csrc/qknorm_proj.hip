@@ -27,11 +27,9 @@
 //
 // Fewer tokens take narrower launches of the same kernel (128-row tiles one
 // head wide up to 512 tokens, or on to 1024 while they fit one round of the
-// CUs; 64-row tiles up to 256), and up to 16 tokens
-// a separate kernel gives each head one block that reads its weight rows
-// once (qkv_proj_decode_kernel).  With a workspace, up to 64 tokens take two
-// other kernels instead: the weight split over many more blocks into fp32
-// partials, then one block per head adding them and normalising
+// CUs; 64-row tiles from 1 token to 256).  With a workspace, up to 64 tokens
+// take two other kernels instead: the weight split over many more blocks
+// into fp32 partials, then one block per head adding them and normalising
 // (qkv_proj_split_kernel, qkv_proj_split_finish_kernel).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -584,130 +582,10 @@ __global__ __launch_bounds__(GF::kThreads) void qkv_proj_kernel(ProjKArgs args, 
   }
 }
 
-// Decode sizes (T <= 16 tokens).  256 x 256 tiles would leave all but a few
-// of the CUs idle and spend their MFMAs on empty rows, while the time is in
-// reading the weight (N x K, each element once).  Here one block of 8 waves
-// takes one head (D columns) for all T tokens: WN groups of 64 columns times
-// WK = 8 / WN groups of 32-wide K chunks.  Each wave accumulates its 64
-// columns x 16*TB tokens over its chunks with the tiled kernel's MFMA (the
-// weight's fragment first), its fragments loaded straight from global memory
-// PF - 1 chunks ahead.  The WK partial sums then meet in LDS, one block of
-// 16 tokens at a time, and are added in K-group order; each token's head is
-// normalised on those fp32 sums (per-head QK-Norm, as in the tiled kernel)
-// and stored, four outputs (8 bytes) per thread.  Rows past T read zeros
-// (their offsets fall outside the activations' descriptor) and are not
-// stored.  A block reads the weight at 30-50 GB/s, so one block per head (48
-// for a Qwen3-8B layer) bounds this path near 2 TB/s.
-template <int DT, int D, int TB>
-__global__ __launch_bounds__(512) void qkv_proj_decode_kernel(ProjKArgs args) {
-  constexpr int WN = D / 64, WK = 8 / WN, JB = 4, PF = 4;
-  constexpr int kPitch = D + 4;                  // floats per token row (padding spreads the banks)
-  static_assert(WN * WK == 8 && TB >= 1 && TB <= 4, "");
-  __shared__ __attribute__((aligned(16))) float part[WK][16][kPitch];
-  typedef typename ProjElem<DT>::T Elem;
-  typedef typename ProjElem<DT>::V8 Frag;
-  const uint32_t tid = threadIdx.x, lane = tid & 63, wave = uniform(tid >> 6);
-  const uint32_t wn = wave % WN, wk = wave / WN;
-  const uint32_t head = blockIdx.x, n0 = head * D;
-  const uint32_t T = args.T, K = args.K;
-  const uint32_t nk = K / 32;                    // K chunks; this wave takes [c0, c1)
-  const uint32_t c0 = wk * nk / WK, c1 = (wk + 1) * nk / WK;
-  const uint32_t fr = lane % 16, fk = 8 * (lane / 16);
-  const Rsrc rw = make_rsrc(args.w + (uint64_t)(n0 + wn * 64) * args.ldw_bytes,
-                            (uint64_t)63 * args.ldw_bytes + K * 2);
-  const Rsrc rx = make_rsrc(args.x, (uint64_t)(T - 1) * args.ldx_bytes + K * 2);
-  uint32_t woff[JB], xoff[TB];
-#pragma unroll
-  for (int j = 0; j < JB; ++j) woff[j] = (j * 16 + fr) * args.ldw_bytes + fk * 2;
-#pragma unroll
-  for (int t = 0; t < TB; ++t) xoff[t] = (t * 16 + fr) * args.ldx_bytes + fk * 2;
-
-  f32x4 acc[TB][JB];
-#pragma unroll
-  for (int t = 0; t < TB; ++t)
-#pragma unroll
-    for (int j = 0; j < JB; ++j) acc[t][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  if (c0 < c1) {
-    // a ring of PF fragment sets; loads past the last chunk fetch the last
-    // chunk again (unused) so that every slot is loaded the same way
-    Frag wf[PF][JB], xf[PF][TB];
-    auto load = [&](Frag (&w)[JB], Frag (&x)[TB], uint32_t c) {
-      const uint32_t so = (c < c1 ? c : c1 - 1) * 64;
-#pragma unroll
-      for (int j = 0; j < JB; ++j)
-        w[j] = __builtin_bit_cast(Frag, __builtin_amdgcn_raw_buffer_load_b128(rw, woff[j], so, 0));
-#pragma unroll
-      for (int t = 0; t < TB; ++t)
-        x[t] = __builtin_bit_cast(Frag, __builtin_amdgcn_raw_buffer_load_b128(rx, xoff[t], so, 0));
-    };
-#pragma unroll
-    for (int p = 0; p < PF - 1; ++p) load(wf[p], xf[p], c0 + p);
-    for (uint32_t c = c0; c < c1; c += PF) {
-#pragma unroll
-      for (int p = 0; p < PF; ++p) {
-        const int kNext = (p + PF - 1) % PF;       // (constant once the loop is unrolled)
-        load(wf[kNext], xf[kNext], c + p + PF - 1);
-        if (c + p < c1) {
-#pragma unroll
-          for (int t = 0; t < TB; ++t)
-#pragma unroll
-            for (int j = 0; j < JB; ++j) acc[t][j] = ProjElem<DT>::mfma(wf[p][j], xf[p][t], acc[t][j]);
-        }
-      }
-    }
-  }
-
-  // per token block: each wave's partial into LDS, then thread tid takes
-  // four consecutive columns (4 * q4 ...) of token tt of the block
-  constexpr int kQuads = D / 4;                  // threads per token
-  constexpr int kTokPerPass = 512 / kQuads;      // 32, 16, 8
-  constexpr int kPasses = kTokPerPass >= 16 ? 1 : 16 / kTokPerPass;
-  const uint32_t q4 = tid % kQuads, tt = tid / kQuads;
-  const bool normed = args.norm && head < args.hq + args.hkv;
-  float g[4] = {1.f, 1.f, 1.f, 1.f};
-  if (normed) {
-    const Elem* gs = reinterpret_cast<const Elem*>(head < args.hq ? args.gamma_q : args.gamma_k);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) g[e] = (float)gs[4 * q4 + e];
-  }
-  const Rsrc ro = make_rsrc(args.out + (uint64_t)n0 * 2, (uint64_t)(T - 1) * args.ld_bytes + D * 2);
-#pragma unroll
-  for (int t = 0; t < TB; ++t) {
-    __syncthreads();                             // the previous block's sums have been read
-#pragma unroll
-    for (int j = 0; j < JB; ++j)
-      *reinterpret_cast<f32x4*>(&part[wk][fr][wn * 64 + j * 16 + 4 * (lane / 16)]) = acc[t][j];
-    __syncthreads();
-#pragma unroll
-    for (int ps = 0; ps < kPasses; ++ps) {
-      const uint32_t tok = ps * kTokPerPass + tt;    // (head_dim 64: the last 4 waves have none)
-      if (tok < 16) {
-        f32x4 v = *reinterpret_cast<const f32x4*>(&part[0][tok][4 * q4]);
-#pragma unroll
-        for (int w = 1; w < WK; ++w) v += *reinterpret_cast<const f32x4*>(&part[w][tok][4 * q4]);
-        const uint32_t row = t * 16 + tok;
-        float y[4] = {v[0], v[1], v[2], v[3]};
-        if (normed) {
-          float ss = 0.f;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) ss = __builtin_fmaf(y[e], y[e], ss);
-          const float sc = rms_scale(group_sum<kQuads>(ss), args.inv_d, args.eps);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) y[e] = (y[e] * g[e]) * sc;
-        }
-        typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-        const u32x2 o = {pack2<DT>(y[0], y[1]), pack2<DT>(y[2], y[3])};
-        __builtin_amdgcn_raw_buffer_store_b64(o, ro, row < T ? row * (uint32_t)args.ld_bytes + q4 * 8 : 0xFFFFFFF0u,
-                                              0, kStorePolicy);
-      }
-    }
-  }
-}
-
-// Small token counts through a workspace (T <= 64).  The kernels above give
-// a head's D columns (or a 64-row tile of them) to one block, and one block
-// reads at most 30-50 GB/s, less still when the weight comes from HBM rather
-// than the Infinity Cache.  Here the weight is cut into 16 * JB columns by KS
+// Small token counts through a workspace (T <= 64).  The tile kernel gives
+// a head's D columns (64 rows of them) to one block, so a decode-size launch
+// has one block per head (48 on a Qwen3-8B layer), each reading its whole
+// weight panel at about 45 GB/s.  Here the weight is cut into 16 * JB columns by KS
 // slices of K, one block of 4 waves each for all T tokens (TB blocks of 16),
 // so that the whole chip streams it.  Each wave takes a quarter of its
 // block's slice with the same MFMA (the weight's fragment first, fragments
@@ -945,39 +823,8 @@ static ProjKArgs kernel_args(const ProjArgs& a) {
   return k;
 }
 
-#ifndef QKNORM_PROJ_DECODE_T
-#define QKNORM_PROJ_DECODE_T 16    // token counts up to this take one block per head
-#endif
-static_assert(QKNORM_PROJ_DECODE_T >= 0 && QKNORM_PROJ_DECODE_T <= 64,
-              "the decode kernel holds at most 4 blocks of 16 tokens");
-
-// The decode kernel for TB blocks of 16 tokens (only the TB the threshold
-// allows are built).
-typedef void (*ProjKernel)(ProjKArgs);
-template <int DT, int D>
-static ProjKernel decode_kernel_d(uint32_t tb) {
-  constexpr uint32_t kMaxTb = (QKNORM_PROJ_DECODE_T + 15) / 16;
-  if constexpr (kMaxTb >= 4) if (tb == 4) return qkv_proj_decode_kernel<DT, D, 4>;
-  if constexpr (kMaxTb >= 3) if (tb == 3) return qkv_proj_decode_kernel<DT, D, 3>;
-  if constexpr (kMaxTb >= 2) if (tb == 2) return qkv_proj_decode_kernel<DT, D, 2>;
-  return qkv_proj_decode_kernel<DT, D, 1>;
-}
-
-template <int DT>
-static ProjKernel decode_kernel(int head_dim, uint32_t tb) {
-  return head_dim == 64 ? decode_kernel_d<DT, 64>(tb)
-                        : (head_dim == 128 ? decode_kernel_d<DT, 128>(tb) : decode_kernel_d<DT, 256>(tb));
-}
-
-static hipError_t launch_qkv_proj_decode(const ProjArgs& a, hipStream_t s) {
-  const uint32_t tb = (uint32_t)((a.T + 15) / 16);
-  auto kern = a.dtype == kF16 ? decode_kernel<kF16>(a.head_dim, tb) : decode_kernel<kBF16>(a.head_dim, tb);
-  hipLaunchKernelGGL(kern, dim3((uint32_t)(a.hq + 2 * a.hkv)), dim3(512), 0, s, kernel_args(a));
-  return hipGetLastError();
-}
-
 #ifndef QKNORM_PROJ_SMALL_T
-#define QKNORM_PROJ_SMALL_T 256    // token counts up to this (above the decode range) take 64-row tiles
+#define QKNORM_PROJ_SMALL_T 256    // token counts up to this take 64-row tiles
 #endif
 // 64-row tiles for small token counts: one head wide (or two heads of 64),
 // 8 waves of 16 x 64 (a head of 128 spans the two column waves), or 256
@@ -1145,7 +992,6 @@ hipError_t proj_scratch(void** ptr) {
 }
 
 hipError_t launch_qkv_proj(const ProjArgs& a, hipStream_t s, int cus) {
-  if (a.T <= QKNORM_PROJ_DECODE_T) return launch_qkv_proj_decode(a, s);
   if (a.T <= QKNORM_PROJ_SMALL_T) return launch_qkv_proj_tiles<GeoS, GeoS256>(a, s);
   const uint32_t N = (uint32_t)((a.hq + 2 * a.hkv) * a.head_dim);
   // 128-row tiles up to 512 tokens, and up to 1024 while they fit one round

@@ -195,17 +195,17 @@ def test_fused_equals_unfused_up_to_the_intermediate_rounding():
     assert np.array_equal(fused[:, (hq + hkv) * D:], unfused[:, (hq + hkv) * D:]), "V identical"
 
 
-# Small token counts: up to 16 the one-block-per-head kernel, 17 to 256 the
-# 64-row tiles.  Every head_dim, token counts on and off the 16-token blocks,
-# K chunks that do not divide evenly among the decode kernel's K groups (or
-# number fewer than them), and each head layout.
+# Small token counts, 1 to 256, take 64-row tiles (without a workspace).
+# Every head_dim, token counts on and off 16-row MFMA blocks, K steps fewer
+# than the tiles' four LDS stages (the ring then refetches the last one) or
+# not a multiple of them, and each head layout.
 @pytest.mark.parametrize("dtype", [BF16, F16], ids=["bf16", "fp16"])
 @pytest.mark.parametrize("T,hidden,hq,hkv,D", [
     (1, 4096, 32, 8, 128),       # a Qwen3-8B decode step
     (8, 4096, 32, 8, 128),
     (32, 4096, 32, 8, 128),
-    (17, 320, 4, 2, 128),        # 10 K chunks over 4 K groups
-    (2, 64, 3, 1, 64),           # 2 K chunks over 8 K groups: most waves have none
+    (17, 320, 4, 2, 128),        # 5 K steps through 4 stages
+    (2, 64, 3, 1, 64),           # one K step
     (31, 192, 5, 0, 64),         # no K or V heads
     (15, 448, 0, 3, 64),         # K heads only
     (16, 256, 2, 1, 256),        # head_dim 256
